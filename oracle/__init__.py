@@ -1,0 +1,123 @@
+"""CPU oracle for the dense GEMM C = A.B (plain C, fp64 accumulation, i-k-j loop).
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+bench's ``cpu_baseline`` leg may import this package.  It never imports the GPU
+library and the GPU library never imports it.
+
+The computation is the definition of the product on the pages ("Advanced CUDA
+features - starting from GEMM", roofline section case (4); "Kernel optimisation
+guide", Level 1; "GEMM kernels" memo, first kernel): C_ij = sum_k A_ik * B_kj.  All
+arithmetic happens in ``oracle.c``; this module only marshals numpy arrays.
+
+Pins (in ``tests/test_oracle.py``): a hand-worked product, identity and permutation
+matrices, small-integer inputs against exact integer products, exact rational brute
+force for every M, N, K in 1..8, the transpose identity, stride handling with
+NaN-filled padding, the error bound against an independent binary64 matrix product,
+exhaustive fp16/bf16 decoding against numpy, and planted mistakes that the pins catch.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "liboracle355.so")
+
+_lib = None
+
+
+def _configure(lib):
+    dp, fp, vp = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p
+    i = ctypes.c_int
+    for name in ("oracle_gemm_f32", "oracle_gemm_f16", "oracle_gemm_bf16"):
+        f = getattr(lib, name)
+        f.argtypes = [i, i, i, vp, i, vp, i, dp, fp, i]
+        f.restype = i
+    lib.oracle_gemm_f64.argtypes = [i, i, i, dp, i, dp, i, dp, fp, i]
+    lib.oracle_gemm_f64.restype = i
+    lib.oracle_f16_to_f64.argtypes = [ctypes.c_uint16]
+    lib.oracle_f16_to_f64.restype = ctypes.c_double
+    lib.oracle_bf16_to_f64.argtypes = [ctypes.c_uint16]
+    lib.oracle_bf16_to_f64.restype = ctypes.c_double
+    lib.oracle_num_threads.argtypes = []
+    lib.oracle_num_threads.restype = i
+    return lib
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            from . import build as _b
+            _b.build()
+        _lib = _configure(ctypes.CDLL(LIB_PATH))
+    return _lib
+
+
+def load_library(path: str):
+    """Load an oracle build from another path (used by the planted-mistake tests)."""
+    return _configure(ctypes.CDLL(path))
+
+
+def num_threads() -> int:
+    return _load().oracle_num_threads()
+
+
+def _row_stride(x: np.ndarray) -> int:
+    """Row stride in elements of a 2-D array whose rows are contiguous."""
+    if x.ndim != 2:
+        raise ValueError("expected a 2-D array")
+    item = x.itemsize
+    if x.size == 0:
+        return max(x.shape[1], 1)
+    if x.shape[1] > 1 and x.strides[1] != item:
+        raise ValueError("rows must be contiguous")
+    if x.shape[0] <= 1:
+        return max(x.shape[1], 1)
+    if x.strides[0] % item:
+        raise ValueError("row stride is not a whole number of elements")
+    return x.strides[0] // item
+
+
+_KIND = {"f32": (np.float32, "oracle_gemm_f32"),
+         "f16": (np.uint16, "oracle_gemm_f16"),
+         "bf16": (np.uint16, "oracle_gemm_bf16"),
+         "f64": (np.float64, "oracle_gemm_f64")}
+
+
+def gemm(A: np.ndarray, B: np.ndarray, dtype: str = "f32", lib=None):
+    """Return (C64, C32): the binary64 sums and their binary32 roundings, both M x N.
+
+    ``A`` (M x K) and ``B`` (K x N) are float32 arrays for ``"f32"``, uint16 bit
+    patterns for ``"f16"``/``"bf16"``, float64 for ``"f64"``.  Rows must be contiguous;
+    a row stride larger than the row length (a view into a padded buffer) is passed on
+    as lda / ldb.
+    """
+    np_t, fname = _KIND[dtype]
+    if A.dtype != np_t or B.dtype != np_t:
+        raise TypeError(f"{dtype} oracle expects {np.dtype(np_t)} operands")
+    M, K = A.shape
+    K2, N = B.shape
+    if K2 != K:
+        raise ValueError("inner dimensions differ")
+    lda = max(_row_stride(A), max(K, 1))
+    ldb = max(_row_stride(B), max(N, 1))
+    C64 = np.zeros((M, N), dtype=np.float64)
+    C32 = np.zeros((M, N), dtype=np.float32)
+    lib = lib or _load()
+    rc = getattr(lib, fname)(M, N, K, A.ctypes.data, lda, B.ctypes.data, ldb,
+                             C64.ctypes.data, C32.ctypes.data, max(N, 1))
+    if rc != 0:
+        raise RuntimeError(f"{fname} failed ({rc})")
+    return C64, C32
+
+
+def f16_to_f64(bits: int) -> float:
+    return _load().oracle_f16_to_f64(int(bits))
+
+
+def bf16_to_f64(bits: int) -> float:
+    return _load().oracle_bf16_to_f64(int(bits))

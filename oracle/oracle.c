@@ -1,0 +1,175 @@
+/*
+ * Reference dense GEMM on the CPU: C = A.B, row-major, plain C, fp64 accumulation.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the oracle that the GPU library is checked
+ * against.  Only the tests, the smoke check and the bench's CPU-baseline leg may load
+ * it; the GPU library never links, includes or calls it, and it shares no code with
+ * the GPU library.
+ *
+ * What it computes (the plain definition): for every 0 <= i < M, 0 <= j < N,
+ *
+ *     C[i][j] = sum_{k=0}^{K-1} A[i][k] * B[k][j]
+ *
+ * as stated on "Advanced CUDA features - starting from GEMM" (roofline section,
+ * case (4): each C_ij is the sum over k of A_ik * B_kj), on "Kernel optimisation
+ * guide" (GEMM optimisation path, Level 1: each output is a running sum over k of
+ * A[row*K+k]*B[k*N+col]) and on the "GEMM kernels" memo (first, textbook kernel).
+ *
+ * Storage: A is M x K with row stride lda (element (i,k) at A[i*lda+k]), B is K x N
+ * with row stride ldb, C is M x N with row stride ldc; the pages use packed strides
+ * (lda = K, ldb = N, ldc = N) and this generalises them to ld >= row length.
+ *
+ * Arithmetic: every input is converted exactly to double (binary32, binary16 and
+ * bfloat16 values are all exactly representable in binary64), each product of two
+ * such values is exact in binary64 (at most 24+24 significant bits), and each element
+ * is summed in increasing k in binary64, starting from +0.0.  The only roundings are
+ * the K-1 binary64 additions and, for the float output, one final round-to-nearest-even
+ * conversion to binary32.  The loop nest is i-k-j, which keeps every element's
+ * summation in increasing k, so the result equals the textbook i-j-k loop bit for bit
+ * and does not depend on the number of threads.  Build with -ffp-contract=off.
+ *
+ * Degenerate sizes: M = 0 or N = 0 writes nothing; K = 0 writes +0.0 (empty sum).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* IEEE 754 binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits.
+ * Subnormals (exponent field 0) are fraction * 2^-24; normals are
+ * (1024 + fraction) * 2^(e - 25); exponent field 31 encodes infinities and NaNs. */
+double oracle_f16_to_f64(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 0x1F;
+    int f = h & 0x3FF;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -24);
+    else if (e == 31)
+        v = (f == 0) ? INFINITY : NAN;
+    else
+        v = ldexp((double)(1024 + f), e - 25);
+    return sign ? -v : v;
+}
+
+/* bfloat16 is the upper half of an IEEE 754 binary32 pattern. */
+double oracle_bf16_to_f64(uint16_t h)
+{
+    uint32_t u = (uint32_t)h << 16;
+    float x;
+    memcpy(&x, &u, sizeof x);
+    return (double)x;
+}
+
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+static int bad_args(int M, int N, int K, int lda, int ldb, int ldc)
+{
+    if (M < 0 || N < 0 || K < 0) return 1;
+    if (lda < (K > 1 ? K : 1) || ldb < (N > 1 ? N : 1) || ldc < (N > 1 ? N : 1)) return 1;
+    return 0;
+}
+
+/* The definition on binary64 operands.  C64 (row stride ldc) receives the binary64
+ * sums; C32, if not NULL, receives the same sums rounded once to binary32 (same
+ * stride).  Returns 0, or -1 on invalid sizes or strides. */
+int oracle_gemm_f64(int M, int N, int K, const double *A, int lda, const double *B, int ldb,
+                    double *C64, float *C32, int ldc)
+{
+    if (bad_args(M, N, K, lda, ldb, ldc)) return -1;
+    if (M == 0 || N == 0) return 0;
+    int fail = 0;
+#pragma omp parallel
+    {
+        double *r = (double *)malloc(sizeof(double) * (size_t)N);
+        if (!r) {
+#pragma omp atomic write
+            fail = 1;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int i = 0; i < M; ++i) {
+            if (!r) continue;
+            for (int j = 0; j < N; ++j) r[j] = 0.0;
+            const double *arow = A + (size_t)i * lda;
+            for (int k = 0; k < K; ++k) {
+                const double a = arow[k];
+                const double *brow = B + (size_t)k * ldb;
+                for (int j = 0; j < N; ++j) r[j] += a * brow[j];
+            }
+            double *c64 = C64 + (size_t)i * ldc;
+            for (int j = 0; j < N; ++j) c64[j] = r[j];
+            if (C32) {
+                float *c32 = C32 + (size_t)i * ldc;
+                for (int j = 0; j < N; ++j) c32[j] = (float)r[j];
+            }
+        }
+        free(r);
+    }
+    return fail ? -1 : 0;
+}
+
+/* Widen a rows x cols block with row stride ld into a packed binary64 array. */
+typedef double (*decode_fn)(const void *base, size_t idx);
+
+static double dec_f32(const void *p, size_t i) { return (double)((const float *)p)[i]; }
+static double dec_f16(const void *p, size_t i) { return oracle_f16_to_f64(((const uint16_t *)p)[i]); }
+static double dec_bf16(const void *p, size_t i) { return oracle_bf16_to_f64(((const uint16_t *)p)[i]); }
+
+static double *widen(const void *src, int rows, int cols, int ld, decode_fn dec)
+{
+    size_t n = (size_t)rows * (size_t)cols;
+    double *out = (double *)malloc(sizeof(double) * (n ? n : 1));
+    if (!out) return NULL;
+#pragma omp parallel for schedule(static)
+    for (int r = 0; r < rows; ++r)
+        for (int c = 0; c < cols; ++c)
+            out[(size_t)r * cols + c] = dec(src, (size_t)r * ld + c);
+    return out;
+}
+
+static int gemm_typed(int M, int N, int K, const void *A, int lda, const void *B, int ldb,
+                      double *C64, float *C32, int ldc, decode_fn dec)
+{
+    if (bad_args(M, N, K, lda, ldb, ldc)) return -1;
+    if (M == 0 || N == 0) return 0;
+    double *a = widen(A, M, K, lda, dec);
+    double *b = widen(B, K, N, ldb, dec);
+    int rc = -1;
+    if (a && b)
+        rc = oracle_gemm_f64(M, N, K, a, K > 0 ? K : 1, b, N, C64, C32, ldc);
+    free(a);
+    free(b);
+    return rc;
+}
+
+/* FP32 operands. */
+int oracle_gemm_f32(int M, int N, int K, const float *A, int lda, const float *B, int ldb,
+                    double *C64, float *C32, int ldc)
+{
+    return gemm_typed(M, N, K, A, lda, B, ldb, C64, C32, ldc, dec_f32);
+}
+
+/* IEEE binary16 operands given as bit patterns. */
+int oracle_gemm_f16(int M, int N, int K, const uint16_t *A, int lda, const uint16_t *B, int ldb,
+                    double *C64, float *C32, int ldc)
+{
+    return gemm_typed(M, N, K, A, lda, B, ldb, C64, C32, ldc, dec_f16);
+}
+
+/* bfloat16 operands given as bit patterns. */
+int oracle_gemm_bf16(int M, int N, int K, const uint16_t *A, int lda, const uint16_t *B, int ldb,
+                     double *C64, float *C32, int ldc)
+{
+    return gemm_typed(M, N, K, A, lda, B, ldb, C64, C32, ldc, dec_bf16);
+}

@@ -1,0 +1,70 @@
+"""The seeded input generator: determinism, stream prefixes and storage rounding."""
+
+import hashlib
+
+import numpy as np
+import pytest
+
+from roofline_optimisation_amd import inputs
+
+# SHA-256 prefixes of A||B recorded when the recipe was fixed; a change here means the
+# synthetic workloads changed.
+DIGESTS = {
+    "f32_256": "56ac2f22bd24a1a6",
+    "f32_256_int": "fba5c0e5c109c05a",
+    "f32_1023x997x515": "9f1a72b5f3dc0cfb",
+}
+
+
+@pytest.mark.parametrize("name", sorted(DIGESTS))
+def test_digests(name):
+    A, B = inputs.operands_for(inputs.CASES[name])
+    assert hashlib.sha256(A.tobytes() + B.tobytes()).hexdigest()[:16] == DIGESTS[name]
+
+
+def test_half_digests():
+    A, B = inputs.make_operands(64, 32, 48, 3, "uniform", "f16")
+    assert hashlib.sha256(A.tobytes() + B.tobytes()).hexdigest()[:16] == "66b12c3ed295e6f5"
+    A, B = inputs.make_operands(64, 32, 48, 4, "uniform", "bf16")
+    assert hashlib.sha256(A.tobytes() + B.tobytes()).hexdigest()[:16] == "b294174e5808473f"
+
+
+@pytest.mark.parametrize("dist", ["uniform", "normal", "int"])
+def test_draw_rows_is_a_prefix(dist):
+    A, _ = inputs.make_operands(50, 7, 33, 9, dist, "f32")
+    assert np.array_equal(inputs.draw_rows(50, 33, 9, dist, "f32", rows=17), A[:17])
+
+
+def test_ranges():
+    A, B = inputs.make_operands(100, 90, 80, 1, "uniform")
+    assert A.dtype == np.float32 and A.min() >= -1 and A.max() <= 1
+    A, _ = inputs.make_operands(100, 90, 80, 1, "int")
+    assert set(np.unique(A).tolist()) <= set(range(-4, 5))
+
+
+def test_bf16_round_to_nearest_even():
+    one = 1.0
+    ulp = 2.0 ** -7                       # bf16 spacing just above 1
+    x = np.array([one, one + ulp / 2, one + 1.5 * ulp, one + 0.75 * ulp, -one - ulp / 4,
+                  3.0e38], np.float32)
+    bits = inputs.f32_to_bf16_bits(x)
+    back = (bits.astype(np.uint32) << 16).view(np.float32)
+    assert back[0] == 1.0
+    assert back[1] == 1.0                 # tie -> even
+    assert back[2] == one + 2 * ulp       # tie -> even (odd neighbour below)
+    assert back[3] == one + ulp           # above half -> up
+    assert back[4] == -1.0
+    assert np.isfinite(back[5])
+
+
+def test_f16_matches_numpy():
+    x = np.random.default_rng(0).uniform(-1, 1, 1000).astype(np.float32)
+    assert np.array_equal(inputs.f32_to_f16_bits(x).view(np.float16), x.astype(np.float16))
+
+
+def test_embed():
+    x = np.arange(6, dtype=np.float32).reshape(2, 3)
+    e = inputs.embed(x, 5, extra_rows=1)
+    assert e.shape == (3, 5) and np.array_equal(e[:2, :3], x) and np.isnan(e[:, 3:]).all()
+    h = inputs.embed(np.ones((2, 2), np.uint16), 3)
+    assert h[0, 2] == 0x7E00
