@@ -1,0 +1,203 @@
+#!/usr/bin/env python3
+"""Benchmark of libgemm355 on one MI355X: GEMM TFLOP/s (2MNK / t) and fraction of peak.
+
+A step is one call of the FP32 entry point gemm_f32 on the 3072 x 3072 x 3072 workload
+(row-major, packed strides, A and B i.i.d. U[-1,1] from seed 1), with the operands
+already resident in HBM.  W untimed warm-up steps are followed by K timed steps on one
+HIP stream, bracketed by device synchronisation; the per-step time comes from HIP
+events recorded on that stream.  The FP16-input / FP32-accumulate 4096^3 workload
+(seed 3) is measured the same way and reported beside it.
+
+The JSON line also carries
+  * "roofline": the dominant kernel's achieved TFLOP/s against the MI355X peak for its
+    arithmetic (FP32 on the matrix cores: 157.3 TFLOP/s), with HBM traffic from the
+    committed rocprofv3 counter summary when it was taken on the current kernel source;
+  * "cpu_baseline": the CPU oracle (plain C, fp64 accumulation, OpenMP over rows) timed
+    on this host on one full step of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAKS = {"f32": 157.3, "f16": 2516.6, "bf16": 2516.6}  # TFLOP/s, dense, 2.4 GHz
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "roofline_optimisation_amd", "csrc")
+KERNEL_SOURCES = {"f32": ["k_mfma_f32.hip", "common.hpp"], "f16": ["k_mfma_f16.hip", "common.hpp"]}
+PMC_FILES = {"f32": "pmc_mfma_f32_n3072.txt", "f16": "pmc_mfma_f16_n4096.txt"}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_hash(kind: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kind]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kind: str):
+    """HBM bytes per launch from the committed counter summary, or None if there is none
+    or it was taken on a different kernel source."""
+    path = os.path.join(PROFILES, PMC_FILES[kind])
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for ln in open(path):
+        if ":" in ln and not ln.lstrip().startswith("#"):
+            k, v = ln.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256") != kernel_hash(kind):
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def time_gemm(kind, M, N, K, seed, steps, warmup):
+    import torch
+
+    from roofline_optimisation_amd import binding as gb
+    from roofline_optimisation_amd import inputs
+
+    dt = "f32" if kind == "f32" else "f16"
+    A, B = inputs.make_operands(M, N, K, seed, "uniform", dt)
+    if dt == "f32":
+        dA, dB = torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda()
+        entry = gb.gemm_f32
+    else:
+        dA = torch.from_numpy(A.view("int16")).cuda()
+        dB = torch.from_numpy(B.view("int16")).cuda()
+        entry = gb.gemm_f16f32acc
+    dC = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.Stream()
+    h = stream.cuda_stream
+    args = (M, N, K, dA.data_ptr(), K, dB.data_ptr(), N, dC.data_ptr(), N, h)
+    desc = gb.gemm355_kernel_desc(-1, gb.DTYPE_CODES[dt], M, N, K, dA.data_ptr(), K,
+                                  dB.data_ptr(), N, dC.data_ptr(), N)
+
+    def step():
+        st = entry(*args)
+        if st != gb.OK:
+            raise gb.Gemm355Error(st, entry.__name__)
+
+    torch.cuda.synchronize()
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    stream.synchronize()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / steps
+    return {"ms": ms, "wall_ms": wall * 1e3 / steps, "desc": desc, "A": A, "B": B, "dC": dC}
+
+
+def cpu_baseline(A, B, M, N, K):
+    import oracle
+    t0 = time.perf_counter()
+    oracle.gemm(A, B, "f32")
+    dt = time.perf_counter() - t0
+    return {"value": round(2.0 * M * N * K / dt / 1e12, 5), "unit": "TFLOP/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"one full step: FP32 {M}x{N}x{K} (same seeded operands), "
+                      f"{dt:.2f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--only", choices=["f32", "f16"], default=None,
+                    help="measure one workload only (for profiler runs)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}, WORLD_SIZE {world}): "
+              "this library is a single-GPU GEMM; see the sharding notes in DESIGN.md",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+
+    from roofline_optimisation_amd import roofline as rl
+
+    results = {}
+    for kind, n, seed in (("f32", 3072, 1), ("f16", 4096, 3)):
+        if args.only and args.only != kind:
+            continue
+        log(f"[bench] {kind} {n}^3: warmup {args.warmup}, steps {args.steps}")
+        r = time_gemm(kind, n, n, n, seed, args.steps, args.warmup)
+        tf = 2.0 * n ** 3 / (r["ms"] * 1e-3) / 1e12
+        r["tflops"] = tf
+        results[kind] = r
+        log(f"[bench] {kind} {n}^3 {r['desc']}: {r['ms']:.4f} ms/launch, {tf:.1f} TFLOP/s "
+            f"({100 * tf / PEAKS[kind]:.1f}% of {PEAKS[kind]})")
+
+    def roof(kind, n):
+        r = results[kind]
+        tr = measured_traffic(kind)
+        in_b = 4 if kind == "f32" else 2
+        return {"bound": "mfma", "achieved": round(r["tflops"], 2), "peak": PEAKS[kind],
+                "unit": "TFLOP/s", "frac": round(r["tflops"] / PEAKS[kind], 4),
+                "traffic": tr, "algorithmic_flops": 2 * n ** 3,
+                "ideal_bytes": rl.ideal_bytes(n, n, n, in_b, 4), "kernel": r["desc"]}
+
+    main_kind = "f32" if "f32" in results else "f16"
+    n = 3072 if main_kind == "f32" else 4096
+    r = results[main_kind]
+    line = {
+        "metric": "GEMM TFLOPS (2MNK/s) + % of peak: FP32 n=3072, FP16->FP32 n=4096, 1 MI355X",
+        "value": round(r["tflops"], 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if main_kind == "f32" else "f16->f32",
+        "data": "synthetic",
+        "config": {"workload": f"gemm_{main_kind}_{n}", "M": n, "N": n, "K": n,
+                   "layout": "row-major, packed strides", "dist": "U[-1,1]",
+                   "seed": 1 if main_kind == "f32" else 3, "kernel": r["desc"]},
+        "roofline": roof(main_kind, n),
+    }
+    if main_kind == "f32" and "f16" in results:
+        f = results["f16"]
+        line["fp16_n4096"] = {"value": round(f["tflops"], 2), "unit": "TFLOP/s",
+                              "ms_per_step": round(f["ms"], 5), "frac": round(f["tflops"] / PEAKS["f16"], 4),
+                              "roofline": roof("f16", 4096)}
+    if not args.no_cpu_baseline and main_kind == "f32":
+        log("[bench] timing the CPU oracle on one full step")
+        line["cpu_baseline"] = cpu_baseline(r["A"], r["B"], n, n, n)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,129 @@
+/*
+ * libgemm355 -- dense general matrix multiply C = A.B on AMD Instinct MI355X (gfx950).
+ *
+ * The operation (the definition used throughout "Advanced CUDA features - starting
+ * from GEMM", roofline section, case (4), and "Kernel optimisation guide", GEMM
+ * optimisation path, Level 1):
+ *
+ *     C[i][j] = sum_{k=0}^{K-1} A[i][k] * B[k][j],   0 <= i < M, 0 <= j < N
+ *
+ * Layout: all matrices are row-major with explicit leading dimensions (row strides,
+ * in elements): element (i,k) of A is A[i*lda + k], element (k,j) of B is
+ * B[k*ldb + j], element (i,j) of C is C[i*ldc + j].  The pages use packed strides
+ * (lda = K, ldb = N, ldc = N); any stride at least the row length is accepted.
+ *
+ * Result: C is overwritten (no alpha/beta).  Accumulation is in FP32.  FP16 and BF16
+ * operands are multiplied exactly and summed in FP32.  Only C[0..M) x [0..N) is
+ * written; padding columns N..ldc-1 and memory outside the logical matrices are
+ * never read (A, B) or written (C).
+ *
+ * Ownership: every pointer is a device pointer owned by the caller; the library
+ * allocates nothing, keeps no per-call state and needs no workspace.  A and B are
+ * read-only.  C must not overlap A or B.
+ *
+ * Asynchrony: the work is enqueued on `stream` (NULL = the null stream) and the call
+ * returns without waiting.  Faults during execution surface at the caller's next
+ * synchronisation on that stream.
+ *
+ * Errors (returned, never aborting the process):
+ *   GEMM355_ERR_INVALID_ARG  any dimension < 0; lda < max(1,K), ldb < max(1,N) or
+ *                            ldc < max(1,N); a NULL pointer for a matrix with a
+ *                            nonzero number of elements; unknown variant or dtype.
+ *                            Detected on the host before any HIP call.
+ *   GEMM355_ERR_DEVICE       no current HIP device, or it is not gfx950.
+ *   GEMM355_ERR_LAUNCH       the kernel launch was rejected by the runtime.
+ *   GEMM355_ERR_UNSUPPORTED  the forced variant does not exist for this dtype.
+ * Degenerate shapes: M = 0 or N = 0 is a no-op returning GEMM355_OK; K = 0 writes
+ * +0.0 to every element of C (the empty sum).
+ *
+ * Thread safety: calls may be made from several host threads; the only shared state
+ * is the cached per-device architecture check.
+ */
+#ifndef GEMM355_H
+#define GEMM355_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same declaration as HIP's own: an opaque stream handle. */
+typedef struct ihipStream_t *hipStream_t;
+
+typedef enum gemm355_status {
+    GEMM355_OK = 0,
+    GEMM355_ERR_INVALID_ARG = 1,
+    GEMM355_ERR_DEVICE = 2,
+    GEMM355_ERR_LAUNCH = 3,
+    GEMM355_ERR_UNSUPPORTED = 4
+} gemm355_status;
+
+/* Operand storage types.  FP16 is IEEE binary16, BF16 is bfloat16; both are passed
+ * as 16-bit patterns (uint16_t). */
+typedef enum gemm355_dtype {
+    GEMM355_F32 = 0,
+    GEMM355_F16 = 1,
+    GEMM355_BF16 = 2
+} gemm355_dtype;
+
+/* Kernel families.  NAIVE: one thread per element of C, every operand read from
+ * global memory ("Kernel optimisation guide", Level 1).  LDS_TILED: A and B tiles
+ * staged in local data share and reused across a workgroup ("Advanced CUDA
+ * features", Shared Memory Tiling).  REGBLOCK: FP32 on the vector ALUs with a per-
+ * thread register micro-tile and a double-buffered LDS pipeline (same page, Register
+ * Tiling; "Kernel optimisation guide", Level 3).  MFMA: the matrix cores (the AMD
+ * counterpart of the tensor-core level, "Kernel optimisation guide", Level 4), for
+ * FP32 (v_mfma_f32_32x32x2_f32) and FP16/BF16 with FP32 accumulation. */
+typedef enum gemm355_variant {
+    GEMM355_VARIANT_AUTO = -1,
+    GEMM355_VARIANT_NAIVE = 0,
+    GEMM355_VARIANT_LDS_TILED = 1,
+    GEMM355_VARIANT_REGBLOCK = 2,
+    GEMM355_VARIANT_MFMA = 3
+} gemm355_variant;
+
+/* C = A.B with FP32 operands and FP32 accumulation. */
+gemm355_status gemm_f32(int M, int N, int K, const float *A, int lda, const float *B, int ldb,
+                        float *C, int ldc, hipStream_t stream);
+
+/* C = A.B with IEEE binary16 operands (bit patterns), exact products, FP32 accumulation
+ * and FP32 output. */
+gemm355_status gemm_f16f32acc(int M, int N, int K, const uint16_t *A, int lda, const uint16_t *B,
+                              int ldb, float *C, int ldc, hipStream_t stream);
+
+/* C = A.B with bfloat16 operands (bit patterns), exact products, FP32 accumulation and
+ * FP32 output. */
+gemm355_status gemm_bf16f32acc(int M, int N, int K, const uint16_t *A, int lda, const uint16_t *B,
+                               int ldb, float *C, int ldc, hipStream_t stream);
+
+/* The same contract with the kernel family chosen by the caller (`variant`, one of
+ * gemm355_variant; AUTO picks as the typed entry points do) and the operand type given
+ * by `dtype` (one of gemm355_dtype).  Available: NAIVE for all dtypes; LDS_TILED and
+ * REGBLOCK for F32; MFMA for all dtypes.  Used to measure and test each family. */
+gemm355_status gemm355_run_variant(int variant, int dtype, int M, int N, int K, const void *A,
+                                   int lda, const void *B, int ldb, float *C, int ldc,
+                                   hipStream_t stream);
+
+/* Host-only: the family the typed entry points would launch for these arguments, or -1
+ * if the arguments are invalid.  Makes no HIP call. */
+int gemm355_select_variant(int dtype, int M, int N, int K, const void *A, int lda, const void *B,
+                           int ldb, const float *C, int ldc);
+
+/* Host-only: a static, NUL-terminated description of the kernel instance (family,
+ * tile shape, load path) that gemm355_run_variant would launch, or "invalid". */
+const char *gemm355_kernel_desc(int variant, int dtype, int M, int N, int K, const void *A, int lda,
+                                const void *B, int ldb, const float *C, int ldc);
+
+/* Host-only: static strings for status codes and variants ("unknown" otherwise). */
+const char *gemm355_status_string(int status);
+const char *gemm355_variant_name(int variant);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int gemm355_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GEMM355_H */

@@ -1,0 +1,188 @@
+"""ctypes binding of libgemm355 (argument marshalling only).
+
+The functions named like the C entry points take plain integers (device pointers as
+ints, a stream handle as an int) and return the C status code.  ``matmul`` is a
+convenience wrapper for torch tensors that derives sizes, strides, pointers and the
+current stream, calls the C entry point and raises on a non-OK status.  Nothing here
+computes any part of the product: every step runs in the HIP kernels of
+``libgemm355.so``.  If the library is missing or cannot be loaded, every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libgemm355.so")
+
+OK, ERR_INVALID_ARG, ERR_DEVICE, ERR_LAUNCH, ERR_UNSUPPORTED = 0, 1, 2, 3, 4
+F32, F16, BF16 = 0, 1, 2
+VARIANT_AUTO, VARIANT_NAIVE, VARIANT_LDS_TILED, VARIANT_REGBLOCK, VARIANT_MFMA = -1, 0, 1, 2, 3
+VARIANTS = {"naive": VARIANT_NAIVE, "lds_tiled": VARIANT_LDS_TILED,
+            "regblock": VARIANT_REGBLOCK, "mfma": VARIANT_MFMA, "auto": VARIANT_AUTO}
+DTYPE_CODES = {"f32": F32, "f16": F16, "bf16": BF16}
+
+# Every symbol the public headers declare.
+EXPORTS = (
+    "gemm_f32", "gemm_f16f32acc", "gemm_bf16f32acc", "gemm355_run_variant",
+    "gemm355_select_variant", "gemm355_kernel_desc", "gemm355_status_string",
+    "gemm355_variant_name", "gemm355_version",
+    "gemm355_probe_mfma_shape", "gemm355_probe_mfma", "gemm355_probe_ds_read_tr16",
+)
+
+
+class Gemm355Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+_lib = None
+
+
+def _configure(lib):
+    i, p, s = ctypes.c_int, ctypes.c_void_p, ctypes.c_char_p
+    gemm_args = [i, i, i, p, i, p, i, p, i, p]
+    for name in ("gemm_f32", "gemm_f16f32acc", "gemm_bf16f32acc"):
+        f = getattr(lib, name)
+        f.argtypes = gemm_args
+        f.restype = i
+    lib.gemm355_run_variant.argtypes = [i, i] + gemm_args
+    lib.gemm355_run_variant.restype = i
+    lib.gemm355_select_variant.argtypes = [i, i, i, i, p, i, p, i, p, i]
+    lib.gemm355_select_variant.restype = i
+    lib.gemm355_kernel_desc.argtypes = [i, i, i, i, i, p, i, p, i, p, i]
+    lib.gemm355_kernel_desc.restype = s
+    lib.gemm355_status_string.argtypes = [i]
+    lib.gemm355_status_string.restype = s
+    lib.gemm355_variant_name.argtypes = [i]
+    lib.gemm355_variant_name.restype = s
+    lib.gemm355_version.argtypes = []
+    lib.gemm355_version.restype = i
+    lib.gemm355_probe_mfma_shape.argtypes = [i, ctypes.POINTER(i), ctypes.POINTER(i)]
+    lib.gemm355_probe_mfma_shape.restype = i
+    lib.gemm355_probe_mfma.argtypes = [i, i, p, p, p, p]
+    lib.gemm355_probe_mfma.restype = i
+    lib.gemm355_probe_ds_read_tr16.argtypes = [ctypes.POINTER(ctypes.c_uint32), p, p]
+    lib.gemm355_probe_ds_read_tr16.restype = i
+    return lib
+
+
+def lib():
+    """The loaded ``libgemm355.so``; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -c 'import __graft_entry__ as g; g.build()'`")
+        _lib = _configure(ctypes.CDLL(LIB_PATH))
+    return _lib
+
+
+# ----------------------------------------------------------- C entry points
+
+def gemm_f32(M, N, K, A, lda, B, ldb, C, ldc, stream=0) -> int:
+    return lib().gemm_f32(M, N, K, A, lda, B, ldb, C, ldc, stream)
+
+
+def gemm_f16f32acc(M, N, K, A, lda, B, ldb, C, ldc, stream=0) -> int:
+    return lib().gemm_f16f32acc(M, N, K, A, lda, B, ldb, C, ldc, stream)
+
+
+def gemm_bf16f32acc(M, N, K, A, lda, B, ldb, C, ldc, stream=0) -> int:
+    return lib().gemm_bf16f32acc(M, N, K, A, lda, B, ldb, C, ldc, stream)
+
+
+def gemm355_run_variant(variant, dtype, M, N, K, A, lda, B, ldb, C, ldc, stream=0) -> int:
+    return lib().gemm355_run_variant(variant, dtype, M, N, K, A, lda, B, ldb, C, ldc, stream)
+
+
+def gemm355_select_variant(dtype, M, N, K, A, lda, B, ldb, C, ldc) -> int:
+    return lib().gemm355_select_variant(dtype, M, N, K, A, lda, B, ldb, C, ldc)
+
+
+def gemm355_kernel_desc(variant, dtype, M, N, K, A, lda, B, ldb, C, ldc) -> str:
+    return lib().gemm355_kernel_desc(variant, dtype, M, N, K, A, lda, B, ldb, C, ldc).decode()
+
+
+def gemm355_status_string(status: int) -> str:
+    return lib().gemm355_status_string(status).decode()
+
+
+def gemm355_variant_name(variant: int) -> str:
+    return lib().gemm355_variant_name(variant).decode()
+
+
+def gemm355_version() -> int:
+    return lib().gemm355_version()
+
+
+def gemm355_probe_mfma_shape(kind: int) -> tuple[int, int]:
+    e, r = ctypes.c_int(), ctypes.c_int()
+    if lib().gemm355_probe_mfma_shape(kind, ctypes.byref(e), ctypes.byref(r)) != 0:
+        raise ValueError(f"unknown probe kind {kind}")
+    return e.value, r.value
+
+
+def gemm355_probe_mfma(kind, nruns, dev_a, dev_b, dev_d, stream=0) -> int:
+    return lib().gemm355_probe_mfma(kind, nruns, dev_a, dev_b, dev_d, stream)
+
+
+def gemm355_probe_ds_read_tr16(host_addrs, dev_out, stream=0) -> int:
+    arr = (ctypes.c_uint32 * 64)(*[int(a) for a in host_addrs])
+    return lib().gemm355_probe_ds_read_tr16(arr, dev_out, stream)
+
+
+def status_string(status: int) -> str:
+    try:
+        return gemm355_status_string(status)
+    except Exception:  # library not loadable: still describe the code
+        return {0: "ok", 1: "invalid argument", 2: "no gfx950 device", 3: "kernel launch failed",
+                4: "variant not available for this dtype"}.get(status, "unknown")
+
+
+# ----------------------------------------------------------- torch marshalling
+
+def _ld(t) -> int:
+    if t.dim() != 2:
+        raise ValueError("expected a 2-D tensor")
+    if t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError("rows must be contiguous (stride(1) == 1)")
+    return max(int(t.stride(0)) if t.shape[0] > 1 else int(t.shape[1]), int(t.shape[1]), 1)
+
+
+def _dtype_code(t) -> int:
+    import torch
+    codes = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
+    if t.dtype not in codes:
+        raise TypeError(f"unsupported operand dtype {t.dtype}")
+    return codes[t.dtype]
+
+
+def matmul(A, B, out=None, variant: int | str = VARIANT_AUTO, stream=None):
+    """C = A.B on the GPU through libgemm355; A, B are 2-D CUDA tensors (float32, float16
+    or bfloat16, rows contiguous), the result is float32.  Raises Gemm355Error on a
+    non-OK status; never falls back to another implementation."""
+    import torch
+    if isinstance(variant, str):
+        variant = VARIANTS[variant]
+    if not (A.is_cuda and B.is_cuda):
+        raise ValueError("operands must be CUDA tensors")
+    if A.dtype != B.dtype:
+        raise TypeError("A and B must have the same dtype")
+    M, K = A.shape
+    K2, N = B.shape
+    if K2 != K:
+        raise ValueError("inner dimensions differ")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    if out.dtype != torch.float32 or tuple(out.shape) != (M, N):
+        raise ValueError("out must be a float32 M x N tensor")
+    s = stream if stream is not None else torch.cuda.current_stream(A.device)
+    handle = s.cuda_stream if hasattr(s, "cuda_stream") else int(s)
+    st = gemm355_run_variant(variant, _dtype_code(A), M, N, K, A.data_ptr(), _ld(A),
+                             B.data_ptr(), _ld(B), out.data_ptr(), _ld(out), handle)
+    if st != OK:
+        raise Gemm355Error(st, "gemm355_run_variant")
+    return out

@@ -1,0 +1,132 @@
+"""The C ABI without a GPU: the library loads, exports every declared symbol, and
+rejects invalid arguments on the host before any HIP call."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from roofline_optimisation_amd import binding as gb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("gemm355.h", "gemm355_probe.h")]
+
+
+def declared_functions():
+    names = []
+    for h in HEADERS:
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\**\s*([A-Za-z_][A-Za-z0-9_]*)\s*\(",
+                             text, flags=re.M):
+            names.append(m.group(1))
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(gb.LIB_PATH):
+        pytest.fail("libgemm355.so is not built (run __graft_entry__.build())")
+    return gb.lib()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) >= 12
+    raw = ctypes.CDLL(gb.LIB_PATH)
+    for n in names:
+        assert hasattr(raw, n), f"{n} declared but not exported"
+    assert set(names) == set(gb.EXPORTS)
+
+
+def test_version_and_strings(lib):
+    assert gb.gemm355_version() == 100
+    assert gb.gemm355_status_string(0) == "ok"
+    assert gb.gemm355_status_string(1) == "invalid argument"
+    assert gb.gemm355_status_string(99) == "unknown"
+    assert [gb.gemm355_variant_name(v) for v in (-1, 0, 1, 2, 3, 7)] == \
+        ["auto", "naive", "lds_tiled", "regblock", "mfma", "unknown"]
+
+
+P = 1 << 20  # a fake, 16-byte aligned "device" address; never dereferenced
+
+
+@pytest.mark.parametrize("args", [
+    (-1, 4, 4, P, 4, P, 4, P, 4),        # negative M
+    (4, -1, 4, P, 4, P, 4, P, 4),        # negative N
+    (4, 4, -1, P, 4, P, 4, P, 4),        # negative K
+    (4, 4, 8, P, 7, P, 4, P, 4),         # lda < K
+    (4, 8, 4, P, 4, P, 7, P, 8),         # ldb < N
+    (4, 8, 4, P, 4, P, 8, P, 7),         # ldc < N
+    (4, 4, 4, 0, 4, P, 4, P, 4),         # null A
+    (4, 4, 4, P, 4, 0, 4, P, 4),         # null B
+    (4, 4, 4, P, 4, P, 4, 0, 4),         # null C
+    (4, 4, 0, P, 0, P, 4, P, 4),         # lda must be >= 1 even when K = 0
+])
+def test_invalid_arguments_rejected_on_host(lib, args):
+    for f in (gb.gemm_f32, gb.gemm_f16f32acc, gb.gemm_bf16f32acc):
+        assert f(*args, 0) == gb.ERR_INVALID_ARG
+    for v in (-1, 0, 3):
+        assert gb.gemm355_run_variant(v, 0, *args, 0) == gb.ERR_INVALID_ARG
+    assert gb.gemm355_select_variant(0, *args) == -1
+    assert gb.gemm355_kernel_desc(-1, 0, *args) == "invalid"
+
+
+def test_unknown_variant_and_dtype(lib):
+    args = (4, 4, 4, P, 4, P, 4, P, 4, 0)
+    assert gb.gemm355_run_variant(4, 0, *args) == gb.ERR_INVALID_ARG
+    assert gb.gemm355_run_variant(-2, 0, *args) == gb.ERR_INVALID_ARG
+    assert gb.gemm355_run_variant(0, 3, *args) == gb.ERR_INVALID_ARG
+    # FP32-only families reject 16-bit operands before touching the device
+    assert gb.gemm355_run_variant(gb.VARIANT_LDS_TILED, gb.F16, *args) == gb.ERR_UNSUPPORTED
+    assert gb.gemm355_run_variant(gb.VARIANT_REGBLOCK, gb.BF16, *args) == gb.ERR_UNSUPPORTED
+
+
+def test_degenerate_shapes_are_noops_without_device(lib):
+    # M = 0 or N = 0: nothing to do, OK even with null pointers and no GPU
+    assert gb.gemm_f32(0, 5, 5, 0, 5, P, 5, 0, 5, 0) == gb.OK
+    assert gb.gemm_f32(5, 0, 5, P, 5, 0, 1, 0, 1, 0) == gb.OK
+    assert gb.gemm_f16f32acc(0, 0, 0, 0, 1, 0, 1, 0, 1, 0) == gb.OK
+
+
+def test_dispatch_choices(lib):
+    d = lambda *a: gb.gemm355_kernel_desc(*a)
+    assert gb.gemm355_select_variant(0, 3072, 3072, 3072, P, 3072, P, 3072, P, 3072) == gb.VARIANT_MFMA
+    assert d(-1, 0, 3072, 3072, 3072, P, 3072, P, 3072, P, 3072).startswith("mfma_f32 192x192")
+    assert d(-1, 0, 4096, 4096, 4096, P, 4096, P, 4096, P, 4096).startswith("mfma_f32 128x128")
+    assert d(-1, 1, 4096, 4096, 4096, P, 4096, P, 4096, P, 4096).startswith("mfma_f16")
+    assert d(-1, 2, 4096, 4096, 4096, P, 4096, P, 4096, P, 4096).startswith("mfma_bf16")
+    # rows not 16-byte aligned (lda = 515 floats) take the dword load path
+    assert d(-1, 0, 1023, 997, 515, P, 515, P, 997, P, 997).endswith("dword")
+    assert d(-1, 0, 1000, 1000, 1000, P, 1000, P, 1000, P, 1000).endswith("dwordx4")
+    assert d(-1, 0, 1000, 1000, 1000, P + 4, 1000, P, 1000, P, 1000).endswith("dword")
+    assert d(0, 1, 8, 8, 8, P, 8, P, 8, P, 8).startswith("naive")
+    assert d(1, 0, 8, 8, 8, P, 8, P, 8, P, 8).startswith("lds_tiled")
+    assert d(2, 0, 8, 8, 8, P, 8, P, 8, P, 8).startswith("regblock")
+    assert d(1, 1, 8, 8, 8, P, 8, P, 8, P, 8) == "invalid"
+
+
+def test_no_device_reports_device_error(lib):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert gb.gemm_f32(4, 4, 4, P, 4, P, 4, P, 4, 0) == gb.ERR_DEVICE
+
+
+def test_probe_argument_checks(lib):
+    assert gb.gemm355_probe_mfma_shape(0) == (1, 16)
+    assert gb.gemm355_probe_mfma_shape(3) == (8, 4)
+    with pytest.raises(ValueError):
+        gb.gemm355_probe_mfma_shape(6)
+    assert gb.gemm355_probe_mfma(6, 1, P, P, P) == gb.ERR_INVALID_ARG
+    assert gb.gemm355_probe_mfma(0, 0, P, P, P) == gb.ERR_INVALID_ARG
+    assert gb.gemm355_probe_ds_read_tr16([8 * i for i in range(63)] + [4], P) == gb.ERR_INVALID_ARG
+    assert gb.gemm355_probe_ds_read_tr16([8 * i for i in range(63)] + [4096], P) == gb.ERR_INVALID_ARG
+
+
+def test_matmul_refuses_cpu_tensors(lib):
+    import torch
+    a = torch.zeros(4, 4)
+    with pytest.raises(ValueError):
+        gb.matmul(a, a)

@@ -1,0 +1,232 @@
+"""GPU parity: every kernel family, through the C ABI, against the CPU oracle.
+
+Bars: bit-exact on small-integer inputs (every partial sum is an exact integer below
+2^24); FP32 with U[-1,1] inputs: relative Frobenius error <= 1e-5 and max-abs error
+<= 1e-4 sqrt(K); FP32 with N(0,1) inputs: 1e-5 and 3e-4 sqrt(K); FP16/BF16 inputs,
+against the oracle on the same rounded inputs: relative Frobenius error <= 1e-3.
+Out-of-range reads are caught by NaN-poisoned padding and guard rows, out-of-range
+writes by a sentinel-filled C buffer.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import errors, gpu_gemm, sample_rows, tolerance
+from roofline_optimisation_amd import binding as gb
+from roofline_optimisation_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+F32_VARIANTS = [gb.VARIANT_NAIVE, gb.VARIANT_LDS_TILED, gb.VARIANT_REGBLOCK, gb.VARIANT_MFMA]
+H_VARIANTS = [gb.VARIANT_NAIVE, gb.VARIANT_MFMA]
+VNAME = {v: k for k, v in gb.VARIANTS.items()}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.init()
+
+
+def check(C, C64, dtype, dist, K, intact, what):
+    assert intact, f"{what}: wrote outside C"
+    assert not np.isnan(C).any(), f"{what}: NaN in result (read outside the operands?)"
+    rel, mx = errors(C, C64)
+    trel, tabs = tolerance(dtype, dist, K)
+    print(f"{what}: rel_frob={rel:.3e} max_abs={mx:.3e}", flush=True)
+    assert rel <= trel and mx <= tabs, f"{what}: rel {rel:.3e} (<= {trel}), max {mx:.3e} (<= {tabs})"
+
+
+def case_params():
+    out = []
+    for v in F32_VARIANTS:
+        out.append(("f32", v))
+    for v in H_VARIANTS:
+        out += [("f16", v), ("bf16", v)]
+    return out
+
+
+# ------------------------------------------------------------ the five workloads
+
+@pytest.mark.parametrize("variant", F32_VARIANTS, ids=lambda v: VNAME[v])
+def test_f32_256(variant):
+    c = inputs.CASES["f32_256"]
+    A, B = inputs.operands_for(c)
+    C64, _ = oracle.gemm(A, B)
+    C, ok = gpu_gemm(A, B, "f32", variant, pad=(3, 5, 7), guard_rows=2)
+    check(C, C64, "f32", c.dist, c.K, ok, f"f32_256 {VNAME[variant]}")
+
+
+@pytest.mark.parametrize("dtype,variant", case_params(), ids=lambda x: str(x))
+def test_small_integers_bit_exact(dtype, variant):
+    c = inputs.CASES["f32_256_int"]
+    A, B = inputs.make_operands(c.M, c.N, c.K, c.seed, "int", dtype)
+    _, C32 = oracle.gemm(A, B, dtype)
+    C, ok = gpu_gemm(A, B, dtype, variant)
+    assert ok and np.array_equal(C, C32), f"{dtype} {VNAME[variant]} not bit-exact"
+    # ragged integer case crossing every tile edge and the K tail
+    A, B = inputs.make_operands(211, 173, 333, 5, "int", dtype)
+    _, C32 = oracle.gemm(A, B, dtype)
+    C, ok = gpu_gemm(A, B, dtype, variant, pad=(1, 3, 2), offset=1, guard_rows=1)
+    assert ok and np.array_equal(C, C32), f"{dtype} {VNAME[variant]} ragged not bit-exact"
+
+
+@pytest.mark.parametrize("name", ["f32_1000", "f32_1023x997x515"])
+@pytest.mark.parametrize("variant", F32_VARIANTS, ids=lambda v: VNAME[v])
+def test_f32_ragged(name, variant):
+    c = inputs.CASES[name]
+    A, B = inputs.operands_for(c)
+    C64, _ = oracle.gemm(A, B)
+    C, ok = gpu_gemm(A, B, "f32", variant, guard_rows=1)
+    check(C, C64, "f32", c.dist, c.K, ok, f"{name} {VNAME[variant]}")
+
+
+def test_f32_3072_full():
+    """The bench's workload, in the bench's launch configuration (typed entry point,
+    packed strides), against the oracle on every element."""
+    c = inputs.CASES["f32_3072"]
+    A, B = inputs.operands_for(c)
+    C, ok = gpu_gemm(A, B, "f32", entry="typed")
+    C64, _ = oracle.gemm(A, B)
+    check(C, C64, "f32", c.dist, c.K, ok, "f32_3072 auto")
+
+
+@pytest.mark.parametrize("variant", [gb.VARIANT_LDS_TILED, gb.VARIANT_REGBLOCK],
+                         ids=lambda v: VNAME[v])
+def test_f32_3072_sampled(variant):
+    c = inputs.CASES["f32_3072"]
+    A, B = inputs.operands_for(c)
+    C, ok = gpu_gemm(A, B, "f32", variant)
+    rows = sample_rows(c.M, 96)
+    C64, _ = oracle.gemm(np.ascontiguousarray(A[rows]), B)
+    check(C[rows], C64, "f32", c.dist, c.K, ok, f"f32_3072 {VNAME[variant]} sampled")
+
+
+def test_f16_4096_sampled():
+    c = inputs.CASES["f16_4096"]
+    A, B = inputs.operands_for(c)
+    C, ok = gpu_gemm(A, B, "f16", entry="typed")
+    rows = sample_rows(c.M, 256)
+    C64, _ = oracle.gemm(np.ascontiguousarray(A[rows]), B, "f16")
+    check(C[rows], C64, "f16", c.dist, c.K, ok, "f16_4096 auto sampled")
+
+
+SWEEP_FULL = (128, 256, 512, 1024)
+SWEEP_SAMPLED = (2048, 4096, 8192)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("n", SWEEP_FULL + SWEEP_SAMPLED)
+def test_sweep(dtype, n):
+    A, B = inputs.make_operands(n, n, n, inputs.SWEEP_SEED, "uniform", dtype)
+    C, ok = gpu_gemm(A, B, dtype)
+    if n in SWEEP_FULL:
+        C64, _ = oracle.gemm(A, B, dtype)
+        check(C, C64, dtype, "uniform", n, ok, f"sweep {dtype} n={n}")
+    else:
+        rows = sample_rows(n, 64 if n < 8192 else 24)
+        C64, _ = oracle.gemm(np.ascontiguousarray(A[rows]), B, dtype)
+        check(C[rows], C64, dtype, "uniform", n, ok, f"sweep {dtype} n={n} sampled")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_tall_skinny(dtype):
+    A, B = inputs.make_operands(16384, 4096, 4096, inputs.SWEEP_SEED, "uniform", dtype)
+    C, ok = gpu_gemm(A, B, dtype)
+    rows = sample_rows(16384, 32)
+    C64, _ = oracle.gemm(np.ascontiguousarray(A[rows]), B, dtype)
+    check(C[rows], C64, dtype, "uniform", 4096, ok, f"tall-skinny {dtype} sampled")
+
+
+# ------------------------------------------------------------ edges and contract
+
+EDGE_SHAPES = [(1, 1, 1), (1, 77, 5), (77, 1, 5), (3, 5, 1), (33, 65, 17), (64, 64, 32),
+               (65, 63, 33), (191, 193, 37), (129, 257, 200), (200, 130, 1), (17, 300, 999)]
+
+
+@pytest.mark.parametrize("shape", EDGE_SHAPES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("dtype,variant", case_params(), ids=lambda x: str(x))
+def test_edge_shapes(shape, dtype, variant):
+    M, N, K = shape
+    A, B = inputs.make_operands(M, N, K, 21, "uniform", dtype)
+    C64, _ = oracle.gemm(A, B, dtype)
+    for pad, off in (((0, 0, 0), 0), ((5, 3, 1), 1), ((8, 8, 4), 0)):
+        C, ok = gpu_gemm(A, B, dtype, variant, pad=pad, offset=off, guard_rows=2)
+        check(C, C64, dtype, "uniform", K, ok, f"{shape} {dtype} {VNAME[variant]} pad={pad} off={off}")
+
+
+@pytest.mark.parametrize("dtype,variant", case_params(), ids=lambda x: str(x))
+def test_k_zero_writes_zero(dtype, variant):
+    A = np.zeros((37, 0), inputs.to_storage(np.zeros(1, np.float32), dtype).dtype)
+    B = np.zeros((0, 45), A.dtype)
+    C, ok = gpu_gemm(A, B, dtype, variant, pad=(1, 0, 3))
+    assert ok and np.all(C == 0) and not np.signbit(C).any()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_empty_m_or_n_is_noop(dtype):
+    A, B = inputs.make_operands(0, 8, 8, 1, "uniform", dtype)
+    C, ok = gpu_gemm(A, B, dtype, pad=(0, 0, 2))
+    assert ok and C.shape == (0, 8)
+    A, B = inputs.make_operands(8, 0, 8, 1, "uniform", dtype)
+    C, ok = gpu_gemm(A, B, dtype, pad=(0, 0, 2))
+    assert ok and C.shape == (8, 0)
+
+
+@pytest.mark.parametrize("dtype,variant", case_params(), ids=lambda x: str(x))
+def test_run_twice_bitwise(dtype, variant):
+    A, B = inputs.make_operands(515, 389, 777, 31, "normal", dtype)
+    C1, _ = gpu_gemm(A, B, dtype, variant)
+    C2, _ = gpu_gemm(A, B, dtype, variant)
+    assert np.array_equal(C1, C2)
+
+
+@pytest.mark.parametrize("name", ["f32_1000", "f32_1023x997x515"])
+def test_valu_families_agree_bitwise(name):
+    """naive, LDS-tiled and register-blocked kernels each sum an element by fmaf in
+    increasing k from +0.0, so they round identically."""
+    A, B = inputs.operands_for(inputs.CASES[name])
+    outs = [gpu_gemm(A, B, "f32", v)[0] for v in
+            (gb.VARIANT_NAIVE, gb.VARIANT_LDS_TILED, gb.VARIANT_REGBLOCK)]
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_typed_entry_matches_auto_variant(dtype):
+    A, B = inputs.make_operands(300, 260, 140, 8, "uniform", dtype)
+    C1, _ = gpu_gemm(A, B, dtype, gb.VARIANT_AUTO)
+    C2, _ = gpu_gemm(A, B, dtype, entry="typed")
+    assert np.array_equal(C1, C2)
+
+
+def test_non_default_stream():
+    import torch
+    s = torch.cuda.Stream()
+    A, B = inputs.make_operands(700, 600, 500, 9, "uniform", "f32")
+    C64, _ = oracle.gemm(A, B)
+    with torch.cuda.stream(s):
+        C, ok = gpu_gemm(A, B, "f32", stream=s)
+    check(C, C64, "f32", "uniform", 500, ok, "side stream")
+
+
+def test_invalid_args_with_device():
+    import torch
+    buf = torch.zeros(64, device="cuda")
+    p = buf.data_ptr()
+    assert gb.gemm_f32(4, 4, 8, p, 7, p, 4, p, 4, 0) == gb.ERR_INVALID_ARG
+    assert gb.gemm_f32(4, 4, 4, 0, 4, p, 4, p, 4, 0) == gb.ERR_INVALID_ARG
+    assert gb.gemm355_run_variant(gb.VARIANT_REGBLOCK, gb.F16, 4, 4, 4, p, 4, p, 4, p, 4, 0) \
+        == gb.ERR_UNSUPPORTED
+
+
+def test_torch_matmul_wrapper():
+    import torch
+    A, B = inputs.make_operands(129, 65, 33, 3, "uniform", "f32")
+    out = gb.matmul(torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda())
+    C64, _ = oracle.gemm(A, B)
+    check(out.cpu().numpy(), C64, "f32", "uniform", 33, True, "matmul wrapper")
