@@ -130,6 +130,9 @@ def main():
     ap.add_argument("--only", choices=["f32", "f16"], default=None,
                     help="measure one workload only (for profiler runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="after the GEMMs, copy this many MiB device-to-device once (a plain "
+                         "copy of known size, used to scale the HBM byte counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -157,6 +160,15 @@ def main():
         results[kind] = r
         log(f"[bench] {kind} {n}^3 {r['desc']}: {r['ms']:.4f} ms/launch, {tf:.1f} TFLOP/s "
             f"({100 * tf / PEAKS[kind]:.1f}% of {PEAKS[kind]})")
+
+    if args.calib_copy_mib:
+        nel = args.calib_copy_mib * (1 << 20) // 4
+        src = torch.ones(nel, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy of {args.calib_copy_mib} MiB done")
 
     def roof(kind, n):
         r = results[kind]

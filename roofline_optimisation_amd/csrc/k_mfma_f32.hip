@@ -50,10 +50,12 @@ struct F32Cfg {
     static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 };
 
-template <bool VEC>
+// Columns [c, c+4) of one row.  EDGE: zero outside [0, ncols) and for invalid rows;
+// otherwise the caller guarantees the chunk is inside the matrix.
+template <bool VEC, bool EDGE>
 __device__ __forceinline__ floatx4 ld_chunk(const float *__restrict__ row, int c, int ncols,
-                                            bool row_ok, bool full) {
-    if (full) {
+                                            bool row_ok) {
+    if (!EDGE) {
         if (VEC) return *reinterpret_cast<const floatx4 *>(row + c);
         return floatx4{row[c], row[c + 1], row[c + 2], row[c + 3]};
     }
@@ -66,22 +68,18 @@ __device__ __forceinline__ floatx4 ld_chunk(const float *__restrict__ row, int c
     return v;
 }
 
-template <int BM, int BN, int WM, int WN, int MINW, bool VEC>
-__global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(MINW)))
-void mfma_f32_gemm_kernel(
-    int M, int N, int K, const float *__restrict__ A, int lda, const float *__restrict__ B,
-    int ldb, float *__restrict__ C, int ldc) {
+// One BM x BN tile of C.  EDGE selects the predicated loads and guarded stores; the
+// interior instance (tile inside M x N, K a multiple of BK) is straight-line code, so
+// the dwordx4 loads of a k-step issue back to back.
+template <int BM, int BN, int WM, int WN, bool VEC, bool EDGE>
+__device__ __forceinline__ void f32_tile(int M, int N, int K, const float *__restrict__ A, int lda,
+                                         const float *__restrict__ B, int ldb,
+                                         float *__restrict__ C, int ldc, int m0, int n0,
+                                         float *lds) {
     using Cfg = F32Cfg<BM, BN, WM, WN>;
     constexpr int T = Cfg::kThreads;
     constexpr int MB = Cfg::kMB, NB = Cfg::kNB;
     constexpr int SB = Cfg::kSB;
-    __shared__ __attribute__((aligned(16))) float lds[2 * (Cfg::kLdsA + Cfg::kLdsB)];
-
-    const int tiles_m = cdiv(M, BM), tiles_n = cdiv(N, BN);
-    int tm, tn;
-    grouped_tile(xcd_contiguous_id(blockIdx.x, tiles_m * tiles_n), tiles_m, tiles_n, 4, tm, tn);
-    const int m0 = tm * BM, n0 = tn * BN;
-    const bool tile_full = (m0 + BM <= M) && (n0 + BN <= N);
 
     const int t = threadIdx.x;
     const int lane = t % 64, wave = t / 64;
@@ -106,18 +104,17 @@ void mfma_f32_gemm_kernel(
 
     floatx4 sa[Cfg::kAChunks], sb[Cfg::kBChunks];
     auto load_tile = [&](int k0) {
-        const bool full = tile_full && (k0 + kBK <= K);
 #pragma unroll
         for (int i = 0; i < Cfg::kAChunks; ++i) {
             const int r = m0 + a_r[i];
-            const bool ok = r < M;
-            sa[i] = ld_chunk<VEC>(A + (size_t)(ok ? r : 0) * lda, k0 + a_c[i], K, ok, full);
+            const bool ok = !EDGE || r < M;
+            sa[i] = ld_chunk<VEC, EDGE>(A + (size_t)(ok ? r : 0) * lda, k0 + a_c[i], K, ok);
         }
 #pragma unroll
         for (int i = 0; i < Cfg::kBChunks; ++i) {
             const int r = k0 + b_r[i];
-            const bool ok = r < K;
-            sb[i] = ld_chunk<VEC>(B + (size_t)(ok ? r : 0) * ldb, n0 + b_c[i], N, ok, full);
+            const bool ok = !EDGE || r < K;
+            sb[i] = ld_chunk<VEC, EDGE>(B + (size_t)(ok ? r : 0) * ldb, n0 + b_c[i], N, ok);
         }
     };
     auto store_tile = [&](int buf) {
@@ -188,10 +185,45 @@ void mfma_f32_gemm_kernel(
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int row = m0 + wm * Cfg::kTM + 32 * i + 8 * (r / 4) + 4 * lhi + (r % 4);
-                if (tile_full || (row < M && col < N)) C[(size_t)row * ldc + col] = acc[i][j][r];
+                if (!EDGE || (row < M && col < N)) C[(size_t)row * ldc + col] = acc[i][j][r];
             }
         }
     }
+}
+
+// Tile coordinates of workgroup `bid`.  Interior launches (EDGE false) cover the
+// tiles_m_full x tiles_n_full tiles that lie inside M x N, in XCD-contiguous grouped
+// order.  Edge launches cover either every tile (all_tiles: K is not a multiple of BK)
+// or only the ragged right column strip followed by the ragged bottom row strip.
+template <bool EDGE>
+__device__ __forceinline__ void tile_of(int bid, int nblocks, int tiles_m, int tiles_n,
+                                        bool ragged_n, bool all_tiles, int &tm, int &tn) {
+    if (!EDGE || all_tiles) {
+        grouped_tile(xcd_contiguous_id(bid, nblocks), tiles_m, tiles_n, 4, tm, tn);
+        return;
+    }
+    const int right = ragged_n ? tiles_m : 0;
+    if (bid < right) {
+        tm = bid;
+        tn = tiles_n - 1;
+    } else {
+        tm = tiles_m - 1;
+        tn = bid - right;
+    }
+}
+
+template <int BM, int BN, int WM, int WN, int MINW, bool VEC, bool EDGE>
+__global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(MINW)))
+void mfma_f32_gemm_kernel(int M, int N, int K, const float *__restrict__ A, int lda,
+                          const float *__restrict__ B, int ldb, float *__restrict__ C, int ldc,
+                          int all_tiles) {
+    using Cfg = F32Cfg<BM, BN, WM, WN>;
+    __shared__ __attribute__((aligned(16))) float lds[2 * (Cfg::kLdsA + Cfg::kLdsB)];
+    const int tiles_m = EDGE ? cdiv(M, BM) : M / BM;
+    const int tiles_n = EDGE ? cdiv(N, BN) : N / BN;
+    int tm, tn;
+    tile_of<EDGE>(blockIdx.x, gridDim.x, tiles_m, tiles_n, N % BN != 0, all_tiles != 0, tm, tn);
+    f32_tile<BM, BN, WM, WN, VEC, EDGE>(M, N, K, A, lda, B, ldb, C, ldc, tm * BM, tn * BN, lds);
 }
 
 struct F32Pick {
@@ -222,20 +254,41 @@ F32Pick pick_f32(const GemmArgs &g) {
 }
 
 // MINW: waves per SIMD the register budget must allow (resident workgroups per CU
-// times waves per workgroup / 4).
+// times waves per workgroup / 4).  Full interior tiles go to the straight-line kernel;
+// ragged strips (or every tile, when K is not a multiple of BK) to the predicated one.
 template <int BM, int BN, int WM, int WN, int MINW>
 hipError_t launch_cfg(const GemmArgs &g, bool vec, hipStream_t s) {
-    const dim3 grid(cdiv(g.M, BM) * cdiv(g.N, BN));
     const dim3 block(64 * WM * WN);
-    if (vec)
-        hipLaunchKernelGGL((mfma_f32_gemm_kernel<BM, BN, WM, WN, MINW, true>), grid, block, 0, s, g.M,
-                           g.N, g.K, (const float *)g.A, g.lda, (const float *)g.B, g.ldb, g.C,
-                           g.ldc);
-    else
-        hipLaunchKernelGGL((mfma_f32_gemm_kernel<BM, BN, WM, WN, MINW, false>), grid, block, 0, s, g.M,
-                           g.N, g.K, (const float *)g.A, g.lda, (const float *)g.B, g.ldb, g.C,
-                           g.ldc);
-    return hipGetLastError();
+    const bool kfull = g.K % kBK == 0;
+    const int full_tiles = kfull ? (g.M / BM) * (g.N / BN) : 0;
+    const int all = cdiv(g.M, BM) * cdiv(g.N, BN);
+    const int edge_tiles = all - full_tiles;
+    const int all_flag = kfull ? 0 : 1;
+    const float *A = (const float *)g.A, *B = (const float *)g.B;
+    if (full_tiles > 0) {
+        if (vec)
+            hipLaunchKernelGGL((mfma_f32_gemm_kernel<BM, BN, WM, WN, MINW, true, false>),
+                               dim3(full_tiles), block, 0, s, g.M, g.N, g.K, A, g.lda, B, g.ldb,
+                               g.C, g.ldc, all_flag);
+        else
+            hipLaunchKernelGGL((mfma_f32_gemm_kernel<BM, BN, WM, WN, MINW, false, false>),
+                               dim3(full_tiles), block, 0, s, g.M, g.N, g.K, A, g.lda, B, g.ldb,
+                               g.C, g.ldc, all_flag);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (edge_tiles > 0) {
+        if (vec)
+            hipLaunchKernelGGL((mfma_f32_gemm_kernel<BM, BN, WM, WN, MINW, true, true>),
+                               dim3(edge_tiles), block, 0, s, g.M, g.N, g.K, A, g.lda, B, g.ldb,
+                               g.C, g.ldc, all_flag);
+        else
+            hipLaunchKernelGGL((mfma_f32_gemm_kernel<BM, BN, WM, WN, MINW, false, true>),
+                               dim3(edge_tiles), block, 0, s, g.M, g.N, g.K, A, g.lda, B, g.ldb,
+                               g.C, g.ldc, all_flag);
+        return hipGetLastError();
+    }
+    return hipSuccess;
 }
 
 }  // namespace
