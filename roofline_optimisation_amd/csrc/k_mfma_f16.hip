@@ -1,21 +1,29 @@
 // FP16 / BF16 GEMM with FP32 accumulation on the gfx950 matrix cores
 // (v_mfma_f32_32x32x16_f16 / _bf16): the AMD counterpart of the tensor-core level of
 // "Kernel optimisation guide" (Level 4: 16-bit A and B fragments, FP32 accumulator
-// fragments, a matrix multiply-accumulate per fragment step) and of the tensor-core
+// fragments, one matrix multiply-accumulate per fragment step) and of the tensor-core
 // section of "Advanced CUDA features - starting from GEMM" (a wave-cooperative
-// D = A.B + C unit whose register layout has to be matched by the data movement).
+// D = A.B + C unit whose register layout the data movement has to match).
 //
 // Structure:
-//  * a workgroup of 2 x 2 waves owns a 128 x 128 tile of C and walks K in steps of
-//    BK = 32 with two LDS stages (dwordx4 loads of step t+1 in flight while step t is
-//    multiplied; one barrier per step);
-//  * each wave owns 64 x 64 of C as 2 x 2 blocks of 32 x 32 FP32 accumulators;
-//  * A fragment: lane l holds 8 consecutive k of row l%32, read with one ds_read_b128
-//    from A kept [m][k] in LDS with the 16-byte chunks of each row XOR-swizzled by
-//    (m/2) mod 4, so the eight lanes of one LDS cycle hit eight distinct bank groups;
-//  * B fragment: lane l needs the same 8 k of column l%32; B is kept [k][n] (as loaded)
-//    and the fragment is gathered with 16-bit LDS reads;
-//  * edges: per-element predicates with zero fill on tiles crossing M, N or the K tail.
+//  * a workgroup of WM x WN waves owns a BM x BN tile of C and walks K in steps of
+//    BK = 64 with two LDS stages: the dwordx4 loads of step t+1 are in flight while
+//    step t is multiplied, then written to the other stage before the one barrier of
+//    the step (the double buffer of "Kernel optimisation guide", Level 3);
+//  * each wave owns (BM/WM) x (BN/WN) of C as 32 x 32 FP32 accumulator blocks;
+//  * A fragment (row l%32 of a block, k = 8(l/32) .. +7 of a 16-wide k step): one
+//    ds_read_b128 from A kept [m][k] in LDS with rows padded to 144 bytes, so the 32
+//    rows one instruction touches fall on distinct bank groups;
+//  * B fragment (column l%32, the same 8 k): B stays [k][n] in LDS as loaded, rows
+//    padded to 2*BN + 64 bytes, and two ds_read_b64_tr_b16 per fragment transpose it on
+//    the way out.  Within each 16-lane group that instruction hands output lane j, as
+//    its element e, halfword j%4 of the 8 bytes read by source lane 4e + (j%16)/4; so
+//    source lane 4e + q addresses row k+e, columns n + 4q .. n + 4q + 3, and output lane
+//    j receives column n + j%16 for rows k .. k+3;
+//  * interior tiles (inside M x N, K a multiple of BK) run a straight-line kernel; the
+//    ragged strips run a predicated one that zero-fills loads and guards stores.
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -23,12 +31,24 @@ namespace g355 {
 
 namespace {
 
-constexpr int kBM = 128, kBN = 128, kBK = 32, kThreads = 256;
-constexpr int kSB = kBN + 8;              // B LDS row stride (halves), 16-byte multiple
-constexpr int kLdsA = kBM * kBK;          // halves per stage
-constexpr int kLdsB = kBK * kSB;
-constexpr int kAChunks = kBM * kBK / 8 / kThreads;  // 16-byte chunks per thread
-constexpr int kBChunks = kBK * kBN / 8 / kThreads;
+constexpr int kBK = 64;
+constexpr int kSA = kBK + 8;  // A LDS row stride in halves (144 bytes)
+
+template <int BM, int BN, int WM, int WN>
+struct H16Cfg {
+    static constexpr int kThreads = 64 * WM * WN;
+    static constexpr int kTM = BM / WM, kTN = BN / WN;
+    static constexpr int kMB = kTM / 32, kNB = kTN / 32;
+    static constexpr int kSB = BN + 32;  // B LDS row stride in halves
+    static constexpr int kLdsA = BM * kSA, kLdsB = kBK * kSB;  // halves per stage
+    static constexpr int kAChunks = BM * kBK / 8 / kThreads;   // 16-byte chunks/thread
+    static constexpr int kBChunks = kBK * BN / 8 / kThreads;
+    static constexpr int kLdsBytes = 2 * (kLdsA + kLdsB) * 2;
+    static_assert(kTM % 32 == 0 && kTN % 32 == 0, "wave tile must be whole 32x32 blocks");
+    static_assert((BM * kBK / 8) % kThreads == 0 && (kBK * BN / 8) % kThreads == 0,
+                  "tile chunks must divide over the threads");
+    static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
+};
 
 template <typename T>
 __device__ __forceinline__ floatx16 mfma32x32x16(u16x8 a, u16x8 b, floatx16 c);
@@ -43,163 +63,358 @@ __device__ __forceinline__ floatx16 mfma32x32x16<bf16_t>(u16x8 a, u16x8 b, float
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-// Columns [c, c+8) of one row, zero outside [0, ncols) and for invalid rows.
-template <bool VEC>
+typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
+
+__device__ __forceinline__ shortx4 ds_read_tr16(const uint16_t *p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_shortx4 *)(__attribute__((address_space(3))) void *)(p));
+}
+
+// Columns [c, c+8) of one row.  EDGE: zero outside [0, ncols) and for invalid rows;
+// otherwise the chunk is known to be inside the matrix.
+template <bool VEC, bool EDGE>
 __device__ __forceinline__ u16x8 ld_chunk8(const uint16_t *__restrict__ row, int c, int ncols,
-                                           bool row_ok, bool full) {
-    if (full && VEC) return *reinterpret_cast<const u16x8 *>(row + c);
+                                           bool row_ok) {
+    if (!EDGE && VEC) return *reinterpret_cast<const u16x8 *>(row + c);
     u16x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (!row_ok) return v;
-    if (VEC && c + 8 <= ncols) return *reinterpret_cast<const u16x8 *>(row + c);
+    if (EDGE && !row_ok) return v;
+    if (EDGE && VEC && c + 8 <= ncols) return *reinterpret_cast<const u16x8 *>(row + c);
 #pragma unroll
     for (int e = 0; e < 8; ++e)
-        if (full || c + e < ncols) v[e] = row[c + e];
+        if (!EDGE || c + e < ncols) v[e] = row[c + e];
     return v;
 }
 
-__device__ __forceinline__ int swz_a(int m, int chunk) { return chunk ^ ((m >> 1) & 3); }
-
-template <typename T, bool VEC>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
-void mfma_f16_gemm_kernel(int M, int N, int K, const uint16_t *__restrict__ A, int lda,
-                          const uint16_t *__restrict__ B, int ldb, float *__restrict__ C,
-                          int ldc) {
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * (kLdsA + kLdsB)];
-
-    const int tiles_m = cdiv(M, kBM), tiles_n = cdiv(N, kBN);
-    int tm, tn;
-    grouped_tile(xcd_contiguous_id(blockIdx.x, tiles_m * tiles_n), tiles_m, tiles_n, 4, tm, tn);
-    const int m0 = tm * kBM, n0 = tn * kBN;
-    const bool tile_full = (m0 + kBM <= M) && (n0 + kBN <= N);
+// LOAD: 0 = 16-bit loads (rows not 16-byte aligned), 1 = dwordx4 through pointers,
+// 2 = dwordx4 through buffer resources (interior tiles, offsets below 2^31 bytes).
+template <typename T, int BM, int BN, int WM, int WN, int LOAD, bool EDGE, bool PAIRED>
+__device__ __forceinline__ void h16_tile(int M, int N, int K, const uint16_t *__restrict__ A,
+                                         int lda, const uint16_t *__restrict__ B, int ldb,
+                                         float *__restrict__ C, int ldc, int m0, int n0,
+                                         uint16_t *lds) {
+    using Cfg = H16Cfg<BM, BN, WM, WN>;
+    constexpr int TT = Cfg::kThreads;
+    constexpr int MB = Cfg::kMB, NB = Cfg::kNB;
+    constexpr int SB = Cfg::kSB;
+    constexpr int kAC = Cfg::kAChunks, kBC = Cfg::kBChunks;
+    // Chunk i of a thread: A row t/8 + (TT/8) i, k offset 8 (t%8); B row t/(BN/8) +
+    // (TT/(BN/8)) i, column 8 (t % (BN/8)).
+    constexpr int kARowStep = TT / (kBK / 8), kBRowStep = TT / (BN / 8);
 
     const int t = threadIdx.x;
     const int lane = t % 64, wave = t / 64;
-    const int wm = wave / 2, wn = wave % 2;
+    const int wm = wave / WN, wn = wave % WN;
     const int l32 = lane % 32, lhi = lane / 32;
+    const int a_r0 = t / (kBK / 8), a_c0 = (t % (kBK / 8)) * 8;
+    const int b_r0 = t / (BN / 8), b_c0 = (t % (BN / 8)) * 8;
 
-    int a_r[kAChunks], a_c[kAChunks], b_r[kBChunks], b_c[kBChunks];
-#pragma unroll
-    for (int i = 0; i < kAChunks; ++i) {
-        const int q = t + kThreads * i;
-        a_r[i] = q / (kBK / 8);
-        a_c[i] = q % (kBK / 8);
-    }
-#pragma unroll
-    for (int i = 0; i < kBChunks; ++i) {
-        const int q = t + kThreads * i;
-        b_r[i] = q / (kBN / 8);
-        b_c[i] = q % (kBN / 8);
-    }
+    // Interior tiles read through buffer resources based at the tile's first row (A) and
+    // first column (B): one VGPR offset per operand, the chunk and k-step parts in SGPRs.
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(A + (size_t)m0 * lda), (short)0, 0x7fffffff, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(B + n0), (short)0, 0x7fffffff, 0x00020000);
+    const int va = (a_r0 * lda + a_c0) * 2, vb = (b_r0 * ldb + b_c0) * 2;
 
-    u16x8 sa[kAChunks], sb[kBChunks];
-    auto load_tile = [&](int k0) {
-        const bool full = tile_full && (k0 + kBK <= K);
-#pragma unroll
-        for (int i = 0; i < kAChunks; ++i) {
-            const int r = m0 + a_r[i];
-            const bool ok = r < M;
-            sa[i] = ld_chunk8<VEC>(A + (size_t)(ok ? r : 0) * lda, k0 + 8 * a_c[i], K, ok, full);
-        }
-#pragma unroll
-        for (int i = 0; i < kBChunks; ++i) {
-            const int r = k0 + b_r[i];
-            const bool ok = r < K;
-            sb[i] = ld_chunk8<VEC>(B + (size_t)(ok ? r : 0) * ldb, n0 + 8 * b_c[i], N, ok, full);
+    // Two staging register sets: the loads of k-step t+3 are issued while step t is
+    // multiplied and written to LDS two steps later.
+    u16x8 sa[2][kAC], sb[2][kBC];
+    // Global -> register staging, one 16-byte chunk per call (chunk w < kAC is A's,
+    // the rest B's).
+    auto load_one = [&](auto set_c, int k0, int w) {
+        constexpr int S = decltype(set_c)::value;
+        if constexpr (LOAD == 2) {
+            if (w < kAC)
+                sa[S][w] = __builtin_bit_cast(
+                    u16x8, __builtin_amdgcn_raw_buffer_load_b128(ra, va, (w * kARowStep * lda + k0) * 2, 0));
+            else
+                sb[S][w - kAC] = __builtin_bit_cast(
+                    u16x8, __builtin_amdgcn_raw_buffer_load_b128(rb, vb, (k0 + (w - kAC) * kBRowStep) * ldb * 2, 0));
+        } else {
+            if (w < kAC) {
+                const int r = m0 + a_r0 + w * kARowStep;
+                const bool ok = !EDGE || r < M;
+                sa[S][w] = ld_chunk8<LOAD == 1, EDGE>(A + (size_t)(ok ? r : 0) * lda, k0 + a_c0, K, ok);
+            } else {
+                const int r = k0 + b_r0 + (w - kAC) * kBRowStep;
+                const bool ok = !EDGE || r < K;
+                sb[S][w - kAC] = ld_chunk8<LOAD == 1, EDGE>(B + (size_t)(ok ? r : 0) * ldb, n0 + b_c0, N, ok);
+            }
         }
     };
-    auto store_tile = [&](int buf) {
-        uint16_t *As = lds + buf * (kLdsA + kLdsB);
-        uint16_t *Bs = As + kLdsA;
-#pragma unroll
-        for (int i = 0; i < kAChunks; ++i)
-            *reinterpret_cast<u16x8 *>(As + a_r[i] * kBK + 8 * swz_a(a_r[i], a_c[i])) = sa[i];
-#pragma unroll
-        for (int i = 0; i < kBChunks; ++i)
-            *reinterpret_cast<u16x8 *>(Bs + b_r[i] * kSB + 8 * b_c[i]) = sb[i];
+    auto store_one = [&](auto set_c, int buf, int w) {
+        constexpr int S = decltype(set_c)::value;
+        uint16_t *As = lds + buf * (Cfg::kLdsA + Cfg::kLdsB);
+        uint16_t *Bs = As + Cfg::kLdsA;
+        if (w < kAC)
+            *reinterpret_cast<u16x8 *>(As + (a_r0 + w * kARowStep) * kSA + a_c0) = sa[S][w];
+        else
+            *reinterpret_cast<u16x8 *>(Bs + (b_r0 + (w - kAC) * kBRowStep) * SB + b_c0) =
+                sb[S][w - kAC];
     };
 
-    floatx16 acc[2][2];
+    floatx16 acc[MB][NB];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < MB; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < NB; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    const int nk = cdiv(K, kBK);
-    if (nk > 0) {
-        load_tile(0);
-        store_tile(0);
-    }
-    __syncthreads();
-
-    const int a_row0 = wm * 64 + l32;
-    const int b_col0 = wn * 64 + l32;
-    for (int kt = 0; kt < nk; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < nk) load_tile((kt + 1) * kBK);
-        const uint16_t *As = lds + buf * (kLdsA + kLdsB);
-        const uint16_t *Bs = As + kLdsA;
-#pragma unroll
-        for (int s = 0; s < kBK / 16; ++s) {
-            u16x8 af[2], bf[2];
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int m = a_row0 + 32 * i;
-                af[i] = *reinterpret_cast<const u16x8 *>(As + m * kBK + 8 * swz_a(m, 2 * s + lhi));
-            }
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    bf[j][e] = Bs[(16 * s + 8 * lhi + e) * kSB + b_col0 + 32 * j];
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16<T>(af[i], bf[j], acc[i][j]);
+    // Per-lane fragment offsets within a stage.
+    const int a_off = (wm * Cfg::kTM + l32) * kSA + 8 * lhi;  // + 32 i rows, + 16 s
+    const int g16 = lane / 16, s16 = lane % 16;
+    const int b_off = (8 * (g16 / 2) + s16 / 4) * SB + wn * Cfg::kTN + 16 * (g16 % 2) +
+                      4 * (s16 % 4);  // + 16 s rows, + 4 r rows, + 32 j columns
+    constexpr int kSteps = kBK / 16;
+    constexpr int kR = MB + 2 * NB;  // fragment reads per sub-step
+    u16x8 af[2][MB];
+    shortx4 bt[2][NB][2];
+    // Fragment read `p` of sub-step s into slot: p < MB is A block p (one ds_read_b128),
+    // the others are the two ds_read_b64_tr_b16 halves of B block (p - MB) / 2.
+    auto read_piece = [&](int buf, int s, int slot, int p) {
+        const uint16_t *As = lds + buf * (Cfg::kLdsA + Cfg::kLdsB);
+        const uint16_t *Bs = As + Cfg::kLdsA;
+        if (p < MB) {
+            af[slot][p] = *reinterpret_cast<const u16x8 *>(As + a_off + 32 * p * kSA + 16 * s);
+        } else {
+            const int j = (p - MB) / 2, h = (p - MB) % 2;
+            bt[slot][j][h] = ds_read_tr16(Bs + b_off + 16 * s * SB + 32 * j + 4 * h * SB);
         }
-        if (kt + 1 < nk) store_tile(buf ^ 1);
+    };
+    auto mfma_one = [&](int slot, int q) {
+        const int i = q / NB, j = q % NB;
+        const u16x8 b = __builtin_bit_cast(
+            u16x8, __builtin_shufflevector(bt[slot][j][0], bt[slot][j][1], 0, 1, 2, 3, 4, 5, 6, 7));
+        acc[i][j] = mfma32x32x16<T>(af[slot][i], b, acc[i][j]);
+    };
+    constexpr int kMf = MB * NB;                  // MFMAs per sub-step
+    constexpr int kPre = (kMf * 5 + 7) / 8;       // of those, issued before the barrier
+    constexpr int kWr = kAC + kBC;                // staged chunks per k-step
+    constexpr int kRdSlots = (kR + 1) / 2;        // reads go two per MFMA, first
+
+    // One k-step t on stage buf.  Every memory instruction is issued between MFMAs so
+    // that no burst blocks the in-order issue of the MFMAs behind it:
+    //  * sub-steps s < last: after MFMA q, fragment reads 2q, 2q+1 of sub-step s+1 (slot
+    //    (s+1) % 2); then, paired variant only, the global loads of k-step t+2 into the
+    //    free staging set O, spread one per MFMA over the remaining slots;
+    //  * last sub-step: the staged k-step t+1 (set S) is written to the idle stage
+    //    between the first kPre MFMAs; barrier; then the fragments of t+1's first
+    //    sub-step (and, unpaired variant, the loads of t+2 into S) between the rest.
+    // The body has no branches (a branch makes the compiler wait for every outstanding
+    // LDS read at the join): near the end the loads re-read the last k-step and the idle
+    // stage takes dummies.
+    const int nk = cdiv(K, kBK);
+    auto kstep = [&](auto set_c, auto other_c, int kt, int buf) {
+        const int kload = min(kt + 2, nk - 1) * kBK;
+#pragma unroll
+        for (int s = 0; s < kSteps - 1; ++s) {
+            constexpr int nl_all = PAIRED ? kWr : 0;
+            const int l_lo = s * nl_all / (kSteps - 1), l_hi = (s + 1) * nl_all / (kSteps - 1);
+#pragma unroll
+            for (int q = 0; q < kMf; ++q) {
+                mfma_one(s & 1, q);
+#pragma unroll
+                for (int p = 2 * q; p < 2 * q + 2; ++p)
+                    if (p < kR) read_piece(buf, s + 1, (s + 1) & 1, p);
+                if constexpr (PAIRED) {
+                    // loads l_lo .. l_hi-1 over slots kRdSlots .. kMf-1
+                    constexpr int slots = kMf - kRdSlots > 0 ? kMf - kRdSlots : 1;
+                    const int qs = q - kRdSlots < 0 ? -1 : q - kRdSlots;
+                    const int n = l_hi - l_lo;
+                    if (qs >= 0) {
+                        const int o_lo = qs * n / slots, o_hi = qs + 1 == slots ? n : (qs + 1) * n / slots;
+                        for (int o = o_lo; o < o_hi; ++o) load_one(other_c, kload, l_lo + o);
+                    } else if (kMf - kRdSlots <= 0 && q == kMf - 1) {
+                        for (int o = 0; o < n; ++o) load_one(other_c, kload, l_lo + o);
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        constexpr int sl = (kSteps - 1) & 1;
+#pragma unroll
+        for (int q = 0; q < kPre; ++q) {
+            mfma_one(sl, q);
+#pragma unroll
+            for (int w = q * kWr / kPre; w < (q + 1) * kWr / kPre; ++w) store_one(set_c, buf ^ 1, w);
+            __builtin_amdgcn_sched_barrier(0);
+        }
         __syncthreads();
+        constexpr int kPost = kMf - kPre;
+        constexpr int nops = kR + (PAIRED ? 0 : kWr);
+#pragma unroll
+        for (int q = kPre; q < kMf; ++q) {
+            const int qq = q - kPre;
+            const int o_lo = qq * nops / kPost, o_hi = (qq + 1) * nops / kPost;
+#pragma unroll
+            for (int o = o_lo; o < o_hi; ++o) {
+                if (o < kR) read_piece(buf ^ 1, 0, 0, o);
+                else load_one(set_c, kload, o - kR);
+            }
+            mfma_one(sl, q);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    if (nk > 0) {
+#pragma unroll
+        for (int w = 0; w < kWr; ++w) load_one(S0{}, 0, w);
+#pragma unroll
+        for (int w = 0; w < kWr; ++w) store_one(S0{}, 0, w);
+        __syncthreads();
+#pragma unroll
+        for (int w = 0; w < kWr; ++w) load_one(S1{}, min(1, nk - 1) * kBK, w);
+#pragma unroll
+        for (int p = 0; p < kR; ++p) read_piece(0, 0, 0, p);
+        if constexpr (PAIRED) {
+            // nk is even: k-steps in pairs, staging sets alternating statically
+            for (int kt = 0; kt < nk; kt += 2) {
+                kstep(S1{}, S0{}, kt, 0);      // loads kt+2 into set 0, stores kt+1 (set 1)
+                kstep(S0{}, S1{}, kt + 1, 1);  // loads kt+3 into set 1, stores kt+2 (set 0)
+            }
+        } else {
+            // any nk: one staging set, loads issued one k-step ahead
+            for (int kt = 0; kt < nk; ++kt) kstep(S1{}, S1{}, kt, kt & 1);
+        }
     }
 
+    // 32x32 accumulator layout: register r of lane l holds row 8(r/4) + 4(l/32) + r%4,
+    // column l%32 of the block.
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < MB; ++i) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int col = n0 + b_col0 + 32 * j;
+        for (int j = 0; j < NB; ++j) {
+            const int col = n0 + wn * Cfg::kTN + 32 * j + l32;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int row = m0 + wm * 64 + 32 * i + 8 * (r / 4) + 4 * lhi + (r % 4);
-                if (tile_full || (row < M && col < N)) C[(size_t)row * ldc + col] = acc[i][j][r];
+                const int row = m0 + wm * Cfg::kTM + 32 * i + 8 * (r / 4) + 4 * lhi + (r % 4);
+                if (!EDGE || (row < M && col < N)) C[(size_t)row * ldc + col] = acc[i][j][r];
             }
         }
     }
 }
 
-bool f16_vec(const GemmArgs &g) {
+// Same tile-numbering scheme as the FP32 kernel: interior launches walk the full tiles
+// in XCD-contiguous grouped order; edge launches take the ragged right strip, then the
+// ragged bottom strip (or every tile when K is ragged).
+template <bool EDGE>
+__device__ __forceinline__ void h16_tile_of(int bid, int nblocks, int tiles_m, int tiles_n,
+                                            bool ragged_n, bool all_tiles, int &tm, int &tn) {
+    if (!EDGE || all_tiles) {
+        grouped_tile(xcd_contiguous_id(bid, nblocks), tiles_m, tiles_n, 4, tm, tn);
+        return;
+    }
+    const int right = ragged_n ? tiles_m : 0;
+    if (bid < right) {
+        tm = bid;
+        tn = tiles_n - 1;
+    } else {
+        tm = tiles_m - 1;
+        tn = bid - right;
+    }
+}
+
+template <typename T, int BM, int BN, int WM, int WN, int MINW, int LOAD, bool EDGE, bool PAIRED>
+__global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(MINW)))
+void mfma_f16_gemm_kernel(int M, int N, int K, const uint16_t *__restrict__ A, int lda,
+                          const uint16_t *__restrict__ B, int ldb, float *__restrict__ C, int ldc,
+                          int all_tiles) {
+    using Cfg = H16Cfg<BM, BN, WM, WN>;
+    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * (Cfg::kLdsA + Cfg::kLdsB)];
+    const int tiles_m = EDGE ? cdiv(M, BM) : M / BM;
+    const int tiles_n = EDGE ? cdiv(N, BN) : N / BN;
+    int tm, tn;
+    h16_tile_of<EDGE>(blockIdx.x, gridDim.x, tiles_m, tiles_n, N % BN != 0, all_tiles != 0, tm, tn);
+    h16_tile<T, BM, BN, WM, WN, LOAD, EDGE, PAIRED>(M, N, K, A, lda, B, ldb, C, ldc, tm * BM,
+                                                   tn * BN, lds);
+}
+
+bool h16_vec(const GemmArgs &g) {
     return rows_aligned16(g.A, g.lda, 2) && rows_aligned16(g.B, g.ldb, 2);
+}
+
+template <typename T, int BM, int BN, int WM, int WN, int MINW, int LOAD, bool EDGE, bool PAIRED>
+hipError_t launch_one(const GemmArgs &g, int tiles, int all_flag, hipStream_t s) {
+    hipLaunchKernelGGL((mfma_f16_gemm_kernel<T, BM, BN, WM, WN, MINW, LOAD, EDGE, PAIRED>),
+                       dim3(tiles), dim3(64 * WM * WN), 0, s, g.M, g.N, g.K,
+                       (const uint16_t *)g.A, g.lda, (const uint16_t *)g.B, g.ldb, g.C, g.ldc,
+                       all_flag);
+    return hipGetLastError();
+}
+
+// Interior tiles: buffer loads when rows are 16-byte aligned and every offset fits in
+// 31 bits, with the two-set pipeline when the number of k-steps is even; ragged strips:
+// predicated pointer loads.
+template <typename T, int BM, int BN, int WM, int WN, int MINW>
+hipError_t launch_cfg(const GemmArgs &g, hipStream_t s) {
+    const bool vec = h16_vec(g);
+    const bool kfull = g.K % kBK == 0;
+    const int full_tiles = kfull ? (g.M / BM) * (g.N / BN) : 0;
+    const int edge_tiles = cdiv(g.M, BM) * cdiv(g.N, BN) - full_tiles;
+    const int all_flag = kfull ? 0 : 1;
+    const bool fits = ((long)BM * g.lda + g.K) * 2 < (1L << 31) &&
+                      ((long)g.K * g.ldb + BN) * 2 < (1L << 31);
+    if (full_tiles > 0) {
+        hipError_t e;
+        if (vec && fits) {
+            if ((g.K / kBK) % 2 == 0)
+                e = launch_one<T, BM, BN, WM, WN, MINW, 2, false, true>(g, full_tiles, all_flag, s);
+            else
+                e = launch_one<T, BM, BN, WM, WN, MINW, 2, false, false>(g, full_tiles, all_flag, s);
+        } else if (vec) {
+            e = launch_one<T, BM, BN, WM, WN, MINW, 1, false, false>(g, full_tiles, all_flag, s);
+        } else {
+            e = launch_one<T, BM, BN, WM, WN, MINW, 0, false, false>(g, full_tiles, all_flag, s);
+        }
+        if (e != hipSuccess) return e;
+    }
+    if (edge_tiles > 0) {
+        if (vec) return launch_one<T, BM, BN, WM, WN, MINW, 1, true, false>(g, edge_tiles, all_flag, s);
+        return launch_one<T, BM, BN, WM, WN, MINW, 0, true, false>(g, edge_tiles, all_flag, s);
+    }
+    return hipSuccess;
+}
+
+// Cost model as for FP32: with w resident workgroups per CU a config needs
+// ceil(tiles / (256 w)) rounds of w * BM * BN work each; ties go to the larger tile,
+// whose LDS traffic per MFMA is half that of the smaller one.
+int pick_tile(const GemmArgs &g) {
+    struct Opt { int tile, per_cu; };
+    const Opt opts[] = {{256, 1}, {128, 2}};
+    long best = -1;
+    int tile = 128;
+    for (const Opt &o : opts) {
+        const long tiles = (long)cdiv(g.M, o.tile) * cdiv(g.N, o.tile);
+        const long slots = 256L * o.per_cu;
+        const long cost = (tiles + slots - 1) / slots * o.per_cu * (long)o.tile * o.tile;
+        if (best < 0 || cost < best) {
+            best = cost;
+            tile = o.tile;
+        }
+    }
+    return tile;
 }
 
 template <typename T>
 hipError_t launch_t(const GemmArgs &g, hipStream_t s) {
-    const dim3 grid(cdiv(g.M, kBM) * cdiv(g.N, kBN));
-    const dim3 block(kThreads);
-    const uint16_t *A = (const uint16_t *)g.A, *B = (const uint16_t *)g.B;
-    if (f16_vec(g))
-        hipLaunchKernelGGL((mfma_f16_gemm_kernel<T, true>), grid, block, 0, s, g.M, g.N, g.K, A,
-                           g.lda, B, g.ldb, g.C, g.ldc);
-    else
-        hipLaunchKernelGGL((mfma_f16_gemm_kernel<T, false>), grid, block, 0, s, g.M, g.N, g.K, A,
-                           g.lda, B, g.ldb, g.C, g.ldc);
-    return hipGetLastError();
+    if (pick_tile(g) == 256) return launch_cfg<T, 256, 256, 2, 2, 1>(g, s);
+    return launch_cfg<T, 128, 128, 2, 2, 2>(g, s);
 }
 
 }  // namespace
 
 const char *desc_mfma_f16(int dtype, const GemmArgs &g) {
-    const bool v = f16_vec(g);
-    if (dtype == kF16) return v ? "mfma_f16 128x128x32 w2x2 dwordx4" : "mfma_f16 128x128x32 w2x2 u16";
-    return v ? "mfma_bf16 128x128x32 w2x2 dwordx4" : "mfma_bf16 128x128x32 w2x2 u16";
+    const bool v = h16_vec(g);
+    const bool big = pick_tile(g) == 256;
+    if (dtype == kF16) {
+        if (big) return v ? "mfma_f16 256x256x64 w2x2 dwordx4" : "mfma_f16 256x256x64 w2x2 u16";
+        return v ? "mfma_f16 128x128x64 w2x2 dwordx4" : "mfma_f16 128x128x64 w2x2 u16";
+    }
+    if (big) return v ? "mfma_bf16 256x256x64 w2x2 dwordx4" : "mfma_bf16 256x256x64 w2x2 u16";
+    return v ? "mfma_bf16 128x128x64 w2x2 dwordx4" : "mfma_bf16 128x128x64 w2x2 u16";
 }
 
 hipError_t launch_mfma_f16(int dtype, const GemmArgs &g, hipStream_t s) {

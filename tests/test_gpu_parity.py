@@ -230,3 +230,35 @@ def test_torch_matmul_wrapper():
     out = gb.matmul(torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda())
     C64, _ = oracle.gemm(A, B)
     check(out.cpu().numpy(), C64, "f32", "uniform", 33, True, "matmul wrapper")
+
+
+# Interior-tile instances of the 16-bit kernel: an even number of 64-wide k-steps
+# (paired staging), an odd number, a single k-step, rows that are not 16-byte
+# aligned (16-bit loads), and a misaligned base; each with M, N multiples of the tile.
+INTERIOR_CASES = [((512, 512, 256), (0, 0, 0), 0), ((512, 512, 320), (0, 0, 0), 0),
+                  ((256, 256, 64), (0, 0, 0), 0), ((512, 256, 256), (1, 3, 0), 0),
+                  ((256, 512, 128), (0, 0, 0), 1), ((1024, 768, 192), (8, 8, 8), 0)]
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("case", INTERIOR_CASES, ids=lambda c: "x".join(map(str, c[0])) + f"_pad{c[1][0]}_off{c[2]}")
+def test_h16_interior_instances(dtype, case):
+    (M, N, K), pad, off = case
+    A, B = inputs.make_operands(M, N, K, 41, "uniform", dtype)
+    C64, _ = oracle.gemm(A, B, dtype)
+    C, ok = gpu_gemm(A, B, dtype, gb.VARIANT_MFMA, pad=pad, offset=off, guard_rows=1)
+    check(C, C64, dtype, "uniform", K, ok, f"interior {dtype} {M}x{N}x{K} pad={pad} off={off}")
+    Ai, Bi = inputs.make_operands(M, N, K, 42, "int", dtype)
+    _, C32 = oracle.gemm(Ai, Bi, dtype)
+    Ci, ok = gpu_gemm(Ai, Bi, dtype, gb.VARIANT_MFMA, pad=pad, offset=off)
+    assert ok and np.array_equal(Ci, C32)
+
+
+@pytest.mark.parametrize("case", [(384, 384, 64), (768, 384, 96), (384, 576, 3072)],
+                         ids=lambda c: "x".join(map(str, c)))
+def test_f32_interior_instances(case):
+    M, N, K = case
+    A, B = inputs.make_operands(M, N, K, 43, "uniform", "f32")
+    C64, _ = oracle.gemm(A, B)
+    C, ok = gpu_gemm(A, B, "f32", gb.VARIANT_MFMA, guard_rows=1)
+    check(C, C64, "f32", "uniform", K, ok, f"interior f32 {M}x{N}x{K}")
