@@ -122,6 +122,88 @@ def cpu_baseline(A, B, M, N, K):
                       f"{dt:.2f} s wall"}
 
 
+def time_variant(variant, dtype, M, N, K, seed, reps=None):
+    """Mean per-launch time (ms) of one kernel family on a seeded U[-1,1] workload, timed
+    with HIP events on one stream after warm-up."""
+    import torch
+
+    from roofline_optimisation_amd import binding as gb
+    from roofline_optimisation_amd import inputs
+
+    A, B = inputs.make_operands(M, N, K, seed, "uniform", dtype)
+    if dtype == "f32":
+        dA, dB = torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda()
+    else:
+        dA = torch.from_numpy(A.view("int16")).cuda()
+        dB = torch.from_numpy(B.view("int16")).cuda()
+    dC = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.Stream()
+    code = gb.DTYPE_CODES[dtype]
+    args = (variant, code, M, N, K, dA.data_ptr(), K, dB.data_ptr(), N, dC.data_ptr(), N,
+            stream.cuda_stream)
+    desc = gb.gemm355_kernel_desc(variant, code, M, N, K, dA.data_ptr(), K, dB.data_ptr(), N,
+                                  dC.data_ptr(), N)
+
+    def launch():
+        st = gb.gemm355_run_variant(*args)
+        if st != gb.OK:
+            raise gb.Gemm355Error(st, "gemm355_run_variant")
+
+    launch()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    launch()
+    e1.record(stream)
+    stream.synchronize()
+    one = max(e0.elapsed_time(e1), 1e-3)
+    if reps is None:
+        reps = int(min(200, max(3, 100.0 / one)))  # about 100 ms of timed work
+    for _ in range(2):
+        launch()
+    e0.record(stream)
+    for _ in range(reps):
+        launch()
+    e1.record(stream)
+    stream.synchronize()
+    return e0.elapsed_time(e1) / reps, desc, reps
+
+
+def write_report(path):
+    from roofline_optimisation_amd import inputs
+    from roofline_optimisation_amd import roofline as rl
+
+    names = {0: "naive", 1: "lds_tiled", 2: "regblock", 3: "mfma"}
+    lines = ["# libgemm355 measurements on one MI355X", "",
+             "Per-launch time from HIP events on one stream (mean over >= 3 launches after warm-up),",
+             "U[-1,1] operands, packed row-major strides.  TFLOP/s = 2MNK / t.  Peaks: FP32 157.3,",
+             "FP16/BF16 2516.6 TFLOP/s (2.4 GHz datasheet); attainable = min(peak, OI x 8 TB/s)",
+             "with OI = 2MNK / ideal bytes (each operand read once, C written once).", "",
+             "## Kernel families, FP32", "",
+             "| workload | family | kernel | reps | time (us) | TFLOP/s | % of FP32 peak |",
+             "|---|---|---|---|---|---|---|"]
+    for (n, seed) in ((256, 0), (3072, 1)):
+        for v in (0, 1, 2, 3):
+            ms, desc, reps = time_variant(v, "f32", n, n, n, seed)
+            tf = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+            lines.append(f"| FP32 {n}^3 | {names[v]} | {desc} | {reps} | {ms * 1e3:.1f} | {tf:.2f} | "
+                         f"{100 * tf / PEAKS['f32']:.1f} |")
+            log(f"[report] f32 {n} {names[v]}: {ms * 1e3:.1f} us {tf:.2f} TFLOP/s")
+    lines += ["", "## Roofline sweep (dispatched kernels)", "",
+              "| dtype | M x N x K | kernel | time (us) | TFLOP/s | % of peak | OI (FLOP/B) | "
+              "attainable TFLOP/s | bound |", "|---|---|---|---|---|---|---|---|---|"]
+    for c in inputs.sweep_cases():
+        ms, desc, reps = time_variant(-1, c.dtype, c.M, c.N, c.K, c.seed)
+        tf = 2.0 * c.M * c.N * c.K / (ms * 1e-3) / 1e12
+        e = rl.roofline_entry(c.M, c.N, c.K, ms * 1e-3, c.dtype)
+        bound = "HBM" if e["attainable_tflops"] < e["peak_tflops"] else "compute"
+        lines.append(f"| {c.dtype} | {c.M}x{c.N}x{c.K} | {desc} | {ms * 1e3:.1f} | {tf:.1f} | "
+                     f"{100 * e['frac']:.1f} | {e['oi']:.1f} | {e['attainable_tflops']:.0f} | {bound} |")
+        log(f"[report] {c.name}: {ms * 1e3:.1f} us {tf:.1f} TFLOP/s")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -130,6 +212,10 @@ def main():
     ap.add_argument("--only", choices=["f32", "f16"], default=None,
                     help="measure one workload only (for profiler runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--report", default=None, metavar="PATH",
+                    help="also time every kernel family on the 256^3 and 3072^3 FP32 workloads "
+                         "and the square FP32/BF16 sweep plus the tall-skinny shape, and write a "
+                         "markdown table to PATH (the JSON line is unchanged)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after the GEMMs, copy this many MiB device-to-device once (a plain "
                          "copy of known size, used to scale the HBM byte counters)")
@@ -160,6 +246,9 @@ def main():
         results[kind] = r
         log(f"[bench] {kind} {n}^3 {r['desc']}: {r['ms']:.4f} ms/launch, {tf:.1f} TFLOP/s "
             f"({100 * tf / PEAKS[kind]:.1f}% of {PEAKS[kind]})")
+
+    if args.report:
+        write_report(args.report)
 
     if args.calib_copy_mib:
         nel = args.calib_copy_mib * (1 << 20) // 4
