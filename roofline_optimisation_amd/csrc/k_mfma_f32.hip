@@ -68,10 +68,10 @@ __device__ __forceinline__ floatx4 ld_chunk(const float *__restrict__ row, int c
     return v;
 }
 
-// One BM x BN tile of C.  EDGE selects the predicated loads and guarded stores; the
-// interior instance (tile inside M x N, K a multiple of BK) is straight-line code, so
-// the dwordx4 loads of a k-step issue back to back.
-template <int BM, int BN, int WM, int WN, bool VEC, bool EDGE>
+// One BM x BN tile of C.  LOAD: 0 = dword loads (rows not 16-byte aligned), 1 = dwordx4
+// through pointers, 2 = dwordx4 through buffer resources (interior tiles, offsets below
+// 2^31 bytes).  EDGE selects the predicated loads and guarded stores.
+template <int BM, int BN, int WM, int WN, int LOAD, bool EDGE>
 __device__ __forceinline__ void f32_tile(int M, int N, int K, const float *__restrict__ A, int lda,
                                          const float *__restrict__ B, int ldb,
                                          float *__restrict__ C, int ldc, int m0, int n0,
@@ -80,52 +80,64 @@ __device__ __forceinline__ void f32_tile(int M, int N, int K, const float *__res
     constexpr int T = Cfg::kThreads;
     constexpr int MB = Cfg::kMB, NB = Cfg::kNB;
     constexpr int SB = Cfg::kSB;
+    constexpr int kAC = Cfg::kAChunks, kBC = Cfg::kBChunks, kWr = kAC + kBC;
 
     const int t = threadIdx.x;
     const int lane = t % 64, wave = t / 64;
     const int wm = wave / WN, wn = wave % WN;
     const int l32 = lane % 32, lhi = lane / 32;
 
-    // Per-thread global chunk coordinates (fixed across k-steps).
-    int a_r[Cfg::kAChunks], a_c[Cfg::kAChunks];
-    int b_r[Cfg::kBChunks], b_c[Cfg::kBChunks];
+    // Per-thread global chunk coordinates (fixed across k-steps): chunk q = t + T i of the
+    // A slice (BM rows of 8 chunks) and of the B slice (BK rows of BN/4 chunks).
+    int a_r[kAC], a_c[kAC], b_r[kBC], b_c[kBC];
 #pragma unroll
-    for (int i = 0; i < Cfg::kAChunks; ++i) {
+    for (int i = 0; i < kAC; ++i) {
         const int q = t + T * i;
         a_r[i] = q / (kBK / 4);
         a_c[i] = (q % (kBK / 4)) * 4;
     }
 #pragma unroll
-    for (int i = 0; i < Cfg::kBChunks; ++i) {
+    for (int i = 0; i < kBC; ++i) {
         const int q = t + T * i;
         b_r[i] = q / (BN / 4);
         b_c[i] = (q % (BN / 4)) * 4;
     }
+    // Buffer resources based at the tile's first row (A) and first column (B).
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(A + (size_t)m0 * lda), (short)0, 0x7fffffff, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(B + n0), (short)0, 0x7fffffff, 0x00020000);
 
-    floatx4 sa[Cfg::kAChunks], sb[Cfg::kBChunks];
-    auto load_tile = [&](int k0) {
-#pragma unroll
-        for (int i = 0; i < Cfg::kAChunks; ++i) {
-            const int r = m0 + a_r[i];
-            const bool ok = !EDGE || r < M;
-            sa[i] = ld_chunk<VEC, EDGE>(A + (size_t)(ok ? r : 0) * lda, k0 + a_c[i], K, ok);
-        }
-#pragma unroll
-        for (int i = 0; i < Cfg::kBChunks; ++i) {
-            const int r = k0 + b_r[i];
-            const bool ok = !EDGE || r < K;
-            sb[i] = ld_chunk<VEC, EDGE>(B + (size_t)(ok ? r : 0) * ldb, n0 + b_c[i], N, ok);
+    floatx4 st[kWr];  // staged chunks of the next k-step (A chunks first)
+    auto load_one = [&](int k0, int w) {
+        if constexpr (LOAD == 2) {
+            if (w < kAC)
+                st[w] = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                        ra, (a_r[w] * lda + a_c[w]) * 4, k0 * 4, 0));
+            else
+                st[w] = __builtin_bit_cast(
+                    floatx4, __builtin_amdgcn_raw_buffer_load_b128(
+                                 rb, (b_r[w - kAC] * ldb + b_c[w - kAC]) * 4, k0 * ldb * 4, 0));
+        } else {
+            if (w < kAC) {
+                const int r = m0 + a_r[w];
+                const bool ok = !EDGE || r < M;
+                st[w] = ld_chunk<LOAD == 1, EDGE>(A + (size_t)(ok ? r : 0) * lda, k0 + a_c[w], K, ok);
+            } else {
+                const int r = k0 + b_r[w - kAC];
+                const bool ok = !EDGE || r < K;
+                st[w] = ld_chunk<LOAD == 1, EDGE>(B + (size_t)(ok ? r : 0) * ldb, n0 + b_c[w - kAC],
+                                                   N, ok);
+            }
         }
     };
-    auto store_tile = [&](int buf) {
+    auto store_one = [&](int buf, int w) {
         float *As = lds + buf * (Cfg::kLdsA + Cfg::kLdsB);
         float *Bs = As + Cfg::kLdsA;
-#pragma unroll
-        for (int i = 0; i < Cfg::kAChunks; ++i)
-            *reinterpret_cast<floatx4 *>(As + a_r[i] * kSA + a_c[i]) = sa[i];
-#pragma unroll
-        for (int i = 0; i < Cfg::kBChunks; ++i)
-            *reinterpret_cast<floatx4 *>(Bs + b_r[i] * SB + b_c[i]) = sb[i];
+        if (w < kAC)
+            *reinterpret_cast<floatx4 *>(As + a_r[w] * kSA + a_c[w]) = st[w];
+        else
+            *reinterpret_cast<floatx4 *>(Bs + b_r[w - kAC] * SB + b_c[w - kAC]) = st[w];
     };
 
     floatx16 acc[MB][NB];
@@ -136,43 +148,88 @@ __device__ __forceinline__ void f32_tile(int M, int N, int K, const float *__res
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    const int nk = cdiv(K, kBK);
-    if (nk > 0) {
-        load_tile(0);
-        store_tile(0);
-    }
-    __syncthreads();
-
-    const int a_row0 = wm * Cfg::kTM + l32;  // + 32 mb
-    const int b_col0 = wn * Cfg::kTN + l32;  // + 32 nb
-    for (int kt = 0; kt < nk; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < nk) load_tile((kt + 1) * kBK);
+    // Fragments of one 8-wide k group: lane l reads A[m][k0+4(l/32) .. +3] with one
+    // ds_read_b128 and B[k0+4(l/32)+s][n] for s = 0..3; MFMA step s then sums k0+s and
+    // k0+4+s.
+    const int a_row0 = wm * Cfg::kTM + l32;  // + 32 i
+    const int b_col0 = wn * Cfg::kTN + l32;  // + 32 j
+    constexpr int kGroups = kBK / 8;
+    constexpr int kR = MB + 4 * NB;   // fragment reads per group
+    constexpr int kMf = 4 * MB * NB;  // MFMAs per group
+    floatx4 af[2][MB];
+    float bf[2][NB][4];
+    auto read_piece = [&](int buf, int g, int slot, int p) {
         const float *As = lds + buf * (Cfg::kLdsA + Cfg::kLdsB);
         const float *Bs = As + Cfg::kLdsA;
-#pragma unroll
-        for (int kg = 0; kg < kBK / 8; ++kg) {
-            const int kq = kg * 8 + 4 * lhi;
-            floatx4 af[MB];
-            float bf[NB][4];
-#pragma unroll
-            for (int i = 0; i < MB; ++i)
-                af[i] = *reinterpret_cast<const floatx4 *>(As + (a_row0 + 32 * i) * kSA + kq);
-#pragma unroll
-            for (int j = 0; j < NB; ++j)
-#pragma unroll
-                for (int s = 0; s < 4; ++s) bf[j][s] = Bs[(kq + s) * SB + b_col0 + 32 * j];
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-#pragma unroll
-                for (int i = 0; i < MB; ++i)
-#pragma unroll
-                    for (int j = 0; j < NB; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[i][s], bf[j][s],
-                                                                         acc[i][j], 0, 0, 0);
+        const int kq = g * 8 + 4 * lhi;
+        if (p < MB) {
+            af[slot][p] = *reinterpret_cast<const floatx4 *>(As + (a_row0 + 32 * p) * kSA + kq);
+        } else {
+            const int s = (p - MB) / NB, j = (p - MB) % NB;
+            bf[slot][j][s] = Bs[(kq + s) * SB + b_col0 + 32 * j];
         }
-        if (kt + 1 < nk) store_tile(buf ^ 1);
+    };
+    auto mfma_one = [&](int slot, int q) {  // step-major: q = (s, i, j)
+        const int s = q / (MB * NB), i = (q / NB) % MB, j = q % NB;
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[slot][i][s], bf[slot][j][s], acc[i][j],
+                                                         0, 0, 0);
+    };
+    constexpr int kPre = (kMf * 2) / 3;  // MFMAs of the last group issued before the barrier
+
+    // Software pipeline (the same shape as the 16-bit kernel): group g reads the
+    // fragments of g+1 between its first MFMAs; the last group writes the staged k-step
+    // t+1 to the idle stage between its first kPre MFMAs, then the barrier, then the
+    // global loads of t+2 and the first fragments of t+1 go between its remaining MFMAs.
+    // No branches in the body; near the end the loads re-read the last k-step.
+    const int nk = cdiv(K, kBK);
+    if (nk > 0) {
+#pragma unroll
+        for (int w = 0; w < kWr; ++w) load_one(0, w);
+#pragma unroll
+        for (int w = 0; w < kWr; ++w) store_one(0, w);
         __syncthreads();
+#pragma unroll
+        for (int w = 0; w < kWr; ++w) load_one(min(1, nk - 1) * kBK, w);
+#pragma unroll
+        for (int p = 0; p < kR; ++p) read_piece(0, 0, 0, p);
+        for (int kt = 0; kt < nk; ++kt) {
+            const int buf = kt & 1;
+#pragma unroll
+            for (int g = 0; g < kGroups - 1; ++g) {
+#pragma unroll
+                for (int q = 0; q < kMf; ++q) {
+                    mfma_one(g & 1, q);
+#pragma unroll
+                    for (int p = 2 * q; p < 2 * q + 2; ++p)
+                        if (p < kR) read_piece(buf, g + 1, (g + 1) & 1, p);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            constexpr int sl = (kGroups - 1) & 1;
+#pragma unroll
+            for (int q = 0; q < kPre; ++q) {
+                mfma_one(sl, q);
+#pragma unroll
+                for (int w = q * kWr / kPre; w < (q + 1) * kWr / kPre; ++w) store_one(buf ^ 1, w);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            __syncthreads();
+            const int kload = min(kt + 2, nk - 1) * kBK;
+            constexpr int kPost = kMf - kPre;
+            constexpr int nops = kR + kWr;
+#pragma unroll
+            for (int q = kPre; q < kMf; ++q) {
+                const int qq = q - kPre;
+                const int o_lo = qq * nops / kPost, o_hi = (qq + 1) * nops / kPost;
+#pragma unroll
+                for (int o = o_lo; o < o_hi; ++o) {
+                    if (o < kR) read_piece(buf ^ 1, 0, 0, o);
+                    else load_one(kload, o - kR);
+                }
+                mfma_one(sl, q);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
     }
 
     // 32x32 accumulator layout: register r of lane l holds row 8(r/4) + 4(l/32) + r%4,
@@ -212,7 +269,7 @@ __device__ __forceinline__ void tile_of(int bid, int nblocks, int tiles_m, int t
     }
 }
 
-template <int BM, int BN, int WM, int WN, int MINW, bool VEC, bool EDGE>
+template <int BM, int BN, int WM, int WN, int MINW, int LOAD, bool EDGE>
 __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(MINW)))
 void mfma_f32_gemm_kernel(int M, int N, int K, const float *__restrict__ A, int lda,
                           const float *__restrict__ B, int ldb, float *__restrict__ C, int ldc,
@@ -223,7 +280,7 @@ void mfma_f32_gemm_kernel(int M, int N, int K, const float *__restrict__ A, int 
     const int tiles_n = EDGE ? cdiv(N, BN) : N / BN;
     int tm, tn;
     tile_of<EDGE>(blockIdx.x, gridDim.x, tiles_m, tiles_n, N % BN != 0, all_tiles != 0, tm, tn);
-    f32_tile<BM, BN, WM, WN, VEC, EDGE>(M, N, K, A, lda, B, ldb, C, ldc, tm * BM, tn * BN, lds);
+    f32_tile<BM, BN, WM, WN, LOAD, EDGE>(M, N, K, A, lda, B, ldb, C, ldc, tm * BM, tn * BN, lds);
 }
 
 struct F32Pick {
@@ -253,40 +310,39 @@ F32Pick pick_f32(const GemmArgs &g) {
     return {tile, vec};
 }
 
+template <int BM, int BN, int WM, int WN, int MINW, int LOAD, bool EDGE>
+hipError_t launch_one(const GemmArgs &g, int tiles, int all_flag, hipStream_t s) {
+    hipLaunchKernelGGL((mfma_f32_gemm_kernel<BM, BN, WM, WN, MINW, LOAD, EDGE>), dim3(tiles),
+                       dim3(64 * WM * WN), 0, s, g.M, g.N, g.K, (const float *)g.A, g.lda,
+                       (const float *)g.B, g.ldb, g.C, g.ldc, all_flag);
+    return hipGetLastError();
+}
+
 // MINW: waves per SIMD the register budget must allow (resident workgroups per CU
-// times waves per workgroup / 4).  Full interior tiles go to the straight-line kernel;
-// ragged strips (or every tile, when K is not a multiple of BK) to the predicated one.
+// times waves per workgroup / 4).  Full interior tiles go to the straight-line kernel
+// (buffer loads when rows are 16-byte aligned and offsets fit in 31 bits); ragged
+// strips (or every tile, when K is not a multiple of BK) to the predicated one.
 template <int BM, int BN, int WM, int WN, int MINW>
 hipError_t launch_cfg(const GemmArgs &g, bool vec, hipStream_t s) {
-    const dim3 block(64 * WM * WN);
     const bool kfull = g.K % kBK == 0;
     const int full_tiles = kfull ? (g.M / BM) * (g.N / BN) : 0;
-    const int all = cdiv(g.M, BM) * cdiv(g.N, BN);
-    const int edge_tiles = all - full_tiles;
+    const int edge_tiles = cdiv(g.M, BM) * cdiv(g.N, BN) - full_tiles;
     const int all_flag = kfull ? 0 : 1;
-    const float *A = (const float *)g.A, *B = (const float *)g.B;
+    const bool fits = ((long)BM * g.lda + g.K) * 4 < (1L << 31) &&
+                      ((long)g.K * g.ldb + BN) * 4 < (1L << 31);
     if (full_tiles > 0) {
-        if (vec)
-            hipLaunchKernelGGL((mfma_f32_gemm_kernel<BM, BN, WM, WN, MINW, true, false>),
-                               dim3(full_tiles), block, 0, s, g.M, g.N, g.K, A, g.lda, B, g.ldb,
-                               g.C, g.ldc, all_flag);
+        hipError_t e;
+        if (vec && fits)
+            e = launch_one<BM, BN, WM, WN, MINW, 2, false>(g, full_tiles, all_flag, s);
+        else if (vec)
+            e = launch_one<BM, BN, WM, WN, MINW, 1, false>(g, full_tiles, all_flag, s);
         else
-            hipLaunchKernelGGL((mfma_f32_gemm_kernel<BM, BN, WM, WN, MINW, false, false>),
-                               dim3(full_tiles), block, 0, s, g.M, g.N, g.K, A, g.lda, B, g.ldb,
-                               g.C, g.ldc, all_flag);
-        const hipError_t e = hipGetLastError();
+            e = launch_one<BM, BN, WM, WN, MINW, 0, false>(g, full_tiles, all_flag, s);
         if (e != hipSuccess) return e;
     }
     if (edge_tiles > 0) {
-        if (vec)
-            hipLaunchKernelGGL((mfma_f32_gemm_kernel<BM, BN, WM, WN, MINW, true, true>),
-                               dim3(edge_tiles), block, 0, s, g.M, g.N, g.K, A, g.lda, B, g.ldb,
-                               g.C, g.ldc, all_flag);
-        else
-            hipLaunchKernelGGL((mfma_f32_gemm_kernel<BM, BN, WM, WN, MINW, false, true>),
-                               dim3(edge_tiles), block, 0, s, g.M, g.N, g.K, A, g.lda, B, g.ldb,
-                               g.C, g.ldc, all_flag);
-        return hipGetLastError();
+        if (vec) return launch_one<BM, BN, WM, WN, MINW, 1, true>(g, edge_tiles, all_flag, s);
+        return launch_one<BM, BN, WM, WN, MINW, 0, true>(g, edge_tiles, all_flag, s);
     }
     return hipSuccess;
 }
