@@ -3,7 +3,8 @@
 Every ``csrc/*.hip`` file is compiled to an object in ``_build/`` in parallel and the
 objects are linked into ``roofline_optimisation_amd/libgemm355.so``.  All device code
 is built with packed FP32 instructions disabled (``-packed-fp32-ops``): the FP32 paths
-use unpacked v_fma_f32 on the vector ALUs or the matrix cores.
+use unpacked v_fma_f32 on the vector ALUs or the matrix cores.  The pipelined loops
+rely on full unrolling, so the pragma-unroll threshold is raised.
 """
 
 from __future__ import annotations
@@ -24,6 +25,9 @@ ARCH = "gfx950"
 HIPFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # the software-pipelined loops are unrolled in full (register arrays indexed by
+    # unrolled loop counters must not fall back to scratch memory)
+    "-mllvm", "-pragma-unroll-threshold=1000000",
     "-I", os.path.join(os.path.dirname(HERE), "include"),
 ]
 

@@ -193,14 +193,30 @@ __device__ __forceinline__ void h16_tile(int M, int N, int K, const uint16_t *__
     constexpr int kWr = kAC + kBC;                // staged chunks per k-step
     constexpr int kRdSlots = (kR + 1) / 2;        // reads go two per MFMA, first
 
+    // Events of one k-step are spread over its kSteps * kMf MFMA slots: event e of n
+    // spread over slots [lo, hi) goes after the MFMA of slot lo + ceil-spread(e).
+    constexpr int kSlots = kSteps * kMf;
+    auto ev_begin = [](int q, int n, int lo, int hi) {  // first event at or after slot q
+        if (q <= lo) return 0;
+        if (q >= hi) return n;
+        return ((q - lo) * n + (hi - lo) - 1) / (hi - lo);
+    };
+    // Store window: the idle stage is free from the start of the k-step, so the staged
+    // chunks of k-step t+1 are written over every slot before the barrier.  Paired loads
+    // of k-step t+2 (into the other, already written-out set) go over the first half.
+    constexpr int kBarrier = (kSteps - 1) * kMf + kPre;   // barrier after this many slots
+    constexpr int kStoreLo = 0, kStoreHi = kBarrier;
+    constexpr int kLoadLo = 0, kLoadHi = kSlots / 2;
+
     // One k-step t on stage buf.  Every memory instruction is issued between MFMAs so
     // that no burst blocks the in-order issue of the MFMAs behind it:
-    //  * sub-steps s < last: after MFMA q, fragment reads 2q, 2q+1 of sub-step s+1 (slot
-    //    (s+1) % 2); then, paired variant only, the global loads of k-step t+2 into the
-    //    free staging set O, spread one per MFMA over the remaining slots;
-    //  * last sub-step: the staged k-step t+1 (set S) is written to the idle stage
-    //    between the first kPre MFMAs; barrier; then the fragments of t+1's first
-    //    sub-step (and, unpaired variant, the loads of t+2 into S) between the rest.
+    //  * sub-step s < last reads the fragments of s+1 (slot (s+1) % 2) two per MFMA
+    //    after its first MFMAs;
+    //  * the staged chunks of k-step t+1 (set S) are written to the idle stage, spread
+    //    over all slots before the barrier; paired variant: the loads of k-step t+2 go
+    //    into the other set O over the first half; unpaired variant: chunk w of t+2 is
+    //    loaded into S right after chunk w of t+1 was written;
+    //  * after the barrier, the first fragments of t+1 are read between the last MFMAs.
     // The body has no branches (a branch makes the compiler wait for every outstanding
     // LDS read at the join): near the end the loads re-read the last k-step and the idle
     // stage takes dummies.
@@ -208,52 +224,41 @@ __device__ __forceinline__ void h16_tile(int M, int N, int K, const uint16_t *__
     auto kstep = [&](auto set_c, auto other_c, int kt, int buf) {
         const int kload = min(kt + 2, nk - 1) * kBK;
 #pragma unroll
-        for (int s = 0; s < kSteps - 1; ++s) {
-            constexpr int nl_all = PAIRED ? kWr : 0;
-            const int l_lo = s * nl_all / (kSteps - 1), l_hi = (s + 1) * nl_all / (kSteps - 1);
+        for (int s = 0; s < kSteps; ++s) {
 #pragma unroll
-            for (int q = 0; q < kMf; ++q) {
-                mfma_one(s & 1, q);
+          for (int q = 0; q < kMf; ++q) {
+            const int qs = s * kMf + q;
+            if (qs >= kBarrier) {
+                // after the barrier: next k-step's first fragments before each MFMA
+                const int r_lo = ev_begin(qs, kR, kBarrier, kSlots);
+                const int r_hi = ev_begin(qs + 1, kR, kBarrier, kSlots);
+#pragma unroll
+                for (int o = r_lo; o < r_hi; ++o) read_piece(buf ^ 1, 0, 0, o);
+            }
+            mfma_one(s & 1, q);
+            if (s + 1 < kSteps) {
 #pragma unroll
                 for (int p = 2 * q; p < 2 * q + 2; ++p)
                     if (p < kR) read_piece(buf, s + 1, (s + 1) & 1, p);
-                if constexpr (PAIRED) {
-                    // loads l_lo .. l_hi-1 over slots kRdSlots .. kMf-1
-                    constexpr int slots = kMf - kRdSlots > 0 ? kMf - kRdSlots : 1;
-                    const int qs = q - kRdSlots < 0 ? -1 : q - kRdSlots;
-                    const int n = l_hi - l_lo;
-                    if (qs >= 0) {
-                        const int o_lo = qs * n / slots, o_hi = qs + 1 == slots ? n : (qs + 1) * n / slots;
-                        for (int o = o_lo; o < o_hi; ++o) load_one(other_c, kload, l_lo + o);
-                    } else if (kMf - kRdSlots <= 0 && q == kMf - 1) {
-                        for (int o = 0; o < n; ++o) load_one(other_c, kload, l_lo + o);
-                    }
+            }
+            if (qs < kBarrier) {
+                const int w_lo = ev_begin(qs, kWr, kStoreLo, kStoreHi);
+                const int w_hi = ev_begin(qs + 1, kWr, kStoreLo, kStoreHi);
+#pragma unroll
+                for (int w = w_lo; w < w_hi; ++w) {
+                    store_one(set_c, buf ^ 1, w);
+                    if constexpr (!PAIRED) load_one(set_c, kload, w);
                 }
-                __builtin_amdgcn_sched_barrier(0);
             }
-        }
-        constexpr int sl = (kSteps - 1) & 1;
+            if constexpr (PAIRED) {
+                const int l_lo = ev_begin(qs, kWr, kLoadLo, kLoadHi);
+                const int l_hi = ev_begin(qs + 1, kWr, kLoadLo, kLoadHi);
 #pragma unroll
-        for (int q = 0; q < kPre; ++q) {
-            mfma_one(sl, q);
-#pragma unroll
-            for (int w = q * kWr / kPre; w < (q + 1) * kWr / kPre; ++w) store_one(set_c, buf ^ 1, w);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        __syncthreads();
-        constexpr int kPost = kMf - kPre;
-        constexpr int nops = kR + (PAIRED ? 0 : kWr);
-#pragma unroll
-        for (int q = kPre; q < kMf; ++q) {
-            const int qq = q - kPre;
-            const int o_lo = qq * nops / kPost, o_hi = (qq + 1) * nops / kPost;
-#pragma unroll
-            for (int o = o_lo; o < o_hi; ++o) {
-                if (o < kR) read_piece(buf ^ 1, 0, 0, o);
-                else load_one(set_c, kload, o - kR);
+                for (int w = l_lo; w < l_hi; ++w) load_one(other_c, kload, w);
             }
-            mfma_one(sl, q);
+            if (qs == kBarrier - 1) __syncthreads();
             __builtin_amdgcn_sched_barrier(0);
+          }
         }
     };
 
