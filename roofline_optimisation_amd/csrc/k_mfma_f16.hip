@@ -189,9 +189,8 @@ __device__ __forceinline__ void h16_tile(int M, int N, int K, const uint16_t *__
         acc[i][j] = mfma32x32x16<T>(af[slot][i], b, acc[i][j]);
     };
     constexpr int kMf = MB * NB;                  // MFMAs per sub-step
-    constexpr int kPre = (kMf * 5 + 7) / 8;       // of those, issued before the barrier
+    constexpr int kPre = (kMf * 3 + 7) / 8;       // of those, issued before the barrier
     constexpr int kWr = kAC + kBC;                // staged chunks per k-step
-    constexpr int kRdSlots = (kR + 1) / 2;        // reads go two per MFMA, first
 
     // Events of one k-step are spread over its kSteps * kMf MFMA slots: event e of n
     // spread over slots [lo, hi) goes after the MFMA of slot lo + ceil-spread(e).
@@ -296,7 +295,9 @@ __device__ __forceinline__ void h16_tile(int M, int N, int K, const uint16_t *__
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int row = m0 + wm * Cfg::kTM + 32 * i + 8 * (r / 4) + 4 * lhi + (r % 4);
-                if (!EDGE || (row < M && col < N)) C[(size_t)row * ldc + col] = acc[i][j][r];
+                // streaming store: C is written once and not re-read by this kernel
+                if (!EDGE || (row < M && col < N))
+                    __builtin_nontemporal_store(acc[i][j][r], C + (size_t)row * ldc + col);
             }
         }
     }

@@ -23,6 +23,8 @@
 //    zero fill and store with a guard; interior tiles take the unpredicated path;
 //  * launch order: tiles are renumbered so each XCD receives a contiguous range, walked
 //    in groups of 4 tile-rows, which keeps shared A and B panels in that XCD's L2.
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -71,7 +73,7 @@ __device__ __forceinline__ floatx4 ld_chunk(const float *__restrict__ row, int c
 // One BM x BN tile of C.  LOAD: 0 = dword loads (rows not 16-byte aligned), 1 = dwordx4
 // through pointers, 2 = dwordx4 through buffer resources (interior tiles, offsets below
 // 2^31 bytes).  EDGE selects the predicated loads and guarded stores.
-template <int BM, int BN, int WM, int WN, int LOAD, bool EDGE>
+template <int BM, int BN, int WM, int WN, int LOAD, bool EDGE, bool PAIRED>
 __device__ __forceinline__ void f32_tile(int M, int N, int K, const float *__restrict__ A, int lda,
                                          const float *__restrict__ B, int ldb,
                                          float *__restrict__ C, int ldc, int m0, int n0,
@@ -192,8 +194,10 @@ __device__ __forceinline__ void f32_tile(int M, int N, int K, const float *__res
         for (int w = 0; w < kWr; ++w) load_one(min(1, nk - 1) * kBK, w);
 #pragma unroll
         for (int p = 0; p < kR; ++p) read_piece(0, 0, 0, p);
-        for (int kt = 0; kt < nk; ++kt) {
-            const int buf = kt & 1;
+        // One k-step t on stage buf (a compile-time constant in the unrolled pair, so
+        // every LDS address is a register base plus an immediate offset).
+        auto kstep = [&](auto buf_c, int kt) {
+            constexpr int buf = decltype(buf_c)::value;
 #pragma unroll
             for (int g = 0; g < kGroups - 1; ++g) {
 #pragma unroll
@@ -228,6 +232,19 @@ __device__ __forceinline__ void f32_tile(int M, int N, int K, const float *__res
                 }
                 mfma_one(sl, q);
                 __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+        using B0 = std::integral_constant<int, 0>;
+        using B1 = std::integral_constant<int, 1>;
+        if constexpr (PAIRED) {
+            for (int kt = 0; kt < nk; kt += 2) {  // nk is even
+                kstep(B0{}, kt);
+                kstep(B1{}, kt + 1);
+            }
+        } else {
+            for (int kt = 0; kt < nk; kt += 2) {
+                kstep(B0{}, kt);
+                if (kt + 1 < nk) kstep(B1{}, kt + 1);
             }
         }
     }
@@ -269,7 +286,7 @@ __device__ __forceinline__ void tile_of(int bid, int nblocks, int tiles_m, int t
     }
 }
 
-template <int BM, int BN, int WM, int WN, int MINW, int LOAD, bool EDGE>
+template <int BM, int BN, int WM, int WN, int MINW, int LOAD, bool EDGE, bool PAIRED>
 __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(MINW)))
 void mfma_f32_gemm_kernel(int M, int N, int K, const float *__restrict__ A, int lda,
                           const float *__restrict__ B, int ldb, float *__restrict__ C, int ldc,
@@ -280,7 +297,8 @@ void mfma_f32_gemm_kernel(int M, int N, int K, const float *__restrict__ A, int 
     const int tiles_n = EDGE ? cdiv(N, BN) : N / BN;
     int tm, tn;
     tile_of<EDGE>(blockIdx.x, gridDim.x, tiles_m, tiles_n, N % BN != 0, all_tiles != 0, tm, tn);
-    f32_tile<BM, BN, WM, WN, LOAD, EDGE>(M, N, K, A, lda, B, ldb, C, ldc, tm * BM, tn * BN, lds);
+    f32_tile<BM, BN, WM, WN, LOAD, EDGE, PAIRED>(M, N, K, A, lda, B, ldb, C, ldc, tm * BM, tn * BN,
+                                                lds);
 }
 
 struct F32Pick {
@@ -310,9 +328,9 @@ F32Pick pick_f32(const GemmArgs &g) {
     return {tile, vec};
 }
 
-template <int BM, int BN, int WM, int WN, int MINW, int LOAD, bool EDGE>
+template <int BM, int BN, int WM, int WN, int MINW, int LOAD, bool EDGE, bool PAIRED = false>
 hipError_t launch_one(const GemmArgs &g, int tiles, int all_flag, hipStream_t s) {
-    hipLaunchKernelGGL((mfma_f32_gemm_kernel<BM, BN, WM, WN, MINW, LOAD, EDGE>), dim3(tiles),
+    hipLaunchKernelGGL((mfma_f32_gemm_kernel<BM, BN, WM, WN, MINW, LOAD, EDGE, PAIRED>), dim3(tiles),
                        dim3(64 * WM * WN), 0, s, g.M, g.N, g.K, (const float *)g.A, g.lda,
                        (const float *)g.B, g.ldb, g.C, g.ldc, all_flag);
     return hipGetLastError();
@@ -332,7 +350,9 @@ hipError_t launch_cfg(const GemmArgs &g, bool vec, hipStream_t s) {
                       ((long)g.K * g.ldb + BN) * 4 < (1L << 31);
     if (full_tiles > 0) {
         hipError_t e;
-        if (vec && fits)
+        if (vec && fits && (g.K / kBK) % 2 == 0)
+            e = launch_one<BM, BN, WM, WN, MINW, 2, false, true>(g, full_tiles, all_flag, s);
+        else if (vec && fits)
             e = launch_one<BM, BN, WM, WN, MINW, 2, false>(g, full_tiles, all_flag, s);
         else if (vec)
             e = launch_one<BM, BN, WM, WN, MINW, 1, false>(g, full_tiles, all_flag, s);
