@@ -70,6 +70,19 @@ __device__ __forceinline__ shortx4 ds_read_tr16(const uint16_t *p) {
         (lds_shortx4 *)(__attribute__((address_space(3))) void *)(p));
 }
 
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
+typedef __attribute__((address_space(3))) u16x8 lds_u16x8;
+
+// An LDS address held in its own VGPR: the empty asm hides its relation to other
+// addresses, so the compiler keeps one base per (stage, region) and addresses every
+// access as base + immediate (DS immediates are 16 bits) instead of adding large
+// constants to a shared base inside the loop.
+__device__ __forceinline__ lds_u16 *lds_base(lds_u16 *p) {
+    uint32_t a = (uint32_t)(uintptr_t)p;
+    asm volatile("" : "+v"(a));
+    return (lds_u16 *)(uintptr_t)a;
+}
+
 // Columns [c, c+8) of one row.  EDGE: zero outside [0, ncols) and for invalid rows;
 // otherwise the chunk is known to be inside the matrix.
 template <bool VEC, bool EDGE>
@@ -142,15 +155,19 @@ __device__ __forceinline__ void h16_tile(int M, int N, int K, const uint16_t *__
             }
         }
     };
+    // Per-lane LDS bases for the staged writes, one per stage and operand.
+    constexpr int kStage = Cfg::kLdsA + Cfg::kLdsB;
+    lds_u16 *const L = (lds_u16 *)lds;
+    lds_u16 *const a_wr[2] = {lds_base(L + a_r0 * kSA + a_c0),
+                              lds_base(L + kStage + a_r0 * kSA + a_c0)};
+    lds_u16 *const b_wr[2] = {lds_base(L + Cfg::kLdsA + b_r0 * SB + b_c0),
+                              lds_base(L + kStage + Cfg::kLdsA + b_r0 * SB + b_c0)};
     auto store_one = [&](auto set_c, int buf, int w) {
         constexpr int S = decltype(set_c)::value;
-        uint16_t *As = lds + buf * (Cfg::kLdsA + Cfg::kLdsB);
-        uint16_t *Bs = As + Cfg::kLdsA;
         if (w < kAC)
-            *reinterpret_cast<u16x8 *>(As + (a_r0 + w * kARowStep) * kSA + a_c0) = sa[S][w];
+            *(lds_u16x8 *)(a_wr[buf] + w * kARowStep * kSA) = sa[S][w];
         else
-            *reinterpret_cast<u16x8 *>(Bs + (b_r0 + (w - kAC) * kBRowStep) * SB + b_c0) =
-                sb[S][w - kAC];
+            *(lds_u16x8 *)(b_wr[buf] + (w - kAC) * kBRowStep * SB) = sb[S][w - kAC];
     };
 
     floatx16 acc[MB][NB];
@@ -172,14 +189,16 @@ __device__ __forceinline__ void h16_tile(int M, int N, int K, const uint16_t *__
     shortx4 bt[2][NB][2];
     // Fragment read `p` of sub-step s into slot: p < MB is A block p (one ds_read_b128),
     // the others are the two ds_read_b64_tr_b16 halves of B block (p - MB) / 2.
+    lds_u16 *const a_rd[2] = {lds_base(L + a_off), lds_base(L + kStage + a_off)};
+    lds_u16 *const b_rd[2] = {lds_base(L + Cfg::kLdsA + b_off),
+                              lds_base(L + kStage + Cfg::kLdsA + b_off)};
     auto read_piece = [&](int buf, int s, int slot, int p) {
-        const uint16_t *As = lds + buf * (Cfg::kLdsA + Cfg::kLdsB);
-        const uint16_t *Bs = As + Cfg::kLdsA;
         if (p < MB) {
-            af[slot][p] = *reinterpret_cast<const u16x8 *>(As + a_off + 32 * p * kSA + 16 * s);
+            af[slot][p] = *(const lds_u16x8 *)(a_rd[buf] + 32 * p * kSA + 16 * s);
         } else {
             const int j = (p - MB) / 2, h = (p - MB) % 2;
-            bt[slot][j][h] = ds_read_tr16(Bs + b_off + 16 * s * SB + 32 * j + 4 * h * SB);
+            bt[slot][j][h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_shortx4 *)(b_rd[buf] + 16 * s * SB + 32 * j + 4 * h * SB));
         }
     };
     auto mfma_one = [&](int slot, int q) {
