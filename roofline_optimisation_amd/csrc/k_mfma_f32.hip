@@ -372,7 +372,7 @@ hipError_t launch_cfg(const GemmArgs &g, bool vec, hipStream_t s) {
 const char *desc_mfma_f32(const GemmArgs &g) {
     const F32Pick p = pick_f32(g);
     switch (p.tile) {
-    case 192: return p.vec ? "mfma_f32 192x192x32 w2x2 dwordx4" : "mfma_f32 192x192x32 w2x2 dword";
+    case 192: return p.vec ? "mfma_f32 192x192x32 w2x6 dwordx4" : "mfma_f32 192x192x32 w2x6 dword";
     case 128: return p.vec ? "mfma_f32 128x128x32 w2x2 dwordx4" : "mfma_f32 128x128x32 w2x2 dword";
     default: return p.vec ? "mfma_f32 64x64x32 w2x2 dwordx4" : "mfma_f32 64x64x32 w2x2 dword";
     }
@@ -381,7 +381,7 @@ const char *desc_mfma_f32(const GemmArgs &g) {
 hipError_t launch_mfma_f32(const GemmArgs &g, hipStream_t s) {
     const F32Pick p = pick_f32(g);
     switch (p.tile) {
-    case 192: return launch_cfg<192, 192, 2, 2, 1>(g, p.vec, s);
+    case 192: return launch_cfg<192, 192, 2, 6, 3>(g, p.vec, s);
     case 128: return launch_cfg<128, 128, 2, 2, 2>(g, p.vec, s);
     default: return launch_cfg<64, 64, 2, 2, 4>(g, p.vec, s);
     }
