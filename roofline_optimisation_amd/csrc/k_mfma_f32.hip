@@ -306,19 +306,22 @@ struct F32Pick {
     bool vec;
 };
 
-// Cost model: a tile config with w resident workgroups per CU finishes in
-// ceil(tiles / (256 w)) rounds of w * BM * BN work each; pick the cheapest, larger
-// tiles first on ties (less L2 traffic per FLOP).
+// Cost model: tiles are spread over the 256 CUs, so a config finishes after
+// ceil(tiles / 256) tile-times per CU, each proportional to the tile's area over the
+// efficiency measured for that tile shape on full tiles (64: 0.85, 128 and 192: 0.95 of
+// the MFMA rate); ragged strips run as a second launch at about half that efficiency.
 F32Pick pick_f32(const GemmArgs &g) {
-    struct Opt { int tile, per_cu; };
-    const Opt opts[] = {{192, 1}, {128, 2}, {64, 4}};
-    long best = -1;
+    struct Opt { int tile; double eff; };
+    const Opt opts[] = {{192, 0.95}, {128, 0.95}, {64, 0.85}};
+    double best = -1.0;
     int tile = 64;
     for (const Opt &o : opts) {
-        const long tiles = (long)cdiv(g.M, o.tile) * cdiv(g.N, o.tile);
-        const long slots = 256L * o.per_cu;
-        const long rounds = (tiles + slots - 1) / slots;
-        const long cost = rounds * o.per_cu * (long)o.tile * o.tile;
+        const long full = (long)(g.M / o.tile) * (g.N / o.tile);
+        const long all = (long)cdiv(g.M, o.tile) * cdiv(g.N, o.tile);
+        const long edge = g.K % kBK == 0 ? all - full : all;
+        const double area = (double)o.tile * o.tile;
+        const double cost = (double)((all - edge + 255) / 256) * area / o.eff +
+                            (double)((edge + 255) / 256) * area / (0.5 * o.eff);
         if (best < 0 || cost < best) {
             best = cost;
             tile = o.tile;
