@@ -136,6 +136,43 @@ def test_random_block_product(kind):
     assert np.array_equal(d, ref[rows, cols])
 
 
+def tr16_expected(addrs):
+    """The mapping the 16-bit kernel relies on: within each 16-lane group, output lane j
+    receives as element e the halfword j % 4 of the 8 bytes read by source lane
+    4 e + (j % 16) / 4 of the same group."""
+    out = np.zeros((64, 4), np.int64)
+    for j in range(64):
+        g = j // 16
+        for e in range(4):
+            src = 16 * g + 4 * e + (j % 16) // 4
+            out[j, e] = addrs[src] // 2 + j % 4
+    return out
+
+
+@pytest.mark.parametrize("pattern", ["linear", "rows576", "reversed", "gemm_b_fragment"])
+def test_ds_read_tr16_mapping(pattern):
+    import torch
+    if pattern == "linear":
+        addrs = [8 * l for l in range(64)]
+    elif pattern == "rows576":
+        addrs = [576 * (l % 16 // 4) + 8 * (l % 4) + 32 * (l // 16) for l in range(64)]
+    elif pattern == "reversed":
+        addrs = [8 * (63 - l) for l in range(64)]
+    else:
+        # the B-fragment addresses of the kernel: group g reads rows 8 (g/2) + e, columns
+        # 16 (g%2) + 4 q, with a 576-byte row stride
+        addrs = []
+        for l in range(64):
+            g, s = l // 16, l % 16
+            addrs.append((8 * (g // 2) + s // 4) * 576 + 2 * (16 * (g % 2) + 4 * (s % 4)))
+    out = torch.zeros(256, dtype=torch.int16, device="cuda")
+    st = gb.gemm355_probe_ds_read_tr16(addrs, out.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    assert st == gb.OK
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.int64).reshape(64, 4)
+    assert np.array_equal(got, tr16_expected(addrs)), pattern
+
+
 def test_ds_read_tr16_mapping_recorded():
     """Records where each output halfword of ds_read_b64_tr_b16 comes from, for linear
     lane addresses (lane l at byte 8l) and for a row-strided pattern; asserts only that
