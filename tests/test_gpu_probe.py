@@ -6,7 +6,9 @@ Layouts asserted (A is M x k, B is k x N, D = A.B, W = 32 or 16 rows per block):
   * the k slots of A-lane l and B-lane l' coincide element by element whenever
     l div W == l' div W (the kernels only rely on this consistency);
   * accumulator: 32 x 32 blocks: register r of lane l is D[8(r/4) + 4(l/32) + r%4][l%32];
-    16 x 16 blocks: register r of lane l is D[4(l/16) + r][l%16].
+    16 x 16 blocks: register r of lane l is D[4(l/16) + r][l%16];
+  * ds_read_b64_tr_b16: within each 16-lane group, output lane j receives as element e
+    halfword j%4 of the 8 bytes addressed by source lane 4e + (j%16)/4.
 """
 
 from __future__ import annotations
@@ -159,12 +161,12 @@ def test_ds_read_tr16_mapping(pattern):
     elif pattern == "reversed":
         addrs = [8 * (63 - l) for l in range(64)]
     else:
-        # the B-fragment addresses of the kernel: group g reads rows 8 (g/2) + e, columns
-        # 16 (g%2) + 4 q, with a 576-byte row stride
+        # the kernel's B-fragment address structure (group g reads rows 8 (g/2) + e,
+        # columns 16 (g%2) + 4 q), with a 320-byte row stride so it fits the probe's 4 KiB
         addrs = []
         for l in range(64):
             g, s = l // 16, l % 16
-            addrs.append((8 * (g // 2) + s // 4) * 576 + 2 * (16 * (g % 2) + 4 * (s % 4)))
+            addrs.append((8 * (g // 2) + s // 4) * 320 + 2 * (16 * (g % 2) + 4 * (s % 4)))
     out = torch.zeros(256, dtype=torch.int16, device="cuda")
     st = gb.gemm355_probe_ds_read_tr16(addrs, out.data_ptr(), torch.cuda.current_stream().cuda_stream)
     assert st == gb.OK
