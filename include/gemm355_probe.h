@@ -43,6 +43,16 @@ gemm355_status gemm355_probe_mfma(int kind, int nruns, const float *dev_a, const
 gemm355_status gemm355_probe_ds_read_tr16(const uint32_t *host_addr, uint16_t *dev_out,
                                           hipStream_t stream);
 
+/* One wave: lane l executes global_load_lds_dwordx4 from dev_src + 4*host_src_chunk[l]
+ * (16-byte chunks of a caller buffer of at least 4*(max chunk + 1) 32-bit words) into a
+ * 2 KiB LDS array zero-filled beforehand, with a wave-uniform LDS base of byte
+ * lds_base (a multiple of 16, at most 1024); after a barrier the whole 2 KiB array is
+ * copied to dev_out (512 words).  host_src_chunk is a host array of 64 entries, each
+ * at most 4095. */
+gemm355_status gemm355_probe_global_load_lds(const uint32_t *dev_src, const uint32_t *host_src_chunk,
+                                             uint32_t lds_base, uint32_t *dev_out,
+                                             hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -29,6 +29,7 @@ EXPORTS = (
     "gemm355_select_variant", "gemm355_kernel_desc", "gemm355_status_string",
     "gemm355_variant_name", "gemm355_version",
     "gemm355_probe_mfma_shape", "gemm355_probe_mfma", "gemm355_probe_ds_read_tr16",
+    "gemm355_probe_global_load_lds",
 )
 
 
@@ -66,6 +67,9 @@ def _configure(lib):
     lib.gemm355_probe_mfma.restype = i
     lib.gemm355_probe_ds_read_tr16.argtypes = [ctypes.POINTER(ctypes.c_uint32), p, p]
     lib.gemm355_probe_ds_read_tr16.restype = i
+    lib.gemm355_probe_global_load_lds.argtypes = [p, ctypes.POINTER(ctypes.c_uint32),
+                                                  ctypes.c_uint32, p, p]
+    lib.gemm355_probe_global_load_lds.restype = i
     return lib
 
 
@@ -132,6 +136,11 @@ def gemm355_probe_mfma(kind, nruns, dev_a, dev_b, dev_d, stream=0) -> int:
 def gemm355_probe_ds_read_tr16(host_addrs, dev_out, stream=0) -> int:
     arr = (ctypes.c_uint32 * 64)(*[int(a) for a in host_addrs])
     return lib().gemm355_probe_ds_read_tr16(arr, dev_out, stream)
+
+
+def gemm355_probe_global_load_lds(dev_src, host_chunks, lds_base, dev_out, stream=0) -> int:
+    arr = (ctypes.c_uint32 * 64)(*[int(c) for c in host_chunks])
+    return lib().gemm355_probe_global_load_lds(dev_src, arr, int(lds_base), dev_out, stream)
 
 
 def status_string(status: int) -> str:

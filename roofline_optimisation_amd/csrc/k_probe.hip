@@ -75,6 +75,26 @@ __global__ __launch_bounds__(64) void probe_tr16_kernel(LaneAddrs addrs, uint16_
     for (int e = 0; e < 4; ++e) out[4 * l + e] = (uint16_t)r[e];
 }
 
+struct LaneChunks {
+    uint32_t c[64];
+};
+
+__global__ __launch_bounds__(64) void probe_gll_kernel(const uint32_t *__restrict__ src,
+                                                       LaneChunks chunks, uint32_t base,
+                                                       uint32_t *__restrict__ out) {
+    __shared__ __attribute__((aligned(16))) uint32_t lds[512];
+    const int l = threadIdx.x;
+    for (int i = l; i < 512; i += 64) lds[i] = 0;
+    __syncthreads();
+    __builtin_amdgcn_global_load_lds(
+        (const __attribute__((address_space(1))) void *)(src + 4 * chunks.c[l]),
+        (__attribute__((address_space(3))) void *)((__attribute__((address_space(3))) char *)lds + base),
+        16, 0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int i = l; i < 512; i += 64) out[i] = lds[i];
+}
+
 bool is_gfx950() {
     int dev = -1;
     hipDeviceProp_t p;
@@ -113,6 +133,22 @@ gemm355_status gemm355_probe_mfma(int kind, int nruns, const float *dev_a, const
     case 4: hipLaunchKernelGGL(probe_mfma_kernel<4>, grid, block, 0, stream, dev_a, dev_b, dev_d); break;
     default: hipLaunchKernelGGL(probe_mfma_kernel<5>, grid, block, 0, stream, dev_a, dev_b, dev_d); break;
     }
+    return hipGetLastError() == hipSuccess ? GEMM355_OK : GEMM355_ERR_LAUNCH;
+}
+
+gemm355_status gemm355_probe_global_load_lds(const uint32_t *dev_src, const uint32_t *host_src_chunk,
+                                             uint32_t lds_base, uint32_t *dev_out,
+                                             hipStream_t stream) {
+    if (!dev_src || !host_src_chunk || !dev_out || lds_base % 16 != 0 || lds_base > 1024)
+        return GEMM355_ERR_INVALID_ARG;
+    LaneChunks lc;
+    for (int l = 0; l < 64; ++l) {
+        if (host_src_chunk[l] > 4095) return GEMM355_ERR_INVALID_ARG;
+        lc.c[l] = host_src_chunk[l];
+    }
+    if (!is_gfx950()) return GEMM355_ERR_DEVICE;
+    hipLaunchKernelGGL(probe_gll_kernel, dim3(1), dim3(64), 0, stream, dev_src, lc, lds_base,
+                       dev_out);
     return hipGetLastError() == hipSuccess ? GEMM355_OK : GEMM355_ERR_LAUNCH;
 }
 

@@ -211,3 +211,41 @@ def test_ds_read_tr16_mapping_recorded():
         os.makedirs(out_dir, exist_ok=True)
         with open(os.path.join(out_dir, "ds_read_tr16_mapping.txt"), "w") as f:
             f.write(text + "\n")
+
+
+def gll_expected(chunks, base):
+    """The placement the direct-to-LDS tile loads rely on: lane l's 16 bytes, read from
+    16-byte chunk chunks[l] of the source, land at LDS bytes base + 16 l .. base + 16 l + 15
+    (the LDS address is the wave-uniform base plus 16 times the lane index)."""
+    out = np.zeros(512, np.int64)
+    for l, c in enumerate(chunks):
+        for i in range(4):
+            out[base // 4 + 4 * l + i] = 4 * c + i + 1
+    return out
+
+
+@pytest.mark.parametrize("pattern,base", [("linear", 0), ("reversed", 0), ("strided", 512),
+                                          ("linear", 1024), ("scattered", 256)])
+def test_global_load_lds_placement(pattern, base):
+    import torch
+    if pattern == "linear":
+        chunks = list(range(64))
+    elif pattern == "reversed":
+        chunks = [63 - l for l in range(64)]
+    elif pattern == "strided":
+        chunks = [37 * l for l in range(64)]
+    else:
+        chunks = np.random.default_rng(7).permutation(4096)[:64].tolist()
+    # source word w holds w + 1, so a zero in the output means "not written"
+    src = torch.arange(1, 4 * 4096 + 1, dtype=torch.int32, device="cuda")
+    out = torch.full((512,), -1, dtype=torch.int32, device="cuda")
+    st = gb.gemm355_probe_global_load_lds(src.data_ptr(), chunks, base, out.data_ptr(),
+                                          torch.cuda.current_stream().cuda_stream)
+    assert st == gb.OK
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.int64)
+    exp = gll_expected(chunks, base)
+    if not np.array_equal(got, exp):
+        where = {int(v): i for i, v in enumerate(got) if v > 0}
+        landed = [where.get(4 * c + 1, -1) for c in chunks]
+        pytest.fail(f"{pattern}/{base}: lane -> LDS word of its first element: {landed}")
