@@ -22,6 +22,12 @@
 //    j receives column n + j%16 for rows k .. k+3;
 //  * interior tiles (inside M x N, K a multiple of BK) run a straight-line kernel; the
 //    ragged strips run a predicated one that zero-fills loads and guards stores.
+//
+// Interior 256 x 256 tiles with K a multiple of 128 take a second design (dma_tile
+// below): the tiles go from memory straight into LDS (buffer_load_dwordx4 ... lds)
+// through a four-stage ring, so no registers stage them and no LDS store instructions
+// are issued; LDS rows are XOR-swizzled instead of padded.  It multiplies in the same
+// order as the register-staged kernel, so both give identical results.
 #include <type_traits>
 
 #include "common.hpp"
@@ -361,6 +367,264 @@ bool h16_vec(const GemmArgs &g) {
     return rows_aligned16(g.A, g.lda, 2) && rows_aligned16(g.B, g.ldb, 2);
 }
 
+// ---------------------------------------------------------------------------------
+// 256 x 256 interior tiles fed by direct global -> LDS loads.
+//
+// Data movement ("Kernel optimisation guide", Level 3 double buffering, extended to a
+// ring; the overlap of loads and arithmetic in the scheduling section of "Advanced
+// CUDA features - starting from GEMM"):
+//  * K is walked in steps of 32 through kNs = 4 LDS stages (32 KiB each: A 256 x 32
+//    and B 32 x 256, 16-bit); the loads of k-step t+3 are issued while step t is
+//    multiplied, into the stage step t-1 has released;
+//  * a load is buffer_load_dwordx4 with the lds flag: lane l's 16 bytes land at
+//    m0 + 16 l, so one instruction fills 1 KiB of LDS (16 rows of A or 2 rows of B)
+//    and the lane -> source mapping chooses where each 16-byte chunk goes;
+//  * A rows are 64 bytes, chunk c of row r stored in slot c ^ ((r / 4) % 4); B rows
+//    are 512 bytes, chunk c of row k in slot c ^ 4 (k % 4).  With these the fragment
+//    reads (ds_read_b128 for A, ds_read_b64_tr_b16 for B, as in the kernel above)
+//    touch 16 distinct 16-byte bank groups per 256 bytes, i.e. no bank conflicts,
+//    without padding (which a contiguous 1 KiB load cannot skip);
+//  * each wave waits for its own loads of step t+1 (vmcnt), then one barrier per
+//    k-step publishes the stage to all four waves.
+// The loads are issued from inline assembly (m0 holds the LDS destination), so the
+// compiler neither tracks them nor waits for them; the kernel's own s_waitcnt vmcnt
+// instructions do, and no other code of this kernel uses m0.
+namespace dma {
+
+constexpr int kBM = 256, kBN = 256, kBK = 32, kNs = 4;
+constexpr int kWM = 2, kWN = 2, kWaves = kWM * kWN;
+constexpr int kTM = kBM / kWM, kTN = kBN / kWN, kMB = kTM / 32, kNB = kTN / 32;
+constexpr int kStageA = kBM * kBK * 2;       // bytes
+constexpr int kStageB = kBK * kBN * 2;
+constexpr int kBOff = kNs * kStageA;         // the B ring follows the A ring
+constexpr int kLds = kNs * (kStageA + kStageB);
+constexpr int kAI = kStageA / 1024 / kWaves; // 1 KiB loads per wave per k-step
+constexpr int kBI = kStageB / 1024 / kWaves;
+constexpr int kLd = kAI + kBI;
+static_assert(kLds <= 160 * 1024, "LDS budget");
+// every ds_read immediate (stage + block offsets) stays below 64 KiB
+static_assert((kNs - 1) * kStageA + (kMB - 1) * 2048 < 65536, "A read offsets");
+static_assert((kNs - 1) * kStageB + 16 * 512 + 4 * 512 < 65536, "B read offsets");
+
+typedef int int4v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) char lds_char;
+
+// A raw buffer resource over `p` (2^31 - 1 bytes; the host checks every offset fits).
+__device__ __forceinline__ int4v rsrc_of(const void *p) {
+    const uint64_t a = (uint64_t)(uintptr_t)p;
+    int4v r;
+    r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+    r[2] = 0x7fffffff;
+    r[3] = 0x00020000;
+    return r;
+}
+
+// 16 bytes per lane from the buffer at voff + soff into LDS at lds_dst + 16 * lane.
+// m0 must be written right before the load; one wait state separates the two.
+__device__ __forceinline__ void load_lds16(uint32_t lds_dst, uint32_t voff, int4v rsrc,
+                                           uint32_t soff) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :: "s"(lds_dst), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+
+__device__ __forceinline__ lds_char *lds_reg(lds_char *p) {
+    uint32_t a = (uint32_t)(uintptr_t)p;
+    asm volatile("" : "+v"(a));
+    return (lds_char *)(uintptr_t)a;
+}
+
+template <typename T>
+__device__ __forceinline__ void dma_tile(int K, const uint16_t *__restrict__ A, int lda,
+                                         const uint16_t *__restrict__ B, int ldb,
+                                         float *__restrict__ C, int ldc, int m0, int n0,
+                                         char *lds_raw) {
+    const int lane = threadIdx.x % 64;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+    const int wm = wave / kWN, wn = wave % kWN;
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_char *)lds_raw;
+
+    // Loads.  A: wave w fills rows [16 kAI w, +16 kAI), instruction i rows 16 i + l/4,
+    // lane slot l%4 taking chunk (l%4) ^ ((l/16)%4).  B: wave w fills rows
+    // [2 kBI w, +2 kBI), instruction i rows 2 i + l/32, lane slot l%32 taking chunk
+    // slot ^ 4 (row % 4), where row % 4 = l/32 + 2 (i % 2).
+    const int4v ra = rsrc_of(A + (size_t)m0 * lda);
+    const int4v rb = rsrc_of(B + n0);
+    const int a_row = 16 * kAI * wave + lane / 4;
+    const int a_chunk = (lane & 3) ^ ((lane >> 4) & 3);
+    const uint32_t a_voff = (uint32_t)((a_row * lda + 8 * a_chunk) * 2);
+    const int b_row = 2 * kBI * wave + lane / 32;
+    const int b_slot = lane & 31;
+    const uint32_t b_voff[2] = {
+        (uint32_t)((b_row * ldb + 8 * (b_slot ^ (4 * (lane >> 5)))) * 2),
+        (uint32_t)((b_row * ldb + 8 * (b_slot ^ (4 * ((lane >> 5) + 2)))) * 2)};
+    auto issue = [&](int st, int k0, int w) {  // w < kAI: A instruction w, else B
+        if (w < kAI) {
+            load_lds16(lds0 + st * kStageA + (wave * kAI + w) * 1024, a_voff, ra,
+                       (uint32_t)((16 * w * lda + k0) * 2));
+        } else {
+            const int i = w - kAI;
+            load_lds16(lds0 + kBOff + st * kStageB + (wave * kBI + i) * 1024, b_voff[i & 1],
+                       rb, (uint32_t)((k0 + 2 * i) * ldb * 2));
+        }
+    };
+
+    // Fragments.  A (row wm kTM + 32 i + l%32, k 16 s + 8 (l/32) .. +7): chunk
+    // 2 s + l/32 of that row, whose swizzle key ((l%32)/4) % 4 does not depend on i.
+    // B (column wn kTN + 32 j + n, rows of one ds_read_b64_tr_b16 as in the kernel
+    // above): lane (g = l/16, e = (l%16)/4, q = l%4) reads row 16 s + 8 (g/2) + 4 h + e,
+    // chunk wn kTN/8 + 4 j + 2 (g%2) + q/2, byte 8 (q%2) of it; its slot is chunk ^ 4 e.
+    lds_char *const L = (lds_char *)lds_raw;
+    const int l32 = lane & 31, lhi = lane >> 5;
+    const int a_rowoff = (wm * kTM + l32) * 64;
+    lds_char *const a_rd[2] = {
+        lds_reg(L + a_rowoff + 16 * ((0 + lhi) ^ ((l32 >> 2) & 3))),
+        lds_reg(L + a_rowoff + 16 * ((2 + lhi) ^ ((l32 >> 2) & 3)))};
+    const int g = lane >> 4, e = (lane & 15) >> 2, q = lane & 3;
+    lds_char *b_rd[kNB];
+#pragma unroll
+    for (int j = 0; j < kNB; ++j)
+        b_rd[j] = lds_reg(L + kBOff + (8 * (g >> 1) + e) * 512 +
+                          16 * ((wn * (kTN / 8) + 4 * j + 2 * (g & 1) + (q >> 1)) ^ (4 * e)) +
+                          8 * (q & 1));
+
+    u16x8 af[2][kMB];
+    shortx4 bt[2][kNB][2];
+    auto read_piece = [&](int st, int s, int slot, int p) {
+        if (p < kMB) {
+            af[slot][p] = *(const lds_u16x8 *)(a_rd[s] + st * kStageA + p * 2048);
+        } else {
+            const int j = (p - kMB) / 2, h = (p - kMB) % 2;
+            bt[slot][j][h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_shortx4 *)(b_rd[j] + st * kStageB + 16 * s * 512 + 4 * h * 512));
+        }
+    };
+
+    floatx16 acc[kMB][kNB];
+#pragma unroll
+    for (int i = 0; i < kMB; ++i)
+#pragma unroll
+        for (int j = 0; j < kNB; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    auto mfma_one = [&](int slot, int qq) {
+        const int i = qq / kNB, j = qq % kNB;
+        const u16x8 b = __builtin_bit_cast(
+            u16x8, __builtin_shufflevector(bt[slot][j][0], bt[slot][j][1], 0, 1, 2, 3, 4, 5, 6, 7));
+        acc[i][j] = mfma32x32x16<T>(af[slot][i], b, acc[i][j]);
+    };
+
+    // One k-step on stage st: 2 sub-steps of kMf MFMAs.  Sub-step 0 reads the fragments
+    // of sub-step 1 two per MFMA; the kLd loads of k-step t+3 are spread one per two
+    // MFMAs over sub-step 0; after kPre MFMAs of sub-step 1 the wave waits for its
+    // loads of step t+1 (the 2 kLd younger ones may stay in flight) and the barrier
+    // publishes that stage; its first fragments are then read under the last MFMAs.
+    // No branches: near the end the loads repeat the last k-step into free stages.
+    constexpr int kR = kMB + 2 * kNB, kMf = kMB * kNB, kSlots = 2 * kMf;
+    constexpr int kPre = (kMf * 3 + 7) / 8;
+    constexpr int kBarrier = kMf + kPre;
+    constexpr int kLoadHi = kMf;
+    static_assert(kLoadHi <= kBarrier, "the furthest k-step's loads precede the wait");
+    auto ev_begin = [](int qs, int n, int lo, int hi) {
+        if (qs <= lo) return 0;
+        if (qs >= hi) return n;
+        return ((qs - lo) * n + (hi - lo) - 1) / (hi - lo);
+    };
+    const int nk = K / kBK;
+    auto kstep = [&](int kt, int st) {
+        const int st_next = (st + 1) % kNs;
+        const int st_load = (st + kNs - 1) % kNs;
+        const int kload = min(kt + kNs - 1, nk - 1) * kBK;
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+#pragma unroll
+            for (int qq = 0; qq < kMf; ++qq) {
+                const int qs = s * kMf + qq;
+                if (qs >= kBarrier) {
+                    const int lo = ev_begin(qs, kR, kBarrier, kSlots);
+                    const int hi = ev_begin(qs + 1, kR, kBarrier, kSlots);
+#pragma unroll
+                    for (int o = lo; o < hi; ++o) read_piece(st_next, 0, 0, o);
+                }
+                mfma_one(s, qq);
+                if (s == 0) {
+#pragma unroll
+                    for (int p = 2 * qq; p < 2 * qq + 2; ++p)
+                        if (p < kR) read_piece(st, 1, 1, p);
+                }
+                {
+                    const int lo = ev_begin(qs, kLd, 0, kLoadHi);
+                    const int hi = ev_begin(qs + 1, kLd, 0, kLoadHi);
+#pragma unroll
+                    for (int w = lo; w < hi; ++w) issue(st_load, kload, w);
+                }
+                if (qs == kBarrier - 1) {
+                    wait_vmcnt<kLd * (kNs - 2)>();
+                    __syncthreads();
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    };
+
+    // k-steps 0 .. kNs-2 in flight, wait for step 0, read its first fragments
+#pragma unroll
+    for (int p = 0; p < kNs - 1; ++p)
+#pragma unroll
+        for (int w = 0; w < kLd; ++w) issue(p, min(p, nk - 1) * kBK, w);
+    wait_vmcnt<kLd * (kNs - 2)>();
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < kR; ++p) read_piece(0, 0, 0, p);
+    for (int kt = 0; kt < nk; kt += kNs) {
+#pragma unroll
+        for (int u = 0; u < kNs; ++u) kstep(kt + u, u);
+    }
+    // nothing may still write this workgroup's LDS when it exits
+    wait_vmcnt<0>();
+
+#pragma unroll
+    for (int i = 0; i < kMB; ++i) {
+#pragma unroll
+        for (int j = 0; j < kNB; ++j) {
+            const int col = n0 + wn * kTN + 32 * j + l32;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = m0 + wm * kTM + 32 * i + 8 * (r / 4) + 4 * lhi + (r % 4);
+                __builtin_nontemporal_store(acc[i][j][r], C + (size_t)row * ldc + col);
+            }
+        }
+    }
+}
+
+}  // namespace dma
+
+template <typename T>
+__global__ __launch_bounds__(64 * dma::kWaves) __attribute__((amdgpu_waves_per_eu(1)))
+void mfma_f16_dma_kernel(int M, int N, int K, const uint16_t *__restrict__ A, int lda,
+                         const uint16_t *__restrict__ B, int ldb, float *__restrict__ C,
+                         int ldc) {
+    __shared__ __attribute__((aligned(1024))) char lds[dma::kLds];
+    int tm, tn;
+    grouped_tile(xcd_contiguous_id(blockIdx.x, gridDim.x), M / dma::kBM, N / dma::kBN, 4, tm, tn);
+    dma::dma_tile<T>(K, A, lda, B, ldb, C, ldc, tm * dma::kBM, tn * dma::kBN, lds);
+}
+
+// The direct-load kernel takes the interior tiles of a 256 x 256 configuration when
+// rows are 16-byte aligned, every byte offset fits the 31-bit buffer range and K is a
+// multiple of kNs k-steps.
+bool use_dma(const GemmArgs &g, int tile) {
+    return tile == dma::kBM && h16_vec(g) && g.K > 0 && g.K % (dma::kBK * dma::kNs) == 0 &&
+           g.M >= dma::kBM && g.N >= dma::kBN &&
+           ((long)dma::kBM * g.lda + g.K) * 2 < (1L << 31) &&
+           ((long)g.K * g.ldb + dma::kBN) * 2 < (1L << 31);
+}
+
 template <typename T, int BM, int BN, int WM, int WN, int MINW, int LOAD, bool EDGE, bool PAIRED>
 hipError_t launch_one(const GemmArgs &g, int tiles, int all_flag, hipStream_t s) {
     hipLaunchKernelGGL((mfma_f16_gemm_kernel<T, BM, BN, WM, WN, MINW, LOAD, EDGE, PAIRED>),
@@ -384,7 +648,12 @@ hipError_t launch_cfg(const GemmArgs &g, hipStream_t s) {
                       ((long)g.K * g.ldb + BN) * 2 < (1L << 31);
     if (full_tiles > 0) {
         hipError_t e;
-        if (vec && fits) {
+        if (use_dma(g, BM)) {
+            hipLaunchKernelGGL(mfma_f16_dma_kernel<T>, dim3(full_tiles), dim3(64 * dma::kWaves), 0, s,
+                               g.M, g.N, g.K, (const uint16_t *)g.A, g.lda, (const uint16_t *)g.B,
+                               g.ldb, g.C, g.ldc);
+            e = hipGetLastError();
+        } else if (vec && fits) {
             if ((g.K / kBK) % 2 == 0)
                 e = launch_one<T, BM, BN, WM, WN, MINW, 2, false, true>(g, full_tiles, all_flag, s);
             else
@@ -434,6 +703,8 @@ hipError_t launch_t(const GemmArgs &g, hipStream_t s) {
 const char *desc_mfma_f16(int dtype, const GemmArgs &g) {
     const bool v = h16_vec(g);
     const bool big = pick_tile(g) == 256;
+    if (big && use_dma(g, 256))
+        return dtype == kF16 ? "mfma_f16 256x256x32 w2x2 lds-dma" : "mfma_bf16 256x256x32 w2x2 lds-dma";
     if (dtype == kF16) {
         if (big) return v ? "mfma_f16 256x256x64 w2x2 dwordx4" : "mfma_f16 256x256x64 w2x2 u16";
         return v ? "mfma_f16 128x128x64 w2x2 dwordx4" : "mfma_f16 128x128x64 w2x2 u16";

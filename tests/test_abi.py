@@ -97,6 +97,13 @@ def test_dispatch_choices(lib):
     assert d(-1, 0, 4096, 4096, 4096, P, 4096, P, 4096, P, 4096).startswith("mfma_f32 128x128")
     assert d(-1, 1, 4096, 4096, 4096, P, 4096, P, 4096, P, 4096).startswith("mfma_f16")
     assert d(-1, 2, 4096, 4096, 4096, P, 4096, P, 4096, P, 4096).startswith("mfma_bf16")
+    # 256 x 256 interior tiles with K a multiple of 128 load straight into LDS; other K,
+    # unaligned rows and the 128-row tiles keep register staging
+    assert d(-1, 1, 4096, 4096, 4096, P, 4096, P, 4096, P, 4096) == "mfma_f16 256x256x32 w2x2 lds-dma"
+    assert d(-1, 2, 4096, 4096, 4096, P, 4096, P, 4096, P, 4096) == "mfma_bf16 256x256x32 w2x2 lds-dma"
+    assert d(-1, 1, 4096, 4096, 4160, P, 4160, P, 4096, P, 4096) == "mfma_f16 256x256x64 w2x2 dwordx4"
+    assert d(-1, 1, 4096, 4096, 4096, P + 2, 4096, P, 4096, P, 4096) == "mfma_f16 256x256x64 w2x2 u16"
+    assert d(-1, 1, 2048, 2048, 2048, P, 2048, P, 2048, P, 2048) == "mfma_f16 128x128x64 w2x2 dwordx4"
     # rows not 16-byte aligned (lda = 515 floats) take the dword load path
     assert d(-1, 0, 1023, 997, 515, P, 515, P, 997, P, 997).endswith("dword")
     assert d(-1, 0, 1000, 1000, 1000, P, 1000, P, 1000, P, 1000).endswith("dwordx4")

@@ -254,6 +254,46 @@ def test_h16_interior_instances(dtype, case):
     assert ok and np.array_equal(Ci, C32)
 
 
+# Interior 256 x 256 tiles with K a multiple of 128 run the direct-to-LDS kernel (the
+# cost model picks 256 x 256 tiles from about 2800^2 outputs): the shortest K (4
+# k-steps, one trip of the ring), 12 k-steps on a non-square grid, padded
+# 16-byte-aligned strides, and a long K.
+DMA_CASES = [((3072, 3072, 128), (0, 0, 0)), ((2816, 3072, 384), (0, 0, 0)),
+             ((3072, 2816, 256), (8, 16, 8)), ((3072, 3072, 2048), (0, 0, 0))]
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("case", DMA_CASES, ids=lambda c: "x".join(map(str, c[0])) + f"_pad{c[1][0]}")
+def test_h16_dma_instances(dtype, case):
+    (M, N, K), pad = case
+    A, B = inputs.make_operands(M, N, K, 44, "uniform", dtype)
+    code = gb.DTYPE_CODES[dtype]
+    lda, ldb, ldc = K + pad[0], N + pad[1], N + pad[2]
+    P = 1 << 20  # any 16-byte-aligned non-null address: the query only inspects it
+    assert "lds-dma" in gb.gemm355_kernel_desc(gb.VARIANT_MFMA, code, M, N, K, P, lda, P, ldb, P, ldc)
+    C64, _ = oracle.gemm(A, B, dtype)
+    C, ok = gpu_gemm(A, B, dtype, gb.VARIANT_MFMA, pad=pad, guard_rows=1)
+    check(C, C64, dtype, "uniform", K, ok, f"dma {dtype} {M}x{N}x{K} pad={pad}")
+    Ai, Bi = inputs.make_operands(M, N, K, 45, "int", dtype)
+    _, C32 = oracle.gemm(Ai, Bi, dtype)
+    Ci, ok = gpu_gemm(Ai, Bi, dtype, gb.VARIANT_MFMA, pad=pad)
+    assert ok and np.array_equal(Ci, C32)
+
+
+def test_h16_dma_interior_with_edges():
+    """4000^2: 15 x 15 interior tiles on the direct-to-LDS kernel, the ragged right and
+    bottom strips on the predicated kernel; rows sampled from both regions."""
+    M = N = 4000
+    K = 256
+    A, B = inputs.make_operands(M, N, K, 46, "uniform", "bf16")
+    P = 1 << 20
+    assert "lds-dma" in gb.gemm355_kernel_desc(gb.VARIANT_AUTO, gb.BF16, M, N, K, P, K, P, N, P, N)
+    C, ok = gpu_gemm(A, B, "bf16", entry="typed")
+    rows = np.array(sorted(set(sample_rows(M, 48).tolist()) | {3839, 3840, 3999}))
+    C64, _ = oracle.gemm(np.ascontiguousarray(A[rows]), B, "bf16")
+    check(C[rows], C64, "bf16", "uniform", K, ok, "dma+edge bf16 4000x4000x256 sampled")
+
+
 @pytest.mark.parametrize("case", [(384, 384, 64), (768, 384, 96), (384, 576, 3072)],
                          ids=lambda c: "x".join(map(str, c)))
 def test_f32_interior_instances(case):

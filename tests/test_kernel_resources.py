@@ -1,5 +1,6 @@
 """Every kernel instance compiles for gfx950 without register spills or scratch memory
-and without packed FP32 instructions (checked on the CPU with hipcc)."""
+and without packed FP32 instructions, and m0 is written only by the direct-to-LDS load
+sequences (checked on the CPU with hipcc)."""
 
 import concurrent.futures as cf
 import os
@@ -71,3 +72,37 @@ def test_no_packed_fp32_instructions():
     with cf.ThreadPoolExecutor(min(8, os.cpu_count() or 1)) as ex:
         for src, bad in ex.map(one, gbuild.sources()):
             assert not bad, (src, bad[:3])
+
+
+def test_m0_only_in_lds_load_sequences():
+    """The direct-to-LDS loads set m0 from inline assembly without declaring it: in every
+    kernel that contains such a sequence no other instruction may read or write m0, and
+    every m0 write is followed by one wait state and a buffer load with the lds flag."""
+    if not os.path.exists(HIPCC) and shutil.which("hipcc") is None:
+        pytest.skip("hipcc not available")
+    def one(src):
+        r = subprocess.run([HIPCC, *gbuild.HIPFLAGS, "--cuda-device-only", "-S", src, "-o", "-"],
+                           capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr[-2000:]
+        return src, r.stdout
+    kernels = 0
+    with cf.ThreadPoolExecutor(min(8, os.cpu_count() or 1)) as ex:
+        for src, asm in ex.map(one, gbuild.sources()):
+            for body in re.split(r"\n(?=_Z\S+:)", asm):
+                if "offen lds" not in body:
+                    continue
+                kernels += 1
+                lines = [ln.strip() for ln in body.splitlines()
+                         if ln.strip() and not ln.strip().startswith((";", ".", "//"))]
+                seqs = 0
+                for i, ln in enumerate(lines):
+                    if re.search(r"\bm0\b", ln):
+                        assert re.match(r"s_mov_b32 m0, s\d+$", ln), (src, ln)
+                        assert lines[i + 1] == "s_nop 0", (src, lines[i + 1])
+                        assert re.match(r"buffer_load_dwordx4 v\d+, s\[\d+:\d+\], s\d+ offen lds$",
+                                        lines[i + 2]), (src, lines[i + 2])
+                        seqs += 1
+                    elif ln.endswith(" lds"):
+                        assert lines[i - 1] == "s_nop 0", (src, ln)
+                assert seqs > 0
+    assert kernels >= 2
