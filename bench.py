@@ -178,6 +178,145 @@ def time_variant(variant, dtype, M, N, K, seed, reps=None):
     return e0.elapsed_time(e1) / reps, desc, reps
 
 
+def memory_slope_lines():
+    """Markdown lines for the memory-slope probe: HBM read bandwidth against resident waves
+    per CU and bytes in flight per wave, dependent-load latency, and the Little's-law
+    in-flight requirement that follows from them."""
+    import numpy as np
+    import torch
+
+    from roofline_optimisation_amd import binding as gb
+    from roofline_optimisation_amd import roofline as rl
+
+    stream = torch.cuda.Stream()
+    h = stream.cuda_stream
+    n_bytes = 2 << 30                      # 2 GiB: 8x the 256 MB MALL
+    src = torch.empty(n_bytes // 4, dtype=torch.int32, device="cuda")
+    src.random_()
+    part = torch.empty(1 << 16, dtype=torch.int32, device="cuda")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def read_rate(vec, unroll, threads, lds, grid, reps=4):
+        def go():
+            st = gb.gemm355_stream(gb.STREAM_READ_XOR, src.data_ptr(), part.data_ptr(), n_bytes,
+                                   vec, unroll, threads, lds, grid, h)
+            if st != gb.OK:
+                raise gb.Gemm355Error(st, "gemm355_stream")
+        go()
+        stream.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            go()
+        e1.record(stream)
+        stream.synchronize()
+        return n_bytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+
+    # resident waves per CU set by workgroup size and LDS reservation (160 KiB per CU)
+    occ = [(1, 64, 163840), (2, 128, 163840), (4, 256, 163840), (8, 256, 81920),
+           (16, 256, 40960), (32, 256, 20480)]
+    ilp = [(4, 1), (16, 1), (16, 4)]
+    rows, best = [], 0.0
+    for waves, threads, lds in occ:
+        wg_per_cu = 163840 // lds
+        grid = 256 * wg_per_cu
+        for vec, unroll in ilp:
+            gbps = read_rate(vec, unroll, threads, lds, grid)
+            inflight = waves * 64 * vec * unroll
+            rows.append((waves, vec, unroll, inflight, gbps))
+            best = max(best, gbps)
+            log(f"[report] stream read: {waves} waves/CU vec {vec} unroll {unroll}: {gbps:.0f} GB/s")
+
+    # copy (read + write) at the same occupancies, 16-byte vectors, one load in flight
+    dst = torch.empty_like(src)
+    copy_rows = []
+    for waves, threads, lds in occ:
+        grid = 256 * (163840 // lds)
+        def go():
+            st = gb.gemm355_stream(gb.STREAM_COPY, src.data_ptr(), dst.data_ptr(), n_bytes, 16, 1,
+                                   threads, lds, grid, h)
+            if st != gb.OK:
+                raise gb.Gemm355Error(st, "gemm355_stream")
+        go()
+        stream.synchronize()
+        e0.record(stream)
+        for _ in range(3):
+            go()
+        e1.record(stream)
+        stream.synchronize()
+        gbps = 2 * n_bytes * 3 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+        copy_rows.append((waves, gbps))
+        log(f"[report] stream copy: {waves} waves/CU: {gbps:.0f} GB/s (read + write)")
+    del dst
+
+    # dependent-load latency: one lane walks a random cycle through stride-aligned word
+    # positions of a table; `warm` walks the whole cycle first, `flush` streams the 2 GiB
+    # source first so that no level of cache holds the table
+    def chase(table_bytes, nodes, stride, hops, warm=False, flush=False):
+        nw = table_bytes // 4
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(5)
+        pos = torch.randperm(nw // stride, device="cuda", generator=gen)[:nodes].to(torch.int64) * stride
+        table = torch.zeros(nw, dtype=torch.int32, device="cuda")
+        table[pos] = torch.roll(pos, -1).to(torch.int32)
+        out = torch.zeros(2, dtype=torch.int64, device="cuda")
+        start = int(pos[0])
+        def walk(k):
+            st = gb.gemm355_chase(table.data_ptr(), nw, start, k, out.data_ptr(), h)
+            if st != gb.OK:
+                raise gb.Gemm355Error(st, "gemm355_chase")
+        res = []
+        for _ in range(3):
+            if warm:
+                walk(nodes)
+            if flush:
+                read_rate(16, 1, 256, 20480, 2048, reps=1)
+            e0.record(stream)
+            walk(hops)
+            e1.record(stream)
+            stream.synchronize()
+            res.append((e0.elapsed_time(e1) * 1e6 / hops, int(out[1].item()) / hops))
+        del table
+        return min(res)
+    lat_l2 = chase(64 << 20, 2048, 1024, 4000, warm=True)           # 256 KB of lines
+    lat_mall = chase(64 << 20, 65536, 256, 65536, warm=True)        # 8 MB of lines > L2
+    lat_hbm = chase(2 << 30, 65536, 1024, 4000, flush=True)
+    for name, lat in (("L2", lat_l2), ("MALL", lat_mall), ("HBM", lat_hbm)):
+        log(f"[report] chase {name}: {lat[0]:.0f} ns/hop {lat[1]:.0f} cycles")
+
+    need = best * 1e9 * lat_hbm[0] * 1e-9                     # bytes in flight (chip)
+    clock_ghz = lat_hbm[1] / lat_hbm[0]
+    need_cycles = rl.littles_law_bytes(lat_hbm[1], best * 1e9, clock_ghz * 1e9)
+    sat = min((r for r in rows if r[4] >= 0.9 * best), key=lambda r: r[3])
+    lines = ["", "## Memory slope (Little's law and occupancy probe)", "",
+             "HBM read bandwidth of `gemm355_stream` (mode READ_XOR) over a 2 GiB source (8x the 256 MB",
+             "MALL), against resident waves per CU (set by workgroup size and LDS reservation out of",
+             "160 KiB per CU) and bytes in flight per wave (64 lanes x vector bytes x loads issued before",
+             "first use).  Mean of 4 passes after one warm pass.", "",
+             "| waves/CU | occupancy (of 32) | vec B | loads in flight | in-flight B per CU | GB/s | % of 8 TB/s |",
+             "|---|---|---|---|---|---|---|"]
+    for waves, vec, unroll, inflight, gbps in rows:
+        lines.append(f"| {waves} | {100 * waves / 32:.1f} % | {vec} | {unroll} | {inflight} | {gbps:.0f} | "
+                     f"{100 * gbps / 8000:.1f} |")
+    lines += ["", "Copy (`gemm355_stream` mode COPY, 16-byte vectors, one load in flight per lane; read + write bytes):", "",
+              "| waves/CU | occupancy (of 32) | GB/s (read + write) | % of best |", "|---|---|---|---|"]
+    cbest = max(g for _, g in copy_rows)
+    for waves, gbps in copy_rows:
+        lines.append(f"| {waves} | {100 * waves / 32:.1f} % | {gbps:.0f} | {100 * gbps / cbest:.0f} % |")
+    lines += ["", "Dependent-load latency (`gemm355_chase`: one lane walks a random cycle; minimum of 3 runs):", "",
+              "| level | table, cycle | preparation | ns per hop | shader cycles per hop |", "|---|---|---|---|---|",
+              f"| L2 | 64 MiB, 2048 nodes (256 KB of lines), 4000 hops | one warm walk | {lat_l2[0]:.0f} | {lat_l2[1]:.0f} |",
+              f"| MALL | 64 MiB, 65536 nodes (8 MB of lines > 4 MB L2), 65536 hops | one warm walk | {lat_mall[0]:.0f} | {lat_mall[1]:.0f} |",
+              f"| HBM | 2 GiB, 65536 nodes 4 KiB apart, 4000 hops | 2 GiB streamed first | {lat_hbm[0]:.0f} | {lat_hbm[1]:.0f} |", "",
+              f"Little's law with these numbers: best measured read rate {best:.0f} GB/s x HBM latency "
+              f"{lat_hbm[0]:.0f} ns = {need / 1e6:.2f} MB in flight for the chip "
+              f"({need / 256 / 1e3:.1f} KB per CU; {need_cycles / 1e6:.2f} MB by the page's cycles x "
+              f"bytes-per-cycle form at the chase's {clock_ghz:.2f} GHz).  The smallest configuration "
+              f"within 90 % of the best rate: {sat[0]} waves/CU with {sat[3]} B in flight per CU "
+              f"({sat[3] * 256 / 1e6:.2f} MB for the chip), {sat[4]:.0f} GB/s."]
+    del src
+    return lines
+
+
 def write_report(path):
     from roofline_optimisation_amd import inputs
     from roofline_optimisation_amd import roofline as rl
@@ -209,6 +348,7 @@ def write_report(path):
         lines.append(f"| {c.dtype} | {c.M}x{c.N}x{c.K} | {desc} | {ms * 1e3:.1f} | {tf:.1f} | "
                      f"{100 * e['frac']:.1f} | {e['oi']:.1f} | {e['attainable_tflops']:.0f} | {bound} |")
         log(f"[report] {c.name}: {ms * 1e3:.1f} us {tf:.1f} TFLOP/s")
+    lines += memory_slope_lines()
     with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")
 
@@ -225,6 +365,10 @@ def main():
                     help="also time every kernel family on the 256^3 and 3072^3 FP32 workloads "
                          "and the square FP32/BF16 sweep plus the tall-skinny shape, and write a "
                          "markdown table to PATH (the JSON line is unchanged)")
+    ap.add_argument("--memory-slope", default=None, metavar="PATH",
+                    help="only run the memory-slope probe (HBM read rate against occupancy and "
+                         "bytes in flight, dependent-load latency) and write its markdown table "
+                         "to PATH; no GEMM timing, no JSON line")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after the GEMMs, copy this many MiB device-to-device once (a plain "
                          "copy of known size, used to scale the HBM byte counters)")
@@ -243,6 +387,13 @@ def main():
         sys.exit(1)
 
     from roofline_optimisation_amd import roofline as rl
+
+    if args.memory_slope:
+        lines = ["# libgemm355 memory-slope probe on one MI355X"] + memory_slope_lines()
+        with open(args.memory_slope, "w") as f:
+            f.write("\n".join(lines) + "\n")
+        log(f"[bench] memory-slope table written to {args.memory_slope}")
+        return
 
     results = {}
     for kind, n, seed in (("f32", 3072, 1), ("f16", 4096, 3)):

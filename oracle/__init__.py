@@ -1,4 +1,5 @@
-"""CPU oracle for the dense GEMM C = A.B (plain C, fp64 accumulation, i-k-j loop).
+"""CPU oracle for the dense GEMM C = A.B (plain C, fp64 accumulation, i-k-j loop), and
+for the memory-slope probes (XOR of a word stream, a dependent-index walk).
 
 TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
 bench's ``cpu_baseline`` leg may import this package.  It never imports the GPU
@@ -14,6 +15,10 @@ matrices, small-integer inputs against exact integer products, exact rational br
 force for every M, N, K in 1..8, the transpose identity, stride handling with
 NaN-filled padding, the error bound against an independent binary64 matrix product,
 exhaustive fp16/bf16 decoding against numpy, and planted mistakes that the pins catch.
+The probe functions (``stream_xor``, ``chase``; "Advanced CUDA features - starting from
+GEMM", section on Little's law and occupancy) are pinned in ``tests/test_oracle_stream.py``:
+the closed form of the XOR of 0..n-1, per-bit parity counts, successor and permutation
+cycles with closed-form positions, and the out-of-range clamp.
 """
 
 from __future__ import annotations
@@ -44,6 +49,10 @@ def _configure(lib):
     lib.oracle_bf16_to_f64.restype = ctypes.c_double
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = i
+    lib.oracle_xor_words.argtypes = [vp, ctypes.c_int64]
+    lib.oracle_xor_words.restype = ctypes.c_uint32
+    lib.oracle_chase.argtypes = [vp, ctypes.c_int64, ctypes.c_uint32, ctypes.c_int64]
+    lib.oracle_chase.restype = ctypes.c_uint32
     return lib
 
 
@@ -121,3 +130,21 @@ def f16_to_f64(bits: int) -> float:
 
 def bf16_to_f64(bits: int) -> float:
     return _load().oracle_bf16_to_f64(int(bits))
+
+
+def stream_xor(words: np.ndarray, lib=None) -> int:
+    """XOR of all 32-bit words of `words` (any shape, viewed as uint32)."""
+    lib = lib or _load()
+    w = np.ascontiguousarray(words).view(np.uint32).reshape(-1)
+    return int(lib.oracle_xor_words(w.ctypes.data if w.size else None, w.size))
+
+
+def chase(next_words: np.ndarray, start: int, hops: int, n: int | None = None, lib=None) -> int:
+    """The index reached from `start` after `hops` steps cur = next[cur] over the first
+    `n` words of `next_words` (default all), an index outside [0, n) replaced by n - 1."""
+    lib = lib or _load()
+    w = np.ascontiguousarray(next_words, dtype=np.uint32).reshape(-1)
+    n = w.size if n is None else int(n)
+    if not (1 <= n <= w.size) or not (0 <= start < n) or hops < 0:
+        raise ValueError("chase: need 1 <= n <= len(next), 0 <= start < n, hops >= 0")
+    return int(lib.oracle_chase(w.ctypes.data, n, start, hops))

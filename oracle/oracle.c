@@ -173,3 +173,29 @@ int oracle_gemm_bf16(int M, int N, int K, const uint16_t *A, int lda, const uint
 {
     return gemm_typed(M, N, K, A, lda, B, ldb, C64, C32, ldc, dec_bf16);
 }
+
+/* ------------------------------------------------------------------------------------
+ * Memory-slope probes ("Advanced CUDA features - starting from GEMM", section on
+ * Little's law and occupancy).  The probes only move data; what they must produce is
+ * fixed by definition and written out here.
+ */
+
+/* XOR of the n 32-bit words w[0..n). */
+uint32_t oracle_xor_words(const uint32_t *w, int64_t n)
+{
+    uint32_t x = 0;
+    for (int64_t i = 0; i < n; ++i) x ^= w[i];
+    return x;
+}
+
+/* The word index reached from `start` after `hops` dependent steps cur = next[cur] over
+ * a table of n words, where a loaded index outside [0, n) is replaced by n - 1. */
+uint32_t oracle_chase(const uint32_t *next, int64_t n, uint32_t start, int64_t hops)
+{
+    uint32_t cur = start;
+    for (int64_t h = 0; h < hops; ++h) {
+        const uint32_t v = next[cur];
+        cur = (int64_t)v < n ? v : (uint32_t)(n - 1);
+    }
+    return cur;
+}

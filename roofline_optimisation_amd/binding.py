@@ -29,8 +29,10 @@ EXPORTS = (
     "gemm355_select_variant", "gemm355_kernel_desc", "gemm355_status_string",
     "gemm355_variant_name", "gemm355_version",
     "gemm355_probe_mfma_shape", "gemm355_probe_mfma", "gemm355_probe_ds_read_tr16",
-    "gemm355_probe_global_load_lds",
+    "gemm355_probe_global_load_lds", "gemm355_stream", "gemm355_chase",
 )
+
+STREAM_COPY, STREAM_READ_XOR = 0, 1
 
 
 class Gemm355Error(RuntimeError):
@@ -70,6 +72,11 @@ def _configure(lib):
     lib.gemm355_probe_global_load_lds.argtypes = [p, ctypes.POINTER(ctypes.c_uint32),
                                                   ctypes.c_uint32, p, p]
     lib.gemm355_probe_global_load_lds.restype = i
+    i64 = ctypes.c_int64
+    lib.gemm355_stream.argtypes = [i, p, p, i64, i, i, i, i, i, p]
+    lib.gemm355_stream.restype = i
+    lib.gemm355_chase.argtypes = [p, i64, ctypes.c_uint32, i, p, p]
+    lib.gemm355_chase.restype = i
     return lib
 
 
@@ -141,6 +148,16 @@ def gemm355_probe_ds_read_tr16(host_addrs, dev_out, stream=0) -> int:
 def gemm355_probe_global_load_lds(dev_src, host_chunks, lds_base, dev_out, stream=0) -> int:
     arr = (ctypes.c_uint32 * 64)(*[int(c) for c in host_chunks])
     return lib().gemm355_probe_global_load_lds(dev_src, arr, int(lds_base), dev_out, stream)
+
+
+def gemm355_stream(mode, src, dst, n_bytes, vec_bytes, unroll, threads, lds_bytes, grid,
+                   stream=0) -> int:
+    return lib().gemm355_stream(mode, src, dst, n_bytes, vec_bytes, unroll, threads, lds_bytes,
+                                grid, stream)
+
+
+def gemm355_chase(next_words, n_words, start, hops, dev_out, stream=0) -> int:
+    return lib().gemm355_chase(next_words, n_words, start, hops, dev_out, stream)
 
 
 def status_string(status: int) -> str:

@@ -89,6 +89,8 @@ gemm355_status run(int variant, int dtype, int M, int N, int K, const void *A, i
 
 }  // namespace
 
+bool current_device_is_gfx950() { return device_ok(); }
+
 }  // namespace g355
 
 using namespace g355;

@@ -22,6 +22,9 @@ const char *desc_regblock_f32(const GemmArgs &g);
 const char *desc_mfma_f32(const GemmArgs &g);
 const char *desc_mfma_f16(int dtype, const GemmArgs &g);
 
+// True when the current HIP device is a gfx950 (queried once per device).
+bool current_device_is_gfx950();
+
 // True when every row of a row-major matrix starts on a 16-byte boundary, i.e. the
 // base is 16-byte aligned and the row stride is a multiple of 16 bytes.
 inline bool rows_aligned16(const void *p, int ld, int elem_bytes) {

@@ -10,7 +10,7 @@ import pytest
 from roofline_optimisation_amd import binding as gb
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADERS = [os.path.join(ROOT, "include", h) for h in ("gemm355.h", "gemm355_probe.h")]
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("gemm355.h", "gemm355_probe.h", "gemm355_stream.h")]
 
 
 def declared_functions():
@@ -130,6 +130,33 @@ def test_probe_argument_checks(lib):
     assert gb.gemm355_probe_mfma(0, 0, P, P, P) == gb.ERR_INVALID_ARG
     assert gb.gemm355_probe_ds_read_tr16([8 * i for i in range(63)] + [4], P) == gb.ERR_INVALID_ARG
     assert gb.gemm355_probe_ds_read_tr16([8 * i for i in range(63)] + [4096], P) == gb.ERR_INVALID_ARG
+
+
+def test_stream_and_chase_argument_checks(lib):
+    ok = dict(mode=gb.STREAM_COPY, src=P, dst=P + (1 << 20), n_bytes=4096, vec_bytes=16, unroll=4,
+              threads=256, lds_bytes=0, grid=256)
+    def st(**kw):
+        a = dict(ok, **kw)
+        return gb.gemm355_stream(a["mode"], a["src"], a["dst"], a["n_bytes"], a["vec_bytes"],
+                                 a["unroll"], a["threads"], a["lds_bytes"], a["grid"])
+    bad = [dict(mode=2), dict(n_bytes=-4), dict(n_bytes=6), dict(vec_bytes=12), dict(unroll=3),
+           dict(threads=32), dict(threads=96), dict(threads=2048), dict(lds_bytes=-1),
+           dict(lds_bytes=163841), dict(grid=0), dict(grid=(1 << 20) + 1), dict(src=0),
+           dict(dst=0), dict(src=P + 4), dict(dst=P + 8 + (1 << 20)),
+           dict(dst=P + 1024),                      # overlaps the source
+           dict(mode=gb.STREAM_READ_XOR, dst=0), dict(mode=gb.STREAM_READ_XOR, dst=P + 2)]
+    for b in bad:
+        assert st(**b) == gb.ERR_INVALID_ARG, b
+    # an empty copy needs no buffers; a READ_XOR always writes its grid entries
+    assert st(n_bytes=0, src=0, dst=0) in (gb.OK, gb.ERR_DEVICE)
+    C = gb.gemm355_chase
+    assert C(0, 16, 0, 1, P) == gb.ERR_INVALID_ARG
+    assert C(P, 16, 0, 1, 0) == gb.ERR_INVALID_ARG
+    assert C(P, 0, 0, 1, P) == gb.ERR_INVALID_ARG
+    assert C(P, (1 << 32) + 1, 0, 1, P) == gb.ERR_INVALID_ARG
+    assert C(P, 16, 16, 1, P) == gb.ERR_INVALID_ARG
+    assert C(P, 16, 0, 0, P) == gb.ERR_INVALID_ARG
+    assert C(P, 16, 0, (1 << 30) + 1, P) == gb.ERR_INVALID_ARG
 
 
 def test_matmul_refuses_cpu_tensors(lib):
