@@ -34,7 +34,8 @@ sys.path.insert(0, ROOT)
 PEAKS = {"f32": 157.3, "f16": 2516.6, "bf16": 2516.6}  # TFLOP/s, dense, 2.4 GHz
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "roofline_optimisation_amd", "csrc")
-KERNEL_SOURCES = {"f32": ["k_mfma_f32.hip", "common.hpp"], "f16": ["k_mfma_f16.hip", "common.hpp"]}
+KERNEL_SOURCES = {"f32": ["k_mfma_f32.hip", "f32_gemm.hpp", "common.hpp"],
+                  "f16": ["k_mfma_f16.hip", "h16_gemm.hpp", "common.hpp"]}
 PMC_FILES = {"f32": "pmc_mfma_f32_n3072.txt", "f16": "pmc_mfma_f16_n4096.txt"}
 
 

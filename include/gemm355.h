@@ -105,6 +105,38 @@ gemm355_status gemm355_run_variant(int variant, int dtype, int M, int N, int K, 
                                    int lda, const void *B, int ldb, float *C, int ldc,
                                    hipStream_t stream);
 
+/* Operand forms of gemm355_gemm_ex (bit flags).  The tensor-core instruction table of
+ * "Advanced CUDA features - starting from GEMM" lists, for its warp-group MMA, D = A*B + D
+ * with transposed or negated A and B and D scaled by 0 or 1; these flags provide that
+ * operation on top of the same kernels. */
+enum {
+    GEMM355_TRANS_A = 1,     /* op(A) = A^T: A is stored K x M (element (k,i) at A[k*lda+i]) */
+    GEMM355_TRANS_B = 2,     /* op(B) = B^T: B is stored N x K (element (j,k) at B[j*ldb+k]) */
+    GEMM355_NEG_A = 4,       /* use -op(A) */
+    GEMM355_NEG_B = 8,       /* use -op(B) */
+    GEMM355_ACCUMULATE = 16  /* D scaled by 1 (C += ...) instead of 0 (C = ...) */
+};
+
+/* C = (+-op(A)) (+-op(B)) [+ C]:
+ *
+ *     C[i][j] = s * sum_k op(A)[i][k] op(B)[k][j]  (+ C[i][j] when GEMM355_ACCUMULATE)
+ *
+ * with s = -1 when exactly one of GEMM355_NEG_A, GEMM355_NEG_B is set, else +1, op(A)
+ * M x K and op(B) K x N.  Leading dimensions are those of the stored matrices: lda >=
+ * max(1, K) (max(1, M) with GEMM355_TRANS_A), ldb >= max(1, N) (max(1, K) with
+ * GEMM355_TRANS_B), ldc >= max(1, N).  `variant` and `dtype` as for gemm355_run_variant;
+ * with any flag set only NAIVE, MFMA and AUTO (= MFMA) are available (others return
+ * GEMM355_ERR_UNSUPPORTED).  Unknown flag bits are GEMM355_ERR_INVALID_ARG.
+ * Accumulation: the MFMA kernels add s * (their FP32 sum) to the old C in the epilogue,
+ * the naive kernel likewise, one rounding each.  K = 0: C = +0.0 without
+ * GEMM355_ACCUMULATE (then negated when s = -1), C unchanged with it.  A negated
+ * product without GEMM355_ACCUMULATE on MFMA runs a second, elementwise kernel that
+ * negates C on the same stream.  Everything else (ownership, asynchrony, errors) as
+ * for gemm_f32. */
+gemm355_status gemm355_gemm_ex(int variant, int dtype, unsigned flags, int M, int N, int K,
+                               const void *A, int lda, const void *B, int ldb, float *C, int ldc,
+                               hipStream_t stream);
+
 /* Host-only: the family the typed entry points would launch for these arguments, or -1
  * if the arguments are invalid.  Makes no HIP call. */
 int gemm355_select_variant(int dtype, int M, int N, int K, const void *A, int lda, const void *B,

@@ -15,7 +15,8 @@ matrices, small-integer inputs against exact integer products, exact rational br
 force for every M, N, K in 1..8, the transpose identity, stride handling with
 NaN-filled padding, the error bound against an independent binary64 matrix product,
 exhaustive fp16/bf16 decoding against numpy, and planted mistakes that the pins catch.
-The probe functions (``stream_xor``, ``chase``; "Advanced CUDA features - starting from
+``gemm_ex`` (transposed / negated operands, accumulation into C) is pinned in
+``tests/test_oracle_ex.py``.  The probe functions (``stream_xor``, ``chase``; "Advanced CUDA features - starting from
 GEMM", section on Little's law and occupancy) are pinned in ``tests/test_oracle_stream.py``:
 the closed form of the XOR of 0..n-1, per-bit parity counts, successor and permutation
 cycles with closed-form positions, and the out-of-range clamp.
@@ -49,6 +50,8 @@ def _configure(lib):
     lib.oracle_bf16_to_f64.restype = ctypes.c_double
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = i
+    lib.oracle_gemm_ex.argtypes = [i, i, i, i, i, i, i, i, i, vp, i, vp, i, vp, dp, fp, i]
+    lib.oracle_gemm_ex.restype = i
     lib.oracle_xor_words.argtypes = [vp, ctypes.c_int64]
     lib.oracle_xor_words.restype = ctypes.c_uint32
     lib.oracle_chase.argtypes = [vp, ctypes.c_int64, ctypes.c_uint32, ctypes.c_int64]
@@ -121,6 +124,45 @@ def gemm(A: np.ndarray, B: np.ndarray, dtype: str = "f32", lib=None):
                              C64.ctypes.data, C32.ctypes.data, max(N, 1))
     if rc != 0:
         raise RuntimeError(f"{fname} failed ({rc})")
+    return C64, C32
+
+
+_DT = {"f32": (np.float32, 0), "f16": (np.uint16, 1), "bf16": (np.uint16, 2)}
+
+
+def gemm_ex(A: np.ndarray, B: np.ndarray, dtype: str = "f32", trans_a: bool = False,
+            trans_b: bool = False, neg_a: bool = False, neg_b: bool = False,
+            C_in: np.ndarray | None = None, lib=None):
+    """(C64, C32) of C = s op(A) op(B) (+ C_in), s = -1 when exactly one operand is
+    negated ("Advanced CUDA features - starting from GEMM", tensor-core instruction
+    table).  ``A`` and ``B`` are the stored matrices: A is M x K, or K x M when
+    trans_a; B is K x N, or N x K when trans_b.  ``C_in`` (float32 M x N) is added when
+    given."""
+    np_t, code = _DT[dtype]
+    if A.dtype != np_t or B.dtype != np_t:
+        raise TypeError(f"{dtype} oracle expects {np.dtype(np_t)} operands")
+    M, K = (A.shape[1], A.shape[0]) if trans_a else A.shape
+    KB, N = (B.shape[1], B.shape[0]) if trans_b else B.shape
+    if KB != K:
+        raise ValueError("inner dimensions differ")
+    A = np.ascontiguousarray(A)
+    B = np.ascontiguousarray(B)
+    lda = max(A.shape[1], 1)
+    ldb = max(B.shape[1], 1)
+    C64 = np.zeros((M, N), dtype=np.float64)
+    C32 = np.zeros((M, N), dtype=np.float32)
+    cin = None
+    if C_in is not None:
+        cin = np.ascontiguousarray(C_in, dtype=np.float32)
+        if cin.shape != (M, N):
+            raise ValueError("C_in must be M x N")
+    lib = lib or _load()
+    rc = lib.oracle_gemm_ex(code, int(trans_a), int(trans_b), int(neg_a), int(neg_b),
+                            int(cin is not None), M, N, K, A.ctypes.data, lda, B.ctypes.data, ldb,
+                            None if cin is None else cin.ctypes.data, C64.ctypes.data,
+                            C32.ctypes.data, max(N, 1))
+    if rc != 0:
+        raise RuntimeError(f"oracle_gemm_ex failed ({rc})")
     return C64, C32
 
 

@@ -175,6 +175,68 @@ int oracle_gemm_bf16(int M, int N, int K, const uint16_t *A, int lda, const uint
 }
 
 /* ------------------------------------------------------------------------------------
+ * The operation of the tensor-core instruction table of "Advanced CUDA features -
+ * starting from GEMM" (its warp-group MMA row: D = A*B + D, A and B optionally
+ * transposed or negated, D scaled by 0 or 1), written out:
+ *
+ *     C[i][j] = s * sum_k op(A)[i][k] op(B)[k][j]  (+ Cin[i][j] when accumulate)
+ *
+ * op(A) is the stored M x K matrix A, or (trans_a) the transpose of the stored K x M
+ * matrix: op(A)[i][k] = A[k*lda + i]; op(B) is the stored K x N matrix or (trans_b) the
+ * transpose of the stored N x K matrix: op(B)[k][j] = B[j*ldb + k].  s = -1 when
+ * exactly one of neg_a, neg_b is nonzero, else +1.  The sum is taken in binary64 by
+ * oracle_gemm_f64 on op(A), op(B) widened exactly; then s * sum + Cin in binary64; C32
+ * is that value rounded once to binary32.  Cin (binary32, row stride ldc) is read only
+ * when accumulate.  dtype: 0 binary32, 1 binary16 bits, 2 bfloat16 bits.
+ */
+
+/* op(X) as a packed rows x cols binary64 array: element (r, c) of the stored matrix
+ * (row stride ld), or of its transpose when trans. */
+static double *widen_op(const void *src, int rows, int cols, int ld, int trans, decode_fn dec)
+{
+    size_t n = (size_t)rows * (size_t)cols;
+    double *out = (double *)malloc(sizeof(double) * (n ? n : 1));
+    if (!out) return NULL;
+#pragma omp parallel for schedule(static)
+    for (int r = 0; r < rows; ++r)
+        for (int c = 0; c < cols; ++c)
+            out[(size_t)r * cols + c] =
+                trans ? dec(src, (size_t)c * ld + r) : dec(src, (size_t)r * ld + c);
+    return out;
+}
+
+int oracle_gemm_ex(int dtype, int trans_a, int trans_b, int neg_a, int neg_b, int accumulate,
+                   int M, int N, int K, const void *A, int lda, const void *B, int ldb,
+                   const float *Cin, double *C64, float *C32, int ldc)
+{
+    decode_fn dec = dtype == 0 ? dec_f32 : dtype == 1 ? dec_f16 : dtype == 2 ? dec_bf16 : NULL;
+    if (!dec || M < 0 || N < 0 || K < 0) return -1;
+    const int min_lda = trans_a ? M : K, min_ldb = trans_b ? K : N;
+    if (lda < (min_lda > 1 ? min_lda : 1) || ldb < (min_ldb > 1 ? min_ldb : 1) ||
+        ldc < (N > 1 ? N : 1))
+        return -1;
+    if (M == 0 || N == 0) return 0;
+    if (accumulate && !Cin) return -1;
+    double *a = widen_op(A, M, K, lda, trans_a, dec);
+    double *b = widen_op(B, K, N, ldb, trans_b, dec);
+    int rc = -1;
+    if (a && b)
+        rc = oracle_gemm_f64(M, N, K, a, K > 0 ? K : 1, b, N, C64, NULL, ldc);
+    free(a);
+    free(b);
+    if (rc != 0) return rc;
+    const double s = ((neg_a != 0) != (neg_b != 0)) ? -1.0 : 1.0;
+    for (int i = 0; i < M; ++i)
+        for (int j = 0; j < N; ++j) {
+            double v = s * C64[(size_t)i * ldc + j];
+            if (accumulate) v += (double)Cin[(size_t)i * ldc + j];
+            C64[(size_t)i * ldc + j] = v;
+            if (C32) C32[(size_t)i * ldc + j] = (float)v;
+        }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------------------
  * Memory-slope probes ("Advanced CUDA features - starting from GEMM", section on
  * Little's law and occupancy).  The probes only move data; what they must produce is
  * fixed by definition and written out here.

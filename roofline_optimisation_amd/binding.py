@@ -22,12 +22,13 @@ VARIANT_AUTO, VARIANT_NAIVE, VARIANT_LDS_TILED, VARIANT_REGBLOCK, VARIANT_MFMA =
 VARIANTS = {"naive": VARIANT_NAIVE, "lds_tiled": VARIANT_LDS_TILED,
             "regblock": VARIANT_REGBLOCK, "mfma": VARIANT_MFMA, "auto": VARIANT_AUTO}
 DTYPE_CODES = {"f32": F32, "f16": F16, "bf16": BF16}
+TRANS_A, TRANS_B, NEG_A, NEG_B, ACCUMULATE = 1, 2, 4, 8, 16
 
 # Every symbol the public headers declare.
 EXPORTS = (
     "gemm_f32", "gemm_f16f32acc", "gemm_bf16f32acc", "gemm355_run_variant",
     "gemm355_select_variant", "gemm355_kernel_desc", "gemm355_status_string",
-    "gemm355_variant_name", "gemm355_version",
+    "gemm355_variant_name", "gemm355_version", "gemm355_gemm_ex",
     "gemm355_probe_mfma_shape", "gemm355_probe_mfma", "gemm355_probe_ds_read_tr16",
     "gemm355_probe_global_load_lds", "gemm355_stream", "gemm355_chase",
 )
@@ -53,6 +54,8 @@ def _configure(lib):
         f.restype = i
     lib.gemm355_run_variant.argtypes = [i, i] + gemm_args
     lib.gemm355_run_variant.restype = i
+    lib.gemm355_gemm_ex.argtypes = [i, i, ctypes.c_uint] + gemm_args
+    lib.gemm355_gemm_ex.restype = i
     lib.gemm355_select_variant.argtypes = [i, i, i, i, p, i, p, i, p, i]
     lib.gemm355_select_variant.restype = i
     lib.gemm355_kernel_desc.argtypes = [i, i, i, i, i, p, i, p, i, p, i]
@@ -107,6 +110,10 @@ def gemm_bf16f32acc(M, N, K, A, lda, B, ldb, C, ldc, stream=0) -> int:
 
 def gemm355_run_variant(variant, dtype, M, N, K, A, lda, B, ldb, C, ldc, stream=0) -> int:
     return lib().gemm355_run_variant(variant, dtype, M, N, K, A, lda, B, ldb, C, ldc, stream)
+
+
+def gemm355_gemm_ex(variant, dtype, flags, M, N, K, A, lda, B, ldb, C, ldc, stream=0) -> int:
+    return lib().gemm355_gemm_ex(variant, dtype, flags, M, N, K, A, lda, B, ldb, C, ldc, stream)
 
 
 def gemm355_select_variant(dtype, M, N, K, A, lda, B, ldb, C, ldc) -> int:
@@ -186,10 +193,14 @@ def _dtype_code(t) -> int:
     return codes[t.dtype]
 
 
-def matmul(A, B, out=None, variant: int | str = VARIANT_AUTO, stream=None):
-    """C = A.B on the GPU through libgemm355; A, B are 2-D CUDA tensors (float32, float16
-    or bfloat16, rows contiguous), the result is float32.  Raises Gemm355Error on a
-    non-OK status; never falls back to another implementation."""
+def matmul(A, B, out=None, variant: int | str = VARIANT_AUTO, stream=None, *,
+           trans_a: bool = False, trans_b: bool = False, neg_a: bool = False,
+           neg_b: bool = False, accumulate: bool = False):
+    """C = (+-op(A)) (+-op(B)) [+ out] on the GPU through libgemm355.  A and B are the
+    stored 2-D CUDA tensors (float32, float16 or bfloat16, rows contiguous): A is M x K,
+    or K x M with trans_a; B is K x N, or N x K with trans_b.  The result is float32;
+    with accumulate, `out` (float32, M x N) is added to and required.  Raises
+    Gemm355Error on a non-OK status; never falls back to another implementation."""
     import torch
     if isinstance(variant, str):
         variant = VARIANTS[variant]
@@ -197,18 +208,28 @@ def matmul(A, B, out=None, variant: int | str = VARIANT_AUTO, stream=None):
         raise ValueError("operands must be CUDA tensors")
     if A.dtype != B.dtype:
         raise TypeError("A and B must have the same dtype")
-    M, K = A.shape
-    K2, N = B.shape
+    M, K = (A.shape[1], A.shape[0]) if trans_a else tuple(A.shape)
+    K2, N = (B.shape[1], B.shape[0]) if trans_b else tuple(B.shape)
     if K2 != K:
         raise ValueError("inner dimensions differ")
     if out is None:
+        if accumulate:
+            raise ValueError("accumulate needs `out`")
         out = torch.empty((M, N), dtype=torch.float32, device=A.device)
     if out.dtype != torch.float32 or tuple(out.shape) != (M, N):
         raise ValueError("out must be a float32 M x N tensor")
     s = stream if stream is not None else torch.cuda.current_stream(A.device)
     handle = s.cuda_stream if hasattr(s, "cuda_stream") else int(s)
-    st = gemm355_run_variant(variant, _dtype_code(A), M, N, K, A.data_ptr(), _ld(A),
+    flags = ((TRANS_A if trans_a else 0) | (TRANS_B if trans_b else 0) | (NEG_A if neg_a else 0)
+             | (NEG_B if neg_b else 0) | (ACCUMULATE if accumulate else 0))
+    if flags:
+        st = gemm355_gemm_ex(variant, _dtype_code(A), flags, M, N, K, A.data_ptr(), _ld(A),
                              B.data_ptr(), _ld(B), out.data_ptr(), _ld(out), handle)
+        where = "gemm355_gemm_ex"
+    else:
+        st = gemm355_run_variant(variant, _dtype_code(A), M, N, K, A.data_ptr(), _ld(A),
+                                 B.data_ptr(), _ld(B), out.data_ptr(), _ld(out), handle)
+        where = "gemm355_run_variant"
     if st != OK:
-        raise Gemm355Error(st, "gemm355_run_variant")
+        raise Gemm355Error(st, where)
     return out

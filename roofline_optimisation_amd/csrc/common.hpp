@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace g355 {
 
 typedef float floatx4 __attribute__((ext_vector_type(4)));
@@ -29,7 +31,9 @@ __device__ __forceinline__ float to_float(bf16_t x) {
 }
 
 // Arguments common to every launcher.  Pointers are device pointers; ld* are row
-// strides in elements.
+// strides in elements.  C = sign * op(A) op(B) (+ C when accumulate), where op(A) is A
+// (M x K rows) or, with trans_a, the transpose of the stored K x M matrix, and likewise
+// op(B) is B (K x N) or the transpose of the stored N x K matrix.
 struct GemmArgs {
     int M, N, K;
     const void *A;
@@ -38,7 +42,70 @@ struct GemmArgs {
     int ldb;
     float *C;
     int ldc;
+    int trans_a = 0, trans_b = 0;
+    float sign = 1.0f;
+    int accumulate = 0;
 };
+
+// Stores one 32 x 32 MFMA accumulator block: register r of this lane holds row
+// row0 + 8 (r/4) + r%4 (row0 already includes the lane's 4 (l/32)), column col.  EDGE
+// guards every access against M x N; NT uses non-temporal stores (C is not re-read).
+// The values go out exactly as accumulated, straight from the accumulator registers (a
+// negated product is negated by a pass after the kernel).
+template <bool EDGE, bool NT>
+__device__ __forceinline__ void store_block32(const floatx16 &acc, float *__restrict__ C, int ldc,
+                                              int row0, int col, int M, int N) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int row = row0 + 8 * (r / 4) + r % 4;
+        float *c = C + (size_t)row * ldc + col;
+        if (!EDGE || (row < M && col < N)) {
+            if (NT) __builtin_nontemporal_store(acc[r], c);
+            else *c = acc[r];
+        }
+    }
+}
+
+// The same block for kernels that accumulate into C: c = sign * acc + c (sign = +1 or
+// -1).  The block is done in two halves of 8 rows; the fences keep each half's loads
+// together and apart from the rest, so that few old values are live at a time.  AREAD:
+// the accumulators live in the AGPR file; each is read with its own v_accvgpr_read at
+// its point of use (otherwise the compiler copies all of them to VGPRs at once when the
+// loop ends, which does not fit next to the loop's other registers).
+template <bool EDGE, bool NT, bool AREAD>
+__device__ __forceinline__ void store_block32_acc(const floatx16 &acc, float *__restrict__ C,
+                                                  int ldc, int row0, int col, int M, int N,
+                                                  float sign) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        __builtin_amdgcn_sched_barrier(0);
+        float old[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int r = 8 * h + q;
+            const int row = row0 + 8 * (r / 4) + r % 4;
+            const bool ok = !EDGE || (row < M && col < N);
+            old[q] = ok ? C[(size_t)(ok ? row : 0) * ldc + (ok ? col : 0)] : 0.f;
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int r = 8 * h + q;
+            const int row = row0 + 8 * (r / 4) + r % 4;
+            float *c = C + (size_t)row * ldc + col;
+            if (!EDGE || (row < M && col < N)) {
+                float a;
+                if constexpr (AREAD)
+                    asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(a) : "a"(acc[r]));
+                else
+                    a = acc[r];
+                const float v = sign * a + old[q];
+                if (NT) __builtin_nontemporal_store(v, c);
+                else *c = v;
+            }
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+}
 
 __host__ __device__ constexpr int cdiv(int a, int b) { return (a + b - 1) / b; }
 

@@ -87,6 +87,46 @@ gemm355_status run(int variant, int dtype, int M, int N, int K, const void *A, i
     return launch(variant, dtype, g, stream) == hipSuccess ? GEMM355_OK : GEMM355_ERR_LAUNCH;
 }
 
+constexpr unsigned kExFlags = GEMM355_TRANS_A | GEMM355_TRANS_B | GEMM355_NEG_A | GEMM355_NEG_B |
+                               GEMM355_ACCUMULATE;
+
+gemm355_status run_ex(int variant, int dtype, unsigned flags, int M, int N, int K, const void *A,
+                      int lda, const void *B, int ldb, float *C, int ldc, hipStream_t stream) {
+    if ((flags & ~kExFlags) != 0) return GEMM355_ERR_INVALID_ARG;
+    const bool ta = flags & GEMM355_TRANS_A, tb = flags & GEMM355_TRANS_B;
+    const bool acc = flags & GEMM355_ACCUMULATE;
+    const bool neg = ((flags & GEMM355_NEG_A) != 0) != ((flags & GEMM355_NEG_B) != 0);
+    if (dtype < kF32 || dtype > kBF16) return GEMM355_ERR_INVALID_ARG;
+    if (M < 0 || N < 0 || K < 0) return GEMM355_ERR_INVALID_ARG;
+    const int min_lda = ta ? M : K, min_ldb = tb ? K : N;
+    if (lda < (min_lda > 1 ? min_lda : 1) || ldb < (min_ldb > 1 ? min_ldb : 1) ||
+        ldc < (N > 1 ? N : 1))
+        return GEMM355_ERR_INVALID_ARG;
+    if ((long)M * K > 0 && A == nullptr) return GEMM355_ERR_INVALID_ARG;
+    if ((long)K * N > 0 && B == nullptr) return GEMM355_ERR_INVALID_ARG;
+    if ((long)M * N > 0 && C == nullptr) return GEMM355_ERR_INVALID_ARG;
+    if (variant < GEMM355_VARIANT_AUTO || variant > GEMM355_VARIANT_MFMA)
+        return GEMM355_ERR_INVALID_ARG;
+    GemmArgs g{M, N, K, A, lda, B, ldb, C, ldc};
+    g.trans_a = ta;
+    g.trans_b = tb;
+    g.sign = neg ? -1.0f : 1.0f;
+    g.accumulate = acc;
+    if (variant == GEMM355_VARIANT_AUTO) variant = auto_variant(dtype, g);
+    if (!variant_supported(variant, dtype)) return GEMM355_ERR_UNSUPPORTED;
+    if (flags != 0 && variant != GEMM355_VARIANT_NAIVE && variant != GEMM355_VARIANT_MFMA)
+        return GEMM355_ERR_UNSUPPORTED;
+    if (M == 0 || N == 0) return GEMM355_OK;
+    if (!device_ok()) return GEMM355_ERR_DEVICE;
+    if (K == 0 && acc) return GEMM355_OK;  // adding the empty sum leaves C as it is
+    if (launch(variant, dtype, g, stream) != hipSuccess) return GEMM355_ERR_LAUNCH;
+    // the MFMA kernels store their accumulators as they are; the naive kernel and the
+    // accumulating variants apply the sign themselves
+    if (neg && !acc && variant == GEMM355_VARIANT_MFMA && launch_negate(g, stream) != hipSuccess)
+        return GEMM355_ERR_LAUNCH;
+    return GEMM355_OK;
+}
+
 }  // namespace
 
 bool current_device_is_gfx950() { return device_ok(); }
@@ -116,6 +156,12 @@ gemm355_status gemm355_run_variant(int variant, int dtype, int M, int N, int K, 
                                    int lda, const void *B, int ldb, float *C, int ldc,
                                    hipStream_t stream) {
     return run(variant, dtype, M, N, K, A, lda, B, ldb, C, ldc, stream);
+}
+
+gemm355_status gemm355_gemm_ex(int variant, int dtype, unsigned flags, int M, int N, int K,
+                               const void *A, int lda, const void *B, int ldb, float *C, int ldc,
+                               hipStream_t stream) {
+    return run_ex(variant, dtype, flags, M, N, K, A, lda, B, ldb, C, ldc, stream);
 }
 
 int gemm355_select_variant(int dtype, int M, int N, int K, const void *A, int lda, const void *B,

@@ -1,0 +1,787 @@
+// FP16 / BF16 GEMM with FP32 accumulation on the gfx950 matrix cores
+// (v_mfma_f32_32x32x16_f16 / _bf16): the AMD counterpart of the tensor-core level of
+// "Kernel optimisation guide" (Level 4: 16-bit A and B fragments, FP32 accumulator
+// fragments, one matrix multiply-accumulate per fragment step) and of the tensor-core
+// section of "Advanced CUDA features - starting from GEMM" (a wave-cooperative
+// D = A.B + C unit whose register layout the data movement has to match; its table of
+// tensor-core instructions lists transposed and negated operands and D scaled by 0 or 1,
+// which the operand kinds and the epilogue below provide).
+//
+// Structure:
+//  * a workgroup of WM x WN waves owns a BM x BN tile of C and walks K in steps of
+//    BK = 64 with two LDS stages: the dwordx4 loads of step t+1 are in flight while
+//    step t is multiplied, then written to the other stage before the one barrier of
+//    the step (the double buffer of "Kernel optimisation guide", Level 3);
+//  * each wave owns (BM/WM) x (BN/WN) of C as 32 x 32 FP32 accumulator blocks;
+//  * the MFMA wants, per lane l of a fragment, 8 consecutive k of row (A) or column (B)
+//    l%32 at k = 8(l/32) .. +7 of a 16-wide k step.  An operand stored with k
+//    contiguous (kind KM: A of C = A.B, or a transposed B) is kept [m or n][k] in LDS
+//    with rows padded to 144 bytes and read with one ds_read_b128 per fragment (the 32
+//    rows one instruction touches fall on distinct bank groups).  An operand stored
+//    with m or n contiguous (kind MN: B, or a transposed A) stays [k][m or n] in LDS as
+//    loaded, rows padded to 2*extent + 64 bytes, and two ds_read_b64_tr_b16 per
+//    fragment transpose it on the way out.  Within each 16-lane group that instruction
+//    hands output lane j, as its element e, halfword j%4 of the 8 bytes read by source
+//    lane 4e + (j%16)/4; so source lane 4e + q addresses row k+e, columns c + 4q ..
+//    c + 4q + 3, and output lane j receives column c + j%16 for rows k .. k+3;
+//  * interior tiles (inside M x N, K a multiple of BK) run a straight-line kernel; the
+//    ragged strips run a predicated one that zero-fills loads and guards stores;
+//  * C = sign * op(A) op(B) (+ C): the plain kernels store the accumulators as they are
+//    (a separate pass negates C for sign -1); the accumulating variants (ACC) load the
+//    old C block by block in the epilogue and store sign * acc + C.
+//
+// Interior 256 x 256 tiles with K a multiple of 128 take a second design (dma_tile
+// below): the tiles go from memory straight into LDS (buffer_load_dwordx4 ... lds)
+// through a four-stage ring, so no registers stage them and no LDS store instructions
+// are issued; LDS rows are XOR-swizzled instead of padded.  It multiplies in the same
+// order as the register-staged kernel, so both give identical results.
+#pragma once
+
+#include <type_traits>
+
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace g355 {
+
+namespace {
+
+constexpr int kBK = 64;
+constexpr int kSA = kBK + 8;  // KM operand LDS row stride in halves (144 bytes)
+
+// One operand of the product as the staged kernel holds it.  MN: rows are k (kBK of
+// them), E halves each; KM: rows are m or n (E of them), kBK halves each.
+template <bool MN, int E, int TT>
+struct H16Op {
+    static constexpr int kStride = MN ? E + 32 : kSA;          // LDS row stride (halves)
+    static constexpr int kRows = MN ? kBK : E;
+    static constexpr int kLds = kRows * kStride;               // halves per stage
+    static constexpr int kPerRow = (MN ? E : kBK) / 8;         // 16-byte chunks per row
+    static constexpr int kChunks = kRows * kPerRow / TT;       // per thread
+    static constexpr int kRowStep = TT / kPerRow;
+    static constexpr int kPieces = MN ? 2 : 1;                 // LDS reads per fragment
+    static_assert((kRows * kPerRow) % TT == 0 && TT % kPerRow == 0,
+                  "tile chunks must divide over the threads");
+};
+
+template <int BM, int BN, int WM, int WN, bool A_MN, bool B_MN>
+struct H16Cfg {
+    static constexpr int kThreads = 64 * WM * WN;
+    static constexpr int kTM = BM / WM, kTN = BN / WN;
+    static constexpr int kMB = kTM / 32, kNB = kTN / 32;
+    using OA = H16Op<A_MN, BM, kThreads>;
+    using OB = H16Op<B_MN, BN, kThreads>;
+    static constexpr int kLdsA = OA::kLds, kLdsB = OB::kLds;   // halves per stage
+    static constexpr int kLdsBytes = 2 * (kLdsA + kLdsB) * 2;
+    static_assert(kTM % 32 == 0 && kTN % 32 == 0, "wave tile must be whole 32x32 blocks");
+    static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
+};
+
+template <typename T>
+__device__ __forceinline__ floatx16 mfma32x32x16(u16x8 a, u16x8 b, floatx16 c);
+template <>
+__device__ __forceinline__ floatx16 mfma32x32x16<f16_t>(u16x8 a, u16x8 b, floatx16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(halfx8, a),
+                                                  __builtin_bit_cast(halfx8, b), c, 0, 0, 0);
+}
+template <>
+__device__ __forceinline__ floatx16 mfma32x32x16<bf16_t>(u16x8 a, u16x8 b, floatx16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
+typedef __attribute__((address_space(3))) u16x8 lds_u16x8;
+
+// An LDS address held in its own VGPR: the empty asm hides its relation to other
+// addresses, so the compiler keeps one base per (stage, region) and addresses every
+// access as base + immediate (DS immediates are 16 bits) instead of adding large
+// constants to a shared base inside the loop.
+__device__ __forceinline__ lds_u16 *lds_base(lds_u16 *p) {
+    uint32_t a = (uint32_t)(uintptr_t)p;
+    asm volatile("" : "+v"(a));
+    return (lds_u16 *)(uintptr_t)a;
+}
+
+__device__ __forceinline__ u16x8 join(shortx4 lo, shortx4 hi) {
+    return __builtin_bit_cast(u16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Columns [c, c+8) of one row.  EDGE: zero outside [0, ncols) and for invalid rows;
+// otherwise the chunk is known to be inside the matrix.
+template <bool VEC, bool EDGE>
+__device__ __forceinline__ u16x8 ld_chunk8(const uint16_t *__restrict__ row, int c, int ncols,
+                                           bool row_ok) {
+    if (!EDGE && VEC) return *reinterpret_cast<const u16x8 *>(row + c);
+    u16x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (EDGE && !row_ok) return v;
+    if (EDGE && VEC && c + 8 <= ncols) return *reinterpret_cast<const u16x8 *>(row + c);
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        if (!EDGE || c + e < ncols) v[e] = row[c + e];
+    return v;
+}
+
+// Fragment registers of one operand: a KM fragment is one ds_read_b128, an MN fragment
+// the two halves of two ds_read_b64_tr_b16.
+template <bool MN, int NBLK>
+struct H16Frag {
+    u16x8 f[2][NBLK];
+    __device__ __forceinline__ u16x8 get(int slot, int b) const { return f[slot][b]; }
+};
+template <int NBLK>
+struct H16Frag<true, NBLK> {
+    shortx4 f[2][NBLK][2];
+    __device__ __forceinline__ u16x8 get(int slot, int b) const {
+        return join(f[slot][b][0], f[slot][b][1]);
+    }
+};
+
+// LOAD: 0 = 16-bit loads (rows not 16-byte aligned), 1 = dwordx4 through pointers,
+// 2 = dwordx4 through buffer resources (interior tiles, offsets below 2^31 bytes).
+template <typename T, int BM, int BN, int WM, int WN, int LOAD, bool EDGE, bool PAIRED,
+          bool A_MN, bool B_MN, bool ACC>
+__device__ __forceinline__ void h16_tile(int M, int N, int K, const uint16_t *__restrict__ A,
+                                         int lda, const uint16_t *__restrict__ B, int ldb,
+                                         float *__restrict__ C, int ldc, float sign, int m0,
+                                         int n0, uint16_t *lds) {
+    using Cfg = H16Cfg<BM, BN, WM, WN, A_MN, B_MN>;
+    using OA = typename Cfg::OA;
+    using OB = typename Cfg::OB;
+    constexpr int TT = Cfg::kThreads;
+    constexpr int MB = Cfg::kMB, NB = Cfg::kNB;
+    constexpr int kAC = OA::kChunks, kBC = OB::kChunks;
+
+    const int t = threadIdx.x;
+    const int lane = t % 64, wave = t / 64;
+    const int wm = wave / WN, wn = wave % WN;
+    const int l32 = lane % 32, lhi = lane / 32;
+    // Chunk i of a thread: row r0 + kRowStep i, column c0 of the operand's LDS image.
+    const int a_r0 = t / OA::kPerRow, a_c0 = (t % OA::kPerRow) * 8;
+    const int b_r0 = t / OB::kPerRow, b_c0 = (t % OB::kPerRow) * 8;
+
+    // Global addressing of chunk (r, c) of a k-step at k0.  KM: row mn0 + r, column
+    // k0 + c; MN: row k0 + r, column mn0 + c.  Interior tiles read through buffer
+    // resources based at the tile's first row (KM) or first column (MN): one VGPR
+    // offset per operand, the chunk and k-step parts in SGPRs.
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(A_MN ? A + m0 : A + (size_t)m0 * lda), (short)0, 0x7fffffff, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(B_MN ? B + n0 : B + (size_t)n0 * ldb), (short)0, 0x7fffffff, 0x00020000);
+    const int va = (a_r0 * lda + a_c0) * 2, vb = (b_r0 * ldb + b_c0) * 2;
+
+    // Two staging register sets: the loads of k-step t+3 are issued while step t is
+    // multiplied and written to LDS two steps later.
+    u16x8 sa[2][kAC], sb[2][kBC];
+    // Global -> register staging, one 16-byte chunk per call (chunk w < kAC is A's,
+    // the rest B's).
+    auto op_chunk = [&](auto mn_c, const uint16_t *__restrict__ X, int ld, int mn0, int MNext,
+                        int r, int c, int k0) -> u16x8 {
+        constexpr bool kMN = decltype(mn_c)::value;
+        const int row = kMN ? k0 + r : mn0 + r;
+        const int col = kMN ? mn0 + c : k0 + c;
+        const bool ok = !EDGE || row < (kMN ? K : MNext);
+        return ld_chunk8<LOAD == 1, EDGE>(X + (size_t)(ok ? row : 0) * ld, col,
+                                          kMN ? MNext : K, ok);
+    };
+    auto load_one = [&](auto set_c, int k0, int w) {
+        constexpr int S = decltype(set_c)::value;
+        if constexpr (LOAD == 2) {
+            if (w < kAC) {
+                const int so = A_MN ? (k0 + w * OA::kRowStep) * lda * 2
+                                    : (w * OA::kRowStep * lda + k0) * 2;
+                sa[S][w] = __builtin_bit_cast(u16x8, __builtin_amdgcn_raw_buffer_load_b128(ra, va, so, 0));
+            } else {
+                const int i = w - kAC;
+                const int so = B_MN ? (k0 + i * OB::kRowStep) * ldb * 2
+                                    : (i * OB::kRowStep * ldb + k0) * 2;
+                sb[S][i] = __builtin_bit_cast(u16x8, __builtin_amdgcn_raw_buffer_load_b128(rb, vb, so, 0));
+            }
+        } else {
+            if (w < kAC)
+                sa[S][w] = op_chunk(std::integral_constant<bool, A_MN>{}, A, lda, m0, M,
+                                    a_r0 + w * OA::kRowStep, a_c0, k0);
+            else
+                sb[S][w - kAC] = op_chunk(std::integral_constant<bool, B_MN>{}, B, ldb, n0, N,
+                                          b_r0 + (w - kAC) * OB::kRowStep, b_c0, k0);
+        }
+    };
+    // Per-lane LDS bases for the staged writes, one per stage and operand.
+    constexpr int kStage = Cfg::kLdsA + Cfg::kLdsB;
+    lds_u16 *const L = (lds_u16 *)lds;
+    lds_u16 *const a_wr[2] = {lds_base(L + a_r0 * OA::kStride + a_c0),
+                              lds_base(L + kStage + a_r0 * OA::kStride + a_c0)};
+    lds_u16 *const b_wr[2] = {lds_base(L + Cfg::kLdsA + b_r0 * OB::kStride + b_c0),
+                              lds_base(L + kStage + Cfg::kLdsA + b_r0 * OB::kStride + b_c0)};
+    auto store_one = [&](auto set_c, int buf, int w) {
+        constexpr int S = decltype(set_c)::value;
+        if (w < kAC)
+            *(lds_u16x8 *)(a_wr[buf] + w * OA::kRowStep * OA::kStride) = sa[S][w];
+        else
+            *(lds_u16x8 *)(b_wr[buf] + (w - kAC) * OB::kRowStep * OB::kStride) = sb[S][w - kAC];
+    };
+
+    floatx16 acc[MB][NB];
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    // Per-lane fragment offsets within a stage, for the wave's first block (wb = the
+    // wave's first row or column).  KM: row wb + l%32, k 8 (l/32) (+ 32 b rows, + 16 s).
+    // MN: lane (g = l/16, s16 = l%16) reads row 8 (g/2) + s16/4, column wb + 16 (g%2) +
+    // 4 (s16%4) (+ 16 s rows, + 4 h rows, + 32 b columns).
+    const int g16 = lane / 16, s16 = lane % 16;
+    auto frag_off = [&](auto mn_c, int stride, int wb) {
+        constexpr bool kMN = decltype(mn_c)::value;
+        if constexpr (kMN)
+            return (8 * (g16 / 2) + s16 / 4) * stride + wb + 16 * (g16 % 2) + 4 * (s16 % 4);
+        else
+            return (wb + l32) * stride + 8 * lhi;
+    };
+    const int a_off = frag_off(std::integral_constant<bool, A_MN>{}, OA::kStride, wm * Cfg::kTM);
+    const int b_off = frag_off(std::integral_constant<bool, B_MN>{}, OB::kStride, wn * Cfg::kTN);
+    constexpr int kSteps = kBK / 16;
+    constexpr int kRA = MB * OA::kPieces;
+    constexpr int kR = kRA + NB * OB::kPieces;  // fragment reads per sub-step
+    H16Frag<A_MN, MB> af;
+    H16Frag<B_MN, NB> bf;
+    lds_u16 *const a_rd[2] = {lds_base(L + a_off), lds_base(L + kStage + a_off)};
+    lds_u16 *const b_rd[2] = {lds_base(L + Cfg::kLdsA + b_off),
+                              lds_base(L + kStage + Cfg::kLdsA + b_off)};
+    // Fragment read `p` of sub-step s into slot: the A pieces first, block-major, then B's.
+    auto read_op = [&](auto mn_c, auto &fr, lds_u16 *base, int stride, int s, int slot, int p) {
+        constexpr bool kMN = decltype(mn_c)::value;
+        if constexpr (kMN) {
+            const int b = p / 2, h = p % 2;
+            fr.f[slot][b][h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_shortx4 *)(base + 16 * s * stride + 32 * b + 4 * h * stride));
+        } else {
+            fr.f[slot][p] = *(const lds_u16x8 *)(base + 32 * p * stride + 16 * s);
+        }
+    };
+    auto read_piece = [&](int buf, int s, int slot, int p) {
+        if (p < kRA)
+            read_op(std::integral_constant<bool, A_MN>{}, af, a_rd[buf], OA::kStride, s, slot, p);
+        else
+            read_op(std::integral_constant<bool, B_MN>{}, bf, b_rd[buf], OB::kStride, s, slot, p - kRA);
+    };
+    auto mfma_one = [&](int slot, int q) {
+        const int i = q / NB, j = q % NB;
+        acc[i][j] = mfma32x32x16<T>(af.get(slot, i), bf.get(slot, j), acc[i][j]);
+    };
+    constexpr int kMf = MB * NB;                  // MFMAs per sub-step
+    constexpr int kPre = (kMf * 3 + 7) / 8;       // of those, issued before the barrier
+    constexpr int kWr = kAC + kBC;                // staged chunks per k-step
+
+    // Events of one k-step are spread over its kSteps * kMf MFMA slots: event e of n
+    // spread over slots [lo, hi) goes after the MFMA of slot lo + ceil-spread(e).
+    constexpr int kSlots = kSteps * kMf;
+    auto ev_begin = [](int q, int n, int lo, int hi) {  // first event at or after slot q
+        if (q <= lo) return 0;
+        if (q >= hi) return n;
+        return ((q - lo) * n + (hi - lo) - 1) / (hi - lo);
+    };
+    // Store window: the idle stage is free from the start of the k-step, so the staged
+    // chunks of k-step t+1 are written over every slot before the barrier.  Paired loads
+    // of k-step t+2 (into the other, already written-out set) go over the first half.
+    constexpr int kBarrier = (kSteps - 1) * kMf + kPre;   // barrier after this many slots
+    constexpr int kStoreLo = 0, kStoreHi = kBarrier;
+    constexpr int kLoadLo = 0, kLoadHi = kSlots / 2;
+
+    // One k-step t on stage buf.  Every memory instruction is issued between MFMAs so
+    // that no burst blocks the in-order issue of the MFMAs behind it:
+    //  * sub-step s < last reads the fragments of s+1 (slot (s+1) % 2) two per MFMA
+    //    after its first MFMAs;
+    //  * the staged chunks of k-step t+1 (set S) are written to the idle stage, spread
+    //    over all slots before the barrier; paired variant: the loads of k-step t+2 go
+    //    into the other set O over the first half; unpaired variant: chunk w of t+2 is
+    //    loaded into S right after chunk w of t+1 was written;
+    //  * after the barrier, the first fragments of t+1 are read between the last MFMAs.
+    // The body has no branches (a branch makes the compiler wait for every outstanding
+    // LDS read at the join): near the end the loads re-read the last k-step and the idle
+    // stage takes dummies.
+    const int nk = cdiv(K, kBK);
+    auto kstep = [&](auto set_c, auto other_c, int kt, int buf) {
+        const int kload = min(kt + 2, nk - 1) * kBK;
+#pragma unroll
+        for (int s = 0; s < kSteps; ++s) {
+#pragma unroll
+          for (int q = 0; q < kMf; ++q) {
+            const int qs = s * kMf + q;
+            if (qs >= kBarrier) {
+                // after the barrier: next k-step's first fragments before each MFMA
+                const int r_lo = ev_begin(qs, kR, kBarrier, kSlots);
+                const int r_hi = ev_begin(qs + 1, kR, kBarrier, kSlots);
+#pragma unroll
+                for (int o = r_lo; o < r_hi; ++o) read_piece(buf ^ 1, 0, 0, o);
+            }
+            mfma_one(s & 1, q);
+            if (s + 1 < kSteps) {
+#pragma unroll
+                for (int p = 2 * q; p < 2 * q + 2; ++p)
+                    if (p < kR) read_piece(buf, s + 1, (s + 1) & 1, p);
+            }
+            if (qs < kBarrier) {
+                const int w_lo = ev_begin(qs, kWr, kStoreLo, kStoreHi);
+                const int w_hi = ev_begin(qs + 1, kWr, kStoreLo, kStoreHi);
+#pragma unroll
+                for (int w = w_lo; w < w_hi; ++w) {
+                    store_one(set_c, buf ^ 1, w);
+                    if constexpr (!PAIRED) load_one(set_c, kload, w);
+                }
+            }
+            if constexpr (PAIRED) {
+                const int l_lo = ev_begin(qs, kWr, kLoadLo, kLoadHi);
+                const int l_hi = ev_begin(qs + 1, kWr, kLoadLo, kLoadHi);
+#pragma unroll
+                for (int w = l_lo; w < l_hi; ++w) load_one(other_c, kload, w);
+            }
+            if (qs == kBarrier - 1) __syncthreads();
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+    };
+
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    if (nk > 0) {
+#pragma unroll
+        for (int w = 0; w < kWr; ++w) load_one(S0{}, 0, w);
+#pragma unroll
+        for (int w = 0; w < kWr; ++w) store_one(S0{}, 0, w);
+        __syncthreads();
+#pragma unroll
+        for (int w = 0; w < kWr; ++w) load_one(S1{}, min(1, nk - 1) * kBK, w);
+#pragma unroll
+        for (int p = 0; p < kR; ++p) read_piece(0, 0, 0, p);
+        if constexpr (PAIRED) {
+            // nk is even: k-steps in pairs, staging sets alternating statically
+            for (int kt = 0; kt < nk; kt += 2) {
+                kstep(S1{}, S0{}, kt, 0);      // loads kt+2 into set 0, stores kt+1 (set 1)
+                kstep(S0{}, S1{}, kt + 1, 1);  // loads kt+3 into set 1, stores kt+2 (set 0)
+            }
+        } else {
+            // any nk: one staging set, loads issued one k-step ahead
+            for (int kt = 0; kt < nk; ++kt) kstep(S1{}, S1{}, kt, kt & 1);
+        }
+    }
+
+    // 32x32 accumulator layout: register r of lane l holds row 8(r/4) + 4(l/32) + r%4,
+    // column l%32 of the block.  Streaming stores: C is not re-read by this kernel.
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+        {
+            const int row0 = m0 + wm * Cfg::kTM + 32 * i + 4 * lhi;
+            const int col = n0 + wn * Cfg::kTN + 32 * j + l32;
+            if constexpr (ACC) store_block32_acc<EDGE, true, (MB * NB > 8)>(acc[i][j], C, ldc, row0, col, M, N, sign);
+            else store_block32<EDGE, true>(acc[i][j], C, ldc, row0, col, M, N);
+        }
+}
+
+// Same tile-numbering scheme as the FP32 kernel: interior launches walk the full tiles
+// in XCD-contiguous grouped order; edge launches take the ragged right strip, then the
+// ragged bottom strip (or every tile when K is ragged).
+template <bool EDGE>
+__device__ __forceinline__ void h16_tile_of(int bid, int nblocks, int tiles_m, int tiles_n,
+                                            bool ragged_n, bool all_tiles, int &tm, int &tn) {
+    if (!EDGE || all_tiles) {
+        grouped_tile(xcd_contiguous_id(bid, nblocks), tiles_m, tiles_n, 4, tm, tn);
+        return;
+    }
+    const int right = ragged_n ? tiles_m : 0;
+    if (bid < right) {
+        tm = bid;
+        tn = tiles_n - 1;
+    } else {
+        tm = tiles_m - 1;
+        tn = bid - right;
+    }
+}
+
+template <typename T, int BM, int BN, int WM, int WN, int MINW, int LOAD, bool EDGE, bool PAIRED,
+          bool A_MN, bool B_MN, bool ACC>
+__global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(MINW)))
+void mfma_f16_gemm_kernel(int M, int N, int K, const uint16_t *__restrict__ A, int lda,
+                          const uint16_t *__restrict__ B, int ldb, float *__restrict__ C, int ldc,
+                          float sign, int all_tiles) {
+    using Cfg = H16Cfg<BM, BN, WM, WN, A_MN, B_MN>;
+    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * (Cfg::kLdsA + Cfg::kLdsB)];
+    const int tiles_m = EDGE ? cdiv(M, BM) : M / BM;
+    const int tiles_n = EDGE ? cdiv(N, BN) : N / BN;
+    int tm, tn;
+    h16_tile_of<EDGE>(blockIdx.x, gridDim.x, tiles_m, tiles_n, N % BN != 0, all_tiles != 0, tm, tn);
+    h16_tile<T, BM, BN, WM, WN, LOAD, EDGE, PAIRED, A_MN, B_MN, ACC>(
+        M, N, K, A, lda, B, ldb, C, ldc, sign, tm * BM, tn * BN, lds);
+}
+
+// Every row of both operands starts on a 16-byte boundary.
+inline bool h16_vec(const GemmArgs &g) {
+    return rows_aligned16(g.A, g.lda, 2) && rows_aligned16(g.B, g.ldb, 2);
+}
+
+// ---------------------------------------------------------------------------------
+// 256 x 256 interior tiles fed by direct global -> LDS loads.
+//
+// Data movement ("Kernel optimisation guide", Level 3 double buffering, extended to a
+// ring; the overlap of loads and arithmetic in the scheduling section of "Advanced
+// CUDA features - starting from GEMM"):
+//  * K is walked in steps of 32 through kNs = 4 LDS stages (32 KiB each: 16 KiB per
+//    operand); the loads of k-step t+3 are issued while step t is multiplied, into the
+//    stage step t-1 has released;
+//  * a load is buffer_load_dwordx4 with the lds flag: lane l's 16 bytes land at
+//    m0 + 16 l, so one instruction fills 1 KiB of LDS (16 rows of a KM operand or 2
+//    rows of an MN operand) and the lane -> source mapping chooses where each 16-byte
+//    chunk goes;
+//  * a KM operand's rows are 64 bytes, chunk c of row r stored in slot c ^ ((r / 4) %
+//    4); an MN operand's rows are 512 bytes, chunk c of row k in slot c ^ 4 (k % 4).
+//    With these the fragment reads (ds_read_b128 for KM, ds_read_b64_tr_b16 for MN, as
+//    in the staged kernel) touch 16 distinct 16-byte bank groups per 256 bytes, i.e.
+//    no bank conflicts, without padding (which a contiguous 1 KiB load cannot skip);
+//  * each wave waits for its own loads of step t+1 (vmcnt), then one barrier per
+//    k-step publishes the stage to all four waves.
+// The loads are issued from inline assembly (m0 holds the LDS destination), so the
+// compiler neither tracks them nor waits for them; the kernel's own s_waitcnt vmcnt
+// instructions do, and no other code of this kernel uses m0.
+namespace dma {
+
+constexpr int kBM = 256, kBN = 256, kBK = 32, kNs = 4;
+constexpr int kWM = 2, kWN = 2, kWaves = kWM * kWN;
+constexpr int kTM = kBM / kWM, kTN = kBN / kWN, kMB = kTM / 32, kNB = kTN / 32;
+constexpr int kStage = kBM * kBK * 2;        // bytes per operand per stage (both 256 x 32)
+constexpr int kBOff = kNs * kStage;          // the B ring follows the A ring
+constexpr int kLds = 2 * kNs * kStage;
+constexpr int kI = kStage / 1024 / kWaves;   // 1 KiB loads per wave per operand per k-step
+constexpr int kLd = 2 * kI;
+static_assert(kBM == kBN, "both operands share the ring geometry");
+static_assert(kLds <= 160 * 1024, "LDS budget");
+// every ds_read immediate (stage + block / row offsets) stays below 64 KiB
+static_assert((kNs - 1) * kStage + (kMB - 1) * 2048 < 65536, "KM read offsets");
+static_assert((kNs - 1) * kStage + 16 * 512 + 4 * 512 < 65536, "MN read offsets");
+
+typedef int int4v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) char lds_char;
+
+// A raw buffer resource over `p` (2^31 - 1 bytes; the host checks every offset fits).
+__device__ __forceinline__ int4v rsrc_of(const void *p) {
+    const uint64_t a = (uint64_t)(uintptr_t)p;
+    int4v r;
+    r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+    r[2] = 0x7fffffff;
+    r[3] = 0x00020000;
+    return r;
+}
+
+// 16 bytes per lane from the buffer at voff + soff into LDS at lds_dst + 16 * lane.
+// m0 must be written right before the load; one wait state separates the two.
+__device__ __forceinline__ void load_lds16(uint32_t lds_dst, uint32_t voff, int4v rsrc,
+                                           uint32_t soff) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :: "s"(lds_dst), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+
+__device__ __forceinline__ lds_char *lds_reg(lds_char *p) {
+    uint32_t a = (uint32_t)(uintptr_t)p;
+    asm volatile("" : "+v"(a));
+    return (lds_char *)(uintptr_t)a;
+}
+
+// Loads and fragment reads of one operand of extent 256 in a ring at byte offset `roff`.
+// KM: wave w fills rows [16 kI w, +16 kI), instruction i rows 16 i + l/4, lane slot l%4
+// taking chunk (l%4) ^ ((l/16)%4).  MN: wave w fills rows [2 kI w, +2 kI), instruction
+// i rows 2 i + l/32, lane slot l%32 taking chunk slot ^ 4 (row % 4), where row % 4 =
+// l/32 + 2 (i % 2).
+template <bool MN, int NBLK>
+struct DmaOp {
+    int4v rsrc;
+    uint32_t voff[2];
+    lds_char *rd[MN ? NBLK : 2];
+    H16Frag<MN, NBLK> fr;
+
+    // X: the operand; mn0: the tile's first row (KM) or column (MN); wb: the wave's first
+    // row or column within the tile.
+    __device__ __forceinline__ void init(const uint16_t *X, int ld, int mn0, int wave, int lane,
+                                         lds_char *L, int roff, int wb) {
+        if constexpr (MN) {
+            rsrc = rsrc_of(X + mn0);
+            const int row = 2 * kI * wave + lane / 32, slot = lane & 31;
+            voff[0] = (uint32_t)((row * ld + 8 * (slot ^ (4 * (lane >> 5)))) * 2);
+            voff[1] = (uint32_t)((row * ld + 8 * (slot ^ (4 * ((lane >> 5) + 2)))) * 2);
+            // lane (g = l/16, e = (l%16)/4, q = l%4) reads row 16 s + 8 (g/2) + 4 h + e,
+            // chunk wb/8 + 4 b + 2 (g%2) + q/2, byte 8 (q%2) of it; its slot is chunk ^ 4 e
+            const int g = lane >> 4, e = (lane & 15) >> 2, q = lane & 3;
+#pragma unroll
+            for (int b = 0; b < NBLK; ++b)
+                rd[b] = lds_reg(L + roff + (8 * (g >> 1) + e) * 512 +
+                                16 * ((wb / 8 + 4 * b + 2 * (g & 1) + (q >> 1)) ^ (4 * e)) +
+                                8 * (q & 1));
+        } else {
+            rsrc = rsrc_of(X + (size_t)mn0 * ld);
+            const int row = 16 * kI * wave + lane / 4;
+            voff[0] = voff[1] = (uint32_t)((row * ld + 8 * ((lane & 3) ^ ((lane >> 4) & 3))) * 2);
+            // row wb + 32 b + l%32, chunk 2 s + l/32, whose swizzle key ((l%32)/4) % 4
+            // does not depend on b
+            const int l32 = lane & 31, lhi = lane >> 5;
+            const int off = (wb + l32) * 64;
+            rd[0] = lds_reg(L + roff + off + 16 * ((0 + lhi) ^ ((l32 >> 2) & 3)));
+            rd[1] = lds_reg(L + roff + off + 16 * ((2 + lhi) ^ ((l32 >> 2) & 3)));
+        }
+    }
+    // Load instruction i (of kI) of the k-step at k0 into stage st.
+    __device__ __forceinline__ void issue(uint32_t lds0, int roff, int wave, int ld, int st,
+                                          int k0, int i) {
+        const uint32_t dst = lds0 + roff + st * kStage + (wave * kI + i) * 1024;
+        if constexpr (MN)
+            load_lds16(dst, voff[i & 1], rsrc, (uint32_t)((k0 + 2 * i) * ld * 2));
+        else
+            load_lds16(dst, voff[0], rsrc, (uint32_t)((16 * i * ld + k0) * 2));
+    }
+    // Piece p (of NBLK * kPieces) of sub-step s of stage st into fragment slot `slot`.
+    __device__ __forceinline__ void read(int st, int s, int slot, int p) {
+        if constexpr (MN) {
+            const int b = p / 2, h = p % 2;
+            fr.f[slot][b][h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_shortx4 *)(rd[b] + st * kStage + 16 * s * 512 + 4 * h * 512));
+        } else {
+            fr.f[slot][p] = *(const lds_u16x8 *)(rd[s] + st * kStage + p * 2048);
+        }
+    }
+};
+
+template <typename T, bool A_MN, bool B_MN, bool ACC>
+__device__ __forceinline__ void dma_tile(int K, const uint16_t *__restrict__ A, int lda,
+                                         const uint16_t *__restrict__ B, int ldb,
+                                         float *__restrict__ C, int ldc, float sign, int m0,
+                                         int n0, char *lds_raw) {
+    const int lane = threadIdx.x % 64;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+    const int wm = wave / kWN, wn = wave % kWN;
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_char *)lds_raw;
+    lds_char *const L = (lds_char *)lds_raw;
+    const int l32 = lane & 31, lhi = lane >> 5;
+
+    DmaOp<A_MN, kMB> oa;
+    DmaOp<B_MN, kNB> ob;
+    oa.init(A, lda, m0, wave, lane, L, 0, wm * kTM);
+    ob.init(B, ldb, n0, wave, lane, L, kBOff, wn * kTN);
+    auto issue = [&](int st, int k0, int w) {  // w < kI: A instruction w, else B
+        if (w < kI) oa.issue(lds0, 0, wave, lda, st, k0, w);
+        else ob.issue(lds0, kBOff, wave, ldb, st, k0, w - kI);
+    };
+    constexpr int kRA = kMB * (A_MN ? 2 : 1);
+    constexpr int kR = kRA + kNB * (B_MN ? 2 : 1);
+    auto read_piece = [&](int st, int s, int slot, int p) {
+        if (p < kRA) oa.read(st, s, slot, p);
+        else ob.read(st, s, slot, p - kRA);
+    };
+
+    floatx16 acc[kMB][kNB];
+#pragma unroll
+    for (int i = 0; i < kMB; ++i)
+#pragma unroll
+        for (int j = 0; j < kNB; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    auto mfma_one = [&](int slot, int qq) {
+        const int i = qq / kNB, j = qq % kNB;
+        acc[i][j] = mfma32x32x16<T>(oa.fr.get(slot, i), ob.fr.get(slot, j), acc[i][j]);
+    };
+
+    // One k-step on stage st: 2 sub-steps of kMf MFMAs.  Sub-step 0 reads the fragments
+    // of sub-step 1 two per MFMA; the kLd loads of k-step t+3 are spread one per two
+    // MFMAs over sub-step 0; after kPre MFMAs of sub-step 1 the wave waits for its
+    // loads of step t+1 (the 2 kLd younger ones may stay in flight) and the barrier
+    // publishes that stage; its first fragments are then read under the last MFMAs.
+    // No branches: near the end the loads repeat the last k-step into free stages.
+    constexpr int kMf = kMB * kNB, kSlots = 2 * kMf;
+    constexpr int kPre = (kMf * 3 + 7) / 8;
+    constexpr int kBarrier = kMf + kPre;
+    constexpr int kLoadHi = kMf;
+    static_assert(kLoadHi <= kBarrier, "the furthest k-step's loads precede the wait");
+    auto ev_begin = [](int qs, int n, int lo, int hi) {
+        if (qs <= lo) return 0;
+        if (qs >= hi) return n;
+        return ((qs - lo) * n + (hi - lo) - 1) / (hi - lo);
+    };
+    const int nk = K / kBK;
+    auto kstep = [&](int kt, int st) {
+        const int st_next = (st + 1) % kNs;
+        const int st_load = (st + kNs - 1) % kNs;
+        const int kload = min(kt + kNs - 1, nk - 1) * kBK;
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+#pragma unroll
+            for (int qq = 0; qq < kMf; ++qq) {
+                const int qs = s * kMf + qq;
+                if (qs >= kBarrier) {
+                    const int lo = ev_begin(qs, kR, kBarrier, kSlots);
+                    const int hi = ev_begin(qs + 1, kR, kBarrier, kSlots);
+#pragma unroll
+                    for (int o = lo; o < hi; ++o) read_piece(st_next, 0, 0, o);
+                }
+                mfma_one(s, qq);
+                if (s == 0) {
+#pragma unroll
+                    for (int p = 2 * qq; p < 2 * qq + 2; ++p)
+                        if (p < kR) read_piece(st, 1, 1, p);
+                }
+                {
+                    const int lo = ev_begin(qs, kLd, 0, kLoadHi);
+                    const int hi = ev_begin(qs + 1, kLd, 0, kLoadHi);
+#pragma unroll
+                    for (int w = lo; w < hi; ++w) issue(st_load, kload, w);
+                }
+                if (qs == kBarrier - 1) {
+                    wait_vmcnt<kLd * (kNs - 2)>();
+                    __syncthreads();
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    };
+
+    // k-steps 0 .. kNs-2 in flight, wait for step 0, read its first fragments
+#pragma unroll
+    for (int p = 0; p < kNs - 1; ++p)
+#pragma unroll
+        for (int w = 0; w < kLd; ++w) issue(p, min(p, nk - 1) * kBK, w);
+    wait_vmcnt<kLd * (kNs - 2)>();
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < kR; ++p) read_piece(0, 0, 0, p);
+    for (int kt = 0; kt < nk; kt += kNs) {
+#pragma unroll
+        for (int u = 0; u < kNs; ++u) kstep(kt + u, u);
+    }
+    // nothing may still write this workgroup's LDS when it exits
+    wait_vmcnt<0>();
+
+#pragma unroll
+    for (int i = 0; i < kMB; ++i)
+#pragma unroll
+        for (int j = 0; j < kNB; ++j)
+        {
+            const int row0 = m0 + wm * kTM + 32 * i + 4 * lhi, col = n0 + wn * kTN + 32 * j + l32;
+            if constexpr (ACC) store_block32_acc<false, true, true>(acc[i][j], C, ldc, row0, col, 0, 0, sign);
+            else store_block32<false, true>(acc[i][j], C, ldc, row0, col, 0, 0);
+        }
+}
+
+}  // namespace dma
+
+template <typename T, bool A_MN, bool B_MN, bool ACC>
+__global__ __launch_bounds__(64 * dma::kWaves) __attribute__((amdgpu_waves_per_eu(1)))
+void mfma_f16_dma_kernel(int M, int N, int K, const uint16_t *__restrict__ A, int lda,
+                         const uint16_t *__restrict__ B, int ldb, float *__restrict__ C,
+                         int ldc, float sign) {
+    __shared__ __attribute__((aligned(1024))) char lds[dma::kLds];
+    int tm, tn;
+    grouped_tile(xcd_contiguous_id(blockIdx.x, gridDim.x), M / dma::kBM, N / dma::kBN, 4, tm, tn);
+    dma::dma_tile<T, A_MN, B_MN, ACC>(K, A, lda, B, ldb, C, ldc, sign, tm * dma::kBM, tn * dma::kBN,
+                                 lds);
+}
+
+// Byte offsets below 2^31 for every chunk of a 256-extent tile of the operand.
+inline bool op_fits(bool mn, int ext, int K, int ld) {
+    return mn ? ((long)K * ld + ext) * 2 < (1L << 31) : ((long)ext * ld + K) * 2 < (1L << 31);
+}
+
+// The direct-load kernel takes the interior tiles of a 256 x 256 configuration when
+// rows are 16-byte aligned, every byte offset fits the 31-bit buffer range and K is a
+// multiple of kNs k-steps.
+inline bool use_dma(const GemmArgs &g, int tile) {
+    return tile == dma::kBM && h16_vec(g) && g.K > 0 && g.K % (dma::kBK * dma::kNs) == 0 &&
+           g.M >= dma::kBM && g.N >= dma::kBN &&
+           op_fits(g.trans_a != 0, dma::kBM, g.K, g.lda) &&
+           op_fits(g.trans_b == 0, dma::kBN, g.K, g.ldb);
+}
+
+template <typename T, int BM, int BN, int WM, int WN, int MINW, int LOAD, bool EDGE, bool PAIRED,
+          bool A_MN, bool B_MN, bool ACC>
+hipError_t launch_one(const GemmArgs &g, int tiles, int all_flag, hipStream_t s) {
+    hipLaunchKernelGGL((mfma_f16_gemm_kernel<T, BM, BN, WM, WN, MINW, LOAD, EDGE, PAIRED, A_MN, B_MN, ACC>),
+                       dim3(tiles), dim3(64 * WM * WN), 0, s, g.M, g.N, g.K,
+                       (const uint16_t *)g.A, g.lda, (const uint16_t *)g.B, g.ldb, g.C, g.ldc,
+                       g.sign, all_flag);
+    return hipGetLastError();
+}
+
+// Interior tiles: direct-to-LDS loads (256 x 256, K % 128 == 0), else buffer loads when
+// rows are 16-byte aligned and every offset fits in 31 bits, with the two-set pipeline
+// when the number of k-steps is even; ragged strips: predicated pointer loads.  The
+// accumulating variants (ACC) keep to the direct-to-LDS and pointer-load kernels, which
+// bounds the number of instances.
+template <typename T, int BM, int BN, int WM, int WN, int MINW, bool A_MN, bool B_MN, bool ACC>
+hipError_t launch_cfg(const GemmArgs &g, hipStream_t s) {
+    const bool vec = h16_vec(g);
+    const bool kfull = g.K % kBK == 0;
+    const int full_tiles = kfull ? (g.M / BM) * (g.N / BN) : 0;
+    const int edge_tiles = cdiv(g.M, BM) * cdiv(g.N, BN) - full_tiles;
+    const int all_flag = kfull ? 0 : 1;
+    const bool fits = op_fits(A_MN, BM, g.K, g.lda) && op_fits(B_MN, BN, g.K, g.ldb);
+    if (full_tiles > 0) {
+        hipError_t e;
+        if (use_dma(g, BM)) {
+            hipLaunchKernelGGL((mfma_f16_dma_kernel<T, A_MN, B_MN, ACC>), dim3(full_tiles),
+                               dim3(64 * dma::kWaves), 0, s, g.M, g.N, g.K, (const uint16_t *)g.A,
+                               g.lda, (const uint16_t *)g.B, g.ldb, g.C, g.ldc, g.sign);
+            e = hipGetLastError();
+        } else if (!ACC && vec && fits) {
+            if ((g.K / kBK) % 2 == 0)
+                e = launch_one<T, BM, BN, WM, WN, MINW, 2, false, true, A_MN, B_MN, false>(g, full_tiles, all_flag, s);
+            else
+                e = launch_one<T, BM, BN, WM, WN, MINW, 2, false, false, A_MN, B_MN, false>(g, full_tiles, all_flag, s);
+        } else if (vec) {
+            e = launch_one<T, BM, BN, WM, WN, MINW, 1, false, false, A_MN, B_MN, ACC>(g, full_tiles, all_flag, s);
+        } else {
+            e = launch_one<T, BM, BN, WM, WN, MINW, 0, false, false, A_MN, B_MN, ACC>(g, full_tiles, all_flag, s);
+        }
+        if (e != hipSuccess) return e;
+    }
+    if (edge_tiles > 0) {
+        if (vec) return launch_one<T, BM, BN, WM, WN, MINW, 1, true, false, A_MN, B_MN, ACC>(g, edge_tiles, all_flag, s);
+        return launch_one<T, BM, BN, WM, WN, MINW, 0, true, false, A_MN, B_MN, ACC>(g, edge_tiles, all_flag, s);
+    }
+    return hipSuccess;
+}
+
+// Cost model as for FP32: with w resident workgroups per CU a config needs
+// ceil(tiles / (256 w)) rounds of w * BM * BN work each; ties go to the larger tile,
+// whose LDS traffic per MFMA is half that of the smaller one.
+inline int pick_tile(const GemmArgs &g) {
+    struct Opt { int tile, per_cu; };
+    const Opt opts[] = {{256, 1}, {128, 2}};
+    long best = -1;
+    int tile = 128;
+    for (const Opt &o : opts) {
+        const long tiles = (long)cdiv(g.M, o.tile) * cdiv(g.N, o.tile);
+        const long slots = 256L * o.per_cu;
+        const long cost = (tiles + slots - 1) / slots * o.per_cu * (long)o.tile * o.tile;
+        if (best < 0 || cost < best) {
+            best = cost;
+            tile = o.tile;
+        }
+    }
+    return tile;
+}
+
+template <typename T, bool A_MN, bool B_MN, bool ACC>
+hipError_t launch_layout(const GemmArgs &g, hipStream_t s) {
+    if (pick_tile(g) == 256) return launch_cfg<T, 256, 256, 2, 2, 1, A_MN, B_MN, ACC>(g, s);
+    return launch_cfg<T, 128, 128, 2, 2, 2, A_MN, B_MN, ACC>(g, s);
+}
+
+}  // namespace
+
+}  // namespace g355

@@ -8,7 +8,8 @@
 //
 // gfx950 mapping: 64 x 4 threads per workgroup, the 64 lanes of a wave along a row of
 // C, so each B row segment and each C store is one contiguous 256-byte access and the
-// A element is a wave-uniform broadcast.
+// A element is a wave-uniform broadcast.  It also takes the transposed, negated and
+// accumulating forms directly (C = sign * op(A) op(B) (+ C)).
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -18,16 +19,39 @@ template <typename T>
 __global__ __launch_bounds__(256) void naive_gemm_kernel(int M, int N, int K,
                                                          const T *__restrict__ A, int lda,
                                                          const T *__restrict__ B, int ldb,
-                                                         float *__restrict__ C, int ldc) {
+                                                         float *__restrict__ C, int ldc,
+                                                         int trans_a, int trans_b, float sign,
+                                                         int accumulate) {
     const int col = blockIdx.x * 64 + threadIdx.x;
     const int row = blockIdx.y * 4 + threadIdx.y;
     if (row >= M || col >= N) return;
-    const T *a = A + (size_t)row * lda;
-    const T *b = B + col;
+    // op(A)[row][k] and op(B)[k][col]: a transposed A is stored K x M, a transposed B N x K
+    const T *a = trans_a ? A + row : A + (size_t)row * lda;
+    const size_t sa = trans_a ? (size_t)lda : 1;
+    const T *b = trans_b ? B + (size_t)col * ldb : B + col;
+    const size_t sb = trans_b ? 1 : (size_t)ldb;
     float acc = 0.0f;
     for (int k = 0; k < K; ++k)
-        acc = __builtin_fmaf(to_float(a[k]), to_float(b[(size_t)k * ldb]), acc);
-    C[(size_t)row * ldc + col] = acc;
+        acc = __builtin_fmaf(to_float(a[k * sa]), to_float(b[k * sb]), acc);
+    float *c = C + (size_t)row * ldc + col;
+    const float v = sign * acc;
+    *c = accumulate ? v + *c : v;
+}
+
+// C = -C on M x N (the sign of a negated product for the kernels that store their
+// accumulators as they are).
+__global__ __launch_bounds__(256) void negate_kernel(int M, int N, float *__restrict__ C, int ldc) {
+    const int col = blockIdx.x * 64 + threadIdx.x;
+    const int row = blockIdx.y * 4 + threadIdx.y;
+    if (row >= M || col >= N) return;
+    float *c = C + (size_t)row * ldc + col;
+    *c = -*c;
+}
+
+hipError_t launch_negate(const GemmArgs &g, hipStream_t s) {
+    hipLaunchKernelGGL(negate_kernel, dim3(cdiv(g.N, 64), cdiv(g.M, 4)), dim3(64, 4), 0, s, g.M,
+                       g.N, g.C, g.ldc);
+    return hipGetLastError();
 }
 
 hipError_t launch_naive(int dtype, const GemmArgs &g, hipStream_t s) {
@@ -36,15 +60,18 @@ hipError_t launch_naive(int dtype, const GemmArgs &g, hipStream_t s) {
     switch (dtype) {
     case kF32:
         hipLaunchKernelGGL(naive_gemm_kernel<float>, grid, block, 0, s, g.M, g.N, g.K,
-                           (const float *)g.A, g.lda, (const float *)g.B, g.ldb, g.C, g.ldc);
+                           (const float *)g.A, g.lda, (const float *)g.B, g.ldb, g.C, g.ldc,
+                           g.trans_a, g.trans_b, g.sign, g.accumulate);
         break;
     case kF16:
         hipLaunchKernelGGL(naive_gemm_kernel<f16_t>, grid, block, 0, s, g.M, g.N, g.K,
-                           (const f16_t *)g.A, g.lda, (const f16_t *)g.B, g.ldb, g.C, g.ldc);
+                           (const f16_t *)g.A, g.lda, (const f16_t *)g.B, g.ldb, g.C, g.ldc,
+                           g.trans_a, g.trans_b, g.sign, g.accumulate);
         break;
     default:
         hipLaunchKernelGGL(naive_gemm_kernel<bf16_t>, grid, block, 0, s, g.M, g.N, g.K,
-                           (const bf16_t *)g.A, g.lda, (const bf16_t *)g.B, g.ldb, g.C, g.ldc);
+                           (const bf16_t *)g.A, g.lda, (const bf16_t *)g.B, g.ldb, g.C, g.ldc,
+                           g.trans_a, g.trans_b, g.sign, g.accumulate);
         break;
     }
     return hipGetLastError();

@@ -132,6 +132,28 @@ def test_probe_argument_checks(lib):
     assert gb.gemm355_probe_ds_read_tr16([8 * i for i in range(63)] + [4096], P) == gb.ERR_INVALID_ARG
 
 
+def test_gemm_ex_argument_checks(lib):
+    E = gb.gemm355_gemm_ex
+    # M=8, N=6, K=4: stored A is 8 x 4 (or 4 x 8 transposed), B 4 x 6 (or 6 x 4)
+    assert E(0, 0, 32, 8, 6, 4, P, 4, P, 6, P, 6) == gb.ERR_INVALID_ARG          # unknown flag
+    assert E(0, 0, gb.TRANS_A, 8, 6, 4, P, 4, P, 6, P, 6) == gb.ERR_INVALID_ARG  # lda < M
+    assert E(0, 0, gb.TRANS_B, 8, 6, 4, P, 4, P, 2, P, 6) == gb.ERR_INVALID_ARG  # ldb < K
+    assert E(0, 0, 0, 8, 6, 4, P, 3, P, 6, P, 6) == gb.ERR_INVALID_ARG           # lda < K
+    assert E(0, 0, 0, 8, 6, 4, P, 4, P, 6, P, 5) == gb.ERR_INVALID_ARG           # ldc < N
+    assert E(0, 3, 0, 8, 6, 4, P, 4, P, 6, P, 6) == gb.ERR_INVALID_ARG           # dtype
+    assert E(7, 0, 0, 8, 6, 4, P, 4, P, 6, P, 6) == gb.ERR_INVALID_ARG           # variant
+    assert E(0, 0, 0, 8, 6, 4, 0, 4, P, 6, P, 6) == gb.ERR_INVALID_ARG           # null A
+    # with a flag only the naive and MFMA families exist
+    for v in (gb.VARIANT_LDS_TILED, gb.VARIANT_REGBLOCK):
+        assert E(v, 0, gb.NEG_A, 8, 6, 4, P, 4, P, 6, P, 6) == gb.ERR_UNSUPPORTED
+    # valid arguments reach the device check (no GPU here) or run
+    for f in (0, gb.TRANS_A, gb.TRANS_B, gb.TRANS_A | gb.TRANS_B | gb.NEG_A | gb.ACCUMULATE):
+        lda = 8 if f & gb.TRANS_A else 4
+        ldb = 4 if f & gb.TRANS_B else 6
+        assert E(-1, 0, f, 8, 6, 4, P, lda, P, ldb, P, 6) in (gb.OK, gb.ERR_DEVICE)
+    assert E(-1, 0, gb.ACCUMULATE, 0, 6, 4, P, 4, P, 6, P, 6) == gb.OK            # M = 0
+
+
 def test_stream_and_chase_argument_checks(lib):
     ok = dict(mode=gb.STREAM_COPY, src=P, dst=P + (1 << 20), n_bytes=4096, vec_bytes=16, unroll=4,
               threads=256, lds_bytes=0, grid=256)

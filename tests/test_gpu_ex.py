@@ -1,0 +1,166 @@
+"""GPU parity of the general form C = s op(A) op(B) (+ C) (``gemm355_gemm_ex``: transposed
+and negated operands, accumulation into C; the tensor-core instruction table of
+"Advanced CUDA features - starting from GEMM") against the oracle, through the C ABI.
+
+Bars as for the plain product (relative Frobenius error of the result against the
+oracle's binary64 value: 1e-5 FP32 with max-abs 1e-4 sqrt(K) (+ the old C's scale when
+accumulating), 1e-3 FP16/BF16; small integers bit-exact).  Stored operands sit in
+NaN-padded buffers with guard rows; C sits between sentinel guard words, and its M x N
+region starts as NaN when it is overwritten (so every element must be written) or as
+the values to accumulate into.
+"""
+
+from __future__ import annotations
+
+import itertools
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import NP_STORAGE, errors, nan_fill, place, to_device
+from roofline_optimisation_amd import binding as gb
+from roofline_optimisation_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+SENT = np.float32(7777.0)
+GUARD = 64
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def flags_of(ta, tb, na, nb, acc):
+    return ((gb.TRANS_A if ta else 0) | (gb.TRANS_B if tb else 0) | (gb.NEG_A if na else 0)
+            | (gb.NEG_B if nb else 0) | (gb.ACCUMULATE if acc else 0))
+
+
+def run_ex(opA, opB, dtype, ta, tb, na, nb, acc, Cin=None, variant=gb.VARIANT_AUTO,
+           pad=(0, 0, 0)):
+    """Run the GPU form on op(A) (M x K) and op(B) (K x N) stored as the flags say.
+    Returns (C, intact, stored A, stored B)."""
+    import torch
+    M, K = opA.shape
+    N = opB.shape[1]
+    SA = np.ascontiguousarray(opA.T) if ta else opA
+    SB = np.ascontiguousarray(opB.T) if tb else opB
+    lda, ldb, ldc = SA.shape[1] + pad[0], SB.shape[1] + pad[1], N + pad[2]
+    dA = to_device(place(SA, max(lda, 1), 0, 1, nan_fill(dtype)))
+    dB = to_device(place(SB, max(ldb, 1), 0, 1, nan_fill(dtype)))
+    cbuf = np.full(2 * GUARD + M * ldc, SENT, np.float32)
+    region = cbuf[GUARD:GUARD + M * ldc].reshape(M, ldc)
+    region[:, :N] = Cin if acc else np.float32(np.nan)
+    dC = to_device(cbuf)
+    st = gb.gemm355_gemm_ex(variant, gb.DTYPE_CODES[dtype], flags_of(ta, tb, na, nb, acc), M, N, K,
+                            dA.data_ptr(), max(lda, 1), dB.data_ptr(), max(ldb, 1),
+                            dC.data_ptr() + 4 * GUARD, max(ldc, 1),
+                            torch.cuda.current_stream().cuda_stream)
+    assert st == gb.OK, st
+    torch.cuda.synchronize()
+    out = dC.cpu().numpy()
+    C = out[GUARD:GUARD + M * ldc].reshape(M, ldc)[:, :N].copy()
+    mask = np.ones(out.shape, bool)
+    mask[GUARD:GUARD + M * ldc].reshape(M, ldc)[:, :N] = False
+    return C, bool(np.all(out[mask] == SENT)), SA, SB
+
+
+def check(C, C64, dtype, K, Cin, intact, what):
+    assert intact, f"{what}: wrote outside C"
+    assert not np.isnan(C).any(), f"{what}: NaN (an element not written, or a read outside)"
+    rel, mx = errors(C, C64)
+    trel = 1e-5 if dtype == "f32" else 1e-3
+    # FP32 absolute bound: 1e-4 sqrt(K) for the sum, plus one rounding of the old C
+    tabs = (1e-4 * np.sqrt(max(K, 1)) + (np.abs(Cin).max() * 2 ** -23 if Cin is not None else 0)
+            if dtype == "f32" else np.inf)
+    print(f"{what}: rel_frob={rel:.3e} max_abs={mx:.3e}", flush=True)
+    assert rel <= trel and mx <= tabs, f"{what}: rel {rel:.3e} (<= {trel}), max {mx:.3e} (<= {tabs})"
+
+
+def operands(M, N, K, dtype, seed, dist="uniform"):
+    A, B = inputs.make_operands(M, N, K, seed, dist, dtype)
+    Cin = np.random.default_rng(seed + 1000).uniform(-1, 1, (M, N)).astype(np.float32)
+    return A, B, Cin
+
+
+def compare(M, N, K, dtype, ta, tb, na, nb, acc, seed, variant=gb.VARIANT_AUTO, pad=(0, 0, 0)):
+    A, B, Cin = operands(M, N, K, dtype, seed)
+    C, ok, SA, SB = run_ex(A, B, dtype, ta, tb, na, nb, acc, Cin, variant, pad)
+    C64, _ = oracle.gemm_ex(SA, SB, dtype, ta, tb, na, nb, Cin if acc else None)
+    check(C, C64, dtype, K, Cin if acc else None, ok,
+          f"ex {dtype} {M}x{N}x{K} ta={ta} tb={tb} na={na} nb={nb} acc={acc} v={variant} pad={pad}")
+
+
+FLAGS = list(itertools.product([False, True], repeat=5))
+
+
+@pytest.mark.parametrize("variant", [gb.VARIANT_MFMA, gb.VARIANT_NAIVE], ids=["mfma", "naive"])
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("fl", FLAGS, ids=lambda f: "".join(n for n, b in zip(("ta", "tb", "na", "nb", "acc"), f) if b) or "plain")
+def test_flag_matrix_ragged(fl, dtype, variant):
+    compare(129, 97, 75, dtype, *fl, seed=50, variant=variant)
+
+
+# Interior tiles of every layout: FP32 192 x 192 (3072), 128 x 128; FP16/BF16 256 x 256
+# direct-to-LDS (3072^2, K % 128 == 0), 256 x 256 register-staged (K % 128 != 0) and
+# 128 x 128; each plain, negated and accumulating.
+LAYOUTS = list(itertools.product([False, True], repeat=2))
+MODES = [(False, False, False), (True, False, False), (False, True, True)]  # na, nb, acc
+SHAPES = {"f32": [(3072, 3072, 64), (1024, 768, 96)],
+          "f16": [(3072, 3072, 128), (3072, 2816, 192), (1024, 1024, 128)],
+          "bf16": [(3072, 3072, 256), (1024, 512, 64)]}
+
+
+@pytest.mark.parametrize("mode", MODES, ids=["plain", "neg_a", "neg_b_acc"])
+@pytest.mark.parametrize("layout", LAYOUTS, ids=lambda l: f"ta{int(l[0])}tb{int(l[1])}")
+@pytest.mark.parametrize("dtype,shape", [(d, s) for d in SHAPES for s in SHAPES[d]],
+                         ids=lambda x: x if isinstance(x, str) else "x".join(map(str, x)))
+def test_tiles_every_layout(dtype, shape, layout, mode):
+    compare(*shape, dtype, *layout, *mode, seed=51)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("layout", LAYOUTS, ids=lambda l: f"ta{int(l[0])}tb{int(l[1])}")
+def test_unaligned_strides(dtype, layout):
+    """Row strides that are not multiples of 16 bytes take the narrow-load paths."""
+    compare(300, 260, 130, dtype, *layout, False, False, True, seed=52, pad=(1, 3, 2))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("fl", [(True, False, True, False, True), (False, True, False, False, False),
+                                (True, True, True, True, True)],
+                         ids=["ta_na_acc", "tb", "all"])
+def test_integers_bit_exact(dtype, fl):
+    for (M, N, K) in [(257, 130, 77), (512, 512, 256)]:
+        A, B = inputs.make_operands(M, N, K, 53, "int", dtype)
+        Cin = np.random.default_rng(54).integers(-50, 51, (M, N)).astype(np.float32)
+        C, ok, SA, SB = run_ex(A, B, dtype, *fl, Cin)
+        _, C32 = oracle.gemm_ex(SA, SB, dtype, *fl[:4], Cin if fl[4] else None)
+        assert ok and np.array_equal(C, C32), (dtype, fl, M, N, K)
+
+
+def test_k_zero():
+    import torch
+    # K = 0: C = +0 (negated: -0, equal in value), or C unchanged when accumulating
+    for acc in (False, True):
+        A = np.zeros((5, 0), np.float32)
+        B = np.zeros((0, 7), np.float32)
+        Cin = np.arange(35, dtype=np.float32).reshape(5, 7)
+        C, ok, _, _ = run_ex(A, B, "f32", False, False, True, False, acc, Cin)
+        assert ok and np.array_equal(C, Cin if acc else np.zeros((5, 7), np.float32))
+
+
+def test_matmul_wrapper_options():
+    import torch
+    A, B, Cin = operands(70, 50, 40, "f32", 55)
+    dA = torch.from_numpy(np.ascontiguousarray(A.T)).cuda()
+    dB = torch.from_numpy(np.ascontiguousarray(B.T)).cuda()
+    out = torch.from_numpy(Cin.copy()).cuda()
+    gb.matmul(dA, dB, out=out, trans_a=True, trans_b=True, neg_a=True, accumulate=True)
+    C64, _ = oracle.gemm_ex(np.ascontiguousarray(A.T), np.ascontiguousarray(B.T), "f32", True, True,
+                            True, False, Cin)
+    check(out.cpu().numpy(), C64, "f32", 40, Cin, True, "matmul wrapper ex")
