@@ -179,6 +179,62 @@ def time_variant(variant, dtype, M, N, K, seed, reps=None):
     return e0.elapsed_time(e1) / reps, desc, reps
 
 
+def general_form_lines():
+    """Markdown lines timing gemm355_gemm_ex (transposed / negated operands, accumulation)
+    at the headline sizes, against the plain product."""
+    import numpy as np
+    import torch
+
+    from roofline_optimisation_amd import binding as gb
+    from roofline_optimisation_amd import inputs
+
+    lines = ["", "## General form C = s op(A) op(B) (+ C) (`gemm355_gemm_ex`)", "",
+             "Same timing method; op(A) = A^T means A is stored K x M, op(B) = B^T means B is stored",
+             "N x K.  TFLOP/s counts 2MNK (the addition of the old C is not counted).  Negated and",
+             "accumulating calls run the kernels' signed variants, which store sign * acc (+ C).", "",
+             "| dtype | n | layout | mode | kernel path | time (us) | TFLOP/s | % of peak | vs plain NN |",
+             "|---|---|---|---|---|---|---|---|---|"]
+    stream = torch.cuda.Stream()
+    for dt, n, seed in (("f32", 3072, 1), ("f16", 4096, 3)):
+        A, B = inputs.make_operands(n, n, n, seed, "uniform", dt)
+        conv = (lambda x: torch.from_numpy(x).cuda()) if dt == "f32" else \
+            (lambda x: torch.from_numpy(x.view("int16")).cuda())
+        dA, dB = conv(np.ascontiguousarray(A)), conv(np.ascontiguousarray(B))
+        dAt, dBt = conv(np.ascontiguousarray(A.T)), conv(np.ascontiguousarray(B.T))
+        dC = torch.zeros((n, n), dtype=torch.float32, device="cuda")
+        base = None
+        for layout, (ta, tb) in (("NN", (0, 0)), ("NT", (0, 1)), ("TN", (1, 0)), ("TT", (1, 1))):
+            for mode, extra in (("plain", 0), ("negated", gb.NEG_A), ("accumulate", gb.ACCUMULATE)):
+                flags = (gb.TRANS_A if ta else 0) | (gb.TRANS_B if tb else 0) | extra
+                a = dAt if ta else dA
+                b = dBt if tb else dB
+                args = (gb.VARIANT_AUTO, gb.DTYPE_CODES[dt], flags, n, n, n, a.data_ptr(), n,
+                        b.data_ptr(), n, dC.data_ptr(), n, stream.cuda_stream)
+
+                def go():
+                    st = gb.gemm355_gemm_ex(*args)
+                    if st != gb.OK:
+                        raise gb.Gemm355Error(st, "gemm355_gemm_ex")
+                for _ in range(60):
+                    go()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for _ in range(100):
+                    go()
+                e1.record(stream)
+                stream.synchronize()
+                ms = e0.elapsed_time(e1) / 100
+                tf = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+                if base is None:
+                    base = ms
+                path = "plain" if mode == "plain" else "signed / accumulating variant"
+                lines.append(f"| {dt} | {n} | {layout} | {mode} | {path} | {ms * 1e3:.1f} | {tf:.1f} | "
+                             f"{100 * tf / PEAKS[dt]:.1f} | {base / ms:.2f} |")
+                log(f"[report] ex {dt} {n} {layout} {mode}: {ms * 1e3:.1f} us {tf:.1f} TFLOP/s")
+        del dA, dB, dAt, dBt, dC
+    return lines
+
+
 def memory_slope_lines():
     """Markdown lines for the memory-slope probe: HBM read bandwidth against resident waves
     per CU and bytes in flight per wave, dependent-load latency, and the Little's-law
@@ -349,6 +405,7 @@ def write_report(path):
         lines.append(f"| {c.dtype} | {c.M}x{c.N}x{c.K} | {desc} | {ms * 1e3:.1f} | {tf:.1f} | "
                      f"{100 * e['frac']:.1f} | {e['oi']:.1f} | {e['attainable_tflops']:.0f} | {bound} |")
         log(f"[report] {c.name}: {ms * 1e3:.1f} us {tf:.1f} TFLOP/s")
+    lines += general_form_lines()
     lines += memory_slope_lines()
     with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")

@@ -127,12 +127,9 @@ enum {
  * GEMM355_TRANS_B), ldc >= max(1, N).  `variant` and `dtype` as for gemm355_run_variant;
  * with any flag set only NAIVE, MFMA and AUTO (= MFMA) are available (others return
  * GEMM355_ERR_UNSUPPORTED).  Unknown flag bits are GEMM355_ERR_INVALID_ARG.
- * Accumulation: the MFMA kernels add s * (their FP32 sum) to the old C in the epilogue,
- * the naive kernel likewise, one rounding each.  K = 0: C = +0.0 without
- * GEMM355_ACCUMULATE (then negated when s = -1), C unchanged with it.  A negated
- * product without GEMM355_ACCUMULATE on MFMA runs a second, elementwise kernel that
- * negates C on the same stream.  Everything else (ownership, asynchrony, errors) as
- * for gemm_f32. */
+ * Accumulation: every kernel adds s * (its FP32 sum) to the old C in its epilogue, one
+ * rounding.  K = 0: C = s * (+0.0) without GEMM355_ACCUMULATE, C unchanged with it.
+ * Everything else (ownership, asynchrony, errors) as for gemm_f32. */
 gemm355_status gemm355_gemm_ex(int variant, int dtype, unsigned flags, int M, int N, int K,
                                const void *A, int lda, const void *B, int ldb, float *C, int ldc,
                                hipStream_t stream);

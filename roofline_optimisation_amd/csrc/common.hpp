@@ -45,6 +45,9 @@ struct GemmArgs {
     int trans_a = 0, trans_b = 0;
     float sign = 1.0f;
     int accumulate = 0;
+    // The MFMA kernels have plain variants (store the accumulators as they are) and
+    // variants that store sign * acc (+ C); the latter serve negated products too.
+    bool signed_or_acc() const { return accumulate || sign < 0.0f; }
 };
 
 // Stores one 32 x 32 MFMA accumulator block: register r of this lane holds row
@@ -66,8 +69,9 @@ __device__ __forceinline__ void store_block32(const floatx16 &acc, float *__rest
     }
 }
 
-// The same block for kernels that accumulate into C: c = sign * acc + c (sign = +1 or
-// -1).  The block is done in two halves of 8 rows; the fences keep each half's loads
+// The same block for the variants that apply a sign or accumulate: c = sign * acc
+// (+ c when use_old; sign = +1 or -1).  The block is done in two halves of 8 rows; the
+// fences keep each half's loads
 // together and apart from the rest, so that few old values are live at a time.  AREAD:
 // the accumulators live in the AGPR file; each is read with its own v_accvgpr_read at
 // its point of use (otherwise the compiler copies all of them to VGPRs at once when the
@@ -75,7 +79,7 @@ __device__ __forceinline__ void store_block32(const floatx16 &acc, float *__rest
 template <bool EDGE, bool NT, bool AREAD>
 __device__ __forceinline__ void store_block32_acc(const floatx16 &acc, float *__restrict__ C,
                                                   int ldc, int row0, int col, int M, int N,
-                                                  float sign) {
+                                                  float sign, int use_old) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         __builtin_amdgcn_sched_barrier(0);
@@ -84,7 +88,7 @@ __device__ __forceinline__ void store_block32_acc(const floatx16 &acc, float *__
         for (int q = 0; q < 8; ++q) {
             const int r = 8 * h + q;
             const int row = row0 + 8 * (r / 4) + r % 4;
-            const bool ok = !EDGE || (row < M && col < N);
+            const bool ok = use_old && (!EDGE || (row < M && col < N));
             old[q] = ok ? C[(size_t)(ok ? row : 0) * ldc + (ok ? col : 0)] : 0.f;
         }
 #pragma unroll

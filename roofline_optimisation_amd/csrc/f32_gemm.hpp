@@ -27,8 +27,8 @@
 //    the tensor-core instruction table of "Advanced CUDA features - starting from
 //    GEMM"): an operand stored with k contiguous (kind KM: A, or a transposed B) takes
 //    the A path above, one stored with m or n contiguous (kind MN: B, or a transposed
-//    A) the B path; the plain kernels store the accumulators as they are (a separate
-//    pass negates C), the accumulating variants (ACC) add sign * acc to the old C.
+//    A) the B path; the plain kernels store the accumulators as they are, the signed /
+//    accumulating variants (ACC) store sign * acc, plus the old C when accumulating.
 #pragma once
 
 #include <type_traits>
@@ -108,8 +108,8 @@ template <int BM, int BN, int WM, int WN, int LOAD, bool EDGE, bool PAIRED, bool
           bool ACC>
 __device__ __forceinline__ void f32_tile(int M, int N, int K, const float *__restrict__ A, int lda,
                                          const float *__restrict__ B, int ldb,
-                                         float *__restrict__ C, int ldc, float sign, int m0,
-                                         int n0, float *lds) {
+                                         float *__restrict__ C, int ldc, float sign,
+                                         int use_old, int m0, int n0, float *lds) {
     using Cfg = F32Cfg<BM, BN, WM, WN, A_MN, B_MN>;
     using OA = typename Cfg::OA;
     using OB = typename Cfg::OB;
@@ -307,7 +307,7 @@ __device__ __forceinline__ void f32_tile(int M, int N, int K, const float *__res
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
             const int row0 = m0 + wm * Cfg::kTM + 32 * i + 4 * lhi, col = n0 + b_rc0 + 32 * j;
-            if constexpr (ACC) store_block32_acc<EDGE, false, false>(acc[i][j], C, ldc, row0, col, M, N, sign);
+            if constexpr (ACC) store_block32_acc<EDGE, false, false>(acc[i][j], C, ldc, row0, col, M, N, sign, use_old);
             else store_block32<EDGE, false>(acc[i][j], C, ldc, row0, col, M, N);
         }
 }
@@ -338,7 +338,7 @@ template <int BM, int BN, int WM, int WN, int MINW, int LOAD, bool EDGE, bool PA
 __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(MINW)))
 void mfma_f32_gemm_kernel(int M, int N, int K, const float *__restrict__ A, int lda,
                           const float *__restrict__ B, int ldb, float *__restrict__ C, int ldc,
-                          float sign, int all_tiles) {
+                          float sign, int use_old, int all_tiles) {
     using Cfg = F32Cfg<BM, BN, WM, WN, A_MN, B_MN>;
     __shared__ __attribute__((aligned(16))) float lds[2 * (Cfg::kLdsA + Cfg::kLdsB)];
     const int tiles_m = EDGE ? cdiv(M, BM) : M / BM;
@@ -346,7 +346,8 @@ void mfma_f32_gemm_kernel(int M, int N, int K, const float *__restrict__ A, int 
     int tm, tn;
     tile_of<EDGE>(blockIdx.x, gridDim.x, tiles_m, tiles_n, N % BN != 0, all_tiles != 0, tm, tn);
     f32_tile<BM, BN, WM, WN, LOAD, EDGE, PAIRED, A_MN, B_MN, ACC>(M, N, K, A, lda, B, ldb, C, ldc,
-                                                                 sign, tm * BM, tn * BN, lds);
+                                                                 sign, use_old, tm * BM, tn * BN,
+                                                                 lds);
 }
 
 struct F32Pick {
@@ -384,7 +385,7 @@ template <int BM, int BN, int WM, int WN, int MINW, int LOAD, bool EDGE, bool PA
 hipError_t launch_one(const GemmArgs &g, int tiles, int all_flag, hipStream_t s) {
     hipLaunchKernelGGL((mfma_f32_gemm_kernel<BM, BN, WM, WN, MINW, LOAD, EDGE, PAIRED, A_MN, B_MN, ACC>),
                        dim3(tiles), dim3(64 * WM * WN), 0, s, g.M, g.N, g.K, (const float *)g.A,
-                       g.lda, (const float *)g.B, g.ldb, g.C, g.ldc, g.sign, all_flag);
+                       g.lda, (const float *)g.B, g.ldb, g.C, g.ldc, g.sign, g.accumulate, all_flag);
     return hipGetLastError();
 }
 
@@ -396,8 +397,8 @@ inline bool f32_fits(bool mn, int ext, int K, int ld) {
 // MINW: waves per SIMD the register budget must allow (resident workgroups per CU
 // times waves per workgroup / 4).  Full interior tiles go to the straight-line kernel
 // (buffer loads when rows are 16-byte aligned and offsets fit in 31 bits); ragged
-// strips (or every tile, when K is not a multiple of BK) to the predicated one.  The
-// accumulating variants (ACC) keep to pointer loads, which bounds the instances.
+// strips (or every tile, when K is not a multiple of BK) to the predicated one.  ACC:
+// the variants that store sign * acc (+ C).
 template <int BM, int BN, int WM, int WN, int MINW, bool A_MN, bool B_MN, bool ACC>
 hipError_t launch_cfg(const GemmArgs &g, bool vec, hipStream_t s) {
     const bool kfull = g.K % kBK == 0;
@@ -406,11 +407,11 @@ hipError_t launch_cfg(const GemmArgs &g, bool vec, hipStream_t s) {
     const int all_flag = kfull ? 0 : 1;
     const bool fits = f32_fits(A_MN, BM, g.K, g.lda) && f32_fits(B_MN, BN, g.K, g.ldb);
     if (full_tiles > 0) {
-        hipError_t e;
-        if (!ACC && vec && fits && (g.K / kBK) % 2 == 0)
-            e = launch_one<BM, BN, WM, WN, MINW, 2, false, true, A_MN, B_MN, false>(g, full_tiles, all_flag, s);
-        else if (!ACC && vec && fits)
-            e = launch_one<BM, BN, WM, WN, MINW, 2, false, false, A_MN, B_MN, false>(g, full_tiles, all_flag, s);
+        hipError_t e = hipSuccess;
+        if (vec && fits && (g.K / kBK) % 2 == 0)
+            e = launch_one<BM, BN, WM, WN, MINW, 2, false, true, A_MN, B_MN, ACC>(g, full_tiles, all_flag, s);
+        else if (vec && fits)
+            e = launch_one<BM, BN, WM, WN, MINW, 2, false, false, A_MN, B_MN, ACC>(g, full_tiles, all_flag, s);
         else if (vec)
             e = launch_one<BM, BN, WM, WN, MINW, 1, false, false, A_MN, B_MN, ACC>(g, full_tiles, all_flag, s);
         else

@@ -119,12 +119,7 @@ gemm355_status run_ex(int variant, int dtype, unsigned flags, int M, int N, int 
     if (M == 0 || N == 0) return GEMM355_OK;
     if (!device_ok()) return GEMM355_ERR_DEVICE;
     if (K == 0 && acc) return GEMM355_OK;  // adding the empty sum leaves C as it is
-    if (launch(variant, dtype, g, stream) != hipSuccess) return GEMM355_ERR_LAUNCH;
-    // the MFMA kernels store their accumulators as they are; the naive kernel and the
-    // accumulating variants apply the sign themselves
-    if (neg && !acc && variant == GEMM355_VARIANT_MFMA && launch_negate(g, stream) != hipSuccess)
-        return GEMM355_ERR_LAUNCH;
-    return GEMM355_OK;
+    return launch(variant, dtype, g, stream) == hipSuccess ? GEMM355_OK : GEMM355_ERR_LAUNCH;
 }
 
 }  // namespace

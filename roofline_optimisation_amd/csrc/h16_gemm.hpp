@@ -26,9 +26,9 @@
 //    c + 4q + 3, and output lane j receives column c + j%16 for rows k .. k+3;
 //  * interior tiles (inside M x N, K a multiple of BK) run a straight-line kernel; the
 //    ragged strips run a predicated one that zero-fills loads and guards stores;
-//  * C = sign * op(A) op(B) (+ C): the plain kernels store the accumulators as they are
-//    (a separate pass negates C for sign -1); the accumulating variants (ACC) load the
-//    old C block by block in the epilogue and store sign * acc + C.
+//  * C = sign * op(A) op(B) (+ C): the plain kernels store the accumulators as they are;
+//    the signed / accumulating variants (ACC) store sign * acc, adding the old C (loaded
+//    block by block in the epilogue) when accumulating.
 //
 // Interior 256 x 256 tiles with K a multiple of 128 take a second design (dma_tile
 // below): the tiles go from memory straight into LDS (buffer_load_dwordx4 ... lds)
@@ -144,8 +144,8 @@ template <typename T, int BM, int BN, int WM, int WN, int LOAD, bool EDGE, bool 
           bool A_MN, bool B_MN, bool ACC>
 __device__ __forceinline__ void h16_tile(int M, int N, int K, const uint16_t *__restrict__ A,
                                          int lda, const uint16_t *__restrict__ B, int ldb,
-                                         float *__restrict__ C, int ldc, float sign, int m0,
-                                         int n0, uint16_t *lds) {
+                                         float *__restrict__ C, int ldc, float sign,
+                                         int use_old, int m0, int n0, uint16_t *lds) {
     using Cfg = H16Cfg<BM, BN, WM, WN, A_MN, B_MN>;
     using OA = typename Cfg::OA;
     using OB = typename Cfg::OB;
@@ -379,7 +379,7 @@ __device__ __forceinline__ void h16_tile(int M, int N, int K, const uint16_t *__
         {
             const int row0 = m0 + wm * Cfg::kTM + 32 * i + 4 * lhi;
             const int col = n0 + wn * Cfg::kTN + 32 * j + l32;
-            if constexpr (ACC) store_block32_acc<EDGE, true, (MB * NB > 8)>(acc[i][j], C, ldc, row0, col, M, N, sign);
+            if constexpr (ACC) store_block32_acc<EDGE, true, (MB * NB > 8)>(acc[i][j], C, ldc, row0, col, M, N, sign, use_old);
             else store_block32<EDGE, true>(acc[i][j], C, ldc, row0, col, M, N);
         }
 }
@@ -409,7 +409,7 @@ template <typename T, int BM, int BN, int WM, int WN, int MINW, int LOAD, bool E
 __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(MINW)))
 void mfma_f16_gemm_kernel(int M, int N, int K, const uint16_t *__restrict__ A, int lda,
                           const uint16_t *__restrict__ B, int ldb, float *__restrict__ C, int ldc,
-                          float sign, int all_tiles) {
+                          float sign, int use_old, int all_tiles) {
     using Cfg = H16Cfg<BM, BN, WM, WN, A_MN, B_MN>;
     __shared__ __attribute__((aligned(16))) uint16_t lds[2 * (Cfg::kLdsA + Cfg::kLdsB)];
     const int tiles_m = EDGE ? cdiv(M, BM) : M / BM;
@@ -417,7 +417,7 @@ void mfma_f16_gemm_kernel(int M, int N, int K, const uint16_t *__restrict__ A, i
     int tm, tn;
     h16_tile_of<EDGE>(blockIdx.x, gridDim.x, tiles_m, tiles_n, N % BN != 0, all_tiles != 0, tm, tn);
     h16_tile<T, BM, BN, WM, WN, LOAD, EDGE, PAIRED, A_MN, B_MN, ACC>(
-        M, N, K, A, lda, B, ldb, C, ldc, sign, tm * BM, tn * BN, lds);
+        M, N, K, A, lda, B, ldb, C, ldc, sign, use_old, tm * BM, tn * BN, lds);
 }
 
 // Every row of both operands starts on a 16-byte boundary.
@@ -562,8 +562,8 @@ struct DmaOp {
 template <typename T, bool A_MN, bool B_MN, bool ACC>
 __device__ __forceinline__ void dma_tile(int K, const uint16_t *__restrict__ A, int lda,
                                          const uint16_t *__restrict__ B, int ldb,
-                                         float *__restrict__ C, int ldc, float sign, int m0,
-                                         int n0, char *lds_raw) {
+                                         float *__restrict__ C, int ldc, float sign,
+                                         int use_old, int m0, int n0, char *lds_raw) {
     const int lane = threadIdx.x % 64;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
     const int wm = wave / kWN, wn = wave % kWN;
@@ -673,7 +673,7 @@ __device__ __forceinline__ void dma_tile(int K, const uint16_t *__restrict__ A, 
         for (int j = 0; j < kNB; ++j)
         {
             const int row0 = m0 + wm * kTM + 32 * i + 4 * lhi, col = n0 + wn * kTN + 32 * j + l32;
-            if constexpr (ACC) store_block32_acc<false, true, true>(acc[i][j], C, ldc, row0, col, 0, 0, sign);
+            if constexpr (ACC) store_block32_acc<false, true, true>(acc[i][j], C, ldc, row0, col, 0, 0, sign, use_old);
             else store_block32<false, true>(acc[i][j], C, ldc, row0, col, 0, 0);
         }
 }
@@ -684,12 +684,12 @@ template <typename T, bool A_MN, bool B_MN, bool ACC>
 __global__ __launch_bounds__(64 * dma::kWaves) __attribute__((amdgpu_waves_per_eu(1)))
 void mfma_f16_dma_kernel(int M, int N, int K, const uint16_t *__restrict__ A, int lda,
                          const uint16_t *__restrict__ B, int ldb, float *__restrict__ C,
-                         int ldc, float sign) {
+                         int ldc, float sign, int use_old) {
     __shared__ __attribute__((aligned(1024))) char lds[dma::kLds];
     int tm, tn;
     grouped_tile(xcd_contiguous_id(blockIdx.x, gridDim.x), M / dma::kBM, N / dma::kBN, 4, tm, tn);
-    dma::dma_tile<T, A_MN, B_MN, ACC>(K, A, lda, B, ldb, C, ldc, sign, tm * dma::kBM, tn * dma::kBN,
-                                 lds);
+    dma::dma_tile<T, A_MN, B_MN, ACC>(K, A, lda, B, ldb, C, ldc, sign, use_old, tm * dma::kBM,
+                                      tn * dma::kBN, lds);
 }
 
 // Byte offsets below 2^31 for every chunk of a 256-extent tile of the operand.
@@ -713,15 +713,15 @@ hipError_t launch_one(const GemmArgs &g, int tiles, int all_flag, hipStream_t s)
     hipLaunchKernelGGL((mfma_f16_gemm_kernel<T, BM, BN, WM, WN, MINW, LOAD, EDGE, PAIRED, A_MN, B_MN, ACC>),
                        dim3(tiles), dim3(64 * WM * WN), 0, s, g.M, g.N, g.K,
                        (const uint16_t *)g.A, g.lda, (const uint16_t *)g.B, g.ldb, g.C, g.ldc,
-                       g.sign, all_flag);
+                       g.sign, g.accumulate, all_flag);
     return hipGetLastError();
 }
 
 // Interior tiles: direct-to-LDS loads (256 x 256, K % 128 == 0), else buffer loads when
 // rows are 16-byte aligned and every offset fits in 31 bits, with the two-set pipeline
 // when the number of k-steps is even; ragged strips: predicated pointer loads.  The
-// accumulating variants (ACC) keep to the direct-to-LDS and pointer-load kernels, which
-// bounds the number of instances.
+// signed / accumulating variants (ACC) keep to the direct-to-LDS and pointer-load
+// kernels, which bounds the number of instances.
 template <typename T, int BM, int BN, int WM, int WN, int MINW, bool A_MN, bool B_MN, bool ACC>
 hipError_t launch_cfg(const GemmArgs &g, hipStream_t s) {
     const bool vec = h16_vec(g);
@@ -731,17 +731,19 @@ hipError_t launch_cfg(const GemmArgs &g, hipStream_t s) {
     const int all_flag = kfull ? 0 : 1;
     const bool fits = op_fits(A_MN, BM, g.K, g.lda) && op_fits(B_MN, BN, g.K, g.ldb);
     if (full_tiles > 0) {
-        hipError_t e;
+        hipError_t e = hipSuccess;
         if (use_dma(g, BM)) {
             hipLaunchKernelGGL((mfma_f16_dma_kernel<T, A_MN, B_MN, ACC>), dim3(full_tiles),
                                dim3(64 * dma::kWaves), 0, s, g.M, g.N, g.K, (const uint16_t *)g.A,
-                               g.lda, (const uint16_t *)g.B, g.ldb, g.C, g.ldc, g.sign);
+                               g.lda, (const uint16_t *)g.B, g.ldb, g.C, g.ldc, g.sign, g.accumulate);
             e = hipGetLastError();
         } else if (!ACC && vec && fits) {
-            if ((g.K / kBK) % 2 == 0)
-                e = launch_one<T, BM, BN, WM, WN, MINW, 2, false, true, A_MN, B_MN, false>(g, full_tiles, all_flag, s);
-            else
-                e = launch_one<T, BM, BN, WM, WN, MINW, 2, false, false, A_MN, B_MN, false>(g, full_tiles, all_flag, s);
+            if constexpr (!ACC) {
+                if ((g.K / kBK) % 2 == 0)
+                    e = launch_one<T, BM, BN, WM, WN, MINW, 2, false, true, A_MN, B_MN, false>(g, full_tiles, all_flag, s);
+                else
+                    e = launch_one<T, BM, BN, WM, WN, MINW, 2, false, false, A_MN, B_MN, false>(g, full_tiles, all_flag, s);
+            }
         } else if (vec) {
             e = launch_one<T, BM, BN, WM, WN, MINW, 1, false, false, A_MN, B_MN, ACC>(g, full_tiles, all_flag, s);
         } else {

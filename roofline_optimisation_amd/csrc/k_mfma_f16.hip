@@ -25,7 +25,7 @@ const char *desc_mfma_f16(int dtype, const GemmArgs &g) {
 }
 
 hipError_t launch_mfma_f16(int dtype, const GemmArgs &g, hipStream_t s) {
-    if (g.accumulate) return dtype == kF16 ? launch_mfma_f16_acc(g, s) : launch_mfma_bf16_acc(g, s);
+    if (g.signed_or_acc()) return dtype == kF16 ? launch_mfma_f16_acc(g, s) : launch_mfma_bf16_acc(g, s);
     if (g.trans_a || g.trans_b) return launch_mfma_f16_tx(dtype, g, s);
     // A is k-contiguous (KM), B n-contiguous (MN)
     return dtype == kF16 ? launch_layout<f16_t, false, true, false>(g, s)

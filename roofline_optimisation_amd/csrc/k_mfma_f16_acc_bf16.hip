@@ -1,5 +1,5 @@
-// BF16-input GEMM that accumulates into C (C = sign * op(A) op(B) + C), every operand
-// layout; kernels in h16_gemm.hpp.
+// BF16-input GEMM, negated and / or accumulating into C (C = sign * op(A) op(B) (+ C)),
+// every operand layout; kernels in h16_gemm.hpp.
 #include "h16_gemm.hpp"
 
 namespace g355 {

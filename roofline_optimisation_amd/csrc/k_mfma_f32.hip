@@ -19,7 +19,7 @@ const char *desc_mfma_f32(const GemmArgs &g) {
 }
 
 hipError_t launch_mfma_f32(const GemmArgs &g, hipStream_t s) {
-    if (g.accumulate) return launch_mfma_f32_acc(g, s);
+    if (g.signed_or_acc()) return launch_mfma_f32_acc(g, s);
     if (g.trans_a || g.trans_b) return launch_mfma_f32_tx(g, s);
     return launch_f32_layout<false, true, false>(g, s);  // A k-contiguous, B n-contiguous
 }

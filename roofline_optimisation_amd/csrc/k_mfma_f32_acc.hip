@@ -1,5 +1,5 @@
-// FP32 GEMM that accumulates into C (C = sign * op(A) op(B) + C), every operand layout
-// (kernel in f32_gemm.hpp).
+// FP32 GEMM, negated and / or accumulating into C (C = sign * op(A) op(B) (+ C)), every
+// operand layout (kernel in f32_gemm.hpp).
 #include "f32_gemm.hpp"
 
 namespace g355 {

@@ -38,22 +38,6 @@ __global__ __launch_bounds__(256) void naive_gemm_kernel(int M, int N, int K,
     *c = accumulate ? v + *c : v;
 }
 
-// C = -C on M x N (the sign of a negated product for the kernels that store their
-// accumulators as they are).
-__global__ __launch_bounds__(256) void negate_kernel(int M, int N, float *__restrict__ C, int ldc) {
-    const int col = blockIdx.x * 64 + threadIdx.x;
-    const int row = blockIdx.y * 4 + threadIdx.y;
-    if (row >= M || col >= N) return;
-    float *c = C + (size_t)row * ldc + col;
-    *c = -*c;
-}
-
-hipError_t launch_negate(const GemmArgs &g, hipStream_t s) {
-    hipLaunchKernelGGL(negate_kernel, dim3(cdiv(g.N, 64), cdiv(g.M, 4)), dim3(64, 4), 0, s, g.M,
-                       g.N, g.C, g.ldc);
-    return hipGetLastError();
-}
-
 hipError_t launch_naive(int dtype, const GemmArgs &g, hipStream_t s) {
     dim3 block(64, 4);
     dim3 grid(cdiv(g.N, 64), cdiv(g.M, 4));
