@@ -19,7 +19,12 @@ exhaustive fp16/bf16 decoding against numpy, and planted mistakes that the pins 
 ``tests/test_oracle_ex.py``.  The probe functions (``stream_xor``, ``chase``; "Advanced CUDA features - starting from
 GEMM", section on Little's law and occupancy) are pinned in ``tests/test_oracle_stream.py``:
 the closed form of the XOR of 0..n-1, per-bit parity counts, successor and permutation
-cycles with closed-form positions, and the out-of-range clamp.
+cycles with closed-form positions, and the out-of-range clamp.  ``softmax`` (the online
+recurrence of "Kernel optimisation guide", section on softmax optimisation) and
+``row_sum`` (its section on warp-shuffle reduction) are pinned in
+``tests/test_oracle_softmax.py``: exact decimal arithmetic at 50 digits, closed forms
+(constant rows, two-element rows), shift invariance, independence of rows and strides,
+integer sums, and planted mistakes.
 """
 
 from __future__ import annotations
@@ -56,6 +61,10 @@ def _configure(lib):
     lib.oracle_xor_words.restype = ctypes.c_uint32
     lib.oracle_chase.argtypes = [vp, ctypes.c_int64, ctypes.c_uint32, ctypes.c_int64]
     lib.oracle_chase.restype = ctypes.c_uint32
+    lib.oracle_softmax.argtypes = [i, i, vp, i, dp, fp, i, dp, dp]
+    lib.oracle_softmax.restype = i
+    lib.oracle_row_sum.argtypes = [i, i, vp, i, dp, fp]
+    lib.oracle_row_sum.restype = i
     return lib
 
 
@@ -190,3 +199,45 @@ def chase(next_words: np.ndarray, start: int, hops: int, n: int | None = None, l
     if not (1 <= n <= w.size) or not (0 <= start < n) or hops < 0:
         raise ValueError("chase: need 1 <= n <= len(next), 0 <= start < n, hops >= 0")
     return int(lib.oracle_chase(w.ctypes.data, n, start, hops))
+
+
+def softmax(X: np.ndarray, lib=None):
+    """Row-wise softmax of a 2-D float32 array by the online recurrence.
+
+    Returns (Y64, Y32, m, l): the binary64 results, their binary32 roundings (both of
+    X's shape, packed), and the per-row running maximum and running sum at the end of
+    the pass."""
+    lib = lib or _load()
+    X = np.asarray(X)
+    if X.dtype != np.float32 or X.ndim != 2:
+        raise ValueError("softmax: expected a 2-D float32 array")
+    rows, cols = X.shape
+    ldx = _row_stride(X)
+    ldy = max(cols, 1)
+    Y64 = np.zeros((rows, cols), np.float64)
+    Y32 = np.zeros((rows, cols), np.float32)
+    m = np.zeros(rows, np.float64)
+    l = np.zeros(rows, np.float64)
+    ptr = X.ctypes.data if X.size else None
+    st = lib.oracle_softmax(rows, cols, ptr, ldx, Y64.ctypes.data, Y32.ctypes.data, ldy,
+                            m.ctypes.data, l.ctypes.data)
+    if st:
+        raise ValueError("oracle_softmax: bad arguments")
+    return Y64, Y32, m, l
+
+
+def row_sum(X: np.ndarray, lib=None):
+    """Sums of the rows of a 2-D float32 array, in binary64 in increasing column order.
+    Returns (S64, S32)."""
+    lib = lib or _load()
+    X = np.asarray(X)
+    if X.dtype != np.float32 or X.ndim != 2:
+        raise ValueError("row_sum: expected a 2-D float32 array")
+    rows, cols = X.shape
+    S64 = np.zeros(rows, np.float64)
+    S32 = np.zeros(rows, np.float32)
+    ptr = X.ctypes.data if X.size else None
+    st = lib.oracle_row_sum(rows, cols, ptr, _row_stride(X), S64.ctypes.data, S32.ctypes.data)
+    if st:
+        raise ValueError("oracle_row_sum: bad arguments")
+    return S64, S32

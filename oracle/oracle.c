@@ -29,6 +29,11 @@
  * and does not depend on the number of threads.  Build with -ffp-contract=off.
  *
  * Degenerate sizes: M = 0 or N = 0 writes nothing; K = 0 writes +0.0 (empty sum).
+ *
+ * The file also holds the oracles of the memory-slope probes (a word XOR and a
+ * dependent-index walk) and of the row-wise softmax and row sum ("Kernel optimisation
+ * guide", sections on softmax optimisation and warp-shuffle reduction), each with its
+ * own header below.
  */
 #include <math.h>
 #include <stdint.h>
@@ -260,4 +265,71 @@ uint32_t oracle_chase(const uint32_t *next, int64_t n, uint32_t start, int64_t h
         cur = (int64_t)v < n ? v : (uint32_t)(n - 1);
     }
     return cur;
+}
+
+/*
+ * Softmax of every row of a rows x cols binary32 matrix (row stride ldx), by the online
+ * recurrence of "Kernel optimisation guide" (section on softmax optimisation, the online
+ * algorithm), in binary64.
+ *
+ * One pass over the row keeps a running maximum m (starting at -infinity) and a running
+ * sum l (starting at 0) of exp(x - m): when an element exceeds m, the sum so far is
+ * rescaled to the new maximum by exp(m_old - x) and m becomes x; then exp(x - m) is
+ * added.  After the pass m = max_i x_i and l = sum_i exp(x_i - m).  A second pass writes
+ * y_i = exp(x_i - m) / l.  Elements are visited in increasing column order.  The row
+ * elements are converted exactly to binary64, so each difference x_i - m is exact; the
+ * roundings are those of exp, the additions, the rescaling products and the division.
+ *
+ * Outputs (each may be NULL): Y64 / Y32 (row stride ldy) the binary64 results and their
+ * binary32 roundings (RNE); m_out / l_out the per-row m and l.  cols = 0 writes nothing
+ * to Y and m = -infinity, l = 0 per row.  Inputs are expected finite (a leading -infinity
+ * would make the first exp(x - m) an exp(NaN), as the recurrence is written).
+ */
+int oracle_softmax(int rows, int cols, const float *X, int ldx, double *Y64, float *Y32,
+                   int ldy, double *m_out, double *l_out)
+{
+    const int need = cols > 1 ? cols : 1;
+    if (rows < 0 || cols < 0 || ldx < need || ldy < need) return 1;
+#pragma omp parallel for schedule(static)
+    for (int r = 0; r < rows; ++r) {
+        const float *x = X + (size_t)r * ldx;
+        double m = -INFINITY;
+        double l = 0.0;
+        for (int i = 0; i < cols; ++i) {
+            const double v = (double)x[i];
+            if (v > m) {
+                l *= exp(m - v);
+                m = v;
+            }
+            l += exp(v - m);
+        }
+        for (int i = 0; i < cols; ++i) {
+            const double y = exp((double)x[i] - m) / l;
+            if (Y64) Y64[(size_t)r * ldy + i] = y;
+            if (Y32) Y32[(size_t)r * ldy + i] = (float)y;
+        }
+        if (m_out) m_out[r] = m;
+        if (l_out) l_out[r] = l;
+    }
+    return 0;
+}
+
+/*
+ * Sum of every row of a rows x cols binary32 matrix (row stride ldx): the reduction the
+ * "Kernel optimisation guide" section on warp-shuffle reduction builds from lane sums.
+ * Each row is summed in binary64 in increasing column order from +0.0 (cols = 0 gives
+ * +0.0); S64 gets the sums, S32 (may be NULL) their binary32 roundings (RNE).
+ */
+int oracle_row_sum(int rows, int cols, const float *X, int ldx, double *S64, float *S32)
+{
+    if (rows < 0 || cols < 0 || ldx < (cols > 1 ? cols : 1)) return 1;
+#pragma omp parallel for schedule(static)
+    for (int r = 0; r < rows; ++r) {
+        const float *x = X + (size_t)r * ldx;
+        double s = 0.0;
+        for (int i = 0; i < cols; ++i) s += (double)x[i];
+        if (S64) S64[r] = s;
+        if (S32) S32[r] = (float)s;
+    }
+    return 0;
 }

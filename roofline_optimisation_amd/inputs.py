@@ -18,6 +18,14 @@ section "Shared Memory Tiling", performance test):
   on the upper 16 bits of the binary32 pattern.
 
 FP16/BF16 operands travel as ``uint16`` bit patterns.
+
+Row-wise softmax and row-sum inputs (``make_logits``; the pages give the online softmax
+and the shuffle reduction without workloads, so these are synthetic rows of logits):
+``default_rng(seed)``, one rows x cols draw in row-major order, rounded to float32:
+``"normal"`` N(0, 1); ``"uniform"`` U[-1, 1]; ``"int"`` integers on {-4, ..., 4};
+``"wide"`` N(0, 1) x 40 (exp of the raw values would overflow binary32, so only a
+max-shifted evaluation is finite); ``"ascending"`` / ``"descending"`` N(0, 1) x 4 sorted
+along each row (a new running maximum at every element, or never after the first).
 """
 
 from __future__ import annotations
@@ -36,6 +44,19 @@ def _draw(rng: np.random.Generator, shape, dist: str) -> np.ndarray:
         return rng.standard_normal(size=shape).astype(np.float32)
     if dist == "int":
         return rng.integers(-4, 5, size=shape).astype(np.float32)
+    raise ValueError(f"unknown distribution {dist!r}")
+
+
+def make_logits(rows: int, cols: int, seed: int, dist: str = "normal") -> np.ndarray:
+    """A rows x cols float32 matrix of synthetic logits (see the module notes)."""
+    rng = np.random.default_rng(seed)
+    if dist in ("normal", "uniform", "int"):
+        return _draw(rng, (rows, cols), dist)
+    if dist == "wide":
+        return (rng.standard_normal(size=(rows, cols)) * 40.0).astype(np.float32)
+    if dist in ("ascending", "descending"):
+        x = np.sort((rng.standard_normal(size=(rows, cols)) * 4.0).astype(np.float32), axis=1)
+        return np.ascontiguousarray(x if dist == "ascending" else x[:, ::-1])
     raise ValueError(f"unknown distribution {dist!r}")
 
 

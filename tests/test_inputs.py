@@ -68,3 +68,20 @@ def test_embed():
     assert e.shape == (3, 5) and np.array_equal(e[:2, :3], x) and np.isnan(e[:, 3:]).all()
     h = inputs.embed(np.ones((2, 2), np.uint16), 3)
     assert h[0, 2] == 0x7E00
+
+
+def test_make_logits_recipe():
+    a = inputs.make_logits(4, 9, 5, "normal")
+    assert a.dtype == np.float32 and a.shape == (4, 9)
+    assert np.array_equal(a, inputs.make_logits(4, 9, 5, "normal"))
+    assert np.array_equal(a, np.random.default_rng(5).standard_normal((4, 9)).astype(np.float32))
+    up = inputs.make_logits(3, 20, 6, "ascending")
+    assert np.all(np.diff(up, axis=1) >= 0)
+    down = inputs.make_logits(3, 20, 6, "descending")
+    assert np.array_equal(down, up[:, ::-1])
+    w = inputs.make_logits(2, 1000, 7, "wide")
+    assert np.abs(w).max() > 89.0  # e^x would overflow binary32
+    i = inputs.make_logits(2, 50, 8, "int")
+    assert np.array_equal(i, np.round(i)) and np.abs(i).max() <= 4
+    with pytest.raises(ValueError):
+        inputs.make_logits(1, 1, 0, "bogus")
