@@ -1,10 +1,10 @@
 """ctypes binding of libgemm355 (argument marshalling only).
 
 The functions named like the C entry points take plain integers (device pointers as
-ints, a stream handle as an int) and return the C status code.  ``matmul`` is a
-convenience wrapper for torch tensors that derives sizes, strides, pointers and the
-current stream, calls the C entry point and raises on a non-OK status.  Nothing here
-computes any part of the product: every step runs in the HIP kernels of
+ints, a stream handle as an int) and return the C status code.  ``matmul``, ``softmax``
+and ``row_sum`` are convenience wrappers for torch tensors that derive sizes, strides,
+pointers and the current stream, call the C entry point and raise on a non-OK status.
+Nothing here computes any part of the results: every step runs in the HIP kernels of
 ``libgemm355.so``.  If the library is missing or cannot be loaded, every call raises.
 """
 
@@ -31,6 +31,7 @@ EXPORTS = (
     "gemm355_variant_name", "gemm355_version", "gemm355_gemm_ex",
     "gemm355_probe_mfma_shape", "gemm355_probe_mfma", "gemm355_probe_ds_read_tr16",
     "gemm355_probe_global_load_lds", "gemm355_stream", "gemm355_chase",
+    "gemm355_softmax_f32", "gemm355_row_sum_f32",
 )
 
 STREAM_COPY, STREAM_READ_XOR = 0, 1
@@ -80,6 +81,10 @@ def _configure(lib):
     lib.gemm355_stream.restype = i
     lib.gemm355_chase.argtypes = [p, i64, ctypes.c_uint32, i, p, p]
     lib.gemm355_chase.restype = i
+    lib.gemm355_softmax_f32.argtypes = [i, i, p, i, p, i, p]
+    lib.gemm355_softmax_f32.restype = i
+    lib.gemm355_row_sum_f32.argtypes = [i, i, p, i, p, p]
+    lib.gemm355_row_sum_f32.restype = i
     return lib
 
 
@@ -167,6 +172,14 @@ def gemm355_chase(next_words, n_words, start, hops, dev_out, stream=0) -> int:
     return lib().gemm355_chase(next_words, n_words, start, hops, dev_out, stream)
 
 
+def gemm355_softmax_f32(rows, cols, X, ldx, Y, ldy, stream=0) -> int:
+    return lib().gemm355_softmax_f32(rows, cols, X, ldx, Y, ldy, stream)
+
+
+def gemm355_row_sum_f32(rows, cols, X, ldx, out, stream=0) -> int:
+    return lib().gemm355_row_sum_f32(rows, cols, X, ldx, out, stream)
+
+
 def status_string(status: int) -> str:
     try:
         return gemm355_status_string(status)
@@ -232,4 +245,50 @@ def matmul(A, B, out=None, variant: int | str = VARIANT_AUTO, stream=None, *,
         where = "gemm355_run_variant"
     if st != OK:
         raise Gemm355Error(st, where)
+    return out
+
+
+def _stream_handle(stream, device):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return s.cuda_stream if hasattr(s, "cuda_stream") else int(s)
+
+
+def _f32_matrix(t, what):
+    import torch
+    if not t.is_cuda or t.dtype != torch.float32 or t.dim() != 2:
+        raise ValueError(f"{what} must be a 2-D float32 CUDA tensor")
+
+
+def softmax(X, out=None, stream=None):
+    """Row-wise softmax of a 2-D float32 CUDA tensor through gemm355_softmax_f32 (`out`
+    may be X itself for an in-place call).  Raises Gemm355Error on a non-OK status."""
+    import torch
+    _f32_matrix(X, "X")
+    if out is None:
+        out = torch.empty_like(X, memory_format=torch.contiguous_format)
+    _f32_matrix(out, "out")
+    if tuple(out.shape) != tuple(X.shape):
+        raise ValueError("out must have X's shape")
+    rows, cols = X.shape
+    st = gemm355_softmax_f32(rows, cols, X.data_ptr(), _ld(X), out.data_ptr(), _ld(out),
+                             _stream_handle(stream, X.device))
+    if st != OK:
+        raise Gemm355Error(st, "gemm355_softmax_f32")
+    return out
+
+
+def row_sum(X, out=None, stream=None):
+    """Sums of the rows of a 2-D float32 CUDA tensor through gemm355_row_sum_f32."""
+    import torch
+    _f32_matrix(X, "X")
+    rows, cols = X.shape
+    if out is None:
+        out = torch.empty(rows, dtype=torch.float32, device=X.device)
+    if not out.is_cuda or out.dtype != torch.float32 or out.numel() != rows or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 CUDA tensor of `rows` elements")
+    st = gemm355_row_sum_f32(rows, cols, X.data_ptr(), _ld(X), out.data_ptr(),
+                             _stream_handle(stream, X.device))
+    if st != OK:
+        raise Gemm355Error(st, "gemm355_row_sum_f32")
     return out

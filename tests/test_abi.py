@@ -10,7 +10,8 @@ import pytest
 from roofline_optimisation_amd import binding as gb
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADERS = [os.path.join(ROOT, "include", h) for h in ("gemm355.h", "gemm355_probe.h", "gemm355_stream.h")]
+HEADERS = [os.path.join(ROOT, "include", h)
+           for h in ("gemm355.h", "gemm355_probe.h", "gemm355_stream.h", "gemm355_softmax.h")]
 
 
 def declared_functions():
@@ -179,6 +180,27 @@ def test_stream_and_chase_argument_checks(lib):
     assert C(P, 16, 16, 1, P) == gb.ERR_INVALID_ARG
     assert C(P, 16, 0, 0, P) == gb.ERR_INVALID_ARG
     assert C(P, 16, 0, (1 << 30) + 1, P) == gb.ERR_INVALID_ARG
+
+
+def test_softmax_and_row_sum_argument_checks(lib):
+    S, R = gb.gemm355_softmax_f32, gb.gemm355_row_sum_f32
+    Q = P + (1 << 24)
+    bad = [(-1, 4, P, 4, Q, 4), (2, -1, P, 4, Q, 4), (2, 4, P, 3, Q, 4), (2, 4, P, 4, Q, 3),
+           (2, (1 << 30) + 1, P, (1 << 30) + 1, Q, (1 << 30) + 1), (2, 4, 0, 4, Q, 4),
+           (2, 4, P, 4, 0, 4),
+           (2, 4, P, 8, P, 4),            # in place with different strides
+           (4, 64, P, 64, P + 256, 64)]   # partial overlap
+    for b in bad:
+        assert S(*b) == gb.ERR_INVALID_ARG, b
+    assert S(0, 4, 0, 4, 0, 4) == gb.OK and S(3, 0, 0, 1, 0, 1) == gb.OK   # no-ops
+    assert S(2, 4, P, 4, P, 4) in (gb.OK, gb.ERR_DEVICE)                   # in place
+    assert S(2, 4, P, 4, P + 32, 4) in (gb.OK, gb.ERR_DEVICE)              # adjacent spans
+    bad = [(-1, 4, P, 4, Q), (2, -1, P, 4, Q), (2, 4, P, 3, Q), (2, 4, 0, 4, Q), (2, 4, P, 4, 0),
+           (2, 4, P, 4, P + 16)]          # out overlaps X
+    for b in bad:
+        assert R(*b) == gb.ERR_INVALID_ARG, b
+    assert R(0, 4, 0, 4, 0) == gb.OK
+    assert R(3, 0, 0, 1, Q) in (gb.OK, gb.ERR_DEVICE)                      # writes zeros
 
 
 def test_matmul_refuses_cpu_tensors(lib):

@@ -1,0 +1,226 @@
+"""GPU parity of the row-wise softmax and row sum (``gemm355_softmax_f32``,
+``gemm355_row_sum_f32``; "Kernel optimisation guide", sections on softmax optimisation
+and warp-shuffle reduction) against the oracle, through the C ABI.
+
+Softmax bar, per element (binary32 against the oracle's binary64 value y):
+    |y_gpu - y| <= 2^-24 (2 |x - m| + 2 n + 64) y + 2^-120
+with m the row maximum and n the number of elements one lane adds in sequence (at most
+32 for rows held on chip, cols / 1024 for longer rows).  The terms: the rounding of
+x - m in binary32 (|x - m| 2^-24, doubled for the two exponentials whose arguments
+carry it), the running sum (n sequential additions plus the 6 + 4 levels of the merge
+tree, each a rounding and a rescale), expf (1 ulp) and the final scaling, plus an
+absolute 2^-120 for results in the subnormal range.  Constant rows and a dominant element
+are exact.  Row sum bar: sums of small integers bit-exact; otherwise
+|s_gpu - s| <= 2^-24 (n + 22) sum |x|.
+
+Inputs sit in NaN-padded buffers (a read outside a row would turn that row into NaN);
+outputs sit between sentinel guards that must stay intact.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import to_device
+from roofline_optimisation_amd import binding as gb
+from roofline_optimisation_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+SENT = np.float32(7777.0)
+U24 = 2.0 ** -24
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def lane_count(cols: int) -> int:
+    return max(32, -(-cols // 1024))
+
+
+def run_softmax(X, padx=0, pady=0, offset=0, in_place=False):
+    """Y = softmax(X) on the GPU.  Returns (Y, intact)."""
+    import torch
+    rows, cols = X.shape
+    ldx, ldy = max(cols, 1) + padx, max(cols, 1) + pady
+    if in_place:
+        ldy = ldx
+    xbuf = np.full(offset + rows * ldx + 64, np.nan, np.float32)
+    if rows and cols:
+        xbuf[offset:offset + rows * ldx].reshape(rows, ldx)[:, :cols] = X
+    dX = to_device(xbuf)
+    if in_place:
+        dY, yoff = dX, offset
+    else:
+        dY, yoff = to_device(np.full(offset + rows * ldy + 64, SENT, np.float32)), offset
+    st = gb.gemm355_softmax_f32(rows, cols, dX.data_ptr() + 4 * offset, ldx,
+                                dY.data_ptr() + 4 * yoff, ldy,
+                                torch.cuda.current_stream().cuda_stream)
+    assert st == gb.OK, st
+    torch.cuda.synchronize()
+    out = dY.cpu().numpy()
+    Y = out[yoff:yoff + rows * ldy].reshape(rows, ldy)[:, :cols].copy() if rows else \
+        np.zeros((0, cols), np.float32)
+    if in_place:
+        return Y, True
+    mask = np.ones(out.shape, bool)
+    if rows and cols:
+        mask[yoff:yoff + rows * ldy].reshape(rows, ldy)[:, :cols] = False
+    return Y, bool(np.all(out[mask] == SENT))
+
+
+def check_softmax(X, Y, what):
+    assert np.isfinite(Y).all(), f"{what}: non-finite output"
+    Y64, _, m, _ = oracle.softmax(X)
+    x = X.astype(np.float64)
+    tol = U24 * (2 * np.abs(x - m[:, None]) + 2 * lane_count(X.shape[1]) + 64) * Y64 + 2.0 ** -120
+    err = np.abs(Y.astype(np.float64) - Y64)
+    bad = err > tol
+    worst = float((err / tol).max()) if Y.size else 0.0
+    print(f"{what}: worst error / bound {worst:.3f}", flush=True)
+    assert not bad.any(), f"{what}: {int(bad.sum())} elements outside the bound, e.g. " \
+        f"{np.argwhere(bad)[:3].tolist()}"
+
+
+COLS = [1, 2, 3, 4, 63, 64, 65, 255, 256, 257, 511, 512, 1000, 1024, 1025, 2047, 2048, 3000,
+        4096, 4097, 5000, 8192, 12000, 16384, 16385, 20000, 32768, 32769, 40000, 70001]
+
+
+def rows_for(cols):
+    return 9 if cols <= 1024 else (5 if cols <= 32768 else 3)
+
+
+@pytest.mark.parametrize("layout", ["packed", "padded", "offset"])
+@pytest.mark.parametrize("cols", COLS)
+def test_softmax_shapes(cols, layout):
+    X = inputs.make_logits(rows_for(cols), cols, 60 + cols % 97, "normal")
+    kw = {"packed": {}, "padded": {"padx": 3, "pady": 5}, "offset": {"offset": 1}}[layout]
+    Y, ok = run_softmax(X, **kw)
+    assert ok, "wrote outside Y"
+    check_softmax(X, Y, f"softmax {X.shape} {layout}")
+
+
+@pytest.mark.parametrize("dist", ["wide", "ascending", "descending", "uniform", "int"])
+@pytest.mark.parametrize("cols", [100, 1024, 4096, 30000, 50000])
+def test_softmax_distributions(cols, dist):
+    X = inputs.make_logits(4, cols, 61, dist)
+    Y, ok = run_softmax(X)
+    assert ok
+    check_softmax(X, Y, f"softmax {dist} {X.shape}")
+
+
+@pytest.mark.parametrize("cols", [1, 3, 64, 1000, 4096, 32768, 40000])
+def test_softmax_exact_cases(cols):
+    # a constant row: every exponential is exp(0) = 1, the sum is cols exactly
+    X = np.full((3, cols), 2.5, np.float32)
+    X[1] = -300.0
+    Y, _ = run_softmax(X)
+    assert np.all(Y == np.float32(1.0 / cols)), cols
+    # one element far above the rest takes everything
+    if cols > 1:
+        X = np.full((2, cols), -2000.0, np.float32)
+        X[0, cols // 3] = 0.0
+        X[1, cols - 1] = 5.0
+        Y, _ = run_softmax(X)
+        want = np.zeros_like(X)
+        want[0, cols // 3] = 1.0
+        want[1, cols - 1] = 1.0
+        assert np.array_equal(Y, want), cols
+
+
+@pytest.mark.parametrize("cols", [200, 1024, 6000, 32768, 33000])
+def test_softmax_in_place(cols):
+    X = inputs.make_logits(6, cols, 62, "normal")
+    Y, _ = run_softmax(X, padx=4 if cols % 4 == 0 else 0, in_place=True)
+    check_softmax(X, Y, f"softmax in place {X.shape}")
+
+
+def test_softmax_noops():
+    for shape in [(0, 10), (5, 0)]:
+        Y, ok = run_softmax(np.zeros(shape, np.float32))
+        assert ok and Y.size == 0
+
+
+@pytest.mark.parametrize("rows,cols", [(65536, 1024), (16384, 4096), (4096, 16384), (2048, 32768),
+                                       (512, 131072)])
+def test_softmax_full_size(rows, cols):
+    """The measured workloads (64 Mi elements, N(0,1) logits), every element checked."""
+    X = inputs.make_logits(rows, cols, 7, "normal")
+    Y, ok = run_softmax(X)
+    assert ok
+    check_softmax(X, Y, f"softmax full {rows}x{cols}")
+
+
+# ------------------------------------------------------------------ row sum
+
+def run_row_sum(X, padx=0, offset=0):
+    import torch
+    rows, cols = X.shape
+    ldx = max(cols, 1) + padx
+    xbuf = np.full(offset + rows * ldx + 64, np.nan, np.float32)
+    if rows and cols:
+        xbuf[offset:offset + rows * ldx].reshape(rows, ldx)[:, :cols] = X
+    dX = to_device(xbuf)
+    dO = to_device(np.full(rows + 64, SENT, np.float32))
+    st = gb.gemm355_row_sum_f32(rows, cols, dX.data_ptr() + 4 * offset, ldx, dO.data_ptr() + 4 * 32,
+                                torch.cuda.current_stream().cuda_stream)
+    assert st == gb.OK, st
+    torch.cuda.synchronize()
+    out = dO.cpu().numpy()
+    ok = bool(np.all(out[:32] == SENT) and np.all(out[32 + rows:] == SENT))
+    return out[32:32 + rows].copy(), ok
+
+
+SUM_COLS = [0, 1, 3, 4, 63, 64, 65, 1000, 1024, 2048, 2049, 4096, 16384, 16385, 100000]
+
+
+@pytest.mark.parametrize("layout", ["packed", "padded", "offset"])
+@pytest.mark.parametrize("cols", SUM_COLS)
+def test_row_sum_integers_exact(cols, layout):
+    X = inputs.make_logits(9, cols, 63, "int")
+    kw = {"packed": {}, "padded": {"padx": 3}, "offset": {"offset": 1}}[layout]
+    S, ok = run_row_sum(X, **kw)
+    _, S32 = oracle.row_sum(X)
+    assert ok and np.array_equal(S, S32), (cols, layout)
+    if cols == 0:
+        assert not np.signbit(S).any()
+
+
+@pytest.mark.parametrize("cols", [64, 1000, 1024, 2049, 4096])
+def test_row_sum_every_position(cols):
+    """Row r holds a single 1 at column r: every column position of every lane and wave
+    must be counted exactly once."""
+    X = np.zeros((cols, cols), np.float32)
+    X[np.arange(cols), np.arange(cols)] = 1.0
+    S, ok = run_row_sum(X)
+    assert ok and np.all(S == 1.0), np.flatnonzero(S != 1.0)[:10]
+
+
+@pytest.mark.parametrize("cols", [17, 1000, 4096, 16385, 100000])
+def test_row_sum_float_bound(cols):
+    X = inputs.make_logits(16, cols, 64, "normal")
+    S, ok = run_row_sum(X)
+    S64, _ = oracle.row_sum(X)
+    bound = U24 * (lane_count(cols) + 22) * np.abs(X.astype(np.float64)).sum(1)
+    assert ok and np.all(np.abs(S - S64) <= bound)
+    S2, _ = run_row_sum(X)
+    assert np.array_equal(S, S2), "repeated calls must give identical bits"
+
+
+def test_wrappers():
+    import torch
+    X = inputs.make_logits(33, 777, 65, "normal")
+    dX = torch.from_numpy(X).cuda()
+    Y = gb.softmax(dX).cpu().numpy()
+    check_softmax(X, Y, "softmax wrapper")
+    gb.softmax(dX, out=dX)
+    assert np.array_equal(dX.cpu().numpy(), Y)
+    Xi = inputs.make_logits(33, 777, 66, "int")
+    s = gb.row_sum(torch.from_numpy(Xi).cuda()).cpu().numpy()
+    assert np.array_equal(s, oracle.row_sum(Xi)[1])
