@@ -11,6 +11,10 @@ rate: per-launch kernel traces show the chip's clocks settling over the first ~5
 management's transient instead of the kernel.  The FP16-input / FP32-accumulate 4096^3 workload
 (seed 3) is measured the same way and reported beside it.
 
+`--softmax PATH` measures the row-wise softmax and row sum instead (64 Mi binary32
+logits per workload) and prints one JSON line for the 16384 x 4096 workload, with its
+roofline against the 8 TB/s HBM peak and the CPU oracle's rate beside it.
+
 The JSON line also carries
   * "roofline": the dominant kernel's achieved TFLOP/s against the MI355X peak for its
     arithmetic (FP32 on the matrix cores: 157.3 TFLOP/s), with HBM traffic from the
@@ -28,6 +32,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -35,8 +41,14 @@ PEAKS = {"f32": 157.3, "f16": 2516.6, "bf16": 2516.6}  # TFLOP/s, dense, 2.4 GHz
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "roofline_optimisation_amd", "csrc")
 KERNEL_SOURCES = {"f32": ["k_mfma_f32.hip", "f32_gemm.hpp", "common.hpp"],
-                  "f16": ["k_mfma_f16.hip", "h16_gemm.hpp", "common.hpp"]}
-PMC_FILES = {"f32": "pmc_mfma_f32_n3072.txt", "f16": "pmc_mfma_f16_n4096.txt"}
+                  "f16": ["k_mfma_f16.hip", "h16_gemm.hpp", "common.hpp"],
+                  "softmax": ["k_softmax.hip", "wave_reduce.hpp"]}
+PMC_FILES = {"f32": "pmc_mfma_f32_n3072.txt", "f16": "pmc_mfma_f16_n4096.txt",
+             "softmax": "pmc_softmax_16384x4096.txt"}
+HBM_PEAK_GBS = 8000.0
+# Row-wise softmax workloads: 64 Mi binary32 logits each, N(0, 1), seed 7 (the pages give
+# the online softmax without sizes); the first is the one the JSON line reports.
+SOFTMAX_SHAPES = ((16384, 4096), (65536, 1024), (4096, 16384), (2048, 32768), (512, 131072))
 
 
 def log(*a):
@@ -245,6 +257,101 @@ def general_form_lines():
     return lines
 
 
+def time_launches(go, stream, warm=50, rounds=3, reps=100):
+    """Median over `rounds` of the mean per-launch time (ms) of `reps` back-to-back calls
+    of go(), timed with HIP events on `stream`, after `warm` untimed calls."""
+    import torch
+    for _ in range(warm):
+        go()
+    times = []
+    for _ in range(rounds):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            go()
+        e1.record(stream)
+        stream.synchronize()
+        times.append(e0.elapsed_time(e1) / reps)
+    return sorted(times)[len(times) // 2]
+
+
+def softmax_measure(warm=50, reps=100):
+    """Per-launch time and algorithmic bandwidth of gemm355_softmax_f32 (4 bytes read and
+    4 written per element) and gemm355_row_sum_f32 (4 bytes read per element, 4 written
+    per row) on every softmax workload."""
+    import torch
+
+    from roofline_optimisation_amd import binding as gb
+    from roofline_optimisation_amd import inputs
+
+    stream = torch.cuda.Stream()
+    h = stream.cuda_stream
+    out = []
+    for rows, cols in SOFTMAX_SHAPES:
+        X = inputs.make_logits(rows, cols, 7, "normal")
+        dX = torch.from_numpy(X).cuda()
+        dY = torch.empty_like(dX)
+        dS = torch.empty(rows, dtype=torch.float32, device="cuda")
+        torch.cuda.synchronize()
+
+        def sm():
+            st = gb.gemm355_softmax_f32(rows, cols, dX.data_ptr(), cols, dY.data_ptr(), cols, h)
+            if st != gb.OK:
+                raise gb.Gemm355Error(st, "gemm355_softmax_f32")
+
+        def rs():
+            st = gb.gemm355_row_sum_f32(rows, cols, dX.data_ptr(), cols, dS.data_ptr(), h)
+            if st != gb.OK:
+                raise gb.Gemm355Error(st, "gemm355_row_sum_f32")
+        ms = time_launches(sm, stream, warm, 3, reps)
+        ms_sum = time_launches(rs, stream, warm, 3, reps)
+        n = rows * cols
+        r = {"rows": rows, "cols": cols, "ms": ms, "gbs": 8.0 * n / (ms * 1e-3) / 1e9,
+             "ms_sum": ms_sum, "gbs_sum": (4.0 * n + 4 * rows) / (ms_sum * 1e-3) / 1e9,
+             "path": "two passes (row streamed twice)" if cols > 32768 else "row held in registers",
+             "X": X if (rows, cols) == SOFTMAX_SHAPES[0] else None}
+        log(f"[softmax] {rows}x{cols}: {ms * 1e3:.1f} us, {r['gbs']:.0f} GB/s "
+            f"({100 * r['gbs'] / HBM_PEAK_GBS:.1f}% of 8 TB/s); row sum {ms_sum * 1e3:.1f} us, "
+            f"{r['gbs_sum']:.0f} GB/s")
+        out.append(r)
+        del dX, dY, dS
+    return out
+
+
+def softmax_lines(res):
+    lines = ["", "## Row-wise softmax and row sum (`gemm355_softmax_f32`, `gemm355_row_sum_f32`)", "",
+             "Binary32 logits, N(0, 1), seed 7, packed rows, 64 Mi elements per workload.",
+             "Algorithmic bytes: softmax 4 read + 4 written per element; row sum 4 read per",
+             "element + 4 written per row.  Per-launch time: median of 3 rounds of 100 launches",
+             "after 50 warm-up launches, HIP events on the launch stream.", "",
+             "| rows x cols | softmax path | softmax (us) | GB/s | % of 8 TB/s | row sum (us) | GB/s | % of 8 TB/s |",
+             "|---|---|---|---|---|---|---|---|"]
+    for r in res:
+        lines.append(f"| {r['rows']} x {r['cols']} | {r['path']} | {r['ms'] * 1e3:.1f} | {r['gbs']:.0f} | "
+                     f"{100 * r['gbs'] / HBM_PEAK_GBS:.1f} | {r['ms_sum'] * 1e3:.1f} | {r['gbs_sum']:.0f} | "
+                     f"{100 * r['gbs_sum'] / HBM_PEAK_GBS:.1f} |")
+    return lines
+
+
+def softmax_cpu_baseline(X, min_seconds=10.0):
+    """The oracle's softmax on this host: the first 1024 rows of the workload, repeated
+    until at least `min_seconds` of wall time, as algorithmic GB/s (8 bytes per element)."""
+    import oracle
+    sample = np.ascontiguousarray(X[:1024])
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.softmax(sample)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
+    n = sample.size * reps
+    return {"value": round(8.0 * n / dt / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{reps} passes over the first 1024 rows ({sample.shape[0]}x{sample.shape[1]}) "
+                      f"of the same seeded workload, {dt:.1f} s wall"}
+
+
 def memory_slope_lines():
     """Markdown lines for the memory-slope probe: HBM read bandwidth against resident waves
     per CU and bytes in flight per wave, dependent-load latency, and the Little's-law
@@ -416,6 +523,7 @@ def write_report(path):
                      f"{100 * e['frac']:.1f} | {e['oi']:.1f} | {e['attainable_tflops']:.0f} | {bound} |")
         log(f"[report] {c.name}: {ms * 1e3:.1f} us {tf:.1f} TFLOP/s")
     lines += general_form_lines()
+    lines += softmax_lines(softmax_measure())
     lines += memory_slope_lines()
     with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")
@@ -437,6 +545,10 @@ def main():
                     help="only run the memory-slope probe (HBM read rate against occupancy and "
                          "bytes in flight, dependent-load latency) and write its markdown table "
                          "to PATH; no GEMM timing, no JSON line")
+    ap.add_argument("--softmax", default=None, metavar="PATH",
+                    help="only measure the row-wise softmax and row sum on their 64 Mi-element "
+                         "workloads, write the markdown table to PATH and print one JSON line "
+                         "for the 16384 x 4096 workload; no GEMM timing")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after the GEMMs, copy this many MiB device-to-device once (a plain "
                          "copy of known size, used to scale the HBM byte counters)")
@@ -463,6 +575,42 @@ def main():
         log(f"[bench] memory-slope table written to {args.memory_slope}")
         return
 
+    def calibration_copy():
+        if args.calib_copy_mib:
+            nel = args.calib_copy_mib * (1 << 20) // 4
+            src = torch.ones(nel, dtype=torch.float32, device="cuda")
+            dst = torch.empty_like(src)
+            torch.cuda.synchronize()
+            dst.copy_(src)
+            torch.cuda.synchronize()
+            log(f"[bench] calibration copy of {args.calib_copy_mib} MiB done")
+
+    if args.softmax:
+        warm, reps = min(args.warmup, 50), max(1, min(args.steps, 100))
+        res = softmax_measure(warm=warm, reps=reps)
+        with open(args.softmax, "w") as f:
+            f.write("\n".join(["# libgemm355 row-wise softmax on one MI355X"] + softmax_lines(res)) + "\n")
+        calibration_copy()
+        r = res[0]
+        tr = measured_traffic("softmax")
+        line = {
+            "metric": "row-wise softmax, algorithmic HBM bandwidth (8 bytes per element), 1 MI355X",
+            "value": round(r["gbs"], 1), "unit": "GB/s", "n_gpus": 1, "steps": 3 * reps, "warmup": warm,
+            "ms_per_step": round(r["ms"], 5), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+            "config": {"workload": f"softmax_f32_{r['rows']}x{r['cols']}", "rows": r["rows"],
+                       "cols": r["cols"], "dist": "N(0,1)", "seed": 7},
+            "roofline": {"bound": "hbm", "achieved": round(r["gbs"], 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(r["gbs"] / HBM_PEAK_GBS, 4), "traffic": tr,
+                         "algorithmic_bytes": 8 * r["rows"] * r["cols"],
+                         "kernel": "softmax_rows_kernel<32, 2, 1, vec> (32 elements per lane, 2 waves per row)"},
+        }
+        if not args.no_cpu_baseline:
+            log("[softmax] timing the CPU oracle (at least 10 s)")
+            line["cpu_baseline"] = softmax_cpu_baseline(r["X"])
+        print(json.dumps(line), flush=True)
+        return
+
     results = {}
     for kind, n, seed in (("f32", 3072, 1), ("f16", 4096, 3)):
         if args.only and args.only != kind:
@@ -478,14 +626,7 @@ def main():
     if args.report:
         write_report(args.report)
 
-    if args.calib_copy_mib:
-        nel = args.calib_copy_mib * (1 << 20) // 4
-        src = torch.ones(nel, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        log(f"[bench] calibration copy of {args.calib_copy_mib} MiB done")
+    calibration_copy()
 
     def roof(kind, n):
         r = results[kind]

@@ -32,9 +32,10 @@ extern "C" {
 /* Y[r][c] = exp(X[r][c] - m_r) / l_r for every 0 <= r < rows, 0 <= c < cols, with
  * m_r = max_c X[r][c] and l_r = sum_c exp(X[r][c] - m_r) (the online softmax above).
  *
- * Results agree with the exact softmax of the binary32 inputs to a relative error of
- * about (|X[r][c] - m_r| + 64) * 2^-24 (the rounding of X - m dominates for elements far
- * below the maximum).  Inputs are expected finite; an infinity or NaN in a row makes
+ * Results agree with the exact softmax of the binary32 inputs to a relative error below
+ * 2^-24 (2 |X[r][c] - m_r| + 2 n + 64), n the number of elements one lane sums in
+ * sequence (at most 64 for rows of up to 32768 elements, cols / 1024 beyond): the
+ * rounding of X - m dominates for elements far below the maximum.  Inputs are expected finite; an infinity or NaN in a row makes
  * that row's results unspecified (other rows are unaffected).
  *
  * Arguments: rows >= 0, 0 <= cols <= 2^30; ldx >= max(1, cols), ldy >= max(1, cols);

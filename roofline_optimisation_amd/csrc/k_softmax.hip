@@ -7,7 +7,8 @@
 //
 // gfx950 mapping (the op is bound by HBM: 4 bytes read and 4 written per element):
 //  * A row is held in registers by 64 * WPR lanes, E elements each (WPR waves per row;
-//    one wave per row and four rows per workgroup for rows of up to 1024).  Loads are
+//    one wave per row and four waves per workgroup for rows of up to 512, a wave taking
+//    two rows of up to 256).  Loads are
 //    16-byte vectors when the rows allow it (lane t's vector q covers columns
 //    4 (q T + t) .. +3, so each load instruction reads 1 KiB contiguous per wave);
 //    every load of the row is issued before the first is used.
@@ -17,7 +18,8 @@
 //    and across the waves through LDS, each merge being the recurrence's rescale of the
 //    pair with the smaller maximum: (m, l) = (m_hi, l_hi + l_lo exp(m_lo - m_hi)).
 //  * Each lane then writes y_i = e_i * (exp(m_t - m) / l): one exponential per element,
-//    and the row is read from memory once.
+//    and the row is read from memory once.  The stores are non-temporal (no L2 lines
+//    allocated for the results), 10-25 % faster than ordinary stores here.
 //  * Rows longer than 32768 elements stream: pass 1 applies the recurrence chunk by
 //    chunk (16 elements per lane per chunk), pass 2 re-reads the row and writes
 //    exp(x - m) * (1 / l).
@@ -30,6 +32,8 @@
 namespace g355 {
 
 namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr int kMaxResident = 32768;  // longest row held in registers (1024 lanes x 32)
@@ -75,69 +79,87 @@ __device__ __forceinline__ void block_merge(float &m, float &l, float *sm, float
 template <int WPR>
 constexpr int block_threads() { return WPR == 1 ? 256 : 64 * WPR; }
 
-// Rows of at most 64 * WPR * E elements, held in registers.
-template <int E, int WPR, bool VEC>
+// Results are written with non-temporal stores, which stream past the L2 without
+// allocating lines there.
+__device__ __forceinline__ void store_nt(float *p, float v) { __builtin_nontemporal_store(v, p); }
+__device__ __forceinline__ void store_nt4(float *p, float a, float b, float c, float d) {
+    __builtin_nontemporal_store(f32x4{a, b, c, d}, (f32x4 *)p);
+}
+
+// Rows of at most 64 * WPR * E elements, held in registers.  With one wave per row
+// (WPR == 1) each wave takes R consecutive rows and issues the loads of all of them
+// before it reduces the first.
+template <int E, int WPR, int R, bool VEC>
 __global__ __launch_bounds__(block_threads<WPR>()) void softmax_rows_kernel(
     int rows, int cols, const float *__restrict__ X, int ldx, float *Y, int ldy) {
     constexpr int T = 64 * WPR;
     static_assert(!VEC || E % 4 == 0, "vector loads take 4 elements");
+    static_assert(WPR == 1 || R == 1, "several rows per workgroup only with one wave per row");
     __shared__ float sm[WPR], sl[WPR];
     const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
-    const int row = WPR == 1 ? blockIdx.x * 4 + wave : blockIdx.x;
+    const int row0 = WPR == 1 ? (blockIdx.x * 4 + wave) * R : blockIdx.x;
     const int t = WPR == 1 ? lane : (int)threadIdx.x;
-    if (WPR == 1 && row >= rows) return;  // a whole wave; no barrier in this shape
-    const float *x = X + (size_t)row * ldx;
-    float *y = Y + (size_t)row * ldy;
+    if (WPR == 1 && row0 >= rows) return;  // a whole wave; no barrier in this shape
 
     // element e of this lane: column col(e); with vectors, 4 consecutive per vector
     auto col = [&](int e) { return VEC ? 4 * ((e / 4) * T + t) + e % 4 : e * T + t; };
-    float v[E];
-    if constexpr (VEC) {
+    float v[R][E];
 #pragma unroll
-        for (int q = 0; q < E / 4; ++q) {
-            const int c = 4 * (q * T + t);
-            float4 f = make_float4(kNegInf, kNegInf, kNegInf, kNegInf);
-            if (c < cols) f = *(const float4 *)(x + c);  // cols % 4 == 0: whole vector in the row
-            v[4 * q] = f.x;
-            v[4 * q + 1] = f.y;
-            v[4 * q + 2] = f.z;
-            v[4 * q + 3] = f.w;
-        }
-    } else {
+    for (int r = 0; r < R; ++r) {
+        const bool in = row0 + r < rows;
+        const float *x = X + (size_t)(row0 + r) * ldx;
+        if constexpr (VEC) {
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-            const int c = col(e);
-            v[e] = c < cols ? x[c] : kNegInf;
+            for (int q = 0; q < E / 4; ++q) {
+                const int c = 4 * (q * T + t);
+                float4 f = make_float4(kNegInf, kNegInf, kNegInf, kNegInf);
+                if (in && c < cols) f = *(const float4 *)(x + c);  // cols % 4 == 0: whole vector in the row
+                v[r][4 * q] = f.x;
+                v[r][4 * q + 1] = f.y;
+                v[r][4 * q + 2] = f.z;
+                v[r][4 * q + 3] = f.w;
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const int c = col(e);
+                v[r][e] = in && c < cols ? x[c] : kNegInf;
+            }
         }
     }
-    float m = kNegInf;
 #pragma unroll
-    for (int e = 0; e < E; ++e) m = fmaxf(m, v[e]);
-    // a lane with no element of the row keeps m = -inf and l = 0; shifting by 0 then
-    // keeps its exponentials at exp(-inf) = 0
-    const float shift = m == kNegInf ? 0.0f : m;
-    float l = 0.0f;
+    for (int r = 0; r < R; ++r) {
+        float m = kNegInf;
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-        v[e] = expf(v[e] - shift);
-        l += v[e];
-    }
-    float M = m, L = l;
-    block_merge<WPR>(M, L, sm, sl, wave, lane);
-    const float s = expf(m - M) / L;
-    if constexpr (VEC) {
-#pragma unroll
-        for (int q = 0; q < E / 4; ++q) {
-            const int c = 4 * (q * T + t);
-            if (c < cols)
-                *(float4 *)(y + c) = make_float4(v[4 * q] * s, v[4 * q + 1] * s, v[4 * q + 2] * s,
-                                                 v[4 * q + 3] * s);
-        }
-    } else {
+        for (int e = 0; e < E; ++e) m = fmaxf(m, v[r][e]);
+        // a lane with no element of the row keeps m = -inf and l = 0; shifting by 0 then
+        // keeps its exponentials at exp(-inf) = 0
+        const float shift = m == kNegInf ? 0.0f : m;
+        float l = 0.0f;
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-            const int c = col(e);
-            if (c < cols) y[c] = v[e] * s;
+            v[r][e] = expf(v[r][e] - shift);
+            l += v[r][e];
+        }
+        float M = m, L = l;
+        block_merge<WPR>(M, L, sm, sl, wave, lane);
+        const float s = expf(m - M) / L;
+        if (row0 + r >= rows) continue;  // past the last row: nothing to write
+        float *y = Y + (size_t)(row0 + r) * ldy;
+        if constexpr (VEC) {
+#pragma unroll
+            for (int q = 0; q < E / 4; ++q) {
+                const int c = 4 * (q * T + t);
+                if (c < cols)
+                    store_nt4(y + c, v[r][4 * q] * s, v[r][4 * q + 1] * s, v[r][4 * q + 2] * s,
+                              v[r][4 * q + 3] * s);
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const int c = col(e);
+                if (c < cols) store_nt(y + c, v[r][e] * s);
+            }
         }
     }
 }
@@ -200,23 +222,22 @@ __global__ __launch_bounds__(1024) void softmax_long_kernel(int rows, int cols,
             for (int q = 0; q < E / 4; ++q) {
                 const int c = base + 4 * (q * T + t);
                 if (c < cols)
-                    *(float4 *)(y + c) = make_float4(
-                        expf(v[4 * q] - M) * inv, expf(v[4 * q + 1] - M) * inv,
-                        expf(v[4 * q + 2] - M) * inv, expf(v[4 * q + 3] - M) * inv);
+                    store_nt4(y + c, expf(v[4 * q] - M) * inv, expf(v[4 * q + 1] - M) * inv,
+                              expf(v[4 * q + 2] - M) * inv, expf(v[4 * q + 3] - M) * inv);
             }
         } else {
 #pragma unroll
             for (int e = 0; e < E; ++e) {
                 const int c = base + e * T + t;
-                if (c < cols) y[c] = expf(v[e] - M) * inv;
+                if (c < cols) store_nt(y + c, expf(v[e] - M) * inv);
             }
         }
     }
 }
 
 // Row sums: each lane adds its elements in order (U vectors or scalars per lane in
-// flight per iteration), then the lanes' sums are combined across the wave and, in wave
-// order, across the workgroup.
+// flight per iteration, loaded non-temporally: each is read once), then the lanes' sums
+// are combined across the wave and, in wave order, across the workgroup.
 template <int WPR, bool VEC>
 __global__ __launch_bounds__(block_threads<WPR>()) void row_sum_kernel(int rows, int cols,
                                                                        const float *__restrict__ X,
@@ -235,7 +256,9 @@ __global__ __launch_bounds__(block_threads<WPR>()) void row_sum_kernel(int rows,
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int c = base + 4 * (u * T + t);
-                f[u] = c < cols ? *(const float4 *)(x + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+                f32x4 z = {0.f, 0.f, 0.f, 0.f};
+                if (c < cols) z = __builtin_nontemporal_load((const f32x4 *)(x + c));
+                f[u] = make_float4(z[0], z[1], z[2], z[3]);
             }
 #pragma unroll
             for (int u = 0; u < U; ++u) acc = ((acc + f[u].x) + f[u].y + f[u].z) + f[u].w;
@@ -246,7 +269,7 @@ __global__ __launch_bounds__(block_threads<WPR>()) void row_sum_kernel(int rows,
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int c = base + u * T + t;
-                f[u] = c < cols ? x[c] : 0.0f;
+                f[u] = c < cols ? __builtin_nontemporal_load(x + c) : 0.0f;
             }
 #pragma unroll
             for (int u = 0; u < U; ++u) acc += f[u];
@@ -265,26 +288,32 @@ __global__ __launch_bounds__(block_threads<WPR>()) void row_sum_kernel(int rows,
     }
 }
 
-template <int E, int WPR, bool VEC>
+template <int E, int WPR, int R, bool VEC>
 hipError_t launch_rows(int rows, int cols, const float *X, int ldx, float *Y, int ldy,
                        hipStream_t s) {
-    const int grid = WPR == 1 ? cdiv(rows, 4) : rows;
-    hipLaunchKernelGGL((softmax_rows_kernel<E, WPR, VEC>), dim3(grid), dim3(block_threads<WPR>()),
-                       0, s, rows, cols, X, ldx, Y, ldy);
+    const int grid = WPR == 1 ? cdiv(rows, 4 * R) : rows;
+    hipLaunchKernelGGL((softmax_rows_kernel<E, WPR, R, VEC>), dim3(grid),
+                       dim3(block_threads<WPR>()), 0, s, rows, cols, X, ldx, Y, ldy);
     return hipGetLastError();
 }
 
 template <bool VEC>
 hipError_t launch_softmax(int rows, int cols, const float *X, int ldx, float *Y, int ldy,
                           hipStream_t s) {
-    if (cols <= 256) return launch_rows<4, 1, VEC>(rows, cols, X, ldx, Y, ldy, s);
-    if (cols <= 512) return launch_rows<8, 1, VEC>(rows, cols, X, ldx, Y, ldy, s);
-    if (cols <= 1024) return launch_rows<16, 1, VEC>(rows, cols, X, ldx, Y, ldy, s);
-    if (cols <= 2048) return launch_rows<8, 4, VEC>(rows, cols, X, ldx, Y, ldy, s);
-    if (cols <= 4096) return launch_rows<16, 4, VEC>(rows, cols, X, ldx, Y, ldy, s);
-    if (cols <= 8192) return launch_rows<16, 8, VEC>(rows, cols, X, ldx, Y, ldy, s);
-    if (cols <= 16384) return launch_rows<16, 16, VEC>(rows, cols, X, ldx, Y, ldy, s);
-    if (cols <= kMaxResident) return launch_rows<32, 16, VEC>(rows, cols, X, ldx, Y, ldy, s);
+    // (elements per lane, waves per row, rows per wave) by row length, from a sweep of
+    // the 64 Mi-element workloads
+    if (cols <= 256) return launch_rows<4, 1, 2, VEC>(rows, cols, X, ldx, Y, ldy, s);
+    if (cols <= 512) return launch_rows<8, 1, 1, VEC>(rows, cols, X, ldx, Y, ldy, s);
+    if (cols <= 1024) return launch_rows<8, 2, 1, VEC>(rows, cols, X, ldx, Y, ldy, s);
+    if (cols <= 2048) return launch_rows<8, 4, 1, VEC>(rows, cols, X, ldx, Y, ldy, s);
+    if (cols <= 4096) return launch_rows<32, 2, 1, VEC>(rows, cols, X, ldx, Y, ldy, s);
+    if (cols <= 8192) return launch_rows<32, 4, 1, VEC>(rows, cols, X, ldx, Y, ldy, s);
+    if (cols <= 16384) return launch_rows<16, 16, 1, VEC>(rows, cols, X, ldx, Y, ldy, s);
+    if (cols <= kMaxResident) {
+        // one element per load: 64 per lane would need more scalar registers than exist
+        if constexpr (VEC) return launch_rows<64, 8, 1, true>(rows, cols, X, ldx, Y, ldy, s);
+        else return launch_rows<32, 16, 1, false>(rows, cols, X, ldx, Y, ldy, s);
+    }
     hipLaunchKernelGGL((softmax_long_kernel<VEC>), dim3(rows), dim3(1024), 0, s, rows, cols, X,
                        ldx, Y, ldy);
     return hipGetLastError();

@@ -5,7 +5,7 @@ and warp-shuffle reduction) against the oracle, through the C ABI.
 Softmax bar, per element (binary32 against the oracle's binary64 value y):
     |y_gpu - y| <= 2^-24 (2 |x - m| + 2 n + 64) y + 2^-120
 with m the row maximum and n the number of elements one lane adds in sequence (at most
-32 for rows held on chip, cols / 1024 for longer rows).  The terms: the rounding of
+64 for rows held on chip, cols / 1024 for longer rows).  The terms: the rounding of
 x - m in binary32 (|x - m| 2^-24, doubled for the two exponentials whose arguments
 carry it), the running sum (n sequential additions plus the 6 + 4 levels of the merge
 tree, each a rounding and a rescale), expf (1 ulp) and the final scaling, plus an
@@ -41,7 +41,7 @@ def _gpu():
 
 
 def lane_count(cols: int) -> int:
-    return max(32, -(-cols // 1024))
+    return max(64, -(-cols // 1024))
 
 
 def run_softmax(X, padx=0, pady=0, offset=0, in_place=False):
