@@ -61,6 +61,12 @@ def _configure(lib):
     lib.oracle_xor_words.restype = ctypes.c_uint32
     lib.oracle_chase.argtypes = [vp, ctypes.c_int64, ctypes.c_uint32, ctypes.c_int64]
     lib.oracle_chase.restype = ctypes.c_uint32
+    lib.oracle_f64_to_f16.argtypes = [ctypes.c_double]
+    lib.oracle_f64_to_f16.restype = ctypes.c_uint16
+    lib.oracle_f64_to_bf16.argtypes = [ctypes.c_double]
+    lib.oracle_f64_to_bf16.restype = ctypes.c_uint16
+    lib.oracle_gemm_ex16.argtypes = [i, i, i, i, i, i, i, i, i, vp, i, vp, i, vp, dp, vp, i]
+    lib.oracle_gemm_ex16.restype = i
     lib.oracle_softmax.argtypes = [i, i, vp, i, dp, fp, i, dp, dp]
     lib.oracle_softmax.restype = i
     lib.oracle_row_sum.argtypes = [i, i, vp, i, dp, fp]
@@ -173,6 +179,55 @@ def gemm_ex(A: np.ndarray, B: np.ndarray, dtype: str = "f32", trans_a: bool = Fa
     if rc != 0:
         raise RuntimeError(f"oracle_gemm_ex failed ({rc})")
     return C64, C32
+
+
+def gemm_ex16(A: np.ndarray, B: np.ndarray, dtype: str, trans_a: bool = False,
+              trans_b: bool = False, neg_a: bool = False, neg_b: bool = False,
+              C_in: np.ndarray | None = None, lib=None):
+    """(C64, C16) of the general form with C in the operands' 16-bit type: C16 holds the
+    binary64 results rounded once (to nearest, ties to even) to binary16 / bfloat16, as
+    uint16 bit patterns; ``C_in`` (uint16 bits, M x N) is added when given."""
+    if dtype not in ("f16", "bf16"):
+        raise ValueError("gemm_ex16 takes f16 or bf16 operands")
+    np_t, code = _DT[dtype]
+    if A.dtype != np_t or B.dtype != np_t:
+        raise TypeError(f"{dtype} oracle expects uint16 operands")
+    M, K = (A.shape[1], A.shape[0]) if trans_a else A.shape
+    KB, N = (B.shape[1], B.shape[0]) if trans_b else B.shape
+    if KB != K:
+        raise ValueError("inner dimensions differ")
+    A = np.ascontiguousarray(A)
+    B = np.ascontiguousarray(B)
+    C64 = np.zeros((M, N), dtype=np.float64)
+    C16 = np.zeros((M, N), dtype=np.uint16)
+    cin = None
+    if C_in is not None:
+        cin = np.ascontiguousarray(C_in, dtype=np.uint16)
+        if cin.shape != (M, N):
+            raise ValueError("C_in must be M x N")
+    lib = lib or _load()
+    rc = lib.oracle_gemm_ex16(code, int(trans_a), int(trans_b), int(neg_a), int(neg_b),
+                              int(cin is not None), M, N, K, A.ctypes.data, max(A.shape[1], 1),
+                              B.ctypes.data, max(B.shape[1], 1),
+                              cin.ctypes.data if cin is not None else None, C64.ctypes.data,
+                              C16.ctypes.data, max(N, 1))
+    if rc != 0:
+        raise RuntimeError(f"oracle_gemm_ex16 failed ({rc})")
+    return C64, C16
+
+
+def f64_to_f16_bits(x, lib=None) -> np.ndarray:
+    """binary64 values rounded once to binary16 (ties to even), as uint16 bit patterns."""
+    lib = lib or _load()
+    x = np.asarray(x, dtype=np.float64).reshape(-1)
+    return np.array([lib.oracle_f64_to_f16(float(v)) for v in x], dtype=np.uint16)
+
+
+def f64_to_bf16_bits(x, lib=None) -> np.ndarray:
+    """binary64 values rounded once to bfloat16 (ties to even), as uint16 bit patterns."""
+    lib = lib or _load()
+    x = np.asarray(x, dtype=np.float64).reshape(-1)
+    return np.array([lib.oracle_f64_to_bf16(float(v)) for v in x], dtype=np.uint16)
 
 
 def f16_to_f64(bits: int) -> float:

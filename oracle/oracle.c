@@ -241,6 +241,81 @@ int oracle_gemm_ex(int dtype, int trans_a, int trans_b, int neg_a, int neg_b, in
     return 0;
 }
 
+/*
+ * Rounding of a binary64 value to binary16 or bfloat16, to nearest with ties to even,
+ * once (never through binary32).  A format with p significant bits and smallest normal
+ * exponent emin represents, near v, the multiples of 2^q with q = max(e, emin) - p + 1,
+ * e the exponent of v's leading bit; v * 2^-q is exact (a power-of-two scaling), and
+ * nearbyint rounds it to an integer with ties to even (the default rounding mode).
+ * binary16: p = 11, emin = -14, largest finite 65504; bfloat16: p = 8, emin = -126,
+ * largest finite (2 - 2^-7) 2^127.  Results beyond the largest finite value become
+ * infinity, as rounding to nearest requires.
+ */
+static double round_to_format(double v, int p, int emin)
+{
+    if (v == 0.0 || !isfinite(v)) return v;
+    int e;
+    frexp(v, &e); /* |v| = f 2^e with 0.5 <= f < 1: the leading bit is 2^(e-1) */
+    int lead = e - 1;
+    if (lead < emin) lead = emin;
+    const int q = lead - (p - 1);
+    return ldexp(nearbyint(ldexp(v, -q)), q);
+}
+
+static uint16_t encode16(double v, int p, int emin, int ebias, double maxfin, uint16_t inf,
+                         uint16_t nan)
+{
+    if (isnan(v)) return nan;
+    const uint16_t sign = signbit(v) ? 0x8000 : 0;
+    const double r = fabs(round_to_format(v, p, emin));
+    if (r > maxfin) return sign | inf;
+    if (r == 0.0) return sign;
+    int e;
+    frexp(r, &e);
+    const int lead = e - 1;
+    if (lead < emin) /* subnormal: the fraction field counts multiples of 2^(emin-p+1) */
+        return sign | (uint16_t)ldexp(r, p - 1 - emin);
+    const uint16_t frac = (uint16_t)(ldexp(r, p - 1 - lead) - ldexp(1.0, p - 1));
+    return sign | (uint16_t)((lead + ebias) << (p - 1)) | frac;
+}
+
+uint16_t oracle_f64_to_f16(double v)
+{
+    return encode16(v, 11, -14, 15, 65504.0, 0x7C00, 0x7E00);
+}
+
+uint16_t oracle_f64_to_bf16(double v)
+{
+    return encode16(v, 8, -126, 127, ldexp(255.0, 120), 0x7F80, 0x7FC0);
+}
+
+/*
+ * The general form with C stored in the operands' 16-bit type (dtype 1: binary16,
+ * 2: bfloat16): as oracle_gemm_ex, with Cin (when accumulate) read in that type and the
+ * binary64 value s * sum (+ Cin) rounded once to it into C16 (bit patterns, row stride
+ * ldc).  C64 receives the binary64 values.
+ */
+int oracle_gemm_ex16(int dtype, int trans_a, int trans_b, int neg_a, int neg_b, int accumulate,
+                     int M, int N, int K, const void *A, int lda, const void *B, int ldb,
+                     const uint16_t *Cin, double *C64, uint16_t *C16, int ldc)
+{
+    if (dtype != 1 && dtype != 2) return -1;
+    if (accumulate && M > 0 && N > 0 && !Cin) return -1;
+    int rc = oracle_gemm_ex(dtype, trans_a, trans_b, neg_a, neg_b, 0, M, N, K, A, lda, B, ldb,
+                            NULL, C64, NULL, ldc);
+    if (rc != 0) return rc;
+    for (int i = 0; i < M; ++i)
+        for (int j = 0; j < N; ++j) {
+            const size_t at = (size_t)i * ldc + j;
+            double v = C64[at];
+            if (accumulate)
+                v += dtype == 1 ? oracle_f16_to_f64(Cin[at]) : oracle_bf16_to_f64(Cin[at]);
+            C64[at] = v;
+            C16[at] = dtype == 1 ? oracle_f64_to_f16(v) : oracle_f64_to_bf16(v);
+        }
+    return 0;
+}
+
 /* ------------------------------------------------------------------------------------
  * Memory-slope probes ("Advanced CUDA features - starting from GEMM", section on
  * Little's law and occupancy).  The probes only move data; what they must produce is
