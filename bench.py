@@ -203,7 +203,8 @@ def general_form_lines():
     lines = ["", "## General form C = s op(A) op(B) (+ C) (`gemm355_gemm_ex`)", "",
              "op(A) = A^T means A is stored K x M, op(B) = B^T means B is stored N x K.  TFLOP/s",
              "counts 2MNK (the addition of the old C is not counted).  Negated and accumulating",
-             "calls run the kernels' signed variants, which store sign * acc (+ C).  Every case is",
+             "calls run the kernels' signed variants, which store sign * acc (+ C); \"16-bit C\" keeps",
+             "C in the operands' type (GEMM355_C_16: half the bytes written).  Every case is",
              "warmed, then the cases are timed interleaved (3 rounds of 100 launches after 20",
              "untimed ones); the table gives the median round.", "",
              "| dtype | n | layout | mode | kernel path | time (us) | TFLOP/s | % of peak | vs plain NN |",
@@ -216,14 +217,19 @@ def general_form_lines():
         dA, dB = conv(np.ascontiguousarray(A)), conv(np.ascontiguousarray(B))
         dAt, dBt = conv(np.ascontiguousarray(A.T)), conv(np.ascontiguousarray(B.T))
         dC = torch.zeros((n, n), dtype=torch.float32, device="cuda")
+        dC16 = torch.zeros((n, n), dtype=torch.int16, device="cuda")
+        modes = [("plain", 0), ("negated", gb.NEG_A), ("accumulate", gb.ACCUMULATE)]
+        if dt != "f32":
+            modes += [("16-bit C", gb.C_16), ("16-bit C, accumulate", gb.C_16 | gb.ACCUMULATE)]
         cases = []
         for layout, (ta, tb) in (("NN", (0, 0)), ("NT", (0, 1)), ("TN", (1, 0)), ("TT", (1, 1))):
-            for mode, extra in (("plain", 0), ("negated", gb.NEG_A), ("accumulate", gb.ACCUMULATE)):
+            for mode, extra in modes:
                 flags = (gb.TRANS_A if ta else 0) | (gb.TRANS_B if tb else 0) | extra
                 a = dAt if ta else dA
                 b = dBt if tb else dB
+                c = dC16 if extra & gb.C_16 else dC
                 cases.append((layout, mode, (gb.VARIANT_AUTO, gb.DTYPE_CODES[dt], flags, n, n, n,
-                                             a.data_ptr(), n, b.data_ptr(), n, dC.data_ptr(), n,
+                                             a.data_ptr(), n, b.data_ptr(), n, c.data_ptr(), n,
                                              stream.cuda_stream)))
 
         def go(args, reps):
@@ -249,11 +255,12 @@ def general_form_lines():
         for i, (layout, mode, _) in enumerate(cases):
             ms = sorted(times[i])[1]
             tf = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
-            path = "plain" if mode == "plain" else "signed / accumulating variant"
+            path = {"plain": "plain", "16-bit C": "16-bit C variant",
+                    "16-bit C, accumulate": "16-bit C variant"}.get(mode, "signed / accumulating variant")
             lines.append(f"| {dt} | {n} | {layout} | {mode} | {path} | {ms * 1e3:.1f} | {tf:.1f} | "
                          f"{100 * tf / PEAKS[dt]:.1f} | {base / ms:.2f} |")
             log(f"[report] ex {dt} {n} {layout} {mode}: {ms * 1e3:.1f} us {tf:.1f} TFLOP/s")
-        del dA, dB, dAt, dBt, dC
+        del dA, dB, dAt, dBt, dC, dC16
     return lines
 
 

@@ -108,13 +108,15 @@ gemm355_status gemm355_run_variant(int variant, int dtype, int M, int N, int K, 
 /* Operand forms of gemm355_gemm_ex (bit flags).  The tensor-core instruction table of
  * "Advanced CUDA features - starting from GEMM" lists, for its warp-group MMA, D = A*B + D
  * with transposed or negated A and B and D scaled by 0 or 1; these flags provide that
- * operation on top of the same kernels. */
+ * operation on top of the same kernels.  The table does not state D's type;
+ * GEMM355_C_16 adds the choice of keeping C in the operands' 16-bit type. */
 enum {
     GEMM355_TRANS_A = 1,     /* op(A) = A^T: A is stored K x M (element (k,i) at A[k*lda+i]) */
     GEMM355_TRANS_B = 2,     /* op(B) = B^T: B is stored N x K (element (j,k) at B[j*ldb+k]) */
     GEMM355_NEG_A = 4,       /* use -op(A) */
     GEMM355_NEG_B = 8,       /* use -op(B) */
-    GEMM355_ACCUMULATE = 16  /* D scaled by 1 (C += ...) instead of 0 (C = ...) */
+    GEMM355_ACCUMULATE = 16, /* D scaled by 1 (C += ...) instead of 0 (C = ...) */
+    GEMM355_C_16 = 32        /* C (and the old C) in the operands' 16-bit type, see below */
 };
 
 /* C = (+-op(A)) (+-op(B)) [+ C]:
@@ -129,9 +131,15 @@ enum {
  * GEMM355_ERR_UNSUPPORTED).  Unknown flag bits are GEMM355_ERR_INVALID_ARG.
  * Accumulation: every kernel adds s * (its FP32 sum) to the old C in its epilogue, one
  * rounding.  K = 0: C = s * (+0.0) without GEMM355_ACCUMULATE, C unchanged with it.
+ * C type: C is binary32 (`C` points to float, ldc counts floats), or with GEMM355_C_16
+ * and dtype GEMM355_F16 / GEMM355_BF16 it is stored in that same 16-bit format (`C`
+ * points to uint16_t patterns, ldc counts them): each result is the binary32 value
+ * s * sum (+ old C widened to binary32) rounded to nearest with ties to even (FP32
+ * accumulation, 16-bit storage).  GEMM355_C_16 with dtype GEMM355_F32 is
+ * GEMM355_ERR_INVALID_ARG.
  * Everything else (ownership, asynchrony, errors) as for gemm_f32. */
 gemm355_status gemm355_gemm_ex(int variant, int dtype, unsigned flags, int M, int N, int K,
-                               const void *A, int lda, const void *B, int ldb, float *C, int ldc,
+                               const void *A, int lda, const void *B, int ldb, void *C, int ldc,
                                hipStream_t stream);
 
 /* Host-only: the family the typed entry points would launch for these arguments, or -1

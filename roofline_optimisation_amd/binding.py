@@ -22,7 +22,7 @@ VARIANT_AUTO, VARIANT_NAIVE, VARIANT_LDS_TILED, VARIANT_REGBLOCK, VARIANT_MFMA =
 VARIANTS = {"naive": VARIANT_NAIVE, "lds_tiled": VARIANT_LDS_TILED,
             "regblock": VARIANT_REGBLOCK, "mfma": VARIANT_MFMA, "auto": VARIANT_AUTO}
 DTYPE_CODES = {"f32": F32, "f16": F16, "bf16": BF16}
-TRANS_A, TRANS_B, NEG_A, NEG_B, ACCUMULATE = 1, 2, 4, 8, 16
+TRANS_A, TRANS_B, NEG_A, NEG_B, ACCUMULATE, C_16 = 1, 2, 4, 8, 16, 32
 
 # Every symbol the public headers declare.
 EXPORTS = (

@@ -30,6 +30,14 @@ __device__ __forceinline__ float to_float(bf16_t x) {
     return __builtin_bit_cast(float, (uint32_t)x.bits << 16);
 }
 
+// binary32 -> the 16-bit storage format, to nearest with ties to even.
+__device__ __forceinline__ uint16_t to_bits(float v, f16_t) {
+    return __builtin_bit_cast(uint16_t, (_Float16)v);
+}
+__device__ __forceinline__ uint16_t to_bits(float v, bf16_t) {
+    return __builtin_bit_cast(uint16_t, (__bf16)v);
+}
+
 // Arguments common to every launcher.  Pointers are device pointers; ld* are row
 // strides in elements.  C = sign * op(A) op(B) (+ C when accumulate), where op(A) is A
 // (M x K rows) or, with trans_a, the transpose of the stored K x M matrix, and likewise
@@ -45,6 +53,9 @@ struct GemmArgs {
     int trans_a = 0, trans_b = 0;
     float sign = 1.0f;
     int accumulate = 0;
+    // C (and the old C when accumulating) is stored in the operands' 16-bit type: C
+    // then points to uint16_t patterns and ldc counts those.
+    int c16 = 0;
     // The MFMA kernels have plain variants (store the accumulators as they are) and
     // variants that store sign * acc (+ C); the latter serve negated products too.
     bool signed_or_acc() const { return accumulate || sign < 0.0f; }
@@ -106,6 +117,92 @@ __device__ __forceinline__ void store_block32_acc(const floatx16 &acc, float *__
                 if (NT) __builtin_nontemporal_store(v, c);
                 else *c = v;
             }
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// The same block with C in the 16-bit type T: c = round16(sign * acc (+ old c widened
+// to binary32)), rounded to nearest with ties to even; two halves of 8 rows as above.
+// `flags`: bit 0 adds the old C; bit 1 (set by the host when ldc is even and C 4-byte
+// aligned) stores column pairs: lanes 2j and 2j+1 hold columns 2j and 2j+1 of the same
+// rows, so one exchange between them (DPP quad permute [1,0,3,2]) of each register pair
+// (r, r+1) gives the even lane both columns of row r and the odd lane both columns of
+// row r+1, and every lane moves 4 bytes per pair instead of 2 per register.  The
+// exchange runs in every lane (full EXEC) before the guarded accesses.
+template <bool EDGE, typename T, bool AREAD>
+__device__ __forceinline__ void store_block32_c16(const floatx16 &acc, uint16_t *__restrict__ C,
+                                                  int ldc, int row0, int col, int M, int N,
+                                                  float sign, int flags) {
+    const bool use_old = flags & 1;
+    auto acc_at = [&](int r) {
+        float a;
+        if constexpr (AREAD)
+            asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(a) : "a"(acc[r]));
+        else
+            a = acc[r];
+        return a;
+    };
+    if (flags & 2) {
+        const int odd = col & 1, pc = col - odd;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            __builtin_amdgcn_sched_barrier(0);
+            float old_lo[4], old_hi[4];
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const int r = 8 * h + 2 * p + odd;
+                const int row = row0 + 8 * (r / 4) + r % 4;
+                const bool in = !EDGE || (row < M && pc < N);
+                const bool both = !EDGE || pc + 1 < N;
+                uint32_t w = 0;
+                if (use_old && in) {
+                    const uint16_t *c = C + (size_t)row * ldc + pc;
+                    w = both ? *(const uint32_t *)c : (uint32_t)c[0];
+                }
+                old_lo[p] = use_old ? to_float(T{(uint16_t)(w & 0xFFFF)}) : 0.f;
+                old_hi[p] = use_old ? to_float(T{(uint16_t)(w >> 16)}) : 0.f;
+            }
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const float a0 = acc_at(8 * h + 2 * p), a1 = acc_at(8 * h + 2 * p + 1);
+                const float send = odd ? a0 : a1;
+                const float recv = __builtin_bit_cast(
+                    float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, send), 0xB1, 0xF,
+                                                       0xF, false));
+                const float lo = odd ? recv : a0, hi = odd ? a1 : recv;
+                const int r = 8 * h + 2 * p + odd;
+                const int row = row0 + 8 * (r / 4) + r % 4;
+                const uint32_t w = (uint32_t)to_bits(sign * lo + old_lo[p], T{}) |
+                                   ((uint32_t)to_bits(sign * hi + old_hi[p], T{}) << 16);
+                uint16_t *c = C + (size_t)row * ldc + pc;
+                if (!EDGE || (row < M && pc + 1 < N))
+                    __builtin_nontemporal_store(w, (uint32_t *)c);
+                else if (row < M && pc < N)
+                    __builtin_nontemporal_store((uint16_t)(w & 0xFFFF), c);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        return;
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        __builtin_amdgcn_sched_barrier(0);
+        float old[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int r = 8 * h + q;
+            const int row = row0 + 8 * (r / 4) + r % 4;
+            const bool ok = use_old && (!EDGE || (row < M && col < N));
+            old[q] = ok ? to_float(T{C[(size_t)(ok ? row : 0) * ldc + (ok ? col : 0)]}) : 0.f;
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int r = 8 * h + q;
+            const int row = row0 + 8 * (r / 4) + r % 4;
+            if (!EDGE || (row < M && col < N))
+                __builtin_nontemporal_store(to_bits(sign * acc_at(r) + old[q], T{}),
+                                            C + (size_t)row * ldc + col);
         }
     }
     __builtin_amdgcn_sched_barrier(0);

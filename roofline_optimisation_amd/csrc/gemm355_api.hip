@@ -88,11 +88,13 @@ gemm355_status run(int variant, int dtype, int M, int N, int K, const void *A, i
 }
 
 constexpr unsigned kExFlags = GEMM355_TRANS_A | GEMM355_TRANS_B | GEMM355_NEG_A | GEMM355_NEG_B |
-                               GEMM355_ACCUMULATE;
+                               GEMM355_ACCUMULATE | GEMM355_C_16;
 
 gemm355_status run_ex(int variant, int dtype, unsigned flags, int M, int N, int K, const void *A,
-                      int lda, const void *B, int ldb, float *C, int ldc, hipStream_t stream) {
+                      int lda, const void *B, int ldb, void *C, int ldc, hipStream_t stream) {
     if ((flags & ~kExFlags) != 0) return GEMM355_ERR_INVALID_ARG;
+    const bool c16 = flags & GEMM355_C_16;
+    if (c16 && dtype != kF16 && dtype != kBF16) return GEMM355_ERR_INVALID_ARG;
     const bool ta = flags & GEMM355_TRANS_A, tb = flags & GEMM355_TRANS_B;
     const bool acc = flags & GEMM355_ACCUMULATE;
     const bool neg = ((flags & GEMM355_NEG_A) != 0) != ((flags & GEMM355_NEG_B) != 0);
@@ -107,7 +109,8 @@ gemm355_status run_ex(int variant, int dtype, unsigned flags, int M, int N, int 
     if ((long)M * N > 0 && C == nullptr) return GEMM355_ERR_INVALID_ARG;
     if (variant < GEMM355_VARIANT_AUTO || variant > GEMM355_VARIANT_MFMA)
         return GEMM355_ERR_INVALID_ARG;
-    GemmArgs g{M, N, K, A, lda, B, ldb, C, ldc};
+    GemmArgs g{M, N, K, A, lda, B, ldb, (float *)C, ldc};
+    g.c16 = c16;
     g.trans_a = ta;
     g.trans_b = tb;
     g.sign = neg ? -1.0f : 1.0f;
@@ -154,7 +157,7 @@ gemm355_status gemm355_run_variant(int variant, int dtype, int M, int N, int K, 
 }
 
 gemm355_status gemm355_gemm_ex(int variant, int dtype, unsigned flags, int M, int N, int K,
-                               const void *A, int lda, const void *B, int ldb, float *C, int ldc,
+                               const void *A, int lda, const void *B, int ldb, void *C, int ldc,
                                hipStream_t stream) {
     return run_ex(variant, dtype, flags, M, N, K, A, lda, B, ldb, C, ldc, stream);
 }

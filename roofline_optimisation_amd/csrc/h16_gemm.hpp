@@ -26,9 +26,10 @@
 //    c + 4q + 3, and output lane j receives column c + j%16 for rows k .. k+3;
 //  * interior tiles (inside M x N, K a multiple of BK) run a straight-line kernel; the
 //    ragged strips run a predicated one that zero-fills loads and guards stores;
-//  * C = sign * op(A) op(B) (+ C): the plain kernels store the accumulators as they are;
-//    the signed / accumulating variants (ACC) store sign * acc, adding the old C (loaded
-//    block by block in the epilogue) when accumulating.
+//  * C = sign * op(A) op(B) (+ C): the epilogue kind EPI selects what the stores do:
+//    0 stores the FP32 accumulators as they are; 1 stores sign * acc in FP32, adding the
+//    old C (loaded block by block in the epilogue) when accumulating; 2 does the same
+//    with C in the operands' 16-bit type (old C widened, result rounded to nearest even).
 //
 // Interior 256 x 256 tiles with K a multiple of 128 take a second design (dma_tile
 // below): the tiles go from memory straight into LDS (buffer_load_dwordx4 ... lds)
@@ -141,7 +142,7 @@ struct H16Frag<true, NBLK> {
 // LOAD: 0 = 16-bit loads (rows not 16-byte aligned), 1 = dwordx4 through pointers,
 // 2 = dwordx4 through buffer resources (interior tiles, offsets below 2^31 bytes).
 template <typename T, int BM, int BN, int WM, int WN, int LOAD, bool EDGE, bool PAIRED,
-          bool A_MN, bool B_MN, bool ACC>
+          bool A_MN, bool B_MN, int EPI>
 __device__ __forceinline__ void h16_tile(int M, int N, int K, const uint16_t *__restrict__ A,
                                          int lda, const uint16_t *__restrict__ B, int ldb,
                                          float *__restrict__ C, int ldc, float sign,
@@ -379,7 +380,9 @@ __device__ __forceinline__ void h16_tile(int M, int N, int K, const uint16_t *__
         {
             const int row0 = m0 + wm * Cfg::kTM + 32 * i + 4 * lhi;
             const int col = n0 + wn * Cfg::kTN + 32 * j + l32;
-            if constexpr (ACC) store_block32_acc<EDGE, true, (MB * NB > 8)>(acc[i][j], C, ldc, row0, col, M, N, sign, use_old);
+            if constexpr (EPI == 2)
+                store_block32_c16<EDGE, T, (MB * NB > 8)>(acc[i][j], (uint16_t *)C, ldc, row0, col, M, N, sign, use_old);
+            else if constexpr (EPI == 1) store_block32_acc<EDGE, true, (MB * NB > 8)>(acc[i][j], C, ldc, row0, col, M, N, sign, use_old);
             else store_block32<EDGE, true>(acc[i][j], C, ldc, row0, col, M, N);
         }
 }
@@ -405,7 +408,7 @@ __device__ __forceinline__ void h16_tile_of(int bid, int nblocks, int tiles_m, i
 }
 
 template <typename T, int BM, int BN, int WM, int WN, int MINW, int LOAD, bool EDGE, bool PAIRED,
-          bool A_MN, bool B_MN, bool ACC>
+          bool A_MN, bool B_MN, int EPI>
 __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(MINW)))
 void mfma_f16_gemm_kernel(int M, int N, int K, const uint16_t *__restrict__ A, int lda,
                           const uint16_t *__restrict__ B, int ldb, float *__restrict__ C, int ldc,
@@ -416,7 +419,7 @@ void mfma_f16_gemm_kernel(int M, int N, int K, const uint16_t *__restrict__ A, i
     const int tiles_n = EDGE ? cdiv(N, BN) : N / BN;
     int tm, tn;
     h16_tile_of<EDGE>(blockIdx.x, gridDim.x, tiles_m, tiles_n, N % BN != 0, all_tiles != 0, tm, tn);
-    h16_tile<T, BM, BN, WM, WN, LOAD, EDGE, PAIRED, A_MN, B_MN, ACC>(
+    h16_tile<T, BM, BN, WM, WN, LOAD, EDGE, PAIRED, A_MN, B_MN, EPI>(
         M, N, K, A, lda, B, ldb, C, ldc, sign, use_old, tm * BM, tn * BN, lds);
 }
 
@@ -576,7 +579,7 @@ struct DmaOp {
     }
 };
 
-template <typename T, bool A_MN, bool B_MN, bool ACC>
+template <typename T, bool A_MN, bool B_MN, int EPI>
 __device__ __forceinline__ void dma_tile(int K, const uint16_t *__restrict__ A, int lda,
                                          const uint16_t *__restrict__ B, int ldb,
                                          float *__restrict__ C, int ldc, float sign,
@@ -731,14 +734,16 @@ __device__ __forceinline__ void dma_tile(int K, const uint16_t *__restrict__ A, 
         for (int j = 0; j < kNB; ++j)
         {
             const int row0 = m0 + wm * kTM + 32 * i + 4 * lhi, col = n0 + wn * kTN + 32 * j + l32;
-            if constexpr (ACC) store_block32_acc<false, true, true>(acc[i][j], C, ldc, row0, col, 0, 0, sign, use_old);
+            if constexpr (EPI == 2)
+                store_block32_c16<false, T, true>(acc[i][j], (uint16_t *)C, ldc, row0, col, 0, 0, sign, use_old);
+            else if constexpr (EPI == 1) store_block32_acc<false, true, true>(acc[i][j], C, ldc, row0, col, 0, 0, sign, use_old);
             else store_block32<false, true>(acc[i][j], C, ldc, row0, col, 0, 0);
         }
 }
 
 }  // namespace dma
 
-template <typename T, bool A_MN, bool B_MN, bool ACC>
+template <typename T, bool A_MN, bool B_MN, int EPI>
 __global__ __launch_bounds__(64 * dma::kWaves) __attribute__((amdgpu_waves_per_eu(1)))
 void mfma_f16_dma_kernel(int M, int N, int K, const uint16_t *__restrict__ A, int lda,
                          const uint16_t *__restrict__ B, int ldb, float *__restrict__ C,
@@ -746,7 +751,7 @@ void mfma_f16_dma_kernel(int M, int N, int K, const uint16_t *__restrict__ A, in
     __shared__ __attribute__((aligned(1024))) char lds[dma::kLds];
     int tm, tn;
     grouped_tile(xcd_contiguous_id(blockIdx.x, gridDim.x), M / dma::kBM, N / dma::kBN, 4, tm, tn);
-    dma::dma_tile<T, A_MN, B_MN, ACC>(K, A, lda, B, ldb, C, ldc, sign, use_old, tm * dma::kBM,
+    dma::dma_tile<T, A_MN, B_MN, EPI>(K, A, lda, B, ldb, C, ldc, sign, use_old, tm * dma::kBM,
                                       tn * dma::kBN, lds);
 }
 
@@ -765,22 +770,31 @@ inline bool use_dma(const GemmArgs &g, int tile) {
            op_fits(g.trans_b == 0, dma::kBN, g.K, g.ldb);
 }
 
+// The epilogue's flags argument: bit 0 adds the old C; with 16-bit C, bit 1 selects
+// column-pair accesses (possible when ldc is even and C 4-byte aligned).
+template <int EPI>
+inline int epi_flags(const GemmArgs &g) {
+    int f = g.accumulate ? 1 : 0;
+    if (EPI == 2 && g.ldc % 2 == 0 && (uintptr_t)g.C % 4 == 0) f |= 2;
+    return f;
+}
+
 template <typename T, int BM, int BN, int WM, int WN, int MINW, int LOAD, bool EDGE, bool PAIRED,
-          bool A_MN, bool B_MN, bool ACC>
+          bool A_MN, bool B_MN, int EPI>
 hipError_t launch_one(const GemmArgs &g, int tiles, int all_flag, hipStream_t s) {
-    hipLaunchKernelGGL((mfma_f16_gemm_kernel<T, BM, BN, WM, WN, MINW, LOAD, EDGE, PAIRED, A_MN, B_MN, ACC>),
+    hipLaunchKernelGGL((mfma_f16_gemm_kernel<T, BM, BN, WM, WN, MINW, LOAD, EDGE, PAIRED, A_MN, B_MN, EPI>),
                        dim3(tiles), dim3(64 * WM * WN), 0, s, g.M, g.N, g.K,
                        (const uint16_t *)g.A, g.lda, (const uint16_t *)g.B, g.ldb, g.C, g.ldc,
-                       g.sign, g.accumulate, all_flag);
+                       g.sign, epi_flags<EPI>(g), all_flag);
     return hipGetLastError();
 }
 
 // Interior tiles: direct-to-LDS loads (256 x 256, K % 128 == 0), else buffer loads when
 // rows are 16-byte aligned and every offset fits in 31 bits, with the two-set pipeline
 // when the number of k-steps is even; ragged strips: predicated pointer loads.  The
-// signed / accumulating variants (ACC) keep to the direct-to-LDS and pointer-load
+// signed / accumulating epilogues (EPI 1, 2) keep to the direct-to-LDS and pointer-load
 // kernels, which bounds the number of instances.
-template <typename T, int BM, int BN, int WM, int WN, int MINW, bool A_MN, bool B_MN, bool ACC>
+template <typename T, int BM, int BN, int WM, int WN, int MINW, bool A_MN, bool B_MN, int EPI>
 hipError_t launch_cfg(const GemmArgs &g, hipStream_t s) {
     const bool vec = h16_vec(g);
     const bool kfull = g.K % kBK == 0;
@@ -791,27 +805,27 @@ hipError_t launch_cfg(const GemmArgs &g, hipStream_t s) {
     if (full_tiles > 0) {
         hipError_t e = hipSuccess;
         if (use_dma(g, BM)) {
-            hipLaunchKernelGGL((mfma_f16_dma_kernel<T, A_MN, B_MN, ACC>), dim3(full_tiles),
+            hipLaunchKernelGGL((mfma_f16_dma_kernel<T, A_MN, B_MN, EPI>), dim3(full_tiles),
                                dim3(64 * dma::kWaves), 0, s, g.M, g.N, g.K, (const uint16_t *)g.A,
-                               g.lda, (const uint16_t *)g.B, g.ldb, g.C, g.ldc, g.sign, g.accumulate);
+                               g.lda, (const uint16_t *)g.B, g.ldb, g.C, g.ldc, g.sign, epi_flags<EPI>(g));
             e = hipGetLastError();
-        } else if (!ACC && vec && fits) {
-            if constexpr (!ACC) {
+        } else if (EPI == 0 && vec && fits) {
+            if constexpr (EPI == 0) {
                 if ((g.K / kBK) % 2 == 0)
                     e = launch_one<T, BM, BN, WM, WN, MINW, 2, false, true, A_MN, B_MN, false>(g, full_tiles, all_flag, s);
                 else
                     e = launch_one<T, BM, BN, WM, WN, MINW, 2, false, false, A_MN, B_MN, false>(g, full_tiles, all_flag, s);
             }
         } else if (vec) {
-            e = launch_one<T, BM, BN, WM, WN, MINW, 1, false, false, A_MN, B_MN, ACC>(g, full_tiles, all_flag, s);
+            e = launch_one<T, BM, BN, WM, WN, MINW, 1, false, false, A_MN, B_MN, EPI>(g, full_tiles, all_flag, s);
         } else {
-            e = launch_one<T, BM, BN, WM, WN, MINW, 0, false, false, A_MN, B_MN, ACC>(g, full_tiles, all_flag, s);
+            e = launch_one<T, BM, BN, WM, WN, MINW, 0, false, false, A_MN, B_MN, EPI>(g, full_tiles, all_flag, s);
         }
         if (e != hipSuccess) return e;
     }
     if (edge_tiles > 0) {
-        if (vec) return launch_one<T, BM, BN, WM, WN, MINW, 1, true, false, A_MN, B_MN, ACC>(g, edge_tiles, all_flag, s);
-        return launch_one<T, BM, BN, WM, WN, MINW, 0, true, false, A_MN, B_MN, ACC>(g, edge_tiles, all_flag, s);
+        if (vec) return launch_one<T, BM, BN, WM, WN, MINW, 1, true, false, A_MN, B_MN, EPI>(g, edge_tiles, all_flag, s);
+        return launch_one<T, BM, BN, WM, WN, MINW, 0, true, false, A_MN, B_MN, EPI>(g, edge_tiles, all_flag, s);
     }
     return hipSuccess;
 }
@@ -836,10 +850,10 @@ inline int pick_tile(const GemmArgs &g) {
     return tile;
 }
 
-template <typename T, bool A_MN, bool B_MN, bool ACC>
+template <typename T, bool A_MN, bool B_MN, int EPI>
 hipError_t launch_layout(const GemmArgs &g, hipStream_t s) {
-    if (pick_tile(g) == 256) return launch_cfg<T, 256, 256, 2, 2, 1, A_MN, B_MN, ACC>(g, s);
-    return launch_cfg<T, 128, 128, 2, 2, 2, A_MN, B_MN, ACC>(g, s);
+    if (pick_tile(g) == 256) return launch_cfg<T, 256, 256, 2, 2, 1, A_MN, B_MN, EPI>(g, s);
+    return launch_cfg<T, 128, 128, 2, 2, 2, A_MN, B_MN, EPI>(g, s);
 }
 
 }  // namespace

@@ -1,8 +1,9 @@
 // FP16 / BF16 GEMM with FP32 accumulation on the gfx950 matrix cores: the plain product
 // in the untransposed layout (A k-contiguous, B n-contiguous) and the dispatch.  The
-// kernels and their design are in h16_gemm.hpp; the transposed layouts and the
-// accumulating variants are instantiated in k_mfma_f16_tx.hip and k_mfma_f16_acc*.hip,
-// so that the translation units compile in parallel.
+// kernels and their design are in h16_gemm.hpp; the transposed layouts, the
+// accumulating variants and the 16-bit-C variants are instantiated in k_mfma_f16_tx.hip,
+// k_mfma_f16_acc*.hip and k_mfma_*_c16.hip, so that the translation units compile in
+// parallel.
 #include "h16_gemm.hpp"
 
 namespace g355 {
@@ -10,6 +11,8 @@ namespace g355 {
 hipError_t launch_mfma_f16_tx(int dtype, const GemmArgs &g, hipStream_t s);
 hipError_t launch_mfma_f16_acc(const GemmArgs &g, hipStream_t s);
 hipError_t launch_mfma_bf16_acc(const GemmArgs &g, hipStream_t s);
+hipError_t launch_mfma_f16_c16(const GemmArgs &g, hipStream_t s);
+hipError_t launch_mfma_bf16_c16(const GemmArgs &g, hipStream_t s);
 
 const char *desc_mfma_f16(int dtype, const GemmArgs &g) {
     const bool v = h16_vec(g);
@@ -25,11 +28,12 @@ const char *desc_mfma_f16(int dtype, const GemmArgs &g) {
 }
 
 hipError_t launch_mfma_f16(int dtype, const GemmArgs &g, hipStream_t s) {
+    if (g.c16) return dtype == kF16 ? launch_mfma_f16_c16(g, s) : launch_mfma_bf16_c16(g, s);
     if (g.signed_or_acc()) return dtype == kF16 ? launch_mfma_f16_acc(g, s) : launch_mfma_bf16_acc(g, s);
     if (g.trans_a || g.trans_b) return launch_mfma_f16_tx(dtype, g, s);
     // A is k-contiguous (KM), B n-contiguous (MN)
-    return dtype == kF16 ? launch_layout<f16_t, false, true, false>(g, s)
-                         : launch_layout<bf16_t, false, true, false>(g, s);
+    return dtype == kF16 ? launch_layout<f16_t, false, true, 0>(g, s)
+                         : launch_layout<bf16_t, false, true, 0>(g, s);
 }
 
 }  // namespace g355

@@ -6,10 +6,10 @@ namespace g355 {
 
 hipError_t launch_mfma_f16_acc(const GemmArgs &g, hipStream_t s) {
     const bool a_mn = g.trans_a != 0, b_mn = g.trans_b == 0;
-    if (!a_mn && b_mn) return launch_layout<f16_t, false, true, true>(g, s);
-    if (a_mn && !b_mn) return launch_layout<f16_t, true, false, true>(g, s);
-    if (a_mn) return launch_layout<f16_t, true, true, true>(g, s);
-    return launch_layout<f16_t, false, false, true>(g, s);
+    if (!a_mn && b_mn) return launch_layout<f16_t, false, true, 1>(g, s);
+    if (a_mn && !b_mn) return launch_layout<f16_t, true, false, 1>(g, s);
+    if (a_mn) return launch_layout<f16_t, true, true, 1>(g, s);
+    return launch_layout<f16_t, false, false, 1>(g, s);
 }
 
 }  // namespace g355

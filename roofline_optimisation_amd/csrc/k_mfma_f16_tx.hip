@@ -8,10 +8,10 @@ namespace g355 {
 hipError_t launch_mfma_f16_tx(int dtype, const GemmArgs &g, hipStream_t s) {
     const bool f16 = dtype == kF16;
     if (g.trans_a && g.trans_b)
-        return f16 ? launch_layout<f16_t, true, false, false>(g, s) : launch_layout<bf16_t, true, false, false>(g, s);
+        return f16 ? launch_layout<f16_t, true, false, 0>(g, s) : launch_layout<bf16_t, true, false, 0>(g, s);
     if (g.trans_a)
-        return f16 ? launch_layout<f16_t, true, true, false>(g, s) : launch_layout<bf16_t, true, true, false>(g, s);
-    return f16 ? launch_layout<f16_t, false, false, false>(g, s) : launch_layout<bf16_t, false, false, false>(g, s);
+        return f16 ? launch_layout<f16_t, true, true, 0>(g, s) : launch_layout<bf16_t, true, true, 0>(g, s);
+    return f16 ? launch_layout<f16_t, false, false, 0>(g, s) : launch_layout<bf16_t, false, false, 0>(g, s);
 }
 
 }  // namespace g355

@@ -9,13 +9,14 @@
 // gfx950 mapping: 64 x 4 threads per workgroup, the 64 lanes of a wave along a row of
 // C, so each B row segment and each C store is one contiguous 256-byte access and the
 // A element is a wave-uniform broadcast.  It also takes the transposed, negated and
-// accumulating forms directly (C = sign * op(A) op(B) (+ C)).
+// accumulating forms directly (C = sign * op(A) op(B) (+ C)), with C in binary32 or
+// (C16) in the operands' 16-bit type.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace g355 {
 
-template <typename T>
+template <typename T, bool C16>
 __global__ __launch_bounds__(256) void naive_gemm_kernel(int M, int N, int K,
                                                          const T *__restrict__ A, int lda,
                                                          const T *__restrict__ B, int ldb,
@@ -33,27 +34,43 @@ __global__ __launch_bounds__(256) void naive_gemm_kernel(int M, int N, int K,
     float acc = 0.0f;
     for (int k = 0; k < K; ++k)
         acc = __builtin_fmaf(to_float(a[k * sa]), to_float(b[k * sb]), acc);
-    float *c = C + (size_t)row * ldc + col;
     const float v = sign * acc;
-    *c = accumulate ? v + *c : v;
+    if constexpr (C16) {
+        uint16_t *c = (uint16_t *)C + (size_t)row * ldc + col;
+        *c = to_bits(accumulate ? v + to_float(T{*c}) : v, T{});
+    } else {
+        float *c = C + (size_t)row * ldc + col;
+        *c = accumulate ? v + *c : v;
+    }
 }
 
 hipError_t launch_naive(int dtype, const GemmArgs &g, hipStream_t s) {
     dim3 block(64, 4);
     dim3 grid(cdiv(g.N, 64), cdiv(g.M, 4));
+    if (g.c16) {
+        if (dtype == kF16)
+            hipLaunchKernelGGL((naive_gemm_kernel<f16_t, true>), grid, block, 0, s, g.M, g.N, g.K,
+                               (const f16_t *)g.A, g.lda, (const f16_t *)g.B, g.ldb, g.C, g.ldc,
+                               g.trans_a, g.trans_b, g.sign, g.accumulate);
+        else
+            hipLaunchKernelGGL((naive_gemm_kernel<bf16_t, true>), grid, block, 0, s, g.M, g.N, g.K,
+                               (const bf16_t *)g.A, g.lda, (const bf16_t *)g.B, g.ldb, g.C, g.ldc,
+                               g.trans_a, g.trans_b, g.sign, g.accumulate);
+        return hipGetLastError();
+    }
     switch (dtype) {
     case kF32:
-        hipLaunchKernelGGL(naive_gemm_kernel<float>, grid, block, 0, s, g.M, g.N, g.K,
+        hipLaunchKernelGGL((naive_gemm_kernel<float, false>), grid, block, 0, s, g.M, g.N, g.K,
                            (const float *)g.A, g.lda, (const float *)g.B, g.ldb, g.C, g.ldc,
                            g.trans_a, g.trans_b, g.sign, g.accumulate);
         break;
     case kF16:
-        hipLaunchKernelGGL(naive_gemm_kernel<f16_t>, grid, block, 0, s, g.M, g.N, g.K,
+        hipLaunchKernelGGL((naive_gemm_kernel<f16_t, false>), grid, block, 0, s, g.M, g.N, g.K,
                            (const f16_t *)g.A, g.lda, (const f16_t *)g.B, g.ldb, g.C, g.ldc,
                            g.trans_a, g.trans_b, g.sign, g.accumulate);
         break;
     default:
-        hipLaunchKernelGGL(naive_gemm_kernel<bf16_t>, grid, block, 0, s, g.M, g.N, g.K,
+        hipLaunchKernelGGL((naive_gemm_kernel<bf16_t, false>), grid, block, 0, s, g.M, g.N, g.K,
                            (const bf16_t *)g.A, g.lda, (const bf16_t *)g.B, g.ldb, g.C, g.ldc,
                            g.trans_a, g.trans_b, g.sign, g.accumulate);
         break;

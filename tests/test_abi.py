@@ -136,7 +136,10 @@ def test_probe_argument_checks(lib):
 def test_gemm_ex_argument_checks(lib):
     E = gb.gemm355_gemm_ex
     # M=8, N=6, K=4: stored A is 8 x 4 (or 4 x 8 transposed), B 4 x 6 (or 6 x 4)
-    assert E(0, 0, 32, 8, 6, 4, P, 4, P, 6, P, 6) == gb.ERR_INVALID_ARG          # unknown flag
+    assert E(0, 0, 64, 8, 6, 4, P, 4, P, 6, P, 6) == gb.ERR_INVALID_ARG          # unknown flag
+    assert E(0, 0, gb.C_16, 8, 6, 4, P, 4, P, 6, P, 6) == gb.ERR_INVALID_ARG     # 16-bit C, FP32 in
+    for dt in (gb.F16, gb.BF16):                                                  # 16-bit C, 16-bit in
+        assert E(-1, dt, gb.C_16 | gb.ACCUMULATE, 8, 6, 4, P, 4, P, 6, P, 6) in (gb.OK, gb.ERR_DEVICE)
     assert E(0, 0, gb.TRANS_A, 8, 6, 4, P, 4, P, 6, P, 6) == gb.ERR_INVALID_ARG  # lda < M
     assert E(0, 0, gb.TRANS_B, 8, 6, 4, P, 4, P, 2, P, 6) == gb.ERR_INVALID_ARG  # ldb < K
     assert E(0, 0, 0, 8, 6, 4, P, 3, P, 6, P, 6) == gb.ERR_INVALID_ARG           # lda < K

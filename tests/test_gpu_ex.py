@@ -164,3 +164,131 @@ def test_matmul_wrapper_options():
     C64, _ = oracle.gemm_ex(np.ascontiguousarray(A.T), np.ascontiguousarray(B.T), "f32", True, True,
                             True, False, Cin)
     check(out.cpu().numpy(), C64, "f32", 40, Cin, True, "matmul wrapper ex")
+
+
+# ---------------------------------------------------------------- C in the 16-bit type
+
+SENT16 = np.uint16(0x7777)
+NAN16 = {"f16": np.uint16(0x7E00), "bf16": np.uint16(0x7FC0)}
+P16 = {"f16": 11, "bf16": 8}
+
+
+def decode16(bits: np.ndarray, dt: str) -> np.ndarray:
+    if dt == "f16":
+        return bits.view(np.float16).astype(np.float64)
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def run_ex16(opA, opB, dtype, ta, tb, na, nb, acc, Cin16=None, variant=gb.VARIANT_AUTO,
+             pad=(0, 0, 0), coff=0):
+    """Like run_ex with GEMM355_C_16: C (and Cin16) are 16-bit patterns of `dtype`; C
+    starts `coff` elements after a 4-byte aligned guard (coff = 1: only 2-byte aligned)."""
+    import torch
+    M, K = opA.shape
+    N = opB.shape[1]
+    SA = np.ascontiguousarray(opA.T) if ta else opA
+    SB = np.ascontiguousarray(opB.T) if tb else opB
+    lda, ldb, ldc = SA.shape[1] + pad[0], SB.shape[1] + pad[1], N + pad[2]
+    dA = to_device(place(SA, max(lda, 1), 0, 1, nan_fill(dtype)))
+    dB = to_device(place(SB, max(ldb, 1), 0, 1, nan_fill(dtype)))
+    g0 = GUARD + coff
+    cbuf = np.full(2 * GUARD + coff + M * ldc, SENT16, np.uint16)
+    region = cbuf[g0:g0 + M * ldc].reshape(M, ldc)
+    region[:, :N] = Cin16 if acc else NAN16[dtype]
+    dC = to_device(cbuf)
+    flags = flags_of(ta, tb, na, nb, acc) | gb.C_16
+    st = gb.gemm355_gemm_ex(variant, gb.DTYPE_CODES[dtype], flags, M, N, K, dA.data_ptr(), max(lda, 1),
+                            dB.data_ptr(), max(ldb, 1), dC.data_ptr() + 2 * g0, max(ldc, 1),
+                            torch.cuda.current_stream().cuda_stream)
+    assert st == gb.OK, st
+    torch.cuda.synchronize()
+    out = dC.cpu().numpy().view(np.uint16)
+    C = out[g0:g0 + M * ldc].reshape(M, ldc)[:, :N].copy()
+    mask = np.ones(out.shape, bool)
+    mask[g0:g0 + M * ldc].reshape(M, ldc)[:, :N] = False
+    return C, bool(np.all(out[mask] == SENT16)), SA, SB
+
+
+def compare16(M, N, K, dtype, ta, tb, na, nb, acc, seed, variant=gb.VARIANT_AUTO, pad=(0, 0, 0),
+              coff=0):
+    A, B = inputs.make_operands(M, N, K, seed, "uniform", dtype)
+    Cin16 = inputs.to_storage(np.random.default_rng(seed + 1000).uniform(-1, 1, (M, N)).astype(np.float32), dtype)
+    C, ok, SA, SB = run_ex16(A, B, dtype, ta, tb, na, nb, acc, Cin16, variant, pad, coff)
+    C64, _ = oracle.gemm_ex16(SA, SB, dtype, ta, tb, na, nb, Cin16 if acc else None)
+    what = (f"ex16 {dtype} {M}x{N}x{K} ta={ta} tb={tb} na={na} nb={nb} acc={acc} v={variant} "
+            f"pad={pad} coff={coff}")
+    assert ok, f"{what}: wrote outside C"
+    got = decode16(C, dtype)
+    assert not np.isnan(got).any(), f"{what}: NaN (an element not written, or a read outside)"
+    rel, mx = errors(got, C64)
+    bar = 2.0 ** -P16[dtype] + 1e-5
+    print(f"{what}: rel_frob={rel:.3e} (bar {bar:.3e})", flush=True)
+    assert rel <= bar, f"{what}: rel {rel:.3e} > {bar:.3e}"
+
+
+FLAGS16 = list(itertools.product([False, True], repeat=5))
+
+
+@pytest.mark.parametrize("variant", [gb.VARIANT_MFMA, gb.VARIANT_NAIVE], ids=["mfma", "naive"])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("fl", FLAGS16, ids=lambda f: "".join(n for n, b in zip(("ta", "tb", "na", "nb", "acc"), f) if b) or "plain")
+def test_c16_flag_matrix_ragged(fl, dtype, variant):
+    compare16(129, 97, 75, dtype, *fl, seed=56, variant=variant)
+
+
+SHAPES16 = [(3072, 3072, 128), (3072, 2816, 192), (1024, 1024, 128), (1024, 512, 64)]
+
+
+@pytest.mark.parametrize("mode", MODES, ids=["plain", "neg_a", "neg_b_acc"])
+@pytest.mark.parametrize("layout", LAYOUTS, ids=lambda l: f"ta{int(l[0])}tb{int(l[1])}")
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("shape", SHAPES16, ids=lambda s: "x".join(map(str, s)))
+def test_c16_tiles_every_layout(shape, dtype, layout, mode):
+    compare16(*shape, dtype, *layout, *mode, seed=57)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("layout", LAYOUTS, ids=lambda l: f"ta{int(l[0])}tb{int(l[1])}")
+def test_c16_unaligned_strides(dtype, layout):
+    compare16(300, 260, 130, dtype, *layout, False, False, True, seed=58, pad=(1, 3, 2))
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("fl", [(False, False, False, False, False), (True, False, True, False, True),
+                                (False, True, False, False, True), (True, True, True, True, True)],
+                         ids=["plain", "ta_na_acc", "tb_acc", "all"])
+def test_c16_integers_bit_exact(dtype, fl):
+    """Integer sums are exact in FP32, so both sides round the same exact value once."""
+    for (M, N, K) in [(257, 130, 77), (512, 512, 256), (3072, 3072, 128)]:
+        A, B = inputs.make_operands(M, N, K, 59, "int", dtype)
+        Cin16 = inputs.to_storage(np.random.default_rng(60).integers(-50, 51, (M, N)).astype(np.float32), dtype)
+        C, ok, SA, SB = run_ex16(A, B, dtype, *fl, Cin16)
+        _, C16 = oracle.gemm_ex16(SA, SB, dtype, *fl[:4], Cin16 if fl[4] else None)
+        # values, not zero signs (a negated product summing to 0 is -0.0)
+        assert ok and np.array_equal(decode16(C, dtype), decode16(C16, dtype)), (dtype, fl, M, N, K)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("fl", [(False, False, False, False, False), (False, False, True, False, True),
+                                (True, True, False, True, True)], ids=["plain", "na_acc", "ta_tb_nb_acc"])
+@pytest.mark.parametrize("case", ["odd_n_even_ldc", "c_2byte_aligned", "big_odd_n"])
+def test_c16_column_pairs(case, fl, dtype):
+    """The column-pair epilogue (even ldc, 4-byte aligned C) with an odd N (its last pair
+    is half inside), and the per-element epilogue when C is only 2-byte aligned."""
+    if case == "odd_n_even_ldc":
+        compare16(129, 97, 75, dtype, *fl, seed=61, pad=(0, 0, 1))
+    elif case == "c_2byte_aligned":
+        compare16(520, 300, 96, dtype, *fl, seed=62, coff=1)
+    else:
+        compare16(1300, 1025, 256, dtype, *fl, seed=63, pad=(0, 0, 3))
+
+
+def test_c16_k_zero():
+    for dtype in ("f16", "bf16"):
+        A = np.zeros((5, 0), np.uint16)
+        B = np.zeros((0, 7), np.uint16)
+        Cin16 = inputs.to_storage(np.arange(35, dtype=np.float32).reshape(5, 7), dtype)
+        for acc in (False, True):
+            C, ok, _, _ = run_ex16(A, B, dtype, False, False, False, False, acc, Cin16)
+            want = decode16(Cin16, dtype) if acc else np.zeros((5, 7))
+            assert ok and np.array_equal(decode16(C, dtype), want), (dtype, acc)

@@ -1,7 +1,7 @@
 """Pins of the oracle's general form with C stored in the operands' 16-bit type
-(``oracle.gemm_ex16``; the tensor-core instruction table of "Advanced CUDA features -
-starting from GEMM" lists 16-bit accumulator/output types beside FP32), and of its
-rounding of binary64 values to binary16 / bfloat16.
+(``oracle.gemm_ex16``: D = A*B + D of the tensor-core instruction table of "Advanced
+CUDA features - starting from GEMM", whose type for D the table leaves open, kept in
+binary16 / bfloat16), and of its rounding of binary64 values to those formats.
 
   * binary16 rounding against numpy's float64 -> float16 conversion (which rounds the
     binary64 value directly, to nearest with ties to even) on random values across the
