@@ -211,9 +211,10 @@ def matmul(A, B, out=None, variant: int | str = VARIANT_AUTO, stream=None, *,
            neg_b: bool = False, accumulate: bool = False):
     """C = (+-op(A)) (+-op(B)) [+ out] on the GPU through libgemm355.  A and B are the
     stored 2-D CUDA tensors (float32, float16 or bfloat16, rows contiguous): A is M x K,
-    or K x M with trans_a; B is K x N, or N x K with trans_b.  The result is float32;
-    with accumulate, `out` (float32, M x N) is added to and required.  Raises
-    Gemm355Error on a non-OK status; never falls back to another implementation."""
+    or K x M with trans_a; B is K x N, or N x K with trans_b.  The result is float32,
+    or A's 16-bit type when `out` is given in that type (GEMM355_C_16); with accumulate,
+    `out` (M x N) is added to and required.  Raises Gemm355Error on a non-OK status;
+    never falls back to another implementation."""
     import torch
     if isinstance(variant, str):
         variant = VARIANTS[variant]
@@ -229,12 +230,13 @@ def matmul(A, B, out=None, variant: int | str = VARIANT_AUTO, stream=None, *,
         if accumulate:
             raise ValueError("accumulate needs `out`")
         out = torch.empty((M, N), dtype=torch.float32, device=A.device)
-    if out.dtype != torch.float32 or tuple(out.shape) != (M, N):
-        raise ValueError("out must be a float32 M x N tensor")
+    c16 = out.dtype != torch.float32
+    if (c16 and (out.dtype != A.dtype or A.dtype == torch.float32)) or tuple(out.shape) != (M, N):
+        raise ValueError("out must be an M x N tensor in float32 or in A's 16-bit type")
     s = stream if stream is not None else torch.cuda.current_stream(A.device)
     handle = s.cuda_stream if hasattr(s, "cuda_stream") else int(s)
     flags = ((TRANS_A if trans_a else 0) | (TRANS_B if trans_b else 0) | (NEG_A if neg_a else 0)
-             | (NEG_B if neg_b else 0) | (ACCUMULATE if accumulate else 0))
+             | (NEG_B if neg_b else 0) | (ACCUMULATE if accumulate else 0) | (C_16 if c16 else 0))
     if flags:
         st = gemm355_gemm_ex(variant, _dtype_code(A), flags, M, N, K, A.data_ptr(), _ld(A),
                              B.data_ptr(), _ld(B), out.data_ptr(), _ld(out), handle)

@@ -292,3 +292,17 @@ def test_c16_k_zero():
             C, ok, _, _ = run_ex16(A, B, dtype, False, False, False, False, acc, Cin16)
             want = decode16(Cin16, dtype) if acc else np.zeros((5, 7))
             assert ok and np.array_equal(decode16(C, dtype), want), (dtype, acc)
+
+
+def test_matmul_wrapper_c16():
+    import torch
+    A, B = inputs.make_operands(70, 50, 40, 64, "uniform", "bf16")
+    Cin16 = inputs.to_storage(np.random.default_rng(65).uniform(-1, 1, (70, 50)).astype(np.float32), "bf16")
+    dA = torch.from_numpy(A.view(np.int16)).cuda().view(torch.bfloat16)
+    dB = torch.from_numpy(B.view(np.int16)).cuda().view(torch.bfloat16)
+    out = torch.from_numpy(Cin16.view(np.int16)).cuda().view(torch.bfloat16)
+    gb.matmul(dA, dB, out=out, neg_b=True, accumulate=True)
+    C64, _ = oracle.gemm_ex16(A, B, "bf16", False, False, False, True, Cin16)
+    got = decode16(out.view(torch.int16).cpu().numpy().view(np.uint16), "bf16")
+    rel, _ = errors(got, C64)
+    assert rel <= 2.0 ** -8 + 1e-5, rel
