@@ -399,7 +399,11 @@ inline bool f32_fits(bool mn, int ext, int K, int ld) {
 // (buffer loads when rows are 16-byte aligned and offsets fit in 31 bits); ragged
 // strips (or every tile, when K is not a multiple of BK) to the predicated one.  ACC:
 // the variants that store sign * acc (+ C).
-template <int BM, int BN, int WM, int WN, int MINW, bool A_MN, bool B_MN, bool ACC>
+// INTERIOR: the caller guarantees whole tiles and K % BK == 0, and only the unpaired
+// interior kernels are instantiated (for configurations whose paired and predicated
+// kernels do not fit in the register budget).
+template <int BM, int BN, int WM, int WN, int MINW, bool A_MN, bool B_MN, bool ACC,
+          bool INTERIOR = false>
 hipError_t launch_cfg(const GemmArgs &g, bool vec, hipStream_t s) {
     const bool kfull = g.K % kBK == 0;
     const int full_tiles = kfull ? (g.M / BM) * (g.N / BN) : 0;
@@ -408,9 +412,10 @@ hipError_t launch_cfg(const GemmArgs &g, bool vec, hipStream_t s) {
     const bool fits = f32_fits(A_MN, BM, g.K, g.lda) && f32_fits(B_MN, BN, g.K, g.ldb);
     if (full_tiles > 0) {
         hipError_t e = hipSuccess;
-        if (vec && fits && (g.K / kBK) % 2 == 0)
-            e = launch_one<BM, BN, WM, WN, MINW, 2, false, true, A_MN, B_MN, ACC>(g, full_tiles, all_flag, s);
-        else if (vec && fits)
+        if (!INTERIOR && vec && fits && (g.K / kBK) % 2 == 0) {
+            if constexpr (!INTERIOR)
+                e = launch_one<BM, BN, WM, WN, MINW, 2, false, true, A_MN, B_MN, ACC>(g, full_tiles, all_flag, s);
+        } else if (vec && fits)
             e = launch_one<BM, BN, WM, WN, MINW, 2, false, false, A_MN, B_MN, ACC>(g, full_tiles, all_flag, s);
         else if (vec)
             e = launch_one<BM, BN, WM, WN, MINW, 1, false, false, A_MN, B_MN, ACC>(g, full_tiles, all_flag, s);
@@ -419,23 +424,29 @@ hipError_t launch_cfg(const GemmArgs &g, bool vec, hipStream_t s) {
         if (e != hipSuccess) return e;
     }
     if (edge_tiles > 0) {
-        if (vec) return launch_one<BM, BN, WM, WN, MINW, 1, true, false, A_MN, B_MN, ACC>(g, edge_tiles, all_flag, s);
-        return launch_one<BM, BN, WM, WN, MINW, 0, true, false, A_MN, B_MN, ACC>(g, edge_tiles, all_flag, s);
+        if constexpr (INTERIOR) {
+            return hipErrorInvalidValue;  // excluded by the caller
+        } else {
+            if (vec) return launch_one<BM, BN, WM, WN, MINW, 1, true, false, A_MN, B_MN, ACC>(g, edge_tiles, all_flag, s);
+            return launch_one<BM, BN, WM, WN, MINW, 0, true, false, A_MN, B_MN, ACC>(g, edge_tiles, all_flag, s);
+        }
     }
     return hipSuccess;
 }
 
-// With both operands m/n-contiguous every fragment takes four ds_read_b32 per group; the
-// 12-wave 192 x 192 tile (168 registers per wave) does not hold that, so this layout
-// takes the 128 x 128 tile instead.
+// With both operands m/n-contiguous every fragment takes four ds_read_b32 per group; in
+// the 12-wave 192 x 192 tile (168 registers per wave) only the unpaired interior kernels
+// hold that, so this layout takes the 192 tile when M and N are multiples of 192 and K of
+// 32 (no edge tiles) and the 128 x 128 tile otherwise.
 template <bool A_MN, bool B_MN, bool ACC>
 hipError_t launch_f32_layout(const GemmArgs &g, hipStream_t s) {
     const F32Pick p = pick_f32(g);
-    const int tile = (A_MN && B_MN && p.tile == 192) ? 128 : p.tile;
+    const bool whole192 = g.M % 192 == 0 && g.N % 192 == 0 && g.K % kBK == 0;
+    const int tile = (A_MN && B_MN && p.tile == 192 && !whole192) ? 128 : p.tile;
     switch (tile) {
     case 192:
         if constexpr (!(A_MN && B_MN)) return launch_cfg<192, 192, 2, 6, 3, A_MN, B_MN, ACC>(g, p.vec, s);
-        else return hipErrorInvalidValue;  // not reached
+        else return launch_cfg<192, 192, 2, 6, 3, A_MN, B_MN, ACC, true>(g, p.vec, s);
     case 128: return launch_cfg<128, 128, 2, 2, 2, A_MN, B_MN, ACC>(g, p.vec, s);
     default: return launch_cfg<64, 64, 2, 2, 4, A_MN, B_MN, ACC>(g, p.vec, s);
     }
