@@ -529,6 +529,15 @@ def write_report(path):
         lines.append(f"| {c.dtype} | {c.M}x{c.N}x{c.K} | {desc} | {ms * 1e3:.1f} | {tf:.1f} | "
                      f"{100 * e['frac']:.1f} | {e['oi']:.1f} | {e['attainable_tflops']:.0f} | {bound} |")
         log(f"[report] {c.name}: {ms * 1e3:.1f} us {tf:.1f} TFLOP/s")
+    # Context only, not a target: the analytic figures "Advanced CUDA features - starting
+    # from GEMM" works through (roofline section) for its RTX 4000 Ada, recomputed from
+    # the peak and bandwidth it states.
+    ada_peak, ada_bw = 26.7e12, 360e9
+    lines += ["", "## Context: the pages' analytic RTX 4000 Ada figures (not a target)", "",
+              f"Peak {ada_peak / 1e12:.1f} TFLOP/s FP32, {ada_bw / 1e9:.0f} GB/s: ridge "
+              f"{rl.ridge(ada_peak, ada_bw):.2f} FLOP/B, compute-bound time for the 3072^3 product "
+              f"{rl.compute_time(3072, 3072, 3072, ada_peak) * 1e3:.2f} ms (this library on one MI355X: "
+              f"see the FP32 3072^3 rows above)."]
     lines += general_form_lines()
     lines += softmax_lines(softmax_measure())
     lines += memory_slope_lines()
