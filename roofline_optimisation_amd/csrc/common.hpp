@@ -123,68 +123,13 @@ __device__ __forceinline__ void store_block32_acc(const floatx16 &acc, float *__
 }
 
 // The same block with C in the 16-bit type T: c = round16(sign * acc (+ old c widened
-// to binary32)), rounded to nearest with ties to even; two halves of 8 rows as above.
-// `flags`: bit 0 adds the old C; bit 1 (set by the host when ldc is even and C 4-byte
-// aligned) stores column pairs: lanes 2j and 2j+1 hold columns 2j and 2j+1 of the same
-// rows, so one exchange between them (DPP quad permute [1,0,3,2]) of each register pair
-// (r, r+1) gives the even lane both columns of row r and the odd lane both columns of
-// row r+1, and every lane moves 4 bytes per pair instead of 2 per register.  The
-// exchange runs in every lane (full EXEC) before the guarded accesses.
+// to binary32)), rounded to nearest with ties to even; two halves of 8 rows as above,
+// one 2-byte access per element.  `flags` bit 0 adds the old C.
 template <bool EDGE, typename T, bool AREAD>
 __device__ __forceinline__ void store_block32_c16(const floatx16 &acc, uint16_t *__restrict__ C,
                                                   int ldc, int row0, int col, int M, int N,
                                                   float sign, int flags) {
     const bool use_old = flags & 1;
-    auto acc_at = [&](int r) {
-        float a;
-        if constexpr (AREAD)
-            asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(a) : "a"(acc[r]));
-        else
-            a = acc[r];
-        return a;
-    };
-    if (flags & 2) {
-        const int odd = col & 1, pc = col - odd;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            __builtin_amdgcn_sched_barrier(0);
-            float old_lo[4], old_hi[4];
-#pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                const int r = 8 * h + 2 * p + odd;
-                const int row = row0 + 8 * (r / 4) + r % 4;
-                const bool in = !EDGE || (row < M && pc < N);
-                const bool both = !EDGE || pc + 1 < N;
-                uint32_t w = 0;
-                if (use_old && in) {
-                    const uint16_t *c = C + (size_t)row * ldc + pc;
-                    w = both ? *(const uint32_t *)c : (uint32_t)c[0];
-                }
-                old_lo[p] = use_old ? to_float(T{(uint16_t)(w & 0xFFFF)}) : 0.f;
-                old_hi[p] = use_old ? to_float(T{(uint16_t)(w >> 16)}) : 0.f;
-            }
-#pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                const float a0 = acc_at(8 * h + 2 * p), a1 = acc_at(8 * h + 2 * p + 1);
-                const float send = odd ? a0 : a1;
-                const float recv = __builtin_bit_cast(
-                    float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, send), 0xB1, 0xF,
-                                                       0xF, false));
-                const float lo = odd ? recv : a0, hi = odd ? a1 : recv;
-                const int r = 8 * h + 2 * p + odd;
-                const int row = row0 + 8 * (r / 4) + r % 4;
-                const uint32_t w = (uint32_t)to_bits(sign * lo + old_lo[p], T{}) |
-                                   ((uint32_t)to_bits(sign * hi + old_hi[p], T{}) << 16);
-                uint16_t *c = C + (size_t)row * ldc + pc;
-                if (!EDGE || (row < M && pc + 1 < N))
-                    __builtin_nontemporal_store(w, (uint32_t *)c);
-                else if (row < M && pc < N)
-                    __builtin_nontemporal_store((uint16_t)(w & 0xFFFF), c);
-            }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        return;
-    }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         __builtin_amdgcn_sched_barrier(0);
@@ -200,9 +145,86 @@ __device__ __forceinline__ void store_block32_c16(const floatx16 &acc, uint16_t 
         for (int q = 0; q < 8; ++q) {
             const int r = 8 * h + q;
             const int row = row0 + 8 * (r / 4) + r % 4;
-            if (!EDGE || (row < M && col < N))
-                __builtin_nontemporal_store(to_bits(sign * acc_at(r) + old[q], T{}),
+            if (!EDGE || (row < M && col < N)) {
+                float a;
+                if constexpr (AREAD)
+                    asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(a) : "a"(acc[r]));
+                else
+                    a = acc[r];
+                __builtin_nontemporal_store(to_bits(sign * a + old[q], T{}),
                                             C + (size_t)row * ldc + col);
+            }
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// Two horizontally adjacent 32 x 32 blocks (columns col0 .. col0+63, lane l holding
+// column l%32 of each) with C in the 16-bit type T.  With `flags` bit 1 (set by the host
+// when ldc is even and C 4-byte aligned) each row of the pair is written as one whole
+// 128-byte line: lanes 2j and 2j+1 exchange one register per row (DPP quad permute
+// [1,0,3,2]; the even lane sends its block-1 value, the odd lane its block-0 value), so
+// the even lane holds columns 2j, 2j+1 of block 0 and the odd lane columns 2j, 2j+1 of
+// block 1, and each lane reads the old C and writes the result 4 bytes at a time.  The
+// exchange runs in every lane (full EXEC) before the guarded accesses.  Without bit 1
+// each block takes store_block32_c16.
+template <bool EDGE, typename T, bool AREAD>
+__device__ __forceinline__ void store_pair32_c16(const floatx16 &acc0, const floatx16 &acc1,
+                                                 uint16_t *__restrict__ C, int ldc, int row0,
+                                                 int col0, int M, int N, float sign, int flags) {
+    const int lane = threadIdx.x & 63;
+    if (!(flags & 2)) {
+        store_block32_c16<EDGE, T, AREAD>(acc0, C, ldc, row0, col0 + (lane & 31), M, N, sign, flags);
+        store_block32_c16<EDGE, T, AREAD>(acc1, C, ldc, row0, col0 + 32 + (lane & 31), M, N, sign,
+                                          flags);
+        return;
+    }
+    const bool use_old = flags & 1;
+    const int odd = lane & 1;
+    const int cw = col0 + (lane & 30) + 32 * odd;  // first of the two columns this lane writes
+    auto rd = [&](const floatx16 &acc, int r) {
+        float a;
+        if constexpr (AREAD)
+            asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(a) : "a"(acc[r]));
+        else
+            a = acc[r];
+        return a;
+    };
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        __builtin_amdgcn_sched_barrier(0);
+        float old_lo[8], old_hi[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int r = 8 * h + q;
+            const int row = row0 + 8 * (r / 4) + r % 4;
+            const bool in = !EDGE || (row < M && cw < N);
+            const bool both = !EDGE || cw + 1 < N;
+            uint32_t w = 0;
+            if (use_old && in) {
+                const uint16_t *c = C + (size_t)row * ldc + cw;
+                w = both ? *(const uint32_t *)c : (uint32_t)c[0];
+            }
+            old_lo[q] = use_old ? to_float(T{(uint16_t)(w & 0xFFFF)}) : 0.f;
+            old_hi[q] = use_old ? to_float(T{(uint16_t)(w >> 16)}) : 0.f;
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int r = 8 * h + q;
+            const float a0 = rd(acc0, r), a1 = rd(acc1, r);
+            const float send = odd ? a0 : a1;
+            const float recv = __builtin_bit_cast(
+                float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, send), 0xB1, 0xF, 0xF,
+                                                   false));
+            const float lo = odd ? recv : a0, hi = odd ? a1 : recv;
+            const int row = row0 + 8 * (r / 4) + r % 4;
+            const uint32_t w = (uint32_t)to_bits(sign * lo + old_lo[q], T{}) |
+                               ((uint32_t)to_bits(sign * hi + old_hi[q], T{}) << 16);
+            uint16_t *c = C + (size_t)row * ldc + cw;
+            if (!EDGE || (row < M && cw + 1 < N))
+                __builtin_nontemporal_store(w, (uint32_t *)c);
+            else if (row < M && cw < N)
+                __builtin_nontemporal_store((uint16_t)(w & 0xFFFF), c);
         }
     }
     __builtin_amdgcn_sched_barrier(0);

@@ -380,9 +380,12 @@ __device__ __forceinline__ void h16_tile(int M, int N, int K, const uint16_t *__
         {
             const int row0 = m0 + wm * Cfg::kTM + 32 * i + 4 * lhi;
             const int col = n0 + wn * Cfg::kTN + 32 * j + l32;
-            if constexpr (EPI == 2)
-                store_block32_c16<EDGE, T, (MB * NB > 8)>(acc[i][j], (uint16_t *)C, ldc, row0, col, M, N, sign, use_old);
-            else if constexpr (EPI == 1) store_block32_acc<EDGE, true, (MB * NB > 8)>(acc[i][j], C, ldc, row0, col, M, N, sign, use_old);
+            if constexpr (EPI == 2) {
+                static_assert(NB % 2 == 0, "16-bit C stores block pairs");
+                if (j % 2 == 0)
+                    store_pair32_c16<EDGE, T, (MB * NB > 8)>(acc[i][j], acc[i][j + 1], (uint16_t *)C, ldc,
+                                                             row0, col - l32, M, N, sign, use_old);
+            } else if constexpr (EPI == 1) store_block32_acc<EDGE, true, (MB * NB > 8)>(acc[i][j], C, ldc, row0, col, M, N, sign, use_old);
             else store_block32<EDGE, true>(acc[i][j], C, ldc, row0, col, M, N);
         }
 }
@@ -734,9 +737,12 @@ __device__ __forceinline__ void dma_tile(int K, const uint16_t *__restrict__ A, 
         for (int j = 0; j < kNB; ++j)
         {
             const int row0 = m0 + wm * kTM + 32 * i + 4 * lhi, col = n0 + wn * kTN + 32 * j + l32;
-            if constexpr (EPI == 2)
-                store_block32_c16<false, T, true>(acc[i][j], (uint16_t *)C, ldc, row0, col, 0, 0, sign, use_old);
-            else if constexpr (EPI == 1) store_block32_acc<false, true, true>(acc[i][j], C, ldc, row0, col, 0, 0, sign, use_old);
+            if constexpr (EPI == 2) {
+                static_assert(kNB % 2 == 0, "16-bit C stores block pairs");
+                if (j % 2 == 0)
+                    store_pair32_c16<false, T, true>(acc[i][j], acc[i][j + 1], (uint16_t *)C, ldc, row0,
+                                                     col - l32, 0, 0, sign, use_old);
+            } else if constexpr (EPI == 1) store_block32_acc<false, true, true>(acc[i][j], C, ldc, row0, col, 0, 0, sign, use_old);
             else store_block32<false, true>(acc[i][j], C, ldc, row0, col, 0, 0);
         }
 }
@@ -771,7 +777,8 @@ inline bool use_dma(const GemmArgs &g, int tile) {
 }
 
 // The epilogue's flags argument: bit 0 adds the old C; with 16-bit C, bit 1 selects
-// column-pair accesses (possible when ldc is even and C 4-byte aligned).
+// 4-byte accesses that write whole lines (possible when ldc is even and C 4-byte
+// aligned).
 template <int EPI>
 inline int epi_flags(const GemmArgs &g) {
     int f = g.accumulate ? 1 : 0;
