@@ -38,7 +38,7 @@ extern "C" {
  * rounding of X - m dominates for elements far below the maximum.  Inputs are expected finite; an infinity or NaN in a row makes
  * that row's results unspecified (other rows are unaffected).
  *
- * Arguments: rows >= 0, 0 <= cols <= 2^30; ldx >= max(1, cols), ldy >= max(1, cols);
+ * Arguments: 0 <= rows <= 2^30, 0 <= cols <= 2^30; ldx >= max(1, cols), ldy >= max(1, cols);
  * X and Y non-null unless rows * cols == 0; Y may equal X (in place) when ldy == ldx,
  * any other overlap of the two matrices' spans is an argument error.  rows == 0 or
  * cols == 0 is a no-op.  Elements of Y outside the rows x cols region are not written. */
@@ -51,7 +51,7 @@ gemm355_status gemm355_softmax_f32(int rows, int cols, const float *X, int ldx, 
  * agrees with the exact sum to within about (cols / (64 * waves per row) + 12) * 2^-24
  * times the sum of the magnitudes (sums of small integers are exact).
  *
- * Arguments: rows >= 0, 0 <= cols <= 2^30, ldx >= max(1, cols); X non-null unless
+ * Arguments: 0 <= rows <= 2^30, 0 <= cols <= 2^30, ldx >= max(1, cols); X non-null unless
  * rows * cols == 0; out (rows binary32 values) non-null unless rows == 0, and not
  * overlapping X's span. */
 gemm355_status gemm355_row_sum_f32(int rows, int cols, const float *X, int ldx, float *out,

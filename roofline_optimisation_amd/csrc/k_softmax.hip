@@ -38,6 +38,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr int kMaxResident = 32768;  // longest row held in registers (1024 lanes x 32)
 constexpr int kMaxCols = 1 << 30;    // column indexes below plus one chunk stay in int
+constexpr int kMaxRows = 1 << 30;    // row indexes (workgroup x 4 + wave) x R stay in int
 
 // Merge (m, l) with another running (maximum, sum) pair: the pair with the smaller
 // maximum is rescaled to the larger.  Equal maxima (including two empty pairs, m =
@@ -354,7 +355,7 @@ extern "C" {
 gemm355_status gemm355_softmax_f32(int rows, int cols, const float *X, int ldx, float *Y,
                                    int ldy, hipStream_t stream) {
     const int need = cols > 1 ? cols : 1;
-    if (rows < 0 || cols < 0 || cols > kMaxCols || ldx < need || ldy < need)
+    if (rows < 0 || rows > kMaxRows || cols < 0 || cols > kMaxCols || ldx < need || ldy < need)
         return GEMM355_ERR_INVALID_ARG;
     if (rows == 0 || cols == 0) return GEMM355_OK;
     if (X == nullptr || Y == nullptr) return GEMM355_ERR_INVALID_ARG;
@@ -375,7 +376,7 @@ gemm355_status gemm355_softmax_f32(int rows, int cols, const float *X, int ldx, 
 
 gemm355_status gemm355_row_sum_f32(int rows, int cols, const float *X, int ldx, float *out,
                                    hipStream_t stream) {
-    if (rows < 0 || cols < 0 || cols > kMaxCols || ldx < (cols > 1 ? cols : 1))
+    if (rows < 0 || rows > kMaxRows || cols < 0 || cols > kMaxCols || ldx < (cols > 1 ? cols : 1))
         return GEMM355_ERR_INVALID_ARG;
     if (rows == 0) return GEMM355_OK;
     if (out == nullptr || (cols > 0 && X == nullptr)) return GEMM355_ERR_INVALID_ARG;

@@ -189,7 +189,8 @@ def test_softmax_and_row_sum_argument_checks(lib):
     S, R = gb.gemm355_softmax_f32, gb.gemm355_row_sum_f32
     Q = P + (1 << 24)
     bad = [(-1, 4, P, 4, Q, 4), (2, -1, P, 4, Q, 4), (2, 4, P, 3, Q, 4), (2, 4, P, 4, Q, 3),
-           (2, (1 << 30) + 1, P, (1 << 30) + 1, Q, (1 << 30) + 1), (2, 4, 0, 4, Q, 4),
+           (2, (1 << 30) + 1, P, (1 << 30) + 1, Q, (1 << 30) + 1), ((1 << 30) + 1, 4, P, 4, Q, 4),
+           (2, 4, 0, 4, Q, 4),
            (2, 4, P, 4, 0, 4),
            (2, 4, P, 8, P, 4),            # in place with different strides
            (4, 64, P, 64, P + 256, 64)]   # partial overlap
@@ -199,6 +200,7 @@ def test_softmax_and_row_sum_argument_checks(lib):
     assert S(2, 4, P, 4, P, 4) in (gb.OK, gb.ERR_DEVICE)                   # in place
     assert S(2, 4, P, 4, P + 32, 4) in (gb.OK, gb.ERR_DEVICE)              # adjacent spans
     bad = [(-1, 4, P, 4, Q), (2, -1, P, 4, Q), (2, 4, P, 3, Q), (2, 4, 0, 4, Q), (2, 4, P, 4, 0),
+           ((1 << 30) + 1, 4, P, 4, Q),
            (2, 4, P, 4, P + 16)]          # out overlaps X
     for b in bad:
         assert R(*b) == gb.ERR_INVALID_ARG, b
