@@ -521,14 +521,20 @@ def write_report(path):
     lines += ["", "## Roofline sweep (dispatched kernels)", "",
               "| dtype | M x N x K | kernel | time (us) | TFLOP/s | % of peak | OI (FLOP/B) | "
               "attainable TFLOP/s | bound |", "|---|---|---|---|---|---|---|---|---|"]
+    chart_points = []
     for c in inputs.sweep_cases():
         ms, desc, reps = time_variant(-1, c.dtype, c.M, c.N, c.K, c.seed)
         tf = 2.0 * c.M * c.N * c.K / (ms * 1e-3) / 1e12
         e = rl.roofline_entry(c.M, c.N, c.K, ms * 1e-3, c.dtype)
+        chart_points.append((e["oi"], tf, "f" if c.dtype == "f32" else "b"))
         bound = "HBM" if e["attainable_tflops"] < e["peak_tflops"] else "compute"
         lines.append(f"| {c.dtype} | {c.M}x{c.N}x{c.K} | {desc} | {ms * 1e3:.1f} | {tf:.1f} | "
                      f"{100 * e['frac']:.1f} | {e['oi']:.1f} | {e['attainable_tflops']:.0f} | {bound} |")
         log(f"[report] {c.name}: {ms * 1e3:.1f} us {tf:.1f} TFLOP/s")
+    lines += ["", "Roofline chart of the sweep (f: FP32 points, b: BF16 points; roofs min(peak, OI x 8 TB/s): "
+              "'=' BF16 2516.6 TFLOP/s, '-' FP32 157.3 TFLOP/s):", "", "```"]
+    lines += rl.text_chart(chart_points, [(PEAKS["bf16"], "="), (PEAKS["f32"], "-")], 8e12)
+    lines += ["```"]
     # Context only, not a target: the analytic figures "Advanced CUDA features - starting
     # from GEMM" works through (roofline section) for its RTX 4000 Ada, recomputed from
     # the peak and bandwidth it states.

@@ -126,3 +126,45 @@ def roofline_entry(M: int, N: int, K: int, seconds: float, dtype: str) -> dict:
         "ideal_bytes": nbytes,
         "ideal_GBps": nbytes / seconds / 1e9,
     }
+
+
+def text_chart(points, roofs, bandwidth_Bps: float, x_range=(8.0, 4096.0), y_range=(0.25, 4096.0),
+               width: int = 64, height: int = 20) -> list[str]:
+    """A log-log roofline chart as text lines.
+
+    ``points``: (intensity FLOP/B, achieved TFLOP/s, marker character); ``roofs``:
+    (peak TFLOP/s, character) -- each roof is drawn as min(peak, intensity x bandwidth).
+    Axes are log2 scaled over x_range (FLOP/B) and y_range (TFLOP/s); a point outside the
+    ranges is clamped to the border.  Later points overwrite earlier ones."""
+    lx0, lx1 = math.log2(x_range[0]), math.log2(x_range[1])
+    ly0, ly1 = math.log2(y_range[0]), math.log2(y_range[1])
+
+    def col(x):
+        return min(width - 1, max(0, round((math.log2(x) - lx0) / (lx1 - lx0) * (width - 1))))
+
+    def row(y):
+        return min(height - 1, max(0, round((ly1 - math.log2(y)) / (ly1 - ly0) * (height - 1))))
+
+    grid = [[" "] * width for _ in range(height)]
+    for peak, ch in roofs:
+        for c in range(width):
+            x = 2.0 ** (lx0 + (lx1 - lx0) * c / (width - 1))
+            grid[row(min(peak, x * bandwidth_Bps / 1e12))][c] = ch
+    for x, y, ch in points:
+        grid[row(max(y, y_range[0]))][col(x)] = ch
+    out = []
+    for r in range(height):
+        y = 2.0 ** (ly1 - (ly1 - ly0) * r / (height - 1))
+        label = f"{y:7.1f} |" if r % 4 == 0 or r == height - 1 else "        |"
+        out.append(label + "".join(grid[r]))
+    out.append("        +" + "-" * width)
+    ticks = [" "] * (width + 9)
+    for x in (8, 32, 128, 512, 2048):
+        if x_range[0] <= x <= x_range[1]:
+            t = str(x)
+            c = 9 + col(x)
+            for i, chx in enumerate(t):
+                if c + i < len(ticks):
+                    ticks[c + i] = chx
+    out.append("".join(ticks).rstrip() + "   (FLOP/B, log scale; TFLOP/s log scale)")
+    return out

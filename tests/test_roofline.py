@@ -93,3 +93,16 @@ def test_roofline_entry():
     assert e["oi"] == pytest.approx(512)
     e = rl.roofline_entry(4096, 4096, 4096, 100e-6, "f16")
     assert e["ideal_bytes"] == 2 * 2 * 4096 ** 2 + 4 * 4096 ** 2
+
+
+def test_text_chart_places_points_and_roofs():
+    lines = rl.text_chart([(1024.0, 1000.0, "b"), (8.0, 0.25, "f")], [(2516.6, "="), (157.3, "-")],
+                          8e12, width=40, height=12)
+    assert len(lines) == 14 and all(len(l) >= 9 for l in lines[:12])
+    body = [l[9:] for l in lines[:12]]
+    # the lowest-intensity, lowest-rate point sits in the bottom-left corner
+    assert body[11][0] == "f"
+    # the FP32 roof is flat at 157.3 to the right of its ridge (19.7 FLOP/B)
+    r157 = [i for i, l in enumerate(body) if l.rstrip().endswith("-")]
+    assert r157 and all(body[r157[0]][c] in "-b" for c in range(20, 40))
+    assert any("b" in l for l in body)
