@@ -361,7 +361,7 @@ struct F32Pick {
 // the MFMA rate); ragged strips run as a second launch at about half that efficiency.
 inline F32Pick pick_f32(const GemmArgs &g) {
     struct Opt { int tile; double eff; };
-    const Opt opts[] = {{192, 0.95}, {128, 0.95}, {64, 0.85}};
+    const Opt opts[] = {{192, 0.95}, {128, 0.95}, {96, 0.93}, {64, 0.85}};
     double best = -1.0;
     int tile = 64;
     for (const Opt &o : opts) {
@@ -447,7 +447,8 @@ hipError_t launch_f32_layout(const GemmArgs &g, hipStream_t s) {
     case 192:
         if constexpr (!(A_MN && B_MN)) return launch_cfg<192, 192, 2, 6, 3, A_MN, B_MN, ACC>(g, p.vec, s);
         else return launch_cfg<192, 192, 2, 6, 3, A_MN, B_MN, ACC, true>(g, p.vec, s);
-    case 128: return launch_cfg<128, 128, 2, 2, 2, A_MN, B_MN, ACC>(g, p.vec, s);
+    case 128: return launch_cfg<128, 128, 2, 4, 2, A_MN, B_MN, ACC>(g, p.vec, s);
+    case 96: return launch_cfg<96, 96, 1, 3, 3, A_MN, B_MN, ACC>(g, p.vec, s);
     default: return launch_cfg<64, 64, 2, 2, 4, A_MN, B_MN, ACC>(g, p.vec, s);
     }
 }

@@ -105,12 +105,13 @@ def test_flag_matrix_ragged(fl, dtype, variant):
     compare(129, 97, 75, dtype, *fl, seed=50, variant=variant)
 
 
-# Interior tiles of every layout: FP32 192 x 192 (3072), 128 x 128; FP16/BF16 256 x 256
+# Interior tiles of every layout: FP32 192 x 192 (3072), 128 x 128 (2048), 96 x 96 (1536; ragged
+# M, N and K), 64 x 64; FP16/BF16 256 x 256
 # direct-to-LDS (3072^2, K % 128 == 0), 256 x 256 register-staged (K % 128 != 0) and
 # 128 x 128; each plain, negated and accumulating.
 LAYOUTS = list(itertools.product([False, True], repeat=2))
 MODES = [(False, False, False), (True, False, False), (False, True, True)]  # na, nb, acc
-SHAPES = {"f32": [(3072, 3072, 64), (1024, 768, 96)],
+SHAPES = {"f32": [(3072, 3072, 64), (1024, 768, 96), (2048, 2048, 64), (1536, 1536, 96), (1351, 1537, 100)],
           "f16": [(3072, 3072, 128), (3072, 2816, 192), (1024, 1024, 128)],
           "bf16": [(3072, 3072, 256), (1024, 512, 64)]}
 

@@ -302,3 +302,23 @@ def test_f32_interior_instances(case):
     C64, _ = oracle.gemm(A, B)
     C, ok = gpu_gemm(A, B, "f32", gb.VARIANT_MFMA, guard_rows=1)
     check(C, C64, "f32", "uniform", K, ok, f"interior f32 {M}x{N}x{K}")
+
+
+# Every FP32 tile class the picker chooses, interior and predicated: 192 (3072^2), 128 with
+# 2 x 4 waves (2048^2), 96 with 1 x 3 waves (1536^2; K tail; ragged M, N and K), 64.
+F32_TILE_CASES = [((1536, 1536, 128), "96x96"), ((1536, 1536, 100), "96x96"),
+                  ((1351, 1537, 100), "96x96"), ((2048, 2048, 96), "128x128"),
+                  ((2000, 2048, 64), "64x64"), ((1024, 1024, 64), "64x64")]
+
+
+@pytest.mark.parametrize("case", F32_TILE_CASES, ids=lambda c: "x".join(map(str, c[0])))
+def test_f32_tile_classes(case):
+    (M, N, K), tile = case
+    P = 1 << 20  # any 16-byte-aligned non-null address: the query only inspects it
+    if tile is not None:
+        assert tile in gb.gemm355_kernel_desc(gb.VARIANT_AUTO, gb.F32, M, N, K, P, K, P, N, P, N)
+    A, B = inputs.make_operands(M, N, K, 44, "uniform", "f32")
+    C, ok = gpu_gemm(A, B, "f32", entry="typed", guard_rows=1)
+    rows = sample_rows(M, 96)
+    C64, _ = oracle.gemm(np.ascontiguousarray(A[rows]), B)
+    check(C[rows], C64, "f32", "uniform", K, ok, f"f32 tile class {tile} {M}x{N}x{K}")
