@@ -201,6 +201,7 @@ __device__ __forceinline__ void f32_tile(int M, int N, int K, const float *__res
     constexpr int kRA = MB * OA::kPieces;
     constexpr int kR = kRA + NB * OB::kPieces;  // fragment reads per group
     constexpr int kMf = 4 * MB * NB;            // MFMAs per group
+    static_assert(kR <= 2 * kMf, "a group's fragment reads go two per MFMA of the one before");
     F32Frag<A_MN, MB> af;
     F32Frag<B_MN, NB> bf;
     auto read_op = [&](auto mn_c, auto &fr, const float *X, int stride, int rc0, int nblk, int kq,

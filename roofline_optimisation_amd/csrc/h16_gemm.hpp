@@ -277,6 +277,7 @@ __device__ __forceinline__ void h16_tile(int M, int N, int K, const uint16_t *__
     constexpr int kMf = MB * NB;                  // MFMAs per sub-step
     constexpr int kPre = (kMf * 3 + 7) / 8;       // of those, issued before the barrier
     constexpr int kWr = kAC + kBC;                // staged chunks per k-step
+    static_assert(kR <= 2 * kMf, "a sub-step's fragment reads go two per MFMA of the one before");
 
     // Events of one k-step are spread over its kSteps * kMf MFMA slots: event e of n
     // spread over slots [lo, hi) goes after the MFMA of slot lo + ceil-spread(e).
@@ -651,6 +652,7 @@ __device__ __forceinline__ void dma_tile(int K, const uint16_t *__restrict__ A, 
     // operands, else 2 nMN.  No branches: near the end the loads repeat the last k-step or
     // double step into free stages or slots.
     constexpr int kMf = kMB * kNB, kSlots = 2 * kMf;
+    static_assert(kR <= 2 * kMf, "a sub-step's fragment reads go two per MFMA of the one before");
     constexpr int kPre = (kMf * 3 + 7) / 8;
     constexpr int kBarrier = kMf + kPre;
     constexpr int kLoadHi = kMf;
