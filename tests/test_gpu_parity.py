@@ -322,3 +322,22 @@ def test_f32_tile_classes(case):
     rows = sample_rows(M, 96)
     C64, _ = oracle.gemm(np.ascontiguousarray(A[rows]), B)
     check(C[rows], C64, "f32", "uniform", K, ok, f"f32 tile class {tile} {M}x{N}x{K}")
+
+
+# FP16/BF16 tile classes: 128 x 64 (plain products whose 128 x 128 tiling leaves CUs idle;
+# interior, ragged, K tail), 128 x 128, 256 x 256 direct-to-LDS.
+H16_TILE_CASES = [("f16", (1024, 1024, 256), "128x64"), ("bf16", (1000, 900, 200), "128x64"),
+                  ("f16", (512, 512, 100), "128x64"), ("bf16", (2048, 2048, 128), "128x128"),
+                  ("f16", (3072, 3072, 128), "lds-dma")]
+
+
+@pytest.mark.parametrize("case", H16_TILE_CASES, ids=lambda c: c[0] + "_" + "x".join(map(str, c[1])))
+def test_h16_tile_classes(case):
+    dtype, (M, N, K), tile = case
+    P = 1 << 20  # any 16-byte-aligned non-null address: the query only inspects it
+    assert tile in gb.gemm355_kernel_desc(gb.VARIANT_AUTO, gb.DTYPE_CODES[dtype], M, N, K, P, K, P, N, P, N)
+    A, B = inputs.make_operands(M, N, K, 45, "uniform", dtype)
+    C, ok = gpu_gemm(A, B, dtype, entry="typed", guard_rows=1)
+    rows = sample_rows(M, 96)
+    C64, _ = oracle.gemm(np.ascontiguousarray(A[rows]), B, dtype)
+    check(C[rows], C64, dtype, "uniform", K, ok, f"{dtype} tile class {tile} {M}x{N}x{K}")
