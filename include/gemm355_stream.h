@@ -29,7 +29,9 @@ extern "C" {
 
 enum {
     GEMM355_STREAM_COPY = 0,     /* dst[0, n_bytes) = src[0, n_bytes) */
-    GEMM355_STREAM_READ_XOR = 1  /* dst[g] = XOR of the 32-bit words workgroup g read */
+    GEMM355_STREAM_READ_XOR = 1, /* dst[g] = XOR of the 32-bit words workgroup g read */
+    GEMM355_STREAM_COPY_NT = 2   /* as COPY, with non-temporal stores (no L2 lines allocated
+                                    for dst), to measure the store cache policy */
 };
 
 /* Streams n_bytes of src through `grid` workgroups of `threads` threads.
@@ -38,8 +40,8 @@ enum {
  * workgroups round-robin (chunk c to workgroup c mod grid).  For each chunk every lane
  * first issues its `unroll` loads of vec_bytes (lane t, load u reads the chunk's bytes
  * [(u * threads + t) * vec_bytes, +vec_bytes), so every load instruction is
- * contiguous across the wave), then consumes them: mode COPY stores them to the same
- * offsets of dst, mode READ_XOR folds their 32-bit words into a running XOR.  The
+ * contiguous across the wave), then consumes them: modes COPY and COPY_NT store them to
+ * the same offsets of dst, mode READ_XOR folds their 32-bit words into a running XOR.  The
  * 32-bit words after the last whole chunk are handled one word per thread.  Each
  * workgroup also reserves lds_bytes of LDS that it does not otherwise use: at most
  * floor(163840 / lds_bytes) workgroups (and the hardware's own limits) are resident
@@ -50,8 +52,8 @@ enum {
  * word workgroup g read, so the XOR of all entries is the XOR of the whole source
  * (which workgroup reads which word depends on grid and threads, the total does not).
  *
- * Arguments: mode COPY or READ_XOR; n_bytes >= 0 and a multiple of 4; src and (mode
- * COPY) dst aligned to vec_bytes, dst aligned to 4 in mode READ_XOR; vec_bytes 4, 8 or
+ * Arguments: mode COPY, COPY_NT or READ_XOR; n_bytes >= 0 and a multiple of 4; src and
+ * (copy modes) dst aligned to vec_bytes, dst aligned to 4 in mode READ_XOR; vec_bytes 4, 8 or
  * 16; unroll 1, 2, 4 or 8; threads a multiple of 64 in [64, 1024]; 0 <= lds_bytes <=
  * 163840; 1 <= grid <= 1048576; src and dst must not overlap; src, dst non-null when
  * they are used (dst always in mode READ_XOR). */

@@ -34,7 +34,7 @@ EXPORTS = (
     "gemm355_softmax_f32", "gemm355_row_sum_f32",
 )
 
-STREAM_COPY, STREAM_READ_XOR = 0, 1
+STREAM_COPY, STREAM_READ_XOR, STREAM_COPY_NT = 0, 1, 2
 
 
 class Gemm355Error(RuntimeError):

@@ -54,10 +54,16 @@ __global__ __launch_bounds__(1024) void stream_kernel(const char *__restrict__ s
         V v[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) v[u] = *(const V *)(s + ((int64_t)u * T + t) * VEC);
-        if constexpr (MODE == GEMM355_STREAM_COPY) {
+        if constexpr (MODE != GEMM355_STREAM_READ_XOR) {
             char *d = dst + c * chunk;
 #pragma unroll
-            for (int u = 0; u < U; ++u) *(V *)(d + ((int64_t)u * T + t) * VEC) = v[u];
+            for (int u = 0; u < U; ++u) {
+                V *p = (V *)(d + ((int64_t)u * T + t) * VEC);
+                if constexpr (MODE == GEMM355_STREAM_COPY_NT)
+                    __builtin_nontemporal_store(v[u], p);
+                else
+                    *p = v[u];
+            }
         } else {
 #pragma unroll
             for (int u = 0; u < U; ++u) x ^= VecT<VEC>::fold(v[u]);
@@ -68,7 +74,9 @@ __global__ __launch_bounds__(1024) void stream_kernel(const char *__restrict__ s
     for (int64_t w = nchunks * chunk / 4 + (int64_t)blockIdx.x * T + t; w < nw;
          w += (int64_t)gridDim.x * T) {
         const uint32_t v = ((const uint32_t *)src)[w];
-        if constexpr (MODE == GEMM355_STREAM_COPY)
+        if constexpr (MODE == GEMM355_STREAM_COPY_NT)
+            __builtin_nontemporal_store(v, (uint32_t *)dst + w);
+        else if constexpr (MODE == GEMM355_STREAM_COPY)
             ((uint32_t *)dst)[w] = v;
         else
             x ^= v;
@@ -144,14 +152,16 @@ extern "C" {
 gemm355_status gemm355_stream(int mode, const void *src, void *dst, int64_t n_bytes,
                               int vec_bytes, int unroll, int threads, int lds_bytes, int grid,
                               hipStream_t stream) {
-    if (mode != GEMM355_STREAM_COPY && mode != GEMM355_STREAM_READ_XOR) return GEMM355_ERR_INVALID_ARG;
+    if (mode != GEMM355_STREAM_COPY && mode != GEMM355_STREAM_READ_XOR &&
+        mode != GEMM355_STREAM_COPY_NT)
+        return GEMM355_ERR_INVALID_ARG;
     if (n_bytes < 0 || n_bytes % 4 != 0) return GEMM355_ERR_INVALID_ARG;
     if (vec_bytes != 4 && vec_bytes != 8 && vec_bytes != 16) return GEMM355_ERR_INVALID_ARG;
     if (unroll != 1 && unroll != 2 && unroll != 4 && unroll != 8) return GEMM355_ERR_INVALID_ARG;
     if (threads < 64 || threads > 1024 || threads % 64 != 0) return GEMM355_ERR_INVALID_ARG;
     if (lds_bytes < 0 || lds_bytes > kLdsMax) return GEMM355_ERR_INVALID_ARG;
     if (grid < 1 || grid > (1 << 20)) return GEMM355_ERR_INVALID_ARG;
-    const bool copy = mode == GEMM355_STREAM_COPY;
+    const bool copy = mode != GEMM355_STREAM_READ_XOR;
     if (n_bytes > 0 && src == nullptr) return GEMM355_ERR_INVALID_ARG;
     if (dst == nullptr && (!copy || n_bytes > 0)) return GEMM355_ERR_INVALID_ARG;
     if (n_bytes > 0 && (uintptr_t)src % vec_bytes != 0) return GEMM355_ERR_INVALID_ARG;
@@ -166,10 +176,14 @@ gemm355_status gemm355_stream(int mode, const void *src, void *dst, int64_t n_by
     // READ_XOR keeps one word per wave of the workgroup in the reserved LDS
     const int lds = copy ? lds_bytes : (lds_bytes > 64 ? lds_bytes : 64);
     const hipError_t e =
-        copy ? launch_stream_m<GEMM355_STREAM_COPY>(vec_bytes, unroll, src, dst, n_bytes, threads,
-                                                    lds, grid, stream)
-             : launch_stream_m<GEMM355_STREAM_READ_XOR>(vec_bytes, unroll, src, dst, n_bytes,
-                                                        threads, lds, grid, stream);
+        mode == GEMM355_STREAM_COPY
+            ? launch_stream_m<GEMM355_STREAM_COPY>(vec_bytes, unroll, src, dst, n_bytes, threads,
+                                                   lds, grid, stream)
+        : mode == GEMM355_STREAM_COPY_NT
+            ? launch_stream_m<GEMM355_STREAM_COPY_NT>(vec_bytes, unroll, src, dst, n_bytes,
+                                                      threads, lds, grid, stream)
+            : launch_stream_m<GEMM355_STREAM_READ_XOR>(vec_bytes, unroll, src, dst, n_bytes,
+                                                       threads, lds, grid, stream);
     return e == hipSuccess ? GEMM355_OK : GEMM355_ERR_LAUNCH;
 }
 

@@ -165,12 +165,13 @@ def test_stream_and_chase_argument_checks(lib):
         a = dict(ok, **kw)
         return gb.gemm355_stream(a["mode"], a["src"], a["dst"], a["n_bytes"], a["vec_bytes"],
                                  a["unroll"], a["threads"], a["lds_bytes"], a["grid"])
-    bad = [dict(mode=2), dict(n_bytes=-4), dict(n_bytes=6), dict(vec_bytes=12), dict(unroll=3),
+    bad = [dict(mode=3), dict(mode=-1), dict(n_bytes=-4), dict(n_bytes=6), dict(vec_bytes=12), dict(unroll=3),
            dict(threads=32), dict(threads=96), dict(threads=2048), dict(lds_bytes=-1),
            dict(lds_bytes=163841), dict(grid=0), dict(grid=(1 << 20) + 1), dict(src=0),
            dict(dst=0), dict(src=P + 4), dict(dst=P + 8 + (1 << 20)),
            dict(dst=P + 1024),                      # overlaps the source
-           dict(mode=gb.STREAM_READ_XOR, dst=0), dict(mode=gb.STREAM_READ_XOR, dst=P + 2)]
+           dict(mode=gb.STREAM_READ_XOR, dst=0), dict(mode=gb.STREAM_READ_XOR, dst=P + 2),
+           dict(mode=gb.STREAM_COPY_NT, dst=P + 1024), dict(mode=gb.STREAM_COPY_NT, src=0)]
     for b in bad:
         assert st(**b) == gb.ERR_INVALID_ARG, b
     # an empty copy needs no buffers; a READ_XOR always writes its grid entries

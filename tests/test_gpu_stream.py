@@ -49,9 +49,10 @@ CONFIGS = [  # vec, unroll, threads, lds_bytes, grid
 SIZES = [0, 4, 4 * 1000, 16 * 64 * 8 * 3 + 4 * 37, (1 << 22) + 4 * 5]
 
 
+@pytest.mark.parametrize("mode", [gb.STREAM_COPY, gb.STREAM_COPY_NT], ids=["copy", "copy_nt"])
 @pytest.mark.parametrize("cfg", CONFIGS, ids=lambda c: "v{}u{}t{}l{}g{}".format(*c))
 @pytest.mark.parametrize("n_bytes", SIZES)
-def test_copy_bit_exact(cfg, n_bytes):
+def test_copy_bit_exact(cfg, n_bytes, mode):
     import torch
     vec, unroll, threads, lds, grid = cfg
     n = n_bytes // 4
@@ -59,7 +60,7 @@ def test_copy_bit_exact(cfg, n_bytes):
     d_src = dev(src)
     buf = torch.full((n + 2 * GUARD,), SENTINEL, dtype=torch.int32, device="cuda")
     dst_ptr = buf.data_ptr() + 4 * GUARD
-    st = gb.gemm355_stream(gb.STREAM_COPY, d_src.data_ptr() if n else 0, dst_ptr, n_bytes, vec,
+    st = gb.gemm355_stream(mode, d_src.data_ptr() if n else 0, dst_ptr, n_bytes, vec,
                            unroll, threads, lds, grid, torch.cuda.current_stream().cuda_stream)
     assert st == gb.OK
     torch.cuda.synchronize()
