@@ -88,7 +88,7 @@ def time_gemm(kind, M, N, K, seed, steps, warmup):
     from roofline_optimisation_amd import binding as gb
     from roofline_optimisation_amd import inputs
 
-    dt = "f32" if kind == "f32" else "f16"
+    dt = kind
     A, B = inputs.make_operands(M, N, K, seed, "uniform", dt)
     if dt == "f32":
         dA, dB = torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda()
@@ -96,7 +96,7 @@ def time_gemm(kind, M, N, K, seed, steps, warmup):
     else:
         dA = torch.from_numpy(A.view("int16")).cuda()
         dB = torch.from_numpy(B.view("int16")).cuda()
-        entry = gb.gemm_f16f32acc
+        entry = gb.gemm_f16f32acc if dt == "f16" else gb.gemm_bf16f32acc
     dC = torch.empty((M, N), dtype=torch.float32, device="cuda")
     stream = torch.cuda.Stream()
     h = stream.cuda_stream
@@ -590,7 +590,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=300)
-    ap.add_argument("--only", choices=["f32", "f16"], default=None,
+    ap.add_argument("--only", choices=["f32", "f16", "bf16"], default=None,
                     help="measure one workload only (for profiler runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--report", default=None, metavar="PATH",
@@ -670,8 +670,10 @@ def main():
         return
 
     results = {}
-    for kind, n, seed in (("f32", 3072, 1), ("f16", 4096, 3)):
-        if args.only and args.only != kind:
+    # BF16 4096^3 (the FP16 workload's values rounded to bfloat16) only on request: the
+    # same kernel as FP16, for comparing clock and matrix-core use between the formats
+    for kind, n, seed in (("f32", 3072, 1), ("f16", 4096, 3), ("bf16", 4096, 3)):
+        if (args.only and args.only != kind) or (not args.only and kind == "bf16"):
             continue
         log(f"[bench] {kind} {n}^3: warmup {args.warmup}, steps {args.steps}")
         r = time_gemm(kind, n, n, n, seed, args.steps, args.warmup)
@@ -688,14 +690,14 @@ def main():
 
     def roof(kind, n):
         r = results[kind]
-        tr = measured_traffic(kind)
+        tr = measured_traffic(kind) if kind in PMC_FILES else None
         in_b = 4 if kind == "f32" else 2
         return {"bound": "mfma", "achieved": round(r["tflops"], 2), "peak": PEAKS[kind],
                 "unit": "TFLOP/s", "frac": round(r["tflops"] / PEAKS[kind], 4),
                 "traffic": tr, "algorithmic_flops": 2 * n ** 3,
                 "ideal_bytes": rl.ideal_bytes(n, n, n, in_b, 4), "kernel": r["desc"]}
 
-    main_kind = "f32" if "f32" in results else "f16"
+    main_kind = "f32" if "f32" in results else ("f16" if "f16" in results else "bf16")
     n = 3072 if main_kind == "f32" else 4096
     r = results[main_kind]
     line = {
@@ -709,7 +711,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32" if main_kind == "f32" else "f16->f32",
+        "dtype": {"f32": "f32", "f16": "f16->f32", "bf16": "bf16->f32"}[main_kind],
         "data": "synthetic",
         "config": {"workload": f"gemm_{main_kind}_{n}", "M": n, "N": n, "K": n,
                    "layout": "row-major, packed strides", "dist": "U[-1,1]",
