@@ -432,336 +432,7 @@ inline bool h16_vec(const GemmArgs &g) {
     return rows_aligned16(g.A, g.lda, 2) && rows_aligned16(g.B, g.ldb, 2);
 }
 
-// ---------------------------------------------------------------------------------
-// 256 x 256 interior tiles fed by direct global -> LDS loads.
-//
-// Data movement ("Kernel optimisation guide", Level 3 double buffering, extended to a
-// ring; the overlap of loads and arithmetic in the scheduling section of "Advanced
-// CUDA features - starting from GEMM"):
-//  * K is walked in steps of 32.  An m/n-contiguous operand goes through a ring of
-//    kNs = 4 stages (16 KiB each), its loads of k-step t+3 issued while step t is
-//    multiplied, into the stage step t-1 has released; a k-contiguous operand goes through
-//    two slots of a 64-wide double step (32 KiB each), loaded every other k-step, so that
-//    its loads read whole 128-byte lines (with 32-wide steps each line would be fetched
-//    twice, half of it each time);
-//  * a load is buffer_load_dwordx4 with the lds flag: lane l's 16 bytes land at
-//    m0 + 16 l, so one instruction fills 1 KiB of LDS (8 rows of a KM operand or 2 rows
-//    of an MN operand) and the lane -> source mapping chooses where each 16-byte chunk
-//    goes;
-//  * a KM operand's rows are 128 bytes, chunk c of row r stored in slot c ^ ((r / 2) %
-//    8); an MN operand's rows are 512 bytes, chunk c of row k in slot c ^ 4 (k % 4).
-//    With these the fragment reads (ds_read_b128 for KM, ds_read_b64_tr_b16 for MN, as
-//    in the staged kernel) touch 16 distinct 16-byte bank groups per 256 bytes, i.e.
-//    no bank conflicts, without padding (which a contiguous 1 KiB load cannot skip);
-//  * each wave waits for its own loads of step t+1 (vmcnt), then one barrier per
-//    k-step publishes them to all four waves.
-// The loads are issued from inline assembly (m0 holds the LDS destination), so the
-// compiler neither tracks them nor waits for them; the kernel's own s_waitcnt vmcnt
-// instructions do, and no other code of this kernel uses m0.
-namespace dma {
-
-constexpr int kBM = 256, kBN = 256, kBK = 32, kNs = 4;
-constexpr int kWM = 2, kWN = 2, kWaves = kWM * kWN;
-constexpr int kTM = kBM / kWM, kTN = kBN / kWN, kMB = kTM / 32, kNB = kTN / 32;
-constexpr int kStage = kBM * kBK * 2;        // bytes per operand per stage (both 256 x 32)
-constexpr int kBOff = kNs * kStage;          // the B ring follows the A ring
-constexpr int kLds = 2 * kNs * kStage;
-constexpr int kI = kStage / 1024 / kWaves;   // 1 KiB loads per wave per operand per k-step
-constexpr int kLd = 2 * kI;
-static_assert(kBM == kBN, "both operands share the ring geometry");
-static_assert(kLds <= 160 * 1024, "LDS budget");
-// every ds_read immediate (stage + block / row offsets) stays below 64 KiB
-static_assert(2 * kStage + (kMB - 1) * 4096 < 65536, "KM read offsets");
-static_assert(2 * (2 * kStage) == kNs * kStage, "both kinds of operand fill the same region");
-static_assert((kNs - 1) * kStage + 16 * 512 + 4 * 512 < 65536, "MN read offsets");
-
-typedef int int4v __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) char lds_char;
-
-// A raw buffer resource over `p` (2^31 - 1 bytes; the host checks every offset fits).
-__device__ __forceinline__ int4v rsrc_of(const void *p) {
-    const uint64_t a = (uint64_t)(uintptr_t)p;
-    int4v r;
-    r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
-    r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
-    r[2] = 0x7fffffff;
-    r[3] = 0x00020000;
-    return r;
-}
-
-// 16 bytes per lane from the buffer at voff + soff into LDS at lds_dst + 16 * lane.
-// m0 must be written right before the load; one wait state separates the two.
-__device__ __forceinline__ void load_lds16(uint32_t lds_dst, uint32_t voff, int4v rsrc,
-                                           uint32_t soff) {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                 :: "s"(lds_dst), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
-}
-
-__device__ __forceinline__ lds_char *lds_reg(lds_char *p) {
-    uint32_t a = (uint32_t)(uintptr_t)p;
-    asm volatile("" : "+v"(a));
-    return (lds_char *)(uintptr_t)a;
-}
-
-// Loads and fragment reads of one operand of extent 256 in its 64 KiB region at byte
-// offset `roff`.
-//  * MN (m/n-contiguous): a ring of kNs stages of one 32-wide k-step (16 KiB, rows of
-//    512 bytes).  Wave w fills rows [2 kI w, +2 kI), instruction i rows 2 i + l/32, lane
-//    slot l%32 taking chunk slot ^ 4 (row % 4), where row % 4 = l/32 + 2 (i % 2).
-//  * KM (k-contiguous): two slots of one 64-wide double step (32 KiB, 256 rows of 128
-//    bytes), so that every load reads whole 128-byte lines; k-step t uses half t % 2 of
-//    slot (t / 2) % 2.  Wave w fills rows [64 w, +64), instruction i rows 8 i + l/8,
-//    lane slot l%8 taking chunk slot ^ ((row / 2) % 8), where (row / 2) % 8 =
-//    4 (i % 2) + l/16.
-template <bool MN, int NBLK>
-struct DmaOp {
-    static constexpr int kIssue = MN ? kI : 2 * kI;  // load instructions per wave per issue
-    static constexpr int kSlot = 2 * kStage;         // KM slot bytes
-    int4v rsrc;
-    uint32_t voff[2];
-    lds_char *rd[MN ? NBLK : 4];
-    H16Frag<MN, NBLK> fr;
-
-    // X: the operand; mn0: the tile's first row (KM) or column (MN); wb: the wave's first
-    // row or column within the tile.
-    __device__ __forceinline__ void init(const uint16_t *X, int ld, int mn0, int wave, int lane,
-                                         lds_char *L, int roff, int wb) {
-        if constexpr (MN) {
-            rsrc = rsrc_of(X + mn0);
-            const int row = 2 * kI * wave + lane / 32, slot = lane & 31;
-            voff[0] = (uint32_t)((row * ld + 8 * (slot ^ (4 * (lane >> 5)))) * 2);
-            voff[1] = (uint32_t)((row * ld + 8 * (slot ^ (4 * ((lane >> 5) + 2)))) * 2);
-            // lane (g = l/16, e = (l%16)/4, q = l%4) reads row 16 s + 8 (g/2) + 4 h + e,
-            // chunk wb/8 + 4 b + 2 (g%2) + q/2, byte 8 (q%2) of it; its slot is chunk ^ 4 e
-            const int g = lane >> 4, e = (lane & 15) >> 2, q = lane & 3;
-#pragma unroll
-            for (int b = 0; b < NBLK; ++b)
-                rd[b] = lds_reg(L + roff + (8 * (g >> 1) + e) * 512 +
-                                16 * ((wb / 8 + 4 * b + 2 * (g & 1) + (q >> 1)) ^ (4 * e)) +
-                                8 * (q & 1));
-        } else {
-            rsrc = rsrc_of(X + (size_t)mn0 * ld);
-            const int row = 64 * wave + lane / 8, slot = lane & 7;
-            voff[0] = (uint32_t)((row * ld + 8 * (slot ^ ((0 + lane / 16) & 7))) * 2);
-            voff[1] = (uint32_t)((row * ld + 8 * (slot ^ ((4 + lane / 16) & 7))) * 2);
-            // half h, sub-step s: row wb + 32 b + l%32, chunk 4 h + 2 s + l/32, whose
-            // swizzle key ((l%32) / 2) % 8 does not depend on b
-            const int l32 = lane & 31, lhi = lane >> 5;
-            const int off = (wb + l32) * 128;
-#pragma unroll
-            for (int hs = 0; hs < 4; ++hs)
-                rd[hs] = lds_reg(L + roff + off + 16 * ((2 * hs + lhi) ^ ((l32 >> 1) & 7)));
-        }
-    }
-    // Load instruction i of one issue: MN: k-step at k0 into stage `place`; KM: the
-    // double step at k0 into slot `place`.
-    __device__ __forceinline__ void issue(uint32_t lds0, int roff, int wave, int ld, int place,
-                                          int k0, int i) {
-        if constexpr (MN) {
-            const uint32_t dst = lds0 + roff + place * kStage + (wave * kI + i) * 1024;
-            load_lds16(dst, voff[i & 1], rsrc, (uint32_t)((k0 + 2 * i) * ld * 2));
-        } else {
-            const uint32_t dst = lds0 + roff + place * kSlot + (wave * 8 + i) * 1024;
-            load_lds16(dst, voff[i & 1], rsrc, (uint32_t)((8 * i * ld + k0) * 2));
-        }
-    }
-    // Piece p of sub-step s of k-step u (u = t % kNs, so the MN stage is u, the KM slot
-    // u / 2 and the KM half u % 2) into fragment slot `fslot`.
-    __device__ __forceinline__ void read(int u, int s, int fslot, int p) {
-        if constexpr (MN) {
-            const int b = p / 2, h = p % 2;
-            fr.f[fslot][b][h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_shortx4 *)(rd[b] + u * kStage + 16 * s * 512 + 4 * h * 512));
-        } else {
-            fr.f[fslot][p] = *(const lds_u16x8 *)(rd[2 * (u % 2) + s] + (u / 2) * kSlot + p * 4096);
-        }
-    }
-};
-
-template <typename T, bool A_MN, bool B_MN, int EPI>
-__device__ __forceinline__ void dma_tile(int K, const uint16_t *__restrict__ A, int lda,
-                                         const uint16_t *__restrict__ B, int ldb,
-                                         float *__restrict__ C, int ldc, float sign,
-                                         int use_old, int m0, int n0, char *lds_raw) {
-    const int lane = threadIdx.x % 64;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
-    const int wm = wave / kWN, wn = wave % kWN;
-    const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_char *)lds_raw;
-    lds_char *const L = (lds_char *)lds_raw;
-    const int l32 = lane & 31, lhi = lane >> 5;
-
-    using OA = DmaOp<A_MN, kMB>;
-    using OB = DmaOp<B_MN, kNB>;
-    OA oa;
-    OB ob;
-    oa.init(A, lda, m0, wave, lane, L, 0, wm * kTM);
-    ob.init(B, ldb, n0, wave, lane, L, kBOff, wn * kTN);
-    // Loads per wave: nMN every k-step (the MN operands' next stage), nKM every other
-    // k-step (the KM operands' next double step), MN loads first.
-    constexpr int nMN = (A_MN ? kI : 0) + (B_MN ? kI : 0);
-    constexpr int nKM = (A_MN ? 0 : 2 * kI) + (B_MN ? 0 : 2 * kI);
-    // issue w of an MN batch (k-step at k0 into stage st) / of a KM batch (double step at
-    // k0 into slot sl)
-    auto issue_mn = [&](int st, int k0, int w) {
-        if constexpr (A_MN) {
-            if (w < kI) { oa.issue(lds0, 0, wave, lda, st, k0, w); return; }
-            w -= kI;
-        }
-        if constexpr (B_MN) ob.issue(lds0, kBOff, wave, ldb, st, k0, w);
-    };
-    auto issue_km = [&](int sl, int k0, int w) {
-        if constexpr (!A_MN) {
-            if (w < 2 * kI) { oa.issue(lds0, 0, wave, lda, sl, k0, w); return; }
-            w -= 2 * kI;
-        }
-        if constexpr (!B_MN) ob.issue(lds0, kBOff, wave, ldb, sl, k0, w);
-    };
-    constexpr int kRA = kMB * (A_MN ? 2 : 1);
-    constexpr int kR = kRA + kNB * (B_MN ? 2 : 1);
-    auto read_piece = [&](int u, int s, int fslot, int p) {
-        if (p < kRA) oa.read(u, s, fslot, p);
-        else ob.read(u, s, fslot, p - kRA);
-    };
-
-    floatx16 acc[kMB][kNB];
-#pragma unroll
-    for (int i = 0; i < kMB; ++i)
-#pragma unroll
-        for (int j = 0; j < kNB; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-    auto mfma_one = [&](int slot, int qq) {
-        const int i = qq / kNB, j = qq % kNB;
-        acc[i][j] = mfma32x32x16<T>(oa.fr.get(slot, i), ob.fr.get(slot, j), acc[i][j]);
-    };
-
-    // One k-step t = kt + u (u = t % 4 is a compile-time constant): 2 sub-steps of kMf
-    // MFMAs.  Sub-step 0 reads the fragments of sub-step 1 two per MFMA; the step's loads
-    // (MN: k-step t+3 into stage (u+3) % 4; on even steps KM: double step t/2 + 1 into
-    // slot (u/2 + 1) % 2) are spread over sub-step 0; after kPre MFMAs of sub-step 1 the
-    // wave waits until the loads step t+1 needs are done, then the barrier publishes them
-    // and the first fragments of t+1 are read under the last MFMAs.  The wait counts: on
-    // an even step the 2 nMN + nKM youngest loads may stay in flight (the MN loads of
-    // steps t+2 and t+3 and this step's KM loads; the KM loads of two steps ago are older
-    // but already complete), on an odd step nMN (this step's MN loads) when there are KM
-    // operands, else 2 nMN.  No branches: near the end the loads repeat the last k-step or
-    // double step into free stages or slots.
-    constexpr int kMf = kMB * kNB, kSlots = 2 * kMf;
-    static_assert(kR <= 2 * kMf, "a sub-step's fragment reads go two per MFMA of the one before");
-    constexpr int kPre = (kMf * 3 + 7) / 8;
-    constexpr int kBarrier = kMf + kPre;
-    constexpr int kLoadHi = kMf;
-    static_assert(kLoadHi <= kBarrier, "the step's loads precede its wait");
-    auto ev_begin = [](int qs, int n, int lo, int hi) {
-        if (qs <= lo) return 0;
-        if (qs >= hi) return n;
-        return ((qs - lo) * n + (hi - lo) - 1) / (hi - lo);
-    };
-    const int nk = K / kBK;
-    auto kstep = [&](int kt, auto u_c) {
-        constexpr int u = decltype(u_c)::value;
-        constexpr int u1 = (u + 1) % kNs;
-        constexpr bool even = u % 2 == 0;
-        constexpr int nLd = nMN + (even ? nKM : 0);
-        constexpr int kWait = even ? 2 * nMN + nKM : (nKM ? nMN : 2 * nMN);
-        const int t = kt + u;
-        const int k_mn = min(t + kNs - 1, nk - 1) * kBK;
-        const int k_km = min(t / 2 + 1, nk / 2 - 1) * 2 * kBK;
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-#pragma unroll
-            for (int qq = 0; qq < kMf; ++qq) {
-                const int qs = s * kMf + qq;
-                if (qs >= kBarrier) {
-                    const int lo = ev_begin(qs, kR, kBarrier, kSlots);
-                    const int hi = ev_begin(qs + 1, kR, kBarrier, kSlots);
-#pragma unroll
-                    for (int o = lo; o < hi; ++o) read_piece(u1, 0, 0, o);
-                }
-                mfma_one(s, qq);
-                if (s == 0) {
-#pragma unroll
-                    for (int p = 2 * qq; p < 2 * qq + 2; ++p)
-                        if (p < kR) read_piece(u, 1, 1, p);
-                }
-                {
-                    const int lo = ev_begin(qs, nLd, 0, kLoadHi);
-                    const int hi = ev_begin(qs + 1, nLd, 0, kLoadHi);
-#pragma unroll
-                    for (int w = lo; w < hi; ++w) {
-                        if (w < nMN) issue_mn((u + kNs - 1) % kNs, k_mn, w);
-                        else issue_km((u / 2 + 1) % 2, k_km, w - nMN);
-                    }
-                }
-                if (qs == kBarrier - 1) {
-                    wait_vmcnt<kWait>();
-                    __syncthreads();
-                }
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        }
-    };
-
-    // KM double step 0 into slot 0, MN k-steps 0 .. kNs-2 into stages 0 .. kNs-2; wait for
-    // step 0's data (the MN loads of steps 1 and 2 may stay in flight), read its first
-    // fragments
-#pragma unroll
-    for (int w = 0; w < nKM; ++w) issue_km(0, 0, w);
-#pragma unroll
-    for (int p = 0; p < kNs - 1; ++p)
-#pragma unroll
-        for (int w = 0; w < nMN; ++w) issue_mn(p, min(p, nk - 1) * kBK, w);
-    wait_vmcnt<2 * nMN>();
-    __syncthreads();
-#pragma unroll
-    for (int p = 0; p < kR; ++p) read_piece(0, 0, 0, p);
-    using U0 = std::integral_constant<int, 0>;
-    using U1 = std::integral_constant<int, 1>;
-    using U2 = std::integral_constant<int, 2>;
-    using U3 = std::integral_constant<int, 3>;
-    for (int kt = 0; kt < nk; kt += kNs) {
-        kstep(kt, U0{});
-        kstep(kt, U1{});
-        kstep(kt, U2{});
-        kstep(kt, U3{});
-    }
-    // nothing may still write this workgroup's LDS when it exits
-    wait_vmcnt<0>();
-
-#pragma unroll
-    for (int i = 0; i < kMB; ++i)
-#pragma unroll
-        for (int j = 0; j < kNB; ++j)
-        {
-            const int row0 = m0 + wm * kTM + 32 * i + 4 * lhi, col = n0 + wn * kTN + 32 * j + l32;
-            if constexpr (EPI == 2) {
-                static_assert(kNB % 2 == 0, "16-bit C stores block pairs");
-                if (j % 2 == 0)
-                    store_pair32_c16<false, T, true>(acc[i][j], acc[i][j + 1], (uint16_t *)C, ldc, row0,
-                                                     col - l32, 0, 0, sign, use_old);
-            } else if constexpr (EPI == 1) store_block32_acc<false, true, true>(acc[i][j], C, ldc, row0, col, 0, 0, sign, use_old);
-            else store_block32<false, true>(acc[i][j], C, ldc, row0, col, 0, 0);
-        }
-}
-
-}  // namespace dma
-
-template <typename T, bool A_MN, bool B_MN, int EPI>
-__global__ __launch_bounds__(64 * dma::kWaves) __attribute__((amdgpu_waves_per_eu(1)))
-void mfma_f16_dma_kernel(int M, int N, int K, const uint16_t *__restrict__ A, int lda,
-                         const uint16_t *__restrict__ B, int ldb, float *__restrict__ C,
-                         int ldc, float sign, int use_old) {
-    __shared__ __attribute__((aligned(1024))) char lds[dma::kLds];
-    int tm, tn;
-    grouped_tile(xcd_contiguous_id(blockIdx.x, gridDim.x), M / dma::kBM, N / dma::kBN, 4, tm, tn);
-    dma::dma_tile<T, A_MN, B_MN, EPI>(K, A, lda, B, ldb, C, ldc, sign, use_old, tm * dma::kBM,
-                                      tn * dma::kBN, lds);
-}
+#include "h16_dma.hpp"
 
 // Byte offsets below 2^31 for every chunk of a 256-extent tile of the operand.
 inline bool op_fits(bool mn, int ext, int K, int ld) {
