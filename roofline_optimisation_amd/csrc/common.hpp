@@ -233,7 +233,8 @@ __device__ __forceinline__ void store_pair32_c16(const floatx16 &acc0, const flo
 // One 16 x 16 accumulator quad of an interior tile with a sign and optional
 // accumulation: register r of this lane holds row row0 + r (row0 already includes the
 // lane's 4 (l/16)), column col; c = sign * acc (+ c when use_old).  Each register is read
-// from the AGPR file at its point of use (see store_block32_acc).
+// from the AGPR file at its point of use (see store_block32_acc).  Ordinary stores: a
+// store writes 64-byte pieces of lines, which the L2 merges.
 __device__ __forceinline__ void store_quad16_acc(const floatx4 &acc, float *__restrict__ C, int ldc,
                                                  int row0, int col, float sign, bool use_old) {
     __builtin_amdgcn_sched_barrier(0);
@@ -245,7 +246,7 @@ __device__ __forceinline__ void store_quad16_acc(const floatx4 &acc, float *__re
     for (int r = 0; r < 4; ++r) {
         float a;
         asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(a) : "a"(acc[r]));
-        __builtin_nontemporal_store(sign * a + old[r], C + (size_t)(row0 + r) * ldc + col);
+        C[(size_t)(row0 + r) * ldc + col] = sign * a + old[r];
     }
     __builtin_amdgcn_sched_barrier(0);
 }
@@ -275,7 +276,7 @@ __device__ __forceinline__ void store_pair16_c16(const floatx4 &acc0, const floa
             for (int r = 0; r < 4; ++r) {
                 uint16_t *c = C + (size_t)(row0 + r) * ldc + col0 + 16 * q + (lane & 15);
                 const float old = use_old ? to_float(T{*c}) : 0.f;
-                __builtin_nontemporal_store(to_bits(sign * rd(q ? acc1 : acc0, r) + old, T{}), c);
+                *c = to_bits(sign * rd(q ? acc1 : acc0, r) + old, T{});
             }
         __builtin_amdgcn_sched_barrier(0);
         return;
@@ -297,7 +298,7 @@ __device__ __forceinline__ void store_pair16_c16(const floatx4 &acc0, const floa
         const float ohi = use_old ? to_float(T{(uint16_t)(oldw[r] >> 16)}) : 0.f;
         const uint32_t w = (uint32_t)to_bits(sign * lo + olo, T{}) |
                            ((uint32_t)to_bits(sign * hi + ohi, T{}) << 16);
-        __builtin_nontemporal_store(w, (uint32_t *)(C + (size_t)(row0 + r) * ldc + cw));
+        *(uint32_t *)(C + (size_t)(row0 + r) * ldc + cw) = w;
     }
     __builtin_amdgcn_sched_barrier(0);
 }
