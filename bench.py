@@ -41,7 +41,7 @@ PEAKS = {"f32": 157.3, "f16": 2516.6, "bf16": 2516.6}  # TFLOP/s, dense, 2.4 GHz
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "roofline_optimisation_amd", "csrc")
 KERNEL_SOURCES = {"f32": ["k_mfma_f32.hip", "f32_gemm.hpp", "common.hpp"],
-                  "f16": ["k_mfma_f16.hip", "h16_gemm.hpp", "common.hpp"],
+                  "f16": ["k_mfma_f16.hip", "h16_gemm.hpp", "h16_dma.hpp", "common.hpp"],
                   "softmax": ["k_softmax.hip", "wave_reduce.hpp"]}
 PMC_FILES = {"f32": "pmc_mfma_f32_n3072.txt", "f16": "pmc_mfma_f16_n4096.txt",
              "softmax": "pmc_softmax_16384x4096.txt"}
