@@ -1,21 +1,22 @@
-// 256 x 256 interior tiles of the FP16 / BF16 GEMM fed by direct global -> LDS loads and
-// multiplied with v_mfma_f32_16x16x32_{f16,bf16}.  Included by h16_gemm.hpp.
+// 256 x 256 and 128 x 128 interior tiles of the FP16 / BF16 GEMM fed by direct global
+// -> LDS loads and multiplied with v_mfma_f32_16x16x32_{f16,bf16}.  Included by
+// h16_gemm.hpp.
 //
 // Data movement ("Kernel optimisation guide", Level 3 double buffering, extended to a
 // ring; the overlap of loads and arithmetic in the scheduling section of "Advanced
 // CUDA features - starting from GEMM"):
-//  * K is walked in steps of 32.  An m/n-contiguous operand goes through a ring of
-//    kNs = 4 stages (16 KiB each), its loads of k-step t+3 issued while step t is
-//    multiplied, into the stage step t-1 has released; a k-contiguous operand goes through
-//    two slots of a 64-wide double step (32 KiB each), loaded every other k-step, so that
-//    its loads read whole 128-byte lines (with 32-wide steps each line would be fetched
-//    twice, half of it each time);
+//  * K is walked in steps of 32.  An m/n-contiguous operand goes through a ring of kNs
+//    stages (4 of 16 KiB for 256-wide tiles, 8 of 8 KiB for 128-wide ones), its loads of
+//    k-step t + kNs - 1 issued while step t is multiplied, into the stage step t-1 has
+//    released; a k-contiguous operand goes through kNs/2 slots of a 64-wide double step,
+//    loaded every other k-step, so that its loads read whole 128-byte lines (with
+//    32-wide steps each line would be fetched twice, half of it each time);
 //  * a load is buffer_load_dwordx4 with the lds flag: lane l's 16 bytes land at
-//    m0 + 16 l, so one instruction fills 1 KiB of LDS (8 rows of a KM operand or 2 rows
-//    of an MN operand) and the lane -> source mapping chooses where each 16-byte chunk
-//    goes;
+//    m0 + 16 l, so one instruction fills 1 KiB of LDS (8 rows of a KM operand, 2 or 4
+//    rows of an MN operand) and the lane -> source mapping chooses where each 16-byte
+//    chunk goes;
 //  * a KM operand's rows are 128 bytes, chunk c of row r stored in slot c ^ ((r / 2) %
-//    8); an MN operand's rows are 512 bytes, chunk c of row k in slot
+//    8); an MN operand's rows are 2 E bytes (E = 256 or 128), chunk c of row k in slot
 //    c ^ 4 (k % 4) ^ 2 ((k / 8) % 2).  With these the fragment reads (ds_read_b128 for
 //    KM, ds_read_b64_tr_b16 for MN) touch distinct banks within every 16 lanes of a
 //    b128 read and every 32 lanes of a b64 read, i.e. no bank conflicts, without padding
@@ -23,7 +24,7 @@
 //  * each wave waits for its own loads of step t+1 (vmcnt), then one barrier per
 //    k-step publishes them to all four waves.
 //
-// Arithmetic: each wave owns 128 x 128 of C as 8 x 8 blocks of 16 x 16 (64 FP32
+// Arithmetic: each wave owns E/2 x E/2 of C as blocks of 16 x 16 (E = 256: 8 x 8 FP32
 // accumulator quads, 256 accumulator registers) and multiplies a whole 32-wide k-step
 // per instruction.  The 16x16x32 form was chosen over 32x32x16 (same arithmetic per
 // k-step, same fragment bytes) because the part sustains a higher clock on it under the
@@ -38,20 +39,38 @@
 
 namespace dma {
 
-constexpr int kBM = 256, kBN = 256, kBK = 32, kNs = 4;
+constexpr int kBK = 32;
 constexpr int kWM = 2, kWN = 2, kWaves = kWM * kWN;
-constexpr int kTM = kBM / kWM, kTN = kBN / kWN, kMB = kTM / 16, kNB = kTN / 16;
-constexpr int kStage = kBM * kBK * 2;        // bytes per operand per stage (both 256 x 32)
-constexpr int kBOff = kNs * kStage;          // the B ring follows the A ring
-constexpr int kLds = 2 * kNs * kStage;
-constexpr int kI = kStage / 1024 / kWaves;   // 1 KiB loads per wave per operand per k-step
-static_assert(kBM == kBN, "both operands share the ring geometry");
-static_assert(kLds <= 160 * 1024, "LDS budget");
-static_assert(kI == 4, "an MN operand's wave fills 8 rows, all of one (k / 8) parity");
-// every ds_read immediate (slot / stage + block / row offsets) stays below 64 KiB
-static_assert(2 * kStage + (kMB - 1) * 2048 < 65536, "KM read offsets");
-static_assert(2 * (2 * kStage) == kNs * kStage, "both kinds of operand fill the same region");
-static_assert((kNs - 1) * kStage + 4 * 512 < 65536, "MN read offsets");
+
+// Geometry of an E x E tile (E = 256 or 128; both operands have extent E).  A 128-wide
+// tile's k-step is a quarter of a 256-wide one's arithmetic (16 MFMAs, ~130 ns), so its
+// ring has kNs = 8 stages instead of 4 to keep the loads as far ahead in time.
+template <int E>
+struct Geo {
+    static constexpr int kNs = E == 256 ? 4 : 8;  // ring stages (k-steps)
+    static constexpr int kTM = E / kWM, kTN = E / kWN;     // wave tile
+    static constexpr int kMB = kTM / 16, kNB = kTN / 16;    // accumulator quads per wave
+    static constexpr int kStage = E * kBK * 2;   // bytes per operand per stage (E x 32)
+    static constexpr int kBOff = kNs * kStage;   // the B ring follows the A ring
+    static constexpr int kLds = 2 * kNs * kStage;
+    static constexpr int kI = kStage / 1024 / kWaves;  // MN: 1 KiB loads per wave per k-step
+    static constexpr int kRowB = 2 * E;          // MN: bytes per LDS row (one k)
+    static constexpr int kRpi = 1024 / kRowB;    // MN: rows one load instruction fills
+    static constexpr int kKMRows = E / kWaves;   // KM: rows one wave fills
+    // MFMAs per k-step, the step's wait and barrier after kBarrier of them, its loads
+    // spread over the first kLoadHi
+    static constexpr int kMf = kMB * kNB;
+    static constexpr int kBarrier = E == 256 ? 40 : 10;
+    static constexpr int kLoadHi = E == 256 ? 32 : 8;
+    static_assert(E == 256 || E == 128, "tile extents");
+    static_assert(kLds <= 160 * 1024, "LDS budget");
+    static_assert(kI * kRpi == 8, "an MN operand's wave fills 8 rows, all of one (k / 8) parity");
+    static_assert(kKMRows / 8 == 2 * kI, "a KM double step takes twice an MN step's loads");
+    // every ds_read immediate (slot / stage + block / row offsets) stays below 64 KiB
+    static_assert((kNs / 2 - 1) * 2 * kStage + (kMB - 1) * 2048 < 65536, "KM read offsets");
+    static_assert((kNs - 1) * kStage + 4 * kRowB < 65536, "MN read offsets");
+    static_assert(kLoadHi <= kBarrier && kBarrier < kMf, "the step's loads precede its wait");
+};
 
 typedef int int4v __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) char lds_char;
@@ -103,48 +122,53 @@ __device__ __forceinline__ lds_char *lds_reg(lds_char *p) {
     return (lds_char *)(uintptr_t)a;
 }
 
-// Loads and fragment reads of one operand of extent 256 in its 64 KiB region at byte
-// offset `roff`.
-//  * MN (m/n-contiguous): a ring of kNs stages of one 32-wide k-step (16 KiB, rows of
-//    512 bytes).  Wave w fills rows [8 w, +8), instruction i rows 8 w + 2 i + l/32, lane
-//    slot l%32 taking chunk slot ^ 4 (row % 4) ^ 2 ((row / 8) % 2), where row % 4 =
-//    l/32 + 2 (i % 2) and (row / 8) % 2 = w % 2.
-//  * KM (k-contiguous): two slots of one 64-wide double step (32 KiB, 256 rows of 128
-//    bytes), so that every load reads whole 128-byte lines; k-step t uses half t % 2 of
-//    slot (t / 2) % 2.  Wave w fills rows [64 w, +64), instruction i rows 8 i + l/8,
-//    lane slot l%8 taking chunk slot ^ ((row / 2) % 8), where (row / 2) % 8 =
+// Loads and fragment reads of one operand of extent E in its region at byte offset
+// `roff` (4 E x 32 x 2 bytes: 64 KiB for E = 256).
+//  * MN (m/n-contiguous): a ring of kNs stages of one 32-wide k-step (E x 32 halves,
+//    rows of 2 E bytes).  Wave w fills rows [8 w, +8): instruction i rows
+//    8 w + R i + l / (64 / R) with R = 1024 / (2 E) rows per instruction, lane slot
+//    l % (64 / R) taking chunk slot ^ 4 (row % 4) ^ 2 ((row / 8) % 2), where
+//    (row / 8) % 2 = w % 2 and row % 4 = l/32 + 2 (i % 2) (E = 256) or l/16 (E = 128).
+//  * KM (k-contiguous): kNs / 2 slots of one 64-wide double step (E rows of 128 bytes),
+//    so that every load reads whole 128-byte lines; k-step t uses half t % 2 of slot
+//    (t / 2) % (kNs / 2).  Wave w fills rows [E/4 w, +E/4), instruction i rows 8 i + l/8, lane
+//    slot l%8 taking chunk slot ^ ((row / 2) % 8), where (row / 2) % 8 =
 //    4 (i % 2) + l/16.
-template <bool MN>
+template <bool MN, int E>
 struct DmaOp {
-    static constexpr int kSlot = 2 * kStage;         // KM slot bytes
+    using G = Geo<E>;
+    static constexpr int NB = E / 32;                // quads along this operand per wave
+    static constexpr int kSlot = 2 * G::kStage;      // KM slot bytes
     static constexpr int kPieces = MN ? 2 : 1;       // LDS reads per fragment
     int4v rsrc;
     uint32_t voff[2];
-    lds_char *rd[MN ? 8 : 2];
-    H16Frag<MN, 8> fr;
+    lds_char *rd[MN ? NB : 2];
+    H16Frag<MN, NB> fr;
 
     // X: the operand; mn0: the tile's first row (KM) or column (MN); wb: the wave's first
     // row or column within the tile.
     __device__ __forceinline__ void init(const uint16_t *X, int ld, int mn0, int wave, int lane,
                                          lds_char *L, int roff, int wb) {
         if constexpr (MN) {
+            constexpr int lpr = 64 / G::kRpi;        // lanes per row of one load
             rsrc = rsrc_of(X + mn0);
-            const int row = 2 * kI * wave + lane / 32, slot = lane & 31;
+            const int rl = lane / lpr, row = 8 * wave + rl, slot = lane % lpr;
             const int kx = 2 * (wave & 1);
-            voff[0] = (uint32_t)((row * ld + 8 * (slot ^ (4 * (lane >> 5)) ^ kx)) * 2);
-            voff[1] = (uint32_t)((row * ld + 8 * (slot ^ (4 * ((lane >> 5) + 2)) ^ kx)) * 2);
+#pragma unroll
+            for (int p = 0; p < 2; ++p)
+                voff[p] = (uint32_t)((row * ld + 8 * (slot ^ (4 * ((G::kRpi * p + rl) % 4)) ^ kx)) * 2);
             // block b, piece h: lane (g = l/16, e = (l%16)/4, q = l%4) reads row 8 g + 4 h +
             // e, chunk wb/8 + 2 b + q/2, byte 8 (q%2) of it; that row's swizzle key is
             // 4 e ^ 2 (g%2)
             const int g = lane >> 4, e = (lane & 15) >> 2, q = lane & 3;
 #pragma unroll
-            for (int b = 0; b < 8; ++b)
-                rd[b] = lds_reg(L + roff + (8 * g + e) * 512 +
-                                16 * (wb / 8 + ((2 * b + (q >> 1)) ^ (4 * e) ^ (2 * (g & 1)))) +
+            for (int b = 0; b < NB; ++b)
+                rd[b] = lds_reg(L + roff + (8 * g + e) * G::kRowB +
+                                16 * ((wb / 8 + 2 * b + (q >> 1)) ^ (4 * e) ^ (2 * (g & 1))) +
                                 8 * (q & 1));
         } else {
             rsrc = rsrc_of(X + (size_t)mn0 * ld);
-            const int row = 64 * wave + lane / 8, slot = lane & 7;
+            const int row = G::kKMRows * wave + lane / 8, slot = lane & 7;
             voff[0] = (uint32_t)((row * ld + 8 * (slot ^ ((0 + lane / 16) & 7))) * 2);
             voff[1] = (uint32_t)((row * ld + 8 * (slot ^ ((4 + lane / 16) & 7))) * 2);
             // block b, half h of the slot: row wb + 16 b + l%16, chunk 4 h + l/16, whose
@@ -160,10 +184,10 @@ struct DmaOp {
     __device__ __forceinline__ void issue(uint32_t lds0, int roff, int wave, int ld, int place,
                                           int k0, int i) {
         if constexpr (MN) {
-            const uint32_t dst = lds0 + roff + place * kStage + (wave * kI + i) * 1024;
-            load_lds16(dst, voff[i & 1], rsrc, (uint32_t)((k0 + 2 * i) * ld * 2));
+            const uint32_t dst = lds0 + roff + place * G::kStage + (wave * G::kI + i) * 1024;
+            load_lds16(dst, voff[i & 1], rsrc, (uint32_t)((k0 + G::kRpi * i) * ld * 2));
         } else {
-            const uint32_t dst = lds0 + roff + place * kSlot + (wave * 8 + i) * 1024;
+            const uint32_t dst = lds0 + roff + place * kSlot + (wave * 2 * G::kI + i) * 1024;
             load_lds16(dst, voff[i & 1], rsrc, (uint32_t)((8 * i * ld + k0) * 2));
         }
     }
@@ -172,7 +196,7 @@ struct DmaOp {
     __device__ __forceinline__ void read(int u, int fslot, int b, int h) {
         if constexpr (MN) {
             fr.f[fslot][b][h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_shortx4 *)(rd[b] + u * kStage + 4 * h * 512));
+                (lds_shortx4 *)(rd[b] + u * G::kStage + 4 * h * G::kRowB));
         } else {
             fr.f[fslot][b] = *(const lds_u16x8 *)(rd[u % 2] + (u / 2) * kSlot + b * 2048);
         }
@@ -182,8 +206,9 @@ struct DmaOp {
 // The order in which a k-step's fragment pieces are read: A block 0, then the B blocks,
 // then the other A blocks, i.e. in the order the MFMAs (A block outer, B block inner,
 // odd rows walking the B blocks backwards) first use them.
-template <bool A_MN, bool B_MN>
+template <bool A_MN, bool B_MN, int E>
 struct PieceOrder {
+    static constexpr int kMB = Geo<E>::kMB, kNB = Geo<E>::kNB;
     static constexpr int kPA = A_MN ? 2 : 1, kPB = B_MN ? 2 : 1;
     static constexpr int kR = kMB * kPA + kNB * kPB;
     // piece p -> (operand 0 = A / 1 = B, block, half)
@@ -196,10 +221,17 @@ struct PieceOrder {
     }
 };
 
+// kstep(kt, integral_constant<u>) for u = 0 .. kNs-1 in order.
+template <typename F, int... U>
+__device__ __forceinline__ void for_steps(F &kstep, int kt, std::integer_sequence<int, U...>) {
+    (kstep(kt, std::integral_constant<int, U>{}), ...);
+}
+
 // Empty volatile statements that take every accumulator quad in and out of an AGPR:
 // code that defines the accumulators stays before them and code that reads them after,
 // so they order the accumulators' writes and reads with respect to the explicit wait
 // states around the inline-assembly MFMAs.
+template <int kMB, int kNB>
 __device__ __forceinline__ void pin_acc(floatx4 (&acc)[kMB][kNB]) {
 #pragma unroll
     for (int i = 0; i < kMB; ++i)
@@ -213,7 +245,7 @@ __device__ __forceinline__ void pin_acc(floatx4 (&acc)[kMB][kNB]) {
 // consecutive stores.  The stores are ordinary (cached) ones: each instruction writes
 // half lines, which the L2 merges; as non-temporal stores the same pattern took 40 %
 // longer (64 MiB from 256 workgroups: 15.8 against 11.2 us).
-template <int EPI, typename T>
+template <int EPI, typename T, int kMB, int kNB>
 __device__ __forceinline__ void store_tile(floatx4 (&acc)[kMB][kNB], float *__restrict__ C, int ldc,
                                            int row0, int col0, float sign, int flags) {
     const int lane = threadIdx.x & 63;
@@ -244,7 +276,7 @@ __device__ __forceinline__ void store_tile(floatx4 (&acc)[kMB][kNB], float *__re
     }
 }
 
-template <typename T, bool A_MN, bool B_MN, int EPI>
+template <typename T, bool A_MN, bool B_MN, int EPI, int E>
 __device__ __forceinline__ void dma_tile(int K, const uint16_t *__restrict__ A, int lda,
                                          const uint16_t *__restrict__ B, int ldb,
                                          float *__restrict__ C, int ldc, float sign,
@@ -255,13 +287,15 @@ __device__ __forceinline__ void dma_tile(int K, const uint16_t *__restrict__ A, 
     const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_char *)lds_raw;
     lds_char *const L = (lds_char *)lds_raw;
 
-    using OA = DmaOp<A_MN>;
-    using OB = DmaOp<B_MN>;
-    using PO = PieceOrder<A_MN, B_MN>;
+    using G = Geo<E>;
+    constexpr int kMB = G::kMB, kNB = G::kNB, kI = G::kI, kBOff = G::kBOff, kNs = G::kNs;
+    using OA = DmaOp<A_MN, E>;
+    using OB = DmaOp<B_MN, E>;
+    using PO = PieceOrder<A_MN, B_MN, E>;
     OA oa;
     OB ob;
-    oa.init(A, lda, m0, wave, lane, L, 0, wm * kTM);
-    ob.init(B, ldb, n0, wave, lane, L, kBOff, wn * kTN);
+    oa.init(A, lda, m0, wave, lane, L, 0, wm * G::kTM);
+    ob.init(B, ldb, n0, wave, lane, L, kBOff, wn * G::kTN);
     // Loads per wave: nMN every k-step (the MN operands' next stage), nKM every other
     // k-step (the KM operands' next double step), MN loads first.
     constexpr int nMN = (A_MN ? kI : 0) + (B_MN ? kI : 0);
@@ -290,21 +324,21 @@ __device__ __forceinline__ void dma_tile(int K, const uint16_t *__restrict__ A, 
 
     floatx4 acc[kMB][kNB];
 
-    // One k-step t = kt + u (u = t % 4 is a compile-time constant): kMf MFMAs on the
-    // fragments in slot u % 2.  The step's loads (MN: k-step t+3 into stage (u+3) % 4; on
-    // even steps KM: double step t/2 + 1 into slot (u/2 + 1) % 2) are spread over the
-    // first kLoadHi MFMAs; after kBarrier MFMAs the wave waits until the loads step t+1
-    // needs are done, then the barrier publishes them and the fragments of t+1 are read
-    // into the other slot under the remaining MFMAs, in the order of their first use.
-    // The wait counts: on an even step the 2 nMN + nKM youngest loads may stay in flight
-    // (the MN loads of steps t+2 and t+3 and this step's KM loads; the KM loads of two
-    // steps ago are older but already complete), on an odd step nMN (this step's MN
-    // loads) when there are KM operands, else 2 nMN.  No branches: near the end the loads
-    // repeat the last k-step or double step into free stages or slots.
-    constexpr int kMf = kMB * kNB;
-    constexpr int kBarrier = 40;
-    constexpr int kLoadHi = 32;
-    static_assert(kLoadHi <= kBarrier, "the step's loads precede its wait");
+    // One k-step t = kt + u (u = t % kNs is a compile-time constant): kMf MFMAs on the
+    // fragments in slot u % 2.  The step's loads (MN: k-step t + kNs - 1 into stage
+    // (u - 1) % kNs; on even steps KM: double step t/2 + kNs/2 - 1 into the slot of double
+    // step t/2 - 1) are spread over the first kLoadHi MFMAs; after kBarrier MFMAs the wave
+    // waits until the loads step t+1 needs are done, then the barrier publishes them and
+    // the fragments of t+1 are read into the other slot under the remaining MFMAs, in the
+    // order of their first use.  Loads are issued in step order (a step's MN loads, then
+    // its KM loads), the prologue's included, so the wait counts are the loads of the
+    // steps after the one that issued what step t+1 needs: on an even step t both of its
+    // operands' loads came from step t - kNs + 2, so the loads of the kNs - 2 steps after
+    // it may stay in flight; on an odd step its KM loads came from step t - kNs + 3
+    // (those of kNs - 3 later steps may stay), its MN loads alone from t - kNs + 2.  No
+    // branches: near the end the loads repeat the last k-step or double step into free
+    // stages or slots.
+    constexpr int kMf = G::kMf, kBarrier = G::kBarrier, kLoadHi = G::kLoadHi;
     auto ev_begin = [](int qs, int n, int lo, int hi) {
         if (qs <= lo) return 0;
         if (qs >= hi) return n;
@@ -317,10 +351,12 @@ __device__ __forceinline__ void dma_tile(int K, const uint16_t *__restrict__ A, 
         constexpr int f = u % 2;
         constexpr bool even = u % 2 == 0;
         constexpr int nLd = nMN + (even ? nKM : 0);
-        constexpr int kWait = even ? 2 * nMN + nKM : (nKM ? nMN : 2 * nMN);
+        constexpr int kWait = even ? (kNs - 2) * nMN + (kNs - 2) / 2 * nKM
+                                   : (nKM ? (kNs - 3) * nMN + (kNs - 4) / 2 * nKM : (kNs - 2) * nMN);
+        static_assert(kWait < 64, "vmcnt range");
         const int t = kt + u;
         const int k_mn = min(t + kNs - 1, nk - 1) * kBK;
-        const int k_km = min(t / 2 + 1, nk / 2 - 1) * 2 * kBK;
+        const int k_km = min(t / 2 + kNs / 2 - 1, nk / 2 - 1) * 2 * kBK;
 #pragma unroll
         for (int qs = 0; qs < kMf; ++qs) {
             // snake order: odd block rows walk the B blocks backwards, so consecutive
@@ -340,7 +376,7 @@ __device__ __forceinline__ void dma_tile(int K, const uint16_t *__restrict__ A, 
 #pragma unroll
                 for (int w = lo; w < hi; ++w) {
                     if (w < nMN) issue_mn((u + kNs - 1) % kNs, k_mn, w);
-                    else issue_km((u / 2 + 1) % 2, k_km, w - nMN);
+                    else issue_km((u / 2 + kNs / 2 - 1) % (kNs / 2), k_km, w - nMN);
                 }
             }
             if (qs == kBarrier - 1) {
@@ -351,15 +387,23 @@ __device__ __forceinline__ void dma_tile(int K, const uint16_t *__restrict__ A, 
         }
     };
 
-    // KM double step 0 into slot 0, MN k-steps 0 .. kNs-2 into stages 0 .. kNs-2; wait for
-    // step 0's data (the MN loads of steps 1 and 2 may stay in flight), read its fragments
+    // Prologue, in the order the steps before step 0 would have issued it: KM double step
+    // 0, then MN k-steps 0 .. kNs-2 into stages 0 .. kNs-2, KM double step d after MN
+    // k-step 2d + 1 (d = 1 .. kNs/2 - 2); wait for step 0's data (everything after MN
+    // k-step 0 may stay in flight), read its fragments
 #pragma unroll
     for (int w = 0; w < nKM; ++w) issue_km(0, 0, w);
 #pragma unroll
-    for (int p = 0; p < kNs - 1; ++p)
+    for (int p = 0; p < kNs - 1; ++p) {
 #pragma unroll
         for (int w = 0; w < nMN; ++w) issue_mn(p, min(p, nk - 1) * kBK, w);
-    wait_vmcnt<2 * nMN>();
+        if (p % 2 == 1 && p >= 3) {
+#pragma unroll
+            for (int w = 0; w < nKM; ++w)
+                issue_km((p - 1) / 2, min((p - 1) / 2, nk / 2 - 1) * 2 * kBK, w);
+        }
+    }
+    wait_vmcnt<(kNs - 2) * nMN + (kNs / 2 - 2) * nKM>();
     __syncthreads();
 #pragma unroll
     for (int p = 0; p < kR; ++p) read_piece(0, 0, p);
@@ -373,34 +417,27 @@ __device__ __forceinline__ void dma_tile(int K, const uint16_t *__restrict__ A, 
         for (int j = 0; j < kNB; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
     pin_acc(acc);
     asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
-    using U0 = std::integral_constant<int, 0>;
-    using U1 = std::integral_constant<int, 1>;
-    using U2 = std::integral_constant<int, 2>;
-    using U3 = std::integral_constant<int, 3>;
-    for (int kt = 0; kt < nk; kt += kNs) {
-        kstep(kt, U0{});
-        kstep(kt, U1{});
-        kstep(kt, U2{});
-        kstep(kt, U3{});
-    }
+    for (int kt = 0; kt < nk; kt += kNs)
+        for_steps(kstep, kt, std::make_integer_sequence<int, kNs>{});
     // nothing may still write this workgroup's LDS when it exits
     wait_vmcnt<0>();
     pin_acc(acc);
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
     pin_acc(acc);
-    store_tile<EPI, T>(acc, C, ldc, m0 + wm * kTM, n0 + wn * kTN, sign, flags);
+    store_tile<EPI, T>(acc, C, ldc, m0 + wm * G::kTM, n0 + wn * G::kTN, sign, flags);
 }
 
 }  // namespace dma
 
-template <typename T, bool A_MN, bool B_MN, int EPI>
+// One workgroup per CU (128 KiB of LDS for either tile; E = 256 also takes all 256
+// accumulator registers of a lane).
+template <typename T, bool A_MN, bool B_MN, int EPI, int E>
 __global__ __launch_bounds__(64 * dma::kWaves) __attribute__((amdgpu_waves_per_eu(1)))
 void mfma_f16_dma_kernel(int M, int N, int K, const uint16_t *__restrict__ A, int lda,
                          const uint16_t *__restrict__ B, int ldb, float *__restrict__ C,
                          int ldc, float sign, int flags) {
-    __shared__ __attribute__((aligned(1024))) char lds[dma::kLds];
+    __shared__ __attribute__((aligned(1024))) char lds[dma::Geo<E>::kLds];
     int tm, tn;
-    grouped_tile(xcd_contiguous_id(blockIdx.x, gridDim.x), M / dma::kBM, N / dma::kBN, 4, tm, tn);
-    dma::dma_tile<T, A_MN, B_MN, EPI>(K, A, lda, B, ldb, C, ldc, sign, flags, tm * dma::kBM,
-                                      tn * dma::kBN, lds);
+    grouped_tile(xcd_contiguous_id(blockIdx.x, gridDim.x), M / E, N / E, 4, tm, tn);
+    dma::dma_tile<T, A_MN, B_MN, EPI, E>(K, A, lda, B, ldb, C, ldc, sign, flags, tm * E, tn * E, lds);
 }

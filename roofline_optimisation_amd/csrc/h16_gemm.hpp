@@ -42,6 +42,7 @@
 #pragma once
 
 #include <type_traits>
+#include <utility>
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -442,14 +443,20 @@ inline bool op_fits(bool mn, int ext, int K, int ld) {
     return mn ? ((long)K * ld + ext) * 2 < (1L << 31) : ((long)ext * ld + K) * 2 < (1L << 31);
 }
 
-// The direct-load kernel takes the interior tiles of a 256 x 256 configuration when
-// rows are 16-byte aligned, every byte offset fits the 31-bit buffer range and K is a
-// multiple of kNs k-steps.
+// The direct-load kernel takes the interior tiles of a 256 x 256 or 128 x 128
+// configuration when rows are 16-byte aligned, every byte offset fits the 31-bit buffer
+// range and K is a multiple of one trip round the ring (128 for 256-wide tiles, 256 for
+// 128-wide ones).  At 128 x 128 the tile's loads (16 KiB per k-step per CU against 256
+// cycles of MFMAs) run at the CU's load-path rate, so the kernel is load-bound there;
+// it still beats the register-staged kernel by 10-20 % at 2048^2 (one tile per CU).
 inline bool use_dma(const GemmArgs &g, int tile) {
-    return tile == dma::kBM && h16_vec(g) && g.K > 0 && g.K % (dma::kBK * dma::kNs) == 0 &&
-           g.M >= dma::kBM && g.N >= dma::kBN &&
-           op_fits(g.trans_a != 0, dma::kBM, g.K, g.lda) &&
-           op_fits(g.trans_b == 0, dma::kBN, g.K, g.ldb);
+    const int ring = tile == 256 ? dma::Geo<256>::kNs : dma::Geo<128>::kNs;
+    // 128-wide tiles hold 128 KiB of LDS, one workgroup per CU: only a single round of
+    // at most 256 interior tiles (more go to the register-staged kernel, two per CU)
+    if (tile == 128 && (long)(g.M / 128) * (g.N / 128) > 256) return false;
+    return (tile == 256 || tile == 128) && h16_vec(g) && g.K > 0 &&
+           g.K % (dma::kBK * ring) == 0 && g.M >= tile && g.N >= tile &&
+           op_fits(g.trans_a != 0, tile, g.K, g.lda) && op_fits(g.trans_b == 0, tile, g.K, g.ldb);
 }
 
 // The epilogue's flags argument: bit 0 adds the old C; with 16-bit C, bit 1 selects
@@ -487,11 +494,18 @@ hipError_t launch_cfg(const GemmArgs &g, hipStream_t s) {
     const bool fits = op_fits(A_MN, BM, g.K, g.lda) && op_fits(B_MN, BN, g.K, g.ldb);
     if (full_tiles > 0) {
         hipError_t e = hipSuccess;
-        if (use_dma(g, BM)) {
-            hipLaunchKernelGGL((mfma_f16_dma_kernel<T, A_MN, B_MN, EPI>), dim3(full_tiles),
-                               dim3(64 * dma::kWaves), 0, s, g.M, g.N, g.K, (const uint16_t *)g.A,
-                               g.lda, (const uint16_t *)g.B, g.ldb, g.C, g.ldc, g.sign, epi_flags<EPI>(g));
-            e = hipGetLastError();
+        bool dma_done = false;
+        if constexpr (BM == BN) {
+            if (use_dma(g, BM)) {
+                hipLaunchKernelGGL((mfma_f16_dma_kernel<T, A_MN, B_MN, EPI, BM>), dim3(full_tiles),
+                                   dim3(64 * dma::kWaves), 0, s, g.M, g.N, g.K, (const uint16_t *)g.A,
+                                   g.lda, (const uint16_t *)g.B, g.ldb, g.C, g.ldc, g.sign,
+                                   epi_flags<EPI>(g));
+                e = hipGetLastError();
+                dma_done = true;
+            }
+        }
+        if (dma_done) {
         } else if (EPI == 0 && vec && fits) {
             if constexpr (EPI == 0) {
                 if ((g.K / kBK) % 2 == 0)

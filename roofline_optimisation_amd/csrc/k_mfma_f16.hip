@@ -20,6 +20,8 @@ const char *desc_mfma_f16(int dtype, const GemmArgs &g) {
     if (big && use_dma(g, 256))
         return dtype == kF16 ? "mfma_f16 256x256x32 w2x2 lds-dma" : "mfma_bf16 256x256x32 w2x2 lds-dma";
     const bool narrow = !big && !g.trans_a && !g.signed_or_acc() && !g.c16 && use_128x64(g);
+    if (!big && !narrow && use_dma(g, 128))
+        return dtype == kF16 ? "mfma_f16 128x128x32 w2x2 lds-dma" : "mfma_bf16 128x128x32 w2x2 lds-dma";
     if (dtype == kF16) {
         if (big) return v ? "mfma_f16 256x256x64 w2x2 dwordx4" : "mfma_f16 256x256x64 w2x2 u16";
         if (narrow) return v ? "mfma_f16 128x64x64 w2x2 dwordx4" : "mfma_f16 128x64x64 w2x2 u16";

@@ -281,6 +281,46 @@ def test_h16_dma_instances(dtype, case):
     assert ok and np.array_equal(Ci, C32)
 
 
+# 128 x 128 tiles on the direct-to-LDS kernel (one round of at most 256 interior tiles,
+# when the cost model prefers 128-wide tiles and plain products have 256 tiles or more;
+# K a multiple of 256, one trip of its 8-stage ring): the shortest K, padded
+# 16-byte-aligned strides on a non-square grid, and a long K.
+DMA128_CASES = [((2048, 2048, 256), (0, 0, 0)), ((4096, 1024, 512), (8, 16, 8)),
+                ((1024, 4096, 2048), (0, 0, 0))]
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("case", DMA128_CASES, ids=lambda c: "x".join(map(str, c[0])) + f"_pad{c[1][0]}")
+def test_h16_dma128_instances(dtype, case):
+    (M, N, K), pad = case
+    A, B = inputs.make_operands(M, N, K, 47, "uniform", dtype)
+    code = gb.DTYPE_CODES[dtype]
+    lda, ldb, ldc = K + pad[0], N + pad[1], N + pad[2]
+    P = 1 << 20
+    assert "128x128x32 w2x2 lds-dma" in gb.gemm355_kernel_desc(gb.VARIANT_MFMA, code, M, N, K, P, lda, P, ldb, P, ldc)
+    rows = np.array(sorted(set(sample_rows(M, 192).tolist()) | {127, 128, M - 1}))
+    C, ok = gpu_gemm(A, B, dtype, gb.VARIANT_MFMA, pad=pad, guard_rows=1)
+    C64, _ = oracle.gemm(np.ascontiguousarray(A[rows]), B, dtype)
+    check(C[rows], C64, dtype, "uniform", K, ok, f"dma128 {dtype} {M}x{N}x{K} pad={pad} sampled")
+    Ai, Bi = inputs.make_operands(M, N, K, 48, "int", dtype)
+    _, C32 = oracle.gemm(np.ascontiguousarray(Ai[rows]), Bi, dtype)
+    Ci, ok = gpu_gemm(Ai, Bi, dtype, gb.VARIANT_MFMA, pad=pad)
+    assert ok and np.array_equal(Ci[rows], C32)
+
+
+def test_h16_dma128_interior_with_edges():
+    """2100 x 2056: 16 x 16 interior tiles of 128 on the direct-to-LDS kernel, the ragged
+    right and bottom strips on the predicated kernel; rows sampled from both regions."""
+    M, N, K = 2100, 2056, 256
+    A, B = inputs.make_operands(M, N, K, 49, "uniform", "f16")
+    P = 1 << 20
+    assert "128x128x32 w2x2 lds-dma" in gb.gemm355_kernel_desc(gb.VARIANT_AUTO, gb.F16, M, N, K, P, K, P, N, P, N)
+    C, ok = gpu_gemm(A, B, "f16", entry="typed")
+    rows = np.array(sorted(set(sample_rows(M, 64).tolist()) | {2047, 2048, 2099}))
+    C64, _ = oracle.gemm(np.ascontiguousarray(A[rows]), B, "f16")
+    check(C[rows], C64, "f16", "uniform", K, ok, "dma128+edge f16 2100x2056x256 sampled")
+
+
 def test_h16_dma_interior_with_edges():
     """4000^2: 15 x 15 interior tiles on the direct-to-LDS kernel, the ragged right and
     bottom strips on the predicated kernel; rows sampled from both regions."""
