@@ -230,37 +230,43 @@ __device__ __forceinline__ void store_pair32_c16(const floatx16 &acc0, const flo
     __builtin_amdgcn_sched_barrier(0);
 }
 
-// One 16 x 16 accumulator quad of an interior tile with a sign and optional
-// accumulation: register r of this lane holds row row0 + r (row0 already includes the
-// lane's 4 (l/16)), column col; c = sign * acc (+ c when use_old).  Each register is read
-// from the AGPR file at its point of use (see store_block32_acc).  Ordinary stores: a
-// store writes 64-byte pieces of lines, which the L2 merges.
+// One 16 x 16 accumulator quad with a sign and optional accumulation: register r of this
+// lane holds row row0 + r (row0 already includes the lane's 4 (l/16)), column col;
+// c = sign * acc (+ c when use_old); EDGE guards every access against M x N.  Each
+// register is read from the AGPR file at its point of use (see store_block32_acc).
+// Ordinary stores: a store writes 64-byte pieces of lines, which the L2 merges.
+template <bool EDGE>
 __device__ __forceinline__ void store_quad16_acc(const floatx4 &acc, float *__restrict__ C, int ldc,
-                                                 int row0, int col, float sign, bool use_old) {
+                                                 int row0, int col, int M, int N, float sign,
+                                                 bool use_old) {
     __builtin_amdgcn_sched_barrier(0);
     float old[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-        old[r] = use_old ? C[(size_t)(row0 + r) * ldc + col] : 0.f;
+    for (int r = 0; r < 4; ++r) {
+        const bool ok = !EDGE || (row0 + r < M && col < N);
+        old[r] = use_old && ok ? C[(size_t)(row0 + r) * ldc + col] : 0.f;
+    }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         float a;
         asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(a) : "a"(acc[r]));
-        C[(size_t)(row0 + r) * ldc + col] = sign * a + old[r];
+        if (!EDGE || (row0 + r < M && col < N)) C[(size_t)(row0 + r) * ldc + col] = sign * a + old[r];
     }
     __builtin_amdgcn_sched_barrier(0);
 }
 
-// Two horizontally adjacent 16 x 16 quads of an interior tile (columns col0 .. col0+31,
-// lane l holding column l%16 of each, rows row0 + r) with C in the 16-bit type T,
-// c = round16(sign * acc (+ old c)).  With `flags` bit 1 (ldc even, C 4-byte aligned)
-// lanes 2m and 2m+1 exchange one register per row as in store_pair32_c16, so the even
-// lane writes columns 2m, 2m+1 of quad 0 and the odd lane those of quad 1, 4 bytes at a
-// time; otherwise every element is one 2-byte access.  `flags` bit 0 adds the old C.
-template <typename T>
+// Two horizontally adjacent 16 x 16 quads (columns col0 .. col0+31, lane l holding column
+// l%16 of each, rows row0 + r) with C in the 16-bit type T, c = round16(sign * acc (+ old
+// c)).  With `flags` bit 1 (ldc even, C 4-byte aligned) lanes 2m and 2m+1 exchange one
+// register per row as in store_pair32_c16, so the even lane writes columns 2m, 2m+1 of
+// quad 0 and the odd lane those of quad 1, 4 bytes at a time; otherwise every element is
+// one 2-byte access.  `flags` bit 0 adds the old C.  EDGE guards every access against
+// M x N (a pair whose second column is outside is read and written 2 bytes at a time;
+// the exchange itself runs in every lane).
+template <bool EDGE, typename T>
 __device__ __forceinline__ void store_pair16_c16(const floatx4 &acc0, const floatx4 &acc1,
                                                  uint16_t *__restrict__ C, int ldc, int row0,
-                                                 int col0, float sign, int flags) {
+                                                 int col0, int M, int N, float sign, int flags) {
     const int lane = threadIdx.x & 63;
     const bool use_old = flags & 1;
     auto rd = [&](const floatx4 &acc, int r) {
@@ -274,9 +280,12 @@ __device__ __forceinline__ void store_pair16_c16(const floatx4 &acc0, const floa
         for (int q = 0; q < 2; ++q)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                uint16_t *c = C + (size_t)(row0 + r) * ldc + col0 + 16 * q + (lane & 15);
-                const float old = use_old ? to_float(T{*c}) : 0.f;
-                *c = to_bits(sign * rd(q ? acc1 : acc0, r) + old, T{});
+                const int col = col0 + 16 * q + (lane & 15);
+                const bool ok = !EDGE || (row0 + r < M && col < N);
+                uint16_t *c = C + (size_t)(row0 + r) * ldc + col;
+                const float old = use_old && ok ? to_float(T{*c}) : 0.f;
+                const uint16_t v = to_bits(sign * rd(q ? acc1 : acc0, r) + old, T{});
+                if (ok) *c = v;
             }
         __builtin_amdgcn_sched_barrier(0);
         return;
@@ -285,8 +294,11 @@ __device__ __forceinline__ void store_pair16_c16(const floatx4 &acc0, const floa
     const int cw = col0 + (lane & 14) + 16 * odd;  // first of the two columns this lane writes
     uint32_t oldw[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-        oldw[r] = use_old ? *(const uint32_t *)(C + (size_t)(row0 + r) * ldc + cw) : 0u;
+    for (int r = 0; r < 4; ++r) {
+        const uint16_t *c = C + (size_t)(row0 + r) * ldc + cw;
+        const bool in = !EDGE || (row0 + r < M && cw < N), both = !EDGE || cw + 1 < N;
+        oldw[r] = use_old && in ? (both ? *(const uint32_t *)c : (uint32_t)c[0]) : 0u;
+    }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const float a0 = rd(acc0, r), a1 = rd(acc1, r);
@@ -298,7 +310,9 @@ __device__ __forceinline__ void store_pair16_c16(const floatx4 &acc0, const floa
         const float ohi = use_old ? to_float(T{(uint16_t)(oldw[r] >> 16)}) : 0.f;
         const uint32_t w = (uint32_t)to_bits(sign * lo + olo, T{}) |
                            ((uint32_t)to_bits(sign * hi + ohi, T{}) << 16);
-        *(uint32_t *)(C + (size_t)(row0 + r) * ldc + cw) = w;
+        uint16_t *c = C + (size_t)(row0 + r) * ldc + cw;
+        if (!EDGE || (row0 + r < M && cw + 1 < N)) *(uint32_t *)c = w;
+        else if (row0 + r < M && cw < N) *c = (uint16_t)(w & 0xFFFF);
     }
     __builtin_amdgcn_sched_barrier(0);
 }

@@ -141,22 +141,26 @@ struct DmaOp {
     static constexpr int kSlot = 2 * G::kStage;      // KM slot bytes
     static constexpr int kPieces = MN ? 2 : 1;       // LDS reads per fragment
     int4v rsrc;
-    uint32_t voff[2];
+    uint32_t voff[MN ? 2 : 2 * G::kI];   // per lane: MN by instruction parity, KM by instruction
     lds_char *rd[MN ? NB : 2];
     H16Frag<MN, NB> fr;
 
-    // X: the operand; mn0: the tile's first row (KM) or column (MN); wb: the wave's first
-    // row or column within the tile.
-    __device__ __forceinline__ void init(const uint16_t *X, int ld, int mn0, int wave, int lane,
-                                         lds_char *L, int roff, int wb) {
+    // X: the operand, whose rows (KM) or columns (MN) number ext (a multiple of 8 for
+    // MN); mn0: the tile's first row (KM) or column (MN); wb: the wave's first row or
+    // column within the tile.  In a ragged tile a lane whose source row (KM) or 16-byte
+    // column chunk (MN) lies beyond ext loads the last one inside instead, so every load
+    // stays within the operand; what it puts in LDS only reaches outputs beyond row M or
+    // column N, which are never stored.
+    __device__ __forceinline__ void init(const uint16_t *X, int ld, int ext, int mn0, int wave,
+                                         int lane, lds_char *L, int roff, int wb) {
         if constexpr (MN) {
             constexpr int lpr = 64 / G::kRpi;        // lanes per row of one load
             rsrc = rsrc_of(X + mn0);
             const int rl = lane / lpr, row = 8 * wave + rl, slot = lane % lpr;
-            const int kx = 2 * (wave & 1);
+            const int kx = 2 * (wave & 1), last = (ext - mn0) / 8 - 1;
 #pragma unroll
             for (int p = 0; p < 2; ++p)
-                voff[p] = (uint32_t)((row * ld + 8 * (slot ^ (4 * ((G::kRpi * p + rl) % 4)) ^ kx)) * 2);
+                voff[p] = (uint32_t)((row * ld + 8 * min(slot ^ (4 * ((G::kRpi * p + rl) % 4)) ^ kx, last)) * 2);
             // block b, piece h: lane (g = l/16, e = (l%16)/4, q = l%4) reads row 8 g + 4 h +
             // e, chunk wb/8 + 2 b + q/2, byte 8 (q%2) of it; that row's swizzle key is
             // 4 e ^ 2 (g%2)
@@ -168,9 +172,11 @@ struct DmaOp {
                                 8 * (q & 1));
         } else {
             rsrc = rsrc_of(X + (size_t)mn0 * ld);
-            const int row = G::kKMRows * wave + lane / 8, slot = lane & 7;
-            voff[0] = (uint32_t)((row * ld + 8 * (slot ^ ((0 + lane / 16) & 7))) * 2);
-            voff[1] = (uint32_t)((row * ld + 8 * (slot ^ ((4 + lane / 16) & 7))) * 2);
+            const int row = G::kKMRows * wave + lane / 8, slot = lane & 7, last = ext - mn0 - 1;
+#pragma unroll
+            for (int i = 0; i < 2 * G::kI; ++i)
+                voff[i] = (uint32_t)((min(row + 8 * i, last) * ld +
+                                      8 * (slot ^ ((4 * (i % 2) + lane / 16) & 7))) * 2);
             // block b, half h of the slot: row wb + 16 b + l%16, chunk 4 h + l/16, whose
             // swizzle key ((l%16) / 2) % 8 does not depend on b
             const int l16 = lane & 15, lq = lane >> 4;
@@ -188,7 +194,7 @@ struct DmaOp {
             load_lds16(dst, voff[i & 1], rsrc, (uint32_t)((k0 + G::kRpi * i) * ld * 2));
         } else {
             const uint32_t dst = lds0 + roff + place * kSlot + (wave * 2 * G::kI + i) * 1024;
-            load_lds16(dst, voff[i & 1], rsrc, (uint32_t)((8 * i * ld + k0) * 2));
+            load_lds16(dst, voff[i], rsrc, (uint32_t)(k0 * 2));
         }
     }
     // Piece h of block b of k-step u (u = t % kNs, so the MN stage is u, the KM slot
@@ -240,14 +246,15 @@ __device__ __forceinline__ void pin_acc(floatx4 (&acc)[kMB][kNB]) {
 }
 
 // The FP32 accumulator quads of one wave, stored to C: quad (i, j) holds rows
-// row0 + 16 i + 4 (l/16) + r, column col0 + 16 j + l%16.  For each row the eight quads of
+// row0 + 16 i + 4 (l/16) + r, column col0 + 16 j + l%16.  EDGE (a tile reaching past
+// row M or column N) guards every access.  For each row the eight quads of
 // a block row go out back to back, so every 128-byte line of C is written whole by two
 // consecutive stores.  The stores are ordinary (cached) ones: each instruction writes
 // half lines, which the L2 merges; as non-temporal stores the same pattern took 40 %
 // longer (64 MiB from 256 workgroups: 15.8 against 11.2 us).
-template <int EPI, typename T, int kMB, int kNB>
+template <int EPI, typename T, bool EDGE, int kMB, int kNB>
 __device__ __forceinline__ void store_tile(floatx4 (&acc)[kMB][kNB], float *__restrict__ C, int ldc,
-                                           int row0, int col0, float sign, int flags) {
+                                           int row0, int col0, int M, int N, float sign, int flags) {
     const int lane = threadIdx.x & 63;
     const int rl = row0 + 4 * (lane >> 4);
     if constexpr (EPI == 0) {
@@ -256,28 +263,30 @@ __device__ __forceinline__ void store_tile(floatx4 (&acc)[kMB][kNB], float *__re
 #pragma unroll
             for (int r = 0; r < 4; ++r)
 #pragma unroll
-                for (int j = 0; j < kNB; ++j)
-                    C[(size_t)(rl + 16 * i + r) * ldc + col0 + 16 * j + (lane & 15)] = acc[i][j][r];
+                for (int j = 0; j < kNB; ++j) {
+                    const int row = rl + 16 * i + r, col = col0 + 16 * j + (lane & 15);
+                    if (!EDGE || (row < M && col < N)) C[(size_t)row * ldc + col] = acc[i][j][r];
+                }
     } else if constexpr (EPI == 1) {
         const bool use_old = flags & 1;
 #pragma unroll
         for (int i = 0; i < kMB; ++i)
 #pragma unroll
             for (int j = 0; j < kNB; ++j)
-                store_quad16_acc(acc[i][j], C, ldc, rl + 16 * i, col0 + 16 * j + (lane & 15), sign,
-                                 use_old);
+                store_quad16_acc<EDGE>(acc[i][j], C, ldc, rl + 16 * i, col0 + 16 * j + (lane & 15),
+                                       M, N, sign, use_old);
     } else {
 #pragma unroll
         for (int i = 0; i < kMB; ++i)
 #pragma unroll
             for (int j = 0; j < kNB; j += 2)
-                store_pair16_c16<T>(acc[i][j], acc[i][j + 1], (uint16_t *)C, ldc, rl + 16 * i,
-                                    col0 + 16 * j, sign, flags);
+                store_pair16_c16<EDGE, T>(acc[i][j], acc[i][j + 1], (uint16_t *)C, ldc, rl + 16 * i,
+                                          col0 + 16 * j, M, N, sign, flags);
     }
 }
 
 template <typename T, bool A_MN, bool B_MN, int EPI, int E>
-__device__ __forceinline__ void dma_tile(int K, const uint16_t *__restrict__ A, int lda,
+__device__ __forceinline__ void dma_tile(int M, int N, int K, const uint16_t *__restrict__ A, int lda,
                                          const uint16_t *__restrict__ B, int ldb,
                                          float *__restrict__ C, int ldc, float sign,
                                          int flags, int m0, int n0, char *lds_raw) {
@@ -294,8 +303,8 @@ __device__ __forceinline__ void dma_tile(int K, const uint16_t *__restrict__ A, 
     using PO = PieceOrder<A_MN, B_MN, E>;
     OA oa;
     OB ob;
-    oa.init(A, lda, m0, wave, lane, L, 0, wm * G::kTM);
-    ob.init(B, ldb, n0, wave, lane, L, kBOff, wn * G::kTN);
+    oa.init(A, lda, M, m0, wave, lane, L, 0, wm * G::kTM);
+    ob.init(B, ldb, N, n0, wave, lane, L, kBOff, wn * G::kTN);
     // Loads per wave: nMN every k-step (the MN operands' next stage), nKM every other
     // k-step (the KM operands' next double step), MN loads first.
     constexpr int nMN = (A_MN ? kI : 0) + (B_MN ? kI : 0);
@@ -424,7 +433,10 @@ __device__ __forceinline__ void dma_tile(int K, const uint16_t *__restrict__ A, 
     pin_acc(acc);
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
     pin_acc(acc);
-    store_tile<EPI, T>(acc, C, ldc, m0 + wm * G::kTM, n0 + wn * G::kTN, sign, flags);
+    if (m0 + E <= M && n0 + E <= N)
+        store_tile<EPI, T, false>(acc, C, ldc, m0 + wm * G::kTM, n0 + wn * G::kTN, M, N, sign, flags);
+    else
+        store_tile<EPI, T, true>(acc, C, ldc, m0 + wm * G::kTM, n0 + wn * G::kTN, M, N, sign, flags);
 }
 
 }  // namespace dma
@@ -438,6 +450,7 @@ void mfma_f16_dma_kernel(int M, int N, int K, const uint16_t *__restrict__ A, in
                          int ldc, float sign, int flags) {
     __shared__ __attribute__((aligned(1024))) char lds[dma::Geo<E>::kLds];
     int tm, tn;
-    grouped_tile(xcd_contiguous_id(blockIdx.x, gridDim.x), M / E, N / E, 4, tm, tn);
-    dma::dma_tile<T, A_MN, B_MN, EPI, E>(K, A, lda, B, ldb, C, ldc, sign, flags, tm * E, tn * E, lds);
+    grouped_tile(xcd_contiguous_id(blockIdx.x, gridDim.x), cdiv(M, E), cdiv(N, E), 4, tm, tn);
+    dma::dma_tile<T, A_MN, B_MN, EPI, E>(M, N, K, A, lda, B, ldb, C, ldc, sign, flags, tm * E, tn * E,
+                                         lds);
 }

@@ -443,17 +443,20 @@ inline bool op_fits(bool mn, int ext, int K, int ld) {
     return mn ? ((long)K * ld + ext) * 2 < (1L << 31) : ((long)ext * ld + K) * 2 < (1L << 31);
 }
 
-// The direct-load kernel takes the interior tiles of a 256 x 256 or 128 x 128
-// configuration when rows are 16-byte aligned, every byte offset fits the 31-bit buffer
-// range and K is a multiple of one trip round the ring (128 for 256-wide tiles, 256 for
-// 128-wide ones).  At 128 x 128 the tile's loads (16 KiB per k-step per CU against 256
+// The direct-load kernel takes every tile (ragged ones included) of a 256 x 256 or
+// 128 x 128 configuration when rows are 16-byte aligned, every byte offset fits the
+// 31-bit buffer range and K is a multiple of one trip round the ring (128 for 256-wide
+// tiles, 256 for 128-wide ones).  At 128 x 128 the tile's loads (16 KiB per k-step per CU against 256
 // cycles of MFMAs) run at the CU's load-path rate, so the kernel is load-bound there;
 // it still beats the register-staged kernel by 10-20 % at 2048^2 (one tile per CU).
 inline bool use_dma(const GemmArgs &g, int tile) {
     const int ring = tile == 256 ? dma::Geo<256>::kNs : dma::Geo<128>::kNs;
     // 128-wide tiles hold 128 KiB of LDS, one workgroup per CU: only a single round of
-    // at most 256 interior tiles (more go to the register-staged kernel, two per CU)
-    if (tile == 128 && (long)(g.M / 128) * (g.N / 128) > 256) return false;
+    // at most 256 tiles (more go to the register-staged kernel, two per CU)
+    if (tile == 128 && (long)cdiv(g.M, 128) * cdiv(g.N, 128) > 256) return false;
+    // an m/n-contiguous operand's extent is a whole number of 16-byte chunks, so no
+    // load straddles the end of its last row
+    if ((g.trans_a && g.M % 8 != 0) || (!g.trans_b && g.N % 8 != 0)) return false;
     return (tile == 256 || tile == 128) && h16_vec(g) && g.K > 0 &&
            g.K % (dma::kBK * ring) == 0 && g.M >= tile && g.N >= tile &&
            op_fits(g.trans_a != 0, tile, g.K, g.lda) && op_fits(g.trans_b == 0, tile, g.K, g.ldb);
@@ -492,21 +495,18 @@ hipError_t launch_cfg(const GemmArgs &g, hipStream_t s) {
     const int edge_tiles = cdiv(g.M, BM) * cdiv(g.N, BN) - full_tiles;
     const int all_flag = kfull ? 0 : 1;
     const bool fits = op_fits(A_MN, BM, g.K, g.lda) && op_fits(B_MN, BN, g.K, g.ldb);
+    if constexpr (BM == BN) {
+        if (use_dma(g, BM)) {
+            hipLaunchKernelGGL((mfma_f16_dma_kernel<T, A_MN, B_MN, EPI, BM>),
+                               dim3(cdiv(g.M, BM) * cdiv(g.N, BN)), dim3(64 * dma::kWaves), 0, s,
+                               g.M, g.N, g.K, (const uint16_t *)g.A, g.lda, (const uint16_t *)g.B,
+                               g.ldb, g.C, g.ldc, g.sign, epi_flags<EPI>(g));
+            return hipGetLastError();
+        }
+    }
     if (full_tiles > 0) {
         hipError_t e = hipSuccess;
-        bool dma_done = false;
-        if constexpr (BM == BN) {
-            if (use_dma(g, BM)) {
-                hipLaunchKernelGGL((mfma_f16_dma_kernel<T, A_MN, B_MN, EPI, BM>), dim3(full_tiles),
-                                   dim3(64 * dma::kWaves), 0, s, g.M, g.N, g.K, (const uint16_t *)g.A,
-                                   g.lda, (const uint16_t *)g.B, g.ldb, g.C, g.ldc, g.sign,
-                                   epi_flags<EPI>(g));
-                e = hipGetLastError();
-                dma_done = true;
-            }
-        }
-        if (dma_done) {
-        } else if (EPI == 0 && vec && fits) {
+        if (EPI == 0 && vec && fits) {
             if constexpr (EPI == 0) {
                 if ((g.K / kBK) % 2 == 0)
                     e = launch_one<T, BM, BN, WM, WN, MINW, 2, false, true, A_MN, B_MN, false>(g, full_tiles, all_flag, s);
@@ -528,17 +528,20 @@ hipError_t launch_cfg(const GemmArgs &g, hipStream_t s) {
 }
 
 // Cost model as for FP32: with w resident workgroups per CU a config needs
-// ceil(tiles / (256 w)) rounds of w * BM * BN work each; ties go to the larger tile,
-// whose LDS traffic per MFMA is half that of the smaller one.
+// ceil(tiles / (256 w)) rounds of w * BM * BN work each, divided by the tile's measured
+// efficiency: per unit of work the 256 x 256 direct-to-LDS tile runs about 1.8x faster
+// than two 128 x 128 tiles per CU (4096^3 FP16: 256^2 x 4096 per CU in 100 us;
+// 4096 x 4104 on 128-wide tiles: two 128^2 x 4096 per CU in 96 us per round), so 128-wide
+// tiles count 1/0.55 of their area.  Ties go to the larger tile.
 inline int pick_tile(const GemmArgs &g) {
-    struct Opt { int tile, per_cu; };
-    const Opt opts[] = {{256, 1}, {128, 2}};
-    long best = -1;
+    struct Opt { int tile, per_cu; double eff; };
+    const Opt opts[] = {{256, 1, 1.0}, {128, 2, 0.55}};
+    double best = -1;
     int tile = 128;
     for (const Opt &o : opts) {
         const long tiles = (long)cdiv(g.M, o.tile) * cdiv(g.N, o.tile);
         const long slots = 256L * o.per_cu;
-        const long cost = (tiles + slots - 1) / slots * o.per_cu * (long)o.tile * o.tile;
+        const double cost = (double)((tiles + slots - 1) / slots * o.per_cu * (long)o.tile * o.tile) / o.eff;
         if (best < 0 || cost < best) {
             best = cost;
             tile = o.tile;

@@ -98,13 +98,20 @@ def test_dispatch_choices(lib):
     assert d(-1, 0, 4096, 4096, 4096, P, 4096, P, 4096, P, 4096).startswith("mfma_f32 128x128")
     assert d(-1, 1, 4096, 4096, 4096, P, 4096, P, 4096, P, 4096).startswith("mfma_f16")
     assert d(-1, 2, 4096, 4096, 4096, P, 4096, P, 4096, P, 4096).startswith("mfma_bf16")
-    # 256 x 256 interior tiles with K a multiple of 128 load straight into LDS; other K,
-    # unaligned rows and the 128-row tiles keep register staging
+    # 256 x 256 tiles with K a multiple of 128, and one round of 128 x 128 tiles with K a
+    # multiple of 256, load straight into LDS, ragged tiles included; other K, unaligned
+    # rows and more 128-wide tiles keep register staging
     assert d(-1, 1, 4096, 4096, 4096, P, 4096, P, 4096, P, 4096) == "mfma_f16 256x256x32 w2x2 lds-dma"
     assert d(-1, 2, 4096, 4096, 4096, P, 4096, P, 4096, P, 4096) == "mfma_bf16 256x256x32 w2x2 lds-dma"
     assert d(-1, 1, 4096, 4096, 4160, P, 4160, P, 4096, P, 4096) == "mfma_f16 256x256x64 w2x2 dwordx4"
     assert d(-1, 1, 4096, 4096, 4096, P + 2, 4096, P, 4096, P, 4096) == "mfma_f16 256x256x64 w2x2 u16"
-    assert d(-1, 1, 2048, 2048, 2048, P, 2048, P, 2048, P, 2048) == "mfma_f16 128x128x64 w2x2 dwordx4"
+    assert d(-1, 1, 2048, 2048, 2048, P, 2048, P, 2048, P, 2048) == "mfma_f16 128x128x32 w2x2 lds-dma"
+    assert d(-1, 1, 2048, 2048, 2176, P, 2176, P, 2048, P, 2048) == "mfma_f16 128x128x64 w2x2 dwordx4"
+    assert d(-1, 2, 2560, 2560, 2560, P, 2560, P, 2560, P, 2560) == "mfma_bf16 128x128x64 w2x2 dwordx4"
+    assert d(-1, 1, 4000, 4000, 4096, P, 4096, P, 4000, P, 4000) == "mfma_f16 256x256x32 w2x2 lds-dma"
+    assert d(-1, 1, 4096, 4104, 4096, P, 4096, P, 4104, P, 4104) == "mfma_f16 256x256x32 w2x2 lds-dma"
+    # an m/n-contiguous extent that is not a whole number of 16-byte chunks stays staged
+    assert d(-1, 1, 4000, 4004, 4096, P, 4096, P, 4008, P, 4004) == "mfma_f16 256x256x64 w2x2 dwordx4"
     # rows not 16-byte aligned (lda = 515 floats) take the dword load path
     assert d(-1, 0, 1023, 997, 515, P, 515, P, 997, P, 997).endswith("dword")
     assert d(-1, 0, 1000, 1000, 1000, P, 1000, P, 1000, P, 1000).endswith("dwordx4")

@@ -112,8 +112,11 @@ def test_flag_matrix_ragged(fl, dtype, variant):
 LAYOUTS = list(itertools.product([False, True], repeat=2))
 MODES = [(False, False, False), (True, False, False), (False, True, True)]  # na, nb, acc
 SHAPES = {"f32": [(3072, 3072, 64), (1024, 768, 96), (2048, 2048, 64), (1536, 1536, 96), (1351, 1537, 100)],
-          "f16": [(3072, 3072, 128), (3072, 2816, 192), (1024, 1024, 128)],
-          "bf16": [(3072, 3072, 256), (1024, 512, 64)]}
+          "f16": [(3072, 3072, 128), (3072, 2816, 192), (1024, 1024, 128), (4000, 3992, 128)],
+          "bf16": [(3072, 3072, 256), (1024, 512, 64), (2000, 2040, 256)]}
+# (4000, 3992, 128) and (2000, 2040, 256): every tile, ragged ones included, on the
+# direct-to-LDS kernel (256 x 256 and 128 x 128 tiles); the padding around the operands
+# holds NaN, so a ragged tile's loads past the matrix would show in its stored outputs.
 
 
 @pytest.mark.parametrize("mode", MODES, ids=["plain", "neg_a", "neg_b_acc"])
@@ -255,6 +258,14 @@ SHAPES16 = [(3072, 3072, 128), (3072, 2816, 192), (1024, 1024, 128), (1024, 512,
 @pytest.mark.parametrize("shape", SHAPES16, ids=lambda s: "x".join(map(str, s)))
 def test_c16_tiles_every_layout(shape, dtype, layout, mode):
     compare16(*shape, dtype, *layout, *mode, seed=57)
+
+
+@pytest.mark.parametrize("mode", [MODES[0], MODES[2]], ids=["plain", "neg_b_acc"])
+@pytest.mark.parametrize("layout", LAYOUTS, ids=lambda l: f"ta{int(l[0])}tb{int(l[1])}")
+def test_c16_ragged_direct_to_lds(layout, mode):
+    """2824^2 x 128: 12 x 12 tiles of 256, the last row and column of tiles 8 wide, all on
+    the direct-to-LDS kernel, with C in FP16 (guarded 2- and 4-byte stores)."""
+    compare16(2824, 2824, 128, "f16", *layout, *mode, seed=58)
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])

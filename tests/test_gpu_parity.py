@@ -308,28 +308,30 @@ def test_h16_dma128_instances(dtype, case):
     assert ok and np.array_equal(Ci[rows], C32)
 
 
-def test_h16_dma128_interior_with_edges():
-    """2100 x 2056: 16 x 16 interior tiles of 128 on the direct-to-LDS kernel, the ragged
-    right and bottom strips on the predicated kernel; rows sampled from both regions."""
-    M, N, K = 2100, 2056, 256
+def test_h16_dma128_ragged():
+    """2040 x 2000: 16 x 16 tiles of 128, the last row of tiles 120 high and the last
+    column 80 wide, every tile on the direct-to-LDS kernel; rows sampled from both
+    regions."""
+    M, N, K = 2040, 2000, 256
     A, B = inputs.make_operands(M, N, K, 49, "uniform", "f16")
     P = 1 << 20
     assert "128x128x32 w2x2 lds-dma" in gb.gemm355_kernel_desc(gb.VARIANT_AUTO, gb.F16, M, N, K, P, K, P, N, P, N)
-    C, ok = gpu_gemm(A, B, "f16", entry="typed")
-    rows = np.array(sorted(set(sample_rows(M, 64).tolist()) | {2047, 2048, 2099}))
+    C, ok = gpu_gemm(A, B, "f16", entry="typed", guard_rows=1)
+    rows = np.array(sorted(set(sample_rows(M, 64).tolist()) | {1919, 1920, 2039}))
     C64, _ = oracle.gemm(np.ascontiguousarray(A[rows]), B, "f16")
-    check(C[rows], C64, "f16", "uniform", K, ok, "dma128+edge f16 2100x2056x256 sampled")
+    check(C[rows], C64, "f16", "uniform", K, ok, "dma128 ragged f16 2040x2000x256 sampled")
 
 
 def test_h16_dma_interior_with_edges():
-    """4000^2: 15 x 15 interior tiles on the direct-to-LDS kernel, the ragged right and
-    bottom strips on the predicated kernel; rows sampled from both regions."""
+    """4000^2: 16 x 16 tiles of 256 on the direct-to-LDS kernel, the last row and column
+    of tiles 160 wide (their loads clamped to the matrix, their stores guarded); rows
+    sampled from both regions."""
     M = N = 4000
     K = 256
     A, B = inputs.make_operands(M, N, K, 46, "uniform", "bf16")
     P = 1 << 20
     assert "lds-dma" in gb.gemm355_kernel_desc(gb.VARIANT_AUTO, gb.BF16, M, N, K, P, K, P, N, P, N)
-    C, ok = gpu_gemm(A, B, "bf16", entry="typed")
+    C, ok = gpu_gemm(A, B, "bf16", entry="typed", guard_rows=1)
     rows = np.array(sorted(set(sample_rows(M, 48).tolist()) | {3839, 3840, 3999}))
     C64, _ = oracle.gemm(np.ascontiguousarray(A[rows]), B, "bf16")
     check(C[rows], C64, "bf16", "uniform", K, ok, "dma+edge bf16 4000x4000x256 sampled")
