@@ -138,6 +138,23 @@ __device__ __forceinline__ void f32_tile(int M, int N, int K, const float *__res
         b_r[i] = q / OB::kPerRow;
         b_c[i] = (q % OB::kPerRow) * 4;
     }
+    // An unpredicated tile that reaches past row M or column N (launched when the host
+    // lets this kernel take every tile: K % kBK == 0, an m/n-contiguous extent a multiple
+    // of 4): a chunk whose row (KM) or 4 columns (MN) lie past the matrix loads the last
+    // one inside instead, so every load stays within the operand; its products only
+    // reach outputs past row M or column N, whose stores are guarded below.
+    if constexpr (!EDGE) {
+#pragma unroll
+        for (int i = 0; i < kAC; ++i) {
+            if (A_MN) a_c[i] = min(a_c[i], M - m0 - 4);
+            else a_r[i] = min(a_r[i], M - m0 - 1);
+        }
+#pragma unroll
+        for (int i = 0; i < kBC; ++i) {
+            if (B_MN) b_c[i] = min(b_c[i], N - n0 - 4);
+            else b_r[i] = min(b_r[i], N - n0 - 1);
+        }
+    }
     // Buffer resources based at the tile's first row (KM) or first column (MN).
     const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(A_MN ? A + m0 : A + (size_t)m0 * lda), (short)0, 0x7fffffff, 0x00020000);
@@ -302,21 +319,28 @@ __device__ __forceinline__ void f32_tile(int M, int N, int K, const float *__res
     }
 
     // 32x32 accumulator layout: register r of lane l holds row 8(r/4) + 4(l/32) + r%4,
-    // column l%32 of the block.
+    // column l%32 of the block.  Guarded stores for predicated tiles and for unpredicated
+    // ones that reach past M x N.
+    auto store_all = [&](auto guard_c) {
+        constexpr bool G = decltype(guard_c)::value;
 #pragma unroll
-    for (int i = 0; i < MB; ++i)
+        for (int i = 0; i < MB; ++i)
 #pragma unroll
-        for (int j = 0; j < NB; ++j) {
-            const int row0 = m0 + wm * Cfg::kTM + 32 * i + 4 * lhi, col = n0 + b_rc0 + 32 * j;
-            if constexpr (ACC) store_block32_acc<EDGE, false, false>(acc[i][j], C, ldc, row0, col, M, N, sign, use_old);
-            else store_block32<EDGE, false>(acc[i][j], C, ldc, row0, col, M, N);
-        }
+            for (int j = 0; j < NB; ++j) {
+                const int row0 = m0 + wm * Cfg::kTM + 32 * i + 4 * lhi, col = n0 + b_rc0 + 32 * j;
+                if constexpr (ACC) store_block32_acc<G, false, false>(acc[i][j], C, ldc, row0, col, M, N, sign, use_old);
+                else store_block32<G, false>(acc[i][j], C, ldc, row0, col, M, N);
+            }
+    };
+    if (EDGE || m0 + BM > M || n0 + BN > N) store_all(std::true_type{});
+    else store_all(std::false_type{});
 }
 
-// Tile coordinates of workgroup `bid`.  Interior launches (EDGE false) cover the
-// tiles_m_full x tiles_n_full tiles that lie inside M x N, in XCD-contiguous grouped
-// order.  Edge launches cover either every tile (all_tiles: K is not a multiple of BK)
-// or only the ragged right column strip followed by the ragged bottom row strip.
+// Tile coordinates of workgroup `bid`.  Unpredicated launches (EDGE false) cover, in
+// XCD-contiguous grouped order, the tiles that lie inside M x N, or with all_tiles every
+// tile (ragged ones clamped as above).  Edge launches cover either every tile
+// (all_tiles: K is not a multiple of BK) or only the ragged right column strip followed
+// by the ragged bottom row strip.
 template <bool EDGE>
 __device__ __forceinline__ void tile_of(int bid, int nblocks, int tiles_m, int tiles_n,
                                         bool ragged_n, bool all_tiles, int &tm, int &tn) {
@@ -342,8 +366,8 @@ void mfma_f32_gemm_kernel(int M, int N, int K, const float *__restrict__ A, int 
                           float sign, int use_old, int all_tiles) {
     using Cfg = F32Cfg<BM, BN, WM, WN, A_MN, B_MN>;
     __shared__ __attribute__((aligned(16))) float lds[2 * (Cfg::kLdsA + Cfg::kLdsB)];
-    const int tiles_m = EDGE ? cdiv(M, BM) : M / BM;
-    const int tiles_n = EDGE ? cdiv(N, BN) : N / BN;
+    const int tiles_m = EDGE || all_tiles ? cdiv(M, BM) : M / BM;
+    const int tiles_n = EDGE || all_tiles ? cdiv(N, BN) : N / BN;
     int tm, tn;
     tile_of<EDGE>(blockIdx.x, gridDim.x, tiles_m, tiles_n, N % BN != 0, all_tiles != 0, tm, tn);
     f32_tile<BM, BN, WM, WN, LOAD, EDGE, PAIRED, A_MN, B_MN, ACC>(M, N, K, A, lda, B, ldb, C, ldc,
@@ -356,19 +380,28 @@ struct F32Pick {
     bool vec;
 };
 
+// Whether the unpredicated kernel may take every tile, ragged ones included: K a whole
+// number of k-steps, rows 16-byte aligned, m/n-contiguous extents whole 16-byte chunks.
+inline bool f32_cover_all(const GemmArgs &g, bool vec) {
+    return g.K % kBK == 0 && vec && (!g.trans_a || g.M % 4 == 0) && (g.trans_b || g.N % 4 == 0);
+}
+
 // Cost model: tiles are spread over the 256 CUs, so a config finishes after
 // ceil(tiles / 256) tile-times per CU, each proportional to the tile's area over the
 // efficiency measured for that tile shape on full tiles (64: 0.85, 128 and 192: 0.95 of
-// the MFMA rate); ragged strips run as a second launch at about half that efficiency.
+// the MFMA rate); ragged strips run as a second launch at about half that efficiency,
+// unless the unpredicated kernel takes every tile.
 inline F32Pick pick_f32(const GemmArgs &g) {
     struct Opt { int tile; double eff; };
     const Opt opts[] = {{192, 0.95}, {128, 0.95}, {96, 0.93}, {64, 0.85}};
+    const bool vec = rows_aligned16(g.A, g.lda, 4) && rows_aligned16(g.B, g.ldb, 4);
+    const bool cover = f32_cover_all(g, vec);
     double best = -1.0;
     int tile = 64;
     for (const Opt &o : opts) {
         const long full = (long)(g.M / o.tile) * (g.N / o.tile);
         const long all = (long)cdiv(g.M, o.tile) * cdiv(g.N, o.tile);
-        const long edge = g.K % kBK == 0 ? all - full : all;
+        const long edge = cover ? 0 : (g.K % kBK == 0 ? all - full : all);
         const double area = (double)o.tile * o.tile;
         const double cost = (double)((all - edge + 255) / 256) * area / o.eff +
                             (double)((edge + 255) / 256) * area / (0.5 * o.eff);
@@ -377,7 +410,6 @@ inline F32Pick pick_f32(const GemmArgs &g) {
             tile = o.tile;
         }
     }
-    const bool vec = rows_aligned16(g.A, g.lda, 4) && rows_aligned16(g.B, g.ldb, 4);
     return {tile, vec};
 }
 
@@ -411,6 +443,16 @@ hipError_t launch_cfg(const GemmArgs &g, bool vec, hipStream_t s) {
     const int edge_tiles = cdiv(g.M, BM) * cdiv(g.N, BN) - full_tiles;
     const int all_flag = kfull ? 0 : 1;
     const bool fits = f32_fits(A_MN, BM, g.K, g.lda) && f32_fits(B_MN, BN, g.K, g.ldb);
+    if (!INTERIOR && f32_cover_all(g, vec) && edge_tiles > 0) {
+        // every tile in one unpredicated launch (ragged tiles clamped, stores guarded)
+        if constexpr (!INTERIOR) {
+            const int all = cdiv(g.M, BM) * cdiv(g.N, BN);
+            if (fits && (g.K / kBK) % 2 == 0)
+                return launch_one<BM, BN, WM, WN, MINW, 2, false, true, A_MN, B_MN, ACC>(g, all, 1, s);
+            if (fits) return launch_one<BM, BN, WM, WN, MINW, 2, false, false, A_MN, B_MN, ACC>(g, all, 1, s);
+            return launch_one<BM, BN, WM, WN, MINW, 1, false, false, A_MN, B_MN, ACC>(g, all, 1, s);
+        }
+    }
     if (full_tiles > 0) {
         hipError_t e = hipSuccess;
         if (!INTERIOR && vec && fits && (g.K / kBK) % 2 == 0) {

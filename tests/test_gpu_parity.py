@@ -351,7 +351,32 @@ def test_f32_interior_instances(case):
 # 2 x 4 waves (2048^2), 96 with 1 x 3 waves (1536^2; K tail; ragged M, N and K), 64.
 F32_TILE_CASES = [((1536, 1536, 128), "96x96"), ((1536, 1536, 100), "96x96"),
                   ((1351, 1537, 100), "96x96"), ((2048, 2048, 96), "128x128"),
-                  ((2000, 2048, 64), "64x64"), ((1024, 1024, 64), "64x64")]
+                  ((2000, 2048, 64), "128x128"), ((1024, 1024, 64), "64x64")]
+
+
+# FP32 shapes whose ragged tiles run in the unpredicated kernel with the full tiles (K a
+# multiple of 32, aligned rows, N a multiple of 4): loads clamped to the matrix, stores
+# guarded; NaN padding around the operands would show in a stored output.
+F32_RAGGED_CASES = [((4000, 4000, 512), (4, 8, 4), "128x128"), ((2000, 1996, 256), (0, 0, 0), "128x128"),
+                    ((3000, 3000, 320), (0, 4, 0), "192x192")]
+
+
+@pytest.mark.parametrize("case", F32_RAGGED_CASES, ids=lambda c: "x".join(map(str, c[0])))
+def test_f32_ragged_all_tiles(case):
+    (M, N, K), pad, tile = case
+    lda, ldb, ldc = K + pad[0], N + pad[1], N + pad[2]
+    P = 1 << 20
+    desc = gb.gemm355_kernel_desc(gb.VARIANT_AUTO, gb.F32, M, N, K, P, lda, P, ldb, P, ldc)
+    assert tile in desc and desc.endswith("dwordx4"), desc
+    A, B = inputs.make_operands(M, N, K, 61, "uniform", "f32")
+    C, ok = gpu_gemm(A, B, "f32", entry="typed", pad=pad, guard_rows=1)
+    rows = np.array(sorted(set(sample_rows(M, 96).tolist()) | {M - 1, M - 2, (M // 128) * 128 - 1}))
+    C64, _ = oracle.gemm(np.ascontiguousarray(A[rows]), B)
+    check(C[rows], C64, "f32", "uniform", K, ok, f"f32 ragged all tiles {M}x{N}x{K} sampled")
+    Ai, Bi = inputs.make_operands(M, N, K, 62, "int", "f32")
+    _, C32 = oracle.gemm(np.ascontiguousarray(Ai[rows]), Bi)
+    Ci, ok = gpu_gemm(Ai, Bi, "f32", entry="typed", pad=pad)
+    assert ok and np.array_equal(Ci[rows], C32)
 
 
 @pytest.mark.parametrize("case", F32_TILE_CASES, ids=lambda c: "x".join(map(str, c[0])))
