@@ -1,6 +1,7 @@
 """Every kernel instance compiles for gfx950 without register spills or scratch memory
-and without packed FP32 instructions, and m0 is written only by the direct-to-LDS load
-sequences (checked on the CPU with hipcc)."""
+and without packed FP32 instructions, m0 is written only by the direct-to-LDS load
+sequences, and the accumulators of the inline-assembly MFMAs are touched by nothing but
+those MFMAs between the wait states that fence them (checked on the CPU with hipcc)."""
 
 import concurrent.futures as cf
 import os
@@ -61,23 +62,9 @@ def test_lds_within_160k(remarks):
             assert f.get("LDS Size [bytes/block]", 0) <= 160 * 1024, (fname, name, f)
 
 
-def test_no_packed_fp32_instructions():
-    if not os.path.exists(HIPCC) and shutil.which("hipcc") is None:
-        pytest.skip("hipcc not available")
-    def one(src):
-        r = subprocess.run([HIPCC, *gbuild.HIPFLAGS, "--cuda-device-only", "-S", src, "-o", "-"],
-                           capture_output=True, text=True)
-        assert r.returncode == 0, r.stderr[-2000:]
-        return src, re.findall(r"\bv_pk_(?:fma|mul|add)_f32\b", r.stdout)
-    with cf.ThreadPoolExecutor(min(8, os.cpu_count() or 1)) as ex:
-        for src, bad in ex.map(one, gbuild.sources()):
-            assert not bad, (src, bad[:3])
-
-
-def test_m0_only_in_lds_load_sequences():
-    """The direct-to-LDS loads set m0 from inline assembly without declaring it: in every
-    kernel that contains such a sequence no other instruction may read or write m0, and
-    every m0 write is followed by one wait state and a buffer load with the lds flag."""
+@pytest.fixture(scope="module")
+def assembly():
+    """{source: gfx950 assembly} for every HIP source (compiled once for the tests below)."""
     if not os.path.exists(HIPCC) and shutil.which("hipcc") is None:
         pytest.skip("hipcc not available")
     def one(src):
@@ -85,24 +72,73 @@ def test_m0_only_in_lds_load_sequences():
                            capture_output=True, text=True)
         assert r.returncode == 0, r.stderr[-2000:]
         return src, r.stdout
-    kernels = 0
     with cf.ThreadPoolExecutor(min(8, os.cpu_count() or 1)) as ex:
-        for src, asm in ex.map(one, gbuild.sources()):
-            for body in re.split(r"\n(?=_Z\S+:)", asm):
-                if "offen lds" not in body:
+        return dict(ex.map(one, gbuild.sources()))
+
+
+def test_no_packed_fp32_instructions(assembly):
+    for src, asm in assembly.items():
+        bad = re.findall(r"\bv_pk_(?:fma|mul|add)_f32\b", asm)
+        assert not bad, (src, bad[:3])
+
+
+def test_inline_mfma_accumulators_fenced(assembly):
+    """The direct-to-LDS kernels issue their MFMAs as inline assembly, so the compiler
+    inserts no wait states for them.  In every kernel whose MFMAs are inline assembly,
+    every compiler-generated instruction that names an accumulator register (a copy, a
+    zeroing write, a store) lies either before the two-`s_nop 7` block that precedes the
+    first MFMA or after the four-`s_nop 7` block that follows the last one."""
+    kernels = 0
+    for src, asm in assembly.items():
+        for body in re.split(r"\n(?=_Z\S+:)", asm):
+            lines = [ln.strip() for ln in body.splitlines() if ln.strip()]
+            in_asm, items = False, []  # (instruction, from inline assembly)
+            for ln in lines:
+                if ln.startswith(";;#ASMSTART"):
+                    in_asm = True
+                elif ln.startswith(";;#ASMEND"):
+                    in_asm = False
+                elif not ln.startswith((";", ".")) and not ln.endswith(":"):
+                    items.append((ln, in_asm))
+            mfma = [i for i, (ln, a) in enumerate(items) if a and ln.startswith("v_mfma")]
+            if not mfma:
+                continue
+            kernels += 1
+            first, last = mfma[0], mfma[-1]
+            nops = [i for i, (ln, a) in enumerate(items) if a and ln.startswith("s_nop 7")]
+            pre = [i for i in nops if i < first]
+            post = [i for i in nops if i > last]
+            assert len(pre) >= 2 and len(post) >= 4, (src, body[:80])
+            lo, hi = pre[-2], post[3]
+            for i in range(lo, hi):
+                ln, a = items[i]
+                if a:
                     continue
-                kernels += 1
-                lines = [ln.strip() for ln in body.splitlines()
-                         if ln.strip() and not ln.strip().startswith((";", ".", "//"))]
-                seqs = 0
-                for i, ln in enumerate(lines):
-                    if re.search(r"\bm0\b", ln):
-                        assert re.match(r"s_mov_b32 m0, s\d+$", ln), (src, ln)
-                        assert lines[i + 1] == "s_nop 0", (src, lines[i + 1])
-                        assert re.match(r"buffer_load_dwordx4 v\d+, s\[\d+:\d+\], s\d+ offen lds$",
-                                        lines[i + 2]), (src, lines[i + 2])
-                        seqs += 1
-                    elif ln.endswith(" lds"):
-                        assert lines[i - 1] == "s_nop 0", (src, ln)
-                assert seqs > 0
+                assert not re.search(r"\ba(?:\d+|\[\d+:\d+\])", ln), (src, body[:60], ln)
+    assert kernels >= 40
+
+
+def test_m0_only_in_lds_load_sequences(assembly):
+    """The direct-to-LDS loads set m0 from inline assembly without declaring it: in every
+    kernel that contains such a sequence no other instruction may read or write m0, and
+    every m0 write is followed by one wait state and a buffer load with the lds flag."""
+    kernels = 0
+    for src, asm in assembly.items():
+        for body in re.split(r"\n(?=_Z\S+:)", asm):
+            if "offen lds" not in body:
+                continue
+            kernels += 1
+            lines = [ln.strip() for ln in body.splitlines()
+                     if ln.strip() and not ln.strip().startswith((";", ".", "//"))]
+            seqs = 0
+            for i, ln in enumerate(lines):
+                if re.search(r"\bm0\b", ln):
+                    assert re.match(r"s_mov_b32 m0, s\d+$", ln), (src, ln)
+                    assert lines[i + 1] == "s_nop 0", (src, lines[i + 1])
+                    assert re.match(r"buffer_load_dwordx4 v\d+, s\[\d+:\d+\], s\d+ offen lds$",
+                                    lines[i + 2]), (src, lines[i + 2])
+                    seqs += 1
+                elif ln.endswith(" lds"):
+                    assert lines[i - 1] == "s_nop 0", (src, ln)
+            assert seqs > 0
     assert kernels >= 2
