@@ -19,8 +19,11 @@
 //  * fragment k order: lane l reads A[m][k0+4(l/32) .. +3] with one ds_read_b128 and
 //    feeds element s to MFMA step s, paired with B[k0+4(l/32)+s][n]; each MFMA then
 //    sums k0+s and k0+4+s, and steps s = 0..3 cover k0..k0+7;
-//  * edges: tiles that cross M, N or the K tail load with per-element predicates and
-//    zero fill and store with a guard; interior tiles take the unpredicated path;
+//  * edges: when K is a multiple of BK, rows are 16-byte aligned and m/n-contiguous
+//    extents are multiples of 4, the unpredicated kernel takes every tile, its chunk
+//    coordinates clamped to the matrix and its stores guarded where a tile crosses M or
+//    N; otherwise tiles that cross M, N or the K tail load with per-element predicates
+//    and zero fill, store with a guard, and run as a second launch;
 //  * launch order: tiles are renumbered so each XCD receives a contiguous range, walked
 //    in groups of 4 tile-rows, which keeps shared A and B panels in that XCD's L2;
 //  * operand layouts (the transposed and negated operands and the D-scaled-by-0-or-1 of
