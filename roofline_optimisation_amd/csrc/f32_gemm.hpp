@@ -19,11 +19,12 @@
 //  * fragment k order: lane l reads A[m][k0+4(l/32) .. +3] with one ds_read_b128 and
 //    feeds element s to MFMA step s, paired with B[k0+4(l/32)+s][n]; each MFMA then
 //    sums k0+s and k0+4+s, and steps s = 0..3 cover k0..k0+7;
-//  * edges: when K is a multiple of BK, rows are 16-byte aligned and m/n-contiguous
-//    extents are multiples of 4, the unpredicated kernel takes every tile, its chunk
-//    coordinates clamped to the matrix and its stores guarded where a tile crosses M or
-//    N; otherwise tiles that cross M, N or the K tail load with per-element predicates
-//    and zero fill, store with a guard, and run as a second launch;
+//  * edges: when rows are 16-byte aligned, m/n-contiguous extents are multiples of 4
+//    and K of BK, the unpredicated kernel takes every tile, its chunk coordinates
+//    clamped to the matrix and its stores guarded where a tile crosses M or N; with K a
+//    multiple of 4 but not of BK an instance (KT) also zero-fills the last k-step;
+//    otherwise tiles that cross M, N or the K tail load with per-element predicates and
+//    zero fill, store with a guard, and run as a second launch;
 //  * launch order: tiles are renumbered so each XCD receives a contiguous range, walked
 //    in groups of 4 tile-rows, which keeps shared A and B panels in that XCD's L2;
 //  * operand layouts (the transposed and negated operands and the D-scaled-by-0-or-1 of
@@ -107,8 +108,11 @@ __device__ __forceinline__ floatx4 ld_chunk(const float *__restrict__ row, int c
 // One BM x BN tile of C.  LOAD: 0 = dword loads (rows not 16-byte aligned), 1 = dwordx4
 // through pointers, 2 = dwordx4 through buffer resources (interior tiles, offsets below
 // 2^31 bytes).  EDGE selects the predicated loads and guarded stores.
+// KT (with LOAD 2, unpredicated): K is not a multiple of BK but of 4; the last k-step's
+// chunks past K load from inside the matrix (a row clamped to K-1, or 4 columns clamped
+// to K-4) and are zeroed when staged to LDS.
 template <int BM, int BN, int WM, int WN, int LOAD, bool EDGE, bool PAIRED, bool A_MN, bool B_MN,
-          bool ACC>
+          bool ACC, bool KT = false>
 __device__ __forceinline__ void f32_tile(int M, int N, int K, const float *__restrict__ A, int lda,
                                          const float *__restrict__ B, int ldb,
                                          float *__restrict__ C, int ldc, float sign,
@@ -175,8 +179,23 @@ __device__ __forceinline__ void f32_tile(int M, int N, int K, const float *__res
     };
 
     floatx4 st[kWr];  // staged chunks of the next k-step (A chunks first)
+    static_assert(!KT || (LOAD == 2 && !EDGE), "the K tail rides on the unpredicated buffer loads");
     auto load_one = [&](int k0, int w) {
-        if constexpr (LOAD == 2) {
+        if constexpr (KT) {
+            // the offset carries the k position, clamped into the matrix
+            if (w < kAC) {
+                const int r = A_MN ? min(k0 + a_r[w], K - 1) : a_r[w];
+                const int c = A_MN ? a_c[w] : min(k0 + a_c[w], K - 4);
+                st[w] = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                        ra, (r * lda + c) * 4, 0, 0));
+            } else {
+                const int v = w - kAC;
+                const int r = B_MN ? min(k0 + b_r[v], K - 1) : b_r[v];
+                const int c = B_MN ? b_c[v] : min(k0 + b_c[v], K - 4);
+                st[w] = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                        rb, (r * ldb + c) * 4, 0, 0));
+            }
+        } else if constexpr (LOAD == 2) {
             if (w < kAC)
                 st[w] = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(
                                                         ra, (a_r[w] * lda + a_c[w]) * 4,
@@ -194,13 +213,20 @@ __device__ __forceinline__ void f32_tile(int M, int N, int K, const float *__res
                                  b_c[w - kAC], k0);
         }
     };
-    auto store_one = [&](int buf, int w) {
+    // k0: the first k of the staged k-step (for KT: chunks at or past K are stored as 0)
+    auto store_one = [&](int buf, int w, int k0) {
         float *As = lds + buf * (Cfg::kLdsA + Cfg::kLdsB);
         float *Bs = As + Cfg::kLdsA;
+        floatx4 v = st[w];
+        if constexpr (KT) {
+            const int kk = w < kAC ? k0 + (A_MN ? a_r[w] : a_c[w])
+                                   : k0 + (B_MN ? b_r[w - kAC] : b_c[w - kAC]);
+            if (kk >= K) v = floatx4{0.f, 0.f, 0.f, 0.f};
+        }
         if (w < kAC)
-            *reinterpret_cast<floatx4 *>(As + a_r[w] * OA::kStride + a_c[w]) = st[w];
+            *reinterpret_cast<floatx4 *>(As + a_r[w] * OA::kStride + a_c[w]) = v;
         else
-            *reinterpret_cast<floatx4 *>(Bs + b_r[w - kAC] * OB::kStride + b_c[w - kAC]) = st[w];
+            *reinterpret_cast<floatx4 *>(Bs + b_r[w - kAC] * OB::kStride + b_c[w - kAC]) = v;
     };
 
     floatx16 acc[MB][NB];
@@ -260,7 +286,7 @@ __device__ __forceinline__ void f32_tile(int M, int N, int K, const float *__res
 #pragma unroll
         for (int w = 0; w < kWr; ++w) load_one(0, w);
 #pragma unroll
-        for (int w = 0; w < kWr; ++w) store_one(0, w);
+        for (int w = 0; w < kWr; ++w) store_one(0, w, 0);
         __syncthreads();
 #pragma unroll
         for (int w = 0; w < kWr; ++w) load_one(min(1, nk - 1) * kBK, w);
@@ -286,7 +312,8 @@ __device__ __forceinline__ void f32_tile(int M, int N, int K, const float *__res
             for (int q = 0; q < kPre; ++q) {
                 mfma_one(sl, q);
 #pragma unroll
-                for (int w = q * kWr / kPre; w < (q + 1) * kWr / kPre; ++w) store_one(buf ^ 1, w);
+                for (int w = q * kWr / kPre; w < (q + 1) * kWr / kPre; ++w)
+                    store_one(buf ^ 1, w, min(kt + 1, nk - 1) * kBK);
                 __builtin_amdgcn_sched_barrier(0);
             }
             __syncthreads();
@@ -362,7 +389,7 @@ __device__ __forceinline__ void tile_of(int bid, int nblocks, int tiles_m, int t
 }
 
 template <int BM, int BN, int WM, int WN, int MINW, int LOAD, bool EDGE, bool PAIRED, bool A_MN,
-          bool B_MN, bool ACC>
+          bool B_MN, bool ACC, bool KT = false>
 __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(MINW)))
 void mfma_f32_gemm_kernel(int M, int N, int K, const float *__restrict__ A, int lda,
                           const float *__restrict__ B, int ldb, float *__restrict__ C, int ldc,
@@ -373,7 +400,7 @@ void mfma_f32_gemm_kernel(int M, int N, int K, const float *__restrict__ A, int 
     const int tiles_n = EDGE || all_tiles ? cdiv(N, BN) : N / BN;
     int tm, tn;
     tile_of<EDGE>(blockIdx.x, gridDim.x, tiles_m, tiles_n, N % BN != 0, all_tiles != 0, tm, tn);
-    f32_tile<BM, BN, WM, WN, LOAD, EDGE, PAIRED, A_MN, B_MN, ACC>(M, N, K, A, lda, B, ldb, C, ldc,
+    f32_tile<BM, BN, WM, WN, LOAD, EDGE, PAIRED, A_MN, B_MN, ACC, KT>(M, N, K, A, lda, B, ldb, C, ldc,
                                                                  sign, use_old, tm * BM, tn * BN,
                                                                  lds);
 }
@@ -389,6 +416,12 @@ inline bool f32_cover_all(const GemmArgs &g, bool vec) {
     return g.K % kBK == 0 && vec && (!g.trans_a || g.M % 4 == 0) && (g.trans_b || g.N % 4 == 0);
 }
 
+// The same with a K tail (K a multiple of 4 but not of BK): the KT kernel.
+inline bool f32_ktail(const GemmArgs &g, bool vec) {
+    return g.K % kBK != 0 && g.K % 4 == 0 && vec && (!g.trans_a || g.M % 4 == 0) &&
+           (g.trans_b || g.N % 4 == 0);
+}
+
 // Cost model: tiles are spread over the 256 CUs, so a config finishes after
 // ceil(tiles / 256) tile-times per CU, each proportional to the tile's area over the
 // efficiency measured for that tile shape on full tiles (64: 0.85, 128 and 192: 0.95 of
@@ -398,7 +431,7 @@ inline F32Pick pick_f32(const GemmArgs &g) {
     struct Opt { int tile; double eff; };
     const Opt opts[] = {{192, 0.95}, {128, 0.95}, {96, 0.93}, {64, 0.85}};
     const bool vec = rows_aligned16(g.A, g.lda, 4) && rows_aligned16(g.B, g.ldb, 4);
-    const bool cover = f32_cover_all(g, vec);
+    const bool cover = f32_cover_all(g, vec) || f32_ktail(g, vec);
     double best = -1.0;
     int tile = 64;
     for (const Opt &o : opts) {
@@ -417,9 +450,9 @@ inline F32Pick pick_f32(const GemmArgs &g) {
 }
 
 template <int BM, int BN, int WM, int WN, int MINW, int LOAD, bool EDGE, bool PAIRED, bool A_MN,
-          bool B_MN, bool ACC>
+          bool B_MN, bool ACC, bool KT = false>
 hipError_t launch_one(const GemmArgs &g, int tiles, int all_flag, hipStream_t s) {
-    hipLaunchKernelGGL((mfma_f32_gemm_kernel<BM, BN, WM, WN, MINW, LOAD, EDGE, PAIRED, A_MN, B_MN, ACC>),
+    hipLaunchKernelGGL((mfma_f32_gemm_kernel<BM, BN, WM, WN, MINW, LOAD, EDGE, PAIRED, A_MN, B_MN, ACC, KT>),
                        dim3(tiles), dim3(64 * WM * WN), 0, s, g.M, g.N, g.K, (const float *)g.A,
                        g.lda, (const float *)g.B, g.ldb, g.C, g.ldc, g.sign, g.accumulate, all_flag);
     return hipGetLastError();
@@ -446,6 +479,11 @@ hipError_t launch_cfg(const GemmArgs &g, bool vec, hipStream_t s) {
     const int edge_tiles = cdiv(g.M, BM) * cdiv(g.N, BN) - full_tiles;
     const int all_flag = kfull ? 0 : 1;
     const bool fits = f32_fits(A_MN, BM, g.K, g.lda) && f32_fits(B_MN, BN, g.K, g.ldb);
+    if constexpr (!INTERIOR) {
+        if (f32_ktail(g, vec) && fits)  // every tile, K tail included, in one launch
+            return launch_one<BM, BN, WM, WN, MINW, 2, false, false, A_MN, B_MN, ACC, true>(
+                g, cdiv(g.M, BM) * cdiv(g.N, BN), 1, s);
+    }
     if (!INTERIOR && f32_cover_all(g, vec) && edge_tiles > 0) {
         // every tile in one unpredicated launch (ragged tiles clamped, stores guarded)
         if constexpr (!INTERIOR) {

@@ -112,10 +112,11 @@ def test_flag_matrix_ragged(fl, dtype, variant):
 LAYOUTS = list(itertools.product([False, True], repeat=2))
 MODES = [(False, False, False), (True, False, False), (False, True, True)]  # na, nb, acc
 SHAPES = {"f32": [(3072, 3072, 64), (1024, 768, 96), (2048, 2048, 64), (1536, 1536, 96), (1351, 1537, 100),
-                  (2000, 1996, 256)],
+                  (2000, 1996, 256), (2000, 1996, 260)],
           "f16": [(3072, 3072, 128), (3072, 2816, 192), (1024, 1024, 128), (4000, 3992, 128)],
           "bf16": [(3072, 3072, 256), (1024, 512, 64), (2000, 2040, 256)]}
-# FP32 (2000, 1996, 256): ragged tiles in the unpredicated kernel with the full ones.
+# FP32 (2000, 1996, 256) and (2000, 1996, 260): ragged tiles in the unpredicated kernel
+# with the full ones, the latter with a zero-filled last k-step.
 # (4000, 3992, 128) and (2000, 2040, 256): every tile, ragged ones included, on the
 # direct-to-LDS kernel (256 x 256 and 128 x 128 tiles); the padding around the operands
 # holds NaN, so a ragged tile's loads past the matrix would show in its stored outputs.

@@ -354,11 +354,15 @@ F32_TILE_CASES = [((1536, 1536, 128), "96x96"), ((1536, 1536, 100), "96x96"),
                   ((2000, 2048, 64), "128x128"), ((1024, 1024, 64), "64x64")]
 
 
-# FP32 shapes whose ragged tiles run in the unpredicated kernel with the full tiles (K a
-# multiple of 32, aligned rows, N a multiple of 4): loads clamped to the matrix, stores
-# guarded; NaN padding around the operands would show in a stored output.
+# FP32 shapes whose ragged tiles run in the unpredicated kernel with the full tiles
+# (aligned rows, N a multiple of 4, K a multiple of 32 or, with a zero-filled last
+# k-step, of 4): loads clamped to the matrix, stores guarded; NaN padding around the
+# operands would show in a stored output.
 F32_RAGGED_CASES = [((4000, 4000, 512), (4, 8, 4), "128x128"), ((2000, 1996, 256), (0, 0, 0), "128x128"),
-                    ((3000, 3000, 320), (0, 4, 0), "192x192")]
+                    ((3000, 3000, 320), (0, 4, 0), "192x192"),
+                    # K not a multiple of 32 (but of 4): the last k-step zero-filled
+                    ((3000, 3000, 3000), (0, 0, 0), "192x192"), ((1000, 1000, 1000), (4, 4, 0), "64x64"),
+                    ((2048, 2048, 1028), (8, 0, 4), "128x128")]
 
 
 @pytest.mark.parametrize("case", F32_RAGGED_CASES, ids=lambda c: "x".join(map(str, c[0])))
