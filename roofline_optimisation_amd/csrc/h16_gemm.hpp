@@ -31,14 +31,15 @@
 //    old C (loaded block by block in the epilogue) when accumulating; 2 does the same
 //    with C in the operands' 16-bit type (old C widened, result rounded to nearest even).
 //
-// Interior 256 x 256 tiles with K a multiple of 128 take a second design (dma_tile in
-// h16_dma.hpp): the tiles go from memory straight into LDS (buffer_load_dwordx4 ... lds)
-// through a four-stage ring, so no registers stage them and no LDS store instructions
-// are issued; LDS rows are XOR-swizzled instead of padded; the arithmetic is
-// v_mfma_f32_16x16x32 on 16 x 16 accumulator quads.  Its MFMAs sum each 32-wide k-step
-// in one instruction where this kernel's take two 16-wide ones, so the two kernels'
-// results may differ in rounding (both are within the FP32-accumulation tolerance; on
-// integer-valued inputs both are exact).
+// Square 256 x 256 or 128 x 128 tiles take a second design (dma_tile in h16_dma.hpp)
+// when K is a whole number of its ring's trips (128 or 256) and the m/n-contiguous
+// extents are multiples of 8; ragged tiles included: the tiles go from memory straight
+// into LDS (buffer_load_dwordx4 ... lds) through a ring of k-steps, so no registers stage
+// them and no LDS store instructions are issued; LDS rows are XOR-swizzled instead of
+// padded; the arithmetic is v_mfma_f32_16x16x32 on 16 x 16 accumulator quads.  Its MFMAs
+// sum each 32-wide k-step in one instruction where this kernel's take two 16-wide ones,
+// so the two kernels' results may differ in rounding (both are within the
+// FP32-accumulation tolerance; on integer-valued inputs both are exact).
 #pragma once
 
 #include <type_traits>
