@@ -55,11 +55,43 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def strip_comments(src: str) -> str:
+    """C++ source without its comments, blank lines and layout whitespace (string and
+    character literals kept as they are), so that an edit of comments or indentation
+    leaves the hash of a kernel's code unchanged."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):
+            while i < n and src[i] != "\n":
+                i += 1
+        elif src.startswith("/*", i):
+            e = src.find("*/", i + 2)
+            i = n if e < 0 else e + 2
+            out.append(" ")
+        elif c in " \t":
+            if out and out[-1] != " ":
+                out.append(" ")
+            i += 1
+        else:
+            out.append(c)
+            i += 1
+    lines = (ln.strip() for ln in "".join(out).split("\n"))
+    return "\n".join(ln for ln in lines if ln)
+
+
 def kernel_hash(kind: str) -> str:
+    """Hash of the code (comments stripped) of the sources a kernel family is built from."""
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[kind]:
-        with open(os.path.join(CSRC, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(CSRC, f), encoding="utf-8") as fh:
+            h.update(strip_comments(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -106,3 +106,22 @@ def test_text_chart_places_points_and_roofs():
     r157 = [i for i, l in enumerate(body) if l.rstrip().endswith("-")]
     assert r157 and all(body[r157[0]][c] in "-b" for c in range(20, 40))
     assert any("b" in l for l in body)
+
+
+def test_kernel_hash_ignores_comments_only():
+    """The counter summaries are matched to the kernel code by a hash of the sources with
+    comments stripped: comment edits keep it, any code edit (strings included) moves it."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "bench_host", os.path.join(os.path.dirname(os.path.dirname(__file__)), "bench.py"))
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    src = 'int f(int x) {  // add one\n  /* block\n comment */ return x + 1;\n}\nconst char* s = "a//b";\n'
+    same = '// header\nint f(int x) {\n\n  return x + 1; /* c */\n}\nconst char* s = "a//b";  // tail\n'
+    assert bench.strip_comments(src) == bench.strip_comments(same)
+    assert "a//b" in bench.strip_comments(src)
+    for edit in (src.replace("x + 1", "x + 2"), src.replace("a//b", "a/b"),
+                 src.replace("x) {", "x) {\n  x++;")):
+        assert bench.strip_comments(edit) != bench.strip_comments(src)
+    for kind in bench.KERNEL_SOURCES:
+        assert len(bench.kernel_hash(kind)) == 16
