@@ -94,20 +94,24 @@ __device__ __forceinline__ floatx4 ld_chunk(const float *__restrict__ row, int c
                                             bool row_ok) {
     if (!EDGE) {
         if (VEC) return *reinterpret_cast<const floatx4 *>(row + c);
-        return floatx4{row[c], row[c + 1], row[c + 2], row[c + 3]};
+        return *reinterpret_cast<const floatx4_ua *>(row + c);
     }
     floatx4 v = {0.f, 0.f, 0.f, 0.f};
     if (!row_ok) return v;
-    if (VEC && c + 4 <= ncols) return *reinterpret_cast<const floatx4 *>(row + c);
+    if (c + 4 <= ncols)
+        return VEC ? *reinterpret_cast<const floatx4 *>(row + c)
+                   : *reinterpret_cast<const floatx4_ua *>(row + c);
 #pragma unroll
     for (int e = 0; e < 4; ++e)
         if (c + e < ncols) v[e] = row[c + e];
     return v;
 }
 
-// One BM x BN tile of C.  LOAD: 0 = dword loads (rows not 16-byte aligned), 1 = dwordx4
-// through pointers, 2 = dwordx4 through buffer resources (interior tiles, offsets below
-// 2^31 bytes).  EDGE selects the predicated loads and guarded stores.
+// One BM x BN tile of C.  LOAD: 0 = dwordx4 at 4-byte alignment (rows not 16-byte
+// aligned), 1 = dwordx4 through pointers, 2 = dwordx4 through buffer resources (interior
+// tiles, offsets below 2^31 bytes).  EDGE selects the predicated loads and guarded
+// stores.  (Clamped loads fixed up when staged, as in the 16-bit kernel, measured 3-15 %
+// slower here than these predicated loads.)
 // KT (with LOAD 2, unpredicated): K is not a multiple of BK but of 4; the last k-step's
 // chunks past K load from inside the matrix (a row clamped to K-1, or 4 columns clamped
 // to K-4) and are zeroed when staged to LDS.

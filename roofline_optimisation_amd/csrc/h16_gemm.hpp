@@ -119,14 +119,42 @@ __device__ __forceinline__ u16x8 join(shortx4 lo, shortx4 hi) {
 template <bool VEC, bool EDGE>
 __device__ __forceinline__ u16x8 ld_chunk8(const uint16_t *__restrict__ row, int c, int ncols,
                                            bool row_ok) {
-    if (!EDGE && VEC) return *reinterpret_cast<const u16x8 *>(row + c);
+    if (!EDGE || (row_ok && c + 8 <= ncols))
+        return VEC ? *reinterpret_cast<const u16x8 *>(row + c)
+                   : *reinterpret_cast<const u16x8_ua *>(row + c);
     u16x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (EDGE && !row_ok) return v;
-    if (EDGE && VEC && c + 8 <= ncols) return *reinterpret_cast<const u16x8 *>(row + c);
+    if (!row_ok) return v;
 #pragma unroll
     for (int e = 0; e < 8; ++e)
         if (!EDGE || c + e < ncols) v[e] = row[c + e];
     return v;
+}
+
+// Ragged-tile chunks without branches: the load reads the 8 elements at column
+// min(c, ncols - 8) of row min(r, nrows - 1), always inside the matrix (ncols >= 8), and
+// the staging to LDS moves element c + e down to slot e (shift d = c - clamped column)
+// and zeroes the slots past the row's end or of a row past the matrix (nv = elements
+// kept).  Loads and fix-ups are apart in time, so the loads stay in flight like the
+// interior kernel's.
+struct ChunkPos { int row, col, nrows, ncols; };
+
+__device__ __forceinline__ u16x8 fix_chunk8(u16x8 v, int d, int nv) {
+    const u32x4 w = __builtin_bit_cast(u32x4, v);
+    const int q = min(d, 7) >> 1;
+    const bool h = (d & 1) != 0;
+    uint32_t x[5];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        x[i] = i + q >= 3 ? w[3] : i + q == 2 ? w[2] : i + q == 1 ? w[1] : w[0];
+    x[4] = w[3];
+    u32x4 y;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t sh = __builtin_amdgcn_alignbit(x[i + 1], x[i], 16);
+        const uint32_t m = 2 * i + 1 < nv ? 0xffffffffu : 2 * i < nv ? 0x0000ffffu : 0u;
+        y[i] = (h ? sh : x[i]) & m;
+    }
+    return __builtin_bit_cast(u16x8, y);
 }
 
 // Fragment registers of one operand: a KM fragment is one ds_read_b128, an MN fragment
@@ -144,8 +172,11 @@ struct H16Frag<true, NBLK> {
     }
 };
 
-// LOAD: 0 = 16-bit loads (rows not 16-byte aligned), 1 = dwordx4 through pointers,
-// 2 = dwordx4 through buffer resources (interior tiles, offsets below 2^31 bytes).
+// LOAD: 0 = dwordx4 at 2-byte alignment (rows not 16-byte aligned), 1 = dwordx4
+// through pointers, 2 = dwordx4 through buffer resources (interior tiles, offsets
+// below 2^31 bytes), 3 (ragged tiles, contiguous extents of at least 8) = dwordx4 at
+// 2-byte alignment clamped into the matrix, fixed up when staged (fix_chunk8); the
+// predicated ragged kernel (EDGE with LOAD 0 or 1) branches per element instead.
 template <typename T, int BM, int BN, int WM, int WN, int LOAD, bool EDGE, bool PAIRED,
           bool A_MN, bool B_MN, int EPI>
 __device__ __forceinline__ void h16_tile(int M, int N, int K, const uint16_t *__restrict__ A,
@@ -191,9 +222,28 @@ __device__ __forceinline__ void h16_tile(int M, int N, int K, const uint16_t *__
         return ld_chunk8<LOAD == 1, EDGE>(X + (size_t)(ok ? row : 0) * ld, col,
                                           kMN ? MNext : K, ok);
     };
+    // LOAD 3: chunk (r, c) of the k-step at k0 as a position in its operand.
+    auto chunk_pos = [&](auto mn_c, int mn0, int MNext, int r, int c, int k0) -> ChunkPos {
+        constexpr bool kMN = decltype(mn_c)::value;
+        return kMN ? ChunkPos{k0 + r, mn0 + c, K, MNext} : ChunkPos{mn0 + r, k0 + c, MNext, K};
+    };
+    auto pos_of = [&](int w, int k0) -> ChunkPos {
+        if (w < kAC)
+            return chunk_pos(std::integral_constant<bool, A_MN>{}, m0, M, a_r0 + w * OA::kRowStep, a_c0, k0);
+        return chunk_pos(std::integral_constant<bool, B_MN>{}, n0, N,
+                         b_r0 + (w - kAC) * OB::kRowStep, b_c0, k0);
+    };
     auto load_one = [&](auto set_c, int k0, int w) {
         constexpr int S = decltype(set_c)::value;
-        if constexpr (LOAD == 2) {
+        if constexpr (LOAD == 3) {
+            const ChunkPos p = pos_of(w, k0);
+            const uint16_t *X = w < kAC ? A : B;
+            const int ld = w < kAC ? lda : ldb;
+            const u16x8 v = *reinterpret_cast<const u16x8_ua *>(
+                X + (size_t)min(p.row, p.nrows - 1) * ld + min(p.col, p.ncols - 8));
+            if (w < kAC) sa[S][w] = v;
+            else sb[S][w - kAC] = v;
+        } else if constexpr (LOAD == 2) {
             if (w < kAC) {
                 const int so = A_MN ? (k0 + w * OA::kRowStep) * lda * 2
                                     : (w * OA::kRowStep * lda + k0) * 2;
@@ -220,12 +270,21 @@ __device__ __forceinline__ void h16_tile(int M, int N, int K, const uint16_t *__
                               lds_base(L + kStage + a_r0 * OA::kStride + a_c0)};
     lds_u16 *const b_wr[2] = {lds_base(L + Cfg::kLdsA + b_r0 * OB::kStride + b_c0),
                               lds_base(L + kStage + Cfg::kLdsA + b_r0 * OB::kStride + b_c0)};
-    auto store_one = [&](auto set_c, int buf, int w) {
+    // k0: the first k of the staged k-step (LOAD 3 recomputes the chunk's fix-up from it)
+    auto store_one = [&](auto set_c, int buf, int w, int k0) {
         constexpr int S = decltype(set_c)::value;
+        u16x8 v = w < kAC ? sa[S][w] : sb[S][w - kAC];
+        if constexpr (LOAD == 3) {
+            const ChunkPos p = pos_of(w, k0);
+            const int nv = p.row < p.nrows ? min(max(p.ncols - p.col, 0), 8) : 0;
+            v = fix_chunk8(v, p.col - min(p.col, p.ncols - 8), nv);
+        } else {
+            (void)k0;
+        }
         if (w < kAC)
-            *(lds_u16x8 *)(a_wr[buf] + w * OA::kRowStep * OA::kStride) = sa[S][w];
+            *(lds_u16x8 *)(a_wr[buf] + w * OA::kRowStep * OA::kStride) = v;
         else
-            *(lds_u16x8 *)(b_wr[buf] + (w - kAC) * OB::kRowStep * OB::kStride) = sb[S][w - kAC];
+            *(lds_u16x8 *)(b_wr[buf] + (w - kAC) * OB::kRowStep * OB::kStride) = v;
     };
 
     floatx16 acc[MB][NB];
@@ -314,6 +373,7 @@ __device__ __forceinline__ void h16_tile(int M, int N, int K, const uint16_t *__
     const int nk = cdiv(K, kBK);
     auto kstep = [&](auto set_c, auto other_c, int kt, int buf) {
         const int kload = min(kt + 2, nk - 1) * kBK;
+        const int kstore = min(kt + 1, nk - 1) * kBK;  // the k-step held in set S
 #pragma unroll
         for (int s = 0; s < kSteps; ++s) {
 #pragma unroll
@@ -337,7 +397,7 @@ __device__ __forceinline__ void h16_tile(int M, int N, int K, const uint16_t *__
                 const int w_hi = ev_begin(qs + 1, kWr, kStoreLo, kStoreHi);
 #pragma unroll
                 for (int w = w_lo; w < w_hi; ++w) {
-                    store_one(set_c, buf ^ 1, w);
+                    store_one(set_c, buf ^ 1, w, kstore);
                     if constexpr (!PAIRED) load_one(set_c, kload, w);
                 }
             }
@@ -359,7 +419,7 @@ __device__ __forceinline__ void h16_tile(int M, int N, int K, const uint16_t *__
 #pragma unroll
         for (int w = 0; w < kWr; ++w) load_one(S0{}, 0, w);
 #pragma unroll
-        for (int w = 0; w < kWr; ++w) store_one(S0{}, 0, w);
+        for (int w = 0; w < kWr; ++w) store_one(S0{}, 0, w, 0);
         __syncthreads();
 #pragma unroll
         for (int w = 0; w < kWr; ++w) load_one(S1{}, min(1, nk - 1) * kBK, w);
@@ -485,7 +545,8 @@ hipError_t launch_one(const GemmArgs &g, int tiles, int all_flag, hipStream_t s)
 
 // Interior tiles: direct-to-LDS loads (256 x 256, K % 128 == 0), else buffer loads when
 // rows are 16-byte aligned and every offset fits in 31 bits, with the two-set pipeline
-// when the number of k-steps is even; ragged strips: predicated pointer loads.  The
+// when the number of k-steps is even; ragged strips: clamped loads fixed up when staged
+// (predicated element loads when a contiguous extent is below 8).  The
 // signed / accumulating epilogues (EPI 1, 2) keep to the direct-to-LDS and pointer-load
 // kernels, which bounds the number of instances.
 template <typename T, int BM, int BN, int WM, int WN, int MINW, bool A_MN, bool B_MN, int EPI>
@@ -505,6 +566,16 @@ hipError_t launch_cfg(const GemmArgs &g, hipStream_t s) {
             return hipGetLastError();
         }
     }
+    // Clamped loads need 8 elements along each operand's contiguous extent.  With them
+    // the ragged-tile kernel can take every tile in one launch; its tiles run about 1.5x
+    // as long as interior ones (one staging set, fix-ups), so it does when that takes
+    // less time than the interior launch followed by the ragged strips' launch.
+    const bool clamp = (A_MN ? g.M : g.K) >= 8 && (B_MN ? g.N : g.K) >= 8;
+    if (clamp && full_tiles > 0 && edge_tiles > 0) {
+        const int all = full_tiles + edge_tiles;
+        if (cdiv(all, 256) * 3 < cdiv(full_tiles, 256) * 2 + cdiv(edge_tiles, 256) * 3)
+            return launch_one<T, BM, BN, WM, WN, MINW, 3, true, false, A_MN, B_MN, EPI>(g, all, 1, s);
+    }
     if (full_tiles > 0) {
         hipError_t e = hipSuccess;
         if (EPI == 0 && vec && fits) {
@@ -522,6 +593,13 @@ hipError_t launch_cfg(const GemmArgs &g, hipStream_t s) {
         if (e != hipSuccess) return e;
     }
     if (edge_tiles > 0) {
+        // Whole tiles with only K ragged (by a multiple of 8) and aligned rows never take
+        // the predicated loads' element paths, which then run faster than the fix-ups
+        // (4096 x 4096 x 4000 BF16: 142 against 174 us); any row or column past the
+        // matrix makes them the slower ones (4000^3: 298 against 178 us).
+        const bool whole = vec && g.M % BM == 0 && g.N % BN == 0 && g.K % 8 == 0;
+        if (clamp && !whole)
+            return launch_one<T, BM, BN, WM, WN, MINW, 3, true, false, A_MN, B_MN, EPI>(g, edge_tiles, all_flag, s);
         if (vec) return launch_one<T, BM, BN, WM, WN, MINW, 1, true, false, A_MN, B_MN, EPI>(g, edge_tiles, all_flag, s);
         return launch_one<T, BM, BN, WM, WN, MINW, 0, true, false, A_MN, B_MN, EPI>(g, edge_tiles, all_flag, s);
     }

@@ -23,13 +23,13 @@ const char *desc_mfma_f16(int dtype, const GemmArgs &g) {
     if (!big && !narrow && use_dma(g, 128))
         return dtype == kF16 ? "mfma_f16 128x128x32 w2x2 lds-dma" : "mfma_bf16 128x128x32 w2x2 lds-dma";
     if (dtype == kF16) {
-        if (big) return v ? "mfma_f16 256x256x64 w2x2 dwordx4" : "mfma_f16 256x256x64 w2x2 u16";
-        if (narrow) return v ? "mfma_f16 128x64x64 w2x2 dwordx4" : "mfma_f16 128x64x64 w2x2 u16";
-        return v ? "mfma_f16 128x128x64 w2x2 dwordx4" : "mfma_f16 128x128x64 w2x2 u16";
+        if (big) return v ? "mfma_f16 256x256x64 w2x2 dwordx4" : "mfma_f16 256x256x64 w2x2 dwordx4 unaligned";
+        if (narrow) return v ? "mfma_f16 128x64x64 w2x2 dwordx4" : "mfma_f16 128x64x64 w2x2 dwordx4 unaligned";
+        return v ? "mfma_f16 128x128x64 w2x2 dwordx4" : "mfma_f16 128x128x64 w2x2 dwordx4 unaligned";
     }
-    if (big) return v ? "mfma_bf16 256x256x64 w2x2 dwordx4" : "mfma_bf16 256x256x64 w2x2 u16";
-    if (narrow) return v ? "mfma_bf16 128x64x64 w2x2 dwordx4" : "mfma_bf16 128x64x64 w2x2 u16";
-    return v ? "mfma_bf16 128x128x64 w2x2 dwordx4" : "mfma_bf16 128x128x64 w2x2 u16";
+    if (big) return v ? "mfma_bf16 256x256x64 w2x2 dwordx4" : "mfma_bf16 256x256x64 w2x2 dwordx4 unaligned";
+    if (narrow) return v ? "mfma_bf16 128x64x64 w2x2 dwordx4" : "mfma_bf16 128x64x64 w2x2 dwordx4 unaligned";
+    return v ? "mfma_bf16 128x128x64 w2x2 dwordx4" : "mfma_bf16 128x128x64 w2x2 dwordx4 unaligned";
 }
 
 hipError_t launch_mfma_f16(int dtype, const GemmArgs &g, hipStream_t s) {

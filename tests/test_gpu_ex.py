@@ -134,15 +134,15 @@ def test_tiles_every_layout(dtype, shape, layout, mode):
 @pytest.mark.parametrize("pad", [(0, 0, 0), (1, 3, 2)], ids=["packed", "unaligned"])
 def test_f32_both_mn_whole_192_tiles(pad, mode):
     """A transposed, B not (both operands m/n-contiguous) with M, N multiples of 192: the
-    192 x 192 tile's unpaired interior kernels, an odd number of k-steps, 16-byte and
-    scalar loads."""
+    192 x 192 tile's unpaired interior kernels, an odd number of k-steps, 16-byte loads
+    at 16-byte and at element alignment."""
     compare(1152, 1536, 96, "f32", True, False, *mode, seed=66, pad=pad)
 
 
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
 @pytest.mark.parametrize("layout", LAYOUTS, ids=lambda l: f"ta{int(l[0])}tb{int(l[1])}")
 def test_unaligned_strides(dtype, layout):
-    """Row strides that are not multiples of 16 bytes take the narrow-load paths."""
+    """Row strides that are not multiples of 16 bytes take 16-byte loads at element alignment."""
     compare(300, 260, 130, dtype, *layout, False, False, True, seed=52, pad=(1, 3, 2))
 
 

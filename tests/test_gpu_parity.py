@@ -235,7 +235,7 @@ def test_torch_matmul_wrapper():
 
 # Interior-tile instances of the 16-bit kernel: an even number of 64-wide k-steps
 # (paired staging), an odd number, a single k-step, rows that are not 16-byte
-# aligned (16-bit loads), and a misaligned base; each with M, N multiples of the tile.
+# aligned (16-byte loads at element alignment), and a misaligned base; each with M, N multiples of the tile.
 INTERIOR_CASES = [((512, 512, 256), (0, 0, 0), 0), ((512, 512, 320), (0, 0, 0), 0),
                   ((256, 256, 64), (0, 0, 0), 0), ((512, 256, 256), (1, 3, 0), 0),
                   ((256, 512, 128), (0, 0, 0), 1), ((1024, 768, 192), (8, 8, 8), 0)]
@@ -335,6 +335,34 @@ def test_h16_dma_interior_with_edges():
     rows = np.array(sorted(set(sample_rows(M, 48).tolist()) | {3839, 3840, 3999}))
     C64, _ = oracle.gemm(np.ascontiguousarray(A[rows]), B, "bf16")
     check(C[rows], C64, "bf16", "uniform", K, ok, "dma+edge bf16 4000x4000x256 sampled")
+
+
+# Ragged tiles of the register-staged 16-bit kernel with clamped loads (each chunk read
+# from inside the matrix and shifted / zeroed when staged to LDS): an n-contiguous extent
+# that is not a multiple of 8 (one launch over every tile), rows that are not 16-byte
+# aligned with K ragged by a non-multiple of 8, odd strides, and more tiles than CUs
+# (interior launch, then the ragged strips).  512 x 768 x 200 (whole tiles, K ragged by
+# a multiple of 8, aligned rows) keeps the predicated loads.
+CLAMP_CASES = [((4000, 4004, 256), (0, 0, 0), "all"), ((1000, 1000, 1000), (1, 0, 0), "all"),
+               ((777, 1030, 301), (3, 5, 0), "all"), ((8000, 8004, 64), (0, 0, 0), "rows"),
+               ((512, 768, 200), (0, 0, 0), "all")]
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("case", CLAMP_CASES, ids=lambda c: "x".join(map(str, c[0])) + f"_pad{c[1][0]}{c[1][1]}")
+def test_h16_clamped_ragged(dtype, case):
+    (M, N, K), pad, cmp = case
+    A, B = inputs.make_operands(M, N, K, 47, "uniform", dtype)
+    C, ok = gpu_gemm(A, B, dtype, gb.VARIANT_MFMA, pad=pad, guard_rows=1)
+    rows = np.arange(M) if cmp == "all" else np.array(sorted(
+        set(sample_rows(M, 48).tolist()) | {M - 65, M - 64, M - 1}))
+    C64, _ = oracle.gemm(np.ascontiguousarray(A[rows]), B, dtype)
+    check(C[rows], C64, dtype, "uniform", K, ok, f"clamped {dtype} {M}x{N}x{K} pad={pad}")
+    if cmp == "all":
+        Ai, Bi = inputs.make_operands(M, N, K, 48, "int", dtype)
+        _, C32 = oracle.gemm(Ai, Bi, dtype)
+        Ci, ok = gpu_gemm(Ai, Bi, dtype, gb.VARIANT_MFMA, pad=pad)
+        assert ok and np.array_equal(Ci, C32)
 
 
 @pytest.mark.parametrize("case", [(384, 384, 64), (768, 384, 96), (384, 576, 3072)],
