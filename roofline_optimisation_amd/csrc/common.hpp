@@ -15,10 +15,9 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef short shortx4 __attribute__((ext_vector_type(4)));
-// 16-byte chunks at element alignment only (rows whose stride is not a multiple of 16
-// bytes): gfx950 under the HSA ABI runs with unaligned global access enabled, so these
-// still load with one global_load_dwordx4.
-typedef float floatx4_ua __attribute__((ext_vector_type(4), aligned(4)));
+// 16-byte chunks of 16-bit elements at element alignment only (rows whose stride is not
+// a multiple of 16 bytes): gfx950 under the HSA ABI runs with unaligned global access
+// enabled, so these still load with one global_load_dwordx4.
 typedef uint16_t u16x8_ua __attribute__((ext_vector_type(8), aligned(2)));
 
 enum DType : int { kF32 = 0, kF16 = 1, kBF16 = 2 };

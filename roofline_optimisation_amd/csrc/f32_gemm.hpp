@@ -94,24 +94,22 @@ __device__ __forceinline__ floatx4 ld_chunk(const float *__restrict__ row, int c
                                             bool row_ok) {
     if (!EDGE) {
         if (VEC) return *reinterpret_cast<const floatx4 *>(row + c);
-        return *reinterpret_cast<const floatx4_ua *>(row + c);
+        return floatx4{row[c], row[c + 1], row[c + 2], row[c + 3]};
     }
     floatx4 v = {0.f, 0.f, 0.f, 0.f};
     if (!row_ok) return v;
-    if (c + 4 <= ncols)
-        return VEC ? *reinterpret_cast<const floatx4 *>(row + c)
-                   : *reinterpret_cast<const floatx4_ua *>(row + c);
+    if (VEC && c + 4 <= ncols) return *reinterpret_cast<const floatx4 *>(row + c);
 #pragma unroll
     for (int e = 0; e < 4; ++e)
         if (c + e < ncols) v[e] = row[c + e];
     return v;
 }
 
-// One BM x BN tile of C.  LOAD: 0 = dwordx4 at 4-byte alignment (rows not 16-byte
-// aligned), 1 = dwordx4 through pointers, 2 = dwordx4 through buffer resources (interior
-// tiles, offsets below 2^31 bytes).  EDGE selects the predicated loads and guarded
-// stores.  (Clamped loads fixed up when staged, as in the 16-bit kernel, measured 3-15 %
-// slower here than these predicated loads.)
+// One BM x BN tile of C.  LOAD: 0 = dword loads (rows not 16-byte aligned), 1 = dwordx4
+// through pointers, 2 = dwordx4 through buffer resources (interior tiles, offsets below
+// 2^31 bytes).  EDGE selects the predicated loads and guarded stores.  (Clamped loads
+// fixed up when staged, as in the 16-bit kernel, and 16-byte loads at 4-byte alignment
+// both measured slower here than these loads.)
 // KT (with LOAD 2, unpredicated): K is not a multiple of BK but of 4; the last k-step's
 // chunks past K load from inside the matrix (a row clamped to K-1, or 4 columns clamped
 // to K-4) and are zeroed when staged to LDS.
@@ -496,6 +494,20 @@ hipError_t launch_cfg(const GemmArgs &g, bool vec, hipStream_t s) {
                 return launch_one<BM, BN, WM, WN, MINW, 2, false, true, A_MN, B_MN, ACC>(g, all, 1, s);
             if (fits) return launch_one<BM, BN, WM, WN, MINW, 2, false, false, A_MN, B_MN, ACC>(g, all, 1, s);
             return launch_one<BM, BN, WM, WN, MINW, 1, false, false, A_MN, B_MN, ACC>(g, all, 1, s);
+        }
+    }
+    if constexpr (!INTERIOR) {
+        // Ragged strips that would take a launch (a round) of their own go with the
+        // interior tiles into one launch of the predicated kernel when that takes fewer
+        // rounds at its slower pace (up to 1.5x an interior tile's time): FP32
+        // 1000 x 1000 x 1024 with lda 1025 61 -> 40 us; 3000 x 3000 x 3008 and 4000^3
+        // (lda + 1) measured 3 % slower in one launch and keep two.
+        if (full_tiles > 0 && edge_tiles > 0) {
+            const int all = full_tiles + edge_tiles;
+            if (cdiv(all, 256) * 3 < cdiv(full_tiles, 256) * 2 + cdiv(edge_tiles, 256) * 3) {
+                if (vec) return launch_one<BM, BN, WM, WN, MINW, 1, true, false, A_MN, B_MN, ACC>(g, all, 1, s);
+                return launch_one<BM, BN, WM, WN, MINW, 0, true, false, A_MN, B_MN, ACC>(g, all, 1, s);
+            }
         }
     }
     if (full_tiles > 0) {

@@ -12,10 +12,10 @@ hipError_t launch_mfma_f32_acc(const GemmArgs &g, hipStream_t s);
 const char *desc_mfma_f32(const GemmArgs &g) {
     const F32Pick p = pick_f32(g);
     switch (p.tile) {
-    case 192: return p.vec ? "mfma_f32 192x192x32 w2x6 dwordx4" : "mfma_f32 192x192x32 w2x6 dwordx4 unaligned";
-    case 128: return p.vec ? "mfma_f32 128x128x32 w2x4 dwordx4" : "mfma_f32 128x128x32 w2x4 dwordx4 unaligned";
-    case 96: return p.vec ? "mfma_f32 96x96x32 w1x3 dwordx4" : "mfma_f32 96x96x32 w1x3 dwordx4 unaligned";
-    default: return p.vec ? "mfma_f32 64x64x32 w2x2 dwordx4" : "mfma_f32 64x64x32 w2x2 dwordx4 unaligned";
+    case 192: return p.vec ? "mfma_f32 192x192x32 w2x6 dwordx4" : "mfma_f32 192x192x32 w2x6 dword";
+    case 128: return p.vec ? "mfma_f32 128x128x32 w2x4 dwordx4" : "mfma_f32 128x128x32 w2x4 dword";
+    case 96: return p.vec ? "mfma_f32 96x96x32 w1x3 dwordx4" : "mfma_f32 96x96x32 w1x3 dword";
+    default: return p.vec ? "mfma_f32 64x64x32 w2x2 dwordx4" : "mfma_f32 64x64x32 w2x2 dword";
     }
 }
 
