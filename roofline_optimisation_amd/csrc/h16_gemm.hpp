@@ -571,10 +571,18 @@ hipError_t launch_cfg(const GemmArgs &g, hipStream_t s) {
     // as long as interior ones (one staging set, fix-ups), so it does when that takes
     // less time than the interior launch followed by the ragged strips' launch.
     const bool clamp = (A_MN ? g.M : g.K) >= 8 && (B_MN ? g.N : g.K) >= 8;
+    // (EPI 0 with an even number of k-steps: the two-set pipeline.)
+    auto launch_clamped = [&](int tiles, int flag) {
+        if constexpr (EPI == 0) {
+            if (cdiv(g.K, kBK) % 2 == 0)
+                return launch_one<T, BM, BN, WM, WN, MINW, 3, true, true, A_MN, B_MN, EPI>(g, tiles, flag, s);
+        }
+        return launch_one<T, BM, BN, WM, WN, MINW, 3, true, false, A_MN, B_MN, EPI>(g, tiles, flag, s);
+    };
     if (clamp && full_tiles > 0 && edge_tiles > 0) {
         const int all = full_tiles + edge_tiles;
         if (cdiv(all, 256) * 3 < cdiv(full_tiles, 256) * 2 + cdiv(edge_tiles, 256) * 3)
-            return launch_one<T, BM, BN, WM, WN, MINW, 3, true, false, A_MN, B_MN, EPI>(g, all, 1, s);
+            return launch_clamped(all, 1);
     }
     if (full_tiles > 0) {
         hipError_t e = hipSuccess;
@@ -598,8 +606,7 @@ hipError_t launch_cfg(const GemmArgs &g, hipStream_t s) {
         // (4096 x 4096 x 4000 BF16: 142 against 174 us); any row or column past the
         // matrix makes them the slower ones (4000^3: 298 against 178 us).
         const bool whole = vec && g.M % BM == 0 && g.N % BN == 0 && g.K % 8 == 0;
-        if (clamp && !whole)
-            return launch_one<T, BM, BN, WM, WN, MINW, 3, true, false, A_MN, B_MN, EPI>(g, edge_tiles, all_flag, s);
+        if (clamp && !whole) return launch_clamped(edge_tiles, all_flag);
         if (vec) return launch_one<T, BM, BN, WM, WN, MINW, 1, true, false, A_MN, B_MN, EPI>(g, edge_tiles, all_flag, s);
         return launch_one<T, BM, BN, WM, WN, MINW, 0, true, false, A_MN, B_MN, EPI>(g, edge_tiles, all_flag, s);
     }
