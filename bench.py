@@ -223,6 +223,44 @@ def time_variant(variant, dtype, M, N, K, seed, reps=None):
     return e0.elapsed_time(e1) / reps, desc, reps
 
 
+def family_run(family, steps, warmup):
+    """`warmup` untimed and `steps` timed launches of one kernel family on the FP32 3072^3
+    workload (seed 1), logged to stderr: the target of the ladder's counter passes."""
+    import torch
+
+    from roofline_optimisation_amd import binding as gb
+    from roofline_optimisation_amd import inputs
+
+    variant = {"naive": gb.VARIANT_NAIVE, "lds_tiled": gb.VARIANT_LDS_TILED,
+               "regblock": gb.VARIANT_REGBLOCK, "mfma": gb.VARIANT_MFMA}[family]
+    n = 3072
+    A, B = inputs.make_operands(n, n, n, 1, "uniform", "f32")
+    dA, dB = torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda()
+    dC = torch.empty((n, n), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.Stream()
+    args = (variant, gb.F32, n, n, n, dA.data_ptr(), n, dB.data_ptr(), n, dC.data_ptr(), n,
+            stream.cuda_stream)
+    desc = gb.gemm355_kernel_desc(*args[:-1])
+
+    def launch():
+        st = gb.gemm355_run_variant(*args)
+        if st != gb.OK:
+            raise gb.Gemm355Error(st, "gemm355_run_variant")
+
+    for _ in range(warmup):
+        launch()
+    stream.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        launch()
+    e1.record(stream)
+    stream.synchronize()
+    ms = e0.elapsed_time(e1) / max(steps, 1)
+    log(f"[bench] family {family} ({desc}) f32 {n}^3: {warmup} + {steps} launches, "
+        f"{ms:.4f} ms/launch, {2.0 * n ** 3 / (ms * 1e-3) / 1e12:.2f} TFLOP/s")
+
+
 def general_form_lines():
     """Markdown lines timing gemm355_gemm_ex (transposed / negated operands, accumulation)
     at the headline sizes, against the plain product."""
@@ -637,6 +675,9 @@ def main():
                     help="only measure the row-wise softmax and row sum on their 64 Mi-element "
                          "workloads, write the markdown table to PATH and print one JSON line "
                          "for the 16384 x 4096 workload; no GEMM timing")
+    ap.add_argument("--family", choices=["naive", "lds_tiled", "regblock", "mfma"], default=None,
+                    help="only launch one kernel family on the FP32 3072^3 workload, --warmup "
+                         "untimed and --steps timed launches (for counter passes); no JSON line")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after the GEMMs, copy this many MiB device-to-device once (a plain "
                          "copy of known size, used to scale the HBM byte counters)")
@@ -672,6 +713,11 @@ def main():
             dst.copy_(src)
             torch.cuda.synchronize()
             log(f"[bench] calibration copy of {args.calib_copy_mib} MiB done")
+
+    if args.family:
+        family_run(args.family, args.steps, args.warmup)
+        calibration_copy()
+        return
 
     if args.softmax:
         warm, reps = min(args.warmup, 50), max(1, min(args.steps, 100))

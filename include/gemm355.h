@@ -147,10 +147,21 @@ gemm355_status gemm355_gemm_ex(int variant, int dtype, unsigned flags, int M, in
 int gemm355_select_variant(int dtype, int M, int N, int K, const void *A, int lda, const void *B,
                            int ldb, const float *C, int ldc);
 
-/* Host-only: a static, NUL-terminated description of the kernel instance (family,
- * tile shape, load path) that gemm355_run_variant would launch, or "invalid". */
+/* Host-only: a NUL-terminated description of the kernel instance (family, tile shape,
+ * load path; for the register-staged 16-bit kernel also its launches: one launch over
+ * every tile, or an interior launch and the ragged strips, with their load mode and
+ * whether the two-set pipeline runs) that gemm355_run_variant would launch, or
+ * "invalid".  Makes no HIP call.  The string is owned by the library and stays valid
+ * until the next call of gemm355_kernel_desc or gemm355_kernel_desc_ex on the same
+ * thread. */
 const char *gemm355_kernel_desc(int variant, int dtype, int M, int N, int K, const void *A, int lda,
                                 const void *B, int ldb, const float *C, int ldc);
+
+/* Host-only: the same for gemm355_gemm_ex with operand forms `flags`; "invalid" where
+ * gemm355_gemm_ex would return an error status before launching. */
+const char *gemm355_kernel_desc_ex(int variant, int dtype, unsigned flags, int M, int N, int K,
+                                   const void *A, int lda, const void *B, int ldb, const void *C,
+                                   int ldc);
 
 /* Host-only: static strings for status codes and variants ("unknown" otherwise). */
 const char *gemm355_status_string(int status);

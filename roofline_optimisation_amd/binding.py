@@ -27,7 +27,8 @@ TRANS_A, TRANS_B, NEG_A, NEG_B, ACCUMULATE, C_16 = 1, 2, 4, 8, 16, 32
 # Every symbol the public headers declare.
 EXPORTS = (
     "gemm_f32", "gemm_f16f32acc", "gemm_bf16f32acc", "gemm355_run_variant",
-    "gemm355_select_variant", "gemm355_kernel_desc", "gemm355_status_string",
+    "gemm355_select_variant", "gemm355_kernel_desc", "gemm355_kernel_desc_ex",
+    "gemm355_status_string",
     "gemm355_variant_name", "gemm355_version", "gemm355_gemm_ex",
     "gemm355_probe_mfma_shape", "gemm355_probe_mfma", "gemm355_probe_ds_read_tr16",
     "gemm355_probe_global_load_lds", "gemm355_stream", "gemm355_chase",
@@ -61,6 +62,8 @@ def _configure(lib):
     lib.gemm355_select_variant.restype = i
     lib.gemm355_kernel_desc.argtypes = [i, i, i, i, i, p, i, p, i, p, i]
     lib.gemm355_kernel_desc.restype = s
+    lib.gemm355_kernel_desc_ex.argtypes = [i, i, ctypes.c_uint, i, i, i, p, i, p, i, p, i]
+    lib.gemm355_kernel_desc_ex.restype = s
     lib.gemm355_status_string.argtypes = [i]
     lib.gemm355_status_string.restype = s
     lib.gemm355_variant_name.argtypes = [i]
@@ -127,6 +130,11 @@ def gemm355_select_variant(dtype, M, N, K, A, lda, B, ldb, C, ldc) -> int:
 
 def gemm355_kernel_desc(variant, dtype, M, N, K, A, lda, B, ldb, C, ldc) -> str:
     return lib().gemm355_kernel_desc(variant, dtype, M, N, K, A, lda, B, ldb, C, ldc).decode()
+
+
+def gemm355_kernel_desc_ex(variant, dtype, flags, M, N, K, A, lda, B, ldb, C, ldc) -> str:
+    return lib().gemm355_kernel_desc_ex(variant, dtype, flags, M, N, K, A, lda, B, ldb, C,
+                                        ldc).decode()
 
 
 def gemm355_status_string(status: int) -> str:

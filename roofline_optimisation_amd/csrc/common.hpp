@@ -68,8 +68,9 @@ struct GemmArgs {
 // Stores one 32 x 32 MFMA accumulator block: register r of this lane holds row
 // row0 + 8 (r/4) + r%4 (row0 already includes the lane's 4 (l/32)), column col.  EDGE
 // guards every access against M x N; NT uses non-temporal stores (C is not re-read).
-// The values go out exactly as accumulated, straight from the accumulator registers (a
-// negated product is negated by a pass after the kernel).
+// The values go out exactly as accumulated, straight from the accumulator registers: the
+// plain variants' epilogue.  The signed and accumulating variants apply the sign (and add
+// the old C) in their own epilogue, store_block32_acc below, with no extra pass.
 template <bool EDGE, bool NT>
 __device__ __forceinline__ void store_block32(const floatx16 &acc, float *__restrict__ C, int ldc,
                                               int row0, int col, int M, int N) {

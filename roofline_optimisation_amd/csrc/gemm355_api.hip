@@ -90,8 +90,9 @@ gemm355_status run(int variant, int dtype, int M, int N, int K, const void *A, i
 constexpr unsigned kExFlags = GEMM355_TRANS_A | GEMM355_TRANS_B | GEMM355_NEG_A | GEMM355_NEG_B |
                                GEMM355_ACCUMULATE | GEMM355_C_16;
 
-gemm355_status run_ex(int variant, int dtype, unsigned flags, int M, int N, int K, const void *A,
-                      int lda, const void *B, int ldb, void *C, int ldc, hipStream_t stream) {
+// Validates gemm355_gemm_ex's arguments and fills `g` (variant resolved from AUTO).
+gemm355_status ex_args(int &variant, int dtype, unsigned flags, int M, int N, int K, const void *A,
+                       int lda, const void *B, int ldb, void *C, int ldc, GemmArgs &g) {
     if ((flags & ~kExFlags) != 0) return GEMM355_ERR_INVALID_ARG;
     const bool c16 = flags & GEMM355_C_16;
     if (c16 && dtype != kF16 && dtype != kBF16) return GEMM355_ERR_INVALID_ARG;
@@ -109,7 +110,7 @@ gemm355_status run_ex(int variant, int dtype, unsigned flags, int M, int N, int 
     if ((long)M * N > 0 && C == nullptr) return GEMM355_ERR_INVALID_ARG;
     if (variant < GEMM355_VARIANT_AUTO || variant > GEMM355_VARIANT_MFMA)
         return GEMM355_ERR_INVALID_ARG;
-    GemmArgs g{M, N, K, A, lda, B, ldb, (float *)C, ldc};
+    g = GemmArgs{M, N, K, A, lda, B, ldb, (float *)C, ldc};
     g.c16 = c16;
     g.trans_a = ta;
     g.trans_b = tb;
@@ -119,10 +120,27 @@ gemm355_status run_ex(int variant, int dtype, unsigned flags, int M, int N, int 
     if (!variant_supported(variant, dtype)) return GEMM355_ERR_UNSUPPORTED;
     if (flags != 0 && variant != GEMM355_VARIANT_NAIVE && variant != GEMM355_VARIANT_MFMA)
         return GEMM355_ERR_UNSUPPORTED;
+    return GEMM355_OK;
+}
+
+gemm355_status run_ex(int variant, int dtype, unsigned flags, int M, int N, int K, const void *A,
+                      int lda, const void *B, int ldb, void *C, int ldc, hipStream_t stream) {
+    GemmArgs g{};
+    const gemm355_status st = ex_args(variant, dtype, flags, M, N, K, A, lda, B, ldb, C, ldc, g);
+    if (st != GEMM355_OK) return st;
     if (M == 0 || N == 0) return GEMM355_OK;
     if (!device_ok()) return GEMM355_ERR_DEVICE;
-    if (K == 0 && acc) return GEMM355_OK;  // adding the empty sum leaves C as it is
+    if (K == 0 && g.accumulate) return GEMM355_OK;  // adding the empty sum leaves C as it is
     return launch(variant, dtype, g, stream) == hipSuccess ? GEMM355_OK : GEMM355_ERR_LAUNCH;
+}
+
+const char *desc_of(int variant, int dtype, const GemmArgs &g) {
+    switch (variant) {
+    case GEMM355_VARIANT_NAIVE: return "naive 64x4 threads, one output each";
+    case GEMM355_VARIANT_LDS_TILED: return desc_lds_tiled_f32(g);
+    case GEMM355_VARIANT_REGBLOCK: return desc_regblock_f32(g);
+    default: return dtype == kF32 ? desc_mfma_f32(g) : desc_mfma_f16(dtype, g);
+    }
 }
 
 }  // namespace
@@ -175,12 +193,17 @@ const char *gemm355_kernel_desc(int variant, int dtype, int M, int N, int K, con
     const GemmArgs g{M, N, K, A, lda, B, ldb, const_cast<float *>(C), ldc};
     if (variant == GEMM355_VARIANT_AUTO) variant = auto_variant(dtype, g);
     if (!variant_supported(variant, dtype)) return "invalid";
-    switch (variant) {
-    case GEMM355_VARIANT_NAIVE: return "naive 64x4 threads, one output each";
-    case GEMM355_VARIANT_LDS_TILED: return desc_lds_tiled_f32(g);
-    case GEMM355_VARIANT_REGBLOCK: return desc_regblock_f32(g);
-    default: return dtype == kF32 ? desc_mfma_f32(g) : desc_mfma_f16(dtype, g);
-    }
+    return desc_of(variant, dtype, g);
+}
+
+const char *gemm355_kernel_desc_ex(int variant, int dtype, unsigned flags, int M, int N, int K,
+                                   const void *A, int lda, const void *B, int ldb, const void *C,
+                                   int ldc) {
+    GemmArgs g{};
+    if (ex_args(variant, dtype, flags, M, N, K, A, lda, B, ldb, const_cast<void *>(C), ldc, g) !=
+        GEMM355_OK)
+        return "invalid";
+    return desc_of(variant, dtype, g);
 }
 
 const char *gemm355_status_string(int status) {

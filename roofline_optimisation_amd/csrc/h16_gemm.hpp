@@ -543,62 +543,57 @@ hipError_t launch_one(const GemmArgs &g, int tiles, int all_flag, hipStream_t s)
     return hipGetLastError();
 }
 
-// Interior tiles: direct-to-LDS loads (256 x 256, K % 128 == 0), else buffer loads when
-// rows are 16-byte aligned and every offset fits in 31 bits, with the two-set pipeline
-// when the number of k-steps is even; ragged strips: clamped loads fixed up when staged
-// (predicated element loads when a contiguous extent is below 8).  The
-// signed / accumulating epilogues (EPI 1, 2) keep to the direct-to-LDS and pointer-load
-// kernels, which bounds the number of instances.
-template <typename T, int BM, int BN, int WM, int WN, int MINW, bool A_MN, bool B_MN, int EPI>
-hipError_t launch_cfg(const GemmArgs &g, hipStream_t s) {
+// The launches one configuration makes.  Interior tiles: direct-to-LDS loads (256 x 256,
+// K % 128 == 0), else buffer loads when rows are 16-byte aligned and every offset fits in
+// 31 bits, with the two-set pipeline when the number of k-steps is even; ragged strips:
+// clamped loads fixed up when staged (predicated element loads when a contiguous extent is
+// below 8).  The signed / accumulating epilogues (EPI 1, 2) keep to the direct-to-LDS and
+// pointer-load kernels, which bounds the number of instances.
+struct H16Plan {
+    bool dma = false;         // the direct-to-LDS kernel takes every tile
+    bool all_tiles = false;   // one clamped launch over every tile (edge_paired applies)
+    int interior = -1;        // interior launch: load mode 2 buffer, 1 pointer, 0 pointer at
+                              // element alignment; -1 none
+    bool interior_paired = false;
+    int edge = -1;            // ragged strips (or every tile when K is ragged): 3 clamped,
+                              // 1 / 0 predicated (aligned / unaligned rows); -1 none
+    bool edge_paired = false;
+};
+
+inline H16Plan plan_cfg(int BM, int BN, bool a_mn, bool b_mn, int epi, const GemmArgs &g) {
+    H16Plan p;
+    if (BM == BN && use_dma(g, BM)) {
+        p.dma = true;
+        return p;
+    }
     const bool vec = h16_vec(g);
     const bool kfull = g.K % kBK == 0;
     const int full_tiles = kfull ? (g.M / BM) * (g.N / BN) : 0;
     const int edge_tiles = cdiv(g.M, BM) * cdiv(g.N, BN) - full_tiles;
-    const int all_flag = kfull ? 0 : 1;
-    const bool fits = op_fits(A_MN, BM, g.K, g.lda) && op_fits(B_MN, BN, g.K, g.ldb);
-    if constexpr (BM == BN) {
-        if (use_dma(g, BM)) {
-            hipLaunchKernelGGL((mfma_f16_dma_kernel<T, A_MN, B_MN, EPI, BM>),
-                               dim3(cdiv(g.M, BM) * cdiv(g.N, BN)), dim3(64 * dma::kWaves), 0, s,
-                               g.M, g.N, g.K, (const uint16_t *)g.A, g.lda, (const uint16_t *)g.B,
-                               g.ldb, g.C, g.ldc, g.sign, epi_flags<EPI>(g));
-            return hipGetLastError();
-        }
-    }
+    const bool fits = op_fits(a_mn, BM, g.K, g.lda) && op_fits(b_mn, BN, g.K, g.ldb);
     // Clamped loads need 8 elements along each operand's contiguous extent.  With them
     // the ragged-tile kernel can take every tile in one launch; its tiles run about 1.5x
     // as long as interior ones (one staging set, fix-ups), so it does when that takes
-    // less time than the interior launch followed by the ragged strips' launch.
-    const bool clamp = (A_MN ? g.M : g.K) >= 8 && (B_MN ? g.N : g.K) >= 8;
-    // (EPI 0 with an even number of k-steps: the two-set pipeline.)
-    auto launch_clamped = [&](int tiles, int flag) {
-        if constexpr (EPI == 0) {
-            if (cdiv(g.K, kBK) % 2 == 0)
-                return launch_one<T, BM, BN, WM, WN, MINW, 3, true, true, A_MN, B_MN, EPI>(g, tiles, flag, s);
-        }
-        return launch_one<T, BM, BN, WM, WN, MINW, 3, true, false, A_MN, B_MN, EPI>(g, tiles, flag, s);
-    };
+    // less time than the interior launch followed by the ragged strips' launch.  (EPI 0
+    // with an even number of k-steps: the two-set pipeline.)
+    const bool clamp = (a_mn ? g.M : g.K) >= 8 && (b_mn ? g.N : g.K) >= 8;
+    const bool clamp_paired = epi == 0 && cdiv(g.K, kBK) % 2 == 0;
     if (clamp && full_tiles > 0 && edge_tiles > 0) {
         const int all = full_tiles + edge_tiles;
-        if (cdiv(all, 256) * 3 < cdiv(full_tiles, 256) * 2 + cdiv(edge_tiles, 256) * 3)
-            return launch_clamped(all, 1);
+        if (cdiv(all, 256) * 3 < cdiv(full_tiles, 256) * 2 + cdiv(edge_tiles, 256) * 3) {
+            p.all_tiles = true;
+            p.edge = 3;
+            p.edge_paired = clamp_paired;
+            return p;
+        }
     }
     if (full_tiles > 0) {
-        hipError_t e = hipSuccess;
-        if (EPI == 0 && vec && fits) {
-            if constexpr (EPI == 0) {
-                if ((g.K / kBK) % 2 == 0)
-                    e = launch_one<T, BM, BN, WM, WN, MINW, 2, false, true, A_MN, B_MN, false>(g, full_tiles, all_flag, s);
-                else
-                    e = launch_one<T, BM, BN, WM, WN, MINW, 2, false, false, A_MN, B_MN, false>(g, full_tiles, all_flag, s);
-            }
-        } else if (vec) {
-            e = launch_one<T, BM, BN, WM, WN, MINW, 1, false, false, A_MN, B_MN, EPI>(g, full_tiles, all_flag, s);
+        if (epi == 0 && vec && fits) {
+            p.interior = 2;
+            p.interior_paired = (g.K / kBK) % 2 == 0;
         } else {
-            e = launch_one<T, BM, BN, WM, WN, MINW, 0, false, false, A_MN, B_MN, EPI>(g, full_tiles, all_flag, s);
+            p.interior = vec ? 1 : 0;
         }
-        if (e != hipSuccess) return e;
     }
     if (edge_tiles > 0) {
         // Whole tiles with only K ragged (by a multiple of 8) and aligned rows never take
@@ -606,10 +601,60 @@ hipError_t launch_cfg(const GemmArgs &g, hipStream_t s) {
         // (4096 x 4096 x 4000 BF16: 142 against 174 us); any row or column past the
         // matrix makes them the slower ones (4000^3: 298 against 178 us).
         const bool whole = vec && g.M % BM == 0 && g.N % BN == 0 && g.K % 8 == 0;
-        if (clamp && !whole) return launch_clamped(edge_tiles, all_flag);
-        if (vec) return launch_one<T, BM, BN, WM, WN, MINW, 1, true, false, A_MN, B_MN, EPI>(g, edge_tiles, all_flag, s);
-        return launch_one<T, BM, BN, WM, WN, MINW, 0, true, false, A_MN, B_MN, EPI>(g, edge_tiles, all_flag, s);
+        if (clamp && !whole) {
+            p.edge = 3;
+            p.edge_paired = clamp_paired;
+        } else {
+            p.edge = vec ? 1 : 0;
+        }
     }
+    return p;
+}
+
+template <typename T, int BM, int BN, int WM, int WN, int MINW, bool A_MN, bool B_MN, int EPI>
+hipError_t launch_cfg(const GemmArgs &g, hipStream_t s) {
+    const H16Plan p = plan_cfg(BM, BN, A_MN, B_MN, EPI, g);
+    if constexpr (BM == BN) {
+        if (p.dma) {
+            hipLaunchKernelGGL((mfma_f16_dma_kernel<T, A_MN, B_MN, EPI, BM>),
+                               dim3(cdiv(g.M, BM) * cdiv(g.N, BN)), dim3(64 * dma::kWaves), 0, s,
+                               g.M, g.N, g.K, (const uint16_t *)g.A, g.lda, (const uint16_t *)g.B,
+                               g.ldb, g.C, g.ldc, g.sign, epi_flags<EPI>(g));
+            return hipGetLastError();
+        }
+    }
+    if (p.dma) return hipErrorInvalidValue;
+    const bool kfull = g.K % kBK == 0;
+    const int full_tiles = kfull ? (g.M / BM) * (g.N / BN) : 0;
+    const int edge_tiles = cdiv(g.M, BM) * cdiv(g.N, BN) - full_tiles;
+    const int all_flag = kfull ? 0 : 1;
+    auto launch_clamped = [&](int tiles, int flag) {
+        if constexpr (EPI == 0) {
+            if (p.edge_paired)
+                return launch_one<T, BM, BN, WM, WN, MINW, 3, true, true, A_MN, B_MN, EPI>(g, tiles, flag, s);
+        }
+        return launch_one<T, BM, BN, WM, WN, MINW, 3, true, false, A_MN, B_MN, EPI>(g, tiles, flag, s);
+    };
+    if (p.all_tiles) return launch_clamped(full_tiles + edge_tiles, 1);
+    if (p.interior >= 0) {
+        hipError_t e = hipSuccess;
+        if (p.interior == 2) {
+            if constexpr (EPI == 0) {
+                if (p.interior_paired)
+                    e = launch_one<T, BM, BN, WM, WN, MINW, 2, false, true, A_MN, B_MN, EPI>(g, full_tiles, all_flag, s);
+                else
+                    e = launch_one<T, BM, BN, WM, WN, MINW, 2, false, false, A_MN, B_MN, EPI>(g, full_tiles, all_flag, s);
+            }
+        } else if (p.interior == 1) {
+            e = launch_one<T, BM, BN, WM, WN, MINW, 1, false, false, A_MN, B_MN, EPI>(g, full_tiles, all_flag, s);
+        } else {
+            e = launch_one<T, BM, BN, WM, WN, MINW, 0, false, false, A_MN, B_MN, EPI>(g, full_tiles, all_flag, s);
+        }
+        if (e != hipSuccess) return e;
+    }
+    if (p.edge == 3) return launch_clamped(edge_tiles, all_flag);
+    if (p.edge == 1) return launch_one<T, BM, BN, WM, WN, MINW, 1, true, false, A_MN, B_MN, EPI>(g, edge_tiles, all_flag, s);
+    if (p.edge == 0) return launch_one<T, BM, BN, WM, WN, MINW, 0, true, false, A_MN, B_MN, EPI>(g, edge_tiles, all_flag, s);
     return hipSuccess;
 }
 

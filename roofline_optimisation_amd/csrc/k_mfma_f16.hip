@@ -4,6 +4,8 @@
 // accumulating variants and the 16-bit-C variants are instantiated in k_mfma_f16_tx.hip,
 // k_mfma_f16_acc*.hip and k_mfma_*_c16.hip, so that the translation units compile in
 // parallel.
+#include <string>
+
 #include "h16_gemm.hpp"
 
 namespace g355 {
@@ -14,22 +16,38 @@ hipError_t launch_mfma_bf16_acc(const GemmArgs &g, hipStream_t s);
 hipError_t launch_mfma_f16_c16(const GemmArgs &g, hipStream_t s);
 hipError_t launch_mfma_bf16_c16(const GemmArgs &g, hipStream_t s);
 
+// The instance (and, for the register-staged kernel, the launches of its plan) that
+// launch_mfma_f16 picks for these arguments.  The string stays valid until the next call
+// on the same thread.
 const char *desc_mfma_f16(int dtype, const GemmArgs &g) {
+    static thread_local std::string out;
     const bool v = h16_vec(g);
     const bool big = pick_tile(g) == 256;
-    if (big && use_dma(g, 256))
-        return dtype == kF16 ? "mfma_f16 256x256x32 w2x2 lds-dma" : "mfma_bf16 256x256x32 w2x2 lds-dma";
-    const bool narrow = !big && !g.trans_a && !g.signed_or_acc() && !g.c16 && use_128x64(g);
-    if (!big && !narrow && use_dma(g, 128))
-        return dtype == kF16 ? "mfma_f16 128x128x32 w2x2 lds-dma" : "mfma_bf16 128x128x32 w2x2 lds-dma";
-    if (dtype == kF16) {
-        if (big) return v ? "mfma_f16 256x256x64 w2x2 dwordx4" : "mfma_f16 256x256x64 w2x2 dwordx4 unaligned";
-        if (narrow) return v ? "mfma_f16 128x64x64 w2x2 dwordx4" : "mfma_f16 128x64x64 w2x2 dwordx4 unaligned";
-        return v ? "mfma_f16 128x128x64 w2x2 dwordx4" : "mfma_f16 128x128x64 w2x2 dwordx4 unaligned";
+    const char *name = dtype == kF16 ? "mfma_f16" : "mfma_bf16";
+    const int epi = g.c16 ? 2 : (g.signed_or_acc() ? 1 : 0);
+    const bool narrow = !big && !g.trans_a && epi == 0 && use_128x64(g);
+    const int bm = big ? 256 : 128, bn = big ? 256 : (narrow ? 64 : 128);
+    const H16Plan p = plan_cfg(bm, bn, g.trans_a != 0, g.trans_b == 0, epi, g);
+    out = name;
+    if (p.dma) {
+        out += big ? " 256x256x32 w2x2 lds-dma" : " 128x128x32 w2x2 lds-dma";
+        return out.c_str();
     }
-    if (big) return v ? "mfma_bf16 256x256x64 w2x2 dwordx4" : "mfma_bf16 256x256x64 w2x2 dwordx4 unaligned";
-    if (narrow) return v ? "mfma_bf16 128x64x64 w2x2 dwordx4" : "mfma_bf16 128x64x64 w2x2 dwordx4 unaligned";
-    return v ? "mfma_bf16 128x128x64 w2x2 dwordx4" : "mfma_bf16 128x128x64 w2x2 dwordx4 unaligned";
+    out += big ? " 256x256x64 w2x2 dwordx4" : (narrow ? " 128x64x64 w2x2 dwordx4" : " 128x128x64 w2x2 dwordx4");
+    if (!v) out += " unaligned";
+    // the launches: [all=...] or [interior=...][edges=...]
+    auto edge_name = [&](int mode, bool paired) {
+        return mode == 3 ? (paired ? "clamped,paired" : "clamped") : "predicated";
+    };
+    if (p.all_tiles) {
+        out += std::string(" | all=") + edge_name(p.edge, p.edge_paired);
+        return out.c_str();
+    }
+    if (p.interior >= 0)
+        out += p.interior == 2 ? (p.interior_paired ? " | interior=buffer,paired" : " | interior=buffer")
+                               : " | interior=pointer";
+    if (p.edge >= 0) out += std::string(p.interior >= 0 ? " edges=" : " | edges=") + edge_name(p.edge, p.edge_paired);
+    return out.c_str();
 }
 
 hipError_t launch_mfma_f16(int dtype, const GemmArgs &g, hipStream_t s) {

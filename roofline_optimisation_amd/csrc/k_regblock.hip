@@ -15,7 +15,8 @@
 //    ds_read_b128, and a wave's B reads cover 256 contiguous bytes (no bank conflict)
 //    while its A reads touch four addresses (broadcast);
 //  * A is stored k-major in LDS (transposed on the way in: four ds_write_b32 per
-//    loaded dwordx4), B as loaded; A rows are padded to 132 words;
+//    loaded dwordx4, lanes arranged so that each write hits distinct banks), B as
+//    loaded; A rows are padded to 132 words;
 //  * 64 v_fma_f32 per 4 ds_read_b128 per k; accumulation is fmaf in increasing k from
 //    +0.0, so every element rounds exactly as in the naive and LDS-tiled kernels.
 // The vector ALU peaks at 128 FP32 FLOP/clk/CU with unpacked FMA (packed FP32 math is
@@ -66,11 +67,19 @@ void regblock_f32_kernel(int M, int N, int K, const float *__restrict__ A, int l
     const int tx = t % 16, ty = t / 16;
 
     int a_r[kAChunks], a_c[kAChunks], b_r[kBChunks], b_c[kBChunks];
+    // A chunks: 64 consecutive q (one wave's instruction) cover 16 rows x 4 chunks, so
+    // each row's 64 bytes are read by one instruction.  Within each 32-lane half the rows
+    // are arranged so that its four ds_write_b32 of the transposed store hit 32 distinct
+    // banks: with the 132-word stride lane (row r, chunk j) writes word (4 j + e) 132 + r,
+    // bank (16 j + 4 e + r) mod 32, and the half puts rows 0-7 under chunks {0, 1} and rows
+    // 8-15 under chunks {2, 3} (the other half the opposite).  Consecutive rows under every
+    // chunk (q / 4) gave two lanes per bank, 16 conflict cycles per wave per k-step.
 #pragma unroll
     for (int i = 0; i < kAChunks; ++i) {
         const int q = t + kThreads * i;
-        a_r[i] = q / (kBK / 4);
-        a_c[i] = (q % (kBK / 4)) * 4;
+        const int l = q % 64, j = l % 4;
+        a_r[i] = 16 * (q / 64) + (l % 32) / 4 + 8 * ((j / 2) ^ (l / 32));
+        a_c[i] = 4 * j;
     }
 #pragma unroll
     for (int i = 0; i < kBChunks; ++i) {

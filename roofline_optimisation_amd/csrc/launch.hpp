@@ -14,7 +14,6 @@ hipError_t launch_lds_tiled_f32(const GemmArgs &g, hipStream_t s);
 hipError_t launch_regblock_f32(const GemmArgs &g, hipStream_t s);
 hipError_t launch_mfma_f32(const GemmArgs &g, hipStream_t s);
 hipError_t launch_mfma_f16(int dtype, const GemmArgs &g, hipStream_t s);
-hipError_t launch_fill_zero(const GemmArgs &g, hipStream_t s);
 
 // Host-side descriptions of the instance each launcher would pick.
 const char *desc_lds_tiled_f32(const GemmArgs &g);

@@ -103,15 +103,15 @@ def test_dispatch_choices(lib):
     # rows and more 128-wide tiles keep register staging
     assert d(-1, 1, 4096, 4096, 4096, P, 4096, P, 4096, P, 4096) == "mfma_f16 256x256x32 w2x2 lds-dma"
     assert d(-1, 2, 4096, 4096, 4096, P, 4096, P, 4096, P, 4096) == "mfma_bf16 256x256x32 w2x2 lds-dma"
-    assert d(-1, 1, 4096, 4096, 4160, P, 4160, P, 4096, P, 4096) == "mfma_f16 256x256x64 w2x2 dwordx4"
-    assert d(-1, 1, 4096, 4096, 4096, P + 2, 4096, P, 4096, P, 4096) == "mfma_f16 256x256x64 w2x2 dwordx4 unaligned"
+    assert d(-1, 1, 4096, 4096, 4160, P, 4160, P, 4096, P, 4096) == "mfma_f16 256x256x64 w2x2 dwordx4 | interior=buffer"
+    assert d(-1, 1, 4096, 4096, 4096, P + 2, 4096, P, 4096, P, 4096) == "mfma_f16 256x256x64 w2x2 dwordx4 unaligned | interior=pointer"
     assert d(-1, 1, 2048, 2048, 2048, P, 2048, P, 2048, P, 2048) == "mfma_f16 128x128x32 w2x2 lds-dma"
-    assert d(-1, 1, 2048, 2048, 2176, P, 2176, P, 2048, P, 2048) == "mfma_f16 128x128x64 w2x2 dwordx4"
-    assert d(-1, 2, 2560, 2560, 2560, P, 2560, P, 2560, P, 2560) == "mfma_bf16 128x128x64 w2x2 dwordx4"
+    assert d(-1, 1, 2048, 2048, 2176, P, 2176, P, 2048, P, 2048) == "mfma_f16 128x128x64 w2x2 dwordx4 | interior=buffer,paired"
+    assert d(-1, 2, 2560, 2560, 2560, P, 2560, P, 2560, P, 2560) == "mfma_bf16 128x128x64 w2x2 dwordx4 | interior=buffer,paired"
     assert d(-1, 1, 4000, 4000, 4096, P, 4096, P, 4000, P, 4000) == "mfma_f16 256x256x32 w2x2 lds-dma"
     assert d(-1, 1, 4096, 4104, 4096, P, 4096, P, 4104, P, 4104) == "mfma_f16 256x256x32 w2x2 lds-dma"
     # an m/n-contiguous extent that is not a whole number of 16-byte chunks stays staged
-    assert d(-1, 1, 4000, 4004, 4096, P, 4096, P, 4008, P, 4004) == "mfma_f16 256x256x64 w2x2 dwordx4"
+    assert d(-1, 1, 4000, 4004, 4096, P, 4096, P, 4008, P, 4004) == "mfma_f16 256x256x64 w2x2 dwordx4 | all=clamped,paired"
     # rows not 16-byte aligned (lda = 515 floats) take the dword load path
     assert d(-1, 0, 1023, 997, 515, P, 515, P, 997, P, 997).endswith("dword")
     assert d(-1, 0, 1000, 1000, 1000, P, 1000, P, 1000, P, 1000).endswith("dwordx4")
@@ -120,6 +120,34 @@ def test_dispatch_choices(lib):
     assert d(1, 0, 8, 8, 8, P, 8, P, 8, P, 8).startswith("lds_tiled")
     assert d(2, 0, 8, 8, 8, P, 8, P, 8, P, 8).startswith("regblock")
     assert d(1, 1, 8, 8, 8, P, 8, P, 8, P, 8) == "invalid"
+    # the register-staged 16-bit kernel's launches: the interior launch with an odd number
+    # of 64-wide k-steps (4160 / 64 = 65) runs one staging set, with an even number the
+    # two-set pipeline; ragged strips with clamped loads
+    assert d(-1, 1, 8000, 8004, 128, P, 128, P, 8008, P, 8004) == \
+        "mfma_f16 256x256x64 w2x2 dwordx4 | interior=buffer,paired edges=clamped,paired"
+    assert d(-1, 1, 8000, 8004, 192, P, 192, P, 8008, P, 8004) == \
+        "mfma_f16 256x256x64 w2x2 dwordx4 | interior=buffer edges=clamped"
+
+
+def test_dispatch_choices_general_form(lib):
+    dx = lambda *a: gb.gemm355_kernel_desc_ex(*a)
+    # flag-free equals the plain query
+    assert dx(-1, 1, 0, 4096, 4096, 4096, P, 4096, P, 4096, P, 4096) == \
+        gb.gemm355_kernel_desc(-1, 1, 4096, 4096, 4096, P, 4096, P, 4096, P, 4096)
+    # transposed operands with K ragged (1000 = 15 64-wide k-steps + 40): every tile takes
+    # the clamped kernel; 16 k-steps (even) run the two-set pipeline
+    assert dx(-1, 1, gb.TRANS_A, 1000, 1000, 1000, P, 1000, P, 1000, P, 1000) == \
+        "mfma_f16 128x128x64 w2x2 dwordx4 | edges=clamped,paired"
+    assert dx(-1, 2, gb.TRANS_B, 1000, 1000, 1000, P, 1000, P, 1000, P, 1000) == \
+        "mfma_bf16 128x64x64 w2x2 dwordx4 | edges=clamped,paired"
+    # signed and accumulating epilogues keep to one staging set
+    assert dx(-1, 1, gb.TRANS_A | gb.NEG_A, 1000, 1000, 1000, P, 1000, P, 1000, P, 1000) == \
+        "mfma_f16 128x128x64 w2x2 dwordx4 | edges=clamped"
+    # what gemm355_gemm_ex rejects
+    assert dx(-1, 0, gb.C_16, 8, 8, 8, P, 8, P, 8, P, 8) == "invalid"
+    assert dx(-1, 1, 64, 8, 8, 8, P, 8, P, 8, P, 8) == "invalid"
+    assert dx(gb.VARIANT_LDS_TILED, 0, gb.TRANS_A, 8, 8, 8, P, 8, P, 8, P, 8) == "invalid"
+    assert dx(-1, 1, gb.TRANS_A, 8, 8, 8, P, 4, P, 8, P, 8) == "invalid"
 
 
 def test_no_device_reports_device_error(lib):

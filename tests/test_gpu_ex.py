@@ -3,8 +3,9 @@ and negated operands, accumulation into C; the tensor-core instruction table of
 "Advanced CUDA features - starting from GEMM") against the oracle, through the C ABI.
 
 Bars as for the plain product (relative Frobenius error of the result against the
-oracle's binary64 value: 1e-5 FP32 with max-abs 1e-4 sqrt(K) (+ the old C's scale when
-accumulating), 1e-3 FP16/BF16; small integers bit-exact).  Stored operands sit in
+oracle's binary64 value: 1e-5 FP32, 1e-3 FP16/BF16, and for every operand type max-abs
+1e-4 sqrt(K) (+ the old C's scale when accumulating); with 16-bit C each element within
+that bound plus its own rounding to the 16-bit format; small integers bit-exact).  Stored operands sit in
 NaN-padded buffers with guard rows; C sits between sentinel guard words, and its M x N
 region starts as NaN when it is overwritten (so every element must be written) or as
 the values to accumulate into.
@@ -74,9 +75,10 @@ def check(C, C64, dtype, K, Cin, intact, what):
     assert not np.isnan(C).any(), f"{what}: NaN (an element not written, or a read outside)"
     rel, mx = errors(C, C64)
     trel = 1e-5 if dtype == "f32" else 1e-3
-    # FP32 absolute bound: 1e-4 sqrt(K) for the sum, plus one rounding of the old C
-    tabs = (1e-4 * np.sqrt(max(K, 1)) + (np.abs(Cin).max() * 2 ** -23 if Cin is not None else 0)
-            if dtype == "f32" else np.inf)
+    # Element bound for every operand type (16-bit products are exact in binary32, so
+    # only the FP32 accumulation rounds): 1e-4 sqrt(K) for the sum, plus one rounding of
+    # the old C
+    tabs = 1e-4 * np.sqrt(max(K, 1)) + (np.abs(Cin).max() * 2 ** -23 if Cin is not None else 0)
     print(f"{what}: rel_frob={rel:.3e} max_abs={mx:.3e}", flush=True)
     assert rel <= trel and mx <= tabs, f"{what}: rel {rel:.3e} (<= {trel}), max {mx:.3e} (<= {tabs})"
 
@@ -159,6 +161,28 @@ def test_integers_bit_exact(dtype, fl):
         assert ok and np.array_equal(C, C32), (dtype, fl, M, N, K)
 
 
+# Transposed layouts on the register-staged kernel's clamped ragged tiles with the
+# two-set pipeline (K = 1000: 16 64-wide k-steps, every tile ragged in K): every element
+# within the float bar, and integer operands bit for bit.
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("layout", [(True, False), (False, True), (True, True)],
+                         ids=["ta", "tb", "tatb"])
+def test_clamped_paired_transposed(dtype, layout):
+    ta, tb = layout
+    M, N, K = 1000, 1000, 1000
+    P = 1 << 20
+    flags = flags_of(ta, tb, False, False, False)
+    lda, ldb = (M if ta else K), (K if tb else N)
+    desc = gb.gemm355_kernel_desc_ex(gb.VARIANT_AUTO, gb.DTYPE_CODES[dtype], flags, M, N, K,
+                                     P, lda, P, ldb, P, N)
+    assert desc.endswith("| edges=clamped,paired"), desc
+    compare(M, N, K, dtype, ta, tb, False, False, False, seed=61)
+    A, B = inputs.make_operands(M, N, K, 62, "int", dtype)
+    C, ok, SA, SB = run_ex(A, B, dtype, ta, tb, False, False, False)
+    _, C32 = oracle.gemm_ex(SA, SB, dtype, ta, tb, False, False, None)
+    assert ok and np.array_equal(C, C32)
+
+
 def test_k_zero():
     import torch
     # K = 0: C = +0 (negated: -0, equal in value), or C unchanged when accumulating
@@ -238,8 +262,17 @@ def compare16(M, N, K, dtype, ta, tb, na, nb, acc, seed, variant=gb.VARIANT_AUTO
     assert not np.isnan(got).any(), f"{what}: NaN (an element not written, or a read outside)"
     rel, mx = errors(got, C64)
     bar = 2.0 ** -P16[dtype] + 1e-5
-    print(f"{what}: rel_frob={rel:.3e} (bar {bar:.3e})", flush=True)
+    # Element bound: the binary32 value s.sum (+ old C) is within 1e-4 sqrt(K) of the
+    # exact one (the FP32 bar; the old C is exact in binary32), and rounding it to the
+    # 16-bit format moves it by at most 2^-p of its magnitude, or by half the binary16
+    # subnormal spacing (2^-25) below the normal range.
+    tabs = 1e-4 * np.sqrt(max(K, 1))
+    sub = 2.0 ** -25 if dtype == "f16" else 0.0
+    elem = tabs * (1 + 2.0 ** -P16[dtype]) + 2.0 ** -P16[dtype] * np.abs(C64) + sub
+    worst = float((np.abs(got - C64) / elem).max()) if got.size else 0.0
+    print(f"{what}: rel_frob={rel:.3e} (bar {bar:.3e}) worst element/bound={worst:.3f}", flush=True)
     assert rel <= bar, f"{what}: rel {rel:.3e} > {bar:.3e}"
+    assert worst <= 1.0, f"{what}: an element is {worst:.3f} x its bound"
 
 
 FLAGS16 = list(itertools.product([False, True], repeat=5))

@@ -3,7 +3,9 @@
 Bars: bit-exact on small-integer inputs (every partial sum is an exact integer below
 2^24); FP32 with U[-1,1] inputs: relative Frobenius error <= 1e-5 and max-abs error
 <= 1e-4 sqrt(K); FP32 with N(0,1) inputs: 1e-5 and 3e-4 sqrt(K); FP16/BF16 inputs,
-against the oracle on the same rounded inputs: relative Frobenius error <= 1e-3.
+against the oracle on the same rounded inputs: relative Frobenius error <= 1e-3 and the
+same element bound as FP32 (16-bit products are exact in binary32; only the FP32
+accumulation rounds).
 Out-of-range reads are caught by NaN-poisoned padding and guard rows, out-of-range
 writes by a sentinel-filled C buffer.
 """
@@ -343,15 +345,27 @@ def test_h16_dma_interior_with_edges():
 # aligned with K ragged by a non-multiple of 8, odd strides, and more tiles than CUs
 # (interior launch, then the ragged strips).  512 x 768 x 200 (whole tiles, K ragged by
 # a multiple of 8, aligned rows) keeps the predicated loads.
-CLAMP_CASES = [((4000, 4004, 256), (0, 0, 0), "all"), ((1000, 1000, 1000), (1, 0, 0), "all"),
-               ((777, 1030, 301), (3, 5, 0), "all"), ((8000, 8004, 64), (0, 0, 0), "rows"),
-               ((512, 768, 200), (0, 0, 0), "all")]
+# Each case states the launches it must get (the kernel description names them): one
+# clamped launch over every tile with the two-set pipeline (an even number of 64-wide
+# k-steps: 4, 16) or with one set (5), an interior launch followed by the clamped strips
+# (a single k-step: one set; two k-steps with 16-byte-aligned padded rows: buffer loads and
+# the two-set pipeline in both launches), and the predicated strips.
+CLAMP_CASES = [((4000, 4004, 256), (0, 0, 0), "all", "all=clamped,paired"),
+               ((1000, 1000, 1000), (1, 0, 0), "all", "edges=clamped,paired"),
+               ((777, 1030, 301), (3, 5, 0), "all", "edges=clamped"),
+               ((8000, 8004, 64), (0, 0, 0), "rows", "interior=pointer edges=clamped"),
+               ((8000, 8004, 128), (0, 4, 4), "rows", "interior=buffer,paired edges=clamped,paired"),
+               ((512, 768, 200), (0, 0, 0), "all", "edges=predicated")]
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("case", CLAMP_CASES, ids=lambda c: "x".join(map(str, c[0])) + f"_pad{c[1][0]}{c[1][1]}")
 def test_h16_clamped_ragged(dtype, case):
-    (M, N, K), pad, cmp = case
+    (M, N, K), pad, cmp, launches = case
+    P = 1 << 20  # a 16-byte-aligned address: the query only inspects it
+    desc = gb.gemm355_kernel_desc(gb.VARIANT_MFMA, gb.DTYPE_CODES[dtype], M, N, K, P, K + pad[0],
+                                  P, N + pad[1], P, N + pad[2])
+    assert desc.endswith("| " + launches), desc
     A, B = inputs.make_operands(M, N, K, 47, "uniform", dtype)
     C, ok = gpu_gemm(A, B, dtype, gb.VARIANT_MFMA, pad=pad, guard_rows=1)
     rows = np.arange(M) if cmp == "all" else np.array(sorted(
