@@ -223,23 +223,27 @@ def time_variant(variant, dtype, M, N, K, seed, reps=None):
     return e0.elapsed_time(e1) / reps, desc, reps
 
 
-def family_run(family, steps, warmup):
+def family_run(family, steps, warmup, dtype="f32", n=0):
     """`warmup` untimed and `steps` timed launches of one kernel family on the FP32 3072^3
-    workload (seed 1), logged to stderr: the target of the ladder's counter passes."""
+    workload (seed 1) or an n^3 FP16/BF16 one (seed 3), logged to stderr: the target of
+    the counter passes."""
     import torch
 
     from roofline_optimisation_amd import binding as gb
     from roofline_optimisation_amd import inputs
 
-    variant = {"naive": gb.VARIANT_NAIVE, "lds_tiled": gb.VARIANT_LDS_TILED,
-               "regblock": gb.VARIANT_REGBLOCK, "mfma": gb.VARIANT_MFMA}[family]
-    n = 3072
-    A, B = inputs.make_operands(n, n, n, 1, "uniform", "f32")
-    dA, dB = torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda()
+    variant = gb.VARIANTS[family]
+    n = n or (3072 if dtype == "f32" else 4096)
+    A, B = inputs.make_operands(n, n, n, 1 if dtype == "f32" else 3, "uniform", dtype)
+    if dtype == "f32":
+        dA, dB = torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda()
+    else:
+        dA = torch.from_numpy(A.view("int16")).cuda()
+        dB = torch.from_numpy(B.view("int16")).cuda()
     dC = torch.empty((n, n), dtype=torch.float32, device="cuda")
     stream = torch.cuda.Stream()
-    args = (variant, gb.F32, n, n, n, dA.data_ptr(), n, dB.data_ptr(), n, dC.data_ptr(), n,
-            stream.cuda_stream)
+    args = (variant, gb.DTYPE_CODES[dtype], n, n, n, dA.data_ptr(), n, dB.data_ptr(), n,
+            dC.data_ptr(), n, stream.cuda_stream)
     desc = gb.gemm355_kernel_desc(*args[:-1])
 
     def launch():
@@ -257,8 +261,68 @@ def family_run(family, steps, warmup):
     e1.record(stream)
     stream.synchronize()
     ms = e0.elapsed_time(e1) / max(steps, 1)
-    log(f"[bench] family {family} ({desc}) f32 {n}^3: {warmup} + {steps} launches, "
+    log(f"[bench] family {family} ({desc}) {dtype} {n}^3: {warmup} + {steps} launches, "
         f"{ms:.4f} ms/launch, {2.0 * n ** 3 / (ms * 1e-3) / 1e12:.2f} TFLOP/s")
+
+
+def schedule_lines(warm=300, rounds=3, reps=100):
+    """The schedules of the FP16 direct-to-LDS kernel at 4096^3 and 8192^3 (U[-1,1] from
+    seed 3): every case warmed, then timed interleaved, median of `rounds` rounds of
+    `reps` launches (HIP events on one stream)."""
+    import torch
+
+    from roofline_optimisation_amd import binding as gb
+    from roofline_optimisation_amd import inputs
+
+    names = [("mfma", "dispatched: 256x256, 4 waves"),
+             ("mfma_split", "split: 256x128, 4 compute + 4 producer waves"),
+             ("mfma_w8", "w8: 256x256, 8 waves (2 per SIMD)"),
+             ("mfma_t256x128", "t256x128: 256x128, 4 waves")]
+    stream = torch.cuda.Stream()
+    out = ["# Schedules of the FP16 direct-to-LDS GEMM kernel on one MI355X", "",
+           f"U[-1,1] binary16 operands (seed 3), FP32 C; {warm} warm-up launches per case, then "
+           f"all cases interleaved, median of {rounds} rounds of {reps} launches; HIP events.", "",
+           "| n | schedule | kernel | µs | TFLOP/s | % of 2516.6 | vs dispatched |", "|---|---|---|---|---|---|---|"]
+    for n in (4096, 8192):
+        A, B = inputs.make_operands(n, n, n, 3, "uniform", "f16")
+        dA = torch.from_numpy(A.view("int16")).cuda()
+        dB = torch.from_numpy(B.view("int16")).cuda()
+        dC = torch.empty((n, n), dtype=torch.float32, device="cuda")
+        runs = []
+        for fam, label in names:
+            v = gb.VARIANTS[fam]
+            args = (v, gb.F16, n, n, n, dA.data_ptr(), n, dB.data_ptr(), n, dC.data_ptr(), n,
+                    stream.cuda_stream)
+            desc = gb.gemm355_kernel_desc(*args[:-1])
+
+            def go(args=args):
+                st = gb.gemm355_run_variant(*args)
+                if st != gb.OK:
+                    raise gb.Gemm355Error(st, "gemm355_run_variant")
+            runs.append((label, desc, go))
+        for label, desc, go in runs:
+            for _ in range(warm):
+                go()
+        stream.synchronize()
+        times = {label: [] for label, _, _ in runs}
+        for _ in range(rounds):
+            for label, desc, go in runs:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for _ in range(reps):
+                    go()
+                e1.record(stream)
+                stream.synchronize()
+                times[label].append(e0.elapsed_time(e1) * 1e3 / reps)
+        base = float(np.median(times[runs[0][0]]))
+        for label, desc, go in runs:
+            us = float(np.median(times[label]))
+            tf = 2.0 * n ** 3 / us / 1e6
+            out.append(f"| {n} | {label} | `{desc}` | {us:.1f} | {tf:.0f} | {100 * tf / PEAKS['f16']:.1f} | "
+                       f"{base / us:.3f}x |")
+            log(f"[schedules] {n}^3 {label}: {us:.1f} us, {tf:.0f} TFLOP/s")
+        del dA, dB, dC
+    return out
 
 
 def general_form_lines():
@@ -675,9 +739,18 @@ def main():
                     help="only measure the row-wise softmax and row sum on their 64 Mi-element "
                          "workloads, write the markdown table to PATH and print one JSON line "
                          "for the 16384 x 4096 workload; no GEMM timing")
-    ap.add_argument("--family", choices=["naive", "lds_tiled", "regblock", "mfma"], default=None,
-                    help="only launch one kernel family on the FP32 3072^3 workload, --warmup "
-                         "untimed and --steps timed launches (for counter passes); no JSON line")
+    ap.add_argument("--family", choices=["naive", "lds_tiled", "regblock", "mfma", "mfma_split",
+                                         "mfma_w8", "mfma_t256x128"], default=None,
+                    help="only launch one kernel family (--warmup untimed and --steps timed "
+                         "launches, for counter passes) on the FP32 3072^3 workload, or with "
+                         "--family-dtype f16/bf16 on the n^3 16-bit workload (seed 3); no JSON line")
+    ap.add_argument("--family-dtype", choices=["f32", "f16", "bf16"], default="f32")
+    ap.add_argument("--family-n", type=int, default=0,
+                    help="square size for --family (default 3072 for f32, 4096 for f16/bf16)")
+    ap.add_argument("--schedules", default=None, metavar="PATH",
+                    help="only time the schedules of the FP16 direct-to-LDS kernel (dispatched, "
+                         "producer/consumer split, eight waves, 256 x 128 tiles) at 4096^3 and "
+                         "8192^3, interleaved, and write the markdown table to PATH")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after the GEMMs, copy this many MiB device-to-device once (a plain "
                          "copy of known size, used to scale the HBM byte counters)")
@@ -715,8 +788,14 @@ def main():
             log(f"[bench] calibration copy of {args.calib_copy_mib} MiB done")
 
     if args.family:
-        family_run(args.family, args.steps, args.warmup)
+        family_run(args.family, args.steps, args.warmup, args.family_dtype, args.family_n)
         calibration_copy()
+        return
+
+    if args.schedules:
+        with open(args.schedules, "w") as f:
+            f.write("\n".join(schedule_lines(warm=max(args.warmup, 1))) + "\n")
+        log(f"[bench] schedule table written to {args.schedules}")
         return
 
     if args.softmax:

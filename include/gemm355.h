@@ -80,7 +80,25 @@ typedef enum gemm355_variant {
     GEMM355_VARIANT_NAIVE = 0,
     GEMM355_VARIANT_LDS_TILED = 1,
     GEMM355_VARIANT_REGBLOCK = 2,
-    GEMM355_VARIANT_MFMA = 3
+    GEMM355_VARIANT_MFMA = 3,
+    /* Other schedules of the FP16/BF16 direct-to-LDS kernel, kept to measure them against
+     * the dispatched one (plain products of F16 / BF16 operands only; any other dtype,
+     * gemm355_gemm_ex flag or a shape the kernel does not take returns
+     * GEMM355_ERR_UNSUPPORTED).  Shapes taken: whole tiles (M a multiple of 256, N of
+     * the tile width), 16-byte-aligned rows, K a multiple of 128.
+     * MFMA_SPLIT: wave specialisation ("Advanced CUDA features - starting from GEMM",
+     *   scheduling section, the warp-specialisation path): 256 x 128 tiles, four producer
+     *   waves issue every global -> LDS load while four compute waves (128 x 64 of C
+     *   each) only read fragments and multiply; one barrier per k-step hands the stages
+     *   over.
+     * MFMA_W8: 256 x 256 tiles on eight waves, two per SIMD (128 x 64 of C each), every
+     *   wave loading its share beside its MFMAs.
+     * MFMA_T256X128: 256 x 128 tiles on four waves (128 x 64 of C each), every wave
+     *   loading: twice as many tiles, so a CU's second tile starts while the first one's
+     *   stores drain. */
+    GEMM355_VARIANT_MFMA_SPLIT = 4,
+    GEMM355_VARIANT_MFMA_W8 = 5,
+    GEMM355_VARIANT_MFMA_T256X128 = 6
 } gemm355_variant;
 
 /* C = A.B with FP32 operands and FP32 accumulation. */

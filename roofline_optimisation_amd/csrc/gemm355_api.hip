@@ -60,6 +60,9 @@ bool variant_supported(int variant, int dtype) {
     case GEMM355_VARIANT_MFMA: return true;
     case GEMM355_VARIANT_LDS_TILED:
     case GEMM355_VARIANT_REGBLOCK: return dtype == kF32;
+    case GEMM355_VARIANT_MFMA_SPLIT:
+    case GEMM355_VARIANT_MFMA_W8:
+    case GEMM355_VARIANT_MFMA_T256X128: return dtype == kF16 || dtype == kBF16;
     default: return false;
     }
 }
@@ -69,18 +72,27 @@ hipError_t launch(int variant, int dtype, const GemmArgs &g, hipStream_t s) {
     case GEMM355_VARIANT_NAIVE: return launch_naive(dtype, g, s);
     case GEMM355_VARIANT_LDS_TILED: return launch_lds_tiled_f32(g, s);
     case GEMM355_VARIANT_REGBLOCK: return launch_regblock_f32(g, s);
+    case GEMM355_VARIANT_MFMA_SPLIT:
+    case GEMM355_VARIANT_MFMA_W8:
+    case GEMM355_VARIANT_MFMA_T256X128: return launch_mfma_f16_sched(variant, dtype, g, s);
     default: return dtype == kF32 ? launch_mfma_f32(g, s) : launch_mfma_f16(dtype, g, s);
     }
+}
+
+bool is_sched_variant(int variant) {
+    return variant >= GEMM355_VARIANT_MFMA_SPLIT && variant <= GEMM355_VARIANT_MFMA_T256X128;
 }
 
 gemm355_status run(int variant, int dtype, int M, int N, int K, const void *A, int lda,
                    const void *B, int ldb, float *C, int ldc, hipStream_t stream) {
     if (!valid_args(dtype, M, N, K, A, lda, B, ldb, C, ldc)) return GEMM355_ERR_INVALID_ARG;
-    if (variant < GEMM355_VARIANT_AUTO || variant > GEMM355_VARIANT_MFMA)
+    if (variant < GEMM355_VARIANT_AUTO || variant > GEMM355_VARIANT_MFMA_T256X128)
         return GEMM355_ERR_INVALID_ARG;
     const GemmArgs g{M, N, K, A, lda, B, ldb, C, ldc};
     if (variant == GEMM355_VARIANT_AUTO) variant = auto_variant(dtype, g);
     if (!variant_supported(variant, dtype)) return GEMM355_ERR_UNSUPPORTED;
+    if (is_sched_variant(variant) && M > 0 && N > 0 && !mfma_f16_sched_ok(variant, g))
+        return GEMM355_ERR_UNSUPPORTED;
     if (M == 0 || N == 0) return GEMM355_OK;
     if (!device_ok()) return GEMM355_ERR_DEVICE;
     // Every kernel starts its accumulators at +0.0, so K = 0 stores the empty sum.
@@ -108,7 +120,7 @@ gemm355_status ex_args(int &variant, int dtype, unsigned flags, int M, int N, in
     if ((long)M * K > 0 && A == nullptr) return GEMM355_ERR_INVALID_ARG;
     if ((long)K * N > 0 && B == nullptr) return GEMM355_ERR_INVALID_ARG;
     if ((long)M * N > 0 && C == nullptr) return GEMM355_ERR_INVALID_ARG;
-    if (variant < GEMM355_VARIANT_AUTO || variant > GEMM355_VARIANT_MFMA)
+    if (variant < GEMM355_VARIANT_AUTO || variant > GEMM355_VARIANT_MFMA_T256X128)
         return GEMM355_ERR_INVALID_ARG;
     g = GemmArgs{M, N, K, A, lda, B, ldb, (float *)C, ldc};
     g.c16 = c16;
@@ -119,6 +131,8 @@ gemm355_status ex_args(int &variant, int dtype, unsigned flags, int M, int N, in
     if (variant == GEMM355_VARIANT_AUTO) variant = auto_variant(dtype, g);
     if (!variant_supported(variant, dtype)) return GEMM355_ERR_UNSUPPORTED;
     if (flags != 0 && variant != GEMM355_VARIANT_NAIVE && variant != GEMM355_VARIANT_MFMA)
+        return GEMM355_ERR_UNSUPPORTED;
+    if (is_sched_variant(variant) && M > 0 && N > 0 && !mfma_f16_sched_ok(variant, g))
         return GEMM355_ERR_UNSUPPORTED;
     return GEMM355_OK;
 }
@@ -139,6 +153,10 @@ const char *desc_of(int variant, int dtype, const GemmArgs &g) {
     case GEMM355_VARIANT_NAIVE: return "naive 64x4 threads, one output each";
     case GEMM355_VARIANT_LDS_TILED: return desc_lds_tiled_f32(g);
     case GEMM355_VARIANT_REGBLOCK: return desc_regblock_f32(g);
+    case GEMM355_VARIANT_MFMA_SPLIT:
+    case GEMM355_VARIANT_MFMA_W8:
+    case GEMM355_VARIANT_MFMA_T256X128:
+        return mfma_f16_sched_ok(variant, g) ? desc_mfma_f16_sched(variant, dtype) : "invalid";
     default: return dtype == kF32 ? desc_mfma_f32(g) : desc_mfma_f16(dtype, g);
     }
 }
@@ -224,6 +242,9 @@ const char *gemm355_variant_name(int variant) {
     case GEMM355_VARIANT_LDS_TILED: return "lds_tiled";
     case GEMM355_VARIANT_REGBLOCK: return "regblock";
     case GEMM355_VARIANT_MFMA: return "mfma";
+    case GEMM355_VARIANT_MFMA_SPLIT: return "mfma_split";
+    case GEMM355_VARIANT_MFMA_W8: return "mfma_w8";
+    case GEMM355_VARIANT_MFMA_T256X128: return "mfma_t256x128";
     default: return "unknown";
     }
 }

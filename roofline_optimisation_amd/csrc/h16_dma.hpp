@@ -35,40 +35,48 @@
 // The loads are issued from inline assembly (m0 holds the LDS destination), so the
 // compiler neither tracks them nor waits for them; the kernel's own s_waitcnt vmcnt
 // instructions do, and no other code of this kernel uses m0.
+//
+// The tile routine is written over a general geometry (an EM x EN tile, WM x WN compute
+// waves, NS ring stages, PW producer waves) so that other schedules of the same data
+// movement can be built and measured against the dispatched one: the dispatched kernels
+// are EM = EN = 256 or 128 on 2 x 2 waves that all load; mfma_f16_dma_sched_kernel
+// instantiates the others (wave specialisation with producer waves, eight waves, 256 x
+// 128 tiles).
 #pragma once
 
 namespace dma {
 
 constexpr int kBK = 32;
-constexpr int kWM = 2, kWN = 2, kWaves = kWM * kWN;
 
-// Geometry of an E x E tile (E = 256 or 128; both operands have extent E).  A 128-wide
-// tile's k-step is a quarter of a 256-wide one's arithmetic (16 MFMAs, ~130 ns), so its
-// ring has kNs = 8 stages instead of 4 to keep the loads as far ahead in time.
-template <int E>
+// Ring stages (32-wide k-steps) of a tile whose operands have extent E: 4 of 16 KiB per
+// operand for 256-wide tiles, 8 of 8 KiB for 128-wide ones.  A 128-wide tile's k-step is a
+// quarter of a 256-wide one's arithmetic (16 MFMAs per wave, ~130 ns), so its ring is
+// twice as deep to keep the loads as far ahead in time.
+constexpr int ring_stages(int E) { return E == 256 ? 4 : 8; }
+
+// Geometry of an EM x EN tile: WM x WN compute waves, each owning (EM / WM) x (EN / WN) of
+// C; NS ring stages; PW producer waves.  With PW = 0 every compute wave issues its share
+// of the loads beside its MFMAs (the dispatched kernels); with PW > 0 only the PW
+// producer waves load and the compute waves only read fragments and multiply.
+template <int EM, int EN, int WM, int WN, int NS, int PW>
 struct Geo {
-    static constexpr int kNs = E == 256 ? 4 : 8;  // ring stages (k-steps)
-    static constexpr int kTM = E / kWM, kTN = E / kWN;     // wave tile
-    static constexpr int kMB = kTM / 16, kNB = kTN / 16;    // accumulator quads per wave
-    static constexpr int kStage = E * kBK * 2;   // bytes per operand per stage (E x 32)
-    static constexpr int kBOff = kNs * kStage;   // the B ring follows the A ring
-    static constexpr int kLds = 2 * kNs * kStage;
-    static constexpr int kI = kStage / 1024 / kWaves;  // MN: 1 KiB loads per wave per k-step
-    static constexpr int kRowB = 2 * E;          // MN: bytes per LDS row (one k)
-    static constexpr int kRpi = 1024 / kRowB;    // MN: rows one load instruction fills
-    static constexpr int kKMRows = E / kWaves;   // KM: rows one wave fills
+    static constexpr int kCW = WM * WN;                   // compute waves
+    static constexpr int kLW = PW > 0 ? PW : kCW;         // waves that issue the loads
+    static constexpr int kWaves = kCW + PW;
+    static constexpr int kNs = NS;
+    static constexpr int kTM = EM / WM, kTN = EN / WN;    // wave tile
+    static constexpr int kMB = kTM / 16, kNB = kTN / 16;  // accumulator quads per wave
+    static constexpr int kStageA = EM * kBK * 2, kStageB = EN * kBK * 2;  // bytes per stage
+    static constexpr int kBOff = NS * kStageA;            // the B ring follows the A ring
+    static constexpr int kLds = NS * (kStageA + kStageB);
     // MFMAs per k-step, the step's wait and barrier after kBarrier of them, its loads
     // spread over the first kLoadHi
     static constexpr int kMf = kMB * kNB;
-    static constexpr int kBarrier = E == 256 ? 40 : 10;
-    static constexpr int kLoadHi = E == 256 ? 32 : 8;
-    static_assert(E == 256 || E == 128, "tile extents");
+    static constexpr int kBarrier = kMf * 5 / 8;
+    static constexpr int kLoadHi = kMf / 2;
+    static_assert(kTM % 16 == 0 && kTN % 16 == 0, "wave tiles are whole 16 x 16 quads");
+    static_assert(NS % 2 == 0 && NS >= 4, "a KM operand's double steps take two stages each");
     static_assert(kLds <= 160 * 1024, "LDS budget");
-    static_assert(kI * kRpi == 8, "an MN operand's wave fills 8 rows, all of one (k / 8) parity");
-    static_assert(kKMRows / 8 == 2 * kI, "a KM double step takes twice an MN step's loads");
-    // every ds_read immediate (slot / stage + block / row offsets) stays below 64 KiB
-    static_assert((kNs / 2 - 1) * 2 * kStage + (kMB - 1) * 2048 < 65536, "KM read offsets");
-    static_assert((kNs - 1) * kStage + 4 * kRowB < 65536, "MN read offsets");
     static_assert(kLoadHi <= kBarrier && kBarrier < kMf, "the step's loads precede its wait");
 };
 
@@ -123,60 +131,79 @@ __device__ __forceinline__ lds_char *lds_reg(lds_char *p) {
 }
 
 // Loads and fragment reads of one operand of extent E in its region at byte offset
-// `roff` (4 E x 32 x 2 bytes: 64 KiB for E = 256).
-//  * MN (m/n-contiguous): a ring of kNs stages of one 32-wide k-step (E x 32 halves,
-//    rows of 2 E bytes).  Wave w fills rows [8 w, +8): instruction i rows
-//    8 w + R i + l / (64 / R) with R = 1024 / (2 E) rows per instruction, lane slot
-//    l % (64 / R) taking chunk slot ^ 4 (row % 4) ^ 2 ((row / 8) % 2), where
-//    (row / 8) % 2 = w % 2 and row % 4 = l/32 + 2 (i % 2) (E = 256) or l/16 (E = 128).
-//  * KM (k-contiguous): kNs / 2 slots of one 64-wide double step (E rows of 128 bytes),
+// `roff` (NS x E x 32 x 2 bytes: 64 KiB for E = 256 and 4 stages), LW waves sharing its
+// loads, NB accumulator quads along it per compute wave.
+//  * MN (m/n-contiguous): a ring of NS stages of one 32-wide k-step (E x 32 halves,
+//    rows of 2 E bytes).  Loading wave w fills rows [R w, +R) with R = 32 / LW (8 or 4):
+//    instruction i rows R w + P i + l / (64 / P) with P = 1024 / (2 E) rows per
+//    instruction, lane slot l % (64 / P) taking chunk slot ^ 4 (row % 4) ^ 2 ((row / 8)
+//    % 2), where (row / 8) % 2 = (R w / 8) % 2 and row % 4 = (P i + l / (64 / P)) % 4,
+//    which depends on i only through its parity.
+//  * KM (k-contiguous): NS / 2 slots of one 64-wide double step (E rows of 128 bytes),
 //    so that every load reads whole 128-byte lines; k-step t uses half t % 2 of slot
-//    (t / 2) % (kNs / 2).  Wave w fills rows [E/4 w, +E/4), instruction i rows 8 i + l/8, lane
-//    slot l%8 taking chunk slot ^ ((row / 2) % 8), where (row / 2) % 8 =
-//    4 (i % 2) + l/16.
-template <bool MN, int E>
+//    (t / 2) % (NS / 2).  Loading wave w fills rows [R w, +R) with R = E / LW (a multiple
+//    of 16), instruction i rows R w + 8 i + l/8, lane slot l%8 taking chunk slot ^ ((row
+//    / 2) % 8), where (row / 2) % 8 = 4 (i % 2) + l/16.
+template <bool MN, int E, int LW, int NS, int NB>
 struct DmaOp {
-    using G = Geo<E>;
-    static constexpr int NB = E / 32;                // quads along this operand per wave
-    static constexpr int kSlot = 2 * G::kStage;      // KM slot bytes
-    static constexpr int kPieces = MN ? 2 : 1;       // LDS reads per fragment
+    static constexpr int kStage = E * kBK * 2;       // MN stage bytes
+    static constexpr int kSlot = 2 * kStage;         // KM slot bytes
+    static constexpr int kRowB = 2 * E;              // MN: bytes per LDS row (one k)
+    static constexpr int kRpi = 1024 / kRowB;        // MN: rows one load instruction fills
+    static constexpr int kRows = MN ? kBK / LW : E / LW;  // rows a loading wave fills
+    // load instructions per loading wave: per k-step (MN) or per double step (KM)
+    static constexpr int kI = MN ? kRows / kRpi : kRows / 8;
+    static_assert(kI >= 1, "every loading wave issues a whole instruction");
+    static_assert(!MN || (kRows * LW == kBK && kI * kRpi == kRows && 8 % kRows == 0),
+                  "an MN operand's loading wave fills rows of one (k / 8) parity");
+    static_assert(MN || (kRows * LW == E && kRows % 16 == 0), "KM rows per loading wave");
+    // every ds_read immediate (slot / stage + block / row offsets) stays below 64 KiB
+    static_assert(MN || (NS / 2 - 1) * kSlot + (NB - 1) * 2048 < 65536, "KM read offsets");
+    static_assert(!MN || (NS - 1) * kStage + 4 * kRowB < 65536, "MN read offsets");
     int4v rsrc;
-    uint32_t voff[MN ? 2 : 2 * G::kI];   // per lane: MN by instruction parity, KM by instruction
+    uint32_t voff[MN ? 2 : kI];   // per lane: MN by instruction parity, KM by instruction
     lds_char *rd[MN ? NB : 2];
     H16Frag<MN, NB> fr;
 
-    // X: the operand, whose rows (KM) or columns (MN) number ext (a multiple of 8 for
-    // MN); mn0: the tile's first row (KM) or column (MN); wb: the wave's first row or
-    // column within the tile.  In a ragged tile a lane whose source row (KM) or 16-byte
+    // Loading side.  X: the operand, whose rows (KM) or columns (MN) number ext (a
+    // multiple of 8 for MN); mn0: the tile's first row (KM) or column (MN); lw: the
+    // loading wave's index.  In a ragged tile a lane whose source row (KM) or 16-byte
     // column chunk (MN) lies beyond ext loads the last one inside instead, so every load
     // stays within the operand; what it puts in LDS only reaches outputs beyond row M or
     // column N, which are never stored.
-    __device__ __forceinline__ void init(const uint16_t *X, int ld, int ext, int mn0, int wave,
-                                         int lane, lds_char *L, int roff, int wb) {
+    __device__ __forceinline__ void init_load(const uint16_t *X, int ld, int ext, int mn0, int lw,
+                                              int lane) {
         if constexpr (MN) {
-            constexpr int lpr = 64 / G::kRpi;        // lanes per row of one load
+            constexpr int lpr = 64 / kRpi;           // lanes per row of one load
             rsrc = rsrc_of(X + mn0);
-            const int rl = lane / lpr, row = 8 * wave + rl, slot = lane % lpr;
-            const int kx = 2 * (wave & 1), last = (ext - mn0) / 8 - 1;
+            const int rl = lane / lpr, row = kRows * lw + rl, slot = lane % lpr;
+            const int kx = 2 * ((kRows * lw / 8) & 1), last = (ext - mn0) / 8 - 1;
 #pragma unroll
             for (int p = 0; p < 2; ++p)
-                voff[p] = (uint32_t)((row * ld + 8 * min(slot ^ (4 * ((G::kRpi * p + rl) % 4)) ^ kx, last)) * 2);
+                voff[p] = (uint32_t)((row * ld + 8 * min(slot ^ (4 * ((kRpi * p + rl) % 4)) ^ kx, last)) * 2);
+        } else {
+            rsrc = rsrc_of(X + (size_t)mn0 * ld);
+            const int row = kRows * lw + lane / 8, slot = lane & 7, last = ext - mn0 - 1;
+#pragma unroll
+            for (int i = 0; i < kI; ++i)
+                voff[i] = (uint32_t)((min(row + 8 * i, last) * ld +
+                                      8 * (slot ^ ((4 * (i % 2) + lane / 16) & 7))) * 2);
+        }
+    }
+    // Compute side: the fragment read addresses of the wave whose first row or column
+    // within the tile is wb (a multiple of 16).
+    __device__ __forceinline__ void init_read(int lane, lds_char *L, int roff, int wb) {
+        if constexpr (MN) {
             // block b, piece h: lane (g = l/16, e = (l%16)/4, q = l%4) reads row 8 g + 4 h +
             // e, chunk wb/8 + 2 b + q/2, byte 8 (q%2) of it; that row's swizzle key is
             // 4 e ^ 2 (g%2)
             const int g = lane >> 4, e = (lane & 15) >> 2, q = lane & 3;
 #pragma unroll
             for (int b = 0; b < NB; ++b)
-                rd[b] = lds_reg(L + roff + (8 * g + e) * G::kRowB +
+                rd[b] = lds_reg(L + roff + (8 * g + e) * kRowB +
                                 16 * ((wb / 8 + 2 * b + (q >> 1)) ^ (4 * e) ^ (2 * (g & 1))) +
                                 8 * (q & 1));
         } else {
-            rsrc = rsrc_of(X + (size_t)mn0 * ld);
-            const int row = G::kKMRows * wave + lane / 8, slot = lane & 7, last = ext - mn0 - 1;
-#pragma unroll
-            for (int i = 0; i < 2 * G::kI; ++i)
-                voff[i] = (uint32_t)((min(row + 8 * i, last) * ld +
-                                      8 * (slot ^ ((4 * (i % 2) + lane / 16) & 7))) * 2);
             // block b, half h of the slot: row wb + 16 b + l%16, chunk 4 h + l/16, whose
             // swizzle key ((l%16) / 2) % 8 does not depend on b
             const int l16 = lane & 15, lq = lane >> 4;
@@ -187,22 +214,22 @@ struct DmaOp {
     }
     // Load instruction i of one issue: MN: k-step at k0 into stage `place`; KM: the
     // double step at k0 into slot `place`.
-    __device__ __forceinline__ void issue(uint32_t lds0, int roff, int wave, int ld, int place,
+    __device__ __forceinline__ void issue(uint32_t lds0, int roff, int lw, int ld, int place,
                                           int k0, int i) {
         if constexpr (MN) {
-            const uint32_t dst = lds0 + roff + place * G::kStage + (wave * G::kI + i) * 1024;
-            load_lds16(dst, voff[i & 1], rsrc, (uint32_t)((k0 + G::kRpi * i) * ld * 2));
+            const uint32_t dst = lds0 + roff + place * kStage + (lw * kI + i) * 1024;
+            load_lds16(dst, voff[i & 1], rsrc, (uint32_t)((k0 + kRpi * i) * ld * 2));
         } else {
-            const uint32_t dst = lds0 + roff + place * kSlot + (wave * 2 * G::kI + i) * 1024;
+            const uint32_t dst = lds0 + roff + place * kSlot + (lw * kI + i) * 1024;
             load_lds16(dst, voff[i], rsrc, (uint32_t)(k0 * 2));
         }
     }
-    // Piece h of block b of k-step u (u = t % kNs, so the MN stage is u, the KM slot
+    // Piece h of block b of k-step u (u = t % NS, so the MN stage is u, the KM slot
     // u / 2 and the KM half u % 2) into fragment slot `fslot`.
     __device__ __forceinline__ void read(int u, int fslot, int b, int h) {
         if constexpr (MN) {
             fr.f[fslot][b][h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_shortx4 *)(rd[b] + u * G::kStage + 4 * h * G::kRowB));
+                (lds_shortx4 *)(rd[b] + u * kStage + 4 * h * kRowB));
         } else {
             fr.f[fslot][b] = *(const lds_u16x8 *)(rd[u % 2] + (u / 2) * kSlot + b * 2048);
         }
@@ -212,9 +239,8 @@ struct DmaOp {
 // The order in which a k-step's fragment pieces are read: A block 0, then the B blocks,
 // then the other A blocks, i.e. in the order the MFMAs (A block outer, B block inner,
 // odd rows walking the B blocks backwards) first use them.
-template <bool A_MN, bool B_MN, int E>
+template <bool A_MN, bool B_MN, int kMB, int kNB>
 struct PieceOrder {
-    static constexpr int kMB = Geo<E>::kMB, kNB = Geo<E>::kNB;
     static constexpr int kPA = A_MN ? 2 : 1, kPB = B_MN ? 2 : 1;
     static constexpr int kR = kMB * kPA + kNB * kPB;
     // piece p -> (operand 0 = A / 1 = B, block, half)
@@ -227,10 +253,10 @@ struct PieceOrder {
     }
 };
 
-// kstep(kt, integral_constant<u>) for u = 0 .. kNs-1 in order.
-template <typename F, int... U>
-__device__ __forceinline__ void for_steps(F &kstep, int kt, std::integer_sequence<int, U...>) {
-    (kstep(kt, std::integral_constant<int, U>{}), ...);
+// kstep(kt, integral_constant<u>, b) for u = 0 .. kNs-1 in order.
+template <typename F, typename B, int... U>
+__device__ __forceinline__ void for_steps(F &kstep, int kt, std::integer_sequence<int, U...>, B b) {
+    (kstep(kt, std::integral_constant<int, U>{}, b), ...);
 }
 
 // Empty volatile statements that take every accumulator quad in and out of an AGPR:
@@ -285,46 +311,122 @@ __device__ __forceinline__ void store_tile(floatx4 (&acc)[kMB][kNB], float *__re
     }
 }
 
-template <typename T, bool A_MN, bool B_MN, int EPI, int E>
+// WHOLE: the caller guarantees that the tile lies inside M x N (no guarded stores).
+template <typename T, bool A_MN, bool B_MN, int EPI, int EM, int EN, int WM, int WN, int NS, int PW,
+          bool WHOLE = false>
 __device__ __forceinline__ void dma_tile(int M, int N, int K, const uint16_t *__restrict__ A, int lda,
                                          const uint16_t *__restrict__ B, int ldb,
                                          float *__restrict__ C, int ldc, float sign,
                                          int flags, int m0, int n0, char *lds_raw) {
+    using G = Geo<EM, EN, WM, WN, NS, PW>;
+    constexpr int kMB = G::kMB, kNB = G::kNB, kBOff = G::kBOff, kNs = NS, kLW = G::kLW;
+    using OA = DmaOp<A_MN, EM, kLW, NS, kMB>;
+    using OB = DmaOp<B_MN, EN, kLW, NS, kNB>;
+    using PO = PieceOrder<A_MN, B_MN, kMB, kNB>;
     const int lane = threadIdx.x % 64;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
-    const int wm = wave / kWN, wn = wave % kWN;
     const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_char *)lds_raw;
     lds_char *const L = (lds_char *)lds_raw;
-
-    using G = Geo<E>;
-    constexpr int kMB = G::kMB, kNB = G::kNB, kI = G::kI, kBOff = G::kBOff, kNs = G::kNs;
-    using OA = DmaOp<A_MN, E>;
-    using OB = DmaOp<B_MN, E>;
-    using PO = PieceOrder<A_MN, B_MN, E>;
     OA oa;
     OB ob;
-    oa.init(A, lda, M, m0, wave, lane, L, 0, wm * G::kTM);
-    ob.init(B, ldb, N, n0, wave, lane, L, kBOff, wn * G::kTN);
-    // Loads per wave: nMN every k-step (the MN operands' next stage), nKM every other
-    // k-step (the KM operands' next double step), MN loads first.
-    constexpr int nMN = (A_MN ? kI : 0) + (B_MN ? kI : 0);
-    constexpr int nKM = (A_MN ? 0 : 2 * kI) + (B_MN ? 0 : 2 * kI);
+    // Loads per loading wave: nMN every k-step (the MN operands' next stage), nKM every
+    // other k-step (the KM operands' next double step), MN loads first.
+    constexpr int nMN = (A_MN ? OA::kI : 0) + (B_MN ? OB::kI : 0);
+    constexpr int nKM = (A_MN ? 0 : OA::kI) + (B_MN ? 0 : OB::kI);
     // issue w of an MN batch (k-step at k0 into stage st) / of a KM batch (double step at
-    // k0 into slot sl)
-    auto issue_mn = [&](int st, int k0, int w) {
+    // k0 into slot sl), by loading wave lw
+    auto issue_mn = [&](int lw, int st, int k0, int w) {
         if constexpr (A_MN) {
-            if (w < kI) { oa.issue(lds0, 0, wave, lda, st, k0, w); return; }
-            w -= kI;
+            if (w < OA::kI) { oa.issue(lds0, 0, lw, lda, st, k0, w); return; }
+            w -= OA::kI;
         }
-        if constexpr (B_MN) ob.issue(lds0, kBOff, wave, ldb, st, k0, w);
+        if constexpr (B_MN) ob.issue(lds0, kBOff, lw, ldb, st, k0, w);
     };
-    auto issue_km = [&](int sl, int k0, int w) {
+    auto issue_km = [&](int lw, int sl, int k0, int w) {
         if constexpr (!A_MN) {
-            if (w < 2 * kI) { oa.issue(lds0, 0, wave, lda, sl, k0, w); return; }
-            w -= 2 * kI;
+            if (w < OA::kI) { oa.issue(lds0, 0, lw, lda, sl, k0, w); return; }
+            w -= OA::kI;
         }
-        if constexpr (!B_MN) ob.issue(lds0, kBOff, wave, ldb, sl, k0, w);
+        if constexpr (!B_MN) ob.issue(lds0, kBOff, lw, ldb, sl, k0, w);
     };
+    const int nk = K / kBK;
+    // The wait before the barrier of k-step u (u = t % kNs): loads are issued in step
+    // order (a step's MN loads, then its KM loads), the prologue's included, so the wait
+    // counts are the loads of the steps after the one that issued what step t+1 needs: on
+    // an even step t both of its operands' loads came from step t - kNs + 2, so the loads
+    // of the kNs - 2 steps after it may stay in flight; on an odd step its KM loads came
+    // from step t - kNs + 3 (those of kNs - 3 later steps may stay), its MN loads alone
+    // from t - kNs + 2.
+    auto wait_before_barrier = [](auto u_c) {
+        constexpr int u = decltype(u_c)::value;
+        constexpr bool even = u % 2 == 0;
+        constexpr int kWait = even ? (kNs - 2) * nMN + (kNs - 2) / 2 * nKM
+                                   : (nKM ? (kNs - 3) * nMN + (kNs - 4) / 2 * nKM : (kNs - 2) * nMN);
+        static_assert(kWait < 64, "vmcnt range");
+        wait_vmcnt<kWait>();
+    };
+    // Prologue, in the order the steps before step 0 would have issued it: KM double step
+    // 0, then MN k-steps 0 .. kNs-2 into stages 0 .. kNs-2, KM double step d after MN
+    // k-step 2d + 1 (d = 1 .. kNs/2 - 2); then wait for step 0's data (everything after
+    // MN k-step 0 may stay in flight).
+    auto prologue_loads = [&](int lw) {
+#pragma unroll
+        for (int w = 0; w < nKM; ++w) issue_km(lw, 0, 0, w);
+#pragma unroll
+        for (int p = 0; p < kNs - 1; ++p) {
+#pragma unroll
+            for (int w = 0; w < nMN; ++w) issue_mn(lw, p, min(p, nk - 1) * kBK, w);
+            if (p % 2 == 1 && p >= 3) {
+#pragma unroll
+                for (int w = 0; w < nKM; ++w)
+                    issue_km(lw, (p - 1) / 2, min((p - 1) / 2, nk / 2 - 1) * 2 * kBK, w);
+            }
+        }
+        wait_vmcnt<(kNs - 2) * nMN + (kNs / 2 - 2) * nKM>();
+    };
+    // The loads of k-step t = kt + u: MN: k-step t + kNs - 1 into stage (u - 1) % kNs; on
+    // even steps KM: double step t/2 + kNs/2 - 1 into the slot of double step t/2 - 1.  No
+    // branches: near the end the loads repeat the last k-step or double step into free
+    // stages or slots.
+    auto k_mn_of = [&](int t) { return min(t + kNs - 1, nk - 1) * kBK; };
+    auto k_km_of = [&](int t) { return min(t / 2 + kNs / 2 - 1, nk / 2 - 1) * 2 * kBK; };
+    auto step_load = [&](int lw, int u, int w, int k_mn, int k_km) {
+        if (w < nMN) issue_mn(lw, (u + kNs - 1) % kNs, k_mn, w);
+        else issue_km(lw, (u / 2 + kNs / 2 - 1) % (kNs / 2), k_km, w - nMN);
+    };
+
+    if constexpr (PW > 0) {
+        // Producer waves: every load of the tile, one barrier per k-step (the compute
+        // waves' barrier), nothing else.
+        if (wave >= G::kCW) {
+            const int lw = wave - G::kCW;
+            oa.init_load(A, lda, M, m0, lw, lane);
+            ob.init_load(B, ldb, N, n0, lw, lane);
+            prologue_loads(lw);
+            __syncthreads();
+            auto pstep = [&](int kt, auto u_c, auto) {
+                constexpr int u = decltype(u_c)::value;
+                constexpr int nLd = nMN + (u % 2 == 0 ? nKM : 0);
+                const int k_mn = k_mn_of(kt + u), k_km = k_km_of(kt + u);
+#pragma unroll
+                for (int w = 0; w < nLd; ++w) step_load(lw, u, w, k_mn, k_km);
+                wait_before_barrier(u_c);
+                __syncthreads();
+            };
+            for (int kt = 0; kt < nk; kt += kNs)
+                for_steps(pstep, kt, std::make_integer_sequence<int, kNs>{}, 0);
+            // nothing may still write this workgroup's LDS when it exits
+            wait_vmcnt<0>();
+            return;
+        }
+    }
+    const int wm = wave / WN, wn = wave % WN;
+    if constexpr (PW == 0) {
+        oa.init_load(A, lda, M, m0, wave, lane);
+        ob.init_load(B, ldb, N, n0, wave, lane);
+    }
+    oa.init_read(lane, L, 0, wm * G::kTM);
+    ob.init_read(lane, L, kBOff, wn * G::kTN);
     constexpr int kR = PO::kR;
     auto read_piece = [&](int u, int fslot, int p) {
         if (PO::op(p) == 0) oa.read(u, fslot, PO::blk(p), PO::half(p));
@@ -334,38 +436,27 @@ __device__ __forceinline__ void dma_tile(int M, int N, int K, const uint16_t *__
     floatx4 acc[kMB][kNB];
 
     // One k-step t = kt + u (u = t % kNs is a compile-time constant): kMf MFMAs on the
-    // fragments in slot u % 2.  The step's loads (MN: k-step t + kNs - 1 into stage
-    // (u - 1) % kNs; on even steps KM: double step t/2 + kNs/2 - 1 into the slot of double
-    // step t/2 - 1) are spread over the first kLoadHi MFMAs; after kBarrier MFMAs the wave
-    // waits until the loads step t+1 needs are done, then the barrier publishes them and
-    // the fragments of t+1 are read into the other slot under the remaining MFMAs, in the
-    // order of their first use.  Loads are issued in step order (a step's MN loads, then
-    // its KM loads), the prologue's included, so the wait counts are the loads of the
-    // steps after the one that issued what step t+1 needs: on an even step t both of its
-    // operands' loads came from step t - kNs + 2, so the loads of the kNs - 2 steps after
-    // it may stay in flight; on an odd step its KM loads came from step t - kNs + 3
-    // (those of kNs - 3 later steps may stay), its MN loads alone from t - kNs + 2.  No
-    // branches: near the end the loads repeat the last k-step or double step into free
-    // stages or slots.
-    constexpr int kMf = G::kMf, kBarrier = G::kBarrier, kLoadHi = G::kLoadHi;
+    // fragments in slot u % 2.  The step's loads (when the compute waves issue them) are
+    // spread over the first kLoadHi MFMAs; after kBarrier MFMAs the wave waits until the
+    // loads step t+1 needs are done, then the barrier publishes them and the fragments of
+    // t+1 are read into the other slot under the remaining MFMAs, in the order of their
+    // first use.
+    constexpr int kMf = G::kMf;
     auto ev_begin = [](int qs, int n, int lo, int hi) {
         if (qs <= lo) return 0;
         if (qs >= hi) return n;
         return ((qs - lo) * n + (hi - lo) - 1) / (hi - lo);
     };
-    const int nk = K / kBK;
-    auto kstep = [&](int kt, auto u_c) {
+    auto kstep = [&](int kt, auto u_c, auto b_c) {
         constexpr int u = decltype(u_c)::value;
+        constexpr int kBarrier = decltype(b_c)::value;
+        constexpr int kLoadHi = kBarrier < G::kLoadHi ? kBarrier : G::kLoadHi;
+        static_assert(kBarrier >= 1 && kBarrier < kMf, "barrier position");
         constexpr int u1 = (u + 1) % kNs;
         constexpr int f = u % 2;
-        constexpr bool even = u % 2 == 0;
-        constexpr int nLd = nMN + (even ? nKM : 0);
-        constexpr int kWait = even ? (kNs - 2) * nMN + (kNs - 2) / 2 * nKM
-                                   : (nKM ? (kNs - 3) * nMN + (kNs - 4) / 2 * nKM : (kNs - 2) * nMN);
-        static_assert(kWait < 64, "vmcnt range");
+        constexpr int nLd = PW > 0 ? 0 : nMN + (u % 2 == 0 ? nKM : 0);
         const int t = kt + u;
-        const int k_mn = min(t + kNs - 1, nk - 1) * kBK;
-        const int k_km = min(t / 2 + kNs / 2 - 1, nk / 2 - 1) * 2 * kBK;
+        const int k_mn = k_mn_of(t), k_km = k_km_of(t);
 #pragma unroll
         for (int qs = 0; qs < kMf; ++qs) {
             // snake order: odd block rows walk the B blocks backwards, so consecutive
@@ -379,40 +470,21 @@ __device__ __forceinline__ void dma_tile(int M, int N, int K, const uint16_t *__
 #pragma unroll
                 for (int o = lo; o < hi; ++o) read_piece(u1, 1 - f, o);
             }
-            {
+            if constexpr (nLd > 0) {
                 const int lo = ev_begin(qs, nLd, 0, kLoadHi);
                 const int hi = ev_begin(qs + 1, nLd, 0, kLoadHi);
 #pragma unroll
-                for (int w = lo; w < hi; ++w) {
-                    if (w < nMN) issue_mn((u + kNs - 1) % kNs, k_mn, w);
-                    else issue_km((u / 2 + kNs / 2 - 1) % (kNs / 2), k_km, w - nMN);
-                }
+                for (int w = lo; w < hi; ++w) step_load(wave, u, w, k_mn, k_km);
             }
             if (qs == kBarrier - 1) {
-                wait_vmcnt<kWait>();
+                if constexpr (PW == 0) wait_before_barrier(u_c);
                 __syncthreads();
             }
             __builtin_amdgcn_sched_barrier(0);
         }
     };
 
-    // Prologue, in the order the steps before step 0 would have issued it: KM double step
-    // 0, then MN k-steps 0 .. kNs-2 into stages 0 .. kNs-2, KM double step d after MN
-    // k-step 2d + 1 (d = 1 .. kNs/2 - 2); wait for step 0's data (everything after MN
-    // k-step 0 may stay in flight), read its fragments
-#pragma unroll
-    for (int w = 0; w < nKM; ++w) issue_km(0, 0, w);
-#pragma unroll
-    for (int p = 0; p < kNs - 1; ++p) {
-#pragma unroll
-        for (int w = 0; w < nMN; ++w) issue_mn(p, min(p, nk - 1) * kBK, w);
-        if (p % 2 == 1 && p >= 3) {
-#pragma unroll
-            for (int w = 0; w < nKM; ++w)
-                issue_km((p - 1) / 2, min((p - 1) / 2, nk / 2 - 1) * 2 * kBK, w);
-        }
-    }
-    wait_vmcnt<(kNs - 2) * nMN + (kNs / 2 - 2) * nKM>();
+    if constexpr (PW == 0) prologue_loads(wave);
     __syncthreads();
 #pragma unroll
     for (int p = 0; p < kR; ++p) read_piece(0, 0, p);
@@ -427,13 +499,14 @@ __device__ __forceinline__ void dma_tile(int M, int N, int K, const uint16_t *__
     pin_acc(acc);
     asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
     for (int kt = 0; kt < nk; kt += kNs)
-        for_steps(kstep, kt, std::make_integer_sequence<int, kNs>{});
+        for_steps(kstep, kt, std::make_integer_sequence<int, kNs>{},
+                  std::integral_constant<int, G::kBarrier>{});
     // nothing may still write this workgroup's LDS when it exits
-    wait_vmcnt<0>();
+    if constexpr (PW == 0) wait_vmcnt<0>();
     pin_acc(acc);
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
     pin_acc(acc);
-    if (m0 + E <= M && n0 + E <= N)
+    if (WHOLE || (m0 + EM <= M && n0 + EN <= N))
         store_tile<EPI, T, false>(acc, C, ldc, m0 + wm * G::kTM, n0 + wn * G::kTN, M, N, sign, flags);
     else
         store_tile<EPI, T, true>(acc, C, ldc, m0 + wm * G::kTM, n0 + wn * G::kTN, M, N, sign, flags);
@@ -444,13 +517,29 @@ __device__ __forceinline__ void dma_tile(int M, int N, int K, const uint16_t *__
 // One workgroup per CU (128 KiB of LDS for either tile; E = 256 also takes all 256
 // accumulator registers of a lane).
 template <typename T, bool A_MN, bool B_MN, int EPI, int E>
-__global__ __launch_bounds__(64 * dma::kWaves) __attribute__((amdgpu_waves_per_eu(1)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1)))
 void mfma_f16_dma_kernel(int M, int N, int K, const uint16_t *__restrict__ A, int lda,
                          const uint16_t *__restrict__ B, int ldb, float *__restrict__ C,
                          int ldc, float sign, int flags) {
-    __shared__ __attribute__((aligned(1024))) char lds[dma::Geo<E>::kLds];
+    constexpr int kNs = dma::ring_stages(E);
+    __shared__ __attribute__((aligned(1024))) char lds[dma::Geo<E, E, 2, 2, kNs, 0>::kLds];
     int tm, tn;
     grouped_tile(xcd_contiguous_id(blockIdx.x, gridDim.x), cdiv(M, E), cdiv(N, E), 4, tm, tn);
-    dma::dma_tile<T, A_MN, B_MN, EPI, E>(M, N, K, A, lda, B, ldb, C, ldc, sign, flags, tm * E, tn * E,
-                                         lds);
+    dma::dma_tile<T, A_MN, B_MN, EPI, E, E, 2, 2, kNs, 0>(M, N, K, A, lda, B, ldb, C, ldc, sign, flags,
+                                                           tm * E, tn * E, lds);
+}
+
+// Schedules of the same data movement that are kept for measurement (gemm355_run_variant
+// with the MFMA_* schedule variants; plain products of whole tiles only): an EM x EN tile
+// on WM x WN compute waves and PW producer waves, NS ring stages, one workgroup per CU.
+template <typename T, int EM, int EN, int WM, int WN, int NS, int PW>
+__global__ __launch_bounds__(64 * (WM * WN + PW)) __attribute__((amdgpu_waves_per_eu((WM * WN + PW + 3) / 4)))
+void mfma_f16_dma_sched_kernel(int M, int N, int K, const uint16_t *__restrict__ A, int lda,
+                               const uint16_t *__restrict__ B, int ldb, float *__restrict__ C,
+                               int ldc) {
+    __shared__ __attribute__((aligned(1024))) char lds[dma::Geo<EM, EN, WM, WN, NS, PW>::kLds];
+    int tm, tn;
+    grouped_tile(xcd_contiguous_id(blockIdx.x, gridDim.x), cdiv(M, EM), cdiv(N, EN), 4, tm, tn);
+    dma::dma_tile<T, false, true, 0, EM, EN, WM, WN, NS, PW, true>(M, N, K, A, lda, B, ldb, C, ldc, 1.0f,
+                                                                    0, tm * EM, tn * EN, lds);
 }

@@ -511,7 +511,7 @@ inline bool op_fits(bool mn, int ext, int K, int ld) {
 // cycles of MFMAs) run at the CU's load-path rate, so the kernel is load-bound there;
 // it still beats the register-staged kernel by 10-20 % at 2048^2 (one tile per CU).
 inline bool use_dma(const GemmArgs &g, int tile) {
-    const int ring = tile == 256 ? dma::Geo<256>::kNs : dma::Geo<128>::kNs;
+    const int ring = dma::ring_stages(tile);
     // 128-wide tiles hold 128 KiB of LDS, one workgroup per CU: only a single round of
     // at most 256 tiles (more go to the register-staged kernel, two per CU)
     if (tile == 128 && (long)cdiv(g.M, 128) * cdiv(g.N, 128) > 256) return false;
@@ -617,7 +617,7 @@ hipError_t launch_cfg(const GemmArgs &g, hipStream_t s) {
     if constexpr (BM == BN) {
         if (p.dma) {
             hipLaunchKernelGGL((mfma_f16_dma_kernel<T, A_MN, B_MN, EPI, BM>),
-                               dim3(cdiv(g.M, BM) * cdiv(g.N, BN)), dim3(64 * dma::kWaves), 0, s,
+                               dim3(cdiv(g.M, BM) * cdiv(g.N, BN)), dim3(256), 0, s,
                                g.M, g.N, g.K, (const uint16_t *)g.A, g.lda, (const uint16_t *)g.B,
                                g.ldb, g.C, g.ldc, g.sign, epi_flags<EPI>(g));
             return hipGetLastError();

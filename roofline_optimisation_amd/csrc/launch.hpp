@@ -14,12 +14,18 @@ hipError_t launch_lds_tiled_f32(const GemmArgs &g, hipStream_t s);
 hipError_t launch_regblock_f32(const GemmArgs &g, hipStream_t s);
 hipError_t launch_mfma_f32(const GemmArgs &g, hipStream_t s);
 hipError_t launch_mfma_f16(int dtype, const GemmArgs &g, hipStream_t s);
+// The measurement-only schedules of the FP16/BF16 direct-to-LDS kernel
+// (GEMM355_VARIANT_MFMA_SPLIT, _W8, _T256X128): whether one takes these arguments, and
+// its launch.
+bool mfma_f16_sched_ok(int variant, const GemmArgs &g);
+hipError_t launch_mfma_f16_sched(int variant, int dtype, const GemmArgs &g, hipStream_t s);
 
 // Host-side descriptions of the instance each launcher would pick.
 const char *desc_lds_tiled_f32(const GemmArgs &g);
 const char *desc_regblock_f32(const GemmArgs &g);
 const char *desc_mfma_f32(const GemmArgs &g);
 const char *desc_mfma_f16(int dtype, const GemmArgs &g);
+const char *desc_mfma_f16_sched(int variant, int dtype);
 
 // True when the current HIP device is a gfx950 (queried once per device).
 bool current_device_is_gfx950();

@@ -76,7 +76,7 @@ def test_invalid_arguments_rejected_on_host(lib, args):
 
 def test_unknown_variant_and_dtype(lib):
     args = (4, 4, 4, P, 4, P, 4, P, 4, 0)
-    assert gb.gemm355_run_variant(4, 0, *args) == gb.ERR_INVALID_ARG
+    assert gb.gemm355_run_variant(7, 0, *args) == gb.ERR_INVALID_ARG
     assert gb.gemm355_run_variant(-2, 0, *args) == gb.ERR_INVALID_ARG
     assert gb.gemm355_run_variant(0, 3, *args) == gb.ERR_INVALID_ARG
     # FP32-only families reject 16-bit operands before touching the device
@@ -249,3 +249,27 @@ def test_matmul_refuses_cpu_tensors(lib):
     a = torch.zeros(4, 4)
     with pytest.raises(ValueError):
         gb.matmul(a, a)
+
+
+def test_schedule_variants_contract(lib):
+    """The measurement-only schedules take plain F16/BF16 products of whole tiles with
+    16-byte-aligned rows and K a multiple of 128; anything else is UNSUPPORTED (checked on
+    the host, before any HIP call)."""
+    d = gb.gemm355_kernel_desc
+    for v in (gb.VARIANT_MFMA_SPLIT, gb.VARIANT_MFMA_W8, gb.VARIANT_MFMA_T256X128):
+        assert "lds-dma" in d(v, gb.F16, 4096, 4096, 4096, P, 4096, P, 4096, P, 4096)
+        assert "mfma_bf16" in d(v, gb.BF16, 4096, 4096, 4096, P, 4096, P, 4096, P, 4096)
+        assert d(v, gb.F32, 4096, 4096, 4096, P, 4096, P, 4096, P, 4096) == "invalid"
+        assert d(v, gb.F16, 4096, 4096, 4000, P, 4000, P, 4096, P, 4096) == "invalid"  # K % 128
+        assert d(v, gb.F16, 4000, 4096, 4096, P, 4096, P, 4096, P, 4096) == "invalid"  # M % 256
+        assert d(v, gb.F16, 4096, 4096, 4096, P + 2, 4096, P, 4096, P, 4096) == "invalid"
+        assert gb.gemm355_run_variant(v, gb.F32, 256, 256, 128, P, 128, P, 256, P, 256, 0) == gb.ERR_UNSUPPORTED
+        assert gb.gemm355_run_variant(v, gb.F16, 256, 256, 100, P, 100, P, 256, P, 256, 0) == gb.ERR_UNSUPPORTED
+        assert gb.gemm355_gemm_ex(v, gb.F16, gb.TRANS_A, 256, 256, 128, P, 256, P, 256, P, 256, 0) == gb.ERR_UNSUPPORTED
+        assert gb.gemm355_variant_name(v).startswith("mfma_")
+    assert d(gb.VARIANT_MFMA_W8, gb.F16, 512, 512, 128, P, 128, P, 512, P, 512) == "mfma_f16 256x256x32 w2x4 lds-dma"
+    assert d(gb.VARIANT_MFMA_T256X128, gb.F16, 512, 384, 128, P, 128, P, 384, P, 384) == "mfma_f16 256x128x32 w2x2 lds-dma"
+    assert d(gb.VARIANT_MFMA_SPLIT, gb.F16, 512, 384, 128, P, 128, P, 384, P, 384) == \
+        "mfma_f16 256x128x32 w2x2 + 4 producer waves lds-dma"
+    assert d(gb.VARIANT_MFMA_W8, gb.F16, 512, 384, 128, P, 128, P, 384, P, 384) == "invalid"  # N % 256
+    assert gb.gemm355_run_variant(7, gb.F16, 8, 8, 8, P, 8, P, 8, P, 8, 0) == gb.ERR_INVALID_ARG
