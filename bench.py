@@ -265,6 +265,59 @@ def family_run(family, steps, warmup, dtype="f32", n=0):
         f"{ms:.4f} ms/launch, {2.0 * n ** 3 / (ms * 1e-3) / 1e12:.2f} TFLOP/s")
 
 
+def ragged_k_lines(warm=300, rounds=3, reps=100):
+    """BF16 4096 x 4096 x K (U[-1,1], seed 4) for K = 4096 and three K that are not whole
+    ring trips of the 256 x 256 direct-to-LDS kernel: every case warmed, then timed
+    interleaved, median of `rounds` rounds of `reps` launches (HIP events)."""
+    import torch
+
+    from roofline_optimisation_amd import binding as gb
+    from roofline_optimisation_amd import inputs
+
+    M = N = 4096
+    stream = torch.cuda.Stream()
+    runs = []
+    for K in (4096, 4000, 4064, 4072):
+        A, B = inputs.make_operands(M, N, K, 4, "uniform", "bf16")
+        dA = torch.from_numpy(A.view("int16")).cuda()
+        dB = torch.from_numpy(B.view("int16")).cuda()
+        dC = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        args = (M, N, K, dA.data_ptr(), K, dB.data_ptr(), N, dC.data_ptr(), N, stream.cuda_stream)
+        desc = gb.gemm355_kernel_desc(gb.VARIANT_AUTO, gb.BF16, *args[:-1])
+
+        def go(args=args):
+            st = gb.gemm_bf16f32acc(*args)
+            if st != gb.OK:
+                raise gb.Gemm355Error(st, "gemm_bf16f32acc")
+        runs.append((K, desc, go, (dA, dB, dC)))
+    for K, desc, go, _ in runs:
+        for _ in range(warm):
+            go()
+    stream.synchronize()
+    times = {K: [] for K, *_ in runs}
+    for _ in range(rounds):
+        for K, desc, go, _ in runs:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                go()
+            e1.record(stream)
+            stream.synchronize()
+            times[K].append(e0.elapsed_time(e1) * 1e3 / reps)
+    out = ["# BF16 4096 x 4096 x K on one MI355X: K not a whole number of ring trips", "",
+           f"U[-1,1] bfloat16 operands (seed 4), FP32 C; {warm} warm-up launches per case, then all "
+           f"cases interleaved, median of {rounds} rounds of {reps} launches; HIP events.", "",
+           "| K | kernel | µs | TFLOP/s | % of 2516.6 | time per FLOP vs K = 4096 |", "|---|---|---|---|---|---|"]
+    base = float(np.median(times[4096])) / 4096
+    for K, desc, go, _ in runs:
+        us = float(np.median(times[K]))
+        tf = 2.0 * M * N * K / us / 1e6
+        out.append(f"| {K} | `{desc}` | {us:.1f} | {tf:.0f} | {100 * tf / PEAKS['bf16']:.1f} | "
+                   f"{us / K / base:.3f} |")
+        log(f"[ragged-k] K={K}: {us:.1f} us, {tf:.0f} TFLOP/s")
+    return out
+
+
 def schedule_lines(warm=300, rounds=3, reps=100):
     """The schedules of the FP16 direct-to-LDS kernel at 4096^3 and 8192^3 (U[-1,1] from
     seed 3): every case warmed, then timed interleaved, median of `rounds` rounds of
@@ -751,6 +804,10 @@ def main():
                     help="only time the schedules of the FP16 direct-to-LDS kernel (dispatched, "
                          "producer/consumer split, eight waves, 256 x 128 tiles) at 4096^3 and "
                          "8192^3, interleaved, and write the markdown table to PATH")
+    ap.add_argument("--ragged-k", default=None, metavar="PATH",
+                    help="only time BF16 4096 x 4096 x K for K in 4096, 4000, 4064, 4072 (the "
+                         "direct-to-LDS kernel with the chunks past K zero-filled), interleaved, "
+                         "and write the markdown table (time per FLOP against K = 4096) to PATH")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after the GEMMs, copy this many MiB device-to-device once (a plain "
                          "copy of known size, used to scale the HBM byte counters)")
@@ -790,6 +847,12 @@ def main():
     if args.family:
         family_run(args.family, args.steps, args.warmup, args.family_dtype, args.family_n)
         calibration_copy()
+        return
+
+    if args.ragged_k:
+        with open(args.ragged_k, "w") as f:
+            f.write("\n".join(ragged_k_lines(warm=max(args.warmup, 1))) + "\n")
+        log(f"[bench] ragged-K table written to {args.ragged_k}")
         return
 
     if args.schedules:

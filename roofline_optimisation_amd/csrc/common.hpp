@@ -267,12 +267,12 @@ __device__ __forceinline__ void store_quad16_acc(const floatx4 &acc, float *__re
 // quad 0 and the odd lane those of quad 1, 4 bytes at a time; otherwise every element is
 // one 2-byte access.  `flags` bit 0 adds the old C.  EDGE guards every access against
 // M x N (a pair whose second column is outside is read and written 2 bytes at a time;
-// the exchange itself runs in every lane).
+// the exchange itself runs in every lane).  `lane` is this lane's index in the wave.
 template <bool EDGE, typename T>
 __device__ __forceinline__ void store_pair16_c16(const floatx4 &acc0, const floatx4 &acc1,
                                                  uint16_t *__restrict__ C, int ldc, int row0,
-                                                 int col0, int M, int N, float sign, int flags) {
-    const int lane = threadIdx.x & 63;
+                                                 int col0, int M, int N, float sign, int flags,
+                                                 int lane) {
     const bool use_old = flags & 1;
     auto rd = [&](const floatx4 &acc, int r) {
         float a;

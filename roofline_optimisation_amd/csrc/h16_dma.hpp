@@ -119,6 +119,14 @@ __device__ __forceinline__ void load_lds16(uint32_t lds_dst, uint32_t voff, int4
                  :: "s"(lds_dst), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
 }
 
+// The lane index from the exec mask, computed where it is used (volatile assembly, so no
+// register holds it across the main loop: the 256-wide tile's loop uses all 256 VGPRs).
+__device__ __forceinline__ int lane_here() {
+    int lane;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane));
+    return lane;
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
     asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
@@ -213,16 +221,42 @@ struct DmaOp {
         }
     }
     // Load instruction i of one issue: MN: k-step at k0 into stage `place`; KM: the
-    // double step at k0 into slot `place`.
-    __device__ __forceinline__ void issue(uint32_t lds0, int roff, int lw, int ld, int place,
-                                          int k0, int i) {
+    // double step at k0 into slot `place`.  KR (K not a whole number of ring trips): a
+    // lane whose chunk lies at k >= K (K a multiple of 8, so a chunk is wholly inside or
+    // outside) takes an offset beyond the buffer's range instead, and the load writes
+    // zeros to its 16 bytes of LDS, so the k-steps past K add nothing.
+    // The k of lane `lane`'s 16-byte chunk in load i of loading wave lw, relative to the
+    // issue's k0: MN its row, KM its chunk's first column (recomputed where needed rather
+    // than held in registers across the loop).
+    __device__ __forceinline__ static int kpos(int i, int lw, int lane) {
+        if constexpr (MN) return kRows * lw + kRpi * i + lane / (64 / kRpi);
+        else return 8 * ((lane & 7) ^ ((4 * (i % 2) + lane / 16) & 7));
+    }
+    // KR: the offset register of a chunk at k >= K is set past the buffer's range in place.
+    // Every later load through that register reads a chunk at a larger or equal k (the
+    // loads are issued in k order, and the clamped repeats at the end do not go back), so
+    // it stays out of range, and no other register is needed.
+    template <bool KR>
+    __device__ __forceinline__ uint32_t off(int k0, int i, int lw, int K) {
+        constexpr uint32_t kOut = 0x80000000u;   // beyond num_records (2^31 - 1)
+        uint32_t &v = voff[MN ? (i & 1) : i];
+        if constexpr (KR) v = k0 + kpos(i, lw, lane_here()) < K ? v : kOut;
+        return v;
+    }
+    __device__ __forceinline__ void issue_at(uint32_t lds0, int roff, int lw, int ld, int place,
+                                             int k0, int i, uint32_t v) {
         if constexpr (MN) {
             const uint32_t dst = lds0 + roff + place * kStage + (lw * kI + i) * 1024;
-            load_lds16(dst, voff[i & 1], rsrc, (uint32_t)((k0 + kRpi * i) * ld * 2));
+            load_lds16(dst, v, rsrc, (uint32_t)((k0 + kRpi * i) * ld * 2));
         } else {
             const uint32_t dst = lds0 + roff + place * kSlot + (lw * kI + i) * 1024;
-            load_lds16(dst, voff[i], rsrc, (uint32_t)(k0 * 2));
+            load_lds16(dst, v, rsrc, (uint32_t)(k0 * 2));
         }
+    }
+    template <bool KR>
+    __device__ __forceinline__ void issue(uint32_t lds0, int roff, int lw, int ld, int place,
+                                          int k0, int i, int K) {
+        issue_at(lds0, roff, lw, ld, place, k0, i, off<KR>(k0, i, lw, K));
     }
     // Piece h of block b of k-step u (u = t % NS, so the MN stage is u, the KM slot
     // u / 2 and the KM half u % 2) into fragment slot `fslot`.
@@ -281,7 +315,7 @@ __device__ __forceinline__ void pin_acc(floatx4 (&acc)[kMB][kNB]) {
 template <int EPI, typename T, bool EDGE, int kMB, int kNB>
 __device__ __forceinline__ void store_tile(floatx4 (&acc)[kMB][kNB], float *__restrict__ C, int ldc,
                                            int row0, int col0, int M, int N, float sign, int flags) {
-    const int lane = threadIdx.x & 63;
+    const int lane = lane_here();
     const int rl = row0 + 4 * (lane >> 4);
     if constexpr (EPI == 0) {
 #pragma unroll
@@ -307,13 +341,15 @@ __device__ __forceinline__ void store_tile(floatx4 (&acc)[kMB][kNB], float *__re
 #pragma unroll
             for (int j = 0; j < kNB; j += 2)
                 store_pair16_c16<EDGE, T>(acc[i][j], acc[i][j + 1], (uint16_t *)C, ldc, rl + 16 * i,
-                                          col0 + 16 * j, M, N, sign, flags);
+                                          col0 + 16 * j, M, N, sign, flags, lane);
     }
 }
 
 // WHOLE: the caller guarantees that the tile lies inside M x N (no guarded stores).
+// KR: K is not a whole number of ring trips (K a multiple of 8): the loop runs to the next
+// whole trip and every chunk at k >= K loads as zeros (DmaOp::issue).
 template <typename T, bool A_MN, bool B_MN, int EPI, int EM, int EN, int WM, int WN, int NS, int PW,
-          bool WHOLE = false>
+          bool WHOLE = false, bool KR = false>
 __device__ __forceinline__ void dma_tile(int M, int N, int K, const uint16_t *__restrict__ A, int lda,
                                          const uint16_t *__restrict__ B, int ldb,
                                          float *__restrict__ C, int ldc, float sign,
@@ -335,21 +371,26 @@ __device__ __forceinline__ void dma_tile(int M, int N, int K, const uint16_t *__
     constexpr int nKM = (A_MN ? 0 : OA::kI) + (B_MN ? 0 : OB::kI);
     // issue w of an MN batch (k-step at k0 into stage st) / of a KM batch (double step at
     // k0 into slot sl), by loading wave lw
-    auto issue_mn = [&](int lw, int st, int k0, int w) {
+    // (kr_c: whether this load may lie past K and selects its lanes' offsets)
+    auto issue_mn = [&](int lw, int st, int k0, int w, auto kr_c) {
+        constexpr bool kKR = decltype(kr_c)::value;
         if constexpr (A_MN) {
-            if (w < OA::kI) { oa.issue(lds0, 0, lw, lda, st, k0, w); return; }
+            if (w < OA::kI) { oa.template issue<kKR>(lds0, 0, lw, lda, st, k0, w, K); return; }
             w -= OA::kI;
         }
-        if constexpr (B_MN) ob.issue(lds0, kBOff, lw, ldb, st, k0, w);
+        if constexpr (B_MN) ob.template issue<kKR>(lds0, kBOff, lw, ldb, st, k0, w, K);
     };
-    auto issue_km = [&](int lw, int sl, int k0, int w) {
+    auto issue_km = [&](int lw, int sl, int k0, int w, auto kr_c) {
+        constexpr bool kKR = decltype(kr_c)::value;
         if constexpr (!A_MN) {
-            if (w < OA::kI) { oa.issue(lds0, 0, lw, lda, sl, k0, w); return; }
+            if (w < OA::kI) { oa.template issue<kKR>(lds0, 0, lw, lda, sl, k0, w, K); return; }
             w -= OA::kI;
         }
-        if constexpr (!B_MN) ob.issue(lds0, kBOff, lw, ldb, sl, k0, w);
+        if constexpr (!B_MN) ob.template issue<kKR>(lds0, kBOff, lw, ldb, sl, k0, w, K);
     };
-    const int nk = K / kBK;
+    using KRc = std::integral_constant<bool, KR>;
+    // k-steps: K / 32, or with KR the k-steps up to the next whole ring trip
+    const int nk = KR ? cdiv(K, kBK * kNs) * kNs : K / kBK;
     // The wait before the barrier of k-step u (u = t % kNs): loads are issued in step
     // order (a step's MN loads, then its KM loads), the prologue's included, so the wait
     // counts are the loads of the steps after the one that issued what step t+1 needs: on
@@ -371,15 +412,15 @@ __device__ __forceinline__ void dma_tile(int M, int N, int K, const uint16_t *__
     // MN k-step 0 may stay in flight).
     auto prologue_loads = [&](int lw) {
 #pragma unroll
-        for (int w = 0; w < nKM; ++w) issue_km(lw, 0, 0, w);
+        for (int w = 0; w < nKM; ++w) issue_km(lw, 0, 0, w, KRc{});
 #pragma unroll
         for (int p = 0; p < kNs - 1; ++p) {
 #pragma unroll
-            for (int w = 0; w < nMN; ++w) issue_mn(lw, p, min(p, nk - 1) * kBK, w);
+            for (int w = 0; w < nMN; ++w) issue_mn(lw, p, min(p, nk - 1) * kBK, w, KRc{});
             if (p % 2 == 1 && p >= 3) {
 #pragma unroll
                 for (int w = 0; w < nKM; ++w)
-                    issue_km(lw, (p - 1) / 2, min((p - 1) / 2, nk / 2 - 1) * 2 * kBK, w);
+                    issue_km(lw, (p - 1) / 2, min((p - 1) / 2, nk / 2 - 1) * 2 * kBK, w, KRc{});
             }
         }
         wait_vmcnt<(kNs - 2) * nMN + (kNs / 2 - 2) * nKM>();
@@ -390,9 +431,9 @@ __device__ __forceinline__ void dma_tile(int M, int N, int K, const uint16_t *__
     // stages or slots.
     auto k_mn_of = [&](int t) { return min(t + kNs - 1, nk - 1) * kBK; };
     auto k_km_of = [&](int t) { return min(t / 2 + kNs / 2 - 1, nk / 2 - 1) * 2 * kBK; };
-    auto step_load = [&](int lw, int u, int w, int k_mn, int k_km) {
-        if (w < nMN) issue_mn(lw, (u + kNs - 1) % kNs, k_mn, w);
-        else issue_km(lw, (u / 2 + kNs / 2 - 1) % (kNs / 2), k_km, w - nMN);
+    auto step_load = [&](int lw, int u, int w, int k_mn, int k_km, auto kr_c) {
+        if (w < nMN) issue_mn(lw, (u + kNs - 1) % kNs, k_mn, w, kr_c);
+        else issue_km(lw, (u / 2 + kNs / 2 - 1) % (kNs / 2), k_km, w - nMN, kr_c);
     };
 
     if constexpr (PW > 0) {
@@ -409,7 +450,7 @@ __device__ __forceinline__ void dma_tile(int M, int N, int K, const uint16_t *__
                 constexpr int nLd = nMN + (u % 2 == 0 ? nKM : 0);
                 const int k_mn = k_mn_of(kt + u), k_km = k_km_of(kt + u);
 #pragma unroll
-                for (int w = 0; w < nLd; ++w) step_load(lw, u, w, k_mn, k_km);
+                for (int w = 0; w < nLd; ++w) step_load(lw, u, w, k_mn, k_km, KRc{});
                 wait_before_barrier(u_c);
                 __syncthreads();
             };
@@ -447,7 +488,7 @@ __device__ __forceinline__ void dma_tile(int M, int N, int K, const uint16_t *__
         if (qs >= hi) return n;
         return ((qs - lo) * n + (hi - lo) - 1) / (hi - lo);
     };
-    auto kstep = [&](int kt, auto u_c, auto b_c) {
+    auto kstep_impl = [&](int kt, auto u_c, auto b_c, auto kr_c) {
         constexpr int u = decltype(u_c)::value;
         constexpr int kBarrier = decltype(b_c)::value;
         constexpr int kLoadHi = kBarrier < G::kLoadHi ? kBarrier : G::kLoadHi;
@@ -474,7 +515,7 @@ __device__ __forceinline__ void dma_tile(int M, int N, int K, const uint16_t *__
                 const int lo = ev_begin(qs, nLd, 0, kLoadHi);
                 const int hi = ev_begin(qs + 1, nLd, 0, kLoadHi);
 #pragma unroll
-                for (int w = lo; w < hi; ++w) step_load(wave, u, w, k_mn, k_km);
+                for (int w = lo; w < hi; ++w) step_load(wave, u, w, k_mn, k_km, kr_c);
             }
             if (qs == kBarrier - 1) {
                 if constexpr (PW == 0) wait_before_barrier(u_c);
@@ -483,6 +524,11 @@ __device__ __forceinline__ void dma_tile(int M, int N, int K, const uint16_t *__
             __builtin_amdgcn_sched_barrier(0);
         }
     };
+
+    // the k-steps whose loads may lie past K (issued in the last two ring trips) take the
+    // zero-filling offsets; the others the plain ones
+    auto kstep = [&](int kt, auto u_c, auto b_c) { kstep_impl(kt, u_c, b_c, std::false_type{}); };
+    auto kstep_kr = [&](int kt, auto u_c, auto b_c) { kstep_impl(kt, u_c, b_c, std::true_type{}); };
 
     if constexpr (PW == 0) prologue_loads(wave);
     __syncthreads();
@@ -498,9 +544,22 @@ __device__ __forceinline__ void dma_tile(int M, int N, int K, const uint16_t *__
         for (int j = 0; j < kNB; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
     pin_acc(acc);
     asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
-    for (int kt = 0; kt < nk; kt += kNs)
-        for_steps(kstep, kt, std::make_integer_sequence<int, kNs>{},
+    if constexpr (KR) {
+        // nk is at least two trips; the loads of every step before the last trip read
+        // whole chunks inside K, so only the last two trips select offsets
+        int kt = 0;
+        for (; kt < nk - 2 * kNs; kt += kNs)
+            for_steps(kstep, kt, std::make_integer_sequence<int, kNs>{},
+                      std::integral_constant<int, G::kBarrier>{});
+        for_steps(kstep_kr, kt, std::make_integer_sequence<int, kNs>{},
                   std::integral_constant<int, G::kBarrier>{});
+        for_steps(kstep_kr, kt + kNs, std::make_integer_sequence<int, kNs>{},
+                  std::integral_constant<int, G::kBarrier>{});
+    } else {
+        for (int kt = 0; kt < nk; kt += kNs)
+            for_steps(kstep, kt, std::make_integer_sequence<int, kNs>{},
+                      std::integral_constant<int, G::kBarrier>{});
+    }
     // nothing may still write this workgroup's LDS when it exits
     if constexpr (PW == 0) wait_vmcnt<0>();
     pin_acc(acc);
@@ -516,7 +575,8 @@ __device__ __forceinline__ void dma_tile(int M, int N, int K, const uint16_t *__
 
 // One workgroup per CU (128 KiB of LDS for either tile; E = 256 also takes all 256
 // accumulator registers of a lane).
-template <typename T, bool A_MN, bool B_MN, int EPI, int E>
+// KR: K not a whole number of ring trips (the last trip's chunks past K load as zeros).
+template <typename T, bool A_MN, bool B_MN, int EPI, int E, bool KR = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1)))
 void mfma_f16_dma_kernel(int M, int N, int K, const uint16_t *__restrict__ A, int lda,
                          const uint16_t *__restrict__ B, int ldb, float *__restrict__ C,
@@ -525,8 +585,8 @@ void mfma_f16_dma_kernel(int M, int N, int K, const uint16_t *__restrict__ A, in
     __shared__ __attribute__((aligned(1024))) char lds[dma::Geo<E, E, 2, 2, kNs, 0>::kLds];
     int tm, tn;
     grouped_tile(xcd_contiguous_id(blockIdx.x, gridDim.x), cdiv(M, E), cdiv(N, E), 4, tm, tn);
-    dma::dma_tile<T, A_MN, B_MN, EPI, E, E, 2, 2, kNs, 0>(M, N, K, A, lda, B, ldb, C, ldc, sign, flags,
-                                                           tm * E, tn * E, lds);
+    dma::dma_tile<T, A_MN, B_MN, EPI, E, E, 2, 2, kNs, 0, false, KR>(M, N, K, A, lda, B, ldb, C, ldc, sign,
+                                                                      flags, tm * E, tn * E, lds);
 }
 
 // Schedules of the same data movement that are kept for measurement (gemm355_run_variant

@@ -505,22 +505,30 @@ inline bool op_fits(bool mn, int ext, int K, int ld) {
 }
 
 // The direct-load kernel takes every tile (ragged ones included) of a 256 x 256 or
-// 128 x 128 configuration when rows are 16-byte aligned, every byte offset fits the
-// 31-bit buffer range and K is a multiple of one trip round the ring (128 for 256-wide
-// tiles, 256 for 128-wide ones).  At 128 x 128 the tile's loads (16 KiB per k-step per CU against 256
-// cycles of MFMAs) run at the CU's load-path rate, so the kernel is load-bound there;
-// it still beats the register-staged kernel by 10-20 % at 2048^2 (one tile per CU).
+// 128 x 128 configuration when rows are 16-byte aligned, K is a multiple of 8 and at least
+// one trip round the ring (128 for 256-wide tiles, 256 for 128-wide ones; a K that is not
+// a whole number of trips runs to the next trip with the chunks past K loaded as zeros),
+// and every byte offset up to that trip fits the 31-bit buffer range.  At 128 x 128 the
+// tile's loads (16 KiB per k-step per CU against 256 cycles of MFMAs) run at the CU's
+// load-path rate, so the kernel is load-bound there; it still beats the register-staged
+// kernel by 10-20 % at 2048^2 (one tile per CU).
 inline bool use_dma(const GemmArgs &g, int tile) {
-    const int ring = dma::ring_stages(tile);
+    const int trip = dma::kBK * dma::ring_stages(tile);
     // 128-wide tiles hold 128 KiB of LDS, one workgroup per CU: only a single round of
     // at most 256 tiles (more go to the register-staged kernel, two per CU)
     if (tile == 128 && (long)cdiv(g.M, 128) * cdiv(g.N, 128) > 256) return false;
     // an m/n-contiguous operand's extent is a whole number of 16-byte chunks, so no
     // load straddles the end of its last row
     if ((g.trans_a && g.M % 8 != 0) || (!g.trans_b && g.N % 8 != 0)) return false;
-    return (tile == 256 || tile == 128) && h16_vec(g) && g.K > 0 &&
-           g.K % (dma::kBK * ring) == 0 && g.M >= tile && g.N >= tile &&
-           op_fits(g.trans_a != 0, tile, g.K, g.lda) && op_fits(g.trans_b == 0, tile, g.K, g.ldb);
+    const int kpad = cdiv(g.K, trip) * trip;
+    return (tile == 256 || tile == 128) && h16_vec(g) && g.K >= trip && g.K % 8 == 0 &&
+           g.M >= tile && g.N >= tile && op_fits(g.trans_a != 0, tile, kpad, g.lda) &&
+           op_fits(g.trans_b == 0, tile, kpad, g.ldb);
+}
+
+// K is not a whole number of the direct-load kernel's ring trips.
+inline bool dma_ragged_k(const GemmArgs &g, int tile) {
+    return g.K % (dma::kBK * dma::ring_stages(tile)) != 0;
 }
 
 // The epilogue's flags argument: bit 0 adds the old C; with 16-bit C, bit 1 selects
@@ -616,10 +624,15 @@ hipError_t launch_cfg(const GemmArgs &g, hipStream_t s) {
     const H16Plan p = plan_cfg(BM, BN, A_MN, B_MN, EPI, g);
     if constexpr (BM == BN) {
         if (p.dma) {
-            hipLaunchKernelGGL((mfma_f16_dma_kernel<T, A_MN, B_MN, EPI, BM>),
-                               dim3(cdiv(g.M, BM) * cdiv(g.N, BN)), dim3(256), 0, s,
-                               g.M, g.N, g.K, (const uint16_t *)g.A, g.lda, (const uint16_t *)g.B,
-                               g.ldb, g.C, g.ldc, g.sign, epi_flags<EPI>(g));
+            const dim3 grid(cdiv(g.M, BM) * cdiv(g.N, BN));
+            if (dma_ragged_k(g, BM))
+                hipLaunchKernelGGL((mfma_f16_dma_kernel<T, A_MN, B_MN, EPI, BM, true>), grid, dim3(256), 0, s,
+                                   g.M, g.N, g.K, (const uint16_t *)g.A, g.lda, (const uint16_t *)g.B,
+                                   g.ldb, g.C, g.ldc, g.sign, epi_flags<EPI>(g));
+            else
+                hipLaunchKernelGGL((mfma_f16_dma_kernel<T, A_MN, B_MN, EPI, BM>), grid, dim3(256), 0, s,
+                                   g.M, g.N, g.K, (const uint16_t *)g.A, g.lda, (const uint16_t *)g.B,
+                                   g.ldb, g.C, g.ldc, g.sign, epi_flags<EPI>(g));
             return hipGetLastError();
         }
     }

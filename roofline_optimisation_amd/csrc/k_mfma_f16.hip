@@ -31,6 +31,7 @@ const char *desc_mfma_f16(int dtype, const GemmArgs &g) {
     out = name;
     if (p.dma) {
         out += big ? " 256x256x32 w2x2 lds-dma" : " 128x128x32 w2x2 lds-dma";
+        if (dma_ragged_k(g, bm)) out += " k-zero-fill";
         return out.c_str();
     }
     out += big ? " 256x256x64 w2x2 dwordx4" : (narrow ? " 128x64x64 w2x2 dwordx4" : " 128x128x64 w2x2 dwordx4");

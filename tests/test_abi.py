@@ -98,18 +98,22 @@ def test_dispatch_choices(lib):
     assert d(-1, 0, 4096, 4096, 4096, P, 4096, P, 4096, P, 4096).startswith("mfma_f32 128x128")
     assert d(-1, 1, 4096, 4096, 4096, P, 4096, P, 4096, P, 4096).startswith("mfma_f16")
     assert d(-1, 2, 4096, 4096, 4096, P, 4096, P, 4096, P, 4096).startswith("mfma_bf16")
-    # 256 x 256 tiles with K a multiple of 128, and one round of 128 x 128 tiles with K a
-    # multiple of 256, load straight into LDS, ragged tiles included; other K, unaligned
-    # rows and more 128-wide tiles keep register staging
+    # 256 x 256 tiles with K a multiple of 8 and at least 128, and one round of 128 x 128
+    # tiles with K a multiple of 8 and at least 256, load straight into LDS, ragged tiles
+    # included; a K that is not a whole number of ring trips (128, 256) zero-fills the
+    # chunks past K; other K, unaligned rows and more 128-wide tiles keep register staging
     assert d(-1, 1, 4096, 4096, 4096, P, 4096, P, 4096, P, 4096) == "mfma_f16 256x256x32 w2x2 lds-dma"
     assert d(-1, 2, 4096, 4096, 4096, P, 4096, P, 4096, P, 4096) == "mfma_bf16 256x256x32 w2x2 lds-dma"
-    assert d(-1, 1, 4096, 4096, 4160, P, 4160, P, 4096, P, 4096) == "mfma_f16 256x256x64 w2x2 dwordx4 | interior=buffer"
+    assert d(-1, 1, 4096, 4096, 4160, P, 4160, P, 4096, P, 4096) == "mfma_f16 256x256x32 w2x2 lds-dma k-zero-fill"
     assert d(-1, 1, 4096, 4096, 4096, P + 2, 4096, P, 4096, P, 4096) == "mfma_f16 256x256x64 w2x2 dwordx4 unaligned | interior=pointer"
     assert d(-1, 1, 2048, 2048, 2048, P, 2048, P, 2048, P, 2048) == "mfma_f16 128x128x32 w2x2 lds-dma"
-    assert d(-1, 1, 2048, 2048, 2176, P, 2176, P, 2048, P, 2048) == "mfma_f16 128x128x64 w2x2 dwordx4 | interior=buffer,paired"
+    assert d(-1, 1, 2048, 2048, 2176, P, 2176, P, 2048, P, 2048) == "mfma_f16 128x128x32 w2x2 lds-dma k-zero-fill"
     assert d(-1, 2, 2560, 2560, 2560, P, 2560, P, 2560, P, 2560) == "mfma_bf16 128x128x64 w2x2 dwordx4 | interior=buffer,paired"
     assert d(-1, 1, 4000, 4000, 4096, P, 4096, P, 4000, P, 4000) == "mfma_f16 256x256x32 w2x2 lds-dma"
     assert d(-1, 1, 4096, 4104, 4096, P, 4096, P, 4104, P, 4104) == "mfma_f16 256x256x32 w2x2 lds-dma"
+    assert d(-1, 2, 4096, 4096, 4000, P, 4000, P, 4096, P, 4096) == "mfma_bf16 256x256x32 w2x2 lds-dma k-zero-fill"
+    assert d(-1, 2, 4096, 4096, 4001, P, 4008, P, 4096, P, 4096) == "mfma_bf16 256x256x64 w2x2 dwordx4 | edges=clamped"
+    assert d(-1, 1, 4096, 4096, 120, P, 120, P, 4096, P, 4096).startswith("mfma_f16 256x256x64 w2x2 dwordx4")
     # an m/n-contiguous extent that is not a whole number of 16-byte chunks stays staged
     assert d(-1, 1, 4000, 4004, 4096, P, 4096, P, 4008, P, 4004) == "mfma_f16 256x256x64 w2x2 dwordx4 | all=clamped,paired"
     # rows not 16-byte aligned (lda = 515 floats) take the dword load path
@@ -134,15 +138,19 @@ def test_dispatch_choices_general_form(lib):
     # flag-free equals the plain query
     assert dx(-1, 1, 0, 4096, 4096, 4096, P, 4096, P, 4096, P, 4096) == \
         gb.gemm355_kernel_desc(-1, 1, 4096, 4096, 4096, P, 4096, P, 4096, P, 4096)
-    # transposed operands with K ragged (1000 = 15 64-wide k-steps + 40): every tile takes
-    # the clamped kernel; 16 k-steps (even) run the two-set pipeline
-    assert dx(-1, 1, gb.TRANS_A, 1000, 1000, 1000, P, 1000, P, 1000, P, 1000) == \
+    # transposed operands with K ragged and not a multiple of 8 (1004 = 15 64-wide k-steps
+    # + 44): every tile takes the clamped kernel; 16 k-steps (even) run the two-set
+    # pipeline
+    assert dx(-1, 1, gb.TRANS_A, 1000, 1000, 1004, P, 1000, P, 1000, P, 1000) == \
         "mfma_f16 128x128x64 w2x2 dwordx4 | edges=clamped,paired"
-    assert dx(-1, 2, gb.TRANS_B, 1000, 1000, 1000, P, 1000, P, 1000, P, 1000) == \
-        "mfma_bf16 128x64x64 w2x2 dwordx4 | edges=clamped,paired"
+    assert dx(-1, 2, gb.TRANS_B, 1000, 1000, 1004, P, 1004, P, 1004, P, 1000) == \
+        "mfma_bf16 128x64x64 w2x2 dwordx4 unaligned | edges=clamped,paired"
     # signed and accumulating epilogues keep to one staging set
-    assert dx(-1, 1, gb.TRANS_A | gb.NEG_A, 1000, 1000, 1000, P, 1000, P, 1000, P, 1000) == \
+    assert dx(-1, 1, gb.TRANS_A | gb.NEG_A, 1000, 1000, 1004, P, 1000, P, 1000, P, 1000) == \
         "mfma_f16 128x128x64 w2x2 dwordx4 | edges=clamped"
+    # with K a multiple of 8 the direct-to-LDS kernel zero-fills past K in every layout
+    assert dx(-1, 1, gb.TRANS_A | gb.TRANS_B, 1000, 1000, 1000, P, 1000, P, 1000, P, 1000) == \
+        "mfma_f16 128x128x32 w2x2 lds-dma k-zero-fill"
     # what gemm355_gemm_ex rejects
     assert dx(-1, 0, gb.C_16, 8, 8, 8, P, 8, P, 8, P, 8) == "invalid"
     assert dx(-1, 1, 64, 8, 8, 8, P, 8, P, 8, P, 8) == "invalid"

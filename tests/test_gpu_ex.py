@@ -108,14 +108,16 @@ def test_flag_matrix_ragged(fl, dtype, variant):
 
 
 # Interior tiles of every layout: FP32 192 x 192 (3072), 128 x 128 (2048), 96 x 96 (1536; ragged
-# M, N and K), 64 x 64; FP16/BF16 256 x 256
-# direct-to-LDS (3072^2, K % 128 == 0), 256 x 256 register-staged (K % 128 != 0) and
-# 128 x 128; each plain, negated and accumulating.
+# M, N and K), 64 x 64; FP16/BF16 256 x 256 direct-to-LDS (3072^2, K % 128 == 0, and K = 192
+# with the chunks past K zero-filled), 256 x 256 register-staged (K = 64, below one ring
+# trip) and 128 x 128; each plain, negated and accumulating.  16-bit C adds K = 196 (not a
+# multiple of 8: the clamped register-staged kernel).
 LAYOUTS = list(itertools.product([False, True], repeat=2))
 MODES = [(False, False, False), (True, False, False), (False, True, True)]  # na, nb, acc
 SHAPES = {"f32": [(3072, 3072, 64), (1024, 768, 96), (2048, 2048, 64), (1536, 1536, 96), (1351, 1537, 100),
                   (2000, 1996, 256), (2000, 1996, 260)],
-          "f16": [(3072, 3072, 128), (3072, 2816, 192), (1024, 1024, 128), (4000, 3992, 128)],
+          "f16": [(3072, 3072, 128), (3072, 2816, 192), (1024, 1024, 128), (4000, 3992, 128),
+                  (3072, 3072, 64)],
           "bf16": [(3072, 3072, 256), (1024, 512, 64), (2000, 2040, 256)]}
 # FP32 (2000, 1996, 256) and (2000, 1996, 260): ragged tiles in the unpredicated kernel
 # with the full ones, the latter with a zero-filled last k-step.
@@ -162,14 +164,15 @@ def test_integers_bit_exact(dtype, fl):
 
 
 # Transposed layouts on the register-staged kernel's clamped ragged tiles with the
-# two-set pipeline (K = 1000: 16 64-wide k-steps, every tile ragged in K): every element
-# within the float bar, and integer operands bit for bit.
+# two-set pipeline (K = 1004: 16 64-wide k-steps, every tile ragged in K, K not a multiple
+# of 8 so the direct-to-LDS kernel does not take it): every element within the float bar,
+# and integer operands bit for bit.
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("layout", [(True, False), (False, True), (True, True)],
                          ids=["ta", "tb", "tatb"])
 def test_clamped_paired_transposed(dtype, layout):
     ta, tb = layout
-    M, N, K = 1000, 1000, 1000
+    M, N, K = 1000, 1000, 1004
     P = 1 << 20
     flags = flags_of(ta, tb, False, False, False)
     lda, ldb = (M if ta else K), (K if tb else N)
@@ -285,7 +288,7 @@ def test_c16_flag_matrix_ragged(fl, dtype, variant):
     compare16(129, 97, 75, dtype, *fl, seed=56, variant=variant)
 
 
-SHAPES16 = [(3072, 3072, 128), (3072, 2816, 192), (1024, 1024, 128), (1024, 512, 64)]
+SHAPES16 = [(3072, 3072, 128), (3072, 2816, 192), (1024, 1024, 128), (1024, 512, 64), (3072, 3072, 196)]
 
 
 @pytest.mark.parametrize("mode", MODES, ids=["plain", "neg_a", "neg_b_acc"])

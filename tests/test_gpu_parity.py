@@ -471,3 +471,36 @@ def test_h16_tile_classes(case):
     rows = sample_rows(M, 96)
     C64, _ = oracle.gemm(np.ascontiguousarray(A[rows]), B, dtype)
     check(C[rows], C64, dtype, "uniform", K, ok, f"{dtype} tile class {tile} {M}x{N}x{K}")
+
+# The direct-to-LDS kernel with K not a whole number of its ring trips (128 for 256-wide
+# tiles, 256 for 128-wide ones): the loop runs to the next trip and every 16-byte chunk at
+# k >= K loads as zeros.  K = 4000, 4064 (ragged by whole 32-wide k-steps), 4072 (a
+# partial last k-step), K just over one trip (136), the 128-wide tile (2000), and ragged
+# tiles with ragged K (4000 x 4000 x 1000).  Padded strides hold NaN past K in every row,
+# so any chunk past K that is read instead of zero-filled poisons the result.
+RAGGED_K_CASES = [("bf16", (4096, 4096, 4000), (0, 0, 0), "full"),
+                  ("f16", (4096, 4096, 4064), (8, 8, 8), "rows"),
+                  ("bf16", (4096, 4096, 4072), (8, 16, 8), "rows"),
+                  ("f16", (3072, 2816, 136), (8, 8, 8), "full"),
+                  ("bf16", (2048, 2048, 2000), (8, 8, 0), "full"),
+                  ("f16", (4000, 4000, 1000), (8, 0, 0), "rows")]
+
+
+@pytest.mark.parametrize("case", RAGGED_K_CASES, ids=lambda c: c[0] + "_" + "x".join(map(str, c[1])) + f"_pad{c[2][0]}")
+def test_dma_ragged_k(case):
+    dtype, (M, N, K), pad, cmp = case
+    P = 1 << 20  # a 16-byte-aligned address: the query only inspects it
+    desc = gb.gemm355_kernel_desc(gb.VARIANT_AUTO, gb.DTYPE_CODES[dtype], M, N, K, P, K + pad[0],
+                                  P, N + pad[1], P, N + pad[2])
+    assert "lds-dma k-zero-fill" in desc, desc
+    A, B = inputs.make_operands(M, N, K, 81, "uniform", dtype)
+    C, ok = gpu_gemm(A, B, dtype, entry="typed", pad=pad, guard_rows=1)
+    rows = np.arange(M) if cmp == "full" else np.array(sorted(
+        set(sample_rows(M, 48).tolist()) | {255, 256, M - 1}))
+    C64, _ = oracle.gemm(np.ascontiguousarray(A[rows]), B, dtype)
+    check(C[rows], C64, dtype, "uniform", K, ok, f"ragged-K dma {dtype} {M}x{N}x{K} pad={pad}")
+    Ai, Bi = inputs.make_operands(M, N, K, 82, "int", dtype)
+    _, C32 = oracle.gemm(np.ascontiguousarray(Ai[rows]), Bi, dtype)
+    Ci, ok = gpu_gemm(Ai, Bi, dtype, entry="typed", pad=pad)
+    assert ok and np.array_equal(Ci[rows], C32), f"ragged-K dma {dtype} {M}x{N}x{K} integers not bit-exact"
+
