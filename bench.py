@@ -312,10 +312,15 @@ def ragged_k_lines(warm=300, rounds=3, reps=100):
     for K, desc, go, _ in runs:
         us = float(np.median(times[K]))
         tf = 2.0 * M * N * K / us / 1e6
-        out.append(f"| {K} | `{desc}` | {us:.1f} | {tf:.0f} | {100 * tf / PEAKS['bf16']:.1f} | "
+        out.append(f"| {K} | `{md_cell(desc)}` | {us:.1f} | {tf:.0f} | {100 * tf / PEAKS['bf16']:.1f} | "
                    f"{us / K / base:.3f} |")
         log(f"[ragged-k] K={K}: {us:.1f} us, {tf:.0f} TFLOP/s")
     return out
+
+
+def md_cell(text: str) -> str:
+    """A markdown table cell: '|' inside the text escaped."""
+    return text.replace("|", "\\|")
 
 
 def schedule_lines(warm=300, rounds=3, reps=100):
@@ -371,7 +376,7 @@ def schedule_lines(warm=300, rounds=3, reps=100):
         for label, desc, go in runs:
             us = float(np.median(times[label]))
             tf = 2.0 * n ** 3 / us / 1e6
-            out.append(f"| {n} | {label} | `{desc}` | {us:.1f} | {tf:.0f} | {100 * tf / PEAKS['f16']:.1f} | "
+            out.append(f"| {n} | {label} | `{md_cell(desc)}` | {us:.1f} | {tf:.0f} | {100 * tf / PEAKS['f16']:.1f} | "
                        f"{base / us:.3f}x |")
             log(f"[schedules] {n}^3 {label}: {us:.1f} us, {tf:.0f} TFLOP/s")
         del dA, dB, dC
@@ -736,7 +741,7 @@ def write_report(path):
         for v in (0, 1, 2, 3):
             ms, desc, reps = time_variant(v, "f32", n, n, n, seed)
             tf = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
-            lines.append(f"| FP32 {n}^3 | {names[v]} | {desc} | {reps} | {ms * 1e3:.1f} | {tf:.2f} | "
+            lines.append(f"| FP32 {n}^3 | {names[v]} | {md_cell(desc)} | {reps} | {ms * 1e3:.1f} | {tf:.2f} | "
                          f"{100 * tf / PEAKS['f32']:.1f} |")
             log(f"[report] f32 {n} {names[v]}: {ms * 1e3:.1f} us {tf:.2f} TFLOP/s")
     lines += ["", "## Roofline sweep (dispatched kernels)", "",
@@ -749,7 +754,7 @@ def write_report(path):
         e = rl.roofline_entry(c.M, c.N, c.K, ms * 1e-3, c.dtype)
         chart_points.append((e["oi"], tf, "f" if c.dtype == "f32" else "b"))
         bound = "HBM" if e["attainable_tflops"] < e["peak_tflops"] else "compute"
-        lines.append(f"| {c.dtype} | {c.M}x{c.N}x{c.K} | {desc} | {ms * 1e3:.1f} | {tf:.1f} | "
+        lines.append(f"| {c.dtype} | {c.M}x{c.N}x{c.K} | {md_cell(desc)} | {ms * 1e3:.1f} | {tf:.1f} | "
                      f"{100 * e['frac']:.1f} | {e['oi']:.1f} | {e['attainable_tflops']:.0f} | {bound} |")
         log(f"[report] {c.name}: {ms * 1e3:.1f} us {tf:.1f} TFLOP/s")
     lines += ["", "Roofline chart of the sweep (f: FP32 points, b: BF16 points; roofs min(peak, OI x 8 TB/s): "

@@ -162,6 +162,8 @@ struct DmaOp {
     // load instructions per loading wave: per k-step (MN) or per double step (KM)
     static constexpr int kI = MN ? kRows / kRpi : kRows / 8;
     static_assert(kI >= 1, "every loading wave issues a whole instruction");
+    // the MN swizzle XORs chunk slots with up to 14: a row needs at least 16 chunks
+    static_assert(!MN || E >= 128, "an MN operand's rows hold at least 16 chunks");
     static_assert(!MN || (kRows * LW == kBK && kI * kRpi == kRows && 8 % kRows == 0),
                   "an MN operand's loading wave fills rows of one (k / 8) parity");
     static_assert(MN || (kRows * LW == E && kRows % 16 == 0), "KM rows per loading wave");
