@@ -265,56 +265,67 @@ def family_run(family, steps, warmup, dtype="f32", n=0):
         f"{ms:.4f} ms/launch, {2.0 * n ** 3 / (ms * 1e-3) / 1e12:.2f} TFLOP/s")
 
 
+RAGGED_K = ((4096, 4096, 4096), (4096, 4000, 4000), (4096, 4064, 4064), (4096, 4072, 4072),
+            (4096, 4104, 4104), (4096, 4000, 4096), (4096, 4072, 4096), (4096, 4096, 4104),
+            (2048, 2048, 2048), (2048, 2000, 2000), (2048, 2000, 2048), (2048, 2048, 2056))
+
+
 def ragged_k_lines(warm=300, rounds=3, reps=100):
-    """BF16 4096 x 4096 x K (U[-1,1], seed 4) for K = 4096 and three K that are not whole
-    ring trips of the 256 x 256 direct-to-LDS kernel: every case warmed, then timed
-    interleaved, median of `rounds` rounds of `reps` launches (HIP events)."""
+    """BF16 n x n x K (U[-1,1], seed 4; n = 4096 on the 256 x 256 direct-to-LDS tile, 2048
+    on the 128 x 128 one) for K = n and K that are not whole ring trips, A's rows packed
+    (lda = K) or padded to 2n halves, and K = n with rows of 2n + 8 halves (off the
+    128-byte lines): every case warmed, then timed interleaved, median of `rounds` rounds
+    of `reps` launches (HIP events).  Time per FLOP is relative to K = lda = n."""
     import torch
 
     from roofline_optimisation_amd import binding as gb
     from roofline_optimisation_amd import inputs
 
-    M = N = 4096
     stream = torch.cuda.Stream()
     runs = []
-    for K in (4096, 4000, 4064, 4072):
-        A, B = inputs.make_operands(M, N, K, 4, "uniform", "bf16")
-        dA = torch.from_numpy(A.view("int16")).cuda()
+    for n, K, lda in RAGGED_K:
+        A, B = inputs.make_operands(n, n, K, 4, "uniform", "bf16")
+        dA = torch.zeros((n, lda), dtype=torch.int16, device="cuda")
+        dA[:, :K] = torch.from_numpy(A.view("int16")).cuda()
         dB = torch.from_numpy(B.view("int16")).cuda()
-        dC = torch.empty((M, N), dtype=torch.float32, device="cuda")
-        args = (M, N, K, dA.data_ptr(), K, dB.data_ptr(), N, dC.data_ptr(), N, stream.cuda_stream)
+        dC = torch.empty((n, n), dtype=torch.float32, device="cuda")
+        args = (n, n, K, dA.data_ptr(), lda, dB.data_ptr(), n, dC.data_ptr(), n, stream.cuda_stream)
         desc = gb.gemm355_kernel_desc(gb.VARIANT_AUTO, gb.BF16, *args[:-1])
 
         def go(args=args):
             st = gb.gemm_bf16f32acc(*args)
             if st != gb.OK:
                 raise gb.Gemm355Error(st, "gemm_bf16f32acc")
-        runs.append((K, desc, go, (dA, dB, dC)))
-    for K, desc, go, _ in runs:
+        runs.append(((n, K, lda), desc, go, (dA, dB, dC)))
+    for key, desc, go, _ in runs:
         for _ in range(warm):
             go()
     stream.synchronize()
-    times = {K: [] for K, *_ in runs}
+    times = {key: [] for key, *_ in runs}
     for _ in range(rounds):
-        for K, desc, go, _ in runs:
+        for key, desc, go, _ in runs:
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
             for _ in range(reps):
                 go()
             e1.record(stream)
             stream.synchronize()
-            times[K].append(e0.elapsed_time(e1) * 1e3 / reps)
-    out = ["# BF16 4096 x 4096 x K on one MI355X: K not a whole number of ring trips", "",
-           f"U[-1,1] bfloat16 operands (seed 4), FP32 C; {warm} warm-up launches per case, then all "
-           f"cases interleaved, median of {rounds} rounds of {reps} launches; HIP events.", "",
-           "| K | kernel | µs | TFLOP/s | % of 2516.6 | time per FLOP vs K = 4096 |", "|---|---|---|---|---|---|"]
-    base = float(np.median(times[4096])) / 4096
-    for K, desc, go, _ in runs:
-        us = float(np.median(times[K]))
-        tf = 2.0 * M * N * K / us / 1e6
-        out.append(f"| {K} | `{md_cell(desc)}` | {us:.1f} | {tf:.0f} | {100 * tf / PEAKS['bf16']:.1f} | "
-                   f"{us / K / base:.3f} |")
-        log(f"[ragged-k] K={K}: {us:.1f} us, {tf:.0f} TFLOP/s")
+            times[key].append(e0.elapsed_time(e1) * 1e3 / reps)
+    out = ["# BF16 n x n x K on one MI355X: K not a whole number of ring trips, and A's row alignment", "",
+           f"U[-1,1] bfloat16 operands (seed 4), FP32 C, B and C packed, A's rows of lda halves; {warm} "
+           f"warm-up launches per case, then all cases interleaved, median of {rounds} rounds of {reps} "
+           f"launches; HIP events. k-steps are 32 wide, run in trips of 4 (256 x 256 tile) or 8 "
+           f"(128 x 128 tile); the last trip's steps wholly past K are skipped. Time per FLOP is "
+           f"relative to K = lda = n.", "",
+           "| n | K | lda | k-steps run | kernel | µs | TFLOP/s | % of 2516.6 | time per FLOP vs K = n |",
+           "|---|---|---|---|---|---|---|---|---|"]
+    for (n, K, lda), desc, go, _ in runs:
+        base = float(np.median(times[(n, n, n)])) / n
+        us = float(np.median(times[(n, K, lda)]))
+        tf = 2.0 * n * n * K / us / 1e6
+        out.append(f"| {n} | {K} | {lda} | {-(-K // 32)} | `{md_cell(desc)}` | {us:.1f} | {tf:.0f} | "
+                   f"{100 * tf / PEAKS['bf16']:.1f} | {us / K / base:.3f} |")
+        log(f"[ragged-k] n={n} K={K} lda={lda}: {us:.1f} us, {tf:.0f} TFLOP/s")
     return out
 
 
@@ -810,9 +821,10 @@ def main():
                          "producer/consumer split, eight waves, 256 x 128 tiles) at 4096^3 and "
                          "8192^3, interleaved, and write the markdown table to PATH")
     ap.add_argument("--ragged-k", default=None, metavar="PATH",
-                    help="only time BF16 4096 x 4096 x K for K in 4096, 4000, 4064, 4072 (the "
-                         "direct-to-LDS kernel with the chunks past K zero-filled), interleaved, "
-                         "and write the markdown table (time per FLOP against K = 4096) to PATH")
+                    help="only time BF16 n x n x K on the direct-to-LDS kernel (n = 4096 and "
+                         "2048; K not a whole number of ring trips, A's rows packed, padded or "
+                         "off the 128-byte lines), interleaved, and write the markdown table "
+                         "(time per FLOP against K = n) to PATH")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after the GEMMs, copy this many MiB device-to-device once (a plain "
                          "copy of known size, used to scale the HBM byte counters)")

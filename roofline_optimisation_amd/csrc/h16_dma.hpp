@@ -234,15 +234,24 @@ struct DmaOp {
         if constexpr (MN) return kRows * lw + kRpi * i + lane / (64 / kRpi);
         else return 8 * ((lane & 7) ^ ((4 * (i % 2) + lane / 16) & 7));
     }
+    // One past the largest k that load i of loading wave lw reads, relative to k0.
+    __device__ __forceinline__ static int kend(int i, int lw) {
+        if constexpr (MN) return kRows * lw + kRpi * (i + 1);
+        else return 2 * kBK;
+    }
     // KR: the offset register of a chunk at k >= K is set past the buffer's range in place.
     // Every later load through that register reads a chunk at a larger or equal k (the
     // loads are issued in k order, and the clamped repeats at the end do not go back), so
-    // it stays out of range, and no other register is needed.
+    // it stays out of range, and no other register is needed.  Only a load that reaches K
+    // selects per lane; the test is uniform over the wave (a scalar branch), so the loads
+    // wholly inside K cost nothing more.
     template <bool KR>
     __device__ __forceinline__ uint32_t off(int k0, int i, int lw, int K) {
         constexpr uint32_t kOut = 0x80000000u;   // beyond num_records (2^31 - 1)
         uint32_t &v = voff[MN ? (i & 1) : i];
-        if constexpr (KR) v = k0 + kpos(i, lw, lane_here()) < K ? v : kOut;
+        if constexpr (KR) {
+            if (k0 + kend(i, lw) > K) v = k0 + kpos(i, lw, lane_here()) < K ? v : kOut;
+        }
         return v;
     }
     __device__ __forceinline__ void issue_at(uint32_t lds0, int roff, int lw, int ld, int place,
@@ -349,13 +358,16 @@ __device__ __forceinline__ void store_tile(floatx4 (&acc)[kMB][kNB], float *__re
 
 // WHOLE: the caller guarantees that the tile lies inside M x N (no guarded stores).
 // KR: K is not a whole number of ring trips (K a multiple of 8): the loop runs to the next
-// whole trip and every chunk at k >= K loads as zeros (DmaOp::issue).
+// whole trip, every chunk at k >= K loads as zeros (DmaOp::issue), and the k-steps of the
+// last trip that lie wholly at k >= K are skipped.
 template <typename T, bool A_MN, bool B_MN, int EPI, int EM, int EN, int WM, int WN, int NS, int PW,
           bool WHOLE = false, bool KR = false>
 __device__ __forceinline__ void dma_tile(int M, int N, int K, const uint16_t *__restrict__ A, int lda,
                                          const uint16_t *__restrict__ B, int ldb,
                                          float *__restrict__ C, int ldc, float sign,
                                          int flags, int m0, int n0, char *lds_raw) {
+    // the producer waves run every k-step's barrier; they do not skip the tail's steps
+    static_assert(!(KR && PW > 0), "K past whole ring trips needs the compute waves to load");
     using G = Geo<EM, EN, WM, WN, NS, PW>;
     constexpr int kMB = G::kMB, kNB = G::kNB, kBOff = G::kBOff, kNs = NS, kLW = G::kLW;
     using OA = DmaOp<A_MN, EM, kLW, NS, kMB>;
@@ -531,6 +543,16 @@ __device__ __forceinline__ void dma_tile(int M, int N, int K, const uint16_t *__
     // zero-filling offsets; the others the plain ones
     auto kstep = [&](int kt, auto u_c, auto b_c) { kstep_impl(kt, u_c, b_c, std::false_type{}); };
     auto kstep_kr = [&](int kt, auto u_c, auto b_c) { kstep_impl(kt, u_c, b_c, std::true_type{}); };
+    // KR, last trip: a k-step that lies wholly at k >= K would multiply zeros, so it is
+    // skipped whole, loads, wait and barrier included.  The test is uniform over the
+    // workgroup, so every wave skips the same steps; the loads the skipped steps would
+    // have waited for read nothing inside K, and the wait after the loop drains them.
+    // The last trip's first step always holds some k < K (nk - kNs < cdiv(K, 32)).
+    const int nk_live = cdiv(K, kBK);
+    auto kstep_tail = [&](int kt, auto u_c, auto b_c) {
+        constexpr int u = decltype(u_c)::value;
+        if (u == 0 || __builtin_expect(kt + u < nk_live, 1)) kstep_impl(kt, u_c, b_c, std::true_type{});
+    };
 
     if constexpr (PW == 0) prologue_loads(wave);
     __syncthreads();
@@ -555,7 +577,7 @@ __device__ __forceinline__ void dma_tile(int M, int N, int K, const uint16_t *__
                       std::integral_constant<int, G::kBarrier>{});
         for_steps(kstep_kr, kt, std::make_integer_sequence<int, kNs>{},
                   std::integral_constant<int, G::kBarrier>{});
-        for_steps(kstep_kr, kt + kNs, std::make_integer_sequence<int, kNs>{},
+        for_steps(kstep_tail, kt + kNs, std::make_integer_sequence<int, kNs>{},
                   std::integral_constant<int, G::kBarrier>{});
     } else {
         for (int kt = 0; kt < nk; kt += kNs)

@@ -117,10 +117,13 @@ MODES = [(False, False, False), (True, False, False), (False, True, True)]  # na
 SHAPES = {"f32": [(3072, 3072, 64), (1024, 768, 96), (2048, 2048, 64), (1536, 1536, 96), (1351, 1537, 100),
                   (2000, 1996, 256), (2000, 1996, 260)],
           "f16": [(3072, 3072, 128), (3072, 2816, 192), (1024, 1024, 128), (4000, 3992, 128),
-                  (3072, 3072, 64)],
+                  (3072, 3072, 64), (2048, 2048, 264)],
           "bf16": [(3072, 3072, 256), (1024, 512, 64), (2000, 2040, 256)]}
 # FP32 (2000, 1996, 256) and (2000, 1996, 260): ragged tiles in the unpredicated kernel
 # with the full ones, the latter with a zero-filled last k-step.
+# (3072, 2816, 192) and (2048, 2048, 264): K not a whole number of ring trips on the
+# direct-to-LDS kernel (256 x 256 and 128 x 128 tiles; the last trip's steps past K are
+# skipped: 2 of 4 and 7 of 8).
 # (4000, 3992, 128) and (2000, 2040, 256): every tile, ragged ones included, on the
 # direct-to-LDS kernel (256 x 256 and 128 x 128 tiles); the padding around the operands
 # holds NaN, so a ragged tile's loads past the matrix would show in its stored outputs.

@@ -483,7 +483,14 @@ RAGGED_K_CASES = [("bf16", (4096, 4096, 4000), (0, 0, 0), "full"),
                   ("bf16", (4096, 4096, 4072), (8, 16, 8), "rows"),
                   ("f16", (3072, 2816, 136), (8, 8, 8), "full"),
                   ("bf16", (2048, 2048, 2000), (8, 8, 0), "full"),
-                  ("f16", (4000, 4000, 1000), (8, 0, 0), "rows")]
+                  ("f16", (4000, 4000, 1000), (8, 0, 0), "rows"),
+                  ("bf16", (4096, 4096, 4104), (0, 0, 0), "rows"),
+                  ("f16", (2048, 2048, 1800), (8, 8, 8), "full"),
+                  ("f16", (2048, 2048, 264), (0, 0, 0), "full")]
+# The ring runs whole trips of 4 (256 x 256 tile) or 8 (128 x 128) 32-wide k-steps, and
+# the k-steps of the last trip that lie wholly past K are skipped: K = 4000 skips 3 of its
+# last trip's 4, 4064 one, 4072 none (its last step is part zeros), 4104 three; 2000, 1800
+# and 264 skip 1, 7 and 7 of 8 (264: one plain trip, then a trip with a single live step).
 
 
 @pytest.mark.parametrize("case", RAGGED_K_CASES, ids=lambda c: c[0] + "_" + "x".join(map(str, c[1])) + f"_pad{c[2][0]}")
