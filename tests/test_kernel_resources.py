@@ -17,17 +17,24 @@ HIPCC = gbuild.HIPCC
 
 
 @pytest.fixture(scope="module")
-def remarks():
+def compiled():
+    """{source: (gfx950 assembly, resource-usage remarks)}: every HIP source compiled once,
+    device code only."""
     if not os.path.exists(HIPCC) and shutil.which("hipcc") is None:
         pytest.skip("hipcc not available")
     def one(src):
-        r = subprocess.run([HIPCC, *gbuild.HIPFLAGS, "-c", src, "-o", os.devnull,
+        r = subprocess.run([HIPCC, *gbuild.HIPFLAGS, "--cuda-device-only", "-S", src, "-o", "-",
                             "-Rpass-analysis=kernel-resource-usage"],
                            capture_output=True, text=True)
         assert r.returncode == 0, r.stderr[-2000:]
-        return os.path.basename(src), r.stderr
+        return src, (r.stdout, r.stderr)
     with cf.ThreadPoolExecutor(min(8, os.cpu_count() or 1)) as ex:
         return dict(ex.map(one, gbuild.sources()))
+
+
+@pytest.fixture(scope="module")
+def remarks(compiled):
+    return {os.path.basename(src): rem for src, (_, rem) in compiled.items()}
 
 
 def parse(text):
@@ -63,17 +70,9 @@ def test_lds_within_160k(remarks):
 
 
 @pytest.fixture(scope="module")
-def assembly():
-    """{source: gfx950 assembly} for every HIP source (compiled once for the tests below)."""
-    if not os.path.exists(HIPCC) and shutil.which("hipcc") is None:
-        pytest.skip("hipcc not available")
-    def one(src):
-        r = subprocess.run([HIPCC, *gbuild.HIPFLAGS, "--cuda-device-only", "-S", src, "-o", "-"],
-                           capture_output=True, text=True)
-        assert r.returncode == 0, r.stderr[-2000:]
-        return src, r.stdout
-    with cf.ThreadPoolExecutor(min(8, os.cpu_count() or 1)) as ex:
-        return dict(ex.map(one, gbuild.sources()))
+def assembly(compiled):
+    """{source: gfx950 assembly} for every HIP source."""
+    return {src: asm for src, (asm, _) in compiled.items()}
 
 
 def test_no_packed_fp32_instructions(assembly):
