@@ -37,9 +37,23 @@ import numpy as np
 DTYPES = ("f32", "f16", "bf16")
 
 
+# U[-1, 1] matrices larger than this many elements are drawn in pieces of this size, so
+# a 2^30-element operand does not need its float64 draw in memory at once.  The values are
+# the same: the generator hands out one double per element in row-major order whatever
+# the size of each call.
+UNIFORM_CHUNK = 1 << 24
+
+
 def _draw(rng: np.random.Generator, shape, dist: str) -> np.ndarray:
     if dist == "uniform":
-        return rng.uniform(-1.0, 1.0, size=shape).astype(np.float32)
+        n = int(np.prod(shape))
+        if n <= UNIFORM_CHUNK:
+            return rng.uniform(-1.0, 1.0, size=shape).astype(np.float32)
+        out = np.empty(n, dtype=np.float32)
+        for s in range(0, n, UNIFORM_CHUNK):
+            e = min(n, s + UNIFORM_CHUNK)
+            out[s:e] = rng.uniform(-1.0, 1.0, size=e - s)  # float64 -> float32, RNE
+        return out.reshape(shape)
     if dist == "normal":
         return rng.standard_normal(size=shape).astype(np.float32)
     if dist == "int":

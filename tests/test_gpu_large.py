@@ -1,0 +1,76 @@
+"""GPU parity on operands larger than 2 GiB (the largest inputs the entry points take
+with int32 sizes): the kernels address each tile of a k-contiguous operand from its own
+64-bit base and keep every buffer offset within 31 bits, so
+
+* an A of more than 2^31 bytes puts the bases of its later tiles past 2^31 bytes while
+  each tile's offsets stay small (the direct-to-LDS and buffer-load kernels), and
+* a B whose byte offsets from its first row reach past 2^31 (K x N x element size above
+  2 GiB) makes the host fall back to pointer loads.
+
+Checked on sampled rows (those whose first byte lies on either side of 2^31 included)
+and, where B is the large operand, sampled columns, against the oracle on the same
+rows and columns; same bars as the other parity tests.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import errors, gpu_gemm, sample_rows, tolerance
+from roofline_optimisation_amd import binding as gb
+from roofline_optimisation_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+ESIZE = {"f32": 4, "f16": 2, "bf16": 2}
+
+# dtype, (M, N, K), the operand above 2 GiB, a part of the kernel description it must get
+LARGE_CASES = [
+    ("f16", (131328, 512, 8192), "A", "256x256x32 w2x2 lds-dma"),      # A 2.15 GB
+    ("f32", (140032, 256, 4096), "A", "mfma_f32 128x128x32"),          # A 2.29 GB
+    ("f16", (256, 26624, 40960), "B", "| interior=pointer"),           # B 2.18 GB
+    ("f32", (256, 33024, 16384), "B", "mfma_f32 64x64x32"),            # B 2.16 GB
+]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.init()
+
+
+@pytest.mark.parametrize("case", LARGE_CASES,
+                         ids=lambda c: f"{c[0]}_" + "x".join(map(str, c[1])) + f"_big{c[2]}")
+def test_operand_over_2gib(case):
+    dtype, (M, N, K), big, part = case
+    es = ESIZE[dtype]
+    assert (M * K if big == "A" else K * N) * es > 2 ** 31
+    P = 1 << 20  # a 16-byte-aligned address: the query only inspects it
+    desc = gb.gemm355_kernel_desc(gb.VARIANT_AUTO, gb.DTYPE_CODES[dtype], M, N, K, P, K, P, N, P, N)
+    assert part in desc, desc
+    print(f"large {dtype} {M}x{N}x{K} ({big} above 2 GiB): {desc}", flush=True)
+    A, B = inputs.make_operands(M, N, K, 61, "uniform", dtype)
+    C, ok = gpu_gemm(A, B, dtype, entry="typed", guard_rows=1)
+    assert ok, "wrote outside C"
+    if big == "A":
+        r0 = 2 ** 31 // (K * es)  # first row that starts at or past byte 2^31
+        rows = np.array(sorted(set(sample_rows(M, 40, seed=1).tolist()) |
+                               {r0 - 1, r0, r0 + 1, M - 1}))
+        cols = np.arange(N)
+    else:
+        rows = sample_rows(M, 16, seed=2)
+        cols = sample_rows(N, 64, seed=3)
+    Ab = np.ascontiguousarray(A[rows])
+    Bb = np.ascontiguousarray(B[:, cols])
+    del A, B
+    C64, _ = oracle.gemm(Ab, Bb, dtype)
+    Cs = C[np.ix_(rows, cols)]
+    assert not np.isnan(Cs).any(), "NaN in result (read outside the operands?)"
+    rel, mx = errors(Cs, C64)
+    trel, tabs = tolerance(dtype, "uniform", K)
+    print(f"large {dtype} {M}x{N}x{K}: rel_frob={rel:.3e} max_abs={mx:.3e}", flush=True)
+    assert rel <= trel and mx <= tabs, f"rel {rel:.3e} (<= {trel}), max {mx:.3e} (<= {tabs})"

@@ -35,6 +35,17 @@ def test_draw_rows_is_a_prefix(dist):
     assert np.array_equal(inputs.draw_rows(50, 33, 9, dist, "f32", rows=17), A[:17])
 
 
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_uniform_pieces_equal_one_draw(monkeypatch, dtype):
+    """Large U[-1,1] matrices are drawn in pieces; the values must be those of one draw
+    (here with pieces of 1000 elements, not a divisor of either operand's size)."""
+    A1, B1 = inputs.make_operands(61, 47, 83, 11, "uniform", dtype)
+    monkeypatch.setattr(inputs, "UNIFORM_CHUNK", 1000)
+    A2, B2 = inputs.make_operands(61, 47, 83, 11, "uniform", dtype)
+    assert np.array_equal(A1, A2) and np.array_equal(B1, B2)
+    assert np.array_equal(inputs.draw_rows(61, 83, 11, "uniform", dtype, rows=29), A1[:29])
+
+
 def test_ranges():
     A, B = inputs.make_operands(100, 90, 80, 1, "uniform")
     assert A.dtype == np.float32 and A.min() >= -1 and A.max() <= 1
