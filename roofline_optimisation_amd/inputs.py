@@ -80,10 +80,18 @@ def f32_to_f16_bits(x: np.ndarray) -> np.ndarray:
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
-    """Round finite float32 values to bfloat16 (RNE) and return the bit patterns."""
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    bias = 0x7FFF + ((u >> 16) & 1)
-    return ((u + bias) >> 16).astype(np.uint16)
+    """Round finite float32 values to bfloat16 (RNE) and return the bit patterns.
+
+    Works on the binary32 patterns in pieces of UNIFORM_CHUNK elements, in uint32: for a
+    finite value the pattern is at most 0xFF7FFFFF, so adding the rounding bias (at most
+    0x8000) cannot wrap."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.reshape(-1).view(np.uint32)
+    out = np.empty(u.size, dtype=np.uint16)
+    for s in range(0, u.size, UNIFORM_CHUNK):
+        v = u[s:s + UNIFORM_CHUNK]
+        out[s:s + UNIFORM_CHUNK] = (v + (np.uint32(0x7FFF) + ((v >> 16) & np.uint32(1)))) >> 16
+    return out.reshape(x.shape)
 
 
 def to_storage(x: np.ndarray, dtype: str) -> np.ndarray:

@@ -18,7 +18,7 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_util import errors, gpu_gemm, sample_rows, tolerance
+from gpu_util import SENTINEL, errors, gpu_gemm, nan_fill, place, sample_rows, to_device, tolerance
 from roofline_optimisation_amd import binding as gb
 from roofline_optimisation_amd import inputs
 
@@ -73,4 +73,64 @@ def test_operand_over_2gib(case):
     rel, mx = errors(Cs, C64)
     trel, tabs = tolerance(dtype, "uniform", K)
     print(f"large {dtype} {M}x{N}x{K}: rel_frob={rel:.3e} max_abs={mx:.3e}", flush=True)
+    assert rel <= trel and mx <= tabs, f"rel {rel:.3e} (<= {trel}), max {mx:.3e} (<= {tabs})"
+
+
+# The general form (gemm355_gemm_ex) with the large operand transposed: A stored K x M
+# (m-contiguous: its offsets pass 2^31, pointer loads) or B stored N x K (k-contiguous:
+# its later tiles start past 2^31, on the buffer-load and direct-to-LDS kernels).  The
+# stored matrices are drawn in their stored shape: A from default_rng(seed), B from
+# default_rng(seed + 1).
+EX_CASES = [
+    ("f16", (26624, 256, 40960), "ta", "| interior=pointer"),          # stored A 2.18 GB
+    ("f32", (256, 140032, 4096), "tb", "mfma_f32 128x128x32"),         # stored B 2.29 GB
+    ("bf16", (256, 131328, 8192), "tb", "256x256x32 w2x2 lds-dma"),    # stored B 2.15 GB
+]
+
+
+@pytest.mark.parametrize("case", EX_CASES,
+                         ids=lambda c: f"{c[0]}_" + "x".join(map(str, c[1])) + f"_{c[2]}")
+def test_general_form_operand_over_2gib(case):
+    import torch
+    dtype, (M, N, K), t, part = case
+    ta = t == "ta"
+    flags = gb.TRANS_A if ta else gb.TRANS_B
+    es = ESIZE[dtype]
+    sa_shape = (K, M) if ta else (M, K)
+    sb_shape = (K, N) if ta else (N, K)
+    assert (M * K if ta else N * K) * es > 2 ** 31
+    P = 1 << 20  # a 16-byte-aligned address: the query only inspects it
+    desc = gb.gemm355_kernel_desc_ex(gb.VARIANT_AUTO, gb.DTYPE_CODES[dtype], flags, M, N, K,
+                                     P, sa_shape[1], P, sb_shape[1], P, N)
+    assert part in desc, desc
+    print(f"large general form {dtype} {M}x{N}x{K} {t}: {desc}", flush=True)
+    SA = inputs.draw_rows(*sa_shape, 63, "uniform", dtype)
+    SB = inputs.draw_rows(*sb_shape, 64, "uniform", dtype)
+    dA = to_device(place(SA, sa_shape[1], 0, 1, nan_fill(dtype)))
+    dB = to_device(place(SB, sb_shape[1], 0, 1, nan_fill(dtype)))
+    dC = torch.full((M + 1, N), float(SENTINEL), dtype=torch.float32, device="cuda")
+    st = gb.gemm355_gemm_ex(gb.VARIANT_AUTO, gb.DTYPE_CODES[dtype], flags, M, N, K,
+                            dA.data_ptr(), sa_shape[1], dB.data_ptr(), sb_shape[1],
+                            dC.data_ptr(), N, torch.cuda.current_stream().cuda_stream)
+    assert st == gb.OK, st
+    torch.cuda.synchronize()
+    out = dC.cpu().numpy()
+    del dA, dB, dC
+    assert np.all(out[M] == SENTINEL), "wrote past C"
+    C = out[:M]
+    if ta:
+        rows = sample_rows(M, 24, seed=4)
+        cols = np.arange(N)
+        C64, _ = oracle.gemm_ex(np.ascontiguousarray(SA[:, rows]), SB, dtype, True, False)
+    else:
+        n0 = 2 ** 31 // (K * es)  # first stored row of B that starts at or past byte 2^31
+        rows = np.arange(M)
+        cols = np.array(sorted(set(sample_rows(N, 40, seed=5).tolist()) | {n0 - 1, n0, n0 + 1}))
+        C64, _ = oracle.gemm_ex(SA, np.ascontiguousarray(SB[cols]), dtype, False, True)
+    Cs = C[np.ix_(rows, cols)]
+    assert not np.isnan(Cs).any(), "NaN in result (read outside the operands?)"
+    rel, mx = errors(Cs, C64)
+    trel, tabs = tolerance(dtype, "uniform", K)
+    print(f"large general form {dtype} {M}x{N}x{K} {t}: rel_frob={rel:.3e} max_abs={mx:.3e}",
+          flush=True)
     assert rel <= trel and mx <= tabs, f"rel {rel:.3e} (<= {trel}), max {mx:.3e} (<= {tabs})"

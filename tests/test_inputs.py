@@ -68,6 +68,20 @@ def test_bf16_round_to_nearest_even():
     assert np.isfinite(back[5])
 
 
+def test_bf16_pieces_match_wide_arithmetic(monkeypatch):
+    """The piecewise uint32 rounding equals RNE done in uint64 on the whole array, for
+    every sign and exponent (extreme finite values and infinities included)."""
+    rng = np.random.default_rng(5)
+    x = np.concatenate([
+        (rng.standard_normal(5000) * np.exp(rng.uniform(-80, 80, 5000))).astype(np.float32),
+        np.array([np.finfo(np.float32).max, -np.finfo(np.float32).max, np.inf, -np.inf,
+                  0.0, -0.0, 1e-45, -1e-45], np.float32)])
+    u = x.view(np.uint32).astype(np.uint64)
+    ref = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    monkeypatch.setattr(inputs, "UNIFORM_CHUNK", 777)
+    assert np.array_equal(inputs.f32_to_bf16_bits(x), ref)
+
+
 def test_f16_matches_numpy():
     x = np.random.default_rng(0).uniform(-1, 1, 1000).astype(np.float32)
     assert np.array_equal(inputs.f32_to_f16_bits(x).view(np.float16), x.astype(np.float16))
