@@ -134,3 +134,43 @@ def test_general_form_operand_over_2gib(case):
     print(f"large general form {dtype} {M}x{N}x{K} {t}: rel_frob={rel:.3e} max_abs={mx:.3e}",
           flush=True)
     assert rel <= trel and mx <= tabs, f"rel {rel:.3e} (<= {trel}), max {mx:.3e} (<= {tabs})"
+
+
+# A C of more than 2^31 elements (8.6 GB of FP32): the epilogues index C in 64 bits.  C
+# starts as NaN (an element left unwritten would show) with one guard row of the
+# sentinel after it; sampled rows (the first row past element 2^31 included) are read
+# back and compared with the oracle on the same rows.
+C_CASES = [("f16", (65792, 32768, 128), "256x256x32 w2x2 lds-dma"),
+           ("f32", (65792, 32768, 100), "mfma_f32 128x128x32")]   # K tail: 100 = 3 x 32 + 4
+
+
+@pytest.mark.parametrize("case", C_CASES, ids=lambda c: f"{c[0]}_" + "x".join(map(str, c[1])))
+def test_c_over_2g_elements(case):
+    import torch
+    dtype, (M, N, K), part = case
+    assert M * N > 2 ** 31
+    P = 1 << 20  # a 16-byte-aligned address: the query only inspects it
+    desc = gb.gemm355_kernel_desc(gb.VARIANT_AUTO, gb.DTYPE_CODES[dtype], M, N, K, P, K, P, N, P, N)
+    assert part in desc, desc
+    print(f"large C {dtype} {M}x{N}x{K}: {desc}", flush=True)
+    A, B = inputs.make_operands(M, N, K, 65, "uniform", dtype)
+    dA, dB = to_device(A), to_device(B)
+    dC = torch.full((M + 1, N), float("nan"), dtype=torch.float32, device="cuda")
+    dC[M] = float(SENTINEL)
+    f = {"f32": gb.gemm_f32, "f16": gb.gemm_f16f32acc, "bf16": gb.gemm_bf16f32acc}[dtype]
+    st = f(M, N, K, dA.data_ptr(), K, dB.data_ptr(), N, dC.data_ptr(), N,
+           torch.cuda.current_stream().cuda_stream)
+    assert st == gb.OK, st
+    torch.cuda.synchronize()
+    r0 = -(-2 ** 31 // N)  # first row whose elements all lie past element 2^31
+    rows = np.array(sorted(set(sample_rows(M, 24, seed=6).tolist()) | {r0 - 1, r0, M - 1}))
+    C = dC[torch.from_numpy(rows).cuda()].cpu().numpy()
+    guard = dC[M].cpu().numpy()
+    del dA, dB, dC
+    assert np.all(guard == SENTINEL), "wrote past C"
+    assert not np.isnan(C).any(), "an element of C was not written"
+    C64, _ = oracle.gemm(np.ascontiguousarray(A[rows]), B, dtype)
+    rel, mx = errors(C, C64)
+    trel, tabs = tolerance(dtype, "uniform", K)
+    print(f"large C {dtype} {M}x{N}x{K}: rel_frob={rel:.3e} max_abs={mx:.3e}", flush=True)
+    assert rel <= trel and mx <= tabs, f"rel {rel:.3e} (<= {trel}), max {mx:.3e} (<= {tabs})"
