@@ -833,7 +833,8 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}, WORLD_SIZE {world}): "
-              "this library is a single-GPU GEMM; see the sharding notes in DESIGN.md",
+              "this library is a single-GPU GEMM (a multi-GPU product would give each GPU a "
+              "block of rows of A and C and all of B, and run this same call on each)",
               file=sys.stderr)
         sys.exit(2)
 
