@@ -25,8 +25,10 @@ const char *desc_mfma_f16(int dtype, const GemmArgs &g) {
     const bool big = pick_tile(g) == 256;
     const char *name = dtype == kF16 ? "mfma_f16" : "mfma_bf16";
     const int epi = g.c16 ? 2 : (g.signed_or_acc() ? 1 : 0);
-    const bool narrow = !big && !g.trans_a && epi == 0 && use_128x64(g);
-    const int bm = big ? 256 : 128, bn = big ? 256 : (narrow ? 64 : 128);
+    const bool plain_km = !big && !g.trans_a && epi == 0;
+    const bool small = plain_km && use_64x64(g);
+    const bool narrow = plain_km && !small && use_128x64(g);
+    const int bm = big ? 256 : (small ? 64 : 128), bn = big ? 256 : (small || narrow ? 64 : 128);
     const H16Plan p = plan_cfg(bm, bn, g.trans_a != 0, g.trans_b == 0, epi, g);
     out = name;
     if (p.dma) {
@@ -34,7 +36,9 @@ const char *desc_mfma_f16(int dtype, const GemmArgs &g) {
         if (dma_ragged_k(g, bm)) out += " k-zero-fill";
         return out.c_str();
     }
-    out += big ? " 256x256x64 w2x2 dwordx4" : (narrow ? " 128x64x64 w2x2 dwordx4" : " 128x128x64 w2x2 dwordx4");
+    out += big ? " 256x256x64 w2x2 dwordx4"
+               : (small ? " 64x64x64 w1x2 dwordx4"
+                        : (narrow ? " 128x64x64 w2x2 dwordx4" : " 128x128x64 w2x2 dwordx4"));
     if (!v) out += " unaligned";
     // the launches: [all=...] or [interior=...][edges=...]
     auto edge_name = [&](int mode, bool paired) {

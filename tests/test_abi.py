@@ -144,7 +144,7 @@ def test_dispatch_choices_general_form(lib):
     assert dx(-1, 1, gb.TRANS_A, 1000, 1000, 1004, P, 1000, P, 1000, P, 1000) == \
         "mfma_f16 128x128x64 w2x2 dwordx4 | edges=clamped,paired"
     assert dx(-1, 2, gb.TRANS_B, 1000, 1000, 1004, P, 1004, P, 1004, P, 1000) == \
-        "mfma_bf16 128x64x64 w2x2 dwordx4 unaligned | edges=clamped,paired"
+        "mfma_bf16 64x64x64 w1x2 dwordx4 unaligned | edges=clamped,paired"
     # signed and accumulating epilogues keep to one staging set
     assert dx(-1, 1, gb.TRANS_A | gb.NEG_A, 1000, 1000, 1004, P, 1000, P, 1000, P, 1000) == \
         "mfma_f16 128x128x64 w2x2 dwordx4 | edges=clamped"

@@ -454,10 +454,12 @@ def test_f32_tile_classes(case):
     check(C[rows], C64, "f32", "uniform", K, ok, f"f32 tile class {tile} {M}x{N}x{K}")
 
 
-# FP16/BF16 tile classes: 128 x 64 (plain products whose 128 x 128 tiling leaves CUs idle;
-# interior, ragged, K tail), 128 x 128, 256 x 256 direct-to-LDS.
-H16_TILE_CASES = [("f16", (1024, 1024, 256), "128x64"), ("bf16", (1000, 900, 200), "128x64"),
-                  ("f16", (512, 512, 100), "128x64"), ("bf16", (2048, 2048, 128), "128x128"),
+# FP16/BF16 tile classes of plain products: 64 x 64 (the 128 x 64 tiling would still leave
+# CUs idle; interior, ragged, K tail), 128 x 64 (the 128 x 128 tiling would; interior and
+# ragged), 128 x 128, 256 x 256 direct-to-LDS.
+H16_TILE_CASES = [("f16", (1024, 1024, 256), "64x64x64 w1x2"), ("bf16", (1000, 900, 200), "64x64x64 w1x2"),
+                  ("f16", (512, 512, 100), "64x64x64 w1x2"), ("bf16", (1536, 1536, 128), "128x64x64"),
+                  ("f16", (1500, 1450, 200), "128x64x64"), ("bf16", (2048, 2048, 128), "128x128"),
                   ("f16", (3072, 3072, 128), "lds-dma")]
 
 
