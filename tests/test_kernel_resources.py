@@ -86,17 +86,22 @@ def test_inline_mfma_accumulators_fenced(assembly):
     inserts no wait states for them.  In every kernel whose MFMAs are inline assembly,
     every compiler-generated instruction that names an accumulator register (a copy, a
     zeroing write, a store) lies either before the two-`s_nop 7` block that precedes the
-    first MFMA or after the four-`s_nop 7` block that follows the last one."""
+    first MFMA or after the four-`s_nop 7` block that follows the last one, and no branch
+    between them leaves that region except to the start of the closing block (so the
+    skipped k-steps of a ragged-K tail still pass it)."""
     kernels = 0
     for src, asm in assembly.items():
         for body in re.split(r"\n(?=_Z\S+:)", asm):
             lines = [ln.strip() for ln in body.splitlines() if ln.strip()]
             in_asm, items = False, []  # (instruction, from inline assembly)
+            labels = {}  # block label -> index of the instruction that follows it
             for ln in lines:
                 if ln.startswith(";;#ASMSTART"):
                     in_asm = True
                 elif ln.startswith(";;#ASMEND"):
                     in_asm = False
+                elif re.match(r"\.LBB\w+:", ln):
+                    labels[ln.split(":")[0]] = len(items)
                 elif not ln.startswith((";", ".")) and not ln.endswith(":"):
                     items.append((ln, in_asm))
             mfma = [i for i, (ln, a) in enumerate(items) if a and ln.startswith("v_mfma")]
@@ -114,6 +119,11 @@ def test_inline_mfma_accumulators_fenced(assembly):
                 if a:
                     continue
                 assert not re.search(r"\ba(?:\d+|\[\d+:\d+\])", ln), (src, body[:60], ln)
+                # every path out of the fenced region passes the closing wait-state block:
+                # a branch inside it lands inside it or at the block's start at the latest
+                m = re.match(r"s_(?:c?branch\w*)\s+(\.LBB\w+)$", ln)
+                if m:
+                    assert lo <= labels[m.group(1)] <= post[0], (src, body[:60], ln)
     assert kernels >= 40
 
 
