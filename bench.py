@@ -213,7 +213,9 @@ def time_variant(variant, dtype, M, N, K, seed, reps=None):
     one = max(e0.elapsed_time(e1), 1e-3)
     if reps is None:
         reps = int(min(200, max(3, 100.0 / one)))  # about 100 ms of timed work
-    for _ in range(2):
+    # about 50 ms of untimed launches first: the clocks take that long to settle after
+    # the host-side set-up of each case has left the GPU idle
+    for _ in range(int(min(2000, max(2, 50.0 / one)))):
         launch()
     e0.record(stream)
     for _ in range(reps):
@@ -741,7 +743,8 @@ def write_report(path):
 
     names = {0: "naive", 1: "lds_tiled", 2: "regblock", 3: "mfma"}
     lines = ["# libgemm355 measurements on one MI355X", "",
-             "Per-launch time from HIP events on one stream (mean over >= 3 launches after warm-up),",
+             "Per-launch time from HIP events on one stream (mean over >= 3 launches after about 50 ms",
+             "of untimed launches of the same case),",
              "U[-1,1] operands, packed row-major strides.  TFLOP/s = 2MNK / t.  Peaks: FP32 157.3,",
              "FP16/BF16 2516.6 TFLOP/s (2.4 GHz datasheet); attainable = min(peak, OI x 8 TB/s)",
              "with OI = 2MNK / ideal bytes (each operand read once, C written once).", "",
