@@ -70,10 +70,12 @@ struct Geo {
     static constexpr int kBOff = NS * kStageA;            // the B ring follows the A ring
     static constexpr int kLds = NS * (kStageA + kStageB);
     // MFMAs per k-step, the step's wait and barrier after kBarrier of them, its loads
-    // spread over the first kLoadHi
+    // spread evenly over every MFMA before the wait (bunching them into fewer MFMAs
+    // measured slower: 256 x 256, loads over 16 / 24 / 32 / 40 of 64 MFMAs at FP16 4096^3:
+    // 104.3 / 102.3 / 101.5 / 100.7 us; over 40 instead of 32, BF16 8192^3 2.5 % faster)
     static constexpr int kMf = kMB * kNB;
     static constexpr int kBarrier = kMf * 5 / 8;
-    static constexpr int kLoadHi = kMf / 2;
+    static constexpr int kLoadHi = kBarrier;
     static_assert(kTM % 16 == 0 && kTN % 16 == 0, "wave tiles are whole 16 x 16 quads");
     static_assert(NS % 2 == 0 && NS >= 4, "a KM operand's double steps take two stages each");
     static_assert(kLds <= 160 * 1024, "LDS budget");
