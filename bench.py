@@ -396,6 +396,74 @@ def schedule_lines(warm=300, rounds=3, reps=100):
     return out
 
 
+# Shapes where the dispatcher takes the 192 x 256 direct-to-LDS tile, each with the
+# 256 x 256 tile timed beside it (dtype, M, N, K).
+TILE_SHAPES = [("f16", 3072, 3072, 3072), ("bf16", 3072, 3072, 3072), ("f16", 3072, 4096, 4096),
+               ("f16", 4096, 4104, 4096), ("f16", 4608, 4608, 4608), ("f16", 6144, 6144, 4096),
+               ("f16", 3000, 3072, 1024), ("bf16", 3072, 3072, 1000)]
+
+
+def tile_lines(warm=300, rounds=5, reps=100):
+    """The 192 x 256 tile against the 256 x 256 one (gemm355_run_variant MFMA_T256X256) on
+    the shapes the dispatcher gives it: U[-1,1] operands (seed 3), packed strides; both
+    cases warmed, then timed interleaved, median of `rounds` rounds of `reps` launches
+    (HIP events on one stream).  Rounds: ceil(tiles / 256), the waves of one-tile-per-CU
+    work each grid takes."""
+    import torch
+
+    from roofline_optimisation_amd import binding as gb
+    from roofline_optimisation_amd import inputs
+
+    cdiv = lambda a, b: -(-a // b)
+    stream = torch.cuda.Stream()
+    out = ["# 192 x 256 against 256 x 256 direct-to-LDS tiles on one MI355X", "",
+           f"U[-1,1] operands (seed 3), packed strides, FP32 C; {warm} warm-up launches per case, then "
+           f"both cases interleaved, median of {rounds} rounds of {reps} launches; HIP events.  "
+           "Rounds = ceil(tiles / 256 CUs).", "",
+           "| dtype | M x N x K | 256x256 tiles (rounds) | 192x256 tiles (rounds) | 256x256 µs | "
+           "dispatched µs | speedup | TFLOP/s | % of peak | dispatched kernel |",
+           "|---|---|---|---|---|---|---|---|---|---|"]
+    for dt, M, N, K in TILE_SHAPES:
+        A, B = inputs.make_operands(M, N, K, 3, "uniform", dt)
+        dA = torch.from_numpy(A.view("int16")).cuda()
+        dB = torch.from_numpy(B.view("int16")).cuda()
+        dC = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        runs = []
+        for v in (gb.VARIANT_MFMA_T256X256, gb.VARIANT_AUTO):
+            args = (v, gb.DTYPE_CODES[dt], M, N, K, dA.data_ptr(), K, dB.data_ptr(), N,
+                    dC.data_ptr(), N, stream.cuda_stream)
+
+            def go(args=args):
+                st = gb.gemm355_run_variant(*args)
+                if st != gb.OK:
+                    raise gb.Gemm355Error(st, "gemm355_run_variant")
+            runs.append((v, gb.gemm355_kernel_desc(*args[:-1]), go))
+        for _, _, go in runs:
+            for _ in range(warm):
+                go()
+        stream.synchronize()
+        times = {v: [] for v, _, _ in runs}
+        for _ in range(rounds):
+            for v, _, go in runs:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for _ in range(reps):
+                    go()
+                e1.record(stream)
+                stream.synchronize()
+                times[v].append(e0.elapsed_time(e1) * 1e3 / reps)
+        sq, dis = (float(np.median(times[v])) for v, _, _ in runs)
+        t256 = cdiv(M, 256) * cdiv(N, 256)
+        t192 = cdiv(M, 192) * cdiv(N, 256)
+        tf = 2.0 * M * N * K / dis / 1e6
+        out.append(f"| {dt} | {M}x{N}x{K} | {t256} ({cdiv(t256, 256)}) | {t192} ({cdiv(t192, 256)}) | "
+                   f"{sq:.2f} | {dis:.2f} | {sq / dis:.3f}x | {tf:.0f} | {100 * tf / PEAKS[dt]:.1f} | "
+                   f"`{md_cell(runs[1][1])}` |")
+        log(f"[tiles] {dt} {M}x{N}x{K}: 256x256 {sq:.2f} us, dispatched {dis:.2f} us ({sq / dis:.3f}x)")
+        del dA, dB, dC
+    return out
+
+
 def general_form_lines():
     """Markdown lines timing gemm355_gemm_ex (transposed / negated operands, accumulation)
     at the headline sizes, against the plain product."""
@@ -812,7 +880,7 @@ def main():
                          "workloads, write the markdown table to PATH and print one JSON line "
                          "for the 16384 x 4096 workload; no GEMM timing")
     ap.add_argument("--family", choices=["naive", "lds_tiled", "regblock", "mfma", "mfma_split",
-                                         "mfma_w8", "mfma_t256x128"], default=None,
+                                         "mfma_w8", "mfma_t256x128", "mfma_t256x256"], default=None,
                     help="only launch one kernel family (--warmup untimed and --steps timed "
                          "launches, for counter passes) on the FP32 3072^3 workload, or with "
                          "--family-dtype f16/bf16 on the n^3 16-bit workload (seed 3); no JSON line")
@@ -823,6 +891,10 @@ def main():
                     help="only time the schedules of the FP16 direct-to-LDS kernel (dispatched, "
                          "producer/consumer split, eight waves, 256 x 128 tiles) at 4096^3 and "
                          "8192^3, interleaved, and write the markdown table to PATH")
+    ap.add_argument("--tiles", default=None, metavar="PATH",
+                    help="only time the 192 x 256 direct-to-LDS tile against the 256 x 256 one on "
+                         "the shapes the dispatcher gives it, interleaved, and write the markdown "
+                         "table to PATH")
     ap.add_argument("--ragged-k", default=None, metavar="PATH",
                     help="only time BF16 n x n x K on the direct-to-LDS kernel (n = 4096 and "
                          "2048; K not a whole number of ring trips, A's rows packed, padded or "
@@ -874,6 +946,12 @@ def main():
         with open(args.ragged_k, "w") as f:
             f.write("\n".join(ragged_k_lines(warm=max(args.warmup, 1))) + "\n")
         log(f"[bench] ragged-K table written to {args.ragged_k}")
+        return
+
+    if args.tiles:
+        with open(args.tiles, "w") as f:
+            f.write("\n".join(tile_lines(warm=max(args.warmup, 1))) + "\n")
+        log(f"[bench] tile table written to {args.tiles}")
         return
 
     if args.schedules:

@@ -60,6 +60,9 @@ struct GemmArgs {
     // C (and the old C when accumulating) is stored in the operands' 16-bit type: C
     // then points to uint16_t patterns and ldc counts those.
     int c16 = 0;
+    // Keep the 16-bit kernels' 256 x 256 direct-to-LDS tile where the dispatcher would
+    // take the 192 x 256 one (a measurement-only variant sets it).
+    int square_tiles = 0;
     // The MFMA kernels have plain variants (store the accumulators as they are) and
     // variants that store sign * acc (+ C); the latter serve negated products too.
     bool signed_or_acc() const { return accumulate || sign < 0.0f; }

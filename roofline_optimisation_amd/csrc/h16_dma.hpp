@@ -39,7 +39,7 @@
 // The tile routine is written over a general geometry (an EM x EN tile, WM x WN compute
 // waves, NS ring stages, PW producer waves) so that other schedules of the same data
 // movement can be built and measured against the dispatched one: the dispatched kernels
-// are EM = EN = 256 or 128 on 2 x 2 waves that all load; mfma_f16_dma_sched_kernel
+// are EM = EN = 256 or 128 and EM x EN = 192 x 256, on 2 x 2 waves that all load; mfma_f16_dma_sched_kernel
 // instantiates the others (wave specialisation with producer waves, eight waves, 256 x
 // 128 tiles).
 #pragma once
@@ -613,6 +613,24 @@ void mfma_f16_dma_kernel(int M, int N, int K, const uint16_t *__restrict__ A, in
     grouped_tile(xcd_contiguous_id(blockIdx.x, gridDim.x), cdiv(M, E), cdiv(N, E), 4, tm, tn);
     dma::dma_tile<T, A_MN, B_MN, EPI, E, E, 2, 2, kNs, 0, false, KR>(M, N, K, A, lda, B, ldb, C, ldc, sign,
                                                                       flags, tm * E, tn * E, lds);
+}
+
+// 192 x 256 tiles: the k-contiguous A's 192 rows by B's 256 columns, for plain products
+// whose 256 x 256 grid leaves CUs idle where a 192-row grid fills them (3072^2: 192 tiles
+// instead of 144).  The same tile routine on four waves of 96 x 128, one workgroup per CU
+// (112 KiB of LDS); B may be n- or k-contiguous.
+// KR: K not a whole number of ring trips (the last trip's chunks past K load as zeros).
+template <typename T, bool B_MN, bool KR = false>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1)))
+void mfma_f16_dma_rect_kernel(int M, int N, int K, const uint16_t *__restrict__ A, int lda,
+                              const uint16_t *__restrict__ B, int ldb, float *__restrict__ C,
+                              int ldc) {
+    constexpr int kEM = 192, kEN = 256, kNs = dma::ring_stages(kEN);
+    __shared__ __attribute__((aligned(1024))) char lds[dma::Geo<kEM, kEN, 2, 2, kNs, 0>::kLds];
+    int tm, tn;
+    grouped_tile(xcd_contiguous_id(blockIdx.x, gridDim.x), cdiv(M, kEM), cdiv(N, kEN), 4, tm, tn);
+    dma::dma_tile<T, false, B_MN, 0, kEM, kEN, 2, 2, kNs, 0, false, KR>(M, N, K, A, lda, B, ldb, C, ldc,
+                                                                        1.0f, 0, tm * kEM, tn * kEN, lds);
 }
 
 // Schedules of the same data movement that are kept for measurement (gemm355_run_variant

@@ -526,6 +526,28 @@ inline bool use_dma(const GemmArgs &g, int tile) {
            op_fits(g.trans_b == 0, tile, kpad, g.ldb);
 }
 
+// The 192 x 256 direct-load tile (plain products with A k-contiguous) on the same terms as
+// the 256 x 256 one: rows 16-byte aligned, K a multiple of 8 and at least one ring trip,
+// every byte offset within 31 bits, and with B n-contiguous N a multiple of 8.
+inline bool use_dma_rect(const GemmArgs &g) {
+    if (g.trans_a || (!g.trans_b && g.N % 8 != 0)) return false;
+    const int trip = dma::kBK * dma::ring_stages(256);
+    const int kpad = cdiv(g.K, trip) * trip;
+    return h16_vec(g) && g.K >= trip && g.K % 8 == 0 && g.M >= 192 && g.N >= 256 &&
+           op_fits(false, 192, kpad, g.lda) && op_fits(g.trans_b == 0, 256, kpad, g.ldb);
+}
+
+// Whether a product headed for 256 x 256 tiles runs faster on 192 x 256 ones: rounds of
+// resident tiles (one per CU) times tile area, the smaller tile at 0.87 of the larger
+// one's rate per unit of work (FP16 3072^3: 51.2 against 59.1 us, 192 against 144 tiles;
+// 6144 x 6144 x 4096: 236.7 against 269.8 us).
+inline bool prefer_rect(const GemmArgs &g) {
+    if (g.square_tiles) return false;
+    const long t256 = (long)cdiv(g.M, 256) * cdiv(g.N, 256);
+    const long t192 = (long)cdiv(g.M, 192) * cdiv(g.N, 256);
+    return (double)((t192 + 255) / 256) * (192 * 256) / 0.87 < (double)((t256 + 255) / 256) * (256 * 256);
+}
+
 // K is not a whole number of the direct-load kernel's ring trips.
 inline bool dma_ragged_k(const GemmArgs &g, int tile) {
     return g.K % (dma::kBK * dma::ring_stages(tile)) != 0;
@@ -709,9 +731,25 @@ inline bool use_64x64(const GemmArgs &g) {
     return (long)cdiv(g.M, 128) * cdiv(g.N, 64) < 256;
 }
 
+template <typename T, bool B_MN>
+hipError_t launch_rect(const GemmArgs &g, hipStream_t s) {
+    const dim3 grid(cdiv(g.M, 192) * cdiv(g.N, 256));
+    if (dma_ragged_k(g, 256))
+        hipLaunchKernelGGL((mfma_f16_dma_rect_kernel<T, B_MN, true>), grid, dim3(256), 0, s, g.M, g.N, g.K,
+                           (const uint16_t *)g.A, g.lda, (const uint16_t *)g.B, g.ldb, g.C, g.ldc);
+    else
+        hipLaunchKernelGGL((mfma_f16_dma_rect_kernel<T, B_MN>), grid, dim3(256), 0, s, g.M, g.N, g.K,
+                           (const uint16_t *)g.A, g.lda, (const uint16_t *)g.B, g.ldb, g.C, g.ldc);
+    return hipGetLastError();
+}
+
 template <typename T, bool A_MN, bool B_MN, int EPI>
 hipError_t launch_layout(const GemmArgs &g, hipStream_t s) {
-    if (pick_tile(g) == 256) return launch_cfg<T, 256, 256, 2, 2, 1, A_MN, B_MN, EPI>(g, s);
+    if (pick_tile(g) == 256) {
+        if constexpr (!A_MN && EPI == 0)
+            if (use_dma_rect(g) && prefer_rect(g)) return launch_rect<T, B_MN>(g, s);
+        return launch_cfg<T, 256, 256, 2, 2, 1, A_MN, B_MN, EPI>(g, s);
+    }
     if constexpr (!A_MN && EPI == 0) {
         if (use_64x64(g)) return launch_cfg<T, 64, 64, 1, 2, 4, A_MN, B_MN, EPI>(g, s);
         if (use_128x64(g)) return launch_cfg<T, 128, 64, 2, 2, 2, A_MN, B_MN, EPI>(g, s);

@@ -29,8 +29,13 @@ const char *desc_mfma_f16(int dtype, const GemmArgs &g) {
     const bool small = plain_km && use_64x64(g);
     const bool narrow = plain_km && !small && use_128x64(g);
     const int bm = big ? 256 : (small ? 64 : 128), bn = big ? 256 : (small || narrow ? 64 : 128);
-    const H16Plan p = plan_cfg(bm, bn, g.trans_a != 0, g.trans_b == 0, epi, g);
     out = name;
+    if (big && !g.trans_a && epi == 0 && use_dma_rect(g) && prefer_rect(g)) {
+        out += " 192x256x32 w2x2 lds-dma";
+        if (dma_ragged_k(g, 256)) out += " k-zero-fill";
+        return out.c_str();
+    }
+    const H16Plan p = plan_cfg(bm, bn, g.trans_a != 0, g.trans_b == 0, epi, g);
     if (p.dma) {
         out += big ? " 256x256x32 w2x2 lds-dma" : " 128x128x32 w2x2 lds-dma";
         if (dma_ragged_k(g, bm)) out += " k-zero-fill";

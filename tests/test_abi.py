@@ -46,7 +46,7 @@ def test_version_and_strings(lib):
     assert gb.gemm355_status_string(0) == "ok"
     assert gb.gemm355_status_string(1) == "invalid argument"
     assert gb.gemm355_status_string(99) == "unknown"
-    assert [gb.gemm355_variant_name(v) for v in (-1, 0, 1, 2, 3, 7)] == \
+    assert [gb.gemm355_variant_name(v) for v in (-1, 0, 1, 2, 3, 8)] == \
         ["auto", "naive", "lds_tiled", "regblock", "mfma", "unknown"]
 
 
@@ -76,7 +76,7 @@ def test_invalid_arguments_rejected_on_host(lib, args):
 
 def test_unknown_variant_and_dtype(lib):
     args = (4, 4, 4, P, 4, P, 4, P, 4, 0)
-    assert gb.gemm355_run_variant(7, 0, *args) == gb.ERR_INVALID_ARG
+    assert gb.gemm355_run_variant(8, 0, *args) == gb.ERR_INVALID_ARG
     assert gb.gemm355_run_variant(-2, 0, *args) == gb.ERR_INVALID_ARG
     assert gb.gemm355_run_variant(0, 3, *args) == gb.ERR_INVALID_ARG
     # FP32-only families reject 16-bit operands before touching the device
@@ -110,7 +110,16 @@ def test_dispatch_choices(lib):
     assert d(-1, 1, 2048, 2048, 2176, P, 2176, P, 2048, P, 2048) == "mfma_f16 128x128x32 w2x2 lds-dma k-zero-fill"
     assert d(-1, 2, 2560, 2560, 2560, P, 2560, P, 2560, P, 2560) == "mfma_bf16 128x128x64 w2x2 dwordx4 | interior=buffer,paired"
     assert d(-1, 1, 4000, 4000, 4096, P, 4096, P, 4000, P, 4000) == "mfma_f16 256x256x32 w2x2 lds-dma"
-    assert d(-1, 1, 4096, 4104, 4096, P, 4096, P, 4104, P, 4104) == "mfma_f16 256x256x32 w2x2 lds-dma"
+    # 192 x 256 tiles where the 256 x 256 grid would take more 256-CU rounds of work per
+    # CU: 3072^2 (144 tiles against 192), 4096 x 4104 (272 tiles, two rounds, against 374),
+    # 4608^2; not at 4096^2 or 8192^2, whose 256 x 256 tiles fill whole rounds, nor for the
+    # transposed A or the other epilogues
+    assert d(-1, 1, 4096, 4104, 4096, P, 4096, P, 4104, P, 4104) == "mfma_f16 192x256x32 w2x2 lds-dma"
+    assert d(-1, 1, 3072, 3072, 3072, P, 3072, P, 3072, P, 3072) == "mfma_f16 192x256x32 w2x2 lds-dma"
+    assert d(-1, 2, 3072, 3072, 1000, P, 1000, P, 3072, P, 3072) == "mfma_bf16 192x256x32 w2x2 lds-dma k-zero-fill"
+    assert d(-1, 1, 4608, 4608, 4608, P, 4608, P, 4608, P, 4608) == "mfma_f16 192x256x32 w2x2 lds-dma"
+    assert d(-1, 2, 8192, 8192, 8192, P, 8192, P, 8192, P, 8192) == "mfma_bf16 256x256x32 w2x2 lds-dma"
+    assert d(-1, 1, 5120, 5120, 5120, P, 5120, P, 5120, P, 5120) == "mfma_f16 256x256x32 w2x2 lds-dma"
     assert d(-1, 2, 4096, 4096, 4000, P, 4000, P, 4096, P, 4096) == "mfma_bf16 256x256x32 w2x2 lds-dma k-zero-fill"
     assert d(-1, 2, 4096, 4096, 4001, P, 4008, P, 4096, P, 4096) == "mfma_bf16 256x256x64 w2x2 dwordx4 | edges=clamped"
     assert d(-1, 1, 4096, 4096, 120, P, 120, P, 4096, P, 4096).startswith("mfma_f16 256x256x64 w2x2 dwordx4")
@@ -151,6 +160,14 @@ def test_dispatch_choices_general_form(lib):
     # with K a multiple of 8 the direct-to-LDS kernel zero-fills past K in every layout
     assert dx(-1, 1, gb.TRANS_A | gb.TRANS_B, 1000, 1000, 1000, P, 1000, P, 1000, P, 1000) == \
         "mfma_f16 128x128x32 w2x2 lds-dma k-zero-fill"
+    # the 192 x 256 tile takes B in either layout; a transposed A and the signed or
+    # accumulating epilogues keep the 256 x 256 tile
+    assert dx(-1, 1, gb.TRANS_B, 3072, 3072, 3072, P, 3072, P, 3072, P, 3072) == \
+        "mfma_f16 192x256x32 w2x2 lds-dma"
+    assert dx(-1, 1, gb.TRANS_A, 3072, 3072, 3072, P, 3072, P, 3072, P, 3072) == \
+        "mfma_f16 256x256x32 w2x2 lds-dma"
+    assert dx(-1, 2, gb.NEG_A, 3072, 3072, 3072, P, 3072, P, 3072, P, 3072) == \
+        "mfma_bf16 256x256x32 w2x2 lds-dma"
     # what gemm355_gemm_ex rejects
     assert dx(-1, 0, gb.C_16, 8, 8, 8, P, 8, P, 8, P, 8) == "invalid"
     assert dx(-1, 1, 64, 8, 8, 8, P, 8, P, 8, P, 8) == "invalid"
@@ -188,7 +205,7 @@ def test_gemm_ex_argument_checks(lib):
     assert E(0, 0, 0, 8, 6, 4, P, 3, P, 6, P, 6) == gb.ERR_INVALID_ARG           # lda < K
     assert E(0, 0, 0, 8, 6, 4, P, 4, P, 6, P, 5) == gb.ERR_INVALID_ARG           # ldc < N
     assert E(0, 3, 0, 8, 6, 4, P, 4, P, 6, P, 6) == gb.ERR_INVALID_ARG           # dtype
-    assert E(7, 0, 0, 8, 6, 4, P, 4, P, 6, P, 6) == gb.ERR_INVALID_ARG           # variant
+    assert E(8, 0, 0, 8, 6, 4, P, 4, P, 6, P, 6) == gb.ERR_INVALID_ARG           # variant
     assert E(0, 0, 0, 8, 6, 4, 0, 4, P, 6, P, 6) == gb.ERR_INVALID_ARG           # null A
     # with a flag only the naive and MFMA families exist
     for v in (gb.VARIANT_LDS_TILED, gb.VARIANT_REGBLOCK):
@@ -280,4 +297,25 @@ def test_schedule_variants_contract(lib):
     assert d(gb.VARIANT_MFMA_SPLIT, gb.F16, 512, 384, 128, P, 128, P, 384, P, 384) == \
         "mfma_f16 256x128x32 w2x2 + 4 producer waves lds-dma"
     assert d(gb.VARIANT_MFMA_W8, gb.F16, 512, 384, 128, P, 128, P, 384, P, 384) == "invalid"  # N % 256
-    assert gb.gemm355_run_variant(7, gb.F16, 8, 8, 8, P, 8, P, 8, P, 8, 0) == gb.ERR_INVALID_ARG
+    assert gb.gemm355_run_variant(8, gb.F16, 8, 8, 8, P, 8, P, 8, P, 8, 0) == gb.ERR_INVALID_ARG
+
+
+def test_square_tile_variant_contract(lib):
+    """MFMA_T256X256 is the dispatcher with the 192 x 256 tile turned off: every plain F16 /
+    BF16 product, as dispatched except that 256 x 256 replaces 192 x 256."""
+    d = gb.gemm355_kernel_desc
+    v = gb.VARIANT_MFMA_T256X256
+    assert gb.gemm355_variant_name(v) == "mfma_t256x256"
+    assert d(-1, gb.F16, 3072, 3072, 3072, P, 3072, P, 3072, P, 3072) == "mfma_f16 192x256x32 w2x2 lds-dma"
+    assert d(v, gb.F16, 3072, 3072, 3072, P, 3072, P, 3072, P, 3072) == "mfma_f16 256x256x32 w2x2 lds-dma"
+    assert d(v, gb.BF16, 3072, 3072, 1000, P, 1000, P, 3072, P, 3072) == \
+        "mfma_bf16 256x256x32 w2x2 lds-dma k-zero-fill"
+    for shape in ((4096, 4096, 4096), (2048, 2048, 2048), (1000, 1000, 1004), (300, 260, 130)):
+        M, N, K = shape
+        for dt in (gb.F16, gb.BF16):
+            assert d(v, dt, M, N, K, P, K, P, N, P, N) == d(-1, dt, M, N, K, P, K, P, N, P, N)
+    assert d(v, gb.F32, 3072, 3072, 3072, P, 3072, P, 3072, P, 3072) == "invalid"
+    assert gb.gemm355_run_variant(v, gb.F32, 256, 256, 128, P, 128, P, 256, P, 256, 0) == gb.ERR_UNSUPPORTED
+    assert gb.gemm355_gemm_ex(v, gb.F16, gb.TRANS_B, 256, 256, 128, P, 128, P, 128, P, 256, 0) == \
+        gb.ERR_UNSUPPORTED
+    assert gb.gemm355_kernel_desc_ex(v, gb.F16, gb.TRANS_B, 256, 256, 128, P, 128, P, 128, P, 256) == "invalid"

@@ -124,6 +124,9 @@ SHAPES = {"f32": [(3072, 3072, 64), (1024, 768, 96), (2048, 2048, 64), (1536, 15
 # (3072, 2816, 192) and (2048, 2048, 264): K not a whole number of ring trips on the
 # direct-to-LDS kernel (256 x 256 and 128 x 128 tiles; the last trip's steps past K are
 # skipped: 2 of 4 and 7 of 8).
+# (3072, 3072, 128), (3072, 2816, 192) and BF16 (3072, 3072, 256), plain and with B
+# transposed (no negation, no accumulation): the 192 x 256 direct-to-LDS tile, the second
+# with K not a whole number of ring trips; the other layouts and modes take 256 x 256.
 # (4000, 3992, 128) and (2000, 2040, 256): every tile, ragged ones included, on the
 # direct-to-LDS kernel (256 x 256 and 128 x 128 tiles); the padding around the operands
 # holds NaN, so a ragged tile's loads past the matrix would show in its stored outputs.

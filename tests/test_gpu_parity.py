@@ -474,6 +474,36 @@ def test_h16_tile_classes(case):
     C64, _ = oracle.gemm(np.ascontiguousarray(A[rows]), B, dtype)
     check(C[rows], C64, dtype, "uniform", K, ok, f"{dtype} tile class {tile} {M}x{N}x{K}")
 
+# The 192 x 256 direct-to-LDS tile (plain products whose 256 x 256 grid would leave CUs
+# idle: 3072^2 takes 192 tiles instead of 144): whole tiles, ragged M (3000 = 15 x 192 +
+# 120) and ragged N (3000 = 11 x 256 + 184) with NaN-padded strides, K not a whole number
+# of ring trips, and three rounds of tiles.
+RECT_CASES = [("f16", (3072, 3072, 3072), (0, 0, 0), "full", "192x256x32 w2x2 lds-dma"),
+              ("bf16", (3000, 3072, 1024), (8, 8, 8), "full", "192x256x32 w2x2 lds-dma"),
+              ("f16", (3072, 3000, 512), (8, 8, 0), "full", "192x256x32 w2x2 lds-dma"),
+              ("f16", (3072, 3072, 1000), (8, 0, 0), "rows", "192x256x32 w2x2 lds-dma k-zero-fill"),
+              ("bf16", (6144, 6144, 512), (0, 0, 0), "rows", "192x256x32 w2x2 lds-dma")]
+
+
+@pytest.mark.parametrize("case", RECT_CASES, ids=lambda c: c[0] + "_" + "x".join(map(str, c[1])) + f"_pad{c[2][0]}")
+def test_dma_rect_tile(case):
+    dtype, (M, N, K), pad, cmp, kernel = case
+    P = 1 << 20  # a 16-byte-aligned address: the query only inspects it
+    desc = gb.gemm355_kernel_desc(gb.VARIANT_AUTO, gb.DTYPE_CODES[dtype], M, N, K, P, K + pad[0],
+                                  P, N + pad[1], P, N + pad[2])
+    assert desc.endswith(kernel), desc
+    A, B = inputs.make_operands(M, N, K, 83, "uniform", dtype)
+    C, ok = gpu_gemm(A, B, dtype, entry="typed", pad=pad, guard_rows=1)
+    rows = np.arange(M) if cmp == "full" else np.array(sorted(
+        set(sample_rows(M, 48).tolist()) | {191, 192, M - 1}))
+    C64, _ = oracle.gemm(np.ascontiguousarray(A[rows]), B, dtype)
+    check(C[rows], C64, dtype, "uniform", K, ok, f"192x256 dma {dtype} {M}x{N}x{K} pad={pad}")
+    Ai, Bi = inputs.make_operands(M, N, K, 84, "int", dtype)
+    _, C32 = oracle.gemm(np.ascontiguousarray(Ai[rows]), Bi, dtype)
+    Ci, ok = gpu_gemm(Ai, Bi, dtype, entry="typed", pad=pad)
+    assert ok and np.array_equal(Ci[rows], C32), f"192x256 dma {dtype} {M}x{N}x{K} integers not bit-exact"
+
+
 # The direct-to-LDS kernel with K not a whole number of its ring trips (128 for 256-wide
 # tiles, 256 for 128-wide ones): the loop runs to the next trip and every 16-byte chunk at
 # k >= K loads as zeros.  K = 4000, 4064 (ragged by whole 32-wide k-steps), 4072 (a

@@ -87,3 +87,30 @@ def test_sched_run_twice_bitwise(variant):
     C1, _ = gpu_gemm(A, B, "f16", variant)
     C2, _ = gpu_gemm(A, B, "f16", variant)
     assert np.array_equal(C1.view(np.uint32), C2.view(np.uint32))
+
+
+# VARIANT_MFMA_T256X256 (the dispatcher without the 192 x 256 tile) at shapes where the
+# dispatcher takes 192 x 256: the same result bit for bit as the dispatched call (both
+# tiles add each element's products in the same order), and within the bars of the
+# oracle on sampled rows; ragged M and N, K not a whole number of ring trips, padded
+# strides.
+SQUARE_CASES = [("f16", (3072, 3072, 3072), (0, 0, 0)), ("bf16", (3000, 3072, 1000), (8, 8, 8)),
+                ("f16", (4096, 4104, 512), (0, 8, 0))]
+
+
+@pytest.mark.parametrize("case", SQUARE_CASES, ids=lambda c: c[0] + "_" + "x".join(map(str, c[1])))
+def test_square_tile_variant_matches_dispatched(case):
+    dtype, (M, N, K), pad = case
+    code = gb.DTYPE_CODES[dtype]
+    v = gb.VARIANT_MFMA_T256X256
+    args = (M, N, K, P, K + pad[0], P, N + pad[1], P, N + pad[2])
+    assert gb.gemm355_kernel_desc(gb.VARIANT_AUTO, code, *args).startswith(f"mfma_{dtype} 192x256x32")
+    assert gb.gemm355_kernel_desc(v, code, *args).startswith(f"mfma_{dtype} 256x256x32")
+    A, B = inputs.make_operands(M, N, K, 75, "uniform", dtype)
+    Cs, ok_s = gpu_gemm(A, B, dtype, v, pad=pad, guard_rows=1)
+    Cd, ok_d = gpu_gemm(A, B, dtype, gb.VARIANT_AUTO, pad=pad, guard_rows=1)
+    assert ok_s and ok_d, "wrote outside C"
+    assert np.array_equal(Cs.view(np.uint32), Cd.view(np.uint32)), "256 x 256 and 192 x 256 tiles differ"
+    rows = np.array(sorted(set(sample_rows(M, 24).tolist()) | {191, 192, 255, 256, M - 1}))
+    C64, _ = oracle.gemm(np.ascontiguousarray(A[rows]), B, dtype)
+    check(Cs[rows], C64, dtype, K, ok_s, f"t256x256 {dtype} {M}x{N}x{K} pad={pad}")
