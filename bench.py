@@ -396,19 +396,21 @@ def schedule_lines(warm=300, rounds=3, reps=100):
     return out
 
 
-# Shapes where the dispatcher takes the 192 x 256 direct-to-LDS tile, each with the
-# 256 x 256 tile timed beside it (dtype, M, N, K).
-TILE_SHAPES = [("f16", 3072, 3072, 3072), ("bf16", 3072, 3072, 3072), ("f16", 3072, 4096, 4096),
-               ("f16", 4096, 4104, 4096), ("f16", 4608, 4608, 4608), ("f16", 6144, 6144, 4096),
-               ("f16", 3000, 3072, 1024), ("bf16", 3072, 3072, 1000)]
+# Calls for which the dispatcher takes the 192 x 256 direct-to-LDS tile, each with the
+# 256 x 256 tile timed beside it: (dtype, M, N, K, gemm355_gemm_ex flags).
+TILE_SHAPES = [("f16", 3072, 3072, 3072, ()), ("bf16", 3072, 3072, 3072, ()), ("f16", 3072, 4096, 4096, ()),
+               ("f16", 4096, 4104, 4096, ()), ("f16", 4608, 4608, 4608, ()), ("f16", 6144, 6144, 4096, ()),
+               ("f16", 3000, 3072, 1024, ()), ("bf16", 3072, 3072, 1000, ()),
+               ("f16", 3072, 3072, 3072, ("TRANS_B",)), ("f16", 3072, 3072, 3072, ("NEG_A", "ACCUMULATE")),
+               ("bf16", 3072, 3072, 3072, ("C_16",))]
 
 
 def tile_lines(warm=300, rounds=5, reps=100):
-    """The 192 x 256 tile against the 256 x 256 one (gemm355_run_variant MFMA_T256X256) on
-    the shapes the dispatcher gives it: U[-1,1] operands (seed 3), packed strides; both
-    cases warmed, then timed interleaved, median of `rounds` rounds of `reps` launches
-    (HIP events on one stream).  Rounds: ceil(tiles / 256), the waves of one-tile-per-CU
-    work each grid takes."""
+    """The 192 x 256 tile against the 256 x 256 one (variant MFMA_T256X256) on calls the
+    dispatcher gives it, through gemm355_gemm_ex: U[-1,1] operands (seed 3; with TRANS_B
+    the K x N draw is stored transposed), packed strides; both cases warmed, then timed
+    interleaved, median of `rounds` rounds of `reps` launches (HIP events on one stream).
+    Rounds: ceil(tiles / 256), the waves of one-tile-per-CU work each grid takes."""
     import torch
 
     from roofline_optimisation_amd import binding as gb
@@ -417,27 +419,35 @@ def tile_lines(warm=300, rounds=5, reps=100):
     cdiv = lambda a, b: -(-a // b)
     stream = torch.cuda.Stream()
     out = ["# 192 x 256 against 256 x 256 direct-to-LDS tiles on one MI355X", "",
-           f"U[-1,1] operands (seed 3), packed strides, FP32 C; {warm} warm-up launches per case, then "
+           f"U[-1,1] operands (seed 3), packed strides, FP32 C (16-bit with C_16; C += with ACCUMULATE); "
+           f"{warm} warm-up launches per case, then "
            f"both cases interleaved, median of {rounds} rounds of {reps} launches; HIP events.  "
            "Rounds = ceil(tiles / 256 CUs).", "",
-           "| dtype | M x N x K | 256x256 tiles (rounds) | 192x256 tiles (rounds) | 256x256 µs | "
+           "| dtype | M x N x K | flags | 256x256 tiles (rounds) | 192x256 tiles (rounds) | 256x256 µs | "
            "dispatched µs | speedup | TFLOP/s | % of peak | dispatched kernel |",
-           "|---|---|---|---|---|---|---|---|---|---|"]
-    for dt, M, N, K in TILE_SHAPES:
+           "|---|---|---|---|---|---|---|---|---|---|---|"]
+    for dt, M, N, K, fl in TILE_SHAPES:
+        flags = 0
+        for f in fl:
+            flags |= getattr(gb, f)
         A, B = inputs.make_operands(M, N, K, 3, "uniform", dt)
+        if "TRANS_B" in fl:
+            B = np.ascontiguousarray(B.T)
         dA = torch.from_numpy(A.view("int16")).cuda()
         dB = torch.from_numpy(B.view("int16")).cuda()
-        dC = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        # an accumulated C grows by one product's worth per launch; well inside FP32's range
+        dC = torch.zeros((M, N), dtype=torch.float32, device="cuda")
+        ldb = B.shape[1]
         runs = []
         for v in (gb.VARIANT_MFMA_T256X256, gb.VARIANT_AUTO):
-            args = (v, gb.DTYPE_CODES[dt], M, N, K, dA.data_ptr(), K, dB.data_ptr(), N,
+            args = (v, gb.DTYPE_CODES[dt], flags, M, N, K, dA.data_ptr(), K, dB.data_ptr(), ldb,
                     dC.data_ptr(), N, stream.cuda_stream)
 
             def go(args=args):
-                st = gb.gemm355_run_variant(*args)
+                st = gb.gemm355_gemm_ex(*args)
                 if st != gb.OK:
-                    raise gb.Gemm355Error(st, "gemm355_run_variant")
-            runs.append((v, gb.gemm355_kernel_desc(*args[:-1]), go))
+                    raise gb.Gemm355Error(st, "gemm355_gemm_ex")
+            runs.append((v, gb.gemm355_kernel_desc_ex(*args[:-1]), go))
         for _, _, go in runs:
             for _ in range(warm):
                 go()
@@ -456,10 +466,13 @@ def tile_lines(warm=300, rounds=5, reps=100):
         t256 = cdiv(M, 256) * cdiv(N, 256)
         t192 = cdiv(M, 192) * cdiv(N, 256)
         tf = 2.0 * M * N * K / dis / 1e6
-        out.append(f"| {dt} | {M}x{N}x{K} | {t256} ({cdiv(t256, 256)}) | {t192} ({cdiv(t192, 256)}) | "
+        fl_text = " \\| ".join(fl) or "plain"
+        out.append(f"| {dt} | {M}x{N}x{K} | {fl_text} | {t256} ({cdiv(t256, 256)}) | "
+                   f"{t192} ({cdiv(t192, 256)}) | "
                    f"{sq:.2f} | {dis:.2f} | {sq / dis:.3f}x | {tf:.0f} | {100 * tf / PEAKS[dt]:.1f} | "
                    f"`{md_cell(runs[1][1])}` |")
-        log(f"[tiles] {dt} {M}x{N}x{K}: 256x256 {sq:.2f} us, dispatched {dis:.2f} us ({sq / dis:.3f}x)")
+        log(f"[tiles] {dt} {M}x{N}x{K} {'|'.join(fl) or 'plain'}: 256x256 {sq:.2f} us, "
+            f"dispatched {dis:.2f} us ({sq / dis:.3f}x)")
         del dA, dB, dC
     return out
 

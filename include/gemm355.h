@@ -86,7 +86,7 @@ typedef enum gemm355_variant {
      * gemm355_gemm_ex flag or a shape the kernel does not take returns
      * GEMM355_ERR_UNSUPPORTED).  Shapes taken: whole tiles (M a multiple of 256, N of
      * the tile width), 16-byte-aligned rows, K a multiple of 128 (MFMA_T256X256: any
-     * plain product).
+     * shape and gemm355_gemm_ex flags).
      * MFMA_SPLIT: wave specialisation ("Advanced CUDA features - starting from GEMM",
      *   scheduling section, the warp-specialisation path): 256 x 128 tiles, four producer
      *   waves issue every global -> LDS load while four compute waves (128 x 64 of C
@@ -99,8 +99,9 @@ typedef enum gemm355_variant {
      *   stores drain.
      * MFMA_T256X256: the dispatched kernels with the 192 x 256 direct-to-LDS tile turned
      *   off: the 256 x 256 tile wherever the dispatcher would take 192 x 256, every other
-     *   shape as dispatched (plain products of any shape; the same results bit for bit,
-     *   since both tiles sum each element's K products in the same order). */
+     *   call as dispatched (any F16 / BF16 product the dispatcher takes, gemm355_gemm_ex
+     *   flags included; the same results bit for bit, since both tiles sum each
+     *   element's K products in the same order). */
     GEMM355_VARIANT_MFMA_SPLIT = 4,
     GEMM355_VARIANT_MFMA_W8 = 5,
     GEMM355_VARIANT_MFMA_T256X128 = 6,

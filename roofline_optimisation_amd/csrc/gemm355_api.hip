@@ -139,7 +139,8 @@ gemm355_status ex_args(int &variant, int dtype, unsigned flags, int M, int N, in
     g.accumulate = acc;
     if (variant == GEMM355_VARIANT_AUTO) variant = auto_variant(dtype, g);
     if (!variant_supported(variant, dtype)) return GEMM355_ERR_UNSUPPORTED;
-    if (flags != 0 && variant != GEMM355_VARIANT_NAIVE && variant != GEMM355_VARIANT_MFMA)
+    if (flags != 0 && variant != GEMM355_VARIANT_NAIVE && variant != GEMM355_VARIANT_MFMA &&
+        variant != GEMM355_VARIANT_MFMA_T256X256)
         return GEMM355_ERR_UNSUPPORTED;
     if (is_sched_variant(variant) && M > 0 && N > 0 && !mfma_f16_sched_ok(variant, g))
         return GEMM355_ERR_UNSUPPORTED;

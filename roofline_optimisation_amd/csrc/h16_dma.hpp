@@ -615,22 +615,24 @@ void mfma_f16_dma_kernel(int M, int N, int K, const uint16_t *__restrict__ A, in
                                                                       flags, tm * E, tn * E, lds);
 }
 
-// 192 x 256 tiles: the k-contiguous A's 192 rows by B's 256 columns, for plain products
-// whose 256 x 256 grid leaves CUs idle where a 192-row grid fills them (3072^2: 192 tiles
+// 192 x 256 tiles: the k-contiguous A's 192 rows by B's 256 columns, for products whose
+// 256 x 256 grid leaves CUs idle where a 192-row grid fills them (3072^2: 192 tiles
 // instead of 144).  The same tile routine on four waves of 96 x 128, one workgroup per CU
-// (112 KiB of LDS); B may be n- or k-contiguous.
+// (112 KiB of LDS); B may be n- or k-contiguous, and every epilogue kind is taken.  (An
+// m-contiguous A would need 192-element LDS rows, 24 chunks, which the ring's XOR swizzle
+// of chunk slots does not map onto themselves.)
 // KR: K not a whole number of ring trips (the last trip's chunks past K load as zeros).
-template <typename T, bool B_MN, bool KR = false>
+template <typename T, bool B_MN, int EPI, bool KR = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1)))
 void mfma_f16_dma_rect_kernel(int M, int N, int K, const uint16_t *__restrict__ A, int lda,
                               const uint16_t *__restrict__ B, int ldb, float *__restrict__ C,
-                              int ldc) {
+                              int ldc, float sign, int flags) {
     constexpr int kEM = 192, kEN = 256, kNs = dma::ring_stages(kEN);
     __shared__ __attribute__((aligned(1024))) char lds[dma::Geo<kEM, kEN, 2, 2, kNs, 0>::kLds];
     int tm, tn;
     grouped_tile(xcd_contiguous_id(blockIdx.x, gridDim.x), cdiv(M, kEM), cdiv(N, kEN), 4, tm, tn);
-    dma::dma_tile<T, false, B_MN, 0, kEM, kEN, 2, 2, kNs, 0, false, KR>(M, N, K, A, lda, B, ldb, C, ldc,
-                                                                        1.0f, 0, tm * kEM, tn * kEN, lds);
+    dma::dma_tile<T, false, B_MN, EPI, kEM, kEN, 2, 2, kNs, 0, false, KR>(M, N, K, A, lda, B, ldb, C, ldc,
+                                                                          sign, flags, tm * kEM, tn * kEN, lds);
 }
 
 // Schedules of the same data movement that are kept for measurement (gemm355_run_variant

@@ -526,7 +526,7 @@ inline bool use_dma(const GemmArgs &g, int tile) {
            op_fits(g.trans_b == 0, tile, kpad, g.ldb);
 }
 
-// The 192 x 256 direct-load tile (plain products with A k-contiguous) on the same terms as
+// The 192 x 256 direct-load tile (A k-contiguous, any epilogue) on the same terms as
 // the 256 x 256 one: rows 16-byte aligned, K a multiple of 8 and at least one ring trip,
 // every byte offset within 31 bits, and with B n-contiguous N a multiple of 8.
 inline bool use_dma_rect(const GemmArgs &g) {
@@ -731,23 +731,25 @@ inline bool use_64x64(const GemmArgs &g) {
     return (long)cdiv(g.M, 128) * cdiv(g.N, 64) < 256;
 }
 
-template <typename T, bool B_MN>
+template <typename T, bool B_MN, int EPI>
 hipError_t launch_rect(const GemmArgs &g, hipStream_t s) {
     const dim3 grid(cdiv(g.M, 192) * cdiv(g.N, 256));
     if (dma_ragged_k(g, 256))
-        hipLaunchKernelGGL((mfma_f16_dma_rect_kernel<T, B_MN, true>), grid, dim3(256), 0, s, g.M, g.N, g.K,
-                           (const uint16_t *)g.A, g.lda, (const uint16_t *)g.B, g.ldb, g.C, g.ldc);
+        hipLaunchKernelGGL((mfma_f16_dma_rect_kernel<T, B_MN, EPI, true>), grid, dim3(256), 0, s, g.M, g.N,
+                           g.K, (const uint16_t *)g.A, g.lda, (const uint16_t *)g.B, g.ldb, g.C, g.ldc,
+                           g.sign, epi_flags<EPI>(g));
     else
-        hipLaunchKernelGGL((mfma_f16_dma_rect_kernel<T, B_MN>), grid, dim3(256), 0, s, g.M, g.N, g.K,
-                           (const uint16_t *)g.A, g.lda, (const uint16_t *)g.B, g.ldb, g.C, g.ldc);
+        hipLaunchKernelGGL((mfma_f16_dma_rect_kernel<T, B_MN, EPI>), grid, dim3(256), 0, s, g.M, g.N, g.K,
+                           (const uint16_t *)g.A, g.lda, (const uint16_t *)g.B, g.ldb, g.C, g.ldc, g.sign,
+                           epi_flags<EPI>(g));
     return hipGetLastError();
 }
 
 template <typename T, bool A_MN, bool B_MN, int EPI>
 hipError_t launch_layout(const GemmArgs &g, hipStream_t s) {
     if (pick_tile(g) == 256) {
-        if constexpr (!A_MN && EPI == 0)
-            if (use_dma_rect(g) && prefer_rect(g)) return launch_rect<T, B_MN>(g, s);
+        if constexpr (!A_MN)
+            if (use_dma_rect(g) && prefer_rect(g)) return launch_rect<T, B_MN, EPI>(g, s);
         return launch_cfg<T, 256, 256, 2, 2, 1, A_MN, B_MN, EPI>(g, s);
     }
     if constexpr (!A_MN && EPI == 0) {

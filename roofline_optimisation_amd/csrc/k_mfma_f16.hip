@@ -30,7 +30,7 @@ const char *desc_mfma_f16(int dtype, const GemmArgs &g) {
     const bool narrow = plain_km && !small && use_128x64(g);
     const int bm = big ? 256 : (small ? 64 : 128), bn = big ? 256 : (small || narrow ? 64 : 128);
     out = name;
-    if (big && !g.trans_a && epi == 0 && use_dma_rect(g) && prefer_rect(g)) {
+    if (big && !g.trans_a && use_dma_rect(g) && prefer_rect(g)) {
         out += " 192x256x32 w2x2 lds-dma";
         if (dma_ragged_k(g, 256)) out += " k-zero-fill";
         return out.c_str();

@@ -160,14 +160,18 @@ def test_dispatch_choices_general_form(lib):
     # with K a multiple of 8 the direct-to-LDS kernel zero-fills past K in every layout
     assert dx(-1, 1, gb.TRANS_A | gb.TRANS_B, 1000, 1000, 1000, P, 1000, P, 1000, P, 1000) == \
         "mfma_f16 128x128x32 w2x2 lds-dma k-zero-fill"
-    # the 192 x 256 tile takes B in either layout; a transposed A and the signed or
-    # accumulating epilogues keep the 256 x 256 tile
+    # the 192 x 256 tile takes B in either layout and every epilogue (signed, accumulating,
+    # 16-bit C); a transposed A keeps the 256 x 256 tile
     assert dx(-1, 1, gb.TRANS_B, 3072, 3072, 3072, P, 3072, P, 3072, P, 3072) == \
         "mfma_f16 192x256x32 w2x2 lds-dma"
     assert dx(-1, 1, gb.TRANS_A, 3072, 3072, 3072, P, 3072, P, 3072, P, 3072) == \
         "mfma_f16 256x256x32 w2x2 lds-dma"
     assert dx(-1, 2, gb.NEG_A, 3072, 3072, 3072, P, 3072, P, 3072, P, 3072) == \
-        "mfma_bf16 256x256x32 w2x2 lds-dma"
+        "mfma_bf16 192x256x32 w2x2 lds-dma"
+    assert dx(-1, 1, gb.TRANS_B | gb.ACCUMULATE, 3072, 3072, 1000, P, 1000, P, 1000, P, 3072) == \
+        "mfma_f16 192x256x32 w2x2 lds-dma k-zero-fill"
+    assert dx(-1, 2, gb.C_16 | gb.NEG_B, 3072, 3072, 3072, P, 3072, P, 3072, P, 3072) == \
+        "mfma_bf16 192x256x32 w2x2 lds-dma"
     # what gemm355_gemm_ex rejects
     assert dx(-1, 0, gb.C_16, 8, 8, 8, P, 8, P, 8, P, 8) == "invalid"
     assert dx(-1, 1, 64, 8, 8, 8, P, 8, P, 8, P, 8) == "invalid"
@@ -301,8 +305,8 @@ def test_schedule_variants_contract(lib):
 
 
 def test_square_tile_variant_contract(lib):
-    """MFMA_T256X256 is the dispatcher with the 192 x 256 tile turned off: every plain F16 /
-    BF16 product, as dispatched except that 256 x 256 replaces 192 x 256."""
+    """MFMA_T256X256 is the dispatcher with the 192 x 256 tile turned off: every F16 / BF16
+    product (general form included), as dispatched except that 256 x 256 replaces 192 x 256."""
     d = gb.gemm355_kernel_desc
     v = gb.VARIANT_MFMA_T256X256
     assert gb.gemm355_variant_name(v) == "mfma_t256x256"
@@ -316,6 +320,11 @@ def test_square_tile_variant_contract(lib):
             assert d(v, dt, M, N, K, P, K, P, N, P, N) == d(-1, dt, M, N, K, P, K, P, N, P, N)
     assert d(v, gb.F32, 3072, 3072, 3072, P, 3072, P, 3072, P, 3072) == "invalid"
     assert gb.gemm355_run_variant(v, gb.F32, 256, 256, 128, P, 128, P, 256, P, 256, 0) == gb.ERR_UNSUPPORTED
-    assert gb.gemm355_gemm_ex(v, gb.F16, gb.TRANS_B, 256, 256, 128, P, 128, P, 128, P, 256, 0) == \
-        gb.ERR_UNSUPPORTED
-    assert gb.gemm355_kernel_desc_ex(v, gb.F16, gb.TRANS_B, 256, 256, 128, P, 128, P, 128, P, 256) == "invalid"
+    # the general form too: 256 x 256 where the dispatcher takes 192 x 256
+    dx = gb.gemm355_kernel_desc_ex
+    for fl in (gb.TRANS_B, gb.NEG_A | gb.ACCUMULATE, gb.C_16):
+        assert dx(-1, gb.F16, fl, 3072, 3072, 3072, P, 3072, P, 3072, P, 3072).startswith("mfma_f16 192x256x32")
+        assert dx(v, gb.F16, fl, 3072, 3072, 3072, P, 3072, P, 3072, P, 3072) == "mfma_f16 256x256x32 w2x2 lds-dma"
+    assert dx(v, gb.BF16, gb.TRANS_A, 1000, 1000, 1004, P, 1000, P, 1000, P, 1000) == \
+        dx(-1, gb.BF16, gb.TRANS_A, 1000, 1000, 1004, P, 1000, P, 1000, P, 1000)
+    assert dx(v, gb.F32, gb.TRANS_B, 256, 256, 128, P, 128, P, 128, P, 256) == "invalid"

@@ -124,9 +124,9 @@ SHAPES = {"f32": [(3072, 3072, 64), (1024, 768, 96), (2048, 2048, 64), (1536, 15
 # (3072, 2816, 192) and (2048, 2048, 264): K not a whole number of ring trips on the
 # direct-to-LDS kernel (256 x 256 and 128 x 128 tiles; the last trip's steps past K are
 # skipped: 2 of 4 and 7 of 8).
-# (3072, 3072, 128), (3072, 2816, 192) and BF16 (3072, 3072, 256), plain and with B
-# transposed (no negation, no accumulation): the 192 x 256 direct-to-LDS tile, the second
-# with K not a whole number of ring trips; the other layouts and modes take 256 x 256.
+# (3072, 3072, 128), (3072, 2816, 192) and BF16 (3072, 3072, 256) with A not transposed
+# (B in either layout, every mode): the 192 x 256 direct-to-LDS tile, the second with K
+# not a whole number of ring trips; with A transposed they take 256 x 256.
 # (4000, 3992, 128) and (2000, 2040, 256): every tile, ragged ones included, on the
 # direct-to-LDS kernel (256 x 256 and 128 x 128 tiles); the padding around the operands
 # holds NaN, so a ragged tile's loads past the matrix would show in its stored outputs.
@@ -308,8 +308,10 @@ def test_c16_tiles_every_layout(shape, dtype, layout, mode):
 @pytest.mark.parametrize("mode", [MODES[0], MODES[2]], ids=["plain", "neg_b_acc"])
 @pytest.mark.parametrize("layout", LAYOUTS, ids=lambda l: f"ta{int(l[0])}tb{int(l[1])}")
 def test_c16_ragged_direct_to_lds(layout, mode):
-    """2824^2 x 128: 12 x 12 tiles of 256, the last row and column of tiles 8 wide, all on
-    the direct-to-LDS kernel, with C in FP16 (guarded 2- and 4-byte stores)."""
+    """2824^2 x 128 on the direct-to-LDS kernel, with C in FP16 (guarded 2- and 4-byte
+    stores): A k-contiguous on 15 x 12 tiles of 192 x 256, the last row of tiles 136 high;
+    A transposed on 12 x 12 tiles of 256, the last row 8 high; the last column of tiles 8
+    wide in both."""
     compare16(2824, 2824, 128, "f16", *layout, *mode, seed=58)
 
 
@@ -372,3 +374,35 @@ def test_matmul_wrapper_c16():
     got = decode16(out.view(torch.int16).cpu().numpy().view(np.uint16), "bf16")
     rel, _ = errors(got, C64)
     assert rel <= 2.0 ** -8 + 1e-5, rel
+
+
+# The 192 x 256 direct-to-LDS tile in the general form: with B transposed, negated and
+# accumulating (K not a whole number of ring trips), and with 16-bit C, against the oracle
+# and bit for bit against the same call on 256 x 256 tiles (VARIANT_MFMA_T256X256).
+RECT_EX = [("f16", (3072, 3072, 264), (False, True, True, False, True), (8, 8, 8)),
+           ("bf16", (3000, 3072, 256), (False, False, False, True, True), (0, 0, 0))]
+
+
+@pytest.mark.parametrize("case", RECT_EX, ids=lambda c: c[0] + "_" + "x".join(map(str, c[1])))
+def test_rect_tile_general_form(case):
+    dtype, (M, N, K), fl, pad = case
+    ta, tb = fl[0], fl[1]
+    lda = (M if ta else K) + pad[0]
+    ldb = (K if tb else N) + pad[1]
+    P = 1 << 20
+    flags = flags_of(*fl)
+    code = gb.DTYPE_CODES[dtype]
+    assert gb.gemm355_kernel_desc_ex(gb.VARIANT_AUTO, code, flags, M, N, K, P, lda, P, ldb, P,
+                                     N + pad[2]).startswith(f"mfma_{dtype} 192x256x32")
+    assert gb.gemm355_kernel_desc_ex(gb.VARIANT_MFMA_T256X256, code, flags, M, N, K, P, lda, P, ldb, P,
+                                     N + pad[2]).startswith(f"mfma_{dtype} 256x256x32")
+    A, B, Cin = operands(M, N, K, dtype, 67)
+    Cr, ok_r, SA, SB = run_ex(A, B, dtype, *fl, Cin, gb.VARIANT_AUTO, pad)
+    Cs, ok_s, _, _ = run_ex(A, B, dtype, *fl, Cin, gb.VARIANT_MFMA_T256X256, pad)
+    assert np.array_equal(Cr.view(np.uint32), Cs.view(np.uint32)), "192 x 256 and 256 x 256 tiles differ"
+    C64, _ = oracle.gemm_ex(SA, SB, dtype, *fl[:4], Cin if fl[4] else None)
+    check(Cr, C64, dtype, K, Cin if fl[4] else None, ok_r and ok_s, f"ex rect {dtype} {M}x{N}x{K} {fl}")
+    Cin16 = inputs.to_storage(Cin, dtype)
+    C16r, ok_r, SA, SB = run_ex16(A, B, dtype, *fl, Cin16, gb.VARIANT_AUTO, pad)
+    C16s, ok_s, _, _ = run_ex16(A, B, dtype, *fl, Cin16, gb.VARIANT_MFMA_T256X256, pad)
+    assert ok_r and ok_s and np.array_equal(C16r, C16s), "16-bit C: 192 x 256 and 256 x 256 tiles differ"
