@@ -403,77 +403,111 @@ TILE_SHAPES = [("f16", 3072, 3072, 3072, ()), ("bf16", 3072, 3072, 3072, ()), ("
                ("f16", 3000, 3072, 1024, ()), ("bf16", 3072, 3072, 1000, ()),
                ("f16", 3072, 3072, 3072, ("TRANS_B",)), ("f16", 3072, 3072, 3072, ("NEG_A", "ACCUMULATE")),
                ("bf16", 3072, 3072, 3072, ("C_16",))]
+# Calls for which the dispatcher takes the 128 x 128 direct-to-LDS tile on its 4-stage ring
+# (two workgroups per CU), each with the register-staged kernel timed beside it.
+RING4_SHAPES = [("f16", 2304, 2304, 2304, ()), ("f16", 2560, 2560, 2560, ()), ("bf16", 2560, 2560, 2560, ()),
+                ("f16", 2816, 2816, 2816, ()), ("f16", 2304, 2304, 4096, ()), ("f16", 2560, 2560, 4096, ()),
+                ("f16", 2048, 4096, 2048, ()), ("bf16", 2500, 2600, 1000, ()),
+                ("f16", 2560, 2560, 2560, ("TRANS_A",)), ("f16", 2560, 2560, 2560, ("NEG_A", "ACCUMULATE"))]
 
 
-def tile_lines(warm=300, rounds=5, reps=100):
-    """The 192 x 256 tile against the 256 x 256 one (variant MFMA_T256X256) on calls the
-    dispatcher gives it, through gemm355_gemm_ex: U[-1,1] operands (seed 3; with TRANS_B
-    the K x N draw is stored transposed), packed strides; both cases warmed, then timed
-    interleaved, median of `rounds` rounds of `reps` launches (HIP events on one stream).
-    Rounds: ceil(tiles / 256), the waves of one-tile-per-CU work each grid takes."""
+def _time_pair(dt, M, N, K, fl, alt, warm, rounds, reps, stream):
+    """Median times (us) of one call on variant `alt` and as dispatched, through
+    gemm355_gemm_ex: U[-1,1] operands (seed 3; a transposed operand is the same draw
+    stored transposed), packed strides; both warmed, then timed interleaved, `rounds`
+    rounds of `reps` launches (HIP events on `stream`).  Returns (alt us, dispatched us,
+    alt kernel, dispatched kernel)."""
     import torch
 
     from roofline_optimisation_amd import binding as gb
     from roofline_optimisation_amd import inputs
 
+    flags = 0
+    for f in fl:
+        flags |= getattr(gb, f)
+    A, B = inputs.make_operands(M, N, K, 3, "uniform", dt)
+    if "TRANS_A" in fl:
+        A = np.ascontiguousarray(A.T)
+    if "TRANS_B" in fl:
+        B = np.ascontiguousarray(B.T)
+    dA = torch.from_numpy(A.view("int16")).cuda()
+    dB = torch.from_numpy(B.view("int16")).cuda()
+    # an accumulated C grows by one product's worth per launch; well inside FP32's range
+    dC = torch.zeros((M, N), dtype=torch.float32, device="cuda")
+    runs = []
+    for v in (alt, gb.VARIANT_AUTO):
+        args = (v, gb.DTYPE_CODES[dt], flags, M, N, K, dA.data_ptr(), A.shape[1], dB.data_ptr(), B.shape[1],
+                dC.data_ptr(), N, stream.cuda_stream)
+
+        def go(args=args):
+            st = gb.gemm355_gemm_ex(*args)
+            if st != gb.OK:
+                raise gb.Gemm355Error(st, "gemm355_gemm_ex")
+        runs.append((v, gb.gemm355_kernel_desc_ex(*args[:-1]), go))
+    for _, _, go in runs:
+        for _ in range(warm):
+            go()
+    stream.synchronize()
+    times = {v: [] for v, _, _ in runs}
+    for _ in range(rounds):
+        for v, _, go in runs:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                go()
+            e1.record(stream)
+            stream.synchronize()
+            times[v].append(e0.elapsed_time(e1) * 1e3 / reps)
+    del dA, dB, dC
+    return (float(np.median(times[alt])), float(np.median(times[gb.VARIANT_AUTO])), runs[0][1], runs[1][1])
+
+
+def tile_lines(warm=300, rounds=5, reps=100):
+    """Two tile classes against what the dispatcher took before them, on calls it gives
+    them: the 192 x 256 tile against the 256 x 256 one (variant MFMA_T256X256), and the
+    two-per-CU 128 x 128 direct-to-LDS tile against the register-staged kernel (variant
+    MFMA_STAGED128).  Rounds: ceil(tiles / slots), the waves of resident work each grid
+    takes (256 slots for one workgroup per CU, 512 for two)."""
+    import torch
+
+    from roofline_optimisation_amd import binding as gb
+
     cdiv = lambda a, b: -(-a // b)
     stream = torch.cuda.Stream()
-    out = ["# 192 x 256 against 256 x 256 direct-to-LDS tiles on one MI355X", "",
-           f"U[-1,1] operands (seed 3), packed strides, FP32 C (16-bit with C_16; C += with ACCUMULATE); "
-           f"{warm} warm-up launches per case, then "
-           f"both cases interleaved, median of {rounds} rounds of {reps} launches; HIP events.  "
-           "Rounds = ceil(tiles / 256 CUs).", "",
+    head = (f"U[-1,1] operands (seed 3), packed strides, FP32 C (16-bit with C_16; C += with ACCUMULATE); "
+            f"{warm} warm-up launches per case, then both cases interleaved, median of {rounds} rounds of "
+            f"{reps} launches; HIP events.")
+    out = ["# Tile classes of the 16-bit direct-to-LDS kernel on one MI355X", "", head, "",
+           "## 192 x 256 against 256 x 256 tiles", "", "Rounds = ceil(tiles / 256 CUs).", "",
            "| dtype | M x N x K | flags | 256x256 tiles (rounds) | 192x256 tiles (rounds) | 256x256 µs | "
            "dispatched µs | speedup | TFLOP/s | % of peak | dispatched kernel |",
            "|---|---|---|---|---|---|---|---|---|---|---|"]
     for dt, M, N, K, fl in TILE_SHAPES:
-        flags = 0
-        for f in fl:
-            flags |= getattr(gb, f)
-        A, B = inputs.make_operands(M, N, K, 3, "uniform", dt)
-        if "TRANS_B" in fl:
-            B = np.ascontiguousarray(B.T)
-        dA = torch.from_numpy(A.view("int16")).cuda()
-        dB = torch.from_numpy(B.view("int16")).cuda()
-        # an accumulated C grows by one product's worth per launch; well inside FP32's range
-        dC = torch.zeros((M, N), dtype=torch.float32, device="cuda")
-        ldb = B.shape[1]
-        runs = []
-        for v in (gb.VARIANT_MFMA_T256X256, gb.VARIANT_AUTO):
-            args = (v, gb.DTYPE_CODES[dt], flags, M, N, K, dA.data_ptr(), K, dB.data_ptr(), ldb,
-                    dC.data_ptr(), N, stream.cuda_stream)
-
-            def go(args=args):
-                st = gb.gemm355_gemm_ex(*args)
-                if st != gb.OK:
-                    raise gb.Gemm355Error(st, "gemm355_gemm_ex")
-            runs.append((v, gb.gemm355_kernel_desc_ex(*args[:-1]), go))
-        for _, _, go in runs:
-            for _ in range(warm):
-                go()
-        stream.synchronize()
-        times = {v: [] for v, _, _ in runs}
-        for _ in range(rounds):
-            for v, _, go in runs:
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                for _ in range(reps):
-                    go()
-                e1.record(stream)
-                stream.synchronize()
-                times[v].append(e0.elapsed_time(e1) * 1e3 / reps)
-        sq, dis = (float(np.median(times[v])) for v, _, _ in runs)
+        sq, dis, _, kd = _time_pair(dt, M, N, K, fl, gb.VARIANT_MFMA_T256X256, warm, rounds, reps, stream)
         t256 = cdiv(M, 256) * cdiv(N, 256)
         t192 = cdiv(M, 192) * cdiv(N, 256)
         tf = 2.0 * M * N * K / dis / 1e6
         fl_text = " \\| ".join(fl) or "plain"
-        out.append(f"| {dt} | {M}x{N}x{K} | {fl_text} | {t256} ({cdiv(t256, 256)}) | "
-                   f"{t192} ({cdiv(t192, 256)}) | "
+        out.append(f"| {dt} | {M}x{N}x{K} | {fl_text} | {t256} ({cdiv(t256, 256)}) | {t192} ({cdiv(t192, 256)}) | "
                    f"{sq:.2f} | {dis:.2f} | {sq / dis:.3f}x | {tf:.0f} | {100 * tf / PEAKS[dt]:.1f} | "
-                   f"`{md_cell(runs[1][1])}` |")
+                   f"`{md_cell(kd)}` |")
         log(f"[tiles] {dt} {M}x{N}x{K} {'|'.join(fl) or 'plain'}: 256x256 {sq:.2f} us, "
             f"dispatched {dis:.2f} us ({sq / dis:.3f}x)")
-        del dA, dB, dC
+    out += ["", "## 128 x 128 direct-to-LDS tiles two per CU against the register-staged kernel", "",
+            "Both run 128 x 128 tiles, two workgroups per CU (512 slots); the direct-to-LDS kernel on a 4-stage "
+            "ring (64 KiB of LDS).", "",
+            "| dtype | M x N x K | flags | 128x128 tiles (rounds) | register-staged µs | dispatched µs | speedup | "
+            "TFLOP/s | % of peak | register-staged kernel | dispatched kernel |",
+            "|---|---|---|---|---|---|---|---|---|---|---|"]
+    for dt, M, N, K, fl in RING4_SHAPES:
+        st, dis, ks, kd = _time_pair(dt, M, N, K, fl, gb.VARIANT_MFMA_STAGED128, warm, rounds, reps, stream)
+        t128 = cdiv(M, 128) * cdiv(N, 128)
+        tf = 2.0 * M * N * K / dis / 1e6
+        fl_text = " \\| ".join(fl) or "plain"
+        out.append(f"| {dt} | {M}x{N}x{K} | {fl_text} | {t128} ({cdiv(t128, 512)}) | {st:.2f} | {dis:.2f} | "
+                   f"{st / dis:.3f}x | {tf:.0f} | {100 * tf / PEAKS[dt]:.1f} | `{md_cell(ks)}` | `{md_cell(kd)}` |")
+        log(f"[tiles] {dt} {M}x{N}x{K} {'|'.join(fl) or 'plain'}: staged {st:.2f} us, "
+            f"dispatched {dis:.2f} us ({st / dis:.3f}x)")
     return out
 
 
@@ -893,7 +927,7 @@ def main():
                          "workloads, write the markdown table to PATH and print one JSON line "
                          "for the 16384 x 4096 workload; no GEMM timing")
     ap.add_argument("--family", choices=["naive", "lds_tiled", "regblock", "mfma", "mfma_split",
-                                         "mfma_w8", "mfma_t256x128", "mfma_t256x256"], default=None,
+                                         "mfma_w8", "mfma_t256x128", "mfma_t256x256", "mfma_staged128"], default=None,
                     help="only launch one kernel family (--warmup untimed and --steps timed "
                          "launches, for counter passes) on the FP32 3072^3 workload, or with "
                          "--family-dtype f16/bf16 on the n^3 16-bit workload (seed 3); no JSON line")
@@ -905,9 +939,10 @@ def main():
                          "producer/consumer split, eight waves, 256 x 128 tiles) at 4096^3 and "
                          "8192^3, interleaved, and write the markdown table to PATH")
     ap.add_argument("--tiles", default=None, metavar="PATH",
-                    help="only time the 192 x 256 direct-to-LDS tile against the 256 x 256 one on "
-                         "the shapes the dispatcher gives it, interleaved, and write the markdown "
-                         "table to PATH")
+                    help="only time the 192 x 256 direct-to-LDS tile against the 256 x 256 one, and "
+                         "the two-per-CU 128 x 128 direct-to-LDS tile against the register-staged "
+                         "kernel, on calls the dispatcher gives them, interleaved, and write the "
+                         "markdown tables to PATH")
     ap.add_argument("--ragged-k", default=None, metavar="PATH",
                     help="only time BF16 n x n x K on the direct-to-LDS kernel (n = 4096 and "
                          "2048; K not a whole number of ring trips, A's rows packed, padded or "

@@ -85,8 +85,8 @@ typedef enum gemm355_variant {
      * the dispatched one (plain products of F16 / BF16 operands only; any other dtype,
      * gemm355_gemm_ex flag or a shape the kernel does not take returns
      * GEMM355_ERR_UNSUPPORTED).  Shapes taken: whole tiles (M a multiple of 256, N of
-     * the tile width), 16-byte-aligned rows, K a multiple of 128 (MFMA_T256X256: any
-     * shape and gemm355_gemm_ex flags).
+     * the tile width), 16-byte-aligned rows, K a multiple of 128 (MFMA_T256X256 and
+     * MFMA_STAGED128: any shape and gemm355_gemm_ex flags).
      * MFMA_SPLIT: wave specialisation ("Advanced CUDA features - starting from GEMM",
      *   scheduling section, the warp-specialisation path): 256 x 128 tiles, four producer
      *   waves issue every global -> LDS load while four compute waves (128 x 64 of C
@@ -101,11 +101,16 @@ typedef enum gemm355_variant {
      *   off: the 256 x 256 tile wherever the dispatcher would take 192 x 256, every other
      *   call as dispatched (any F16 / BF16 product the dispatcher takes, gemm355_gemm_ex
      *   flags included; the same results bit for bit, since both tiles sum each
-     *   element's K products in the same order). */
+     *   element's K products in the same order).
+     * MFMA_STAGED128: the dispatched kernels with the two-per-CU 128 x 128 direct-to-LDS
+     *   tile turned off: grids of more than 256 128-wide tiles go to the register-staged
+     *   kernel, every other call as dispatched (any F16 / BF16 product the dispatcher
+     *   takes, gemm355_gemm_ex flags included). */
     GEMM355_VARIANT_MFMA_SPLIT = 4,
     GEMM355_VARIANT_MFMA_W8 = 5,
     GEMM355_VARIANT_MFMA_T256X128 = 6,
-    GEMM355_VARIANT_MFMA_T256X256 = 7
+    GEMM355_VARIANT_MFMA_T256X256 = 7,
+    GEMM355_VARIANT_MFMA_STAGED128 = 8
 } gemm355_variant;
 
 /* C = A.B with FP32 operands and FP32 accumulation. */

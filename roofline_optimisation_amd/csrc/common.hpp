@@ -63,6 +63,9 @@ struct GemmArgs {
     // Keep the 16-bit kernels' 256 x 256 direct-to-LDS tile where the dispatcher would
     // take the 192 x 256 one (a measurement-only variant sets it).
     int square_tiles = 0;
+    // Keep the 128 x 128 direct-to-LDS tile to grids of at most 256 tiles (one per CU);
+    // larger grids go to the register-staged kernel (a measurement-only variant sets it).
+    int one_round_128 = 0;
     // The MFMA kernels have plain variants (store the accumulators as they are) and
     // variants that store sign * acc (+ C); the latter serve negated products too.
     bool signed_or_acc() const { return accumulate || sign < 0.0f; }

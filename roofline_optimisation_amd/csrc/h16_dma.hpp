@@ -48,10 +48,11 @@ namespace dma {
 
 constexpr int kBK = 32;
 
-// Ring stages (32-wide k-steps) of a tile whose operands have extent E: 4 of 16 KiB per
-// operand for 256-wide tiles, 8 of 8 KiB for 128-wide ones.  A 128-wide tile's k-step is a
-// quarter of a 256-wide one's arithmetic (16 MFMAs per wave, ~130 ns), so its ring is
-// twice as deep to keep the loads as far ahead in time.
+// Ring stages (32-wide k-steps) of a tile whose operands have extent E, one workgroup per
+// CU: 4 of 16 KiB per operand for 256-wide tiles, 8 of 8 KiB for 128-wide ones.  A
+// 128-wide tile's k-step is a quarter of a 256-wide one's arithmetic (16 MFMAs per wave,
+// ~130 ns), so its ring is twice as deep to keep the loads as far ahead in time.  (With two
+// 128-wide workgroups per CU each k-step takes twice as long, and 4 stages, 64 KiB, do.)
 constexpr int ring_stages(int E) { return E == 256 ? 4 : 8; }
 
 // Geometry of an EM x EN tile: WM x WN compute waves, each owning (EM / WM) x (EN / WN) of
@@ -599,15 +600,16 @@ __device__ __forceinline__ void dma_tile(int M, int N, int K, const uint16_t *__
 
 }  // namespace dma
 
-// One workgroup per CU (128 KiB of LDS for either tile; E = 256 also takes all 256
-// accumulator registers of a lane).
+// One workgroup per CU with the default ring (128 KiB of LDS for either tile; E = 256 also
+// takes all 256 accumulator registers of a lane); E = 128 with NS = 4 (64 KiB, 144
+// registers per lane) runs two workgroups per CU.
 // KR: K not a whole number of ring trips (the last trip's chunks past K load as zeros).
-template <typename T, bool A_MN, bool B_MN, int EPI, int E, bool KR = false>
+template <typename T, bool A_MN, bool B_MN, int EPI, int E, bool KR = false, int NS = dma::ring_stages(E)>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1)))
 void mfma_f16_dma_kernel(int M, int N, int K, const uint16_t *__restrict__ A, int lda,
                          const uint16_t *__restrict__ B, int ldb, float *__restrict__ C,
                          int ldc, float sign, int flags) {
-    constexpr int kNs = dma::ring_stages(E);
+    constexpr int kNs = NS;
     __shared__ __attribute__((aligned(1024))) char lds[dma::Geo<E, E, 2, 2, kNs, 0>::kLds];
     int tm, tn;
     grouped_tile(xcd_contiguous_id(blockIdx.x, gridDim.x), cdiv(M, E), cdiv(N, E), 4, tm, tn);

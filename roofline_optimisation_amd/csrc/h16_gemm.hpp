@@ -504,19 +504,27 @@ inline bool op_fits(bool mn, int ext, int K, int ld) {
     return mn ? ((long)K * ld + ext) * 2 < (1L << 31) : ((long)ext * ld + K) * 2 < (1L << 31);
 }
 
+// Ring stages of the direct-load kernel for this call: 256-wide tiles 4; 128-wide tiles 8
+// (128 KiB, one per CU) when the grid fits one round of 256, else 4 (64 KiB, two per CU:
+// grids of more than 256 tiles then run at most ceil(tiles / 512) rounds, where one
+// workgroup per CU would take ceil(tiles / 256); with one tile per CU the deeper ring is
+// the faster one, 2048^3 FP16 19.5 against 24.7 us).
+inline int dma_stages(const GemmArgs &g, int tile) {
+    if (tile == 128 && (long)cdiv(g.M, 128) * cdiv(g.N, 128) > 256) return 4;
+    return dma::ring_stages(tile);
+}
+
 // The direct-load kernel takes every tile (ragged ones included) of a 256 x 256 or
 // 128 x 128 configuration when rows are 16-byte aligned, K is a multiple of 8 and at least
-// one trip round the ring (128 for 256-wide tiles, 256 for 128-wide ones; a K that is not
-// a whole number of trips runs to the next trip with the chunks past K loaded as zeros),
-// and every byte offset up to that trip fits the 31-bit buffer range.  At 128 x 128 the
-// tile's loads (16 KiB per k-step per CU against 256 cycles of MFMAs) run at the CU's
-// load-path rate, so the kernel is load-bound there; it still beats the register-staged
-// kernel by 10-20 % at 2048^2 (one tile per CU).
+// one trip round the ring (32 x the ring stages: 128 or 256; a K that is not a whole
+// number of trips runs to the next trip with the chunks past K loaded as zeros), and every
+// byte offset up to that trip fits the 31-bit buffer range.  At 128 x 128 the tile's loads
+// (16 KiB per k-step per tile against 256 cycles of MFMAs) run at the CU's load-path rate,
+// so the kernel is load-bound there; it still beats the register-staged kernel: by 10-20 %
+// at 2048^2 (one tile per CU), by 5-17 % from 2304^2 to 2816^2 (two per CU).
 inline bool use_dma(const GemmArgs &g, int tile) {
-    const int trip = dma::kBK * dma::ring_stages(tile);
-    // 128-wide tiles hold 128 KiB of LDS, one workgroup per CU: only a single round of
-    // at most 256 tiles (more go to the register-staged kernel, two per CU)
-    if (tile == 128 && (long)cdiv(g.M, 128) * cdiv(g.N, 128) > 256) return false;
+    const int trip = dma::kBK * dma_stages(g, tile);
+    if (tile == 128 && g.one_round_128 && (long)cdiv(g.M, 128) * cdiv(g.N, 128) > 256) return false;
     // an m/n-contiguous operand's extent is a whole number of 16-byte chunks, so no
     // load straddles the end of its last row
     if ((g.trans_a && g.M % 8 != 0) || (!g.trans_b && g.N % 8 != 0)) return false;
@@ -550,7 +558,7 @@ inline bool prefer_rect(const GemmArgs &g) {
 
 // K is not a whole number of the direct-load kernel's ring trips.
 inline bool dma_ragged_k(const GemmArgs &g, int tile) {
-    return g.K % (dma::kBK * dma::ring_stages(tile)) != 0;
+    return g.K % (dma::kBK * dma_stages(g, tile)) != 0;
 }
 
 // The epilogue's flags argument: bit 0 adds the old C; with 16-bit C, bit 1 selects
@@ -641,21 +649,28 @@ inline H16Plan plan_cfg(int BM, int BN, bool a_mn, bool b_mn, int epi, const Gem
     return p;
 }
 
+template <typename T, bool A_MN, bool B_MN, int EPI, int E, int NS>
+hipError_t launch_dma(const GemmArgs &g, hipStream_t s) {
+    const dim3 grid(cdiv(g.M, E) * cdiv(g.N, E));
+    if (dma_ragged_k(g, E))
+        hipLaunchKernelGGL((mfma_f16_dma_kernel<T, A_MN, B_MN, EPI, E, true, NS>), grid, dim3(256), 0, s, g.M,
+                           g.N, g.K, (const uint16_t *)g.A, g.lda, (const uint16_t *)g.B, g.ldb, g.C, g.ldc,
+                           g.sign, epi_flags<EPI>(g));
+    else
+        hipLaunchKernelGGL((mfma_f16_dma_kernel<T, A_MN, B_MN, EPI, E, false, NS>), grid, dim3(256), 0, s, g.M,
+                           g.N, g.K, (const uint16_t *)g.A, g.lda, (const uint16_t *)g.B, g.ldb, g.C, g.ldc,
+                           g.sign, epi_flags<EPI>(g));
+    return hipGetLastError();
+}
+
 template <typename T, int BM, int BN, int WM, int WN, int MINW, bool A_MN, bool B_MN, int EPI>
 hipError_t launch_cfg(const GemmArgs &g, hipStream_t s) {
     const H16Plan p = plan_cfg(BM, BN, A_MN, B_MN, EPI, g);
     if constexpr (BM == BN && BM >= 128) {
         if (p.dma) {
-            const dim3 grid(cdiv(g.M, BM) * cdiv(g.N, BN));
-            if (dma_ragged_k(g, BM))
-                hipLaunchKernelGGL((mfma_f16_dma_kernel<T, A_MN, B_MN, EPI, BM, true>), grid, dim3(256), 0, s,
-                                   g.M, g.N, g.K, (const uint16_t *)g.A, g.lda, (const uint16_t *)g.B,
-                                   g.ldb, g.C, g.ldc, g.sign, epi_flags<EPI>(g));
-            else
-                hipLaunchKernelGGL((mfma_f16_dma_kernel<T, A_MN, B_MN, EPI, BM>), grid, dim3(256), 0, s,
-                                   g.M, g.N, g.K, (const uint16_t *)g.A, g.lda, (const uint16_t *)g.B,
-                                   g.ldb, g.C, g.ldc, g.sign, epi_flags<EPI>(g));
-            return hipGetLastError();
+            if constexpr (BM == 128)
+                if (dma_stages(g, BM) == 4) return launch_dma<T, A_MN, B_MN, EPI, BM, 4>(g, s);
+            return launch_dma<T, A_MN, B_MN, EPI, BM, dma::ring_stages(BM)>(g, s);
         }
     }
     if (p.dma) return hipErrorInvalidValue;

@@ -46,7 +46,7 @@ def test_version_and_strings(lib):
     assert gb.gemm355_status_string(0) == "ok"
     assert gb.gemm355_status_string(1) == "invalid argument"
     assert gb.gemm355_status_string(99) == "unknown"
-    assert [gb.gemm355_variant_name(v) for v in (-1, 0, 1, 2, 3, 8)] == \
+    assert [gb.gemm355_variant_name(v) for v in (-1, 0, 1, 2, 3, 9)] == \
         ["auto", "naive", "lds_tiled", "regblock", "mfma", "unknown"]
 
 
@@ -76,7 +76,7 @@ def test_invalid_arguments_rejected_on_host(lib, args):
 
 def test_unknown_variant_and_dtype(lib):
     args = (4, 4, 4, P, 4, P, 4, P, 4, 0)
-    assert gb.gemm355_run_variant(8, 0, *args) == gb.ERR_INVALID_ARG
+    assert gb.gemm355_run_variant(9, 0, *args) == gb.ERR_INVALID_ARG
     assert gb.gemm355_run_variant(-2, 0, *args) == gb.ERR_INVALID_ARG
     assert gb.gemm355_run_variant(0, 3, *args) == gb.ERR_INVALID_ARG
     # FP32-only families reject 16-bit operands before touching the device
@@ -108,7 +108,12 @@ def test_dispatch_choices(lib):
     assert d(-1, 1, 4096, 4096, 4096, P + 2, 4096, P, 4096, P, 4096) == "mfma_f16 256x256x64 w2x2 dwordx4 unaligned | interior=pointer"
     assert d(-1, 1, 2048, 2048, 2048, P, 2048, P, 2048, P, 2048) == "mfma_f16 128x128x32 w2x2 lds-dma"
     assert d(-1, 1, 2048, 2048, 2176, P, 2176, P, 2048, P, 2048) == "mfma_f16 128x128x32 w2x2 lds-dma k-zero-fill"
-    assert d(-1, 2, 2560, 2560, 2560, P, 2560, P, 2560, P, 2560) == "mfma_bf16 128x128x64 w2x2 dwordx4 | interior=buffer,paired"
+    # more than 256 128-wide tiles: the 4-stage ring, two workgroups per CU; K below its
+    # trip (128) stays staged
+    assert d(-1, 2, 2560, 2560, 2560, P, 2560, P, 2560, P, 2560) == "mfma_bf16 128x128x32 w2x2 lds-dma ring4"
+    assert d(-1, 1, 2560, 2560, 1000, P, 1000, P, 2560, P, 2560) == \
+        "mfma_f16 128x128x32 w2x2 lds-dma ring4 k-zero-fill"
+    assert d(-1, 1, 2560, 2560, 120, P, 120, P, 2560, P, 2560).startswith("mfma_f16 128x128x64 w2x2 dwordx4")
     assert d(-1, 1, 4000, 4000, 4096, P, 4096, P, 4000, P, 4000) == "mfma_f16 256x256x32 w2x2 lds-dma"
     # 192 x 256 tiles where the 256 x 256 grid would take more 256-CU rounds of work per
     # CU: 3072^2 (144 tiles against 192), 4096 x 4104 (272 tiles, two rounds, against 374),
@@ -209,7 +214,7 @@ def test_gemm_ex_argument_checks(lib):
     assert E(0, 0, 0, 8, 6, 4, P, 3, P, 6, P, 6) == gb.ERR_INVALID_ARG           # lda < K
     assert E(0, 0, 0, 8, 6, 4, P, 4, P, 6, P, 5) == gb.ERR_INVALID_ARG           # ldc < N
     assert E(0, 3, 0, 8, 6, 4, P, 4, P, 6, P, 6) == gb.ERR_INVALID_ARG           # dtype
-    assert E(8, 0, 0, 8, 6, 4, P, 4, P, 6, P, 6) == gb.ERR_INVALID_ARG           # variant
+    assert E(9, 0, 0, 8, 6, 4, P, 4, P, 6, P, 6) == gb.ERR_INVALID_ARG           # variant
     assert E(0, 0, 0, 8, 6, 4, 0, 4, P, 6, P, 6) == gb.ERR_INVALID_ARG           # null A
     # with a flag only the naive and MFMA families exist
     for v in (gb.VARIANT_LDS_TILED, gb.VARIANT_REGBLOCK):
@@ -301,7 +306,7 @@ def test_schedule_variants_contract(lib):
     assert d(gb.VARIANT_MFMA_SPLIT, gb.F16, 512, 384, 128, P, 128, P, 384, P, 384) == \
         "mfma_f16 256x128x32 w2x2 + 4 producer waves lds-dma"
     assert d(gb.VARIANT_MFMA_W8, gb.F16, 512, 384, 128, P, 128, P, 384, P, 384) == "invalid"  # N % 256
-    assert gb.gemm355_run_variant(8, gb.F16, 8, 8, 8, P, 8, P, 8, P, 8, 0) == gb.ERR_INVALID_ARG
+    assert gb.gemm355_run_variant(9, gb.F16, 8, 8, 8, P, 8, P, 8, P, 8, 0) == gb.ERR_INVALID_ARG
 
 
 def test_square_tile_variant_contract(lib):
@@ -328,3 +333,25 @@ def test_square_tile_variant_contract(lib):
     assert dx(v, gb.BF16, gb.TRANS_A, 1000, 1000, 1004, P, 1000, P, 1000, P, 1000) == \
         dx(-1, gb.BF16, gb.TRANS_A, 1000, 1000, 1004, P, 1000, P, 1000, P, 1000)
     assert dx(v, gb.F32, gb.TRANS_B, 256, 256, 128, P, 128, P, 128, P, 256) == "invalid"
+
+
+def test_staged128_variant_contract(lib):
+    """MFMA_STAGED128 is the dispatcher with the two-per-CU 128 x 128 direct-to-LDS tile
+    turned off: grids of more than 256 128-wide tiles go to the register-staged kernel,
+    every other F16 / BF16 call (general form included) as dispatched."""
+    d = gb.gemm355_kernel_desc
+    dx = gb.gemm355_kernel_desc_ex
+    v = gb.VARIANT_MFMA_STAGED128
+    assert gb.gemm355_variant_name(v) == "mfma_staged128"
+    assert d(v, gb.BF16, 2560, 2560, 2560, P, 2560, P, 2560, P, 2560) == \
+        "mfma_bf16 128x128x64 w2x2 dwordx4 | interior=buffer,paired"
+    assert dx(v, gb.F16, gb.TRANS_A, 2560, 2048, 192, P, 2560, P, 2048, P, 2048) == \
+        "mfma_f16 128x128x64 w2x2 dwordx4 | interior=buffer"
+    assert dx(-1, gb.F16, gb.TRANS_A, 2560, 2048, 192, P, 2560, P, 2048, P, 2048) == \
+        "mfma_f16 128x128x32 w2x2 lds-dma ring4 k-zero-fill"
+    for shape in ((4096, 4096, 4096), (3072, 3072, 3072), (2048, 2048, 2048), (1000, 1000, 1004), (300, 260, 130)):
+        M, N, K = shape
+        for dt in (gb.F16, gb.BF16):
+            assert d(v, dt, M, N, K, P, K, P, N, P, N) == d(-1, dt, M, N, K, P, K, P, N, P, N)
+    assert d(v, gb.F32, 2560, 2560, 2560, P, 2560, P, 2560, P, 2560) == "invalid"
+    assert gb.gemm355_run_variant(v, gb.F32, 256, 256, 128, P, 128, P, 256, P, 256, 0) == gb.ERR_UNSUPPORTED

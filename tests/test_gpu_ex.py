@@ -117,13 +117,15 @@ MODES = [(False, False, False), (True, False, False), (False, True, True)]  # na
 SHAPES = {"f32": [(3072, 3072, 64), (1024, 768, 96), (2048, 2048, 64), (1536, 1536, 96), (1351, 1537, 100),
                   (2000, 1996, 256), (2000, 1996, 260)],
           "f16": [(3072, 3072, 128), (3072, 2816, 192), (1024, 1024, 128), (4000, 3992, 128),
-                  (3072, 3072, 64), (2048, 2048, 264)],
+                  (3072, 3072, 64), (2048, 2048, 264), (2560, 2048, 192)],
           "bf16": [(3072, 3072, 256), (1024, 512, 64), (2000, 2040, 256)]}
 # FP32 (2000, 1996, 256) and (2000, 1996, 260): ragged tiles in the unpredicated kernel
 # with the full ones, the latter with a zero-filled last k-step.
 # (3072, 2816, 192) and (2048, 2048, 264): K not a whole number of ring trips on the
 # direct-to-LDS kernel (256 x 256 and 128 x 128 tiles; the last trip's steps past K are
 # skipped: 2 of 4 and 7 of 8).
+# (2560, 2048, 192): 320 tiles of 128 x 128 on the direct-to-LDS kernel's 4-stage ring, two
+# workgroups per CU, K not a whole number of its trips (192 = 128 + 64).
 # (3072, 3072, 128), (3072, 2816, 192) and BF16 (3072, 3072, 256) with A not transposed
 # (B in either layout, every mode): the 192 x 256 direct-to-LDS tile, the second with K
 # not a whole number of ring trips; with A transposed they take 256 x 256.
@@ -294,7 +296,8 @@ def test_c16_flag_matrix_ragged(fl, dtype, variant):
     compare16(129, 97, 75, dtype, *fl, seed=56, variant=variant)
 
 
-SHAPES16 = [(3072, 3072, 128), (3072, 2816, 192), (1024, 1024, 128), (1024, 512, 64), (3072, 3072, 196)]
+SHAPES16 = [(3072, 3072, 128), (3072, 2816, 192), (1024, 1024, 128), (1024, 512, 64), (3072, 3072, 196),
+            (2560, 2048, 192)]
 
 
 @pytest.mark.parametrize("mode", MODES, ids=["plain", "neg_a", "neg_b_acc"])

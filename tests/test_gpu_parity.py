@@ -504,6 +504,32 @@ def test_dma_rect_tile(case):
     assert ok and np.array_equal(Ci[rows], C32), f"192x256 dma {dtype} {M}x{N}x{K} integers not bit-exact"
 
 
+# The 128 x 128 direct-to-LDS tile with a 4-stage ring, two workgroups per CU (grids of
+# more than 256 128-wide tiles): whole tiles with K a whole number of trips, exactly two
+# tiles per CU, and ragged M and N (2500 = 19 x 128 + 68, 2600 = 20 x 128 + 40) with
+# NaN-padded strides and K not a whole number of trips (1000 = 7 x 128 + 104).
+RING4_CASES = [("f16", (2304, 2304, 512), (0, 0, 0), "mfma_f16 128x128x32 w2x2 lds-dma ring4"),
+               ("bf16", (2048, 4096, 256), (0, 0, 0), "mfma_bf16 128x128x32 w2x2 lds-dma ring4"),
+               ("bf16", (2500, 2600, 1000), (8, 8, 8), "mfma_bf16 128x128x32 w2x2 lds-dma ring4 k-zero-fill")]
+
+
+@pytest.mark.parametrize("case", RING4_CASES, ids=lambda c: c[0] + "_" + "x".join(map(str, c[1])) + f"_pad{c[2][0]}")
+def test_dma_128_two_per_cu(case):
+    dtype, (M, N, K), pad, kernel = case
+    P = 1 << 20  # a 16-byte-aligned address: the query only inspects it
+    desc = gb.gemm355_kernel_desc(gb.VARIANT_AUTO, gb.DTYPE_CODES[dtype], M, N, K, P, K + pad[0],
+                                  P, N + pad[1], P, N + pad[2])
+    assert desc == kernel, desc
+    A, B = inputs.make_operands(M, N, K, 85, "uniform", dtype)
+    C, ok = gpu_gemm(A, B, dtype, entry="typed", pad=pad, guard_rows=1)
+    C64, _ = oracle.gemm(A, B, dtype)
+    check(C, C64, dtype, "uniform", K, ok, f"128 ring4 dma {dtype} {M}x{N}x{K} pad={pad}")
+    Ai, Bi = inputs.make_operands(M, N, K, 86, "int", dtype)
+    _, C32 = oracle.gemm(Ai, Bi, dtype)
+    Ci, ok = gpu_gemm(Ai, Bi, dtype, entry="typed", pad=pad)
+    assert ok and np.array_equal(Ci, C32), f"128 ring4 dma {dtype} {M}x{N}x{K} integers not bit-exact"
+
+
 # The direct-to-LDS kernel with K not a whole number of its ring trips (128 for 256-wide
 # tiles, 256 for 128-wide ones): the loop runs to the next trip and every 16-byte chunk at
 # k >= K loads as zeros.  K = 4000, 4064 (ragged by whole 32-wide k-steps), 4072 (a

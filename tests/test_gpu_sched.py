@@ -114,3 +114,24 @@ def test_square_tile_variant_matches_dispatched(case):
     rows = np.array(sorted(set(sample_rows(M, 24).tolist()) | {191, 192, 255, 256, M - 1}))
     C64, _ = oracle.gemm(np.ascontiguousarray(A[rows]), B, dtype)
     check(Cs[rows], C64, dtype, K, ok_s, f"t256x256 {dtype} {M}x{N}x{K} pad={pad}")
+
+
+# VARIANT_MFMA_STAGED128 (the dispatcher without the two-per-CU 128 x 128 direct-to-LDS
+# tile) where the dispatcher takes that tile: the register-staged kernel, within the bars
+# of the oracle (the two kernels may round differently: one or two MFMAs per 32-wide
+# k-step).
+STAGED_CASES = [("f16", (2304, 2304, 512), (0, 0, 0)), ("bf16", (2500, 2600, 1000), (8, 8, 8))]
+
+
+@pytest.mark.parametrize("case", STAGED_CASES, ids=lambda c: c[0] + "_" + "x".join(map(str, c[1])))
+def test_staged128_variant(case):
+    dtype, (M, N, K), pad = case
+    code = gb.DTYPE_CODES[dtype]
+    v = gb.VARIANT_MFMA_STAGED128
+    args = (M, N, K, P, K + pad[0], P, N + pad[1], P, N + pad[2])
+    assert "lds-dma ring4" in gb.gemm355_kernel_desc(gb.VARIANT_AUTO, code, *args)
+    assert "128x128x64 w2x2 dwordx4" in gb.gemm355_kernel_desc(v, code, *args)
+    A, B = inputs.make_operands(M, N, K, 76, "uniform", dtype)
+    C, ok = gpu_gemm(A, B, dtype, v, pad=pad, guard_rows=1)
+    C64, _ = oracle.gemm(A, B, dtype)
+    check(C, C64, dtype, K, ok, f"staged128 {dtype} {M}x{N}x{K} pad={pad}")
