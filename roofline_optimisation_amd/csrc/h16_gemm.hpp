@@ -547,8 +547,8 @@ inline bool use_dma_rect(const GemmArgs &g) {
 
 // Whether a product headed for 256 x 256 tiles runs faster on 192 x 256 ones: rounds of
 // resident tiles (one per CU) times tile area, the smaller tile at 0.87 of the larger
-// one's rate per unit of work (FP16 3072^3: 51.2 against 59.1 us, 192 against 144 tiles;
-// 6144 x 6144 x 4096: 236.7 against 269.8 us).
+// one's rate per unit of area (FP16 3072^3: 50.8 against 57.0 us, 192 against 144 tiles;
+// 6144 x 6144 x 4096: 229.6 against 263.0 us, 768 against 576).
 inline bool prefer_rect(const GemmArgs &g) {
     if (g.square_tiles) return false;
     const long t256 = (long)cdiv(g.M, 256) * cdiv(g.N, 256);
