@@ -396,13 +396,15 @@ def schedule_lines(warm=300, rounds=3, reps=100):
     return out
 
 
-# Calls for which the dispatcher takes the 192 x 256 direct-to-LDS tile, each with the
-# 256 x 256 tile timed beside it: (dtype, M, N, K, gemm355_gemm_ex flags).
+# Calls for which the dispatcher takes the 192 x 256 or 256 x 192 direct-to-LDS tile, each
+# with the 256 x 256 tile timed beside it: (dtype, M, N, K, gemm355_gemm_ex flags).
 TILE_SHAPES = [("f16", 3072, 3072, 3072, ()), ("bf16", 3072, 3072, 3072, ()), ("f16", 3072, 4096, 4096, ()),
                ("f16", 4096, 4104, 4096, ()), ("f16", 4608, 4608, 4608, ()), ("f16", 6144, 6144, 4096, ()),
                ("f16", 3000, 3072, 1024, ()), ("bf16", 3072, 3072, 1000, ()),
                ("f16", 3072, 3072, 3072, ("TRANS_B",)), ("f16", 3072, 3072, 3072, ("NEG_A", "ACCUMULATE")),
-               ("bf16", 3072, 3072, 3072, ("C_16",))]
+               ("bf16", 3072, 3072, 3072, ("C_16",)), ("f16", 4096, 3072, 4096, ("TRANS_B",)),
+               ("bf16", 4096, 3072, 4096, ("TRANS_B",)), ("f16", 3072, 3072, 3072, ("TRANS_A", "TRANS_B")),
+               ("bf16", 3000, 3000, 1000, ("TRANS_A", "TRANS_B", "ACCUMULATE"))]
 # Calls for which the dispatcher takes the 128 x 128 direct-to-LDS tile on its 4-stage ring
 # (two workgroups per CU), each with the register-staged kernel timed beside it.
 RING4_SHAPES = [("f16", 2304, 2304, 2304, ()), ("f16", 2560, 2560, 2560, ()), ("bf16", 2560, 2560, 2560, ()),
@@ -464,7 +466,7 @@ def _time_pair(dt, M, N, K, fl, alt, warm, rounds, reps, stream):
 
 def tile_lines(warm=300, rounds=5, reps=100):
     """Two tile classes against what the dispatcher took before them, on calls it gives
-    them: the 192 x 256 tile against the 256 x 256 one (variant MFMA_T256X256), and the
+    them: the 192 x 256 and 256 x 192 tiles against the 256 x 256 one (variant MFMA_T256X256), and the
     two-per-CU 128 x 128 direct-to-LDS tile against the register-staged kernel (variant
     MFMA_STAGED128).  Rounds: ceil(tiles / slots), the waves of resident work each grid
     takes (256 slots for one workgroup per CU, 512 for two)."""
@@ -478,14 +480,14 @@ def tile_lines(warm=300, rounds=5, reps=100):
             f"{warm} warm-up launches per case, then both cases interleaved, median of {rounds} rounds of "
             f"{reps} launches; HIP events.")
     out = ["# Tile classes of the 16-bit direct-to-LDS kernel on one MI355X", "", head, "",
-           "## 192 x 256 against 256 x 256 tiles", "", "Rounds = ceil(tiles / 256 CUs).", "",
-           "| dtype | M x N x K | flags | 256x256 tiles (rounds) | 192x256 tiles (rounds) | 256x256 µs | "
+           "## 192 x 256 and 256 x 192 against 256 x 256 tiles", "", "Rounds = ceil(tiles / 256 CUs).", "",
+           "| dtype | M x N x K | flags | 256x256 tiles (rounds) | dispatched tiles (rounds) | 256x256 µs | "
            "dispatched µs | speedup | TFLOP/s | % of peak | dispatched kernel |",
            "|---|---|---|---|---|---|---|---|---|---|---|"]
     for dt, M, N, K, fl in TILE_SHAPES:
         sq, dis, _, kd = _time_pair(dt, M, N, K, fl, gb.VARIANT_MFMA_T256X256, warm, rounds, reps, stream)
         t256 = cdiv(M, 256) * cdiv(N, 256)
-        t192 = cdiv(M, 192) * cdiv(N, 256)
+        t192 = cdiv(M, 256) * cdiv(N, 192) if "256x192" in kd else cdiv(M, 192) * cdiv(N, 256)
         tf = 2.0 * M * N * K / dis / 1e6
         fl_text = " \\| ".join(fl) or "plain"
         out.append(f"| {dt} | {M}x{N}x{K} | {fl_text} | {t256} ({cdiv(t256, 256)}) | {t192} ({cdiv(t192, 256)}) | "

@@ -39,7 +39,7 @@
 // The tile routine is written over a general geometry (an EM x EN tile, WM x WN compute
 // waves, NS ring stages, PW producer waves) so that other schedules of the same data
 // movement can be built and measured against the dispatched one: the dispatched kernels
-// are EM = EN = 256 or 128 and EM x EN = 192 x 256, on 2 x 2 waves that all load; mfma_f16_dma_sched_kernel
+// are EM = EN = 256 or 128 and EM x EN = 192 x 256 or 256 x 192, on 2 x 2 waves that all load; mfma_f16_dma_sched_kernel
 // instantiates the others (wave specialisation with producer waves, eight waves, 256 x
 // 128 tiles).
 #pragma once
@@ -325,7 +325,10 @@ __device__ __forceinline__ void pin_acc(floatx4 (&acc)[kMB][kNB]) {
 // a block row go out back to back, so every 128-byte line of C is written whole by two
 // consecutive stores.  The stores are ordinary (cached) ones: each instruction writes
 // half lines, which the L2 merges; as non-temporal stores the same pattern took 40 %
-// longer (64 MiB from 256 workgroups: 15.8 against 11.2 us).
+// longer (64 MiB from 256 workgroups: 15.8 against 11.2 us).  Accumulating into C, the old
+// values of a whole row of quads are loaded before any of them is used, and the next row's
+// loads are issued before this row's stores, so the loads wait on memory kMB times rather
+// than once per quad (the loop's fragment registers are free by then).
 template <int EPI, typename T, bool EDGE, int kMB, int kNB>
 __device__ __forceinline__ void store_tile(floatx4 (&acc)[kMB][kNB], float *__restrict__ C, int ldc,
                                            int row0, int col0, int M, int N, float sign, int flags) {
@@ -343,12 +346,50 @@ __device__ __forceinline__ void store_tile(floatx4 (&acc)[kMB][kNB], float *__re
                 }
     } else if constexpr (EPI == 1) {
         const bool use_old = flags & 1;
+        if (!use_old) {
 #pragma unroll
-        for (int i = 0; i < kMB; ++i)
+            for (int i = 0; i < kMB; ++i)
 #pragma unroll
-            for (int j = 0; j < kNB; ++j)
-                store_quad16_acc<EDGE>(acc[i][j], C, ldc, rl + 16 * i, col0 + 16 * j + (lane & 15),
-                                       M, N, sign, use_old);
+                for (int j = 0; j < kNB; ++j)
+                    store_quad16_acc<EDGE>(acc[i][j], C, ldc, rl + 16 * i, col0 + 16 * j + (lane & 15),
+                                           M, N, sign, false);
+            return;
+        }
+        // this lane's element of quad row i, quad j, row r: Cl[(16 i + r) ldc + 16 j]
+        float *const Cl = C + (size_t)rl * ldc + col0 + (lane & 15);
+        const int cl = col0 + (lane & 15);
+        float old[2][kNB][4];
+        const auto load_row = [&](int i, float (&o)[kNB][4]) {
+            const float *Ci = Cl + (size_t)(16 * i) * ldc;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int j = 0; j < kNB; ++j) {
+                    const bool ok = !EDGE || (rl + 16 * i + r < M && cl + 16 * j < N);
+                    // an element outside M x N reads this lane's first one instead, so the
+                    // load is in bounds even where the compiler issues it anyway
+                    o[j][r] = ok ? Ci[ok ? (size_t)r * ldc + 16 * j : 0] : 0.f;
+                }
+        };
+        __builtin_amdgcn_sched_barrier(0);
+        load_row(0, old[0]);
+#pragma unroll
+        for (int i = 0; i < kMB; ++i) {
+            __builtin_amdgcn_sched_barrier(0);
+            if (i + 1 < kMB) load_row(i + 1, old[(i + 1) & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+            float *Ci = Cl + (size_t)(16 * i) * ldc;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int j = 0; j < kNB; ++j) {
+                    float a;
+                    asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(a) : "a"(acc[i][j][r]));
+                    if (!EDGE || (rl + 16 * i + r < M && cl + 16 * j < N))
+                        Ci[(size_t)r * ldc + 16 * j] = sign * a + old[i & 1][j][r];
+                }
+        }
+        __builtin_amdgcn_sched_barrier(0);
     } else {
 #pragma unroll
         for (int i = 0; i < kMB; ++i)
@@ -617,24 +658,27 @@ void mfma_f16_dma_kernel(int M, int N, int K, const uint16_t *__restrict__ A, in
                                                                       flags, tm * E, tn * E, lds);
 }
 
-// 192 x 256 tiles: the k-contiguous A's 192 rows by B's 256 columns, for products whose
-// 256 x 256 grid leaves CUs idle where a 192-row grid fills them (3072^2: 192 tiles
-// instead of 144).  The same tile routine on four waves of 96 x 128, one workgroup per CU
-// (112 KiB of LDS); B may be n- or k-contiguous, and every epilogue kind is taken.  (An
-// m-contiguous A would need 192-element LDS rows, 24 chunks, which the ring's XOR swizzle
-// of chunk slots does not map onto themselves.)
+// 192 x 256 and 256 x 192 tiles, for products whose 256 x 256 grid leaves CUs idle where
+// a grid with one extent of 192 fills them (3072^2: 192 tiles instead of 144; 4096 x 3072:
+// 256 instead of 192).  The 192 extent belongs to a k-contiguous operand: A (EM = 192, B in
+// either layout) or B (EN = 192, A in either layout); an m/n-contiguous operand would need
+// 192-element LDS rows, 24 chunks, which the ring's XOR swizzle of chunk slots does not map
+// onto themselves.  The same tile routine on four waves of 96 x 128 or 128 x 96, one
+// workgroup per CU (112 KiB of LDS); every epilogue kind is taken.
 // KR: K not a whole number of ring trips (the last trip's chunks past K load as zeros).
-template <typename T, bool B_MN, int EPI, bool KR = false>
+template <typename T, bool A_MN, bool B_MN, int EPI, int EM, int EN, bool KR = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1)))
 void mfma_f16_dma_rect_kernel(int M, int N, int K, const uint16_t *__restrict__ A, int lda,
                               const uint16_t *__restrict__ B, int ldb, float *__restrict__ C,
                               int ldc, float sign, int flags) {
-    constexpr int kEM = 192, kEN = 256, kNs = dma::ring_stages(kEN);
-    __shared__ __attribute__((aligned(1024))) char lds[dma::Geo<kEM, kEN, 2, 2, kNs, 0>::kLds];
+    static_assert((EM == 192 && EN == 256 && !A_MN) || (EM == 256 && EN == 192 && !B_MN),
+                  "the 192 extent on a k-contiguous operand");
+    constexpr int kNs = dma::ring_stages(256);
+    __shared__ __attribute__((aligned(1024))) char lds[dma::Geo<EM, EN, 2, 2, kNs, 0>::kLds];
     int tm, tn;
-    grouped_tile(xcd_contiguous_id(blockIdx.x, gridDim.x), cdiv(M, kEM), cdiv(N, kEN), 4, tm, tn);
-    dma::dma_tile<T, false, B_MN, EPI, kEM, kEN, 2, 2, kNs, 0, false, KR>(M, N, K, A, lda, B, ldb, C, ldc,
-                                                                          sign, flags, tm * kEM, tn * kEN, lds);
+    grouped_tile(xcd_contiguous_id(blockIdx.x, gridDim.x), cdiv(M, EM), cdiv(N, EN), 4, tm, tn);
+    dma::dma_tile<T, A_MN, B_MN, EPI, EM, EN, 2, 2, kNs, 0, false, KR>(M, N, K, A, lda, B, ldb, C, ldc, sign,
+                                                                       flags, tm * EM, tn * EN, lds);
 }
 
 // Schedules of the same data movement that are kept for measurement (gemm355_run_variant

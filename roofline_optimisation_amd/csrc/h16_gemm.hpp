@@ -534,26 +534,38 @@ inline bool use_dma(const GemmArgs &g, int tile) {
            op_fits(g.trans_b == 0, tile, kpad, g.ldb);
 }
 
-// The 192 x 256 direct-load tile (A k-contiguous, any epilogue) on the same terms as
-// the 256 x 256 one: rows 16-byte aligned, K a multiple of 8 and at least one ring trip,
-// every byte offset within 31 bits, and with B n-contiguous N a multiple of 8.
-inline bool use_dma_rect(const GemmArgs &g) {
-    if (g.trans_a || (!g.trans_b && g.N % 8 != 0)) return false;
+// The EM x EN direct-load tile with one extent of 192 (192 x 256: A k-contiguous; 256 x
+// 192: B k-contiguous; any epilogue) on the same terms as the 256 x 256 one: rows 16-byte
+// aligned, K a multiple of 8 and at least one ring trip, every byte offset within 31 bits,
+// and an m/n-contiguous operand's extent a multiple of 8.
+inline bool use_dma_rect(const GemmArgs &g, int em, int en) {
+    if (em == 192 ? g.trans_a != 0 : g.trans_b == 0) return false;
+    if ((g.trans_a && g.M % 8 != 0) || (!g.trans_b && g.N % 8 != 0)) return false;
     const int trip = dma::kBK * dma::ring_stages(256);
     const int kpad = cdiv(g.K, trip) * trip;
-    return h16_vec(g) && g.K >= trip && g.K % 8 == 0 && g.M >= 192 && g.N >= 256 &&
-           op_fits(false, 192, kpad, g.lda) && op_fits(g.trans_b == 0, 256, kpad, g.ldb);
+    return h16_vec(g) && g.K >= trip && g.K % 8 == 0 && g.M >= em && g.N >= en &&
+           op_fits(g.trans_a != 0, em, kpad, g.lda) && op_fits(g.trans_b == 0, en, kpad, g.ldb);
 }
 
-// Whether a product headed for 256 x 256 tiles runs faster on 192 x 256 ones: rounds of
-// resident tiles (one per CU) times tile area, the smaller tile at 0.87 of the larger
-// one's rate per unit of area (FP16 3072^3: 50.8 against 57.0 us, 192 against 144 tiles;
-// 6144 x 6144 x 4096: 229.6 against 263.0 us, 768 against 576).
-inline bool prefer_rect(const GemmArgs &g) {
-    if (g.square_tiles) return false;
-    const long t256 = (long)cdiv(g.M, 256) * cdiv(g.N, 256);
-    const long t192 = (long)cdiv(g.M, 192) * cdiv(g.N, 256);
-    return (double)((t192 + 255) / 256) * (192 * 256) / 0.87 < (double)((t256 + 255) / 256) * (256 * 256);
+// Which tile a product headed for 256 x 256 tiles takes: 256 (the square tile), 192 (192 x
+// 256) or -192 (256 x 192), by rounds of resident tiles (one per CU) times tile area, a
+// tile with a 192 extent at 0.87 of the square one's rate per unit of area (FP16 3072^3:
+// 50.8 against 57.0 us, 192 against 144 tiles; 6144 x 6144 x 4096: 229.6 against 263.0 us,
+// 768 against 576).  Ties keep the square tile, then 192 x 256.
+inline int rect_choice(const GemmArgs &g) {
+    if (g.square_tiles) return 256;
+    const auto cost = [&](int em, int en) {
+        const long t = (long)cdiv(g.M, em) * cdiv(g.N, en);
+        return (double)((t + 255) / 256) * em * en / (em == en ? 1.0 : 0.87);
+    };
+    int best = 256;
+    double c = cost(256, 256);
+    if (use_dma_rect(g, 192, 256) && cost(192, 256) < c) {
+        best = 192;
+        c = cost(192, 256);
+    }
+    if (use_dma_rect(g, 256, 192) && cost(256, 192) < c) best = -192;
+    return best;
 }
 
 // K is not a whole number of the direct-load kernel's ring trips.
@@ -746,25 +758,28 @@ inline bool use_64x64(const GemmArgs &g) {
     return (long)cdiv(g.M, 128) * cdiv(g.N, 64) < 256;
 }
 
-template <typename T, bool B_MN, int EPI>
+template <typename T, bool A_MN, bool B_MN, int EPI, int EM, int EN>
 hipError_t launch_rect(const GemmArgs &g, hipStream_t s) {
-    const dim3 grid(cdiv(g.M, 192) * cdiv(g.N, 256));
+    const dim3 grid(cdiv(g.M, EM) * cdiv(g.N, EN));
     if (dma_ragged_k(g, 256))
-        hipLaunchKernelGGL((mfma_f16_dma_rect_kernel<T, B_MN, EPI, true>), grid, dim3(256), 0, s, g.M, g.N,
-                           g.K, (const uint16_t *)g.A, g.lda, (const uint16_t *)g.B, g.ldb, g.C, g.ldc,
-                           g.sign, epi_flags<EPI>(g));
+        hipLaunchKernelGGL((mfma_f16_dma_rect_kernel<T, A_MN, B_MN, EPI, EM, EN, true>), grid, dim3(256), 0, s,
+                           g.M, g.N, g.K, (const uint16_t *)g.A, g.lda, (const uint16_t *)g.B, g.ldb, g.C,
+                           g.ldc, g.sign, epi_flags<EPI>(g));
     else
-        hipLaunchKernelGGL((mfma_f16_dma_rect_kernel<T, B_MN, EPI>), grid, dim3(256), 0, s, g.M, g.N, g.K,
-                           (const uint16_t *)g.A, g.lda, (const uint16_t *)g.B, g.ldb, g.C, g.ldc, g.sign,
-                           epi_flags<EPI>(g));
+        hipLaunchKernelGGL((mfma_f16_dma_rect_kernel<T, A_MN, B_MN, EPI, EM, EN>), grid, dim3(256), 0, s, g.M,
+                           g.N, g.K, (const uint16_t *)g.A, g.lda, (const uint16_t *)g.B, g.ldb, g.C, g.ldc,
+                           g.sign, epi_flags<EPI>(g));
     return hipGetLastError();
 }
 
 template <typename T, bool A_MN, bool B_MN, int EPI>
 hipError_t launch_layout(const GemmArgs &g, hipStream_t s) {
     if (pick_tile(g) == 256) {
+        const int rect = rect_choice(g);
         if constexpr (!A_MN)
-            if (use_dma_rect(g) && prefer_rect(g)) return launch_rect<T, B_MN, EPI>(g, s);
+            if (rect == 192) return launch_rect<T, A_MN, B_MN, EPI, 192, 256>(g, s);
+        if constexpr (!B_MN)
+            if (rect == -192) return launch_rect<T, A_MN, B_MN, EPI, 256, 192>(g, s);
         return launch_cfg<T, 256, 256, 2, 2, 1, A_MN, B_MN, EPI>(g, s);
     }
     if constexpr (!A_MN && EPI == 0) {

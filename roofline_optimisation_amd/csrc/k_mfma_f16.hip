@@ -30,8 +30,9 @@ const char *desc_mfma_f16(int dtype, const GemmArgs &g) {
     const bool narrow = plain_km && !small && use_128x64(g);
     const int bm = big ? 256 : (small ? 64 : 128), bn = big ? 256 : (small || narrow ? 64 : 128);
     out = name;
-    if (big && !g.trans_a && use_dma_rect(g) && prefer_rect(g)) {
-        out += " 192x256x32 w2x2 lds-dma";
+    const int rect = big ? rect_choice(g) : 256;
+    if (rect != 256) {
+        out += rect == 192 ? " 192x256x32 w2x2 lds-dma" : " 256x192x32 w2x2 lds-dma";
         if (dma_ragged_k(g, 256)) out += " k-zero-fill";
         return out.c_str();
     }

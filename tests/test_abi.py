@@ -166,7 +166,8 @@ def test_dispatch_choices_general_form(lib):
     assert dx(-1, 1, gb.TRANS_A | gb.TRANS_B, 1000, 1000, 1000, P, 1000, P, 1000, P, 1000) == \
         "mfma_f16 128x128x32 w2x2 lds-dma k-zero-fill"
     # the 192 x 256 tile takes B in either layout and every epilogue (signed, accumulating,
-    # 16-bit C); a transposed A keeps the 256 x 256 tile
+    # 16-bit C); with B transposed (k-contiguous) the 256 x 192 tile takes A in either
+    # layout; a transposed A with B n-contiguous keeps the 256 x 256 tile
     assert dx(-1, 1, gb.TRANS_B, 3072, 3072, 3072, P, 3072, P, 3072, P, 3072) == \
         "mfma_f16 192x256x32 w2x2 lds-dma"
     assert dx(-1, 1, gb.TRANS_A, 3072, 3072, 3072, P, 3072, P, 3072, P, 3072) == \
@@ -177,6 +178,14 @@ def test_dispatch_choices_general_form(lib):
         "mfma_f16 192x256x32 w2x2 lds-dma k-zero-fill"
     assert dx(-1, 2, gb.C_16 | gb.NEG_B, 3072, 3072, 3072, P, 3072, P, 3072, P, 3072) == \
         "mfma_bf16 192x256x32 w2x2 lds-dma"
+    assert dx(-1, 1, gb.TRANS_A | gb.TRANS_B, 3072, 3072, 3072, P, 3072, P, 3072, P, 3072) == \
+        "mfma_f16 256x192x32 w2x2 lds-dma"
+    # 4096 x 3072: 192 tiles of 256 x 256, 264 of 192 x 256 (two rounds), 256 of 256 x 192
+    assert dx(-1, 1, gb.TRANS_B, 4096, 3072, 4096, P, 4096, P, 4096, P, 3072) == \
+        "mfma_f16 256x192x32 w2x2 lds-dma"
+    assert dx(-1, 1, 0, 4096, 3072, 4096, P, 4096, P, 3072, P, 3072) == "mfma_f16 256x256x32 w2x2 lds-dma"
+    assert dx(-1, 2, gb.TRANS_A | gb.TRANS_B | gb.ACCUMULATE, 3000, 3000, 1000, P, 3000, P, 1000, P, 3000) == \
+        "mfma_bf16 256x192x32 w2x2 lds-dma k-zero-fill"
     # what gemm355_gemm_ex rejects
     assert dx(-1, 0, gb.C_16, 8, 8, 8, P, 8, P, 8, P, 8) == "invalid"
     assert dx(-1, 1, 64, 8, 8, 8, P, 8, P, 8, P, 8) == "invalid"

@@ -128,7 +128,8 @@ SHAPES = {"f32": [(3072, 3072, 64), (1024, 768, 96), (2048, 2048, 64), (1536, 15
 # workgroups per CU, K not a whole number of its trips (192 = 128 + 64).
 # (3072, 3072, 128), (3072, 2816, 192) and BF16 (3072, 3072, 256) with A not transposed
 # (B in either layout, every mode): the 192 x 256 direct-to-LDS tile, the second with K
-# not a whole number of ring trips; with A transposed they take 256 x 256.
+# not a whole number of ring trips; with both transposed the 256 x 192 tile; with A
+# transposed and B not, 256 x 256.
 # (4000, 3992, 128) and (2000, 2040, 256): every tile, ragged ones included, on the
 # direct-to-LDS kernel (256 x 256 and 128 x 128 tiles); the padding around the operands
 # holds NaN, so a ragged tile's loads past the matrix would show in its stored outputs.
@@ -379,16 +380,21 @@ def test_matmul_wrapper_c16():
     assert rel <= 2.0 ** -8 + 1e-5, rel
 
 
-# The 192 x 256 direct-to-LDS tile in the general form: with B transposed, negated and
-# accumulating (K not a whole number of ring trips), and with 16-bit C, against the oracle
-# and bit for bit against the same call on 256 x 256 tiles (VARIANT_MFMA_T256X256).
-RECT_EX = [("f16", (3072, 3072, 264), (False, True, True, False, True), (8, 8, 8)),
-           ("bf16", (3000, 3072, 256), (False, False, False, True, True), (0, 0, 0))]
+# The 192 x 256 and 256 x 192 direct-to-LDS tiles in the general form: 192 x 256 with B
+# transposed, negated and accumulating (K not a whole number of ring trips) and with B not
+# transposed; 256 x 192 (B transposed, so k-contiguous) with A transposed, ragged M and N,
+# K not a whole number of ring trips, negated and accumulating, and plain on 4096 x 3072
+# (256 tiles against 192 of 256 x 256); each with FP32 and with 16-bit C, against the
+# oracle and bit for bit against the same call on 256 x 256 tiles (VARIANT_MFMA_T256X256).
+RECT_EX = [("f16", (3072, 3072, 264), (False, True, True, False, True), (8, 8, 8), "192x256x32"),
+           ("bf16", (3000, 3072, 256), (False, False, False, True, True), (0, 0, 0), "192x256x32"),
+           ("bf16", (3000, 3000, 1000), (True, True, True, False, True), (8, 8, 8), "256x192x32"),
+           ("f16", (4096, 3072, 512), (False, True, False, False, False), (0, 0, 0), "256x192x32")]
 
 
-@pytest.mark.parametrize("case", RECT_EX, ids=lambda c: c[0] + "_" + "x".join(map(str, c[1])))
+@pytest.mark.parametrize("case", RECT_EX, ids=lambda c: c[0] + "_" + "x".join(map(str, c[1])) + "_" + c[4][:7])
 def test_rect_tile_general_form(case):
-    dtype, (M, N, K), fl, pad = case
+    dtype, (M, N, K), fl, pad, tile = case
     ta, tb = fl[0], fl[1]
     lda = (M if ta else K) + pad[0]
     ldb = (K if tb else N) + pad[1]
@@ -396,7 +402,7 @@ def test_rect_tile_general_form(case):
     flags = flags_of(*fl)
     code = gb.DTYPE_CODES[dtype]
     assert gb.gemm355_kernel_desc_ex(gb.VARIANT_AUTO, code, flags, M, N, K, P, lda, P, ldb, P,
-                                     N + pad[2]).startswith(f"mfma_{dtype} 192x256x32")
+                                     N + pad[2]).startswith(f"mfma_{dtype} {tile}")
     assert gb.gemm355_kernel_desc_ex(gb.VARIANT_MFMA_T256X256, code, flags, M, N, K, P, lda, P, ldb, P,
                                      N + pad[2]).startswith(f"mfma_{dtype} 256x256x32")
     A, B, Cin = operands(M, N, K, dtype, 67)

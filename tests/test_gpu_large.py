@@ -78,13 +78,15 @@ def test_operand_over_2gib(case):
 
 # The general form (gemm355_gemm_ex) with the large operand transposed: A stored K x M
 # (m-contiguous: its offsets pass 2^31, pointer loads) or B stored N x K (k-contiguous:
-# its later tiles start past 2^31, on the buffer-load and direct-to-LDS kernels).  The
+# its later tiles start past 2^31, on the buffer-load and direct-to-LDS kernels; the BF16
+# case takes 256 x 192 tiles, 684 of them against 513 of 256 x 256, three rounds either
+# way).  The
 # stored matrices are drawn in their stored shape: A from default_rng(seed), B from
 # default_rng(seed + 1).
 EX_CASES = [
     ("f16", (26624, 256, 40960), "ta", "| interior=pointer"),          # stored A 2.18 GB
     ("f32", (256, 140032, 4096), "tb", "mfma_f32 128x128x32"),         # stored B 2.29 GB
-    ("bf16", (256, 131328, 8192), "tb", "256x256x32 w2x2 lds-dma"),    # stored B 2.15 GB
+    ("bf16", (256, 131328, 8192), "tb", "256x192x32 w2x2 lds-dma"),    # stored B 2.15 GB
 ]
 
 
