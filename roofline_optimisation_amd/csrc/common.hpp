@@ -274,6 +274,21 @@ __device__ __forceinline__ void store_quad16_acc(const floatx4 &acc, float *__re
 // one 2-byte access.  `flags` bit 0 adds the old C.  EDGE guards every access against
 // M x N (a pair whose second column is outside is read and written 2 bytes at a time;
 // the exchange itself runs in every lane).  `lane` is this lane's index in the wave.
+// One row of such a pair in paired mode: the 4-byte word this lane writes, from its own
+// values a0 (quad 0) and a1 (quad 1) of the row and the old word (two 16-bit values) when
+// use_old.  The exchange between lanes 2m and 2m+1 runs in every lane.
+template <typename T>
+__device__ __forceinline__ uint32_t pair16_word(float a0, float a1, int odd, float sign, uint32_t oldw,
+                                                bool use_old) {
+    const float send = odd ? a0 : a1;
+    const float recv = __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, send), 0xB1, 0xF, 0xF, false));
+    const float lo = odd ? recv : a0, hi = odd ? a1 : recv;
+    const float olo = use_old ? to_float(T{(uint16_t)(oldw & 0xFFFF)}) : 0.f;
+    const float ohi = use_old ? to_float(T{(uint16_t)(oldw >> 16)}) : 0.f;
+    return (uint32_t)to_bits(sign * lo + olo, T{}) | ((uint32_t)to_bits(sign * hi + ohi, T{}) << 16);
+}
+
 template <bool EDGE, typename T>
 __device__ __forceinline__ void store_pair16_c16(const floatx4 &acc0, const floatx4 &acc1,
                                                  uint16_t *__restrict__ C, int ldc, int row0,
@@ -312,15 +327,7 @@ __device__ __forceinline__ void store_pair16_c16(const floatx4 &acc0, const floa
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        const float a0 = rd(acc0, r), a1 = rd(acc1, r);
-        const float send = odd ? a0 : a1;
-        const float recv = __builtin_bit_cast(
-            float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, send), 0xB1, 0xF, 0xF, false));
-        const float lo = odd ? recv : a0, hi = odd ? a1 : recv;
-        const float olo = use_old ? to_float(T{(uint16_t)(oldw[r] & 0xFFFF)}) : 0.f;
-        const float ohi = use_old ? to_float(T{(uint16_t)(oldw[r] >> 16)}) : 0.f;
-        const uint32_t w = (uint32_t)to_bits(sign * lo + olo, T{}) |
-                           ((uint32_t)to_bits(sign * hi + ohi, T{}) << 16);
+        const uint32_t w = pair16_word<T>(rd(acc0, r), rd(acc1, r), odd, sign, oldw[r], use_old);
         uint16_t *c = C + (size_t)(row0 + r) * ldc + cw;
         if (!EDGE || (row0 + r < M && cw + 1 < N)) *(uint32_t *)c = w;
         else if (row0 + r < M && cw < N) *c = (uint16_t)(w & 0xFFFF);

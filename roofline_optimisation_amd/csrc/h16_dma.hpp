@@ -325,10 +325,11 @@ __device__ __forceinline__ void pin_acc(floatx4 (&acc)[kMB][kNB]) {
 // a block row go out back to back, so every 128-byte line of C is written whole by two
 // consecutive stores.  The stores are ordinary (cached) ones: each instruction writes
 // half lines, which the L2 merges; as non-temporal stores the same pattern took 40 %
-// longer (64 MiB from 256 workgroups: 15.8 against 11.2 us).  Accumulating into C, the old
-// values of a whole row of quads are loaded before any of them is used, and the next row's
-// loads are issued before this row's stores, so the loads wait on memory kMB times rather
-// than once per quad (the loop's fragment registers are free by then).
+// longer (64 MiB from 256 workgroups: 15.8 against 11.2 us).  Accumulating into C (FP32 in
+// every tile; 16-bit in 4-byte words in interior tiles), the old values of a whole row of
+// quads are loaded before any of them is used, and the next row's loads are issued before
+// this row's stores, so the loads wait on memory kMB times rather than once per quad or pair
+// (the loop's fragment registers are free by then).
 template <int EPI, typename T, bool EDGE, int kMB, int kNB>
 __device__ __forceinline__ void store_tile(floatx4 (&acc)[kMB][kNB], float *__restrict__ C, int ldc,
                                            int row0, int col0, int M, int N, float sign, int flags) {
@@ -366,9 +367,10 @@ __device__ __forceinline__ void store_tile(floatx4 (&acc)[kMB][kNB], float *__re
 #pragma unroll
                 for (int j = 0; j < kNB; ++j) {
                     const bool ok = !EDGE || (rl + 16 * i + r < M && cl + 16 * j < N);
-                    // an element outside M x N reads this lane's first one instead, so the
-                    // load is in bounds even where the compiler issues it anyway
-                    o[j][r] = ok ? Ci[ok ? (size_t)r * ldc + 16 * j : 0] : 0.f;
+                    // an element outside M x N reads C's first one instead, so the load is
+                    // in bounds even where the compiler issues it anyway
+                    const float *p = Ci + (size_t)r * ldc + 16 * j;
+                    o[j][r] = ok ? *(ok ? p : C) : 0.f;
                 }
         };
         __builtin_amdgcn_sched_barrier(0);
@@ -391,12 +393,49 @@ __device__ __forceinline__ void store_tile(floatx4 (&acc)[kMB][kNB], float *__re
         }
         __builtin_amdgcn_sched_barrier(0);
     } else {
+        if (EDGE || (flags & 3) != 3) {
 #pragma unroll
-        for (int i = 0; i < kMB; ++i)
+            for (int i = 0; i < kMB; ++i)
 #pragma unroll
-            for (int j = 0; j < kNB; j += 2)
-                store_pair16_c16<EDGE, T>(acc[i][j], acc[i][j + 1], (uint16_t *)C, ldc, rl + 16 * i,
-                                          col0 + 16 * j, M, N, sign, flags, lane);
+                for (int j = 0; j < kNB; j += 2)
+                    store_pair16_c16<EDGE, T>(acc[i][j], acc[i][j + 1], (uint16_t *)C, ldc, rl + 16 * i,
+                                              col0 + 16 * j, M, N, sign, flags, lane);
+            return;
+        }
+        // interior tiles accumulating with 4-byte words (store_pair16_c16's paired mode): the
+        // old words of a row of quad pairs loaded a row ahead as above
+        constexpr int kP = kNB / 2;
+        const int odd = lane & 1;
+        const int cw = col0 + (lane & 14) + 16 * odd;  // first column of this lane's word in pair 0
+        uint16_t *const Cl = (uint16_t *)C + (size_t)rl * ldc + cw;
+        uint32_t oldw[2][kP][4];
+        const auto load_row = [&](int i, uint32_t (&o)[kP][4]) {
+            const uint16_t *Ci = Cl + (size_t)(16 * i) * ldc;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int p = 0; p < kP; ++p) o[p][r] = *(const uint32_t *)(Ci + (size_t)r * ldc + 32 * p);
+        };
+        __builtin_amdgcn_sched_barrier(0);
+        load_row(0, oldw[0]);
+#pragma unroll
+        for (int i = 0; i < kMB; ++i) {
+            __builtin_amdgcn_sched_barrier(0);
+            if (i + 1 < kMB) load_row(i + 1, oldw[(i + 1) & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+            uint16_t *Ci = Cl + (size_t)(16 * i) * ldc;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int p = 0; p < kP; ++p) {
+                    float a0, a1;
+                    asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(a0) : "a"(acc[i][2 * p][r]));
+                    asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(a1) : "a"(acc[i][2 * p + 1][r]));
+                    *(uint32_t *)(Ci + (size_t)r * ldc + 32 * p) =
+                        pair16_word<T>(a0, a1, odd, sign, oldw[i & 1][p][r], true);
+                }
+        }
+        __builtin_amdgcn_sched_barrier(0);
     }
 }
 

@@ -186,7 +186,6 @@ __device__ __forceinline__ void h16_tile(int M, int N, int K, const uint16_t *__
     using Cfg = H16Cfg<BM, BN, WM, WN, A_MN, B_MN>;
     using OA = typename Cfg::OA;
     using OB = typename Cfg::OB;
-    constexpr int TT = Cfg::kThreads;
     constexpr int MB = Cfg::kMB, NB = Cfg::kNB;
     constexpr int kAC = OA::kChunks, kBC = OB::kChunks;
 
