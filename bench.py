@@ -396,15 +396,18 @@ def schedule_lines(warm=300, rounds=3, reps=100):
     return out
 
 
-# Calls for which the dispatcher takes the 192 x 256 or 256 x 192 direct-to-LDS tile, each
-# with the 256 x 256 tile timed beside it: (dtype, M, N, K, gemm355_gemm_ex flags).
+# Calls for which the dispatcher takes the 192 x 256 or 256 x 192 direct-to-LDS tile (the
+# last five with the 192 side m/n-contiguous, loaded 256 wide), each with the 256 x 256 tile
+# timed beside it: (dtype, M, N, K, gemm355_gemm_ex flags).
 TILE_SHAPES = [("f16", 3072, 3072, 3072, ()), ("bf16", 3072, 3072, 3072, ()), ("f16", 3072, 4096, 4096, ()),
                ("f16", 4096, 4104, 4096, ()), ("f16", 4608, 4608, 4608, ()), ("f16", 6144, 6144, 4096, ()),
                ("f16", 3000, 3072, 1024, ()), ("bf16", 3072, 3072, 1000, ()),
                ("f16", 3072, 3072, 3072, ("TRANS_B",)), ("f16", 3072, 3072, 3072, ("NEG_A", "ACCUMULATE")),
                ("bf16", 3072, 3072, 3072, ("C_16",)), ("f16", 4096, 3072, 4096, ("TRANS_B",)),
                ("bf16", 4096, 3072, 4096, ("TRANS_B",)), ("f16", 3072, 3072, 3072, ("TRANS_A", "TRANS_B")),
-               ("bf16", 3000, 3000, 1000, ("TRANS_A", "TRANS_B", "ACCUMULATE"))]
+               ("bf16", 3000, 3000, 1000, ("TRANS_A", "TRANS_B", "ACCUMULATE")),
+               ("f16", 4096, 3072, 4096, ()), ("bf16", 4096, 3072, 4096, ()), ("f16", 3072, 3072, 3072, ("TRANS_A",)),
+               ("bf16", 3072, 3072, 3072, ("TRANS_A",)), ("f16", 4608, 4608, 4608, ("TRANS_A",))]
 # Calls for which the dispatcher takes the 128 x 128 direct-to-LDS tile on its 4-stage ring
 # (two workgroups per CU), each with the register-staged kernel timed beside it.
 RING4_SHAPES = [("f16", 2304, 2304, 2304, ()), ("f16", 2560, 2560, 2560, ()), ("bf16", 2560, 2560, 2560, ()),

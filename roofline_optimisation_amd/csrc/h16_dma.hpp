@@ -59,7 +59,11 @@ constexpr int ring_stages(int E) { return E == 256 ? 4 : 8; }
 // C; NS ring stages; PW producer waves.  With PW = 0 every compute wave issues its share
 // of the loads beside its MFMAs (the dispatched kernels); with PW > 0 only the PW
 // producer waves load and the compute waves only read fragments and multiply.
-template <int EM, int EN, int WM, int WN, int NS, int PW>
+// EML, ENL: the extents the operands are loaded and laid out in LDS with, when they differ
+// from the tile's (an m/n-contiguous operand of extent 192 is loaded 256 wide: its rows of
+// 24 chunks would not map onto themselves under the ring's XOR swizzle; the last 64
+// columns of each row are loaded but never read).
+template <int EM, int EN, int WM, int WN, int NS, int PW, int EML = EM, int ENL = EN>
 struct Geo {
     static constexpr int kCW = WM * WN;                   // compute waves
     static constexpr int kLW = PW > 0 ? PW : kCW;         // waves that issue the loads
@@ -67,7 +71,7 @@ struct Geo {
     static constexpr int kNs = NS;
     static constexpr int kTM = EM / WM, kTN = EN / WN;    // wave tile
     static constexpr int kMB = kTM / 16, kNB = kTN / 16;  // accumulator quads per wave
-    static constexpr int kStageA = EM * kBK * 2, kStageB = EN * kBK * 2;  // bytes per stage
+    static constexpr int kStageA = EML * kBK * 2, kStageB = ENL * kBK * 2;  // bytes per stage
     static constexpr int kBOff = NS * kStageA;            // the B ring follows the A ring
     static constexpr int kLds = NS * (kStageA + kStageB);
     // MFMAs per k-step, the step's wait and barrier after kBarrier of them, its loads
@@ -444,17 +448,19 @@ __device__ __forceinline__ void store_tile(floatx4 (&acc)[kMB][kNB], float *__re
 // whole trip, every chunk at k >= K loads as zeros (DmaOp::issue), and the k-steps of the
 // last trip that lie wholly at k >= K are skipped.
 template <typename T, bool A_MN, bool B_MN, int EPI, int EM, int EN, int WM, int WN, int NS, int PW,
-          bool WHOLE = false, bool KR = false>
+          bool WHOLE = false, bool KR = false, int EML = EM, int ENL = EN>
 __device__ __forceinline__ void dma_tile(int M, int N, int K, const uint16_t *__restrict__ A, int lda,
                                          const uint16_t *__restrict__ B, int ldb,
                                          float *__restrict__ C, int ldc, float sign,
                                          int flags, int m0, int n0, char *lds_raw) {
     // the producer waves run every k-step's barrier; they do not skip the tail's steps
     static_assert(!(KR && PW > 0), "K past whole ring trips needs the compute waves to load");
-    using G = Geo<EM, EN, WM, WN, NS, PW>;
+    using G = Geo<EM, EN, WM, WN, NS, PW, EML, ENL>;
     constexpr int kMB = G::kMB, kNB = G::kNB, kBOff = G::kBOff, kNs = NS, kLW = G::kLW;
-    using OA = DmaOp<A_MN, EM, kLW, NS, kMB>;
-    using OB = DmaOp<B_MN, EN, kLW, NS, kNB>;
+    static_assert((EML == EM || (A_MN && EML == 256)) && (ENL == EN || (B_MN && ENL == 256)),
+                  "only an m/n-contiguous operand is loaded wider than the tile");
+    using OA = DmaOp<A_MN, EML, kLW, NS, kMB>;
+    using OB = DmaOp<B_MN, ENL, kLW, NS, kNB>;
     using PO = PieceOrder<A_MN, B_MN, kMB, kNB>;
     const int lane = threadIdx.x % 64;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
@@ -699,25 +705,24 @@ void mfma_f16_dma_kernel(int M, int N, int K, const uint16_t *__restrict__ A, in
 
 // 192 x 256 and 256 x 192 tiles, for products whose 256 x 256 grid leaves CUs idle where
 // a grid with one extent of 192 fills them (3072^2: 192 tiles instead of 144; 4096 x 3072:
-// 256 instead of 192).  The 192 extent belongs to a k-contiguous operand: A (EM = 192, B in
-// either layout) or B (EN = 192, A in either layout); an m/n-contiguous operand would need
-// 192-element LDS rows, 24 chunks, which the ring's XOR swizzle of chunk slots does not map
-// onto themselves.  The same tile routine on four waves of 96 x 128 or 128 x 96, one
-// workgroup per CU (112 KiB of LDS); every epilogue kind is taken.
+// 256 instead of 192).  The same tile routine on four waves of 96 x 128 or 128 x 96, one
+// workgroup per CU; every epilogue kind is taken.  A k-contiguous operand on the 192 side
+// is loaded 192 rows deep (112 KiB of LDS); an m/n-contiguous one is loaded 256 wide (128
+// KiB), since rows of 24 chunks would not map onto themselves under the ring's swizzle.
 // KR: K not a whole number of ring trips (the last trip's chunks past K load as zeros).
 template <typename T, bool A_MN, bool B_MN, int EPI, int EM, int EN, bool KR = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1)))
 void mfma_f16_dma_rect_kernel(int M, int N, int K, const uint16_t *__restrict__ A, int lda,
                               const uint16_t *__restrict__ B, int ldb, float *__restrict__ C,
                               int ldc, float sign, int flags) {
-    static_assert((EM == 192 && EN == 256 && !A_MN) || (EM == 256 && EN == 192 && !B_MN),
-                  "the 192 extent on a k-contiguous operand");
+    static_assert((EM == 192 && EN == 256) || (EM == 256 && EN == 192), "one extent of 192");
     constexpr int kNs = dma::ring_stages(256);
-    __shared__ __attribute__((aligned(1024))) char lds[dma::Geo<EM, EN, 2, 2, kNs, 0>::kLds];
+    constexpr int kEML = A_MN ? 256 : EM, kENL = B_MN ? 256 : EN;
+    __shared__ __attribute__((aligned(1024))) char lds[dma::Geo<EM, EN, 2, 2, kNs, 0, kEML, kENL>::kLds];
     int tm, tn;
     grouped_tile(xcd_contiguous_id(blockIdx.x, gridDim.x), cdiv(M, EM), cdiv(N, EN), 4, tm, tn);
-    dma::dma_tile<T, A_MN, B_MN, EPI, EM, EN, 2, 2, kNs, 0, false, KR>(M, N, K, A, lda, B, ldb, C, ldc, sign,
-                                                                       flags, tm * EM, tn * EN, lds);
+    dma::dma_tile<T, A_MN, B_MN, EPI, EM, EN, 2, 2, kNs, 0, false, KR, kEML, kENL>(
+        M, N, K, A, lda, B, ldb, C, ldc, sign, flags, tm * EM, tn * EN, lds);
 }
 
 // Schedules of the same data movement that are kept for measurement (gemm355_run_variant

@@ -165,13 +165,13 @@ def test_dispatch_choices_general_form(lib):
     # with K a multiple of 8 the direct-to-LDS kernel zero-fills past K in every layout
     assert dx(-1, 1, gb.TRANS_A | gb.TRANS_B, 1000, 1000, 1000, P, 1000, P, 1000, P, 1000) == \
         "mfma_f16 128x128x32 w2x2 lds-dma k-zero-fill"
-    # the 192 x 256 tile takes B in either layout and every epilogue (signed, accumulating,
-    # 16-bit C); with B transposed (k-contiguous) the 256 x 192 tile takes A in either
-    # layout; a transposed A with B n-contiguous keeps the 256 x 256 tile
+    # the 192 x 256 and 256 x 192 tiles take every layout (an m/n-contiguous operand of
+    # extent 192 is loaded 256 wide) and every epilogue (signed, accumulating, 16-bit C);
+    # between equal grids the one whose 192 side is k-contiguous wins, then 192 x 256
     assert dx(-1, 1, gb.TRANS_B, 3072, 3072, 3072, P, 3072, P, 3072, P, 3072) == \
         "mfma_f16 192x256x32 w2x2 lds-dma"
     assert dx(-1, 1, gb.TRANS_A, 3072, 3072, 3072, P, 3072, P, 3072, P, 3072) == \
-        "mfma_f16 256x256x32 w2x2 lds-dma"
+        "mfma_f16 192x256x32 w2x2 lds-dma"
     assert dx(-1, 2, gb.NEG_A, 3072, 3072, 3072, P, 3072, P, 3072, P, 3072) == \
         "mfma_bf16 192x256x32 w2x2 lds-dma"
     assert dx(-1, 1, gb.TRANS_B | gb.ACCUMULATE, 3072, 3072, 1000, P, 1000, P, 1000, P, 3072) == \
@@ -183,7 +183,8 @@ def test_dispatch_choices_general_form(lib):
     # 4096 x 3072: 192 tiles of 256 x 256, 264 of 192 x 256 (two rounds), 256 of 256 x 192
     assert dx(-1, 1, gb.TRANS_B, 4096, 3072, 4096, P, 4096, P, 4096, P, 3072) == \
         "mfma_f16 256x192x32 w2x2 lds-dma"
-    assert dx(-1, 1, 0, 4096, 3072, 4096, P, 4096, P, 3072, P, 3072) == "mfma_f16 256x256x32 w2x2 lds-dma"
+    assert dx(-1, 1, 0, 4096, 3072, 4096, P, 4096, P, 3072, P, 3072) == "mfma_f16 256x192x32 w2x2 lds-dma"
+    assert dx(-1, 2, gb.TRANS_A, 4096, 3072, 4096, P, 4096, P, 3072, P, 3072) == "mfma_bf16 256x192x32 w2x2 lds-dma"
     assert dx(-1, 2, gb.TRANS_A | gb.TRANS_B | gb.ACCUMULATE, 3000, 3000, 1000, P, 3000, P, 1000, P, 3000) == \
         "mfma_bf16 256x192x32 w2x2 lds-dma k-zero-fill"
     # what gemm355_gemm_ex rejects

@@ -126,10 +126,10 @@ SHAPES = {"f32": [(3072, 3072, 64), (1024, 768, 96), (2048, 2048, 64), (1536, 15
 # skipped: 2 of 4 and 7 of 8).
 # (2560, 2048, 192): 320 tiles of 128 x 128 on the direct-to-LDS kernel's 4-stage ring, two
 # workgroups per CU, K not a whole number of its trips (192 = 128 + 64).
-# (3072, 3072, 128), (3072, 2816, 192) and BF16 (3072, 3072, 256) with A not transposed
-# (B in either layout, every mode): the 192 x 256 direct-to-LDS tile, the second with K
-# not a whole number of ring trips; with both transposed the 256 x 192 tile; with A
-# transposed and B not, 256 x 256.
+# (3072, 3072, 128), (3072, 2816, 192) and BF16 (3072, 3072, 256), every layout and mode:
+# the 192 x 256 direct-to-LDS tile (with A transposed its A loaded 256 wide), the second
+# with K not a whole number of ring trips; with both transposed the 256 x 192 tile (B
+# k-contiguous on the 192 side).
 # (4000, 3992, 128) and (2000, 2040, 256): every tile, ragged ones included, on the
 # direct-to-LDS kernel (256 x 256 and 128 x 128 tiles); the padding around the operands
 # holds NaN, so a ragged tile's loads past the matrix would show in its stored outputs.
@@ -384,12 +384,17 @@ def test_matmul_wrapper_c16():
 # transposed, negated and accumulating (K not a whole number of ring trips) and with B not
 # transposed; 256 x 192 (B transposed, so k-contiguous) with A transposed, ragged M and N,
 # K not a whole number of ring trips, negated and accumulating, and plain on 4096 x 3072
-# (256 tiles against 192 of 256 x 256); each with FP32 and with 16-bit C, against the
-# oracle and bit for bit against the same call on 256 x 256 tiles (VARIANT_MFMA_T256X256).
+# (256 tiles against 192 of 256 x 256); and with the 192 side m/n-contiguous, loaded 256
+# wide: 192 x 256 with A transposed (ragged N, K past whole trips, negated B, accumulating)
+# and 256 x 192 with B n-contiguous (negated A, padded B rows, 520 = 4 x 128 + 8); each with
+# FP32 and with 16-bit C, against the oracle and bit for bit against the same call on
+# 256 x 256 tiles (VARIANT_MFMA_T256X256).
 RECT_EX = [("f16", (3072, 3072, 264), (False, True, True, False, True), (8, 8, 8), "192x256x32"),
            ("bf16", (3000, 3072, 256), (False, False, False, True, True), (0, 0, 0), "192x256x32"),
            ("bf16", (3000, 3000, 1000), (True, True, True, False, True), (8, 8, 8), "256x192x32"),
-           ("f16", (4096, 3072, 512), (False, True, False, False, False), (0, 0, 0), "256x192x32")]
+           ("f16", (4096, 3072, 512), (False, True, False, False, False), (0, 0, 0), "256x192x32"),
+           ("f16", (3072, 3000, 264), (True, False, False, True, True), (8, 8, 8), "192x256x32"),
+           ("bf16", (4096, 3072, 520), (False, False, True, False, False), (0, 8, 0), "256x192x32")]
 
 
 @pytest.mark.parametrize("case", RECT_EX, ids=lambda c: c[0] + "_" + "x".join(map(str, c[1])) + "_" + c[4][:7])
