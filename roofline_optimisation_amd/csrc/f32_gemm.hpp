@@ -413,9 +413,10 @@ struct F32Pick {
 };
 
 // Whether the unpredicated kernel may take every tile, ragged ones included: K a whole
-// number of k-steps, rows 16-byte aligned, m/n-contiguous extents whole 16-byte chunks.
-inline bool f32_cover_all(const GemmArgs &g, bool vec) {
-    return g.K % kBK == 0 && vec && (!g.trans_a || g.M % 4 == 0) && (g.trans_b || g.N % 4 == 0);
+// number of k-steps and m/n-contiguous extents whole 4-element chunks (rows 16-byte
+// aligned load each chunk with one dwordx4, other rows with four dword loads).
+inline bool f32_cover_all(const GemmArgs &g) {
+    return g.K % kBK == 0 && (!g.trans_a || g.M % 4 == 0) && (g.trans_b || g.N % 4 == 0);
 }
 
 // The same with a K tail (K a multiple of 4 but not of BK): the KT kernel.
@@ -433,7 +434,7 @@ inline F32Pick pick_f32(const GemmArgs &g) {
     struct Opt { int tile; double eff; };
     const Opt opts[] = {{192, 0.95}, {128, 0.95}, {96, 0.93}, {64, 0.85}};
     const bool vec = rows_aligned16(g.A, g.lda, 4) && rows_aligned16(g.B, g.ldb, 4);
-    const bool cover = f32_cover_all(g, vec) || f32_ktail(g, vec);
+    const bool cover = f32_cover_all(g) || f32_ktail(g, vec);
     double best = -1.0;
     int tile = 64;
     for (const Opt &o : opts) {
@@ -486,10 +487,11 @@ hipError_t launch_cfg(const GemmArgs &g, bool vec, hipStream_t s) {
             return launch_one<BM, BN, WM, WN, MINW, 2, false, false, A_MN, B_MN, ACC, true>(
                 g, cdiv(g.M, BM) * cdiv(g.N, BN), 1, s);
     }
-    if (!INTERIOR && f32_cover_all(g, vec) && edge_tiles > 0) {
+    if (!INTERIOR && f32_cover_all(g) && edge_tiles > 0) {
         // every tile in one unpredicated launch (ragged tiles clamped, stores guarded)
         if constexpr (!INTERIOR) {
             const int all = cdiv(g.M, BM) * cdiv(g.N, BN);
+            if (!vec) return launch_one<BM, BN, WM, WN, MINW, 0, false, false, A_MN, B_MN, ACC>(g, all, 1, s);
             if (fits && (g.K / kBK) % 2 == 0)
                 return launch_one<BM, BN, WM, WN, MINW, 2, false, true, A_MN, B_MN, ACC>(g, all, 1, s);
             if (fits) return launch_one<BM, BN, WM, WN, MINW, 2, false, false, A_MN, B_MN, ACC>(g, all, 1, s);

@@ -379,20 +379,26 @@ def test_h16_clamped_ragged(dtype, case):
         assert ok and np.array_equal(Ci, C32)
 
 
-# FP32 with rows that are not 16-byte aligned and ragged M and N: when every tile fits in
-# two rounds the predicated kernel takes the interior tiles too, in one launch.
-@pytest.mark.parametrize("case", [((1000, 1000, 1024), (1, 0, 0)), ((700, 650, 96), (1, 3, 0))],
+# FP32 with rows that are not 16-byte aligned and ragged M and N, in one launch: with K a
+# multiple of 32 and N of 4 the unpredicated kernel takes every tile with dword loads at
+# clamped coordinates (1000 x 1000 x 1024, 4000^3 and 3000 x 3000 x 3008 sampled); with N
+# not a multiple of 4, when every tile fits in two rounds, the predicated kernel takes the
+# interior tiles too (700 x 650 x 96).
+@pytest.mark.parametrize("case", [((1000, 1000, 1024), (1, 0, 0)), ((700, 650, 96), (1, 3, 0)),
+                                  ((4000, 4000, 4000), (1, 1, 0)), ((3000, 3000, 3008), (1, 1, 1))],
                          ids=lambda c: "x".join(map(str, c[0])) + f"_pad{c[1][0]}{c[1][1]}")
 def test_f32_ragged_one_launch(case):
     (M, N, K), pad = case
     A, B = inputs.make_operands(M, N, K, 49, "uniform", "f32")
-    C64, _ = oracle.gemm(A, B, "f32")
     C, ok = gpu_gemm(A, B, "f32", gb.VARIANT_MFMA, pad=pad, guard_rows=1)
-    check(C, C64, "f32", "uniform", K, ok, f"one-launch f32 {M}x{N}x{K} pad={pad}")
+    rows = np.arange(M) if M * N * K <= 1 << 30 else np.array(
+        sorted(set(sample_rows(M, 48).tolist()) | {M - 1, M - 2, (M // 128) * 128 - 1, (M // 192) * 192}))
+    C64, _ = oracle.gemm(np.ascontiguousarray(A[rows]), B, "f32")
+    check(C[rows], C64, "f32", "uniform", K, ok, f"one-launch f32 {M}x{N}x{K} pad={pad}")
     Ai, Bi = inputs.make_operands(M, N, K, 50, "int", "f32")
-    _, C32 = oracle.gemm(Ai, Bi, "f32")
+    _, C32 = oracle.gemm(np.ascontiguousarray(Ai[rows]), Bi, "f32")
     Ci, ok = gpu_gemm(Ai, Bi, "f32", gb.VARIANT_MFMA, pad=pad)
-    assert ok and np.array_equal(Ci, C32)
+    assert ok and np.array_equal(Ci[rows], C32)
 
 
 @pytest.mark.parametrize("case", [(384, 384, 64), (768, 384, 96), (384, 576, 3072)],
