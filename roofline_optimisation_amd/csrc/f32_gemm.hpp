@@ -110,9 +110,10 @@ __device__ __forceinline__ floatx4 ld_chunk(const float *__restrict__ row, int c
 // 2^31 bytes).  EDGE selects the predicated loads and guarded stores.  (Clamped loads
 // fixed up when staged, as in the 16-bit kernel, and 16-byte loads at 4-byte alignment
 // both measured slower here than these loads.)
-// KT (with LOAD 2, unpredicated): K is not a multiple of BK but of 4; the last k-step's
+// KT (unpredicated, LOAD 2 or 0): K is not a multiple of BK but of 4; the last k-step's
 // chunks past K load from inside the matrix (a row clamped to K-1, or 4 columns clamped
-// to K-4) and are zeroed when staged to LDS.
+// to K-4) and are zeroed when staged to LDS.  With LOAD 0 (rows not 16-byte aligned) each
+// chunk is four dword buffer loads at the same offsets.
 template <int BM, int BN, int WM, int WN, int LOAD, bool EDGE, bool PAIRED, bool A_MN, bool B_MN,
           bool ACC, bool KT = false>
 __device__ __forceinline__ void f32_tile(int M, int N, int K, const float *__restrict__ A, int lda,
@@ -181,21 +182,29 @@ __device__ __forceinline__ void f32_tile(int M, int N, int K, const float *__res
     };
 
     floatx4 st[kWr];  // staged chunks of the next k-step (A chunks first)
-    static_assert(!KT || (LOAD == 2 && !EDGE), "the K tail rides on the unpredicated buffer loads");
+    static_assert(!KT || (LOAD != 1 && !EDGE), "the K tail rides on the unpredicated buffer loads");
     auto load_one = [&](int k0, int w) {
         if constexpr (KT) {
+            // one chunk at byte offset off of a buffer: one dwordx4 (LOAD 2) or four dwords
+            const auto buf_chunk = [](__amdgpu_buffer_rsrc_t r, int off) {
+                if constexpr (LOAD == 2)
+                    return __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+                floatx4 v;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    v[e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off + 4 * e, 0, 0));
+                return v;
+            };
             // the offset carries the k position, clamped into the matrix
             if (w < kAC) {
                 const int r = A_MN ? min(k0 + a_r[w], K - 1) : a_r[w];
                 const int c = A_MN ? a_c[w] : min(k0 + a_c[w], K - 4);
-                st[w] = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                        ra, (r * lda + c) * 4, 0, 0));
+                st[w] = buf_chunk(ra, (r * lda + c) * 4);
             } else {
                 const int v = w - kAC;
                 const int r = B_MN ? min(k0 + b_r[v], K - 1) : b_r[v];
                 const int c = B_MN ? b_c[v] : min(k0 + b_c[v], K - 4);
-                st[w] = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                        rb, (r * ldb + c) * 4, 0, 0));
+                st[w] = buf_chunk(rb, (r * ldb + c) * 4);
             }
         } else if constexpr (LOAD == 2) {
             if (w < kAC)
@@ -420,9 +429,8 @@ inline bool f32_cover_all(const GemmArgs &g) {
 }
 
 // The same with a K tail (K a multiple of 4 but not of BK): the KT kernel.
-inline bool f32_ktail(const GemmArgs &g, bool vec) {
-    return g.K % kBK != 0 && g.K % 4 == 0 && vec && (!g.trans_a || g.M % 4 == 0) &&
-           (g.trans_b || g.N % 4 == 0);
+inline bool f32_ktail(const GemmArgs &g) {
+    return g.K % kBK != 0 && g.K % 4 == 0 && (!g.trans_a || g.M % 4 == 0) && (g.trans_b || g.N % 4 == 0);
 }
 
 // Cost model: tiles are spread over the 256 CUs, so a config finishes after
@@ -434,7 +442,7 @@ inline F32Pick pick_f32(const GemmArgs &g) {
     struct Opt { int tile; double eff; };
     const Opt opts[] = {{192, 0.95}, {128, 0.95}, {96, 0.93}, {64, 0.85}};
     const bool vec = rows_aligned16(g.A, g.lda, 4) && rows_aligned16(g.B, g.ldb, 4);
-    const bool cover = f32_cover_all(g) || f32_ktail(g, vec);
+    const bool cover = f32_cover_all(g) || f32_ktail(g);
     double best = -1.0;
     int tile = 64;
     for (const Opt &o : opts) {
@@ -483,9 +491,13 @@ hipError_t launch_cfg(const GemmArgs &g, bool vec, hipStream_t s) {
     const int all_flag = kfull ? 0 : 1;
     const bool fits = f32_fits(A_MN, BM, g.K, g.lda) && f32_fits(B_MN, BN, g.K, g.ldb);
     if constexpr (!INTERIOR) {
-        if (f32_ktail(g, vec) && fits)  // every tile, K tail included, in one launch
-            return launch_one<BM, BN, WM, WN, MINW, 2, false, false, A_MN, B_MN, ACC, true>(
+        if (f32_ktail(g) && fits) {  // every tile, K tail included, in one launch
+            if (vec)
+                return launch_one<BM, BN, WM, WN, MINW, 2, false, false, A_MN, B_MN, ACC, true>(
+                    g, cdiv(g.M, BM) * cdiv(g.N, BN), 1, s);
+            return launch_one<BM, BN, WM, WN, MINW, 0, false, false, A_MN, B_MN, ACC, true>(
                 g, cdiv(g.M, BM) * cdiv(g.N, BN), 1, s);
+        }
     }
     if (!INTERIOR && f32_cover_all(g) && edge_tiles > 0) {
         // every tile in one unpredicated launch (ragged tiles clamped, stores guarded)

@@ -155,10 +155,11 @@ def test_f32_both_mn_whole_192_tiles(pad, mode):
 @pytest.mark.parametrize("mode", MODES, ids=["plain", "neg_a", "neg_b_acc"])
 @pytest.mark.parametrize("layout", LAYOUTS, ids=lambda l: f"ta{int(l[0])}tb{int(l[1])}")
 def test_f32_unaligned_rows_every_tile(layout, mode):
-    """FP32 rows that are not 16-byte aligned, K a multiple of 32 and m/n-contiguous extents
+    """FP32 rows that are not 16-byte aligned, K a multiple of 4 and m/n-contiguous extents
     multiples of 4: every tile, ragged ones included, in one unpredicated launch with dword
-    loads at clamped coordinates."""
+    loads at clamped coordinates (K = 500: the last k-step zero-filled)."""
     compare(996, 1000, 512, "f32", *layout, *mode, seed=68, pad=(1, 3, 2))
+    compare(996, 1000, 500, "f32", *layout, *mode, seed=69, pad=(1, 3, 2))
 
 
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])

@@ -380,12 +380,14 @@ def test_h16_clamped_ragged(dtype, case):
 
 
 # FP32 with rows that are not 16-byte aligned and ragged M and N, in one launch: with K a
-# multiple of 32 and N of 4 the unpredicated kernel takes every tile with dword loads at
-# clamped coordinates (1000 x 1000 x 1024, 4000^3 and 3000 x 3000 x 3008 sampled); with N
+# multiple of 4 and N of 4 the unpredicated kernel takes every tile with dword loads at
+# clamped coordinates (1000 x 1000 x 1024, 4000^3 and 3000 x 3000 x 3008 sampled; K not a
+# multiple of 32, the last k-step zero-filled: 1000^3, 3000 x 2996 x 2996 sampled); with N
 # not a multiple of 4, when every tile fits in two rounds, the predicated kernel takes the
 # interior tiles too (700 x 650 x 96).
 @pytest.mark.parametrize("case", [((1000, 1000, 1024), (1, 0, 0)), ((700, 650, 96), (1, 3, 0)),
-                                  ((4000, 4000, 4000), (1, 1, 0)), ((3000, 3000, 3008), (1, 1, 1))],
+                                  ((4000, 4000, 4000), (1, 1, 0)), ((3000, 3000, 3008), (1, 1, 1)),
+                                  ((1000, 1000, 1000), (1, 1, 0)), ((3000, 2996, 2996), (3, 1, 2))],
                          ids=lambda c: "x".join(map(str, c[0])) + f"_pad{c[1][0]}{c[1][1]}")
 def test_f32_ragged_one_launch(case):
     (M, N, K), pad = case
