@@ -469,9 +469,9 @@ def _time_pair(dt, M, N, K, fl, alt, warm, rounds, reps, stream):
 
 def tile_lines(warm=300, rounds=5, reps=100):
     """Two tile classes against what the dispatcher took before them, on calls it gives
-    them: the 192 x 256 and 256 x 192 tiles against the 256 x 256 one (variant MFMA_T256X256), and the
-    two-per-CU 128 x 128 direct-to-LDS tile against the register-staged kernel (variant
-    MFMA_STAGED128).  Rounds: ceil(tiles / slots), the waves of resident work each grid
+    them: the 192 x 256 and 256 x 192 tiles against the 256 x 256 one (variant
+    MFMA_T256X256), and the two-per-CU 128 x 128 direct-to-LDS tile against the
+    register-staged kernel (variant MFMA_STAGED128).  Rounds: ceil(tiles / slots), the waves of resident work each grid
     takes (256 slots for one workgroup per CU, 512 for two)."""
     import torch
 

@@ -553,7 +553,8 @@ inline bool use_dma_rect(const GemmArgs &g, int em, int en) {
 // 50.8 against 57.0 us, 192 against 144 tiles; 6144 x 6144 x 4096: 229.6 against 263.0 us,
 // 768 against 576), or 0.85 when its 192 side is an m/n-contiguous operand loaded 256 wide
 // (FP16 3072^3 with A transposed: 52.5 against 51.6 us for the plain product on the same
-// box).  Ties keep the square tile, then 192 x 256.
+// box), so between otherwise equal grids the tile whose 192 side is k-contiguous wins.
+// Ties keep the square tile, then 192 x 256.
 inline int rect_choice(const GemmArgs &g) {
     if (g.square_tiles) return 256;
     const auto cost = [&](int em, int en) {
