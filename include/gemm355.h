@@ -97,11 +97,11 @@ typedef enum gemm355_variant {
      * MFMA_T256X128: 256 x 128 tiles on four waves (128 x 64 of C each), every wave
      *   loading: twice as many tiles, so a CU's second tile starts while the first one's
      *   stores drain.
-     * MFMA_T256X256: the dispatched kernels with the 192 x 256 direct-to-LDS tile turned
-     *   off: the 256 x 256 tile wherever the dispatcher would take 192 x 256, every other
-     *   call as dispatched (any F16 / BF16 product the dispatcher takes, gemm355_gemm_ex
-     *   flags included; the same results bit for bit, since both tiles sum each
-     *   element's K products in the same order).
+     * MFMA_T256X256: the dispatched kernels with the 192 x 256 and 256 x 192
+     *   direct-to-LDS tiles turned off: the 256 x 256 tile wherever the dispatcher would
+     *   take one of them, every other call as dispatched (any F16 / BF16 product the
+     *   dispatcher takes, gemm355_gemm_ex flags included; the same results bit for bit,
+     *   since every tile sums each element's K products in the same order).
      * MFMA_STAGED128: the dispatched kernels with the two-per-CU 128 x 128 direct-to-LDS
      *   tile turned off: grids of more than 256 128-wide tiles go to the register-staged
      *   kernel, every other call as dispatched (any F16 / BF16 product the dispatcher

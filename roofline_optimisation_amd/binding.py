@@ -21,8 +21,8 @@ F32, F16, BF16 = 0, 1, 2
 VARIANT_AUTO, VARIANT_NAIVE, VARIANT_LDS_TILED, VARIANT_REGBLOCK, VARIANT_MFMA = -1, 0, 1, 2, 3
 # measurement-only schedules of the FP16/BF16 direct-to-LDS kernel (plain products)
 VARIANT_MFMA_SPLIT, VARIANT_MFMA_W8, VARIANT_MFMA_T256X128 = 4, 5, 6
-# measurement only: the dispatched kernels without the 192 x 256 tile, or without the
-# two-per-CU 128 x 128 direct-to-LDS tile
+# measurement only: the dispatched kernels without the 192 x 256 and 256 x 192 tiles, or
+# without the two-per-CU 128 x 128 direct-to-LDS tile
 VARIANT_MFMA_T256X256, VARIANT_MFMA_STAGED128 = 7, 8
 VARIANTS = {"naive": VARIANT_NAIVE, "lds_tiled": VARIANT_LDS_TILED,
             "regblock": VARIANT_REGBLOCK, "mfma": VARIANT_MFMA, "auto": VARIANT_AUTO,

@@ -61,7 +61,7 @@ struct GemmArgs {
     // then points to uint16_t patterns and ldc counts those.
     int c16 = 0;
     // Keep the 16-bit kernels' 256 x 256 direct-to-LDS tile where the dispatcher would
-    // take the 192 x 256 one (a measurement-only variant sets it).
+    // take the 192 x 256 or 256 x 192 one (a measurement-only variant sets it).
     int square_tiles = 0;
     // Keep the 128 x 128 direct-to-LDS tile to grids of at most 256 tiles (one per CU);
     // larger grids go to the register-staged kernel (a measurement-only variant sets it).

@@ -54,7 +54,7 @@ bool valid_args(int dtype, int M, int N, int K, const void *A, int lda, const vo
 // (v_mfma_f32_32x32x2_f32 runs at the full FP32 rate); FP16/BF16 likewise.
 int auto_variant(int /*dtype*/, const GemmArgs & /*g*/) { return GEMM355_VARIANT_MFMA; }
 
-// The dispatched 16-bit kernels with the 192 x 256 tile class turned off.
+// The dispatched 16-bit kernels with the 192 x 256 and 256 x 192 tiles turned off.
 GemmArgs square(const GemmArgs &g) {
     GemmArgs h = g;
     h.square_tiles = 1;

@@ -320,8 +320,9 @@ def test_schedule_variants_contract(lib):
 
 
 def test_square_tile_variant_contract(lib):
-    """MFMA_T256X256 is the dispatcher with the 192 x 256 tile turned off: every F16 / BF16
-    product (general form included), as dispatched except that 256 x 256 replaces 192 x 256."""
+    """MFMA_T256X256 is the dispatcher with the 192 x 256 and 256 x 192 tiles turned off:
+    every F16 / BF16 product (general form included), as dispatched except that 256 x 256
+    replaces them."""
     d = gb.gemm355_kernel_desc
     v = gb.VARIANT_MFMA_T256X256
     assert gb.gemm355_variant_name(v) == "mfma_t256x256"

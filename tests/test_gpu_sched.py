@@ -89,7 +89,7 @@ def test_sched_run_twice_bitwise(variant):
     assert np.array_equal(C1.view(np.uint32), C2.view(np.uint32))
 
 
-# VARIANT_MFMA_T256X256 (the dispatcher without the 192 x 256 tile) at shapes where the
+# VARIANT_MFMA_T256X256 (the dispatcher without the 192-wide tiles) at shapes where the
 # dispatcher takes 192 x 256: the same result bit for bit as the dispatched call (both
 # tiles add each element's products in the same order), and within the bars of the
 # oracle on sampled rows; ragged M and N, K not a whole number of ring trips, padded
