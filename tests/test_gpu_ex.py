@@ -404,7 +404,10 @@ RECT_EX = [("f16", (3072, 3072, 264), (False, True, True, False, True), (8, 8, 8
            ("bf16", (3000, 3000, 1000), (True, True, True, False, True), (8, 8, 8), "256x192x32"),
            ("f16", (4096, 3072, 512), (False, True, False, False, False), (0, 0, 0), "256x192x32"),
            ("f16", (3072, 3000, 264), (True, False, False, True, True), (8, 8, 8), "192x256x32"),
-           ("bf16", (4096, 3072, 520), (False, False, True, False, False), (0, 8, 0), "256x192x32")]
+           ("bf16", (4096, 3072, 520), (False, False, True, False, False), (0, 8, 0), "256x192x32"),
+           # one ring trip exactly, and one trip plus one 8-wide chunk of K
+           ("f16", (3072, 3072, 128), (False, False, False, False, False), (0, 0, 0), "192x256x32"),
+           ("bf16", (3000, 3000, 136), (True, False, False, False, True), (8, 8, 8), "192x256x32")]
 
 
 @pytest.mark.parametrize("case", RECT_EX, ids=lambda c: c[0] + "_" + "x".join(map(str, c[1])) + "_" + c[4][:7])
