@@ -397,7 +397,7 @@ def schedule_lines(warm=300, rounds=3, reps=100):
 
 
 # Calls for which the dispatcher takes the 192 x 256 or 256 x 192 direct-to-LDS tile (the
-# last five with the 192 side m/n-contiguous, loaded 256 wide), each with the 256 x 256 tile
+# last five with the 192 side m/n-contiguous, in LDS rows of 24 chunks), each with the 256 x 256 tile
 # timed beside it: (dtype, M, N, K, gemm355_gemm_ex flags).
 TILE_SHAPES = [("f16", 3072, 3072, 3072, ()), ("bf16", 3072, 3072, 3072, ()), ("f16", 3072, 4096, 4096, ()),
                ("f16", 4096, 4104, 4096, ()), ("f16", 4608, 4608, 4608, ()), ("f16", 6144, 6144, 4096, ()),

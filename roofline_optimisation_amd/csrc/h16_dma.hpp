@@ -59,11 +59,7 @@ constexpr int ring_stages(int E) { return E == 256 ? 4 : 8; }
 // C; NS ring stages; PW producer waves.  With PW = 0 every compute wave issues its share
 // of the loads beside its MFMAs (the dispatched kernels); with PW > 0 only the PW
 // producer waves load and the compute waves only read fragments and multiply.
-// EML, ENL: the extents the operands are loaded and laid out in LDS with, when they differ
-// from the tile's (an m/n-contiguous operand of extent 192 is loaded 256 wide: its rows of
-// 24 chunks would not map onto themselves under the ring's XOR swizzle; the last 64
-// columns of each row are loaded but never read).
-template <int EM, int EN, int WM, int WN, int NS, int PW, int EML = EM, int ENL = EN>
+template <int EM, int EN, int WM, int WN, int NS, int PW>
 struct Geo {
     static constexpr int kCW = WM * WN;                   // compute waves
     static constexpr int kLW = PW > 0 ? PW : kCW;         // waves that issue the loads
@@ -71,7 +67,7 @@ struct Geo {
     static constexpr int kNs = NS;
     static constexpr int kTM = EM / WM, kTN = EN / WN;    // wave tile
     static constexpr int kMB = kTM / 16, kNB = kTN / 16;  // accumulator quads per wave
-    static constexpr int kStageA = EML * kBK * 2, kStageB = ENL * kBK * 2;  // bytes per stage
+    static constexpr int kStageA = EM * kBK * 2, kStageB = EN * kBK * 2;  // bytes per stage
     static constexpr int kBOff = NS * kStageA;            // the B ring follows the A ring
     static constexpr int kLds = NS * (kStageA + kStageB);
     // MFMAs per k-step, the step's wait and barrier after kBarrier of them, its loads
@@ -159,26 +155,43 @@ __device__ __forceinline__ lds_char *lds_reg(lds_char *p) {
 //    (t / 2) % (NS / 2).  Loading wave w fills rows [R w, +R) with R = E / LW (a multiple
 //    of 16), instruction i rows R w + 8 i + l/8, lane slot l%8 taking chunk slot ^ ((row
 //    / 2) % 8), where (row / 2) % 8 = 4 (i % 2) + l/16.
+//  * MN with E = 192 (kLin): rows of 384 bytes, 24 chunks, which the XOR keys above (up to
+//    14) would carry past the row's end.  Chunk c of row k is stored in slot c ^ 4 ((k %
+//    4) / 2) ^ 2 ((k / 8) % 2): keys below 8 keep every chunk within its aligned group of
+//    8, and since consecutive rows start 128 bytes apart modulo the 256 bytes of the 64
+//    banks, the rows of odd k cover the bank half that the even ones leave, so the eight
+//    rows a half-wave's b64 read touches (k % 4, (k / 8) % 2) still land on distinct
+//    banks.  A stage (32 x 384 bytes = 12 KiB) is filled as 12 whole 1 KiB instructions in
+//    order, wave w issuing instructions 3 w .. 3 w + 2 (rows 8 w .. 8 w + 7): lane l of
+//    instruction j fills stage chunk 64 j + l, i.e. row (64 j + l) / 24, slot (64 j + l) %
+//    24, each instruction with its own per-lane offset.
 template <bool MN, int E, int LW, int NS, int NB>
 struct DmaOp {
+    static constexpr bool kLin = MN && E == 192;
     static constexpr int kStage = E * kBK * 2;       // MN stage bytes
     static constexpr int kSlot = 2 * kStage;         // KM slot bytes
     static constexpr int kRowB = 2 * E;              // MN: bytes per LDS row (one k)
+    static constexpr int kCpr = E / 8;               // MN: 16-byte chunks per row
     static constexpr int kRpi = 1024 / kRowB;        // MN: rows one load instruction fills
     static constexpr int kRows = MN ? kBK / LW : E / LW;  // rows a loading wave fills
     // load instructions per loading wave: per k-step (MN) or per double step (KM)
-    static constexpr int kI = MN ? kRows / kRpi : kRows / 8;
+    static constexpr int kI = kLin ? kRows * kCpr / 64 : MN ? kRows / kRpi : kRows / 8;
     static_assert(kI >= 1, "every loading wave issues a whole instruction");
     // the MN swizzle XORs chunk slots with up to 14: a row needs at least 16 chunks
-    static_assert(!MN || E >= 128, "an MN operand's rows hold at least 16 chunks");
-    static_assert(!MN || (kRows * LW == kBK && kI * kRpi == kRows && 8 % kRows == 0),
+    static_assert(!MN || E == 128 || E == 256 || E == 192, "an MN operand's rows hold 16, 24 or 32 chunks");
+    static_assert(!MN || kLin || (kRows * LW == kBK && kI * kRpi == kRows && 8 % kRows == 0),
                   "an MN operand's loading wave fills rows of one (k / 8) parity");
+    static_assert(!kLin || (kRows * LW == kBK && kI * 64 == kRows * kCpr),
+                  "a 24-chunk operand's loading wave fills whole rows with whole instructions");
     static_assert(MN || (kRows * LW == E && kRows % 16 == 0), "KM rows per loading wave");
     // every ds_read immediate (slot / stage + block / row offsets) stays below 64 KiB
     static_assert(MN || (NS / 2 - 1) * kSlot + (NB - 1) * 2048 < 65536, "KM read offsets");
     static_assert(!MN || (NS - 1) * kStage + 4 * kRowB < 65536, "MN read offsets");
     int4v rsrc;
-    uint32_t voff[MN ? 2 : kI];   // per lane: MN by instruction parity, KM by instruction
+    // per lane: MN by instruction parity, KM and kLin by instruction
+    uint32_t voff[MN && !kLin ? 2 : kI];
+    // kLin: the swizzle key of row k
+    __device__ __forceinline__ static int key24(int k) { return 4 * ((k & 3) >> 1) ^ 2 * ((k >> 3) & 1); }
     lds_char *rd[MN ? NB : 2];
     H16Frag<MN, NB> fr;
 
@@ -190,7 +203,15 @@ struct DmaOp {
     // column N, which are never stored.
     __device__ __forceinline__ void init_load(const uint16_t *X, int ld, int ext, int mn0, int lw,
                                               int lane) {
-        if constexpr (MN) {
+        if constexpr (kLin) {
+            rsrc = rsrc_of(X + mn0);
+            const int last = (ext - mn0) / 8 - 1;
+#pragma unroll
+            for (int i = 0; i < kI; ++i) {
+                const int p = 64 * (kI * lw + i) + lane, row = p / kCpr, slot = p % kCpr;
+                voff[i] = (uint32_t)((row * ld + 8 * min(slot ^ key24(row), last)) * 2);
+            }
+        } else if constexpr (MN) {
             constexpr int lpr = 64 / kRpi;           // lanes per row of one load
             rsrc = rsrc_of(X + mn0);
             const int rl = lane / lpr, row = kRows * lw + rl, slot = lane % lpr;
@@ -213,13 +234,13 @@ struct DmaOp {
         if constexpr (MN) {
             // block b, piece h: lane (g = l/16, e = (l%16)/4, q = l%4) reads row 8 g + 4 h +
             // e, chunk wb/8 + 2 b + q/2, byte 8 (q%2) of it; that row's swizzle key is
-            // 4 e ^ 2 (g%2)
+            // 4 e ^ 2 (g%2) (kLin: 4 (e/2) ^ 2 (g%2)), the same for both pieces
             const int g = lane >> 4, e = (lane & 15) >> 2, q = lane & 3;
+            const int key = kLin ? key24(8 * g + e) : (4 * e) ^ (2 * (g & 1));
 #pragma unroll
             for (int b = 0; b < NB; ++b)
                 rd[b] = lds_reg(L + roff + (8 * g + e) * kRowB +
-                                16 * ((wb / 8 + 2 * b + (q >> 1)) ^ (4 * e) ^ (2 * (g & 1))) +
-                                8 * (q & 1));
+                                16 * ((wb / 8 + 2 * b + (q >> 1)) ^ key) + 8 * (q & 1));
         } else {
             // block b, half h of the slot: row wb + 16 b + l%16, chunk 4 h + l/16, whose
             // swizzle key ((l%16) / 2) % 8 does not depend on b
@@ -238,12 +259,14 @@ struct DmaOp {
     // issue's k0: MN its row, KM its chunk's first column (recomputed where needed rather
     // than held in registers across the loop).
     __device__ __forceinline__ static int kpos(int i, int lw, int lane) {
-        if constexpr (MN) return kRows * lw + kRpi * i + lane / (64 / kRpi);
+        if constexpr (kLin) return (64 * (kI * lw + i) + lane) / kCpr;
+        else if constexpr (MN) return kRows * lw + kRpi * i + lane / (64 / kRpi);
         else return 8 * ((lane & 7) ^ ((4 * (i % 2) + lane / 16) & 7));
     }
     // One past the largest k that load i of loading wave lw reads, relative to k0.
     __device__ __forceinline__ static int kend(int i, int lw) {
-        if constexpr (MN) return kRows * lw + kRpi * (i + 1);
+        if constexpr (kLin) return (64 * (kI * lw + i) + 63) / kCpr + 1;
+        else if constexpr (MN) return kRows * lw + kRpi * (i + 1);
         else return 2 * kBK;
     }
     // KR: the offset register of a chunk at k >= K is set past the buffer's range in place.
@@ -255,7 +278,7 @@ struct DmaOp {
     template <bool KR>
     __device__ __forceinline__ uint32_t off(int k0, int i, int lw, int K) {
         constexpr uint32_t kOut = 0x80000000u;   // beyond num_records (2^31 - 1)
-        uint32_t &v = voff[MN ? (i & 1) : i];
+        uint32_t &v = voff[MN && !kLin ? (i & 1) : i];
         if constexpr (KR) {
             if (k0 + kend(i, lw) > K) v = k0 + kpos(i, lw, lane_here()) < K ? v : kOut;
         }
@@ -265,7 +288,8 @@ struct DmaOp {
                                              int k0, int i, uint32_t v) {
         if constexpr (MN) {
             const uint32_t dst = lds0 + roff + place * kStage + (lw * kI + i) * 1024;
-            load_lds16(dst, v, rsrc, (uint32_t)((k0 + kRpi * i) * ld * 2));
+            // kLin: the row within the stage is in the lane's offset
+            load_lds16(dst, v, rsrc, (uint32_t)((k0 + (kLin ? 0 : kRpi * i)) * ld * 2));
         } else {
             const uint32_t dst = lds0 + roff + place * kSlot + (lw * kI + i) * 1024;
             load_lds16(dst, v, rsrc, (uint32_t)(k0 * 2));
@@ -448,19 +472,17 @@ __device__ __forceinline__ void store_tile(floatx4 (&acc)[kMB][kNB], float *__re
 // whole trip, every chunk at k >= K loads as zeros (DmaOp::issue), and the k-steps of the
 // last trip that lie wholly at k >= K are skipped.
 template <typename T, bool A_MN, bool B_MN, int EPI, int EM, int EN, int WM, int WN, int NS, int PW,
-          bool WHOLE = false, bool KR = false, int EML = EM, int ENL = EN>
+          bool WHOLE = false, bool KR = false>
 __device__ __forceinline__ void dma_tile(int M, int N, int K, const uint16_t *__restrict__ A, int lda,
                                          const uint16_t *__restrict__ B, int ldb,
                                          float *__restrict__ C, int ldc, float sign,
                                          int flags, int m0, int n0, char *lds_raw) {
     // the producer waves run every k-step's barrier; they do not skip the tail's steps
     static_assert(!(KR && PW > 0), "K past whole ring trips needs the compute waves to load");
-    using G = Geo<EM, EN, WM, WN, NS, PW, EML, ENL>;
+    using G = Geo<EM, EN, WM, WN, NS, PW>;
     constexpr int kMB = G::kMB, kNB = G::kNB, kBOff = G::kBOff, kNs = NS, kLW = G::kLW;
-    static_assert((EML == EM || (A_MN && EML == 256)) && (ENL == EN || (B_MN && ENL == 256)),
-                  "only an m/n-contiguous operand is loaded wider than the tile");
-    using OA = DmaOp<A_MN, EML, kLW, NS, kMB>;
-    using OB = DmaOp<B_MN, ENL, kLW, NS, kNB>;
+    using OA = DmaOp<A_MN, EM, kLW, NS, kMB>;
+    using OB = DmaOp<B_MN, EN, kLW, NS, kNB>;
     using PO = PieceOrder<A_MN, B_MN, kMB, kNB>;
     const int lane = threadIdx.x % 64;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
@@ -706,9 +728,9 @@ void mfma_f16_dma_kernel(int M, int N, int K, const uint16_t *__restrict__ A, in
 // 192 x 256 and 256 x 192 tiles, for products whose 256 x 256 grid leaves CUs idle where
 // a grid with one extent of 192 fills them (3072^2: 192 tiles instead of 144; 4096 x 3072:
 // 256 instead of 192).  The same tile routine on four waves of 96 x 128 or 128 x 96, one
-// workgroup per CU; every epilogue kind is taken.  A k-contiguous operand on the 192 side
-// is loaded 192 rows deep (112 KiB of LDS); an m/n-contiguous one is loaded 256 wide (128
-// KiB), since rows of 24 chunks would not map onto themselves under the ring's swizzle.
+// workgroup per CU; every epilogue kind is taken.  The operand on the 192 side takes 192
+// rows (k-contiguous) or 192-element rows of 24 chunks (m/n-contiguous) per k-step, 112 KiB
+// of LDS in all.
 // KR: K not a whole number of ring trips (the last trip's chunks past K load as zeros).
 template <typename T, bool A_MN, bool B_MN, int EPI, int EM, int EN, bool KR = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1)))
@@ -717,11 +739,10 @@ void mfma_f16_dma_rect_kernel(int M, int N, int K, const uint16_t *__restrict__ 
                               int ldc, float sign, int flags) {
     static_assert((EM == 192 && EN == 256) || (EM == 256 && EN == 192), "one extent of 192");
     constexpr int kNs = dma::ring_stages(256);
-    constexpr int kEML = A_MN ? 256 : EM, kENL = B_MN ? 256 : EN;
-    __shared__ __attribute__((aligned(1024))) char lds[dma::Geo<EM, EN, 2, 2, kNs, 0, kEML, kENL>::kLds];
+    __shared__ __attribute__((aligned(1024))) char lds[dma::Geo<EM, EN, 2, 2, kNs, 0>::kLds];
     int tm, tn;
     grouped_tile(xcd_contiguous_id(blockIdx.x, gridDim.x), cdiv(M, EM), cdiv(N, EN), 4, tm, tn);
-    dma::dma_tile<T, A_MN, B_MN, EPI, EM, EN, 2, 2, kNs, 0, false, KR, kEML, kENL>(
+    dma::dma_tile<T, A_MN, B_MN, EPI, EM, EN, 2, 2, kNs, 0, false, KR>(
         M, N, K, A, lda, B, ldb, C, ldc, sign, flags, tm * EM, tn * EN, lds);
 }
 

@@ -535,32 +535,31 @@ inline bool use_dma(const GemmArgs &g, int tile) {
 
 // The EM x EN direct-load tile with one extent of 192 (192 x 256 or 256 x 192, any layout
 // and epilogue) on the same terms as the 256 x 256 one: rows 16-byte aligned, K a multiple
-// of 8 and at least one ring trip, every byte offset within 31 bits (an m/n-contiguous
-// operand is loaded 256 wide), and an m/n-contiguous operand's extent a multiple of 8.
+// of 8 and at least one ring trip, every byte offset within 31 bits, and an m/n-contiguous
+// operand's extent a multiple of 8.
 inline bool use_dma_rect(const GemmArgs &g, int em, int en) {
     if ((g.trans_a && g.M % 8 != 0) || (!g.trans_b && g.N % 8 != 0)) return false;
     const int trip = dma::kBK * dma::ring_stages(256);
     const int kpad = cdiv(g.K, trip) * trip;
-    // an m/n-contiguous operand is loaded 256 wide
-    const int eml = g.trans_a ? 256 : em, enl = g.trans_b ? en : 256;
     return h16_vec(g) && g.K >= trip && g.K % 8 == 0 && g.M >= em && g.N >= en &&
-           op_fits(g.trans_a != 0, eml, kpad, g.lda) && op_fits(g.trans_b == 0, enl, kpad, g.ldb);
+           op_fits(g.trans_a != 0, em, kpad, g.lda) && op_fits(g.trans_b == 0, en, kpad, g.ldb);
 }
 
 // Which tile a product headed for 256 x 256 tiles takes: 256 (the square tile), 192 (192 x
 // 256) or -192 (256 x 192), by rounds of resident tiles (one per CU) times tile area, a
 // tile with a 192 extent at 0.87 of the square one's rate per unit of area (FP16 3072^3:
 // 50.8 against 57.0 us, 192 against 144 tiles; 6144 x 6144 x 4096: 229.6 against 263.0 us,
-// 768 against 576), or 0.85 when its 192 side is an m/n-contiguous operand loaded 256 wide
-// (FP16 3072^3 with A transposed: 52.5 against 51.6 us for the plain product on the same
-// box), so between otherwise equal grids the tile whose 192 side is k-contiguous wins.
+// 768 against 576), or 0.85 when its 192 side is an m/n-contiguous operand, so that between
+// otherwise equal grids the tile whose 192 side is k-contiguous wins (A and B both
+// transposed, K-contiguous 192 side against m/n-contiguous: FP16 3072^2 x 4096 65.1 against
+// 67.3 us, BF16 61.7 against 65.3, BF16 3000^2 x 1000 accumulating 31.5 against 35.5).
 // Ties keep the square tile, then 192 x 256.
 inline int rect_choice(const GemmArgs &g) {
     if (g.square_tiles) return 256;
     const auto cost = [&](int em, int en) {
         const long t = (long)cdiv(g.M, em) * cdiv(g.N, en);
-        const bool wide = em == 192 ? g.trans_a != 0 : g.trans_b == 0;  // loaded 256 wide
-        return (double)((t + 255) / 256) * em * en / (em == en ? 1.0 : wide ? 0.85 : 0.87);
+        const bool mn192 = em == 192 ? g.trans_a != 0 : g.trans_b == 0;  // 192 side m/n-contiguous
+        return (double)((t + 255) / 256) * em * en / (em == en ? 1.0 : mn192 ? 0.85 : 0.87);
     };
     int best = 256;
     double c = cost(256, 256);

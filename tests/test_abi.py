@@ -166,8 +166,8 @@ def test_dispatch_choices_general_form(lib):
     assert dx(-1, 1, gb.TRANS_A | gb.TRANS_B, 1000, 1000, 1000, P, 1000, P, 1000, P, 1000) == \
         "mfma_f16 128x128x32 w2x2 lds-dma k-zero-fill"
     # the 192 x 256 and 256 x 192 tiles take every layout (an m/n-contiguous operand of
-    # extent 192 is loaded 256 wide) and every epilogue (signed, accumulating, 16-bit C);
-    # between equal grids the one whose 192 side is k-contiguous wins, then 192 x 256
+    # extent 192 in LDS rows of 24 chunks) and every epilogue (signed, accumulating, 16-bit
+    # C); between equal grids the one whose 192 side is k-contiguous wins, then 192 x 256
     assert dx(-1, 1, gb.TRANS_B, 3072, 3072, 3072, P, 3072, P, 3072, P, 3072) == \
         "mfma_f16 192x256x32 w2x2 lds-dma"
     assert dx(-1, 1, gb.TRANS_A, 3072, 3072, 3072, P, 3072, P, 3072, P, 3072) == \

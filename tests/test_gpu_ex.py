@@ -127,7 +127,7 @@ SHAPES = {"f32": [(3072, 3072, 64), (1024, 768, 96), (2048, 2048, 64), (1536, 15
 # (2560, 2048, 192): 320 tiles of 128 x 128 on the direct-to-LDS kernel's 4-stage ring, two
 # workgroups per CU, K not a whole number of its trips (192 = 128 + 64).
 # (3072, 3072, 128), (3072, 2816, 192) and BF16 (3072, 3072, 256), every layout and mode:
-# the 192 x 256 direct-to-LDS tile (with A transposed its A loaded 256 wide), the second
+# the 192 x 256 direct-to-LDS tile (with A transposed its A in LDS rows of 24 chunks), the second
 # with K not a whole number of ring trips; with both transposed the 256 x 192 tile (B
 # k-contiguous on the 192 side).
 # (4000, 3992, 128) and (2000, 2040, 256): every tile, ragged ones included, on the
