@@ -155,19 +155,20 @@ __device__ __forceinline__ lds_char *lds_reg(lds_char *p) {
 //    (t / 2) % (NS / 2).  Loading wave w fills rows [R w, +R) with R = E / LW (a multiple
 //    of 16), instruction i rows R w + 8 i + l/8, lane slot l%8 taking chunk slot ^ ((row
 //    / 2) % 8), where (row / 2) % 8 = 4 (i % 2) + l/16.
-//  * MN with E = 192 (kLin): rows of 384 bytes, 24 chunks, which the XOR keys above (up to
-//    14) would carry past the row's end.  Chunk c of row k is stored in slot c ^ 4 ((k %
-//    4) / 2) ^ 2 ((k / 8) % 2): keys below 8 keep every chunk within its aligned group of
-//    8, and since consecutive rows start 128 bytes apart modulo the 256 bytes of the 64
-//    banks, the rows of odd k cover the bank half that the even ones leave, so the eight
-//    rows a half-wave's b64 read touches (k % 4, (k / 8) % 2) still land on distinct
-//    banks.  A stage (32 x 384 bytes = 12 KiB) is filled as 12 whole 1 KiB instructions in
-//    order, wave w issuing instructions 3 w .. 3 w + 2 (rows 8 w .. 8 w + 7): lane l of
-//    instruction j fills stage chunk 64 j + l, i.e. row (64 j + l) / 24, slot (64 j + l) %
-//    24, each instruction with its own per-lane offset.
+//  * MN with E = 192 or 64 (kLin): rows of 384 or 128 bytes, 24 or 8 chunks, which the XOR
+//    keys above (up to 14) would carry past the row's end.  Chunk c of row k is stored in
+//    slot c ^ 4 ((k % 4) / 2) ^ 2 ((k / 8) % 2): keys below 8 keep every chunk within its
+//    aligned group of 8, and since consecutive rows start 128 bytes apart modulo the 256
+//    bytes of the 64 banks, the rows of odd k cover the bank half that the even ones
+//    leave, so the eight rows a half-wave's b64 read touches (k % 4, (k / 8) % 2) still
+//    land on distinct banks.  A stage (32 rows: 12 or 4 KiB) is filled as whole 1 KiB
+//    instructions in order, wave w issuing instructions kI w .. kI w + kI - 1 (rows 8 w ..
+//    8 w + 7; kI = 3 or 1): lane l of instruction j fills stage chunk 64 j + l, i.e. row
+//    (64 j + l) / (E / 8), slot (64 j + l) % (E / 8), each instruction with its own
+//    per-lane offset.
 template <bool MN, int E, int LW, int NS, int NB>
 struct DmaOp {
-    static constexpr bool kLin = MN && E == 192;
+    static constexpr bool kLin = MN && (E == 64 || E == 192);
     static constexpr int kStage = E * kBK * 2;       // MN stage bytes
     static constexpr int kSlot = 2 * kStage;         // KM slot bytes
     static constexpr int kRowB = 2 * E;              // MN: bytes per LDS row (one k)
@@ -178,11 +179,11 @@ struct DmaOp {
     static constexpr int kI = kLin ? kRows * kCpr / 64 : MN ? kRows / kRpi : kRows / 8;
     static_assert(kI >= 1, "every loading wave issues a whole instruction");
     // the MN swizzle XORs chunk slots with up to 14: a row needs at least 16 chunks
-    static_assert(!MN || E == 128 || E == 256 || E == 192, "an MN operand's rows hold 16, 24 or 32 chunks");
+    static_assert(!MN || E == 64 || E == 128 || E == 192 || E == 256, "an MN operand's rows hold 8, 16, 24 or 32 chunks");
     static_assert(!MN || kLin || (kRows * LW == kBK && kI * kRpi == kRows && 8 % kRows == 0),
                   "an MN operand's loading wave fills rows of one (k / 8) parity");
     static_assert(!kLin || (kRows * LW == kBK && kI * 64 == kRows * kCpr),
-                  "a 24-chunk operand's loading wave fills whole rows with whole instructions");
+                  "an 8- or 24-chunk operand's loading wave fills whole rows with whole instructions");
     static_assert(MN || (kRows * LW == E && kRows % 16 == 0), "KM rows per loading wave");
     // every ds_read immediate (slot / stage + block / row offsets) stays below 64 KiB
     static_assert(MN || (NS / 2 - 1) * kSlot + (NB - 1) * 2048 < 65536, "KM read offsets");

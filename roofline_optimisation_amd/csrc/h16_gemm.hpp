@@ -528,7 +528,7 @@ inline bool use_dma(const GemmArgs &g, int tile) {
     // load straddles the end of its last row
     if ((g.trans_a && g.M % 8 != 0) || (!g.trans_b && g.N % 8 != 0)) return false;
     const int kpad = cdiv(g.K, trip) * trip;
-    return (tile == 256 || tile == 128) && h16_vec(g) && g.K >= trip && g.K % 8 == 0 &&
+    return (tile == 256 || tile == 128 || tile == 64) && h16_vec(g) && g.K >= trip && g.K % 8 == 0 &&
            g.M >= tile && g.N >= tile && op_fits(g.trans_a != 0, tile, kpad, g.lda) &&
            op_fits(g.trans_b == 0, tile, kpad, g.ldb);
 }
@@ -681,7 +681,7 @@ hipError_t launch_dma(const GemmArgs &g, hipStream_t s) {
 template <typename T, int BM, int BN, int WM, int WN, int MINW, bool A_MN, bool B_MN, int EPI>
 hipError_t launch_cfg(const GemmArgs &g, hipStream_t s) {
     const H16Plan p = plan_cfg(BM, BN, A_MN, B_MN, EPI, g);
-    if constexpr (BM == BN && BM >= 128) {
+    if constexpr (BM == BN && BM >= 64) {
         if (p.dma) {
             if constexpr (BM == 128)
                 if (dma_stages(g, BM) == 4) return launch_dma<T, A_MN, B_MN, EPI, BM, 4>(g, s);

@@ -38,7 +38,7 @@ const char *desc_mfma_f16(int dtype, const GemmArgs &g) {
     }
     const H16Plan p = plan_cfg(bm, bn, g.trans_a != 0, g.trans_b == 0, epi, g);
     if (p.dma) {
-        out += big ? " 256x256x32 w2x2 lds-dma" : " 128x128x32 w2x2 lds-dma";
+        out += big ? " 256x256x32 w2x2 lds-dma" : (small ? " 64x64x32 w2x2 lds-dma" : " 128x128x32 w2x2 lds-dma");
         if (!big && dma_stages(g, bm) == 4) out += " ring4";
         if (dma_ragged_k(g, bm)) out += " k-zero-fill";
         return out.c_str();

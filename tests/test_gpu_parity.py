@@ -463,9 +463,11 @@ def test_f32_tile_classes(case):
 
 
 # FP16/BF16 tile classes of plain products: 64 x 64 (the 128 x 64 tiling would still leave
-# CUs idle; interior, ragged, K tail), 128 x 64 (the 128 x 128 tiling would; interior and
+# CUs idle) register-staged (K below one ring trip of 256 or not a multiple of 8; interior,
+# ragged, K tail) and direct-to-LDS, 128 x 64 (the 128 x 128 tiling would; interior and
 # ragged), 128 x 128, 256 x 256 direct-to-LDS.
-H16_TILE_CASES = [("f16", (1024, 1024, 256), "64x64x64 w1x2"), ("bf16", (1000, 900, 200), "64x64x64 w1x2"),
+H16_TILE_CASES = [("f16", (1024, 1024, 128), "64x64x64 w1x2"), ("f16", (1024, 1024, 256), "64x64x32 w2x2 lds-dma"),
+                  ("bf16", (1000, 900, 200), "64x64x64 w1x2"),
                   ("f16", (512, 512, 100), "64x64x64 w1x2"), ("bf16", (1536, 1536, 128), "128x64x64"),
                   ("f16", (1500, 1450, 200), "128x64x64"), ("bf16", (2048, 2048, 128), "128x128"),
                   ("f16", (3072, 3072, 128), "lds-dma")]
@@ -536,6 +538,35 @@ def test_dma_128_two_per_cu(case):
     _, C32 = oracle.gemm(Ai, Bi, dtype)
     Ci, ok = gpu_gemm(Ai, Bi, dtype, entry="typed", pad=pad)
     assert ok and np.array_equal(Ci, C32), f"128 ring4 dma {dtype} {M}x{N}x{K} integers not bit-exact"
+
+
+# The 64 x 64 direct-to-LDS tile (plain products whose 128 x 64 grid would leave CUs idle,
+# K a multiple of 8 and at least one 256-deep ring trip): a single tile, whole tiles, ragged
+# M (1000 = 15 x 64 + 40) and N (904 = 14 x 64 + 8: a last tile one 16-byte chunk wide)
+# with NaN-padded strides and K not a whole number of trips (1000 = 3 x 256 + 232, 264 =
+# 256 + 8), and a deep K (4096).
+DMA64_CASES = [("f16", (64, 64, 256), (0, 0, 0), "mfma_f16 64x64x32 w2x2 lds-dma"),
+               ("f16", (1024, 1024, 1024), (0, 0, 0), "mfma_f16 64x64x32 w2x2 lds-dma"),
+               ("bf16", (1000, 904, 1000), (8, 8, 8), "mfma_bf16 64x64x32 w2x2 lds-dma k-zero-fill"),
+               ("bf16", (512, 512, 264), (8, 0, 8), "mfma_bf16 64x64x32 w2x2 lds-dma k-zero-fill"),
+               ("f16", (520, 1000, 4096), (0, 8, 0), "mfma_f16 64x64x32 w2x2 lds-dma")]
+
+
+@pytest.mark.parametrize("case", DMA64_CASES, ids=lambda c: c[0] + "_" + "x".join(map(str, c[1])) + f"_pad{c[2][0]}")
+def test_dma_64_tile(case):
+    dtype, (M, N, K), pad, kernel = case
+    P = 1 << 20  # a 16-byte-aligned address: the query only inspects it
+    desc = gb.gemm355_kernel_desc(gb.VARIANT_AUTO, gb.DTYPE_CODES[dtype], M, N, K, P, K + pad[0],
+                                  P, N + pad[1], P, N + pad[2])
+    assert desc == kernel, desc
+    A, B = inputs.make_operands(M, N, K, 87, "uniform", dtype)
+    C, ok = gpu_gemm(A, B, dtype, entry="typed", pad=pad, guard_rows=1)
+    C64, _ = oracle.gemm(A, B, dtype)
+    check(C, C64, dtype, "uniform", K, ok, f"64 dma {dtype} {M}x{N}x{K} pad={pad}")
+    Ai, Bi = inputs.make_operands(M, N, K, 88, "int", dtype)
+    _, C32 = oracle.gemm(Ai, Bi, dtype)
+    Ci, ok = gpu_gemm(Ai, Bi, dtype, entry="typed", pad=pad)
+    assert ok and np.array_equal(Ci, C32), f"64 dma {dtype} {M}x{N}x{K} integers not bit-exact"
 
 
 # The direct-to-LDS kernel with K not a whole number of its ring trips (128 for 256-wide
