@@ -39,7 +39,8 @@
 // The tile routine is written over a general geometry (an EM x EN tile, WM x WN compute
 // waves, NS ring stages, PW producer waves) so that other schedules of the same data
 // movement can be built and measured against the dispatched one: the dispatched kernels
-// are EM = EN = 256 or 128 and EM x EN = 192 x 256 or 256 x 192, on 2 x 2 waves that all load; mfma_f16_dma_sched_kernel
+// are EM = EN = 256, 128 or 64 and EM x EN = 192 x 256 or 256 x 192, on 2 x 2 waves that
+// all load; mfma_f16_dma_sched_kernel
 // instantiates the others (wave specialisation with producer waves, eight waves, 256 x
 // 128 tiles).
 #pragma once
@@ -49,10 +50,11 @@ namespace dma {
 constexpr int kBK = 32;
 
 // Ring stages (32-wide k-steps) of a tile whose operands have extent E, one workgroup per
-// CU: 4 of 16 KiB per operand for 256-wide tiles, 8 of 8 KiB for 128-wide ones.  A
-// 128-wide tile's k-step is a quarter of a 256-wide one's arithmetic (16 MFMAs per wave,
-// ~130 ns), so its ring is twice as deep to keep the loads as far ahead in time.  (With two
-// 128-wide workgroups per CU each k-step takes twice as long, and 4 stages, 64 KiB, do.)
+// CU: 4 of 16 KiB per operand for 256-wide tiles, 8 of 8 KiB for 128-wide ones (8 of 4 KiB
+// for 64-wide ones).  A 128-wide tile's k-step is a quarter of a 256-wide one's arithmetic
+// (16 MFMAs per wave, ~130 ns), so its ring is twice as deep to keep the loads as far ahead
+// in time.  (With two 128-wide workgroups per CU each k-step takes twice as long, and 4
+// stages, 64 KiB, do.)
 constexpr int ring_stages(int E) { return E == 256 ? 4 : 8; }
 
 // Geometry of an EM x EN tile: WM x WN compute waves, each owning (EM / WM) x (EN / WN) of

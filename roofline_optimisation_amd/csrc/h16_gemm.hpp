@@ -757,8 +757,24 @@ inline bool use_128x64(const GemmArgs &g) {
 // When even the 128 x 64 tiling leaves CUs idle, 64 x 64 tiles on two waves (64 x 32 of C
 // each): half the operand bytes per CU, and at these sizes the CU's load path, not its
 // matrix cores, sets the time (BF16 1024^3: 7.2 against 7.9 us; 512^3: 4.8 against 5.3).
+// The register-staged kernel's tile, for the calls the direct-to-LDS 64 x 64 tile does not
+// take (rows not 16-byte aligned, K not a multiple of 8 or below 256).
 inline bool use_64x64(const GemmArgs &g) {
     return (long)cdiv(g.M, 128) * cdiv(g.N, 64) < 256;
+}
+
+// The 64 x 64 direct-to-LDS tile (8-stage ring, 64 KiB of LDS, up to two per CU), any layout
+// and epilogue, where the 128 x 128 tiling leaves CUs idle and the 64 x 64 grid holds at most
+// 640 tiles (2.5 per CU).  Measured (FP16 / BF16, µs, against what these calls took before):
+// 1024^3 5.8-6.0 against 9.2-10.4 with either operand transposed, accumulating, negated or
+// with 16-bit C (the 128 x 128 tile on 64 CUs), against 7.6 for plain products (the
+// register-staged 64 x 64 tile); 1536^3 equal, 1536^2 x 4096 37.3 against 39.8 and ragged
+// 1500 x 1456 x 1000 16.5 against 24.7 (the register-staged 128 x 64 tile); 1792^3 (784
+// tiles) 10 % slower than that tile, and 30 % slower with A transposed than the 128 x 128
+// direct-to-LDS one.
+inline bool use_dma64(const GemmArgs &g) {
+    return (long)cdiv(g.M, 128) * cdiv(g.N, 128) < 256 && (long)cdiv(g.M, 64) * cdiv(g.N, 64) <= 640 &&
+           use_dma(g, 64);
 }
 
 template <typename T, bool A_MN, bool B_MN, int EPI, int EM, int EN>
@@ -783,6 +799,7 @@ hipError_t launch_layout(const GemmArgs &g, hipStream_t s) {
         if (rect == -192) return launch_rect<T, A_MN, B_MN, EPI, 256, 192>(g, s);
         return launch_cfg<T, 256, 256, 2, 2, 1, A_MN, B_MN, EPI>(g, s);
     }
+    if (use_dma64(g)) return launch_dma<T, A_MN, B_MN, EPI, 64, dma::ring_stages(64)>(g, s);
     if constexpr (!A_MN && EPI == 0) {
         if (use_64x64(g)) return launch_cfg<T, 64, 64, 1, 2, 4, A_MN, B_MN, EPI>(g, s);
         if (use_128x64(g)) return launch_cfg<T, 128, 64, 2, 2, 2, A_MN, B_MN, EPI>(g, s);

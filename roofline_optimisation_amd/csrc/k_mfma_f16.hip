@@ -31,6 +31,11 @@ const char *desc_mfma_f16(int dtype, const GemmArgs &g) {
     const int bm = big ? 256 : (small ? 64 : 128), bn = big ? 256 : (small || narrow ? 64 : 128);
     out = name;
     const int rect = big ? rect_choice(g) : 256;
+    if (!big && use_dma64(g)) {
+        out += " 64x64x32 w2x2 lds-dma";
+        if (dma_ragged_k(g, 64)) out += " k-zero-fill";
+        return out.c_str();
+    }
     if (rect != 256) {
         out += rect == 192 ? " 192x256x32 w2x2 lds-dma" : " 256x192x32 w2x2 lds-dma";
         if (dma_ragged_k(g, 256)) out += " k-zero-fill";

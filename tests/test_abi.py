@@ -164,7 +164,20 @@ def test_dispatch_choices_general_form(lib):
         "mfma_f16 128x128x64 w2x2 dwordx4 | edges=clamped"
     # with K a multiple of 8 the direct-to-LDS kernel zero-fills past K in every layout
     assert dx(-1, 1, gb.TRANS_A | gb.TRANS_B, 1000, 1000, 1000, P, 1000, P, 1000, P, 1000) == \
-        "mfma_f16 128x128x32 w2x2 lds-dma k-zero-fill"
+        "mfma_f16 64x64x32 w2x2 lds-dma k-zero-fill"
+    # the 64 x 64 direct-to-LDS tile: any layout and epilogue where the 128 x 128 grid leaves
+    # CUs idle and the 64 x 64 one holds at most 640 tiles; register staging below K = 256
+    assert dx(-1, 2, gb.TRANS_A | gb.ACCUMULATE, 1024, 1024, 1024, P, 1024, P, 1024, P, 1024) == \
+        "mfma_bf16 64x64x32 w2x2 lds-dma"
+    assert dx(-1, 1, gb.C_16 | gb.NEG_B, 768, 768, 1024, P, 1024, P, 768, P, 768) == \
+        "mfma_f16 64x64x32 w2x2 lds-dma"
+    assert dx(-1, 2, 0, 1500, 1456, 1000, P, 1000, P, 1456, P, 1456) == \
+        "mfma_bf16 64x64x32 w2x2 lds-dma k-zero-fill"
+    assert dx(-1, 1, gb.TRANS_A, 1792, 1792, 1792, P, 1792, P, 1792, P, 1792) == \
+        "mfma_f16 128x128x32 w2x2 lds-dma"
+    assert dx(-1, 1, 0, 1792, 1792, 1792, P, 1792, P, 1792, P, 1792).startswith("mfma_f16 128x64x64")
+    assert dx(-1, 1, gb.TRANS_B, 1024, 1024, 128, P, 128, P, 128, P, 1024).startswith("mfma_f16 64x64x64 w1x2")
+    assert dx(-1, 1, gb.TRANS_A, 1024, 1024, 128, P, 1024, P, 1024, P, 1024).startswith("mfma_f16 128x128x64")
     # the 192 x 256 and 256 x 192 tiles take every layout (an m/n-contiguous operand of
     # extent 192 in LDS rows of 24 chunks) and every epilogue (signed, accumulating, 16-bit
     # C); between equal grids the one whose 192 side is k-contiguous wins, then 192 x 256

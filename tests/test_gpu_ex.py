@@ -394,8 +394,8 @@ def test_matmul_wrapper_c16():
 # transposed, negated and accumulating (K not a whole number of ring trips) and with B not
 # transposed; 256 x 192 (B transposed, so k-contiguous) with A transposed, ragged M and N,
 # K not a whole number of ring trips, negated and accumulating, and plain on 4096 x 3072
-# (256 tiles against 192 of 256 x 256); and with the 192 side m/n-contiguous, loaded 256
-# wide: 192 x 256 with A transposed (ragged N, K past whole trips, negated B, accumulating)
+# (256 tiles against 192 of 256 x 256); and with the 192 side m/n-contiguous, in LDS rows
+# of 24 chunks: 192 x 256 with A transposed (ragged N, K past whole trips, negated B, accumulating)
 # and 256 x 192 with B n-contiguous (negated A, padded B rows, 520 = 4 x 128 + 8); each with
 # FP32 and with 16-bit C, against the oracle and bit for bit against the same call on
 # 256 x 256 tiles (VARIANT_MFMA_T256X256).
@@ -433,3 +433,37 @@ def test_rect_tile_general_form(case):
     C16r, ok_r, SA, SB = run_ex16(A, B, dtype, *fl, Cin16, gb.VARIANT_AUTO, pad)
     C16s, ok_s, _, _ = run_ex16(A, B, dtype, *fl, Cin16, gb.VARIANT_MFMA_T256X256, pad)
     assert ok_r and ok_s and np.array_equal(C16r, C16s), "16-bit C: 192 x 256 and 256 x 256 tiles differ"
+
+
+# The 64 x 64 direct-to-LDS tile in the general form (the 128 x 128 grid would leave CUs
+# idle, the 64 x 64 one holds at most 640 tiles): every transpose, negation and
+# accumulation, ragged M and N (1000 = 15 x 64 + 40, 904 = 14 x 64 + 8), K not a whole
+# number of 256-deep ring trips (1000, 264) with NaN-padded strides, 1500 x 1456 (552
+# tiles); each with FP32 and with 16-bit C, against the oracle.
+DMA64_EX = [("f16", (1024, 1024, 1024), (True, False, False, False, False), (0, 0, 0)),
+            ("bf16", (1024, 1024, 1024), (False, True, True, False, True), (0, 0, 0)),
+            ("f16", (1000, 904, 1000), (True, True, False, True, True), (8, 8, 8)),
+            ("bf16", (512, 512, 264), (True, False, True, True, False), (8, 0, 8)),
+            ("f16", (768, 768, 1024), (False, False, True, True, True), (0, 8, 0)),
+            ("bf16", (1500, 1456, 1000), (False, False, False, False, False), (8, 8, 8))]
+
+
+@pytest.mark.parametrize("case", DMA64_EX, ids=lambda c: c[0] + "_" + "x".join(map(str, c[1])) + "_" +
+                         "".join("1" if f else "0" for f in c[2]))
+def test_dma64_general_form(case):
+    dtype, (M, N, K), fl, pad = case
+    ta, tb = fl[0], fl[1]
+    lda = (M if ta else K) + pad[0]
+    ldb = (K if tb else N) + pad[1]
+    P = 1 << 20
+    flags = flags_of(*fl)
+    code = gb.DTYPE_CODES[dtype]
+    desc = gb.gemm355_kernel_desc_ex(gb.VARIANT_AUTO, code, flags, M, N, K, P, lda, P, ldb, P, N + pad[2])
+    assert desc.startswith(f"mfma_{dtype} 64x64x32 w2x2 lds-dma"), desc
+    A, B, Cin = operands(M, N, K, dtype, 71)
+    C, ok, SA, SB = run_ex(A, B, dtype, *fl, Cin, gb.VARIANT_AUTO, pad)
+    C64, _ = oracle.gemm_ex(SA, SB, dtype, *fl[:4], Cin if fl[4] else None)
+    check(C, C64, dtype, K, Cin if fl[4] else None, ok, f"ex dma64 {dtype} {M}x{N}x{K} {fl}")
+    assert gb.gemm355_kernel_desc_ex(gb.VARIANT_AUTO, code, flags | gb.C_16, M, N, K, P, lda, P, ldb, P,
+                                     N + pad[2]).startswith(f"mfma_{dtype} 64x64x32 w2x2 lds-dma")
+    compare16(M, N, K, dtype, *fl, 72, gb.VARIANT_AUTO, pad)
