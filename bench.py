@@ -863,6 +863,8 @@ def write_report(path):
 
     names = {0: "naive", 1: "lds_tiled", 2: "regblock", 3: "mfma"}
     lines = ["# libgemm355 measurements on one MI355X", "",
+             "Made by `python3 bench.py --no-cpu-baseline --warmup 50 --steps 50 --report PATH` from the",
+             "repository root (the report's own cases; `--steps` and `--warmup` set only the JSON line's run).", "",
              "Per-launch time from HIP events on one stream (mean over >= 3 launches after about 50 ms",
              "of untimed launches of the same case),",
              "U[-1,1] operands, packed row-major strides.  TFLOP/s = 2MNK / t.  Peaks: FP32 157.3,",
