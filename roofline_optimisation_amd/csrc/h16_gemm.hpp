@@ -764,18 +764,22 @@ inline bool use_64x64(const GemmArgs &g) {
 }
 
 // The 64 x 64 direct-to-LDS tile (8-stage ring, 64 KiB of LDS, up to two per CU), any layout
-// and epilogue, where the 128 x 128 tiling leaves CUs idle and the 64 x 64 grid holds at most
-// 640 tiles (2.5 per CU).  Measured (FP16 / BF16, µs, against what these calls took before):
-// 1024^3 5.8-6.0 against 9.2-10.4 with either operand transposed, accumulating, negated or
-// with 16-bit C (the 128 x 128 tile on 64 CUs), against 7.6 for plain products (the
-// register-staged 64 x 64 tile); 1536^3 equal, 1536^2 x 4096 37.3 against 39.8 and ragged
-// 1500 x 1456 x 1000 16.5 against 24.7 (the register-staged 128 x 64 tile); 1792^3 (784
-// tiles) 10 % slower than that tile, and 30 % slower with A transposed than the 128 x 128
-// direct-to-LDS one.
+// and epilogue, where the 128 x 128 tiling leaves CUs idle and the 64 x 64 grid fits one
+// round of two per CU (at most 512 tiles).  Against the 128 x 128 direct-to-LDS tile (FP16 /
+// BF16, µs, transposed, accumulating, negated or 16-bit-C products): 1024^3 5.8-6.0 against
+// 9.2-10.4 (64 CUs busy), 1152^3 9.7 against 12.4, 1280^3 11.1 against 13.2, 1408^3 12.1
+// against 14.6 (484 tiles); from 576 tiles the larger tile wins (1536^3 16.9-18.4 against
+// 14.2-14.6, 1600^3 18.1 against 16.5, 1536^2 x 4096 38.5 against 27.8).
 inline bool use_dma64(const GemmArgs &g) {
-    return (long)cdiv(g.M, 128) * cdiv(g.N, 128) < 256 && (long)cdiv(g.M, 64) * cdiv(g.N, 64) <= 640 &&
+    return (long)cdiv(g.M, 128) * cdiv(g.N, 128) < 256 && (long)cdiv(g.M, 64) * cdiv(g.N, 64) <= 512 &&
            use_dma(g, 64);
 }
+
+// Plain products with A k-contiguous take the register-staged 128 x 64 and 64 x 64 tiles
+// only where the 128 x 128 direct-to-LDS tile cannot run (rows not 16-byte aligned, K not a
+// multiple of 8 or below 256): that tile, on the CUs it leaves idle, is faster than either
+// once the 64 x 64 one no longer fits one round.
+inline bool staged_small_tiles(const GemmArgs &g) { return !use_dma(g, 128); }
 
 template <typename T, bool A_MN, bool B_MN, int EPI, int EM, int EN>
 hipError_t launch_rect(const GemmArgs &g, hipStream_t s) {
@@ -801,8 +805,10 @@ hipError_t launch_layout(const GemmArgs &g, hipStream_t s) {
     }
     if (use_dma64(g)) return launch_dma<T, A_MN, B_MN, EPI, 64, dma::ring_stages(64)>(g, s);
     if constexpr (!A_MN && EPI == 0) {
-        if (use_64x64(g)) return launch_cfg<T, 64, 64, 1, 2, 4, A_MN, B_MN, EPI>(g, s);
-        if (use_128x64(g)) return launch_cfg<T, 128, 64, 2, 2, 2, A_MN, B_MN, EPI>(g, s);
+        if (staged_small_tiles(g)) {
+            if (use_64x64(g)) return launch_cfg<T, 64, 64, 1, 2, 4, A_MN, B_MN, EPI>(g, s);
+            if (use_128x64(g)) return launch_cfg<T, 128, 64, 2, 2, 2, A_MN, B_MN, EPI>(g, s);
+        }
     }
     return launch_cfg<T, 128, 128, 2, 2, 2, A_MN, B_MN, EPI>(g, s);
 }

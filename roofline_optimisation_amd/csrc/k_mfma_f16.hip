@@ -25,7 +25,7 @@ const char *desc_mfma_f16(int dtype, const GemmArgs &g) {
     const bool big = pick_tile(g) == 256;
     const char *name = dtype == kF16 ? "mfma_f16" : "mfma_bf16";
     const int epi = g.c16 ? 2 : (g.signed_or_acc() ? 1 : 0);
-    const bool plain_km = !big && !g.trans_a && epi == 0;
+    const bool plain_km = !big && !g.trans_a && epi == 0 && staged_small_tiles(g);
     const bool small = plain_km && use_64x64(g);
     const bool narrow = plain_km && !small && use_128x64(g);
     const int bm = big ? 256 : (small ? 64 : 128), bn = big ? 256 : (small || narrow ? 64 : 128);

@@ -166,16 +166,23 @@ def test_dispatch_choices_general_form(lib):
     assert dx(-1, 1, gb.TRANS_A | gb.TRANS_B, 1000, 1000, 1000, P, 1000, P, 1000, P, 1000) == \
         "mfma_f16 64x64x32 w2x2 lds-dma k-zero-fill"
     # the 64 x 64 direct-to-LDS tile: any layout and epilogue where the 128 x 128 grid leaves
-    # CUs idle and the 64 x 64 one holds at most 640 tiles; register staging below K = 256
+    # CUs idle and the 64 x 64 one holds at most 512 tiles (beyond, the 128 x 128
+    # direct-to-LDS tile, plain products included); register staging below K = 256
     assert dx(-1, 2, gb.TRANS_A | gb.ACCUMULATE, 1024, 1024, 1024, P, 1024, P, 1024, P, 1024) == \
         "mfma_bf16 64x64x32 w2x2 lds-dma"
     assert dx(-1, 1, gb.C_16 | gb.NEG_B, 768, 768, 1024, P, 1024, P, 768, P, 768) == \
         "mfma_f16 64x64x32 w2x2 lds-dma"
-    assert dx(-1, 2, 0, 1500, 1456, 1000, P, 1000, P, 1456, P, 1456) == \
+    assert dx(-1, 2, 0, 1400, 1400, 1000, P, 1000, P, 1400, P, 1400) == \
         "mfma_bf16 64x64x32 w2x2 lds-dma k-zero-fill"
+    assert dx(-1, 2, 0, 1500, 1456, 1000, P, 1000, P, 1456, P, 1456) == \
+        "mfma_bf16 128x128x32 w2x2 lds-dma k-zero-fill"
+    assert dx(-1, 1, gb.TRANS_A, 1536, 1536, 1536, P, 1536, P, 1536, P, 1536) == \
+        "mfma_f16 128x128x32 w2x2 lds-dma"
     assert dx(-1, 1, gb.TRANS_A, 1792, 1792, 1792, P, 1792, P, 1792, P, 1792) == \
         "mfma_f16 128x128x32 w2x2 lds-dma"
-    assert dx(-1, 1, 0, 1792, 1792, 1792, P, 1792, P, 1792, P, 1792).startswith("mfma_f16 128x64x64")
+    assert dx(-1, 1, 0, 1792, 1792, 1792, P, 1792, P, 1792, P, 1792) == "mfma_f16 128x128x32 w2x2 lds-dma"
+    # the register-staged 128 x 64 tile where the direct-to-LDS one cannot run (K below 256)
+    assert dx(-1, 1, 0, 1792, 1792, 200, P, 200, P, 1792, P, 1792).startswith("mfma_f16 128x64x64")
     assert dx(-1, 1, gb.TRANS_B, 1024, 1024, 128, P, 128, P, 128, P, 1024).startswith("mfma_f16 64x64x64 w1x2")
     assert dx(-1, 1, gb.TRANS_A, 1024, 1024, 128, P, 1024, P, 1024, P, 1024).startswith("mfma_f16 128x128x64")
     # the 192 x 256 and 256 x 192 tiles take every layout (an m/n-contiguous operand of

@@ -436,16 +436,16 @@ def test_rect_tile_general_form(case):
 
 
 # The 64 x 64 direct-to-LDS tile in the general form (the 128 x 128 grid would leave CUs
-# idle, the 64 x 64 one holds at most 640 tiles): every transpose, negation and
+# idle, the 64 x 64 one holds at most 512 tiles): every transpose, negation and
 # accumulation, ragged M and N (1000 = 15 x 64 + 40, 904 = 14 x 64 + 8), K not a whole
-# number of 256-deep ring trips (1000, 264) with NaN-padded strides, 1500 x 1456 (552
+# number of 256-deep ring trips (1000, 264) with NaN-padded strides, 1400 x 1400 (484
 # tiles); each with FP32 and with 16-bit C, against the oracle.
 DMA64_EX = [("f16", (1024, 1024, 1024), (True, False, False, False, False), (0, 0, 0)),
             ("bf16", (1024, 1024, 1024), (False, True, True, False, True), (0, 0, 0)),
             ("f16", (1000, 904, 1000), (True, True, False, True, True), (8, 8, 8)),
             ("bf16", (512, 512, 264), (True, False, True, True, False), (8, 0, 8)),
             ("f16", (768, 768, 1024), (False, False, True, True, True), (0, 8, 0)),
-            ("bf16", (1500, 1456, 1000), (False, False, False, False, False), (8, 8, 8))]
+            ("bf16", (1400, 1400, 1000), (False, False, False, False, False), (8, 8, 8))]
 
 
 @pytest.mark.parametrize("case", DMA64_EX, ids=lambda c: c[0] + "_" + "x".join(map(str, c[1])) + "_" +
