@@ -507,9 +507,12 @@ inline bool op_fits(bool mn, int ext, int K, int ld) {
 // (128 KiB, one per CU) when the grid fits one round of 256, else 4 (64 KiB, two per CU:
 // grids of more than 256 tiles then run at most ceil(tiles / 512) rounds, where one
 // workgroup per CU would take ceil(tiles / 256); with one tile per CU the deeper ring is
-// the faster one, 2048^3 FP16 19.5 against 24.7 us).
+// the faster one, 2048^3 FP16 19.5 against 24.7 us).  64-wide tiles 8 (64 KiB).  A K below
+// an 8-stage trip (128 <= K < 256) takes the 4-stage ring, one trip of 128, on 128- and
+// 64-wide tiles alike.
 inline int dma_stages(const GemmArgs &g, int tile) {
     if (tile == 128 && (long)cdiv(g.M, 128) * cdiv(g.N, 128) > 256) return 4;
+    if (tile != 256 && g.K < dma::kBK * 8) return 4;
     return dma::ring_stages(tile);
 }
 
@@ -527,6 +530,16 @@ inline bool use_dma(const GemmArgs &g, int tile) {
     // an m/n-contiguous operand's extent is a whole number of 16-byte chunks, so no
     // load straddles the end of its last row
     if ((g.trans_a && g.M % 8 != 0) || (!g.trans_b && g.N % 8 != 0)) return false;
+    // K from 128 to 255 on a tile that takes the 8-stage ring otherwise (64 wide, or 128 wide
+    // one per CU) runs on the 4-stage ring, except for plain products with K a whole number of
+    // 64-wide k-steps, whose register-staged interior tiles (two staging sets, no predicates)
+    // were as fast or faster: BF16 2048^2 x 128 6.25 against 7.19 us, FP16 1536^2 x 192 6.57
+    // against 6.81; elsewhere the ring won (1024^2 x 200 with A transposed 4.96 against 8.21,
+    // 2048^2 x 136 8.16 against 10.81, 2048^2 x 192 accumulating 8.32 against 9.29)
+    const bool two_per_cu = tile == 128 && (long)cdiv(g.M, 128) * cdiv(g.N, 128) > 256;
+    if (tile != 256 && !two_per_cu && g.K < dma::kBK * 8 && g.K % 64 == 0 && !g.trans_a &&
+        !g.signed_or_acc() && !g.c16)
+        return false;
     const int kpad = cdiv(g.K, trip) * trip;
     return (tile == 256 || tile == 128 || tile == 64) && h16_vec(g) && g.K >= trip && g.K % 8 == 0 &&
            g.M >= tile && g.N >= tile && op_fits(g.trans_a != 0, tile, kpad, g.lda) &&
@@ -683,7 +696,7 @@ hipError_t launch_cfg(const GemmArgs &g, hipStream_t s) {
     const H16Plan p = plan_cfg(BM, BN, A_MN, B_MN, EPI, g);
     if constexpr (BM == BN && BM >= 64) {
         if (p.dma) {
-            if constexpr (BM == 128)
+            if constexpr (BM == 128 || BM == 64)
                 if (dma_stages(g, BM) == 4) return launch_dma<T, A_MN, B_MN, EPI, BM, 4>(g, s);
             return launch_dma<T, A_MN, B_MN, EPI, BM, dma::ring_stages(BM)>(g, s);
         }
@@ -803,7 +816,10 @@ hipError_t launch_layout(const GemmArgs &g, hipStream_t s) {
         if (rect == -192) return launch_rect<T, A_MN, B_MN, EPI, 256, 192>(g, s);
         return launch_cfg<T, 256, 256, 2, 2, 1, A_MN, B_MN, EPI>(g, s);
     }
-    if (use_dma64(g)) return launch_dma<T, A_MN, B_MN, EPI, 64, dma::ring_stages(64)>(g, s);
+    if (use_dma64(g)) {
+        if (dma_stages(g, 64) == 4) return launch_dma<T, A_MN, B_MN, EPI, 64, 4>(g, s);
+        return launch_dma<T, A_MN, B_MN, EPI, 64, dma::ring_stages(64)>(g, s);
+    }
     if constexpr (!A_MN && EPI == 0) {
         if (staged_small_tiles(g)) {
             if (use_64x64(g)) return launch_cfg<T, 64, 64, 1, 2, 4, A_MN, B_MN, EPI>(g, s);

@@ -33,6 +33,7 @@ const char *desc_mfma_f16(int dtype, const GemmArgs &g) {
     const int rect = big ? rect_choice(g) : 256;
     if (!big && use_dma64(g)) {
         out += " 64x64x32 w2x2 lds-dma";
+        if (dma_stages(g, 64) == 4) out += " ring4";
         if (dma_ragged_k(g, 64)) out += " k-zero-fill";
         return out.c_str();
     }

@@ -181,10 +181,18 @@ def test_dispatch_choices_general_form(lib):
     assert dx(-1, 1, gb.TRANS_A, 1792, 1792, 1792, P, 1792, P, 1792, P, 1792) == \
         "mfma_f16 128x128x32 w2x2 lds-dma"
     assert dx(-1, 1, 0, 1792, 1792, 1792, P, 1792, P, 1792, P, 1792) == "mfma_f16 128x128x32 w2x2 lds-dma"
-    # the register-staged 128 x 64 tile where the direct-to-LDS one cannot run (K below 256)
-    assert dx(-1, 1, 0, 1792, 1792, 200, P, 200, P, 1792, P, 1792).startswith("mfma_f16 128x64x64")
-    assert dx(-1, 1, gb.TRANS_B, 1024, 1024, 128, P, 128, P, 128, P, 1024).startswith("mfma_f16 64x64x64 w1x2")
-    assert dx(-1, 1, gb.TRANS_A, 1024, 1024, 128, P, 1024, P, 1024, P, 1024).startswith("mfma_f16 128x128x64")
+    # K from 128 to 255 on the 4-stage ring, but for plain products with K of 128 or 192; the
+    # register-staged 128 x 64 and 64 x 64 tiles where the direct-to-LDS one does not run
+    assert dx(-1, 1, 0, 1792, 1792, 200, P, 200, P, 1792, P, 1792) == \
+        "mfma_f16 128x128x32 w2x2 lds-dma ring4 k-zero-fill"
+    assert dx(-1, 2, gb.TRANS_A, 1024, 1024, 128, P, 1024, P, 1024, P, 1024) == "mfma_bf16 64x64x32 w2x2 lds-dma ring4"
+    assert dx(-1, 1, 0, 1792, 1792, 100, P, 100, P, 1792, P, 1792).startswith("mfma_f16 128x64x64")
+    assert dx(-1, 1, gb.TRANS_B, 1024, 1024, 120, P, 120, P, 120, P, 1024).startswith("mfma_f16 64x64x64 w1x2")
+    assert dx(-1, 2, 0, 2048, 2048, 128, P, 128, P, 2048, P, 2048).startswith("mfma_bf16 128x128x64 w2x2 dwordx4")
+    assert dx(-1, 2, 0, 2048, 4096, 128, P, 128, P, 4096, P, 4096) == "mfma_bf16 128x128x32 w2x2 lds-dma ring4"
+    assert dx(-1, 2, gb.ACCUMULATE, 2048, 2048, 192, P, 192, P, 2048, P, 2048) == \
+        "mfma_bf16 128x128x32 w2x2 lds-dma ring4 k-zero-fill"
+    assert dx(-1, 1, gb.TRANS_A, 1024, 1024, 120, P, 1024, P, 1024, P, 1024).startswith("mfma_f16 128x128x64")
     # the 192 x 256 and 256 x 192 tiles take every layout (an m/n-contiguous operand of
     # extent 192 in LDS rows of 24 chunks) and every epilogue (signed, accumulating, 16-bit
     # C); between equal grids the one whose 192 side is k-contiguous wins, then 192 x 256

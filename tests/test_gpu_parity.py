@@ -235,9 +235,11 @@ def test_torch_matmul_wrapper():
     check(out.cpu().numpy(), C64, "f32", "uniform", 33, True, "matmul wrapper")
 
 
-# Interior-tile instances of the 16-bit kernel: an even number of 64-wide k-steps
-# (paired staging), an odd number, a single k-step, rows that are not 16-byte
-# aligned (16-byte loads at element alignment), and a misaligned base; each with M, N multiples of the tile.
+# Whole-tile products of the 16-bit kernel at small sizes: K of 256 and 320 (the 64 x 64
+# direct-to-LDS tile, the second past whole ring trips), 192 (three 64-wide k-steps on the
+# register-staged tile) and a single k-step, rows that are not 16-byte aligned (register
+# staging, 16-byte loads at element alignment), and a misaligned base; each with M, N
+# multiples of the tile.
 INTERIOR_CASES = [((512, 512, 256), (0, 0, 0), 0), ((512, 512, 320), (0, 0, 0), 0),
                   ((256, 256, 64), (0, 0, 0), 0), ((512, 256, 256), (1, 3, 0), 0),
                   ((256, 512, 128), (0, 0, 0), 1), ((1024, 768, 192), (8, 8, 8), 0)]
@@ -355,7 +357,7 @@ CLAMP_CASES = [((4000, 4004, 256), (0, 0, 0), "all", "all=clamped,paired"),
                ((777, 1030, 301), (3, 5, 0), "all", "edges=clamped"),
                ((8000, 8004, 64), (0, 0, 0), "rows", "interior=pointer edges=clamped"),
                ((8000, 8004, 128), (0, 4, 4), "rows", "interior=buffer,paired edges=clamped,paired"),
-               ((512, 768, 200), (0, 0, 0), "all", "edges=predicated")]
+               ((512, 768, 120), (0, 0, 0), "all", "edges=predicated")]
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
@@ -463,12 +465,16 @@ def test_f32_tile_classes(case):
 
 
 # FP16/BF16 tile classes of plain products: 64 x 64 (the 128 x 64 tiling would still leave
-# CUs idle) register-staged (K below one ring trip of 256 or not a multiple of 8; interior,
-# ragged, K tail) and direct-to-LDS, 128 x 64 (the 128 x 128 tiling would; interior and
-# ragged), 128 x 128, 256 x 256 direct-to-LDS.
-H16_TILE_CASES = [("f16", (1024, 1024, 128), "64x64x64 w1x2"), ("f16", (1024, 1024, 256), "64x64x32 w2x2 lds-dma"),
+# CUs idle) register-staged (K below 128, not a multiple of 8, rows not 16-byte aligned, or
+# a plain product with K of 128 or 192; interior, ragged, K tail) and direct-to-LDS
+# (8-stage ring, and the 4-stage one for other K from 128 to 255), 128 x 64 register-staged
+# (the 128 x 128 tiling would leave CUs idle; interior and ragged), 128 x 128 direct-to-LDS
+# on the 4-stage ring, 256 x 256 direct-to-LDS.
+H16_TILE_CASES = [("f16", (1024, 1024, 120), "64x64x64 w1x2"), ("f16", (1024, 1024, 256), "64x64x32 w2x2 lds-dma"),
+                  ("f16", (1024, 1024, 128), "64x64x64 w1x2"), ("f16", (1024, 1024, 136), "64x64x32 w2x2 lds-dma ring4"),
                   ("bf16", (1000, 900, 200), "64x64x64 w1x2"),
-                  ("f16", (512, 512, 100), "64x64x64 w1x2"), ("bf16", (1536, 1536, 128), "128x64x64"),
+                  ("f16", (512, 512, 100), "64x64x64 w1x2"), ("bf16", (1536, 1536, 120), "128x64x64"),
+                  ("bf16", (1536, 1536, 128), "128x64x64"), ("bf16", (1536, 1536, 200), "128x128x32 w2x2 lds-dma ring4"),
                   ("f16", (1500, 1450, 200), "128x64x64"), ("bf16", (2048, 2048, 128), "128x128"),
                   ("f16", (3072, 3072, 128), "lds-dma")]
 
@@ -520,7 +526,9 @@ def test_dma_rect_tile(case):
 # NaN-padded strides and K not a whole number of trips (1000 = 7 x 128 + 104).
 RING4_CASES = [("f16", (2304, 2304, 512), (0, 0, 0), "mfma_f16 128x128x32 w2x2 lds-dma ring4"),
                ("bf16", (2048, 4096, 256), (0, 0, 0), "mfma_bf16 128x128x32 w2x2 lds-dma ring4"),
-               ("bf16", (2500, 2600, 1000), (8, 8, 8), "mfma_bf16 128x128x32 w2x2 lds-dma ring4 k-zero-fill")]
+               ("bf16", (2500, 2600, 1000), (8, 8, 8), "mfma_bf16 128x128x32 w2x2 lds-dma ring4 k-zero-fill"),
+               # one workgroup per CU with K from 128 to 255 (136 = 128 + 8)
+               ("f16", (2048, 2048, 136), (8, 8, 8), "mfma_f16 128x128x32 w2x2 lds-dma ring4 k-zero-fill")]
 
 
 @pytest.mark.parametrize("case", RING4_CASES, ids=lambda c: c[0] + "_" + "x".join(map(str, c[1])) + f"_pad{c[2][0]}")
@@ -544,12 +552,15 @@ def test_dma_128_two_per_cu(case):
 # K a multiple of 8 and at least one 256-deep ring trip): a single tile, whole tiles, ragged
 # M (1000 = 15 x 64 + 40) and N (904 = 14 x 64 + 8: a last tile one 16-byte chunk wide)
 # with NaN-padded strides and K not a whole number of trips (1000 = 3 x 256 + 232, 264 =
-# 256 + 8), and a deep K (4096).
+# 256 + 8), a deep K (4096), and K from 128 to 255 on the 4-stage ring (136 = 128 + 8,
+# and 200 = 128 + 72 on ragged tiles).
 DMA64_CASES = [("f16", (64, 64, 256), (0, 0, 0), "mfma_f16 64x64x32 w2x2 lds-dma"),
                ("f16", (1024, 1024, 1024), (0, 0, 0), "mfma_f16 64x64x32 w2x2 lds-dma"),
                ("bf16", (1000, 904, 1000), (8, 8, 8), "mfma_bf16 64x64x32 w2x2 lds-dma k-zero-fill"),
                ("bf16", (512, 512, 264), (8, 0, 8), "mfma_bf16 64x64x32 w2x2 lds-dma k-zero-fill"),
-               ("f16", (520, 1000, 4096), (0, 8, 0), "mfma_f16 64x64x32 w2x2 lds-dma")]
+               ("f16", (520, 1000, 4096), (0, 8, 0), "mfma_f16 64x64x32 w2x2 lds-dma"),
+               ("f16", (512, 512, 136), (0, 0, 0), "mfma_f16 64x64x32 w2x2 lds-dma ring4 k-zero-fill"),
+               ("bf16", (1000, 904, 200), (8, 8, 8), "mfma_bf16 64x64x32 w2x2 lds-dma ring4 k-zero-fill")]
 
 
 @pytest.mark.parametrize("case", DMA64_CASES, ids=lambda c: c[0] + "_" + "x".join(map(str, c[1])) + f"_pad{c[2][0]}")
