@@ -415,6 +415,19 @@ RING4_SHAPES = [("f16", 2304, 2304, 2304, ()), ("f16", 2560, 2560, 2560, ()), ("
                 ("f16", 2048, 4096, 2048, ()), ("bf16", 2500, 2600, 1000, ()),
                 ("f16", 2560, 2560, 2560, ("TRANS_A",)), ("f16", 2560, 2560, 2560, ("NEG_A", "ACCUMULATE"))]
 
+# Calls of small grids that the dispatcher gives a direct-to-LDS tile and variant
+# MFMA_STAGED_SMALL does not: the 64 x 64 tile (plain, general form, ragged, deep K), the
+# 128 x 128 one for plain products whose grid leaves CUs idle, and the 4-stage ring for K
+# from 128 to 255.
+SMALL_SHAPES = [("bf16", 1024, 1024, 1024, ()), ("f16", 1024, 1024, 1024, ()), ("bf16", 512, 512, 512, ()),
+                ("f16", 1024, 1024, 4096, ()), ("bf16", 1000, 1000, 1000, ()),
+                ("f16", 1024, 1024, 1024, ("TRANS_A",)), ("bf16", 1024, 1024, 1024, ("C_16",)),
+                ("f16", 1280, 1280, 1280, ("TRANS_B", "ACCUMULATE")), ("bf16", 1408, 1408, 1408, ("NEG_A",)),
+                ("f16", 1536, 1536, 1536, ()), ("f16", 1792, 1792, 1792, ()), ("f16", 1536, 1536, 4096, ()),
+                ("bf16", 1500, 1456, 1000, ()), ("f16", 1600, 1600, 1600, ()),
+                ("bf16", 1024, 1024, 200, ("TRANS_A",)), ("f16", 2048, 2048, 136, ()),
+                ("f16", 1792, 1792, 248, ("TRANS_B",)), ("bf16", 2048, 2048, 192, ("ACCUMULATE",))]
+
 
 def _time_pair(dt, M, N, K, fl, alt, warm, rounds, reps, stream):
     """Median times (us) of one call on variant `alt` and as dispatched, through
@@ -468,11 +481,12 @@ def _time_pair(dt, M, N, K, fl, alt, warm, rounds, reps, stream):
 
 
 def tile_lines(warm=300, rounds=5, reps=100):
-    """Two tile classes against what the dispatcher took before them, on calls it gives
-    them: the 192 x 256 and 256 x 192 tiles against the 256 x 256 one (variant
-    MFMA_T256X256), and the two-per-CU 128 x 128 direct-to-LDS tile against the
-    register-staged kernel (variant MFMA_STAGED128).  Rounds: ceil(tiles / slots), the waves of resident work each grid
-    takes (256 slots for one workgroup per CU, 512 for two)."""
+    """Tile classes against what the dispatcher took before them, on calls it gives them:
+    the 192 x 256 and 256 x 192 tiles against the 256 x 256 one (variant MFMA_T256X256),
+    the two-per-CU 128 x 128 direct-to-LDS tile against the register-staged kernel (variant
+    MFMA_STAGED128), and the direct-to-LDS tiles of small grids against the register-staged
+    and 128 x 128 ones (variant MFMA_STAGED_SMALL).  Rounds: ceil(tiles / slots), the waves
+    of resident work each grid takes (256 slots for one workgroup per CU, 512 for two)."""
     import torch
 
     from roofline_optimisation_amd import binding as gb
@@ -512,6 +526,22 @@ def tile_lines(warm=300, rounds=5, reps=100):
         out.append(f"| {dt} | {M}x{N}x{K} | {fl_text} | {t128} ({cdiv(t128, 512)}) | {st:.2f} | {dis:.2f} | "
                    f"{st / dis:.3f}x | {tf:.0f} | {100 * tf / PEAKS[dt]:.1f} | `{md_cell(ks)}` | `{md_cell(kd)}` |")
         log(f"[tiles] {dt} {M}x{N}x{K} {'|'.join(fl) or 'plain'}: staged {st:.2f} us, "
+            f"dispatched {dis:.2f} us ({st / dis:.3f}x)")
+    out += ["", "## Direct-to-LDS tiles of small grids against the kernels they replaced", "",
+            "The 64 x 64 direct-to-LDS tile (8-stage ring, or 4-stage for K from 128 to 255) where the 128 x 128 "
+            "grid leaves CUs idle and the 64 x 64 one fits one round of two per CU; the 128 x 128 direct-to-LDS tile "
+            "for plain products past that; the 4-stage ring for K from 128 to 255.  Before: variant "
+            "`mfma_staged_small`.", "",
+            "| dtype | M x N x K | flags | before µs | dispatched µs | speedup | TFLOP/s | % of peak | "
+            "kernel before | dispatched kernel |",
+            "|---|---|---|---|---|---|---|---|---|---|"]
+    for dt, M, N, K, fl in SMALL_SHAPES:
+        st, dis, ks, kd = _time_pair(dt, M, N, K, fl, gb.VARIANT_MFMA_STAGED_SMALL, warm, rounds, reps, stream)
+        tf = 2.0 * M * N * K / dis / 1e6
+        fl_text = " \\| ".join(fl) or "plain"
+        out.append(f"| {dt} | {M}x{N}x{K} | {fl_text} | {st:.2f} | {dis:.2f} | {st / dis:.3f}x | {tf:.0f} | "
+                   f"{100 * tf / PEAKS[dt]:.1f} | `{md_cell(ks)}` | `{md_cell(kd)}` |")
+        log(f"[tiles] {dt} {M}x{N}x{K} {'|'.join(fl) or 'plain'}: before {st:.2f} us, "
             f"dispatched {dis:.2f} us ({st / dis:.3f}x)")
     return out
 
@@ -934,7 +964,7 @@ def main():
                          "workloads, write the markdown table to PATH and print one JSON line "
                          "for the 16384 x 4096 workload; no GEMM timing")
     ap.add_argument("--family", choices=["naive", "lds_tiled", "regblock", "mfma", "mfma_split",
-                                         "mfma_w8", "mfma_t256x128", "mfma_t256x256", "mfma_staged128"], default=None,
+                                         "mfma_w8", "mfma_t256x128", "mfma_t256x256", "mfma_staged128", "mfma_staged_small"], default=None,
                     help="only launch one kernel family (--warmup untimed and --steps timed "
                          "launches, for counter passes) on the FP32 3072^3 workload, or with "
                          "--family-dtype f16/bf16 on the n^3 16-bit workload (seed 3); no JSON line")

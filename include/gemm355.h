@@ -86,7 +86,7 @@ typedef enum gemm355_variant {
      * gemm355_gemm_ex flag or a shape the kernel does not take returns
      * GEMM355_ERR_UNSUPPORTED).  Shapes taken: whole tiles (M a multiple of 256, N of
      * the tile width), 16-byte-aligned rows, K a multiple of 128 (MFMA_T256X256 and
-     * MFMA_STAGED128: any shape and gemm355_gemm_ex flags).
+     * MFMA_STAGED128 and MFMA_STAGED_SMALL: any shape and gemm355_gemm_ex flags).
      * MFMA_SPLIT: wave specialisation ("Advanced CUDA features - starting from GEMM",
      *   scheduling section, the warp-specialisation path): 256 x 128 tiles, four producer
      *   waves issue every global -> LDS load while four compute waves (128 x 64 of C
@@ -105,12 +105,19 @@ typedef enum gemm355_variant {
      * MFMA_STAGED128: the dispatched kernels with the two-per-CU 128 x 128 direct-to-LDS
      *   tile turned off: grids of more than 256 128-wide tiles go to the register-staged
      *   kernel, every other call as dispatched (any F16 / BF16 product the dispatcher
-     *   takes, gemm355_gemm_ex flags included). */
+     *   takes, gemm355_gemm_ex flags included).
+     * MFMA_STAGED_SMALL: the dispatched kernels with the direct-to-LDS tiles of small
+     *   grids turned off: no 64 x 64 direct-to-LDS tile, no 4-stage ring for K from 128
+     *   to 255 on tiles that otherwise take the 8-stage one, and plain products whose
+     *   128 x 128 grid leaves CUs idle on the register-staged 128 x 64 and 64 x 64 tiles;
+     *   every other call as dispatched (any F16 / BF16 product the dispatcher takes,
+     *   gemm355_gemm_ex flags included). */
     GEMM355_VARIANT_MFMA_SPLIT = 4,
     GEMM355_VARIANT_MFMA_W8 = 5,
     GEMM355_VARIANT_MFMA_T256X128 = 6,
     GEMM355_VARIANT_MFMA_T256X256 = 7,
-    GEMM355_VARIANT_MFMA_STAGED128 = 8
+    GEMM355_VARIANT_MFMA_STAGED128 = 8,
+    GEMM355_VARIANT_MFMA_STAGED_SMALL = 9
 } gemm355_variant;
 
 /* C = A.B with FP32 operands and FP32 accumulation. */

@@ -21,14 +21,15 @@ F32, F16, BF16 = 0, 1, 2
 VARIANT_AUTO, VARIANT_NAIVE, VARIANT_LDS_TILED, VARIANT_REGBLOCK, VARIANT_MFMA = -1, 0, 1, 2, 3
 # measurement-only schedules of the FP16/BF16 direct-to-LDS kernel (plain products)
 VARIANT_MFMA_SPLIT, VARIANT_MFMA_W8, VARIANT_MFMA_T256X128 = 4, 5, 6
-# measurement only: the dispatched kernels without the 192 x 256 and 256 x 192 tiles, or
-# without the two-per-CU 128 x 128 direct-to-LDS tile
-VARIANT_MFMA_T256X256, VARIANT_MFMA_STAGED128 = 7, 8
+# measurement only: the dispatched kernels without the 192 x 256 and 256 x 192 tiles,
+# without the two-per-CU 128 x 128 direct-to-LDS tile, or without the direct-to-LDS tiles
+# of small grids
+VARIANT_MFMA_T256X256, VARIANT_MFMA_STAGED128, VARIANT_MFMA_STAGED_SMALL = 7, 8, 9
 VARIANTS = {"naive": VARIANT_NAIVE, "lds_tiled": VARIANT_LDS_TILED,
             "regblock": VARIANT_REGBLOCK, "mfma": VARIANT_MFMA, "auto": VARIANT_AUTO,
             "mfma_split": VARIANT_MFMA_SPLIT, "mfma_w8": VARIANT_MFMA_W8,
             "mfma_t256x128": VARIANT_MFMA_T256X128, "mfma_t256x256": VARIANT_MFMA_T256X256,
-            "mfma_staged128": VARIANT_MFMA_STAGED128}
+            "mfma_staged128": VARIANT_MFMA_STAGED128, "mfma_staged_small": VARIANT_MFMA_STAGED_SMALL}
 DTYPE_CODES = {"f32": F32, "f16": F16, "bf16": BF16}
 TRANS_A, TRANS_B, NEG_A, NEG_B, ACCUMULATE, C_16 = 1, 2, 4, 8, 16, 32
 

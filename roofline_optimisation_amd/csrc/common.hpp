@@ -66,6 +66,7 @@ struct GemmArgs {
     // Keep the 128 x 128 direct-to-LDS tile to grids of at most 256 tiles (one per CU);
     // larger grids go to the register-staged kernel (a measurement-only variant sets it).
     int one_round_128 = 0;
+    int staged_small = 0;
     // The MFMA kernels have plain variants (store the accumulators as they are) and
     // variants that store sign * acc (+ C); the latter serve negated products too.
     bool signed_or_acc() const { return accumulate || sign < 0.0f; }

@@ -68,6 +68,13 @@ GemmArgs one_round_128(const GemmArgs &g) {
     return h;
 }
 
+// The dispatched 16-bit kernels with the direct-to-LDS tiles of small grids turned off.
+GemmArgs staged_small(const GemmArgs &g) {
+    GemmArgs h = g;
+    h.staged_small = 1;
+    return h;
+}
+
 bool variant_supported(int variant, int dtype) {
     switch (variant) {
     case GEMM355_VARIANT_NAIVE:
@@ -78,7 +85,8 @@ bool variant_supported(int variant, int dtype) {
     case GEMM355_VARIANT_MFMA_W8:
     case GEMM355_VARIANT_MFMA_T256X128:
     case GEMM355_VARIANT_MFMA_T256X256:
-    case GEMM355_VARIANT_MFMA_STAGED128: return dtype == kF16 || dtype == kBF16;
+    case GEMM355_VARIANT_MFMA_STAGED128:
+    case GEMM355_VARIANT_MFMA_STAGED_SMALL: return dtype == kF16 || dtype == kBF16;
     default: return false;
     }
 }
@@ -93,6 +101,7 @@ hipError_t launch(int variant, int dtype, const GemmArgs &g, hipStream_t s) {
     case GEMM355_VARIANT_MFMA_T256X128: return launch_mfma_f16_sched(variant, dtype, g, s);
     case GEMM355_VARIANT_MFMA_T256X256: return launch_mfma_f16(dtype, square(g), s);
     case GEMM355_VARIANT_MFMA_STAGED128: return launch_mfma_f16(dtype, one_round_128(g), s);
+    case GEMM355_VARIANT_MFMA_STAGED_SMALL: return launch_mfma_f16(dtype, staged_small(g), s);
     default: return dtype == kF32 ? launch_mfma_f32(g, s) : launch_mfma_f16(dtype, g, s);
     }
 }
@@ -104,7 +113,7 @@ bool is_sched_variant(int variant) {
 gemm355_status run(int variant, int dtype, int M, int N, int K, const void *A, int lda,
                    const void *B, int ldb, float *C, int ldc, hipStream_t stream) {
     if (!valid_args(dtype, M, N, K, A, lda, B, ldb, C, ldc)) return GEMM355_ERR_INVALID_ARG;
-    if (variant < GEMM355_VARIANT_AUTO || variant > GEMM355_VARIANT_MFMA_STAGED128)
+    if (variant < GEMM355_VARIANT_AUTO || variant > GEMM355_VARIANT_MFMA_STAGED_SMALL)
         return GEMM355_ERR_INVALID_ARG;
     const GemmArgs g{M, N, K, A, lda, B, ldb, C, ldc};
     if (variant == GEMM355_VARIANT_AUTO) variant = auto_variant(dtype, g);
@@ -138,7 +147,7 @@ gemm355_status ex_args(int &variant, int dtype, unsigned flags, int M, int N, in
     if ((long)M * K > 0 && A == nullptr) return GEMM355_ERR_INVALID_ARG;
     if ((long)K * N > 0 && B == nullptr) return GEMM355_ERR_INVALID_ARG;
     if ((long)M * N > 0 && C == nullptr) return GEMM355_ERR_INVALID_ARG;
-    if (variant < GEMM355_VARIANT_AUTO || variant > GEMM355_VARIANT_MFMA_STAGED128)
+    if (variant < GEMM355_VARIANT_AUTO || variant > GEMM355_VARIANT_MFMA_STAGED_SMALL)
         return GEMM355_ERR_INVALID_ARG;
     g = GemmArgs{M, N, K, A, lda, B, ldb, (float *)C, ldc};
     g.c16 = c16;
@@ -149,7 +158,8 @@ gemm355_status ex_args(int &variant, int dtype, unsigned flags, int M, int N, in
     if (variant == GEMM355_VARIANT_AUTO) variant = auto_variant(dtype, g);
     if (!variant_supported(variant, dtype)) return GEMM355_ERR_UNSUPPORTED;
     if (flags != 0 && variant != GEMM355_VARIANT_NAIVE && variant != GEMM355_VARIANT_MFMA &&
-        variant != GEMM355_VARIANT_MFMA_T256X256 && variant != GEMM355_VARIANT_MFMA_STAGED128)
+        variant != GEMM355_VARIANT_MFMA_T256X256 && variant != GEMM355_VARIANT_MFMA_STAGED128 &&
+        variant != GEMM355_VARIANT_MFMA_STAGED_SMALL)
         return GEMM355_ERR_UNSUPPORTED;
     if (is_sched_variant(variant) && M > 0 && N > 0 && !mfma_f16_sched_ok(variant, g))
         return GEMM355_ERR_UNSUPPORTED;
@@ -178,6 +188,7 @@ const char *desc_of(int variant, int dtype, const GemmArgs &g) {
         return mfma_f16_sched_ok(variant, g) ? desc_mfma_f16_sched(variant, dtype) : "invalid";
     case GEMM355_VARIANT_MFMA_T256X256: return desc_mfma_f16(dtype, square(g));
     case GEMM355_VARIANT_MFMA_STAGED128: return desc_mfma_f16(dtype, one_round_128(g));
+    case GEMM355_VARIANT_MFMA_STAGED_SMALL: return desc_mfma_f16(dtype, staged_small(g));
     default: return dtype == kF32 ? desc_mfma_f32(g) : desc_mfma_f16(dtype, g);
     }
 }
@@ -268,6 +279,7 @@ const char *gemm355_variant_name(int variant) {
     case GEMM355_VARIANT_MFMA_T256X128: return "mfma_t256x128";
     case GEMM355_VARIANT_MFMA_T256X256: return "mfma_t256x256";
     case GEMM355_VARIANT_MFMA_STAGED128: return "mfma_staged128";
+    case GEMM355_VARIANT_MFMA_STAGED_SMALL: return "mfma_staged_small";
     default: return "unknown";
     }
 }

@@ -540,6 +540,9 @@ inline bool use_dma(const GemmArgs &g, int tile) {
     if (tile != 256 && !two_per_cu && g.K < dma::kBK * 8 && g.K % 64 == 0 && !g.trans_a &&
         !g.signed_or_acc() && !g.c16)
         return false;
+    // staged_small (a measurement variant): neither the 64 x 64 tile nor the 4-stage ring on
+    // tiles that otherwise take the 8-stage one
+    if (g.staged_small && (tile == 64 || (tile == 128 && !two_per_cu && g.K < dma::kBK * 8))) return false;
     const int kpad = cdiv(g.K, trip) * trip;
     return (tile == 256 || tile == 128 || tile == 64) && h16_vec(g) && g.K >= trip && g.K % 8 == 0 &&
            g.M >= tile && g.N >= tile && op_fits(g.trans_a != 0, tile, kpad, g.lda) &&
@@ -792,7 +795,7 @@ inline bool use_dma64(const GemmArgs &g) {
 // only where the 128 x 128 direct-to-LDS tile cannot run (rows not 16-byte aligned, K not a
 // multiple of 8 or below 256): that tile, on the CUs it leaves idle, is faster than either
 // once the 64 x 64 one no longer fits one round.
-inline bool staged_small_tiles(const GemmArgs &g) { return !use_dma(g, 128); }
+inline bool staged_small_tiles(const GemmArgs &g) { return g.staged_small || !use_dma(g, 128); }
 
 template <typename T, bool A_MN, bool B_MN, int EPI, int EM, int EN>
 hipError_t launch_rect(const GemmArgs &g, hipStream_t s) {

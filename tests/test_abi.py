@@ -46,7 +46,7 @@ def test_version_and_strings(lib):
     assert gb.gemm355_status_string(0) == "ok"
     assert gb.gemm355_status_string(1) == "invalid argument"
     assert gb.gemm355_status_string(99) == "unknown"
-    assert [gb.gemm355_variant_name(v) for v in (-1, 0, 1, 2, 3, 9)] == \
+    assert [gb.gemm355_variant_name(v) for v in (-1, 0, 1, 2, 3, 10)] == \
         ["auto", "naive", "lds_tiled", "regblock", "mfma", "unknown"]
 
 
@@ -76,7 +76,7 @@ def test_invalid_arguments_rejected_on_host(lib, args):
 
 def test_unknown_variant_and_dtype(lib):
     args = (4, 4, 4, P, 4, P, 4, P, 4, 0)
-    assert gb.gemm355_run_variant(9, 0, *args) == gb.ERR_INVALID_ARG
+    assert gb.gemm355_run_variant(10, 0, *args) == gb.ERR_INVALID_ARG
     assert gb.gemm355_run_variant(-2, 0, *args) == gb.ERR_INVALID_ARG
     assert gb.gemm355_run_variant(0, 3, *args) == gb.ERR_INVALID_ARG
     # FP32-only families reject 16-bit operands before touching the device
@@ -252,7 +252,7 @@ def test_gemm_ex_argument_checks(lib):
     assert E(0, 0, 0, 8, 6, 4, P, 3, P, 6, P, 6) == gb.ERR_INVALID_ARG           # lda < K
     assert E(0, 0, 0, 8, 6, 4, P, 4, P, 6, P, 5) == gb.ERR_INVALID_ARG           # ldc < N
     assert E(0, 3, 0, 8, 6, 4, P, 4, P, 6, P, 6) == gb.ERR_INVALID_ARG           # dtype
-    assert E(9, 0, 0, 8, 6, 4, P, 4, P, 6, P, 6) == gb.ERR_INVALID_ARG           # variant
+    assert E(10, 0, 0, 8, 6, 4, P, 4, P, 6, P, 6) == gb.ERR_INVALID_ARG          # variant
     assert E(0, 0, 0, 8, 6, 4, 0, 4, P, 6, P, 6) == gb.ERR_INVALID_ARG           # null A
     # with a flag only the naive and MFMA families exist
     for v in (gb.VARIANT_LDS_TILED, gb.VARIANT_REGBLOCK):
@@ -344,7 +344,7 @@ def test_schedule_variants_contract(lib):
     assert d(gb.VARIANT_MFMA_SPLIT, gb.F16, 512, 384, 128, P, 128, P, 384, P, 384) == \
         "mfma_f16 256x128x32 w2x2 + 4 producer waves lds-dma"
     assert d(gb.VARIANT_MFMA_W8, gb.F16, 512, 384, 128, P, 128, P, 384, P, 384) == "invalid"  # N % 256
-    assert gb.gemm355_run_variant(9, gb.F16, 8, 8, 8, P, 8, P, 8, P, 8, 0) == gb.ERR_INVALID_ARG
+    assert gb.gemm355_run_variant(10, gb.F16, 8, 8, 8, P, 8, P, 8, P, 8, 0) == gb.ERR_INVALID_ARG
 
 
 def test_square_tile_variant_contract(lib):
@@ -393,4 +393,30 @@ def test_staged128_variant_contract(lib):
         for dt in (gb.F16, gb.BF16):
             assert d(v, dt, M, N, K, P, K, P, N, P, N) == d(-1, dt, M, N, K, P, K, P, N, P, N)
     assert d(v, gb.F32, 2560, 2560, 2560, P, 2560, P, 2560, P, 2560) == "invalid"
+    assert gb.gemm355_run_variant(v, gb.F32, 256, 256, 128, P, 128, P, 256, P, 256, 0) == gb.ERR_UNSUPPORTED
+
+
+def test_staged_small_variant_contract(lib):
+    """MFMA_STAGED_SMALL is the dispatcher with the direct-to-LDS tiles of small grids turned
+    off: no 64 x 64 direct-to-LDS tile, no 4-stage ring for K from 128 to 255 where the
+    8-stage one would run, plain products on the register-staged 128 x 64 / 64 x 64 tiles
+    where the 128 x 128 grid leaves CUs idle; every other F16 / BF16 call as dispatched."""
+    d = gb.gemm355_kernel_desc
+    dx = gb.gemm355_kernel_desc_ex
+    v = gb.VARIANT_MFMA_STAGED_SMALL
+    assert gb.gemm355_variant_name(v) == "mfma_staged_small"
+    assert d(-1, gb.BF16, 1024, 1024, 1024, P, 1024, P, 1024, P, 1024) == "mfma_bf16 64x64x32 w2x2 lds-dma"
+    assert d(v, gb.BF16, 1024, 1024, 1024, P, 1024, P, 1024, P, 1024) == \
+        "mfma_bf16 64x64x64 w1x2 dwordx4 | interior=buffer,paired"
+    assert d(v, gb.F16, 1536, 1536, 1536, P, 1536, P, 1536, P, 1536).startswith("mfma_f16 128x64x64 w2x2 dwordx4")
+    assert dx(v, gb.F16, gb.TRANS_A, 1024, 1024, 1024, P, 1024, P, 1024, P, 1024) == \
+        "mfma_f16 128x128x32 w2x2 lds-dma"
+    assert dx(v, gb.F16, gb.TRANS_A, 1024, 1024, 200, P, 1024, P, 1024, P, 1024).startswith(
+        "mfma_f16 128x128x64 w2x2 dwordx4")
+    # two per CU on the 4-stage ring, and the larger tiles, as dispatched
+    for shape in ((4096, 4096, 4096), (3072, 3072, 3072), (2048, 4096, 128), (2560, 2560, 2560), (1000, 1000, 1004)):
+        M, N, K = shape
+        for dt in (gb.F16, gb.BF16):
+            assert d(v, dt, M, N, K, P, K, P, N, P, N) == d(-1, dt, M, N, K, P, K, P, N, P, N)
+    assert d(v, gb.F32, 1024, 1024, 1024, P, 1024, P, 1024, P, 1024) == "invalid"
     assert gb.gemm355_run_variant(v, gb.F32, 256, 256, 128, P, 128, P, 256, P, 256, 0) == gb.ERR_UNSUPPORTED

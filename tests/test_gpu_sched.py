@@ -135,3 +135,27 @@ def test_staged128_variant(case):
     C, ok = gpu_gemm(A, B, dtype, v, pad=pad, guard_rows=1)
     C64, _ = oracle.gemm(A, B, dtype)
     check(C, C64, dtype, K, ok, f"staged128 {dtype} {M}x{N}x{K} pad={pad}")
+
+
+# VARIANT_MFMA_STAGED_SMALL (the dispatcher without the direct-to-LDS tiles of small grids)
+# where the dispatcher takes one of them: the register-staged 64 x 64 and 128 x 64 tiles of
+# plain products, and register staging for K from 128 to 255 (136, predicated tiles); within
+# the bars of the oracle.
+STAGED_SMALL_CASES = [("bf16", (1024, 1024, 1024), (0, 0, 0), "64x64x64 w1x2 dwordx4"),
+                      ("f16", (1536, 1536, 1536), (8, 8, 8), "128x64x64 w2x2 dwordx4"),
+                      ("f16", (2048, 2048, 136), (8, 8, 8), "128x128x64 w2x2 dwordx4")]
+
+
+@pytest.mark.parametrize("case", STAGED_SMALL_CASES, ids=lambda c: c[0] + "_" + "x".join(map(str, c[1])))
+def test_staged_small_variant(case):
+    dtype, (M, N, K), pad, kernel = case
+    code = gb.DTYPE_CODES[dtype]
+    v = gb.VARIANT_MFMA_STAGED_SMALL
+    args = (M, N, K, P, K + pad[0], P, N + pad[1], P, N + pad[2])
+    assert "lds-dma" in gb.gemm355_kernel_desc(gb.VARIANT_AUTO, code, *args)
+    desc = gb.gemm355_kernel_desc(v, code, *args)
+    assert kernel in desc, desc
+    A, B = inputs.make_operands(M, N, K, 77, "uniform", dtype)
+    C, ok = gpu_gemm(A, B, dtype, v, pad=pad, guard_rows=1)
+    C64, _ = oracle.gemm(A, B, dtype)
+    check(C, C64, dtype, K, ok, f"staged_small {dtype} {M}x{N}x{K} pad={pad}")
