@@ -6,7 +6,8 @@
 // ring; the overlap of loads and arithmetic in the scheduling section of "Advanced
 // CUDA features - starting from GEMM"):
 //  * K is walked in steps of 32.  An m/n-contiguous operand goes through a ring of kNs
-//    stages (4 of 16 KiB for 256-wide tiles, 8 of 8 KiB for 128-wide ones), its loads of
+//    stages (4 of 16 KiB for 256-wide tiles, 8 of 8 KiB for 128-wide ones, 8 of 4 KiB for
+//    64-wide ones; 4 for 128- and 64-wide tiles two per CU or with K below 256), its loads of
 //    k-step t + kNs - 1 issued while step t is multiplied, into the stage step t-1 has
 //    released; a k-contiguous operand goes through kNs/2 slots of a 64-wide double step,
 //    loaded every other k-step, so that its loads read whole 128-byte lines (with
@@ -17,7 +18,8 @@
 //    chunk goes;
 //  * a KM operand's rows are 128 bytes, chunk c of row r stored in slot c ^ ((r / 2) %
 //    8); an MN operand's rows are 2 E bytes (E = 256 or 128), chunk c of row k in slot
-//    c ^ 4 (k % 4) ^ 2 ((k / 8) % 2).  With these the fragment reads (ds_read_b128 for
+//    c ^ 4 (k % 4) ^ 2 ((k / 8) % 2) (E = 192 or 64: the keys in DmaOp below).  With
+//    these the fragment reads (ds_read_b128 for
 //    KM, ds_read_b64_tr_b16 for MN) touch distinct banks within every 16 lanes of a
 //    b128 read and every 32 lanes of a b64 read, i.e. no bank conflicts, without padding
 //    (which a contiguous 1 KiB load cannot skip);
@@ -711,9 +713,10 @@ __device__ __forceinline__ void dma_tile(int M, int N, int K, const uint16_t *__
 
 }  // namespace dma
 
-// One workgroup per CU with the default ring (128 KiB of LDS for either tile; E = 256 also
-// takes all 256 accumulator registers of a lane); E = 128 with NS = 4 (64 KiB, 144
-// registers per lane) runs two workgroups per CU.
+// One workgroup per CU with the default ring (128 KiB of LDS for E = 256 and 128; E = 256
+// also takes all 256 accumulator registers of a lane); E = 128 with NS = 4 (64 KiB, 144
+// registers per lane) and E = 64 (64 KiB with 8 stages, 32 KiB with 4; 40-56 registers)
+// run two workgroups per CU.
 // KR: K not a whole number of ring trips (the last trip's chunks past K load as zeros).
 template <typename T, bool A_MN, bool B_MN, int EPI, int E, bool KR = false, int NS = dma::ring_stages(E)>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1)))

@@ -31,8 +31,9 @@
 //    old C (loaded block by block in the epilogue) when accumulating; 2 does the same
 //    with C in the operands' 16-bit type (old C widened, result rounded to nearest even).
 //
-// Square 256 x 256 or 128 x 128 tiles take a second design (dma_tile in h16_dma.hpp)
-// when K is a whole number of its ring's trips (128 or 256) and the m/n-contiguous
+// Square 256 x 256, 128 x 128 or 64 x 64 tiles (and 192 x 256, 256 x 192) take a second
+// design (dma_tile in h16_dma.hpp) when K is a multiple of 8 and at least one trip of its
+// ring (128 or 256), rows are 16-byte aligned and the m/n-contiguous
 // extents are multiples of 8; ragged tiles included: the tiles go from memory straight
 // into LDS (buffer_load_dwordx4 ... lds) through a ring of k-steps, so no registers stage
 // them and no LDS store instructions are issued; LDS rows are XOR-swizzled instead of
@@ -516,8 +517,8 @@ inline int dma_stages(const GemmArgs &g, int tile) {
     return dma::ring_stages(tile);
 }
 
-// The direct-load kernel takes every tile (ragged ones included) of a 256 x 256 or
-// 128 x 128 configuration when rows are 16-byte aligned, K is a multiple of 8 and at least
+// The direct-load kernel takes every tile (ragged ones included) of a 256 x 256, 128 x 128
+// or 64 x 64 configuration when rows are 16-byte aligned, K is a multiple of 8 and at least
 // one trip round the ring (32 x the ring stages: 128 or 256; a K that is not a whole
 // number of trips runs to the next trip with the chunks past K loaded as zeros), and every
 // byte offset up to that trip fits the 31-bit buffer range.  At 128 x 128 the tile's loads
