@@ -225,10 +225,10 @@ def time_variant(variant, dtype, M, N, K, seed, reps=None):
     return e0.elapsed_time(e1) / reps, desc, reps
 
 
-def family_run(family, steps, warmup, dtype="f32", n=0):
+def family_run(family, steps, warmup, dtype="f32", n=0, m=0):
     """`warmup` untimed and `steps` timed launches of one kernel family on the FP32 3072^3
-    workload (seed 1) or an n^3 FP16/BF16 one (seed 3), logged to stderr: the target of
-    the counter passes."""
+    workload (seed 1) or an n^3 FP16/BF16 one (seed 3; m x n x n with m given), logged to
+    stderr: the target of the counter passes."""
     import torch
 
     from roofline_optimisation_amd import binding as gb
@@ -236,15 +236,16 @@ def family_run(family, steps, warmup, dtype="f32", n=0):
 
     variant = gb.VARIANTS[family]
     n = n or (3072 if dtype == "f32" else 4096)
-    A, B = inputs.make_operands(n, n, n, 1 if dtype == "f32" else 3, "uniform", dtype)
+    M = m or n
+    A, B = inputs.make_operands(M, n, n, 1 if dtype == "f32" else 3, "uniform", dtype)
     if dtype == "f32":
         dA, dB = torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda()
     else:
         dA = torch.from_numpy(A.view("int16")).cuda()
         dB = torch.from_numpy(B.view("int16")).cuda()
-    dC = torch.empty((n, n), dtype=torch.float32, device="cuda")
+    dC = torch.empty((M, n), dtype=torch.float32, device="cuda")
     stream = torch.cuda.Stream()
-    args = (variant, gb.DTYPE_CODES[dtype], n, n, n, dA.data_ptr(), n, dB.data_ptr(), n,
+    args = (variant, gb.DTYPE_CODES[dtype], M, n, n, dA.data_ptr(), n, dB.data_ptr(), n,
             dC.data_ptr(), n, stream.cuda_stream)
     desc = gb.gemm355_kernel_desc(*args[:-1])
 
@@ -263,8 +264,8 @@ def family_run(family, steps, warmup, dtype="f32", n=0):
     e1.record(stream)
     stream.synchronize()
     ms = e0.elapsed_time(e1) / max(steps, 1)
-    log(f"[bench] family {family} ({desc}) {dtype} {n}^3: {warmup} + {steps} launches, "
-        f"{ms:.4f} ms/launch, {2.0 * n ** 3 / (ms * 1e-3) / 1e12:.2f} TFLOP/s")
+    log(f"[bench] family {family} ({desc}) {dtype} {M}x{n}x{n}: {warmup} + {steps} launches, "
+        f"{ms:.4f} ms/launch, {2.0 * M * n * n / (ms * 1e-3) / 1e12:.2f} TFLOP/s")
 
 
 RAGGED_K = ((4096, 4096, 4096), (4096, 4000, 4000), (4096, 4064, 4064), (4096, 4072, 4072),
@@ -971,6 +972,8 @@ def main():
     ap.add_argument("--family-dtype", choices=["f32", "f16", "bf16"], default="f32")
     ap.add_argument("--family-n", type=int, default=0,
                     help="square size for --family (default 3072 for f32, 4096 for f16/bf16)")
+    ap.add_argument("--family-m", type=int, default=0,
+                    help="rows of A and C for --family (default --family-n: a square product)")
     ap.add_argument("--schedules", default=None, metavar="PATH",
                     help="only time the schedules of the FP16 direct-to-LDS kernel (dispatched, "
                          "producer/consumer split, eight waves, 256 x 128 tiles) at 4096^3 and "
@@ -1023,7 +1026,7 @@ def main():
             log(f"[bench] calibration copy of {args.calib_copy_mib} MiB done")
 
     if args.family:
-        family_run(args.family, args.steps, args.warmup, args.family_dtype, args.family_n)
+        family_run(args.family, args.steps, args.warmup, args.family_dtype, args.family_n, args.family_m)
         calibration_copy()
         return
 
