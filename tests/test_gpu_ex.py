@@ -447,7 +447,10 @@ DMA64_EX = [("f16", (1024, 1024, 1024), (True, False, False, False, False), (0, 
             ("f16", (768, 768, 1024), (False, False, True, True, True), (0, 8, 0)),
             ("bf16", (1400, 1400, 1000), (False, False, False, False, False), (8, 8, 8)),
             # K from 128 to 255: the 4-stage ring (192 = 128 + 64)
-            ("f16", (1024, 1024, 192), (True, True, True, False, True), (8, 8, 8))]
+            ("f16", (1024, 1024, 192), (True, True, True, False, True), (8, 8, 8)),
+            # thin M or N of 72 (a last tile 8 wide): A m-contiguous, B n-contiguous
+            ("bf16", (72, 4096, 512), (True, False, False, False, False), (8, 8, 8)),
+            ("f16", (4096, 72, 1024), (False, False, False, True, True), (0, 8, 0))]
 
 
 @pytest.mark.parametrize("case", DMA64_EX, ids=lambda c: c[0] + "_" + "x".join(map(str, c[1])) + "_" +
